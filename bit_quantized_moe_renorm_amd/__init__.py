@@ -1,6 +1,207 @@
 """MI355X-native 2-bit routed-MoE block (ds4 / DeepSeek-V4-Flash shapes).
 
-The compute lives in ``libds4moe.so`` (hand-written HIP kernels for gfx950
-behind a C ABI, declared in ``include/ds4moe.h``).  This package is a thin
-ctypes binding: it marshals torch device tensors and streams into that ABI.
+All compute lives in ``libds4moe.so``: hand-written HIP kernels for gfx950
+behind the C ABI declared in ``include/ds4moe.h``.  This module is a thin
+ctypes binding with the same entry points: it only marshals torch device
+tensors and streams (torch is used for device memory and streams) and raises
+when the library returns an error.  There is no fallback: without the built
+library every call raises.
 """
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+from typing import Optional
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libds4moe.so"
+
+OK, EINVAL, ENOMEM, EHIP, EUNSUPPORTED, EPOISONED = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
+ABI_VERSION = 1
+TIMING_KINDS = ("route", "gate_up", "down", "fused", "bucket")
+
+SYMBOLS = ("ds4moe_create", "ds4moe_route", "ds4moe_forward", "ds4moe_set_path", "ds4moe_dequantize",
+           "ds4moe_rmsnorm", "ds4moe_timing_enable", "ds4moe_timing_read", "ds4moe_destroy",
+           "ds4moe_last_error")
+
+
+class Ds4MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"ds4moe error {code}: {msg}")
+        self.code = code
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("n_embd", ctypes.c_int32), ("n_ff", ctypes.c_int32),
+                ("n_expert", ctypes.c_int32), ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("up", ctypes.c_void_p), ("down", ctypes.c_void_p), ("codebook", ctypes.c_void_p),
+                ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: Optional[Path] = None) -> ctypes.CDLL:
+    """Load libds4moe.so.  torch is imported first so that the library binds to
+    the same HIP runtime as torch's tensors and streams."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    import torch  # noqa: F401  (HIP runtime shared with torch)
+    p = Path(path) if path else LIB_PATH
+    if not p.exists():
+        raise RuntimeError(f"{p} is not built; run __graft_entry__.build() or "
+                           "python -m bit_quantized_moe_renorm_amd.build")
+    L = ctypes.CDLL(str(p))
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.ds4moe_create.argtypes = [ctypes.POINTER(Desc), P, ctypes.POINTER(P)]
+    L.ds4moe_route.argtypes = [P, P, i32, P, P, P, P, P]
+    L.ds4moe_forward.argtypes = [P, P, i32, P, P]
+    L.ds4moe_set_path.argtypes = [P, i32]
+    L.ds4moe_dequantize.argtypes = [P, i32, i32, P, P]
+    L.ds4moe_rmsnorm.argtypes = [P, i32, i32, ctypes.c_double, P, P]
+    L.ds4moe_timing_enable.argtypes = [P, i32]
+    L.ds4moe_timing_read.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.ds4moe_destroy.argtypes = [P]
+    L.ds4moe_last_error.restype = ctypes.c_char_p
+    for name in SYMBOLS:
+        if name != "ds4moe_last_error":
+            getattr(L, name).restype = ctypes.c_int
+    if path is None:
+        _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise Ds4MoeError(rc, load_library().ds4moe_last_error().decode())
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+class MoELayer:
+    """One MoE layer resident on the GPU (a ``ds4moe_t`` handle).
+
+    ``weights`` holds device tensors in the canonical block layout:
+    router fp32 [NE, E], router_bias fp32 [NE] or None, gate/up uint8
+    [NE, F, E/256, 66], down uint8 [NE, E, F/256, 84], codebook (host, 256
+    uint16 values), sh_gate/sh_up/sh_down bf16 or None.
+    """
+
+    def __init__(self, spec, weights: dict, max_tokens: int, act_dtype: int = BF16, stream=None):
+        import numpy as np
+        L = load_library()
+        cb = np.ascontiguousarray(weights["codebook"], dtype=np.uint16)
+        self._cb = cb
+        d = Desc(ABI_VERSION, spec.n_embd, spec.n_ff, spec.n_expert, spec.top_k,
+                 1 if weights.get("sh_gate") is not None else 0, max_tokens, act_dtype,
+                 _ptr(weights["router"]), _ptr(weights.get("router_bias")), _ptr(weights["gate"]),
+                 _ptr(weights["up"]), _ptr(weights["down"]), cb.ctypes.data,
+                 _ptr(weights.get("sh_gate")), _ptr(weights.get("sh_up")), _ptr(weights.get("sh_down")))
+        h = ctypes.c_void_p()
+        _check(L.ds4moe_create(ctypes.byref(d), _stream(stream), ctypes.byref(h)))
+        self.h = h
+        self.spec = spec
+        self.max_tokens = max_tokens
+        self.act_dtype = act_dtype
+
+    def close(self):
+        if getattr(self, "h", None):
+            load_library().ds4moe_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_path(self, path: int):
+        _check(load_library().ds4moe_set_path(self.h, path))
+
+    def forward(self, x, out, stream=None):
+        """out += MoE(x) (x [n, E] bf16/fp32, out [n, E] fp32, both on the GPU)."""
+        n = x.shape[0]
+        _check(load_library().ds4moe_forward(self.h, _ptr(x), n, _ptr(out), _stream(stream)))
+
+    def route(self, x, stream=None):
+        """Returns (idx int32 [n,k], w fp32 [n,k], offsets int32 [NE+1], tokens int32 [n*k])."""
+        import torch
+        n, k, NE = x.shape[0], self.spec.top_k, self.spec.n_expert
+        dev = x.device
+        idx = torch.empty((n, k), dtype=torch.int32, device=dev)
+        w = torch.empty((n, k), dtype=torch.float32, device=dev)
+        off = torch.empty((NE + 1,), dtype=torch.int32, device=dev)
+        tok = torch.empty((max(n * k, 1),), dtype=torch.int32, device=dev)
+        _check(load_library().ds4moe_route(self.h, _ptr(x), n, _ptr(idx), _ptr(w), _ptr(off), _ptr(tok),
+                                           _stream(stream)))
+        return idx, w, off, tok[: n * k]
+
+    def dequantize(self, expert: int, which: int, stream=None):
+        """fp32 matrix decoded from the library's repacked layout (0 gate, 1 up, 2 down)."""
+        import torch
+        s = self.spec
+        shape = (s.n_ff, s.n_embd) if which < 2 else (s.n_embd, s.n_ff)
+        dst = torch.empty(shape, dtype=torch.float32, device="cuda")
+        _check(load_library().ds4moe_dequantize(self.h, expert, which, _ptr(dst), _stream(stream)))
+        return dst
+
+    def timing_enable(self, on: bool = True):
+        _check(load_library().ds4moe_timing_enable(self.h, 1 if on else 0))
+
+    def timing_read(self):
+        ms = (ctypes.c_double * 8)()
+        cnt = (ctypes.c_int64 * 8)()
+        _check(load_library().ds4moe_timing_read(self.h, ms, cnt))
+        return {TIMING_KINDS[i]: (ms[i], cnt[i]) for i in range(len(TIMING_KINDS)) if cnt[i]}
+
+
+def rmsnorm(h, eps: float = 1e-6, out=None, stream=None):
+    """bf16 RMSNorm (unit gain) of fp32 h [n, E] on the GPU."""
+    import torch
+    n, E = h.shape
+    if out is None:
+        out = torch.empty((n, E), dtype=torch.bfloat16, device=h.device)
+    _check(load_library().ds4moe_rmsnorm(_ptr(h), n, E, eps, _ptr(out), _stream(stream)))
+    return out
+
+
+def upload_layer(layer, device="cuda"):
+    """Copy a host ``synth.Layer`` to device tensors in the canonical layout."""
+    import numpy as np
+    import torch
+
+    def t(a, dtype=None):
+        if a is None:
+            return None
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if dtype is not None:
+            x = x.view(dtype)
+        return x.to(device)
+
+    return dict(router=t(layer.router), router_bias=t(layer.router_bias), gate=t(layer.gate), up=t(layer.up),
+                down=t(layer.down), codebook=layer.codebook,
+                sh_gate=t(None if layer.sh_gate is None else layer.sh_gate.view(np.int16), torch.bfloat16),
+                sh_up=t(None if layer.sh_up is None else layer.sh_up.view(np.int16), torch.bfloat16),
+                sh_down=t(None if layer.sh_down is None else layer.sh_down.view(np.int16), torch.bfloat16))
+
+
+def to_device_x(x_np, device="cuda"):
+    """Activations from synth (uint16 bf16 bits or fp32) as a device tensor."""
+    import numpy as np
+    import torch
+    if x_np.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x_np).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(x_np, dtype=np.float32)).to(device)

@@ -1,0 +1,102 @@
+// common.h - internal declarations shared by the libds4moe HIP sources.
+//
+// Library-owned device layout of one layer (all planes 256-byte aligned):
+//
+//   IQ2-style gate / up, per matrix [n_expert][n_ff rows][nbe = n_embd/256 blocks]:
+//     qs plane  : 64 bytes per block = 8 sub-blocks x 4 groups x one 16-bit field
+//     d  plane  : fp16 d per block
+//   Each 16-bit group field re-encodes the canonical (index byte, 7 sign bits,
+//   one bit of the sub-block scale) without changing the information:
+//     bits 0-2   signs of weights 0,1,2
+//     bit  3     P = parity of the signs of weights 0..3
+//     bits 4-11  codebook index
+//     bits 12-14 signs of weights 4,5,6
+//     bit  15    bit g of the sub-block scale ls (group g of the sub-block)
+//   so that bits 0..11 index a 4096-entry table of the signed levels of
+//   weights 0..3 and bits 3..14 a 4096-entry table of weights 4..7 (the sign
+//   of weight 7 is P ^ s4 ^ s5 ^ s6, the canonical parity rule).
+//
+//   Q2_K-style down, per matrix [n_expert][n_embd rows][nbf = n_ff/256 blocks]:
+//     qs plane  : 64 bytes per block (canonical qs[64])
+//     sc plane  : 16 bytes per block (canonical scales[16])
+//     dd plane  : uint32 per block = d | dmin << 16 (fp16 bits)
+//
+// The planes hold exactly the canonical bytes (66 = 64 + 2, 84 = 64 + 16 + 4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ds4 {
+
+constexpr int QK = 256;
+constexpr int MAX_TOPK = 8;
+constexpr int MAX_EXPERT = 256;
+constexpr int GEMV_MAX_TOK = 4;   // GEMV path keeps up to this many tokens' x in registers
+
+struct Layer {
+    int n_embd, n_ff, n_expert, top_k, n_shared, max_tokens, act_dtype;
+    int nbe, nbf;                   // blocks per gate/up row, per down row
+    // weights (library-owned)
+    const float *router;            // [NE][E]
+    const float *router_bias;       // [NE] or nullptr
+    const uint16_t *codebook;       // [256] device copy
+    const uint8_t *iq2_qs[2];       // gate, up: [NE][F][nbe][64]
+    const uint16_t *iq2_d[2];       // [NE][F][nbe]
+    const uint8_t *q2k_qs;          // [NE][E][nbf][64]
+    const uint8_t *q2k_sc;          // [NE][E][nbf][16]
+    const uint32_t *q2k_dd;         // [NE][E][nbf]
+    const uint16_t *sh_gate, *sh_up, *sh_down;
+};
+
+// Workspace (device), carved from one allocation at create time.
+struct Work {
+    float *logits;        // [max_tokens][NE]
+    int32_t *idx;         // [max_tokens][k]
+    float *w;             // [max_tokens][k]
+    int32_t *offsets;     // [NE+1]
+    int32_t *list;        // [max_tokens*k] entries t*k + j, grouped by expert, ascending t
+    int32_t *active;      // [NE+1]: active[0] = U, active[1..U] = experts with tokens, ascending
+    int32_t *counters;    // [16] completion counters (self-resetting)
+    float *hbuf;          // [max_tokens*(k+1)][F] fp32 activations between gate/up and down
+    uint16_t *hbuf16;     // [max_tokens*(k+1)][F] fp16 activations (GEMM path)
+    float *wsum;          // unused padding slot
+};
+
+// ---------------------------------------------------------------- small device helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ float half_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// ---------------------------------------------------------------- host-side launchers
+// Each returns hipGetLastError() after enqueueing.
+hipError_t launch_repack_iq2(const uint8_t *canon, int64_t n_blocks, uint8_t *qs, uint16_t *d,
+                             hipStream_t s);
+hipError_t launch_repack_q2k(const uint8_t *canon, int64_t n_blocks, uint8_t *qs, uint8_t *sc,
+                             uint32_t *dd, hipStream_t s);
+hipError_t launch_dequant_iq2(const Layer &L, int which, int expert, float *dst, hipStream_t s);
+hipError_t launch_dequant_q2k(const Layer &L, int expert, float *dst, hipStream_t s);
+
+hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s,
+                        hipEvent_t *ev /* nullable: [2] around the route kernels */);
+hipError_t launch_route_export(const Layer &L, const Work &W, int n_tok, int32_t *idx, float *w,
+                               int32_t *offsets, int32_t *tokens, hipStream_t s);
+
+hipError_t launch_gemv_gateup(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);
+hipError_t launch_gemv_down(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
+
+bool gemm_enabled();
+hipError_t launch_gemm_gateup(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);
+hipError_t launch_gemm_down(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
+
+hipError_t launch_rmsnorm(const float *h, int n_tok, int n_embd, double eps, uint16_t *x, hipStream_t s);
+
+}  // namespace ds4

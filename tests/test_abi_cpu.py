@@ -1,0 +1,75 @@
+"""The C-ABI library loads and exports every entry point include/ds4moe.h
+declares; argument validation returns errors without touching a GPU."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "ds4moe.h"
+
+
+def declared_symbols():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^(?:int|const char \*)\s*(ds4moe_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import bit_quantized_moe_renorm_amd as m
+    if not m.LIB_PATH.exists():
+        from bit_quantized_moe_renorm_amd import build
+        build.build()
+    return m.load_library()
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for s in ("ds4moe_create", "ds4moe_route", "ds4moe_forward", "ds4moe_destroy", "ds4moe_last_error"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import bit_quantized_moe_renorm_amd as m
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+    assert sorted(m.SYMBOLS) == declared_symbols()
+
+
+def test_validation_without_gpu(lib):
+    import bit_quantized_moe_renorm_amd as m
+    h = ctypes.c_void_p()
+    # NULL description
+    assert lib.ds4moe_create(None, None, ctypes.byref(h)) == m.EINVAL
+    # bad sizes: n_embd not a supported power of two
+    d = m.Desc(m.ABI_VERSION, 300, 256, 8, 2, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None)
+    assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
+    assert b"n_embd" in lib.ds4moe_last_error()
+    # top_k > n_expert
+    d = m.Desc(m.ABI_VERSION, 256, 256, 4, 6, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None)
+    assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
+    # wrong ABI version
+    d = m.Desc(99, 256, 256, 8, 2, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None)
+    assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
+    # shared expert requested but missing
+    d = m.Desc(m.ABI_VERSION, 256, 256, 8, 2, 1, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None)
+    assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
+    # NULL handle on every per-handle entry point
+    assert lib.ds4moe_forward(None, None, 1, None, None) == m.EINVAL
+    assert lib.ds4moe_route(None, None, 1, None, None, None, None, None) == m.EINVAL
+    assert lib.ds4moe_set_path(None, 0) == m.EINVAL
+    assert lib.ds4moe_dequantize(None, 0, 0, None, None) == m.EINVAL
+    assert lib.ds4moe_timing_enable(None, 1) == m.EINVAL
+    assert lib.ds4moe_destroy(None) == m.OK
+    # rmsnorm argument checks; n_tok == 0 is a no-op
+    assert lib.ds4moe_rmsnorm(None, -1, 16, 1e-6, None, None) == m.EINVAL
+    assert lib.ds4moe_rmsnorm(None, 1, 0, 1e-6, None, None) == m.EINVAL
+    assert lib.ds4moe_rmsnorm(None, 0, 16, 1e-6, None, None) == m.OK
+
+
+def test_binding_has_no_fallback(tmp_path):
+    """Without the built library the binding raises instead of computing anything."""
+    import bit_quantized_moe_renorm_amd as m
+    with pytest.raises(RuntimeError):
+        m.load_library(tmp_path / "missing.so")

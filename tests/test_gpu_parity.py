@@ -1,0 +1,151 @@
+"""GPU parity against the CPU oracle, through the C ABI.
+
+Bit-exact: decoded weights, routed expert indices, per-expert token lists.
+Within tolerance: renormalised routing weights (fp32 ulps) and block outputs
+(max|gpu - ref| / max|ref| <= 2e-3).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from bit_quantized_moe_renorm_amd import synth
+from gpu_common import GEMV_TOL, REL_TOL, device_layer, host_layer, log, rel_err
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bit_quantized_moe_renorm_amd as m  # noqa: E402
+
+
+# ------------------------------------------------------------------ dequantisation
+@pytest.mark.parametrize("kind,experts", [("tiny", list(range(8))), ("ds4", [0, 97, 255])])
+def test_dequant_bitwise(kind, experts):
+    lay = host_layer(kind)
+    dev = device_layer(kind)
+    for e in experts:
+        for which, name in enumerate(("gate", "up", "down")):
+            log(f"[gpu] dequant {kind} expert {e} {name}")
+            got = dev.dequantize(e, which).cpu().numpy()
+            ref = oracle.dequant_matrix(lay, e, name)
+            assert got.shape == ref.shape
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (kind, e, name)
+
+
+# ------------------------------------------------------------------ routing
+def _check_route(kind, x_np, dev, lay):
+    x = m.to_device_x(x_np)
+    idx, w, off, tok = dev.route(x)
+    torch.cuda.synchronize()
+    lg, ridx, rw, rw64 = oracle.route(x_np, lay.router, lay.router_bias, lay.spec.top_k)
+    roff, rtok = oracle.bucket(ridx, lay.spec.n_expert)
+    idx, w, off, tok = idx.cpu().numpy(), w.cpu().numpy(), off.cpu().numpy(), tok.cpu().numpy()
+    bad = np.nonzero(np.any(idx != ridx, axis=1))[0]
+    if len(bad):
+        t = bad[0]
+        srt = np.sort(lg[t])[::-1]
+        log(f"[gpu] route mismatch token {t}: gpu {idx[t]} ref {ridx[t]} gap6/7 {srt[5] - srt[6]}")
+    assert np.array_equal(idx, ridx), kind
+    assert np.array_equal(off, roff), kind
+    assert np.array_equal(tok, rtok), kind
+    assert np.max(np.abs(w.astype(np.float64) - rw64)) <= 2.5e-7, kind
+    assert np.allclose(w.sum(1), 1.0, atol=1e-6)
+
+
+def test_route_tiny():
+    lay = host_layer("tiny")
+    _check_route("tiny", synth.activations(0, 4, 256, bf16=False), device_layer("tiny"), lay)
+
+
+@pytest.mark.parametrize("n", [1, 3, 16, 64])
+def test_route_ds4_decode(n):
+    lay = host_layer("ds4")
+    log(f"[gpu] route ds4 n={n}")
+    _check_route("ds4", synth.activations(1, n, 4096), device_layer("ds4"), lay)
+
+
+@pytest.mark.parametrize("n", [8, 16, 32])
+def test_route_zipf_batches(n):
+    lay = host_layer("ds4_zipf")
+    log(f"[gpu] route ds4 zipf n={n}")
+    _check_route("zipf", synth.activations(1, n, 4096), device_layer("ds4_zipf"), lay)
+
+
+def test_route_prefill_2048():
+    lay = host_layer("ds4")
+    log("[gpu] route ds4 n=2048")
+    _check_route("prefill", synth.activations(1, 2048, 4096), device_layer("ds4", 2048), lay)
+
+
+def test_route_empty_and_errors():
+    dev = device_layer("tiny")
+    x = torch.zeros((0, 256), device="cuda")
+    idx, w, off, tok = dev.route(x)     # n_tok == 0: nothing enqueued
+    assert idx.numel() == 0
+    with pytest.raises(m.Ds4MoeError) as ei:
+        dev.forward(torch.zeros((65, 256), device="cuda"), torch.zeros((65, 256), device="cuda"))
+    assert ei.value.code == m.EINVAL
+
+
+# ------------------------------------------------------------------ block output, GEMV path
+def _forward(dev, x_np, path=m.PATH_AUTO, out0=None):
+    x = m.to_device_x(x_np)
+    out = torch.zeros((x.shape[0], x.shape[1]), dtype=torch.float32, device="cuda")
+    if out0 is not None:
+        out.copy_(torch.from_numpy(out0))
+    dev.set_path(path)
+    dev.forward(x, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_forward_tiny_gemv():
+    lay = host_layer("tiny")
+    x = synth.activations(0, 4, 256, bf16=False)
+    got = _forward(device_layer("tiny"), x, m.PATH_GEMV)
+    ref, _, _ = oracle.forward(lay, x)
+    err = rel_err(got, ref)
+    log(f"[gpu] tiny gemv rel err {err:.3e}")
+    assert err <= GEMV_TOL
+
+
+@pytest.mark.parametrize("n", [1, 2, 4])
+def test_forward_ds4_gemv(n):
+    lay = host_layer("ds4")
+    x = synth.activations(1, n, 4096, start=10)
+    log(f"[gpu] ds4 gemv n={n}")
+    got = _forward(device_layer("ds4"), x, m.PATH_GEMV)
+    ref, _, _ = oracle.forward(lay, x)
+    err = rel_err(got, ref)
+    log(f"[gpu] ds4 gemv n={n} rel err {err:.3e}")
+    assert err <= REL_TOL and err <= GEMV_TOL
+
+
+def test_forward_accumulates_into_residual():
+    lay = host_layer("ds4")
+    x = synth.activations(1, 1, 4096, start=3)
+    r = synth.residual(5, 1, 4096)
+    got = _forward(device_layer("ds4"), x, m.PATH_GEMV, out0=r)
+    ref, _, _ = oracle.forward(lay, x)
+    assert rel_err(got - r, ref) <= GEMV_TOL
+
+
+def test_forward_gemv_rejects_large_batches():
+    dev = device_layer("ds4")
+    dev.set_path(m.PATH_GEMV)
+    x = torch.zeros((5, 4096), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((5, 4096), device="cuda")
+    with pytest.raises(m.Ds4MoeError) as ei:
+        dev.forward(x, out)
+    assert ei.value.code == m.EUNSUPPORTED
+    dev.set_path(m.PATH_AUTO)
+
+
+# ------------------------------------------------------------------ RMSNorm
+def test_rmsnorm_matches_oracle():
+    h = (synth.residual(7, 33, 4096) * 3).astype(np.float32)
+    got = m.rmsnorm(torch.from_numpy(h).cuda()).cpu().view(torch.int16).numpy().view(np.uint16)
+    ref, _ = oracle.rmsnorm(h, 1e-6)
+    assert np.array_equal(got, ref)
