@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Benchmark of the 2-bit routed-MoE block on one MI355X.
+
+Default workload (a step = one decode token through one DS4-shape MoE layer:
+router, top-6, bucketing, 6 routed IQ2/Q2_K experts, bf16 shared expert and
+the weighted scatter into the residual):
+  n_embd 4096, n_ff 2048, 256 experts, top-6, 1 shared expert, seed 1,
+  a stream of 1000 seeded N(0,1) bf16 tokens, one forward call per token.
+
+The layer is created R times (identical bytes, separate buffers) and the
+steps cycle through the copies, so consecutive uses of one copy are R * 97 MB
+apart and nothing is served from the 256 MB Infinity Cache: every step
+streams its weights from HBM, as in a stack of distinct layers.
+
+Prints ONE JSON line on stdout; details go to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE-layer tok/s + achieved HBM GB/s (% of peak), decode b=1 and prefill 2048"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def touched_bytes(spec, n_distinct_experts, shared=True):
+    from bit_quantized_moe_renorm_amd import synth
+    nb = synth.layer_nbytes(spec)
+    return n_distinct_experts * nb["per_expert"] + (nb["shared"] if shared else 0)
+
+
+def kernel_bytes_decode(spec):
+    """Algorithmic bytes per launch of each decode kernel at b = 1 (6 distinct experts).
+
+    "fused" is the single persistent launch that reads all of them: the router
+    (fp32), the shared expert (bf16) and the 6 selected experts as stored."""
+    from bit_quantized_moe_renorm_amd import synth
+    nb = synth.layer_nbytes(spec)
+    E, F, k = spec.n_embd, spec.n_ff, spec.top_k
+    parts = {
+        "route": nb["router"],
+        "gateup_shared": 2 * E * F * 2,
+        "gateup_routed": k * 2 * nb["gate"],
+        "down_routed": k * nb["down"],
+        "down_shared": E * F * 2,
+    }
+    parts["fused"] = sum(parts.values())
+    return parts
+
+
+def cpu_baseline_decode(layer, x_np, budget_s=12.0):
+    """The oracle (as it stands) on the host cores, on a bounded sample of the same
+    token stream: batches of 16 tokens until about budget_s seconds have passed."""
+    import oracle
+    done, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(layer, x_np[done:done + 16])
+        done += 16
+        el = time.perf_counter() - t0
+        if el >= budget_s or done + 16 > len(x_np):
+            break
+    return {"value": done / el, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {done} of the 1000 decode tokens, oracle.forward in batches of 16 "
+                      f"({el:.1f} s)"}
+
+
+def run_decode(args):
+    import numpy as np
+    import torch
+
+    import bit_quantized_moe_renorm_amd as m
+    from bit_quantized_moe_renorm_amd import synth
+
+    spec = synth.DS4
+    t0 = time.perf_counter()
+    layer = synth.make_layer(spec, seed=1)
+    x_np = synth.activations(1, 1000, spec.n_embd)
+    log(f"[bench] generated layer + 1000 tokens in {time.perf_counter() - t0:.1f} s")
+    w = m.upload_layer(layer)
+    reps = [m.MoELayer(spec, w, max_tokens=1) for _ in range(args.replicas)]
+    del w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    x = m.to_device_x(x_np)
+    out = torch.zeros((1000, spec.n_embd), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    R = len(reps)
+
+    def step(i):
+        t = i % 1000
+        reps[i % R].forward(x[t:t + 1], out[t:t + 1], stream)
+
+    for i in range(args.warmup):
+        step(i)
+    # pass 1 (the value): K steps back to back, bracketed by synchronisation only
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    # pass 2 (kernel durations): the same K steps with HIP events recorded by the
+    # library around each kernel on the caller's stream (an event pair per launch
+    # adds about 4 us of stream time, so pass 1 alone gives the throughput)
+    for r in reps:
+        r.timing_enable(True)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i)
+    torch.cuda.synchronize()
+    wall_ev = time.perf_counter() - t2
+    tot = {}
+    for r in reps:
+        for kind, (ms, cnt) in r.timing_read().items():
+            a = tot.setdefault(kind, [0.0, 0])
+            a[0] += ms
+            a[1] += cnt
+        r.timing_enable(False)
+    avg_us = {k: 1000.0 * v[0] / v[1] for k, v in tot.items() if v[1]}
+    log(f"[bench] pass with per-launch events: {1e6 * wall_ev / args.steps:.2f} us/step")
+    kb = kernel_bytes_decode(spec)
+    per_kernel = {k: {"avg_us": round(avg_us[k], 3), "bytes": kb[k],
+                      "GB_s": round(kb[k] / (avg_us[k] * 1e-6) / 1e9, 1)} for k in avg_us if k in kb}
+    log("[bench] per-kernel: " + json.dumps(per_kernel))
+    # the kernel with the most algorithmic bytes is the dominant one
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["bytes"])
+    achieved = per_kernel[dom]["GB_s"]
+
+    tok_s = args.steps / wall
+    ms_step = 1000.0 * wall / args.steps
+    layer_bytes = touched_bytes(spec, spec.top_k)
+    layer_gbs = layer_bytes / (wall / args.steps) / 1e9
+    log(f"[bench] decode b=1: {tok_s:.0f} tok/s, {ms_step * 1000:.2f} us/token, touched-expert "
+        f"{layer_gbs:.0f} GB/s = {100 * layer_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s")
+
+    res = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "DS4-shape MoE layer decode b=1 (n_embd 4096, n_ff 2048, 256 experts, top-6, "
+                               "1 shared; IQ2-style gate/up, Q2_K-style down; seed 1; 1000-token stream)",
+                   "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)",
+                   "replicas": R,
+                   "touched_expert_bytes_per_token": layer_bytes,
+                   "layer_GB_s": round(layer_gbs, 1),
+                   "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+                   "per_kernel": per_kernel},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(layer, x_np)
+        log(f"[bench] cpu baseline: {res['cpu_baseline']}")
+    for r in reps:
+        r.close()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X only: this build runs the MoE block on a single GPU "
+              "(no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    res = run_decode(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,7 +20,8 @@ OK, EINVAL, ENOMEM, EHIP, EUNSUPPORTED, EPOISONED = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
 ABI_VERSION = 1
-TIMING_KINDS = ("route", "gate_up", "down", "fused", "bucket")
+TIMING_KINDS = ("route", "gateup_routed", "gateup_shared", "down_routed", "down_shared", "gemm_gateup",
+                "gemm_down", "fused")
 
 SYMBOLS = ("ds4moe_create", "ds4moe_route", "ds4moe_forward", "ds4moe_set_path", "ds4moe_dequantize",
            "ds4moe_rmsnorm", "ds4moe_timing_enable", "ds4moe_timing_read", "ds4moe_destroy",

@@ -3,18 +3,9 @@
 // Library-owned device layout of one layer (all planes 256-byte aligned):
 //
 //   IQ2-style gate / up, per matrix [n_expert][n_ff rows][nbe = n_embd/256 blocks]:
-//     qs plane  : 64 bytes per block = 8 sub-blocks x 4 groups x one 16-bit field
+//     qs plane  : 64 bytes per block = the 8 canonical sub-blocks of 8 bytes
+//                 (4 codebook indices, then the sign/scale word), 8-byte aligned
 //     d  plane  : fp16 d per block
-//   Each 16-bit group field re-encodes the canonical (index byte, 7 sign bits,
-//   one bit of the sub-block scale) without changing the information:
-//     bits 0-2   signs of weights 0,1,2
-//     bit  3     P = parity of the signs of weights 0..3
-//     bits 4-11  codebook index
-//     bits 12-14 signs of weights 4,5,6
-//     bit  15    bit g of the sub-block scale ls (group g of the sub-block)
-//   so that bits 0..11 index a 4096-entry table of the signed levels of
-//   weights 0..3 and bits 3..14 a 4096-entry table of weights 4..7 (the sign
-//   of weight 7 is P ^ s4 ^ s5 ^ s6, the canonical parity rule).
 //
 //   Q2_K-style down, per matrix [n_expert][n_embd rows][nbf = n_ff/256 blocks]:
 //     qs plane  : 64 bytes per block (canonical qs[64])
@@ -56,7 +47,7 @@ struct Work {
     int32_t *offsets;     // [NE+1]
     int32_t *list;        // [max_tokens*k] entries t*k + j, grouped by expert, ascending t
     int32_t *active;      // [NE+1]: active[0] = U, active[1..U] = experts with tokens, ascending
-    int32_t *counters;    // [16] completion counters (self-resetting)
+    int32_t *counters;    // [16 * 64] completion counters, one per 256-byte slot (self-resetting)
     float *hbuf;          // [max_tokens*(k+1)][F] fp32 activations between gate/up and down
     uint16_t *hbuf16;     // [max_tokens*(k+1)][F] fp16 activations (GEMM path)
     float *wsum;          // unused padding slot
@@ -90,12 +81,23 @@ hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok,
 hipError_t launch_route_export(const Layer &L, const Work &W, int n_tok, int32_t *idx, float *w,
                                int32_t *offsets, int32_t *tokens, hipStream_t s);
 
-hipError_t launch_gemv_gateup(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);
-hipError_t launch_gemv_down(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
+hipError_t launch_gemv_gateup_routed(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);
+hipError_t launch_gemv_gateup_shared(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);
+hipError_t launch_gemv_down_routed(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
+hipError_t launch_gemv_down_shared(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
+
+// Timing brackets recorded by ds4moe_forward when timing is enabled.
+enum TimingKind {
+    TK_ROUTE = 0, TK_GU_ROUTED = 1, TK_GU_SHARED = 2, TK_DN_ROUTED = 3, TK_DN_SHARED = 4,
+    TK_GEMM_GU = 5, TK_GEMM_DN = 6, TK_FUSED = 7
+};
 
 bool gemm_enabled();
 hipError_t launch_gemm_gateup(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);
 hipError_t launch_gemm_down(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
+
+int decode_grid(int act_bf16);
+hipError_t launch_decode_fused(const Layer &L, const Work &W, const void *x, float *out, int grid, hipStream_t s);
 
 hipError_t launch_rmsnorm(const float *h, int n_tok, int n_embd, double eps, uint16_t *x, hipStream_t s);
 

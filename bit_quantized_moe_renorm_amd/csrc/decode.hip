@@ -1,0 +1,618 @@
+// decode.hip - the whole MoE block for one decode token in ONE persistent launch.
+//
+// Generation is bandwidth-bound ("ds4 深度实战...", section 5.1) and the pages
+// fuse MoE routing with the expert computation into one GPU dispatch (same
+// page, section 2.3).  Here one persistent launch walks a fixed list of work
+// items in five phases:
+//   P0 router    : logits of 4 experts per item (fp64 accumulation, one wave per
+//                  expert); the wave that completes the last expert also does
+//                  top-k and renormalisation, then publishes "route ready";
+//   P1 shared g/u: 4 rows of the shared expert's gate and up per item;
+//   P2 routed g/u: 16 rows of one selected expert's IQ2 gate and up per item,
+//                  SiLU(g)*u kept in fp32 (waits for "route ready");
+//   P3 shared dn : rows of the shared down projection (waits for P1);
+//   P4 routed dn : rows of one selected expert's Q2_K down projection, scaled
+//                  by its routing weight (waits for that expert's P2 items).
+// Items are dealt round-robin over the workgroups in phase order, and the grid
+// is sized to what the GPU holds at once, so every wait is on an item that a
+// resident workgroup took earlier and that never waits on a later one.  Each
+// wait is also bounded: if it ever expires (the GPU shared with other work),
+// the kernel poisons the output with NaN instead of hanging.
+//
+// Hand-offs avoid cache-maintenance fences (an L2 write-back or invalidate per
+// hand-off costs more than the whole block).  Data another workgroup will read
+// (logits, routing, the h vectors) is written with agent-scope stores, which
+// write through to the device's point of coherence; the producer waits for
+// its stores to complete and then bumps a counter with an agent-scope atomic.
+// Consumers poll the counter with agent-scope loads and then read the data
+// with plain loads: no workgroup touches those lines earlier in the launch and
+// caches are invalidated between launches, so no stale copy can be hit.  The
+// last workgroup to leave resets the counters for the next call.  P1 needs no
+// routing, so the 50 MB shared expert streams while the router resolves.
+// The block output (routed + shared) is added into the residual with fp32
+// atomics.
+#include "common.h"
+#include "iq2_tables.h"
+
+namespace ds4 {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ float dec_dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+__device__ __forceinline__ float dec_silu(float z) { return z / (1.0f + expf(-z)); }
+__device__ __forceinline__ float dec_group_sum(float v, int lpr) {
+    for (int off = lpr >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// counters: each in its own 256-byte slot of W.counters so that polling one
+// does not contend with updates of another
+constexpr int CSTRIDE = 64;
+constexpr int C_ROUTE = 0 * CSTRIDE, C_READY = 1 * CSTRIDE, C_SHGU = 2 * CSTRIDE, C_EXIT = 3 * CSTRIDE;
+constexpr int C_ERR = 4 * CSTRIDE;
+constexpr int C_GU = 5 * CSTRIDE;  // + slot * CSTRIDE
+constexpr int C_COUNT = 5 + MAX_TOPK;
+
+constexpr int DEC_WAVES = 4;
+constexpr int DEC_THREADS = 64 * DEC_WAVES;
+constexpr int DEC_GU_NR = 4;  // routed gate/up row slots per wave
+constexpr int DEC_DN_NR = 4;  // routed down row slots per wave
+
+struct DecPlan {
+    int n_route, n_shgu, n_rgu, n_shdn, n_rdn;
+    int rgu_per_slot, rdn_per_slot;
+    int shdn_cpr;
+    int total;
+};
+
+constexpr int SPIN_LIMIT = 1 << 20;      // polls before giving up (about a second)
+
+// Loads of data produced by other workgroups in this launch.
+__device__ __forceinline__ float ld_shared(const float *p) {
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ int ld_shared(const int *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Store that other workgroups (any XCD) can read after the hand-off.
+__device__ __forceinline__ void st_shared(float *p, float v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_shared(int *p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The workgroup's shared stores are complete; then count the item (once).
+__device__ __forceinline__ void publish_item(int *ctr) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait (one poller per workgroup, with backoff) until *ctr >= target.  Returns
+// false, and flags the error, if the bounded wait expired.
+__device__ __forceinline__ bool wait_items(int *ctr, int *err, int target, int *lds_flag) {
+    if (threadIdx.x == 0) {
+        int ok = 1, spins = 0;
+        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(8);
+            if (++spins > SPIN_LIMIT) {
+                __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = 0;
+                break;
+            }
+        }
+        *lds_flag = ok;
+    }
+    __syncthreads();
+    const bool ok = *lds_flag != 0;
+    __syncthreads();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return ok;
+}
+
+__device__ __forceinline__ uint64_t dec_key(float L, int e) {
+    uint32_t u = __float_as_uint(L);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(0xFFFF - e);
+}
+
+// ---------------------------------------------------------------- P0: router
+// Top-k + renormalised weights + per-expert lists for the single token, then
+// "route ready".  Run by the one wavefront that completed the last logit; kept
+// out of line so its fp64 exp does not raise the register budget of the rest.
+__device__ __noinline__ void dec_topk_publish(const Layer &L, const Work &W) {
+    const int lane = threadIdx.x & 63;
+    const int NE = L.n_expert, k = L.top_k;
+    uint64_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ee = lane + 64 * i;
+        key[i] = (ee < NE) ? dec_key(ld_shared(W.logits + ee), ee) : 0ull;
+    }
+    float selL[MAX_TOPK];
+    int selE[MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK; ++j) {
+        if (j >= k) break;
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            uint64_t o = __shfl_xor(best, off, 64);
+            best = o > best ? o : best;
+        }
+        const int ee = 0xFFFF - (int)(best & 0xFFFFu);
+        uint32_t u = (uint32_t)(best >> 32);
+        u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+        selE[j] = ee;
+        selL[j] = __uint_as_float(u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (lane + 64 * i == ee) key[i] = 0ull;
+    }
+    if (lane < k) {
+        const double m = (double)selL[0];
+        double z = 0.0, num = 0.0;
+        int me = 0;
+#pragma unroll
+        for (int j = 0; j < MAX_TOPK; ++j) {
+            if (j >= k) break;
+            const double ex = exp((double)selL[j] - m);
+            z += ex;
+            if (j == lane) num = ex, me = selE[j];
+        }
+        st_shared(W.idx + lane, me);
+        st_shared(W.w + lane, (float)(num / z));
+    }
+    // per-expert lists for the single token (kept for ds4moe_route's export)
+    for (int ee = lane; ee <= NE; ee += 64) {
+        int before = 0;
+#pragma unroll
+        for (int j = 0; j < MAX_TOPK; ++j)
+            if (j < k) before += selE[j] < ee;
+        W.offsets[ee] = before;
+    }
+    if (lane == 0) W.active[0] = k;
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK; ++j) {
+        if (j < k && lane == j) {
+            int rank = 0;
+#pragma unroll
+            for (int i = 0; i < MAX_TOPK; ++i)
+                if (i < k) rank += selE[i] < selE[j];
+            W.active[1 + rank] = selE[j];
+            W.list[rank] = j;
+        }
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0) __hip_atomic_fetch_add(W.counters + C_READY, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool XBF16>
+__device__ void dec_route_item(const Layer &L, const Work &W, const void *__restrict__ x, int item, int *lds_flag,
+                               const DecPlan &P) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int E = L.n_embd, NE = L.n_expert;
+    const int e = item * DEC_WAVES + wave;
+    if (e < NE) {
+        const int nb = E >> 8;  // 256 elements per wave step
+        double acc = 0.0;
+        // two halves of 8 steps: 8 router float4 and 8 x loads in flight per lane
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float4 r[8];
+            float4 xv[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int cc = 8 * h + c;
+                if (cc < nb) {
+                    const int i = 256 * cc + 4 * lane;
+                    r[c] = *reinterpret_cast<const float4 *>(L.router + (int64_t)e * E + i);
+                    if (XBF16) {
+                        const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(x) + i);
+                        xv[c] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                                            __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+                    } else {
+                        xv[c] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + i);
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                if (8 * h + c < nb) {
+                    acc = fma((double)xv[c].x, (double)r[c].x, acc);
+                    acc = fma((double)xv[c].y, (double)r[c].y, acc);
+                    acc = fma((double)xv[c].z, (double)r[c].z, acc);
+                    acc = fma((double)xv[c].w, (double)r[c].w, acc);
+                }
+            }
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) st_shared(W.logits + e, (float)(acc + (L.router_bias ? (double)L.router_bias[e] : 0.0)));
+    }
+    // count the item; the workgroup that completes the last one does top-k
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *lds_flag = __hip_atomic_fetch_add(W.counters + C_ROUTE, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int prev = *lds_flag;
+    __syncthreads();
+    if (prev == P.n_route - 1 && wave == 0) dec_topk_publish(L, W);
+}
+
+// ---------------------------------------------------------------- P1: shared gate/up
+template <bool XBF16>
+__device__ void dec_shgu_item(const Layer &L, const Work &W, const void *__restrict__ x, int item) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int E = L.n_embd, F = L.n_ff, k = L.top_k;
+    const int nch = E >> 3;  // 16-byte chunks per row
+    const int f = item * DEC_WAVES + wave;
+    if (f < F) {
+        uint4 wg[8], wu[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int ch = lane + 64 * c;
+            if (ch < nch) {
+                wg[c] = *reinterpret_cast<const uint4 *>(L.sh_gate + (int64_t)f * E + ch * 8);
+                wu[c] = *reinterpret_cast<const uint4 *>(L.sh_up + (int64_t)f * E + ch * 8);
+            } else {
+                wg[c] = wu[c] = make_uint4(0, 0, 0, 0);
+            }
+        }
+        float g = 0.0f, u = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int ch = lane + 64 * c;
+            if (ch < nch) {
+                if (XBF16) {
+                    const uint4 xv = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + ch * 8);
+                    g = dec_dot2(wg[c].x, xv.x, g), g = dec_dot2(wg[c].y, xv.y, g);
+                    g = dec_dot2(wg[c].z, xv.z, g), g = dec_dot2(wg[c].w, xv.w, g);
+                    u = dec_dot2(wu[c].x, xv.x, u), u = dec_dot2(wu[c].y, xv.y, u);
+                    u = dec_dot2(wu[c].z, xv.z, u), u = dec_dot2(wu[c].w, xv.w, u);
+                } else {
+                    const float4 *xp = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + ch * 8);
+                    const float4 a = xp[0], b = xp[1];
+                    const float xf[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                    const uint32_t gw[4] = {wg[c].x, wg[c].y, wg[c].z, wg[c].w};
+                    const uint32_t uw[4] = {wu[c].x, wu[c].y, wu[c].z, wu[c].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        g = fmaf(__uint_as_float(gw[i] << 16), xf[2 * i], g);
+                        g = fmaf(__uint_as_float(gw[i] & 0xFFFF0000u), xf[2 * i + 1], g);
+                        u = fmaf(__uint_as_float(uw[i] << 16), xf[2 * i], u);
+                        u = fmaf(__uint_as_float(uw[i] & 0xFFFF0000u), xf[2 * i + 1], u);
+                    }
+                }
+            }
+        }
+        g = wave_sum(g);
+        u = wave_sum(u);
+        if (lane == 0) st_shared(W.hbuf + (int64_t)k * F + f, dec_silu(g) * u);
+    }
+    publish_item(W.counters + C_SHGU);
+}
+
+// ---------------------------------------------------------------- P2: routed gate/up (IQ2)
+template <bool XBF16>
+struct DecX;
+template <>
+struct DecX<true> {
+    uint32_t v[32];
+    __device__ __forceinline__ void load(const void *x, int off) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + off);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 r = p[i];
+            v[4 * i] = r.x, v[4 * i + 1] = r.y, v[4 * i + 2] = r.z, v[4 * i + 3] = r.w;
+        }
+    }
+    __device__ __forceinline__ float dot8(const uint4 &Lv, int o, float s) const {
+        s = dec_dot2(Lv.x, v[o], s);
+        s = dec_dot2(Lv.y, v[o + 1], s);
+        s = dec_dot2(Lv.z, v[o + 2], s);
+        s = dec_dot2(Lv.w, v[o + 3], s);
+        return s;
+    }
+};
+template <>
+struct DecX<false> {
+    float v[64];
+    __device__ __forceinline__ void load(const void *x, int off) {
+        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float4 r = p[i];
+            v[4 * i] = r.x, v[4 * i + 1] = r.y, v[4 * i + 2] = r.z, v[4 * i + 3] = r.w;
+        }
+    }
+    __device__ __forceinline__ float dot8(const uint4 &Lv, int o, float s) const {
+        const uint32_t l[4] = {Lv.x, Lv.y, Lv.z, Lv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s = fmaf(__uint_as_float(l[i] << 16), v[2 * (o + i)], s);
+            s = fmaf(__uint_as_float(l[i] & 0xFFFF0000u), v[2 * (o + i) + 1], s);
+        }
+        return s;
+    }
+};
+
+// 64 IQ2 weights of one lane (two canonical sub-blocks) against x, before d/64.
+template <bool XBF16>
+__device__ __forceinline__ float dec_iq2_dot(const uint4 *T, uint4 q, const DecX<XBF16> &xc, int rep) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+        const uint32_t ib = sb ? q.z : q.x;   // 4 codebook indices
+        const uint32_t sw = sb ? q.w : q.y;   // signs (7 x 4) | ls << 28
+        float s = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint4 Lv = iq2_group_levels(T, (ib >> (8 * g)) & 0xFFu, (sw >> (7 * g)) & 0x7Fu, rep);
+            s = xc.dot8(Lv, 16 * sb + 4 * g, s);
+        }
+        acc = fmaf((float)(2u * (sw >> 28) + 1u), s, acc);
+    }
+    return acc;
+}
+
+template <bool XBF16>
+__device__ void dec_rgu_item(const Layer &L, const Work &W, const void *__restrict__ x, const uint4 *T, int item,
+                             const DecPlan &P, int *lds_flag) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int E = L.n_embd, F = L.n_ff;
+    const int lpr = E >> 6, rpw = 64 / lpr;
+    const int c = lane & (lpr - 1);
+    const int j = item / P.rgu_per_slot, tile = item - j * P.rgu_per_slot;
+    const int rows_per_wave = DEC_GU_NR * rpw;
+    const int f0 = (tile * DEC_WAVES + wave) * rows_per_wave + lane / lpr;
+    DecX<XBF16> xc;
+    xc.load(x, 64 * c);
+    if (!wait_items(W.counters + C_READY, W.counters + C_ERR, 1, lds_flag)) return;
+    const int e = ld_shared(W.idx + j);
+    uint4 qg[DEC_GU_NR], qu[DEC_GU_NR];
+    float dg[DEC_GU_NR], du[DEC_GU_NR];
+#pragma unroll
+    for (int r = 0; r < DEC_GU_NR; ++r) {
+        const int f = f0 + r * rpw;
+        if (f < F) {
+            const int64_t rb = ((int64_t)e * F + f) * L.nbe;
+            qg[r] = *reinterpret_cast<const uint4 *>(L.iq2_qs[0] + rb * 64 + c * 16);
+            qu[r] = *reinterpret_cast<const uint4 *>(L.iq2_qs[1] + rb * 64 + c * 16);
+            dg[r] = half_to_f32(L.iq2_d[0][rb + (c >> 2)]);
+            du[r] = half_to_f32(L.iq2_d[1][rb + (c >> 2)]);
+        } else {
+            qg[r] = qu[r] = make_uint4(0, 0, 0, 0);
+            dg[r] = du[r] = 0.0f;
+        }
+    }
+    const int rep = lane & (IQ2_REPL - 1);
+#pragma unroll
+    for (int r = 0; r < DEC_GU_NR; ++r) {
+        const int f = f0 + r * rpw;
+        float g = dec_iq2_dot<XBF16>(T, qg[r], xc, rep) * dg[r];
+        float u = dec_iq2_dot<XBF16>(T, qu[r], xc, rep) * du[r];
+        g = dec_group_sum(g, lpr) * 0.015625f;
+        u = dec_group_sum(u, lpr) * 0.015625f;
+        if (c == 0 && f < F) st_shared(W.hbuf + (int64_t)j * F + f, dec_silu(g) * u);
+    }
+    publish_item(W.counters + C_GU + j * CSTRIDE);
+}
+
+// ---------------------------------------------------------------- P3: shared down
+// CPR = 16-byte chunks per lane per row (F / 512, at least 1); 16 chunk loads in
+// flight per wave, i.e. 16 / CPR rows per wave.
+template <int CPR>
+__device__ void dec_shdn_item(const Layer &L, const Work &W, float *__restrict__ out, int item, const DecPlan &P,
+                              int *lds_flag) {
+    constexpr int RPW = 16 / CPR;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int E = L.n_embd, F = L.n_ff, k = L.top_k;
+    const int nch = F >> 3;
+    const int r0 = (item * DEC_WAVES + wave) * RPW;
+    // the weights do not depend on the gate/up phase: issue them first
+    uint4 wv[RPW][CPR];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+        for (int c = 0; c < CPR; ++c) {
+            const int row = r0 + rr, ch = lane + 64 * c;
+            wv[rr][c] = (row < E && ch < nch) ? *reinterpret_cast<const uint4 *>(L.sh_down + (int64_t)row * F + ch * 8)
+                                              : make_uint4(0, 0, 0, 0);
+        }
+    if (!wait_items(W.counters + C_SHGU, W.counters + C_ERR, P.n_shgu, lds_flag)) return;
+    const float *hs = W.hbuf + (int64_t)k * F;
+    float hv[CPR][8];
+#pragma unroll
+    for (int c = 0; c < CPR; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nch) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) hv[c][i] = ld_shared(hs + ch * 8 + i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) hv[c][i] = 0.0f;
+        }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+        float y = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPR; ++c) {
+            const uint32_t a[4] = {wv[rr][c].x, wv[rr][c].y, wv[rr][c].z, wv[rr][c].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                y = fmaf(__uint_as_float(a[i] << 16), hv[c][2 * i], y);
+                y = fmaf(__uint_as_float(a[i] & 0xFFFF0000u), hv[c][2 * i + 1], y);
+            }
+        }
+        y = wave_sum(y);
+        const int row = r0 + rr;
+        if (lane == 0 && row < E) atomicAdd(out + row, y);
+    }
+}
+
+// ---------------------------------------------------------------- P4: routed down (Q2_K)
+__device__ __forceinline__ float dec_q2k_dot(uint4 qs, uint32_t sc, uint32_t dd, const float *hv, const float *hsum) {
+    const uint32_t Q[4] = {qs.x, qs.y, qs.z, qs.w};
+    float A = 0.0f, B = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t tq = (Q[s] >> (2 * u)) & 0x03030303u;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) dot = fmaf((float)((tq >> (8 * b)) & 0xFFu), hv[16 * s + 4 * b + u], dot);
+        }
+        const uint32_t scb = (sc >> (8 * s)) & 0xFFu;
+        A = fmaf((float)(scb & 15u), dot, A);
+        B = fmaf((float)(scb >> 4), hsum[s], B);
+    }
+    return half_to_f32((uint16_t)(dd & 0xFFFFu)) * A - half_to_f32((uint16_t)(dd >> 16)) * B;
+}
+
+__device__ void dec_rdn_item(const Layer &L, const Work &W, float *__restrict__ out, int item, const DecPlan &P,
+                             int *lds_flag) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int E = L.n_embd, F = L.n_ff;
+    const int lpr = F >> 6, rpw = 64 / lpr;
+    const int c = lane & (lpr - 1);
+    const int j = item / P.rdn_per_slot, tile = item - j * P.rdn_per_slot;
+    const int rows_per_wave = DEC_DN_NR * rpw;
+    const int r0 = (tile * DEC_WAVES + wave) * rows_per_wave + lane / lpr;
+    if (!wait_items(W.counters + C_GU + j * CSTRIDE, W.counters + C_ERR, P.rgu_per_slot, lds_flag)) return;
+    const int e = ld_shared(W.idx + j);
+    const float wgt = ld_shared(W.w + j);
+    uint4 qs[DEC_DN_NR];
+    uint32_t sc[DEC_DN_NR], dd[DEC_DN_NR];
+#pragma unroll
+    for (int r = 0; r < DEC_DN_NR; ++r) {
+        const int row = r0 + r * rpw;
+        if (row < E) {
+            const int64_t rb = ((int64_t)e * E + row) * L.nbf;
+            qs[r] = *reinterpret_cast<const uint4 *>(L.q2k_qs + rb * 64 + c * 16);
+            sc[r] = *reinterpret_cast<const uint32_t *>(L.q2k_sc + rb * 16 + c * 4);
+            dd[r] = L.q2k_dd[rb + (c >> 2)];
+        } else {
+            qs[r] = make_uint4(0, 0, 0, 0);
+            sc[r] = dd[r] = 0u;
+        }
+    }
+    float hv[64], hsum[4];
+    const float *hp = W.hbuf + (int64_t)j * F + 64 * c;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) hv[i] = ld_shared(hp + i);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a += hv[16 * s + i];
+        hsum[s] = a;
+    }
+#pragma unroll
+    for (int r = 0; r < DEC_DN_NR; ++r) {
+        const int row = r0 + r * rpw;
+        float y = dec_q2k_dot(qs[r], sc[r], dd[r], hv, hsum);
+        y = dec_group_sum(y, lpr);
+        if (c == 0 && row < E) atomicAdd(out + row, wgt * y);
+    }
+}
+
+// ---------------------------------------------------------------- the persistent kernel
+template <bool XBF16>
+__global__ __launch_bounds__(DEC_THREADS, 2) void k_decode_fused(Layer L, Work W, const void *__restrict__ x,
+                                                             float *__restrict__ out, DecPlan P) {
+    __shared__ uint4 T[256 * IQ2_REPL];
+    __shared__ int lds_flag;
+    iq2_build_lut<false>(T, L.codebook, threadIdx.x, DEC_THREADS);
+    __syncthreads();
+    const int G = gridDim.x;
+    const int b0 = P.n_route, b1 = b0 + P.n_shgu, b2 = b1 + P.n_rgu, b3 = b2 + P.n_shdn;
+    for (int it = blockIdx.x; it < P.total; it += G) {
+        if (it < b0) dec_route_item<XBF16>(L, W, x, it, &lds_flag, P);
+        else if (it < b1) dec_shgu_item<XBF16>(L, W, x, it - b0);
+        else if (it < b2) dec_rgu_item<XBF16>(L, W, x, T, it - b1, P, &lds_flag);
+        else if (it < b3) {
+            switch (P.shdn_cpr) {
+                case 1: dec_shdn_item<1>(L, W, out, it - b2, P, &lds_flag); break;
+                case 2: dec_shdn_item<2>(L, W, out, it - b2, P, &lds_flag); break;
+                case 4: dec_shdn_item<4>(L, W, out, it - b2, P, &lds_flag); break;
+                default: dec_shdn_item<8>(L, W, out, it - b2, P, &lds_flag); break;
+            }
+        } else dec_rdn_item(L, W, out, it - b3, P, &lds_flag);
+    }
+    // leave; the last workgroup out resets the counters for the next call
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_s_waitcnt(0);
+        const int prev = __hip_atomic_fetch_add(W.counters + C_EXIT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == G - 1) {
+            if (__hip_atomic_load(W.counters + C_ERR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                out[0] = __builtin_nanf("");   // a bounded wait expired: make it visible
+            for (int i = 0; i < C_COUNT; ++i)
+                __hip_atomic_store(W.counters + i * CSTRIDE, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+static DecPlan make_plan(const Layer &L) {
+    DecPlan P{};
+    const int E = L.n_embd, F = L.n_ff, k = L.top_k;
+    P.n_route = (L.n_expert + DEC_WAVES - 1) / DEC_WAVES;
+    P.n_shgu = L.n_shared ? (F + DEC_WAVES - 1) / DEC_WAVES : 0;
+    const int rows_gu_item = DEC_WAVES * DEC_GU_NR * (64 / (E >> 6));
+    P.rgu_per_slot = (F + rows_gu_item - 1) / rows_gu_item;
+    P.n_rgu = k * P.rgu_per_slot;
+    P.shdn_cpr = ((F >> 3) + 63) >> 6;
+    const int rows_sd_item = DEC_WAVES * (16 / P.shdn_cpr);
+    P.n_shdn = L.n_shared ? (E + rows_sd_item - 1) / rows_sd_item : 0;
+    const int rows_dn_item = DEC_WAVES * DEC_DN_NR * (64 / (F >> 6));
+    P.rdn_per_slot = (E + rows_dn_item - 1) / rows_dn_item;
+    P.n_rdn = k * P.rdn_per_slot;
+    P.total = P.n_route + P.n_shgu + P.n_rgu + P.n_shdn + P.n_rdn;
+    return P;
+}
+
+int decode_grid(int act_bf16) {
+    int dev = 0, ncu = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    hipError_t e;
+    if (act_bf16)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&k_decode_fused<true>),
+                                                     DEC_THREADS, 0);
+    else
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&k_decode_fused<false>),
+                                                     DEC_THREADS, 0);
+    if (e != hipSuccess) return 0;
+    per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
+    return ncu * per_cu;
+}
+
+hipError_t launch_decode_fused(const Layer &L, const Work &W, const void *x, float *out, int grid, hipStream_t s) {
+    DecPlan P = make_plan(L);
+    Layer Lc = L;
+    Work Wc = W;
+    const void *xc = x;
+    float *oc = out;
+    void *args[] = {&Lc, &Wc, &xc, &oc, &P};
+    const void *fn = (L.act_dtype == 1) ? reinterpret_cast<const void *>(&k_decode_fused<true>)
+                                        : reinterpret_cast<const void *>(&k_decode_fused<false>);
+    hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(DEC_THREADS), args, 0, s);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+}  // namespace ds4

@@ -44,6 +44,7 @@ struct ds4moe {
     Layer L{};
     Work W{};
     int path = DS4MOE_PATH_AUTO;
+    int decode_grid = 0;    // workgroups of the persistent decode kernel
     bool poisoned = false;
     int device = 0;
     std::vector<void *> allocs;
@@ -150,7 +151,7 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     auto carve = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     size_t o_logits = carve(T * NE * 4), o_idx = carve(T * k * 4), o_w = carve(T * k * 4);
     size_t o_off = carve((NE + 1) * 4), o_list = carve(T * k * 4), o_act = carve((NE + 1) * 4);
-    size_t o_cnt = carve(64 * 4), o_h = carve(gemv_slots * F * 4), o_h16 = carve(slots * F * 2);
+    size_t o_cnt = carve(16 * 64 * 4), o_h = carve(gemv_slots * F * 4), o_h16 = carve(slots * F * 2);
     char *ws = (char *)A(off);
     if (err != hipSuccess) {
         delete h;
@@ -194,6 +195,11 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     L.iq2_qs[0] = gq, L.iq2_qs[1] = uq, L.iq2_d[0] = gd, L.iq2_d[1] = ud;
     L.q2k_qs = dq, L.q2k_sc = dsc, L.q2k_dd = ddd;
     L.sh_gate = sg, L.sh_up = su, L.sh_down = sd;
+    h->decode_grid = decode_grid(d->act_dtype == DS4MOE_BF16);
+    if (h->decode_grid <= 0) {
+        delete h;
+        return fail(DS4MOE_EHIP, "create: cannot size the decode grid");
+    }
     *out = h;
     g_err.clear();
     return DS4MOE_OK;
@@ -229,7 +235,7 @@ int ds4moe_route(ds4moe_t *h, const void *x, int32_t n_tok, int32_t *topk_idx, f
         return fail(DS4MOE_EINVAL, "route: NULL output");
     if (n_tok == 0) return DS4MOE_OK;
     hipStream_t s = (hipStream_t)stream;
-    int tb = h->tbegin(0, s);
+    int tb = h->tbegin(TK_ROUTE, s);
     rc = check_launch(h, launch_route(h->L, h->W, x, n_tok, s, nullptr), "route");
     h->tend(tb, s);
     if (rc) return rc;
@@ -249,25 +255,44 @@ int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *
     if (path == DS4MOE_PATH_GEMM && !gemm_available())
         return fail(DS4MOE_EUNSUPPORTED, "forward: the grouped GEMM path is not available in this build");
     hipStream_t s = (hipStream_t)stream;
-    int tb = h->tbegin(0, s);
+    if (path == DS4MOE_PATH_GEMV && n_tok == 1) {
+        // the whole block for one token in one persistent launch
+        int tf = h->tbegin(TK_FUSED, s);
+        rc = check_launch(h, launch_decode_fused(h->L, h->W, x, out, h->decode_grid, s), "fused decode");
+        h->tend(tf, s);
+        return rc;
+    }
+    int tb = h->tbegin(TK_ROUTE, s);
     rc = check_launch(h, launch_route(h->L, h->W, x, n_tok, s, nullptr), "route");
     h->tend(tb, s);
     if (rc) return rc;
     if (path == DS4MOE_PATH_GEMV) {
-        tb = h->tbegin(1, s);
-        rc = check_launch(h, launch_gemv_gateup(h->L, h->W, x, n_tok, s), "gemv gate/up");
+        if (h->L.n_shared) {
+            tb = h->tbegin(TK_GU_SHARED, s);
+            rc = check_launch(h, launch_gemv_gateup_shared(h->L, h->W, x, n_tok, s), "gemv shared gate/up");
+            h->tend(tb, s);
+            if (rc) return rc;
+        }
+        tb = h->tbegin(TK_GU_ROUTED, s);
+        rc = check_launch(h, launch_gemv_gateup_routed(h->L, h->W, x, n_tok, s), "gemv routed gate/up");
         h->tend(tb, s);
         if (rc) return rc;
-        tb = h->tbegin(2, s);
-        rc = check_launch(h, launch_gemv_down(h->L, h->W, n_tok, out, s), "gemv down");
+        tb = h->tbegin(TK_DN_ROUTED, s);
+        rc = check_launch(h, launch_gemv_down_routed(h->L, h->W, n_tok, out, s), "gemv routed down");
         h->tend(tb, s);
+        if (rc) return rc;
+        if (h->L.n_shared) {
+            tb = h->tbegin(TK_DN_SHARED, s);
+            rc = check_launch(h, launch_gemv_down_shared(h->L, h->W, n_tok, out, s), "gemv shared down");
+            h->tend(tb, s);
+        }
         return rc;
     }
-    tb = h->tbegin(1, s);
+    tb = h->tbegin(TK_GEMM_GU, s);
     rc = check_launch(h, launch_gemm_gateup(h->L, h->W, x, n_tok, s), "gemm gate/up");
     h->tend(tb, s);
     if (rc) return rc;
-    tb = h->tbegin(2, s);
+    tb = h->tbegin(TK_GEMM_DN, s);
     rc = check_launch(h, launch_gemm_down(h->L, h->W, n_tok, out, s), "gemm down");
     h->tend(tb, s);
     return rc;

@@ -78,24 +78,22 @@ struct XChunk<false> {
     }
 };
 
-// Dot of one lane's 64 IQ2 weights (2 sub-blocks, repacked dwords q) with x,
-// before the fp16 d and the 1/64 of the level and scale encodings.
+// Dot of one lane's 64 IQ2 weights (2 canonical sub-blocks) with x, before the
+// fp16 d and the 1/64 of the level and scale encodings.
 template <bool XBF16>
-__device__ __forceinline__ float iq2_chunk_dot(const uint2 *T, uint4 q, const XChunk<XBF16> &xc) {
-    const uint32_t D[4] = {q.x, q.y, q.z, q.w};
+__device__ __forceinline__ float iq2_chunk_dot(const uint4 *T, uint4 q, const XChunk<XBF16> &xc, int rep) {
     float acc = 0.0f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-        const uint32_t D0 = D[2 * sb], D1 = D[2 * sb + 1];
-        const Iq2Pair p0 = iq2_lookup(T, D0);
-        const Iq2Pair p1 = iq2_lookup(T, D1);
-        const int o = 16 * sb;
+        const uint32_t ib = sb ? q.z : q.x;
+        const uint32_t sw = sb ? q.w : q.y;
         float s = 0.0f;
-        s = xc.dot8(p0.a0.x, p0.a0.y, p0.a1.x, p0.a1.y, o, s);
-        s = xc.dot8(p0.b0.x, p0.b0.y, p0.b1.x, p0.b1.y, o + 4, s);
-        s = xc.dot8(p1.a0.x, p1.a0.y, p1.a1.x, p1.a1.y, o + 8, s);
-        s = xc.dot8(p1.b0.x, p1.b0.y, p1.b1.x, p1.b1.y, o + 12, s);
-        acc = fmaf((float)(2u * iq2_ls(D0, D1) + 1u), s, acc);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint4 Lv = iq2_group_levels(T, (ib >> (8 * g)) & 0xFFu, (sw >> (7 * g)) & 0x7Fu, rep);
+            s = xc.dot8(Lv.x, Lv.y, Lv.z, Lv.w, 16 * sb + 4 * g, s);
+        }
+        acc = fmaf((float)(2u * (sw >> 28) + 1u), s, acc);
     }
     return acc;
 }
@@ -106,8 +104,7 @@ constexpr int GU_NR = 4;
 // Routed gate/up: blockIdx.y = active expert slot, blockIdx.x = tile of rows.
 template <bool XBF16>
 __global__ __launch_bounds__(512) void k_gemv_gateup_routed(Layer L, Work W, const void *__restrict__ x) {
-    __shared__ uint2 T[IQ2_TABLE_ENTRIES];
-    __shared__ uint16_t cb[256];
+    __shared__ uint4 T[256 * IQ2_REPL];
     const int U = W.active[0];
     const int u = blockIdx.y;
     if (u >= U) return;
@@ -148,10 +145,9 @@ __global__ __launch_bounds__(512) void k_gemv_gateup_routed(Layer L, Work W, con
             xc[i].load(x, (int64_t)(q / k) * E + 64 * c);
         }
     }
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) cb[i] = L.codebook[i];
+    iq2_build_lut<false>(T, L.codebook, threadIdx.x, blockDim.x);
     __syncthreads();
-    iq2_build_tables<false>(T, cb, threadIdx.x, blockDim.x);
-    __syncthreads();
+    const int rep = lane & (IQ2_REPL - 1);
 
 #pragma unroll
     for (int r = 0; r < GU_NR; ++r) {
@@ -159,8 +155,8 @@ __global__ __launch_bounds__(512) void k_gemv_gateup_routed(Layer L, Work W, con
 #pragma unroll
         for (int i = 0; i < GEMV_MAX_TOK; ++i) {
             if (i < m) {
-                float g = iq2_chunk_dot<XBF16>(T, qg[r], xc[i]) * dg[r];
-                float uu = iq2_chunk_dot<XBF16>(T, qu[r], xc[i]) * du[r];
+                float g = iq2_chunk_dot<XBF16>(T, qg[r], xc[i], rep) * dg[r];
+                float uu = iq2_chunk_dot<XBF16>(T, qu[r], xc[i], rep) * du[r];
                 g = group_sum(g, lpr) * 0.015625f;
                 uu = group_sum(uu, lpr) * 0.015625f;
                 if (c == 0 && f < F) W.hbuf[(int64_t)slot[i] * F + f] = silu(g) * uu;
@@ -381,41 +377,45 @@ __global__ __launch_bounds__(256) void k_gemv_down_shared(Layer L, Work W, int n
     }
 }
 
-hipError_t launch_gemv_gateup(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s) {
+hipError_t launch_gemv_gateup_routed(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s) {
     const int slots = min(n_tok * L.top_k, L.n_expert);
     const int rpw = 64 / (L.n_embd >> 6);
     const int rows_wg = GU_WAVES * GU_NR * rpw;
     dim3 grid((L.n_ff + rows_wg - 1) / rows_wg, slots);
-    const bool bf = L.act_dtype == 1;
-    if (bf)
+    if (L.act_dtype == 1)
         hipLaunchKernelGGL(k_gemv_gateup_routed<true>, grid, dim3(64 * GU_WAVES), 0, s, L, W, x);
     else
         hipLaunchKernelGGL(k_gemv_gateup_routed<false>, grid, dim3(64 * GU_WAVES), 0, s, L, W, x);
-    if (L.n_shared) {
-        const int nr = (n_tok == 1) ? 2 : 1;
-        dim3 g2((L.n_ff + 4 * nr - 1) / (4 * nr));
-        if (n_tok == 1) {
-            if (bf) hipLaunchKernelGGL((k_gemv_gateup_shared<true, 1>), g2, dim3(256), 0, s, L, W, x, n_tok);
-            else hipLaunchKernelGGL((k_gemv_gateup_shared<false, 1>), g2, dim3(256), 0, s, L, W, x, n_tok);
-        } else {
-            if (bf) hipLaunchKernelGGL((k_gemv_gateup_shared<true, GEMV_MAX_TOK>), g2, dim3(256), 0, s, L, W, x, n_tok);
-            else hipLaunchKernelGGL((k_gemv_gateup_shared<false, GEMV_MAX_TOK>), g2, dim3(256), 0, s, L, W, x, n_tok);
-        }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_gateup_shared(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s) {
+    const bool bf = L.act_dtype == 1;
+    const int nr = (n_tok == 1) ? 2 : 1;
+    dim3 g2((L.n_ff + 4 * nr - 1) / (4 * nr));
+    if (n_tok == 1) {
+        if (bf) hipLaunchKernelGGL((k_gemv_gateup_shared<true, 1>), g2, dim3(256), 0, s, L, W, x, n_tok);
+        else hipLaunchKernelGGL((k_gemv_gateup_shared<false, 1>), g2, dim3(256), 0, s, L, W, x, n_tok);
+    } else {
+        if (bf) hipLaunchKernelGGL((k_gemv_gateup_shared<true, GEMV_MAX_TOK>), g2, dim3(256), 0, s, L, W, x, n_tok);
+        else hipLaunchKernelGGL((k_gemv_gateup_shared<false, GEMV_MAX_TOK>), g2, dim3(256), 0, s, L, W, x, n_tok);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_down(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s) {
+hipError_t launch_gemv_down_routed(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s) {
     const int slots = min(n_tok * L.top_k, L.n_expert);
     const int rpw = 64 / (L.n_ff >> 6);
     const int rows_wg = DN_WAVES * DN_NR * rpw;
     dim3 grid((L.n_embd + rows_wg - 1) / rows_wg, slots);
     hipLaunchKernelGGL(k_gemv_down_routed, grid, dim3(64 * DN_WAVES), 0, s, L, W, out);
-    if (L.n_shared) {
-        dim3 g2((L.n_embd + 7) / 8);
-        if (n_tok == 1) hipLaunchKernelGGL(k_gemv_down_shared<1>, g2, dim3(256), 0, s, L, W, n_tok, out);
-        else hipLaunchKernelGGL(k_gemv_down_shared<GEMV_MAX_TOK>, g2, dim3(256), 0, s, L, W, n_tok, out);
-    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_down_shared(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s) {
+    dim3 g2((L.n_embd + 7) / 8);
+    if (n_tok == 1) hipLaunchKernelGGL(k_gemv_down_shared<1>, g2, dim3(256), 0, s, L, W, n_tok, out);
+    else hipLaunchKernelGGL(k_gemv_down_shared<GEMV_MAX_TOK>, g2, dim3(256), 0, s, L, W, n_tok, out);
     return hipGetLastError();
 }
 

@@ -1,102 +1,67 @@
-// iq2_tables.h - LDS lookup tables for the IQ2-style codebook blocks.
+// iq2_tables.h - decoding IQ2-style codebook groups on gfx950.
 //
-// The codebook format (2-bit codebook weights, "Redis 作者出手！ds4...", section 2.3:
-// block_iq2_xxs, 66 bytes per 256 weights) stores per group of 8 weights one
-// codebook index and 7 sign bits; the 8th sign follows from parity.  In the
-// library's repacked layout each group is one 16-bit field (see common.h).
+// The codebook format ("Redis 作者出手！ds4...", section 2.3: block_iq2_xxs, 66
+// bytes per 256 weights) stores per group of 8 weights one codebook index and
+// 7 sign bits (the 8th sign makes the count of negatives even), and per 32
+// weights a 4-bit scale.  The library keeps each sub-block's canonical 8 bytes
+// (4 index bytes, then the sign/scale word) in its qs plane.
 //
-// Two 4096-entry tables, built per workgroup in LDS from the 256-entry codebook,
-// turn a field into 8 signed levels +-(2c+1) without any per-weight bit work:
-//   T[0    + (field & 0xFFF)]        -> levels of weights 0..3 (4 x 16 bit)
-//   T[4096 + ((field >> 3) & 0xFFF)] -> levels of weights 4..7
-// Each entry is a uint2 holding two packed pairs (w0|w1<<16, w2|w3<<16).  The
-// levels are bf16 (decode dot products) or fp16 (MFMA operands scaled by
-// packed fp16 multiplies); both are exact for the small odd integers 1..7.
+// The 256-entry codebook is expanded once per workgroup into an LDS table of
+// unsigned levels (2c+1) for all 8 coordinates (16 bytes per entry, packed
+// pairs).  The table is replicated 8 times with the replicas interleaved at
+// 16-byte granularity, and lane l reads replica l & 7: the 8 lanes that share a
+// ds_read_b128 cycle then always hit 8 different bank quads, whatever indices
+// they look up, so lookups never conflict.  Signs are applied with XOR masks
+// built from the sign bits by rotates (v_alignbit) and one v_bitop3 each.
 #pragma once
 #include "common.h"
 
 namespace ds4 {
 
-constexpr int IQ2_TABLE_ENTRIES = 8192;  // 64 KB of uint2
+constexpr int IQ2_REPL = 8;
+constexpr int IQ2_LUT_BYTES = 256 * IQ2_REPL * 16;  // 32 KB
 
-template <bool FP16>
-__device__ __forceinline__ uint32_t iq2_level_bits(uint32_t c, uint32_t neg) {
-    // +-(2c+1) for c in 0..3
-    uint32_t v;
-    if (FP16)
-        v = (c == 0) ? 0x3C00u : (c == 1) ? 0x4200u : (c == 2) ? 0x4500u : 0x4700u;
-    else
-        v = (c == 0) ? 0x3F80u : (c == 1) ? 0x4040u : (c == 2) ? 0x40A0u : 0x40E0u;
-    return v | (neg << 15);
+// Unsigned level (2c+1) bit patterns, c in 0..3.
+__device__ __forceinline__ uint32_t iq2_level_bf16(uint32_t c) {
+    return (c == 0) ? 0x3F80u : (c == 1) ? 0x4040u : (c == 2) ? 0x40A0u : 0x40E0u;
+}
+__device__ __forceinline__ uint32_t iq2_level_f16(uint32_t c) {
+    return (c == 0) ? 0x3C00u : (c == 1) ? 0x4200u : (c == 2) ? 0x4500u : 0x4700u;
 }
 
-// Fill T[0..8191] from the codebook cb[256] (already in LDS); caller syncs after.
+// Build the replicated table (entry e, replica r at uint4 index e*8 + r): each
+// thread loads whole codebook entries once and writes their 8 replicas.
 template <bool FP16>
-__device__ __forceinline__ void iq2_build_tables(uint2 *T, const uint16_t *cb, int tid, int nthreads) {
-    for (int i = tid; i < IQ2_TABLE_ENTRIES; i += nthreads) {
-        uint32_t s[4], codes, idx;
-        if (i < 4096) {
-            uint32_t P = (i >> 3) & 1;
-            idx = (i >> 4) & 0xFF;
-            s[0] = i & 1;
-            s[1] = (i >> 1) & 1;
-            s[2] = (i >> 2) & 1;
-            s[3] = P ^ s[0] ^ s[1] ^ s[2];
-            codes = cb[idx] & 0xFF;
-        } else {
-            int j = i - 4096;
-            uint32_t P = j & 1;
-            idx = (j >> 1) & 0xFF;
-            s[0] = (j >> 9) & 1;
-            s[1] = (j >> 10) & 1;
-            s[2] = (j >> 11) & 1;
-            s[3] = P ^ s[0] ^ s[1] ^ s[2];
-            codes = cb[idx] >> 8;
-        }
-        uint32_t v0 = iq2_level_bits<FP16>(codes & 3, s[0]);
-        uint32_t v1 = iq2_level_bits<FP16>((codes >> 2) & 3, s[1]);
-        uint32_t v2 = iq2_level_bits<FP16>((codes >> 4) & 3, s[2]);
-        uint32_t v3 = iq2_level_bits<FP16>((codes >> 6) & 3, s[3]);
-        T[i] = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+__device__ __forceinline__ void iq2_build_lut(uint4 *T, const uint16_t *__restrict__ codebook, int tid, int nthreads) {
+    for (int e = tid; e < 256; e += nthreads) {
+        const uint32_t c = codebook[e];
+        uint32_t v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = FP16 ? iq2_level_f16((c >> (2 * k)) & 3u) : iq2_level_bf16((c >> (2 * k)) & 3u);
+        const uint4 q = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+#pragma unroll
+        for (int r = 0; r < IQ2_REPL; ++r) T[e * IQ2_REPL + r] = q;
     }
 }
 
-// Levels of the two groups packed in one dword D (group fields D & 0xFFFF, D >> 16).
-// Byte offsets are formed directly from the field bits (entry size 8 bytes).
-struct Iq2Pair {
-    uint2 a0, a1;  // low group: weights 0..3, 4..7
-    uint2 b0, b1;  // high group
-};
-
-__device__ __forceinline__ Iq2Pair iq2_lookup(const uint2 *T, uint32_t D) {
-    const char *Tb = reinterpret_cast<const char *>(T);
-    Iq2Pair p;
-    p.a0 = *reinterpret_cast<const uint2 *>(Tb + ((D << 3) & 0x7FF8u));
-    p.a1 = *reinterpret_cast<const uint2 *>(Tb + 32768 + (D & 0x7FF8u));
-    p.b0 = *reinterpret_cast<const uint2 *>(Tb + ((D >> 13) & 0x7FF8u));
-    p.b1 = *reinterpret_cast<const uint2 *>(Tb + 32768 + ((D >> 16) & 0x7FF8u));
-    return p;
-}
-
-// Sub-block scale ls from the sub-block's two dwords (bit 15 of each group field).
-__device__ __forceinline__ uint32_t iq2_ls(uint32_t D0, uint32_t D1) {
-    return ((D0 >> 15) & 1u) | ((D0 >> 30) & 2u) | ((D1 >> 13) & 4u) | ((D1 >> 28) & 8u);
-}
-
-// Repack one canonical sub-block (4 index bytes + sign/scale word) into the
-// four 16-bit group fields, returned as two dwords (groups 0|1, 2|3).
-__host__ __device__ inline void iq2_encode_subblock(const uint8_t idx[4], uint32_t word, uint32_t &D0,
-                                                    uint32_t &D1) {
-    uint32_t ls = word >> 28;
-    uint32_t f[4];
-    for (int g = 0; g < 4; ++g) {
-        uint32_t s7 = (word >> (7 * g)) & 0x7Fu;
-        uint32_t P = (s7 ^ (s7 >> 1) ^ (s7 >> 2) ^ (s7 >> 3)) & 1u;
-        f[g] = (s7 & 7u) | (P << 3) | ((uint32_t)idx[g] << 4) | (((s7 >> 4) & 7u) << 12) |
-               (((ls >> g) & 1u) << 15);
-    }
-    D0 = f[0] | (f[1] << 16);
-    D1 = f[2] | (f[3] << 16);
+// Signed levels of one group: idx = codebook index, s7 = stored sign bits of
+// weights 0..6.  Returns 4 dwords of packed pairs (w0|w1, w2|w3, w4|w5, w6|w7).
+__device__ __forceinline__ uint4 iq2_group_levels(const uint4 *T, uint32_t idx, uint32_t s7, int rep) {
+    uint4 L = T[idx * IQ2_REPL + rep];
+    // 8th sign: the group holds an even number of negatives (bit 7 = parity;
+    // bits 8-9 receive the rest of the count and are never selected below)
+    const uint32_t s8 = s7 | (__builtin_popcount(s7) << 7);
+    // copy A of the signs at bits 0-9, copy B at bits 15-24
+    const uint32_t S = s8 | (s8 << 15);
+    // dword j holds weights (2j, 2j+1): their sign bits go to bit 15 (from copy A,
+    // bit 2j) and bit 31 (from copy B, bit 2j+1).  Rotating S left by 15-2j (a
+    // right rotate by 17+2j with v_alignbit) puts both there at once.
+    const uint32_t M = 0x80008000u;
+    L.x ^= __builtin_amdgcn_alignbit(S, S, 17) & M;
+    L.y ^= __builtin_amdgcn_alignbit(S, S, 19) & M;
+    L.z ^= __builtin_amdgcn_alignbit(S, S, 21) & M;
+    L.w ^= __builtin_amdgcn_alignbit(S, S, 23) & M;
+    return L;
 }
 
 }  // namespace ds4

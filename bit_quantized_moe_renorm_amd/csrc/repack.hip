@@ -5,7 +5,8 @@
 
 namespace ds4 {
 
-// One thread per 32-weight sub-block: canonical 66-byte blocks -> qs plane + d plane.
+// One thread per 32-weight sub-block: canonical 66-byte blocks -> qs plane (the
+// sub-block's 8 canonical bytes, 8-byte aligned) + d plane.
 __global__ void k_repack_iq2(const uint8_t *__restrict__ canon, int64_t n_sub, uint8_t *__restrict__ qs,
                              uint16_t *__restrict__ dplane) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -13,14 +14,11 @@ __global__ void k_repack_iq2(const uint8_t *__restrict__ canon, int64_t n_sub, u
     int64_t b = i >> 3;
     int s = (int)(i & 7);
     const uint8_t *blk = canon + b * 66;
-    const uint8_t *sub = blk + 2 + 8 * s;
-    uint8_t idx[4] = {sub[0], sub[1], sub[2], sub[3]};
-    uint32_t word = (uint32_t)sub[4] | ((uint32_t)sub[5] << 8) | ((uint32_t)sub[6] << 16) |
-                    ((uint32_t)sub[7] << 24);
-    uint32_t D0, D1;
-    iq2_encode_subblock(idx, word, D0, D1);
+    const uint16_t *sub = reinterpret_cast<const uint16_t *>(blk + 2 + 8 * s);  // 2-byte aligned
+    uint32_t D0 = (uint32_t)sub[0] | ((uint32_t)sub[1] << 16);
+    uint32_t D1 = (uint32_t)sub[2] | ((uint32_t)sub[3] << 16);
     *reinterpret_cast<uint2 *>(qs + b * 64 + s * 8) = make_uint2(D0, D1);
-    if (s == 0) dplane[b] = (uint16_t)(blk[0] | (blk[1] << 8));
+    if (s == 0) dplane[b] = *reinterpret_cast<const uint16_t *>(blk);
 }
 
 // One thread per 84-byte block (4-byte aligned): split into qs / scales / d|dmin planes.
@@ -53,16 +51,13 @@ hipError_t launch_repack_q2k(const uint8_t *canon, int64_t n_blocks, uint8_t *qs
     return hipGetLastError();
 }
 
-// Debug decode of one IQ2 matrix [F][E] to fp32 through the same LDS tables the
-// GEMV kernels use.  One thread per group of 8 weights.
+// Debug decode of one IQ2 matrix [F][E] to fp32 through the same LDS table and
+// sign logic the GEMV kernels use.  One thread per group of 8 weights.
 __global__ __launch_bounds__(256) void k_dequant_iq2(const uint8_t *__restrict__ qs, const uint16_t *__restrict__ dpl,
                                                      const uint16_t *__restrict__ codebook, int64_t n_groups,
                                                      float *__restrict__ dst) {
-    __shared__ uint2 T[IQ2_TABLE_ENTRIES];
-    __shared__ uint16_t cb[256];
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) cb[i] = codebook[i];
-    __syncthreads();
-    iq2_build_tables<false>(T, cb, threadIdx.x, blockDim.x);
+    __shared__ uint4 T[256 * IQ2_REPL];
+    iq2_build_lut<false>(T, codebook, threadIdx.x, blockDim.x);
     __syncthreads();
     int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gi >= n_groups) return;
@@ -70,14 +65,10 @@ __global__ __launch_bounds__(256) void k_dequant_iq2(const uint8_t *__restrict__
     int sub = (int)((gi >> 2) & 7);
     int g = (int)(gi & 3);
     const uint32_t *sw = reinterpret_cast<const uint32_t *>(qs + blk * 64 + sub * 8);
-    uint32_t D0 = sw[0], D1 = sw[1];
-    uint32_t ls = iq2_ls(D0, D1);
-    uint32_t D = (g < 2) ? D0 : D1;
-    Iq2Pair p = iq2_lookup(T, D);
-    uint2 lo = (g & 1) ? p.b0 : p.a0;
-    uint2 hi = (g & 1) ? p.b1 : p.a1;
-    float scale = half_to_f32(dpl[blk]) * (float)(2 * ls + 1);
-    uint32_t lv[4] = {lo.x, lo.y, hi.x, hi.y};
+    const uint32_t ib = sw[0], signs = sw[1];
+    uint4 L = iq2_group_levels(T, (ib >> (8 * g)) & 0xFFu, (signs >> (7 * g)) & 0x7Fu, threadIdx.x & (IQ2_REPL - 1));
+    float scale = half_to_f32(dpl[blk]) * (float)(2u * (signs >> 28) + 1u);
+    uint32_t lv[4] = {L.x, L.y, L.z, L.w};
     float *o = dst + gi * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -166,9 +166,10 @@ int ds4moe_rmsnorm(const float *h, int32_t n_tok, int32_t n_embd, double eps, ui
  * Per-kernel timing for benchmarks.  When enabled, ds4moe_forward records HIP
  * events around each kernel it launches on the caller's stream; read back the
  * accumulated milliseconds and launch counts (after synchronising the stream)
- * with ds4moe_timing_read.  kinds: 0 route, 1 gate/up, 2 down, 3 fused decode,
- * 4 bucket.  ms and counts have room for 8 entries each.  Enabling resets
- * the counters.
+ * with ds4moe_timing_read.  kinds: 0 route (logits, top-k, lists), 1 routed
+ * gate/up GEMV, 2 shared gate/up GEMV, 3 routed down GEMV, 4 shared down GEMV,
+ * 5 grouped gate/up GEMM, 6 grouped down GEMM, 7 fused decode kernel.  ms and
+ * counts have room for 8 entries each.  Enabling resets the counters.
  */
 int ds4moe_timing_enable(ds4moe_t *h, int32_t enable);
 int ds4moe_timing_read(ds4moe_t *h, double *ms, int64_t *counts);

@@ -123,6 +123,40 @@ def test_forward_ds4_gemv(n):
     assert err <= REL_TOL and err <= GEMV_TOL
 
 
+def test_forward_tiny_fused_decode():
+    """n_tok = 1 takes the single persistent launch."""
+    lay = host_layer("tiny")
+    x = synth.activations(0, 4, 256, bf16=False)
+    dev = device_layer("tiny")
+    for t in range(4):
+        got = _forward(dev, x[t:t + 1], m.PATH_AUTO)
+        ref, _, _ = oracle.forward(lay, x[t:t + 1])
+        err = rel_err(got, ref)
+        log(f"[gpu] tiny fused token {t} rel err {err:.3e}")
+        assert err <= GEMV_TOL
+
+
+def test_forward_ds4_fused_decode_many_tokens():
+    """Consecutive single-token calls (the counters reset between launches)."""
+    lay = host_layer("ds4")
+    dev = device_layer("ds4")
+    x = synth.activations(1, 24, 4096, start=100)
+    got = np.stack([_forward(dev, x[t:t + 1], m.PATH_AUTO)[0] for t in range(24)])
+    ref, _, _ = oracle.forward(lay, x)
+    err = rel_err(got, ref)
+    log(f"[gpu] ds4 fused 24 tokens rel err {err:.3e}")
+    assert err <= REL_TOL and err <= GEMV_TOL
+
+
+def test_forward_fused_zipf_bias():
+    lay = host_layer("ds4_zipf")
+    dev = device_layer("ds4_zipf")
+    x = synth.activations(1, 4, 4096, start=7)
+    got = np.stack([_forward(dev, x[t:t + 1], m.PATH_AUTO)[0] for t in range(4)])
+    ref, _, _ = oracle.forward(lay, x)
+    assert rel_err(got, ref) <= GEMV_TOL
+
+
 def test_forward_accumulates_into_residual():
     lay = host_layer("ds4")
     x = synth.activations(1, 1, 4096, start=3)
@@ -130,6 +164,8 @@ def test_forward_accumulates_into_residual():
     got = _forward(device_layer("ds4"), x, m.PATH_GEMV, out0=r)
     ref, _, _ = oracle.forward(lay, x)
     assert rel_err(got - r, ref) <= GEMV_TOL
+    got2 = _forward(device_layer("ds4"), np.concatenate([x, x]), m.PATH_GEMV, out0=np.concatenate([r, r]))
+    assert rel_err(got2[1] - r[0], ref[0]) <= GEMV_TOL
 
 
 def test_forward_gemv_rejects_large_batches():
