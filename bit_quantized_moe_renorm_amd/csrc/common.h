@@ -47,7 +47,7 @@ struct Work {
     int32_t *offsets;     // [NE+1]
     int32_t *list;        // [max_tokens*k] entries t*k + j, grouped by expert, ascending t
     int32_t *active;      // [NE+1]: active[0] = U, active[1..U] = experts with tokens, ascending
-    int32_t *counters;    // [16 * 64] completion counters, one per 256-byte slot (self-resetting)
+    int32_t *counters;    // counter slots of 256 bytes: slot 0 router tail, then the decode phases
     float *hbuf;          // [max_tokens*(k+1)][F] fp32 activations between gate/up and down
     uint16_t *hbuf16;     // [max_tokens*(k+1)][F] fp16 activations (GEMM path)
     float *wsum;          // unused padding slot
@@ -97,7 +97,8 @@ hipError_t launch_gemm_gateup(const Layer &L, const Work &W, const void *x, int 
 hipError_t launch_gemm_down(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
 
 int decode_grid(int act_bf16);
-hipError_t launch_decode_fused(const Layer &L, const Work &W, const void *x, float *out, int grid, hipStream_t s);
+hipError_t launch_decode_fused(const Layer &L, const Work &W, const void *x, float *out, int grid,
+                               unsigned long long ep, hipStream_t s);
 
 hipError_t launch_rmsnorm(const float *h, int n_tok, int n_embd, double eps, uint16_t *x, hipStream_t s);
 

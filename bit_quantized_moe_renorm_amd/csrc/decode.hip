@@ -47,13 +47,15 @@ __device__ __forceinline__ float dec_group_sum(float v, int lpr) {
     return v;
 }
 
-// counters: each in its own 256-byte slot of W.counters so that polling one
-// does not contend with updates of another
-constexpr int CSTRIDE = 64;
-constexpr int C_ROUTE = 0 * CSTRIDE, C_READY = 1 * CSTRIDE, C_SHGU = 2 * CSTRIDE, C_EXIT = 3 * CSTRIDE;
-constexpr int C_ERR = 4 * CSTRIDE;
-constexpr int C_GU = 5 * CSTRIDE;  // + slot * CSTRIDE
-constexpr int C_COUNT = 5 + MAX_TOPK;
+// Phase counters: 64-bit, each in its own 256-byte slot of W.counters (slot 0
+// belongs to the multi-kernel router).  They only ever increase: call number
+// `ep` of a handle waits for (ep + 1) times the per-call count, so nothing has
+// to be reset at the end of a launch.
+constexpr int CSTRIDE = 32;  // in uint64
+constexpr int C_ROUTE = 1, C_READY = 2, C_SHGU = 3, C_ERR = 4, C_GU = 5;  // C_GU + slot; slot units
+__device__ __forceinline__ unsigned long long *ctr(const Work &W, int slot) {
+    return reinterpret_cast<unsigned long long *>(W.counters) + slot * CSTRIDE;
+}
 
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_THREADS = 64 * DEC_WAVES;
@@ -61,6 +63,7 @@ constexpr int DEC_GU_NR = 4;  // routed gate/up row slots per wave
 constexpr int DEC_DN_NR = 4;  // routed down row slots per wave
 
 struct DecPlan {
+    unsigned long long ep;  // calls already made on this workspace
     int n_route, n_shgu, n_rgu, n_shdn, n_rdn;
     int rgu_per_slot, rdn_per_slot;
     int shdn_cpr;
@@ -69,7 +72,7 @@ struct DecPlan {
 
 constexpr int SPIN_LIMIT = 1 << 20;      // polls before giving up (about a second)
 
-// Loads of data produced by other workgroups in this launch.
+// Loads of data produced by other workgroups in this launch (small items).
 __device__ __forceinline__ float ld_shared(const float *p) {
     return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT));
@@ -86,23 +89,33 @@ __device__ __forceinline__ void st_shared(int *p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The workgroup's shared stores are complete; then count the item (once).
-__device__ __forceinline__ void publish_item(int *ctr) {
+// This wavefront's shared stores are complete.
+__device__ __forceinline__ void stores_done() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Wait (one poller per workgroup, with backoff) until *ctr >= target.  Returns
+// The workgroup's shared stores are complete; then count the item (once).
+// Returns the counter value before the increment (valid in thread 0).
+__device__ __forceinline__ unsigned long long publish_item(unsigned long long *c) {
+    stores_done();
+    __syncthreads();
+    unsigned long long prev = 0;
+    if (threadIdx.x == 0) prev = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return prev;
+}
+
+// Wait (one poller per workgroup, with backoff) until *c >= target.  Returns
 // false, and flags the error, if the bounded wait expired.
-__device__ __forceinline__ bool wait_items(int *ctr, int *err, int target, int *lds_flag) {
+__device__ __forceinline__ bool wait_items(const Work &W, unsigned long long *c, unsigned long long target,
+                                           int *lds_flag) {
     if (threadIdx.x == 0) {
         int ok = 1, spins = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
             __builtin_amdgcn_s_sleep(8);
             if (++spins > SPIN_LIMIT) {
-                __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(ctr(W, C_ERR), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ok = 0;
                 break;
             }
@@ -191,64 +204,77 @@ __device__ __noinline__ void dec_topk_publish(const Layer &L, const Work &W) {
             W.list[rank] = j;
         }
     }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (lane == 0) __hip_atomic_fetch_add(W.counters + C_READY, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    stores_done();
+    if (lane == 0) __hip_atomic_fetch_add(ctr(W, C_READY), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <bool XBF16>
-__device__ void dec_route_item(const Layer &L, const Work &W, const void *__restrict__ x, int item, int *lds_flag,
-                               const DecPlan &P) {
+__device__ void dec_route_item(const Layer &L, const Work &W, const void *__restrict__ x, int e, int *lds_flag,
+                               double *lds_part, const DecPlan &P) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int E = L.n_embd, NE = L.n_expert;
-    const int e = item * DEC_WAVES + wave;
-    if (e < NE) {
-        const int nb = E >> 8;  // 256 elements per wave step
-        double acc = 0.0;
-        // two halves of 8 steps: 8 router float4 and 8 x loads in flight per lane
+    const int E = L.n_embd;
+    // wave w covers elements [w*E/4, (w+1)*E/4): E/1024 steps of 256
+    const int steps = E >> 10;
+    double acc = 0.0;
+    {
+        float4 r[4];
+        float4 xv[4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float4 r[8];
-            float4 xv[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int cc = 8 * h + c;
-                if (cc < nb) {
-                    const int i = 256 * cc + 4 * lane;
-                    r[c] = *reinterpret_cast<const float4 *>(L.router + (int64_t)e * E + i);
-                    if (XBF16) {
-                        const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(x) + i);
-                        xv[c] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
-                                            __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
-                    } else {
-                        xv[c] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + i);
-                    }
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                if (8 * h + c < nb) {
-                    acc = fma((double)xv[c].x, (double)r[c].x, acc);
-                    acc = fma((double)xv[c].y, (double)r[c].y, acc);
-                    acc = fma((double)xv[c].z, (double)r[c].z, acc);
-                    acc = fma((double)xv[c].w, (double)r[c].w, acc);
+        for (int c = 0; c < 4; ++c) {
+            if (c < steps) {
+                const int i = wave * (E >> 2) + 256 * c + 4 * lane;
+                r[c] = *reinterpret_cast<const float4 *>(L.router + (int64_t)e * E + i);
+                if (XBF16) {
+                    const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(x) + i);
+                    xv[c] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                                        __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+                } else {
+                    xv[c] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + i);
                 }
             }
         }
-        acc = wave_sum(acc);
-        if (lane == 0) st_shared(W.logits + e, (float)(acc + (L.router_bias ? (double)L.router_bias[e] : 0.0)));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (c < steps) {
+                acc = fma((double)xv[c].x, (double)r[c].x, acc);
+                acc = fma((double)xv[c].y, (double)r[c].y, acc);
+                acc = fma((double)xv[c].z, (double)r[c].z, acc);
+                acc = fma((double)xv[c].w, (double)r[c].w, acc);
+            }
+        }
+        // E < 1024: wave 0 takes the whole row in 256-element steps
+        if (steps == 0 && wave == 0) {
+            for (int i = 4 * lane; i < E; i += 256) {
+                const float4 rr = *reinterpret_cast<const float4 *>(L.router + (int64_t)e * E + i);
+                float4 xx;
+                if (XBF16) {
+                    const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(x) + i);
+                    xx = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+                } else {
+                    xx = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + i);
+                }
+                acc = fma((double)xx.x, (double)rr.x, acc);
+                acc = fma((double)xx.y, (double)rr.y, acc);
+                acc = fma((double)xx.z, (double)rr.z, acc);
+                acc = fma((double)xx.w, (double)rr.w, acc);
+            }
+        }
     }
-    // count the item; the workgroup that completes the last one does top-k
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
+    acc = wave_sum(acc);
+    if (lane == 0) lds_part[wave] = acc;
     __syncthreads();
-    if (threadIdx.x == 0)
-        *lds_flag = __hip_atomic_fetch_add(W.counters + C_ROUTE, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+        const double s = lds_part[0] + lds_part[1] + lds_part[2] + lds_part[3];
+        st_shared(W.logits + e, (float)(s + (L.router_bias ? (double)L.router_bias[e] : 0.0)));
+    }
+    // count the expert; the workgroup that completes the last one does top-k
+    const unsigned long long prev = publish_item(ctr(W, C_ROUTE));
+    if (threadIdx.x == 0) *lds_flag = (prev == (P.ep + 1) * (unsigned long long)P.n_route - 1ull);
     __syncthreads();
-    const int prev = *lds_flag;
+    const int last = *lds_flag;
     __syncthreads();
-    if (prev == P.n_route - 1 && wave == 0) dec_topk_publish(L, W);
+    if (last && wave == 0) dec_topk_publish(L, W);
 }
 
 // ---------------------------------------------------------------- P1: shared gate/up
@@ -301,7 +327,7 @@ __device__ void dec_shgu_item(const Layer &L, const Work &W, const void *__restr
         u = wave_sum(u);
         if (lane == 0) st_shared(W.hbuf + (int64_t)k * F + f, dec_silu(g) * u);
     }
-    publish_item(W.counters + C_SHGU);
+    publish_item(ctr(W, C_SHGU));
 }
 
 // ---------------------------------------------------------------- P2: routed gate/up (IQ2)
@@ -367,9 +393,30 @@ __device__ __forceinline__ float dec_iq2_dot(const uint4 *T, uint4 q, const DecX
     return acc;
 }
 
+// Routing of the token, read once per workgroup after "route ready".
+struct RouteCache {
+    int ready;
+    int idx[MAX_TOPK];
+    float w[MAX_TOPK];
+};
+
+__device__ __forceinline__ bool route_cached(const Layer &L, const Work &W, const DecPlan &P, RouteCache *rc,
+                                             int *lds_flag) {
+    if (rc->ready) return true;
+    if (!wait_items(W, ctr(W, C_READY), P.ep + 1, lds_flag)) return false;
+    if (threadIdx.x < L.top_k) {
+        rc->idx[threadIdx.x] = ld_shared(W.idx + threadIdx.x);
+        rc->w[threadIdx.x] = ld_shared(W.w + threadIdx.x);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) rc->ready = 1;
+    __syncthreads();
+    return true;
+}
+
 template <bool XBF16>
 __device__ void dec_rgu_item(const Layer &L, const Work &W, const void *__restrict__ x, const uint4 *T, int item,
-                             const DecPlan &P, int *lds_flag) {
+                             const DecPlan &P, int *lds_flag, RouteCache *rc) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd, F = L.n_ff;
     const int lpr = E >> 6, rpw = 64 / lpr;
@@ -379,8 +426,8 @@ __device__ void dec_rgu_item(const Layer &L, const Work &W, const void *__restri
     const int f0 = (tile * DEC_WAVES + wave) * rows_per_wave + lane / lpr;
     DecX<XBF16> xc;
     xc.load(x, 64 * c);
-    if (!wait_items(W.counters + C_READY, W.counters + C_ERR, 1, lds_flag)) return;
-    const int e = ld_shared(W.idx + j);
+    if (!route_cached(L, W, P, rc, lds_flag)) return;
+    const int e = rc->idx[j];
     uint4 qg[DEC_GU_NR], qu[DEC_GU_NR];
     float dg[DEC_GU_NR], du[DEC_GU_NR];
 #pragma unroll
@@ -407,7 +454,7 @@ __device__ void dec_rgu_item(const Layer &L, const Work &W, const void *__restri
         u = dec_group_sum(u, lpr) * 0.015625f;
         if (c == 0 && f < F) st_shared(W.hbuf + (int64_t)j * F + f, dec_silu(g) * u);
     }
-    publish_item(W.counters + C_GU + j * CSTRIDE);
+    publish_item(ctr(W, C_GU + j));
 }
 
 // ---------------------------------------------------------------- P3: shared down
@@ -431,15 +478,18 @@ __device__ void dec_shdn_item(const Layer &L, const Work &W, float *__restrict__
             wv[rr][c] = (row < E && ch < nch) ? *reinterpret_cast<const uint4 *>(L.sh_down + (int64_t)row * F + ch * 8)
                                               : make_uint4(0, 0, 0, 0);
         }
-    if (!wait_items(W.counters + C_SHGU, W.counters + C_ERR, P.n_shgu, lds_flag)) return;
+    if (!wait_items(W, ctr(W, C_SHGU), (P.ep + 1) * (unsigned long long)P.n_shgu, lds_flag)) return;
     const float *hs = W.hbuf + (int64_t)k * F;
     float hv[CPR][8];
 #pragma unroll
     for (int c = 0; c < CPR; ++c) {
         const int ch = lane + 64 * c;
         if (ch < nch) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) hv[c][i] = ld_shared(hs + ch * 8 + i);
+            // plain loads: these lines are first touched now, after every producer finished
+            const float4 *p = reinterpret_cast<const float4 *>(hs + ch * 8);
+            const float4 a = p[0], b = p[1];
+            hv[c][0] = a.x, hv[c][1] = a.y, hv[c][2] = a.z, hv[c][3] = a.w;
+            hv[c][4] = b.x, hv[c][5] = b.y, hv[c][6] = b.z, hv[c][7] = b.w;
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) hv[c][i] = 0.0f;
@@ -484,7 +534,7 @@ __device__ __forceinline__ float dec_q2k_dot(uint4 qs, uint32_t sc, uint32_t dd,
 }
 
 __device__ void dec_rdn_item(const Layer &L, const Work &W, float *__restrict__ out, int item, const DecPlan &P,
-                             int *lds_flag) {
+                             int *lds_flag, RouteCache *rc) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd, F = L.n_ff;
     const int lpr = F >> 6, rpw = 64 / lpr;
@@ -492,9 +542,10 @@ __device__ void dec_rdn_item(const Layer &L, const Work &W, float *__restrict__ 
     const int j = item / P.rdn_per_slot, tile = item - j * P.rdn_per_slot;
     const int rows_per_wave = DEC_DN_NR * rpw;
     const int r0 = (tile * DEC_WAVES + wave) * rows_per_wave + lane / lpr;
-    if (!wait_items(W.counters + C_GU + j * CSTRIDE, W.counters + C_ERR, P.rgu_per_slot, lds_flag)) return;
-    const int e = ld_shared(W.idx + j);
-    const float wgt = ld_shared(W.w + j);
+    if (!route_cached(L, W, P, rc, lds_flag)) return;
+    const int e = rc->idx[j];
+    const float wgt = rc->w[j];
+    if (!wait_items(W, ctr(W, C_GU + j), (P.ep + 1) * (unsigned long long)P.rgu_per_slot, lds_flag)) return;
     uint4 qs[DEC_DN_NR];
     uint32_t sc[DEC_DN_NR], dd[DEC_DN_NR];
 #pragma unroll
@@ -511,9 +562,13 @@ __device__ void dec_rdn_item(const Layer &L, const Work &W, float *__restrict__ 
         }
     }
     float hv[64], hsum[4];
-    const float *hp = W.hbuf + (int64_t)j * F + 64 * c;
+    // plain loads: these lines are first touched now, after every producer finished
+    const float4 *hp = reinterpret_cast<const float4 *>(W.hbuf + (int64_t)j * F + 64 * c);
 #pragma unroll
-    for (int i = 0; i < 64; ++i) hv[i] = ld_shared(hp + i);
+    for (int i = 0; i < 16; ++i) {
+        const float4 v = hp[i];
+        hv[4 * i] = v.x, hv[4 * i + 1] = v.y, hv[4 * i + 2] = v.z, hv[4 * i + 3] = v.w;
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         float a = 0.0f;
@@ -536,14 +591,17 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void k_decode_fused(Layer L, Work W
                                                              float *__restrict__ out, DecPlan P) {
     __shared__ uint4 T[256 * IQ2_REPL];
     __shared__ int lds_flag;
+    __shared__ double lds_part[DEC_WAVES];
+    __shared__ RouteCache rc;
+    if (threadIdx.x == 0) rc.ready = 0;
     iq2_build_lut<false>(T, L.codebook, threadIdx.x, DEC_THREADS);
     __syncthreads();
     const int G = gridDim.x;
     const int b0 = P.n_route, b1 = b0 + P.n_shgu, b2 = b1 + P.n_rgu, b3 = b2 + P.n_shdn;
     for (int it = blockIdx.x; it < P.total; it += G) {
-        if (it < b0) dec_route_item<XBF16>(L, W, x, it, &lds_flag, P);
+        if (it < b0) dec_route_item<XBF16>(L, W, x, it, &lds_flag, lds_part, P);
         else if (it < b1) dec_shgu_item<XBF16>(L, W, x, it - b0);
-        else if (it < b2) dec_rgu_item<XBF16>(L, W, x, T, it - b1, P, &lds_flag);
+        else if (it < b2) dec_rgu_item<XBF16>(L, W, x, T, it - b1, P, &lds_flag, &rc);
         else if (it < b3) {
             switch (P.shdn_cpr) {
                 case 1: dec_shdn_item<1>(L, W, out, it - b2, P, &lds_flag); break;
@@ -551,26 +609,18 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void k_decode_fused(Layer L, Work W
                 case 4: dec_shdn_item<4>(L, W, out, it - b2, P, &lds_flag); break;
                 default: dec_shdn_item<8>(L, W, out, it - b2, P, &lds_flag); break;
             }
-        } else dec_rdn_item(L, W, out, it - b3, P, &lds_flag);
+        } else dec_rdn_item(L, W, out, it - b3, P, &lds_flag, &rc);
     }
-    // leave; the last workgroup out resets the counters for the next call
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_s_waitcnt(0);
-        const int prev = __hip_atomic_fetch_add(W.counters + C_EXIT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == G - 1) {
-            if (__hip_atomic_load(W.counters + C_ERR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-                out[0] = __builtin_nanf("");   // a bounded wait expired: make it visible
-            for (int i = 0; i < C_COUNT; ++i)
-                __hip_atomic_store(W.counters + i * CSTRIDE, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    // a bounded wait expired somewhere: make the failure visible in the output
+    if (blockIdx.x == 0 && threadIdx.x == 0 &&
+        __hip_atomic_load(ctr(W, C_ERR), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        out[0] = __builtin_nanf("");
 }
 
 static DecPlan make_plan(const Layer &L) {
     DecPlan P{};
     const int E = L.n_embd, F = L.n_ff, k = L.top_k;
-    P.n_route = (L.n_expert + DEC_WAVES - 1) / DEC_WAVES;
+    P.n_route = L.n_expert;  // one expert per item
     P.n_shgu = L.n_shared ? (F + DEC_WAVES - 1) / DEC_WAVES : 0;
     const int rows_gu_item = DEC_WAVES * DEC_GU_NR * (64 / (E >> 6));
     P.rgu_per_slot = (F + rows_gu_item - 1) / rows_gu_item;
@@ -601,8 +651,10 @@ int decode_grid(int act_bf16) {
     return ncu * per_cu;
 }
 
-hipError_t launch_decode_fused(const Layer &L, const Work &W, const void *x, float *out, int grid, hipStream_t s) {
+hipError_t launch_decode_fused(const Layer &L, const Work &W, const void *x, float *out, int grid,
+                               unsigned long long ep, hipStream_t s) {
     DecPlan P = make_plan(L);
+    P.ep = ep;
     Layer Lc = L;
     Work Wc = W;
     const void *xc = x;

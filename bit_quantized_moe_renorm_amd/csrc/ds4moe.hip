@@ -45,6 +45,7 @@ struct ds4moe {
     Work W{};
     int path = DS4MOE_PATH_AUTO;
     int decode_grid = 0;    // workgroups of the persistent decode kernel
+    unsigned long long decode_calls = 0;  // fused launches so far (the phase counters' epoch)
     bool poisoned = false;
     int device = 0;
     std::vector<void *> allocs;
@@ -151,7 +152,7 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     auto carve = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     size_t o_logits = carve(T * NE * 4), o_idx = carve(T * k * 4), o_w = carve(T * k * 4);
     size_t o_off = carve((NE + 1) * 4), o_list = carve(T * k * 4), o_act = carve((NE + 1) * 4);
-    size_t o_cnt = carve(16 * 64 * 4), o_h = carve(gemv_slots * F * 4), o_h16 = carve(slots * F * 2);
+    size_t o_cnt = carve(16 * 256), o_h = carve(gemv_slots * F * 4), o_h16 = carve(slots * F * 2);
     char *ws = (char *)A(off);
     if (err != hipSuccess) {
         delete h;
@@ -258,7 +259,9 @@ int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *
     if (path == DS4MOE_PATH_GEMV && n_tok == 1) {
         // the whole block for one token in one persistent launch
         int tf = h->tbegin(TK_FUSED, s);
-        rc = check_launch(h, launch_decode_fused(h->L, h->W, x, out, h->decode_grid, s), "fused decode");
+        rc = check_launch(h, launch_decode_fused(h->L, h->W, x, out, h->decode_grid, h->decode_calls, s),
+                          "fused decode");
+        h->decode_calls += 1;
         h->tend(tf, s);
         return rc;
     }

@@ -8,18 +8,19 @@
 //
 // The 256-entry codebook is expanded once per workgroup into an LDS table of
 // unsigned levels (2c+1) for all 8 coordinates (16 bytes per entry, packed
-// pairs).  The table is replicated 8 times with the replicas interleaved at
-// 16-byte granularity, and lane l reads replica l & 7: the 8 lanes that share a
-// ds_read_b128 cycle then always hit 8 different bank quads, whatever indices
-// they look up, so lookups never conflict.  Signs are applied with XOR masks
+// pairs).  The table is replicated 16 times with the replicas interleaved at
+// 16-byte granularity (entry e, replica r at byte 256 e + 16 r), and lane l
+// reads replica l & 15: replica r always sits in bank quad r (of 64 banks), so
+// the 16 lanes served together by a ds_read_b128 never conflict, whatever
+// indices they look up.  Signs are applied with XOR masks
 // built from the sign bits by rotates (v_alignbit) and one v_bitop3 each.
 #pragma once
 #include "common.h"
 
 namespace ds4 {
 
-constexpr int IQ2_REPL = 8;
-constexpr int IQ2_LUT_BYTES = 256 * IQ2_REPL * 16;  // 32 KB
+constexpr int IQ2_REPL = 16;
+constexpr int IQ2_LUT_BYTES = 256 * IQ2_REPL * 16;  // 64 KB
 
 // Unsigned level (2c+1) bit patterns, c in 0..3.
 __device__ __forceinline__ uint32_t iq2_level_bf16(uint32_t c) {
@@ -29,7 +30,7 @@ __device__ __forceinline__ uint32_t iq2_level_f16(uint32_t c) {
     return (c == 0) ? 0x3C00u : (c == 1) ? 0x4200u : (c == 2) ? 0x4500u : 0x4700u;
 }
 
-// Build the replicated table (entry e, replica r at uint4 index e*8 + r): each
+// Build the replicated table (entry e, replica r at uint4 index e*16 + r): each
 // thread loads whole codebook entries once and writes their 8 replicas.
 template <bool FP16>
 __device__ __forceinline__ void iq2_build_lut(uint4 *T, const uint16_t *__restrict__ codebook, int tid, int nthreads) {
@@ -42,6 +43,16 @@ __device__ __forceinline__ void iq2_build_lut(uint4 *T, const uint16_t *__restri
 #pragma unroll
         for (int r = 0; r < IQ2_REPL; ++r) T[e * IQ2_REPL + r] = q;
     }
+}
+
+// Rotate right (v_alignbit_b32 with both sources equal).  Written as one
+// instruction so the compiler cannot fold the rotate and the following mask
+// into a quarter-rate 32-bit multiply.
+template <int R>
+__device__ __forceinline__ uint32_t rotr(uint32_t v) {
+    uint32_t r;
+    asm("v_alignbit_b32 %0, %1, %1, %2" : "=v"(r) : "v"(v), "i"(R));
+    return r;
 }
 
 // Signed levels of one group: idx = codebook index, s7 = stored sign bits of
@@ -57,10 +68,10 @@ __device__ __forceinline__ uint4 iq2_group_levels(const uint4 *T, uint32_t idx, 
     // bit 2j) and bit 31 (from copy B, bit 2j+1).  Rotating S left by 15-2j (a
     // right rotate by 17+2j with v_alignbit) puts both there at once.
     const uint32_t M = 0x80008000u;
-    L.x ^= __builtin_amdgcn_alignbit(S, S, 17) & M;
-    L.y ^= __builtin_amdgcn_alignbit(S, S, 19) & M;
-    L.z ^= __builtin_amdgcn_alignbit(S, S, 21) & M;
-    L.w ^= __builtin_amdgcn_alignbit(S, S, 23) & M;
+    L.x ^= rotr<17>(S) & M;
+    L.y ^= rotr<19>(S) & M;
+    L.z ^= rotr<21>(S) & M;
+    L.w ^= rotr<23>(S) & M;
     return L;
 }
 
