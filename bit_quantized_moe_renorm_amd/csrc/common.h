@@ -48,9 +48,15 @@ struct Work {
     int32_t *list;        // [max_tokens*k] entries t*k + j, grouped by expert, ascending t
     int32_t *active;      // [NE+1]: active[0] = U, active[1..U] = experts with tokens, ascending
     int32_t *counters;    // counter slots of 256 bytes: slot 0 router tail, then the decode phases
-    float *hbuf;          // [max_tokens*(k+1)][F] fp32 activations between gate/up and down
-    uint16_t *hbuf16;     // [max_tokens*(k+1)][F] fp16 activations (GEMM path)
-    float *wsum;          // unused padding slot
+    float *hbuf;          // [min(max_tokens, 4)*(k+1)][F] fp32 activations between gate/up and down (GEMV)
+    // batched (GEMM) path
+    uint16_t *hbuf16;     // [max_tokens*k][F] fp16 routed activations, row = slot t*k + j
+    uint16_t *hsum;       // [max_tokens*k][F/16] fp16 sums of 16 consecutive hbuf16 values
+    uint16_t *x16;        // [max_tokens][E] fp16 copy of x
+    uint16_t *xhi, *xlo;  // [max_tokens][E] bf16 high / low parts of fp32 x (fp32 activations only)
+    uint16_t *hsh_hi, *hsh_lo;  // [max_tokens][F] shared-expert activations, bf16 high / low parts
+    int4 *chunks;         // [gemm_max_chunks] (expert, first list position, count)
+    int32_t *nchunks;     // number of valid chunks
 };
 
 // ---------------------------------------------------------------- small device helpers
@@ -93,6 +99,7 @@ enum TimingKind {
 };
 
 bool gemm_enabled();
+int gemm_max_chunks(int n_tok, int NE, int k);   // upper bound of the routed chunk count
 hipError_t launch_gemm_gateup(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);
 hipError_t launch_gemm_down(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
 

@@ -146,13 +146,17 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
         sd = (uint16_t *)A(E * F * 2);
     }
     // workspace
-    const int64_t slots = T * (k + 1);
     const int64_t gemv_slots = std::min<int64_t>(T, GEMV_MAX_TOK) * (k + 1);
     size_t off = 0;
     auto carve = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     size_t o_logits = carve(T * NE * 4), o_idx = carve(T * k * 4), o_w = carve(T * k * 4);
     size_t o_off = carve((NE + 1) * 4), o_list = carve(T * k * 4), o_act = carve((NE + 1) * 4);
-    size_t o_cnt = carve(16 * 256), o_h = carve(gemv_slots * F * 4), o_h16 = carve(slots * F * 2);
+    size_t o_cnt = carve(16 * 256), o_h = carve(gemv_slots * F * 4), o_h16 = carve(T * k * F * 2);
+    size_t o_hsum = carve(T * k * (F / 16) * 2), o_x16 = carve(T * E * 2);
+    const bool xf32 = d->act_dtype == DS4MOE_F32;
+    size_t o_xhi = carve(xf32 ? T * E * 2 : 0), o_xlo = carve(xf32 ? T * E * 2 : 0);
+    size_t o_shh = carve(d->n_shared ? T * F * 2 : 0), o_shl = carve(d->n_shared ? T * F * 2 : 0);
+    size_t o_chunks = carve((size_t)gemm_max_chunks((int)T, (int)NE, (int)k) * 16), o_nch = carve(4);
     char *ws = (char *)A(off);
     if (err != hipSuccess) {
         delete h;
@@ -169,6 +173,14 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     W.counters = (int32_t *)(ws + o_cnt);
     W.hbuf = (float *)(ws + o_h);
     W.hbuf16 = (uint16_t *)(ws + o_h16);
+    W.hsum = (uint16_t *)(ws + o_hsum);
+    W.x16 = (uint16_t *)(ws + o_x16);
+    W.xhi = xf32 ? (uint16_t *)(ws + o_xhi) : nullptr;
+    W.xlo = xf32 ? (uint16_t *)(ws + o_xlo) : nullptr;
+    W.hsh_hi = d->n_shared ? (uint16_t *)(ws + o_shh) : nullptr;
+    W.hsh_lo = d->n_shared ? (uint16_t *)(ws + o_shl) : nullptr;
+    W.chunks = (int4 *)(ws + o_chunks);
+    W.nchunks = (int32_t *)(ws + o_nch);
 
 #define CK(call)                                                                                      \
     do {                                                                                              \
