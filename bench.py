@@ -167,6 +167,80 @@ def run_decode(args):
     return res
 
 
+def flops_prefill(spec, n):
+    """Algorithmic floating-point operations of each batched-path kernel for n tokens
+    (2 per multiply-add; the Q2_K min term and the shared expert's low-part
+    MFMAs are implementation overhead and not counted)."""
+    E, F, NE, k = spec.n_embd, spec.n_ff, spec.n_expert, spec.top_k
+    S = n * k
+    return {"route": 2 * n * E * NE, "gemm_gateup_routed": 4 * E * F * S, "gemm_gateup_shared": 4 * E * F * n,
+            "gemm_down_routed": 2 * E * F * S, "gemm_down_shared": 2 * E * F * n}
+
+
+def run_prefill(args):
+    import numpy as np
+    import torch
+
+    import bit_quantized_moe_renorm_amd as m
+    from bit_quantized_moe_renorm_amd import synth
+
+    spec = synth.DS4
+    n = args.tokens
+    layer = synth.make_layer(spec, seed=1)
+    x_np = synth.activations(1, n, spec.n_embd)
+    w = m.upload_layer(layer)
+    dev = m.MoELayer(spec, w, max_tokens=n)
+    del w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    x = m.to_device_x(x_np)
+    out = torch.zeros((n, spec.n_embd), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        dev.forward(x, out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dev.forward(x, out)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dev.timing_enable(True)
+    for _ in range(args.steps):
+        dev.forward(x, out)
+    torch.cuda.synchronize()
+    tim = dev.timing_read()
+    dev.timing_enable(False)
+    fl = flops_prefill(spec, n)
+    per_kernel = {}
+    for kind, (ms, cnt) in tim.items():
+        us = 1000.0 * ms / cnt
+        d = {"avg_us": round(us, 2)}
+        if kind in fl:
+            d["TFLOP_s"] = round(fl[kind] / (us * 1e-6) / 1e12, 1)
+        per_kernel[kind] = d
+    log("[bench] prefill per-kernel: " + json.dumps(per_kernel))
+    dom = "gemm_gateup_routed"
+    achieved = per_kernel[dom]["TFLOP_s"]
+    ms_step = 1000.0 * wall / args.steps
+    tok_s = n / (wall / args.steps)
+    total_tf = sum(fl.values()) / (wall / args.steps) / 1e12
+    log(f"[bench] prefill {n}: {ms_step:.3f} ms/step, {tok_s:.0f} tok/s, {total_tf:.0f} TFLOP/s whole layer")
+    res = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16/bf16 MFMA, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"DS4-shape MoE layer prefill of {n} tokens in one call (n_embd 4096, n_ff 2048, "
+                               "256 experts, top-6, 1 shared; IQ2-style gate/up, Q2_K-style down; seed 1)",
+                   "global_batch": n, "seq_len": n, "parallelism": "none (1 GPU)",
+                   "layer_TFLOP_s": round(total_tf, 1), "layer_flop": sum(fl.values()),
+                   "per_kernel": per_kernel},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    dev.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,6 +248,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=("decode", "prefill"), default="decode")
+    ap.add_argument("--tokens", type=int, default=2048, help="prefill tokens per call")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X only: this build runs the MoE block on a single GPU "
@@ -183,7 +259,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    res = run_decode(args)
+    if args.workload == "prefill":
+        if args.steps == 1000 and args.warmup == 100:   # defaults sized for decode
+            args.steps, args.warmup = 50, 5
+        res = run_prefill(args)
+    else:
+        res = run_decode(args)
     print(json.dumps(res), flush=True)
 
 

@@ -20,8 +20,8 @@ OK, EINVAL, ENOMEM, EHIP, EUNSUPPORTED, EPOISONED = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
 ABI_VERSION = 1
-TIMING_KINDS = ("route", "gateup_routed", "gateup_shared", "down_routed", "down_shared", "gemm_gateup",
-                "gemm_down", "fused")
+TIMING_KINDS = ("route", "gateup_routed", "gateup_shared", "down_routed", "down_shared", "gemm_gateup_routed",
+                "gemm_down_routed", "fused", "gemm_prep", "gemm_gateup_shared", "gemm_down_shared")
 
 SYMBOLS = ("ds4moe_create", "ds4moe_route", "ds4moe_forward", "ds4moe_set_path", "ds4moe_dequantize",
            "ds4moe_rmsnorm", "ds4moe_timing_enable", "ds4moe_timing_read", "ds4moe_destroy",
@@ -163,8 +163,8 @@ class MoELayer:
         _check(load_library().ds4moe_timing_enable(self.h, 1 if on else 0))
 
     def timing_read(self):
-        ms = (ctypes.c_double * 8)()
-        cnt = (ctypes.c_int64 * 8)()
+        ms = (ctypes.c_double * len(TIMING_KINDS))()
+        cnt = (ctypes.c_int64 * len(TIMING_KINDS))()
         _check(load_library().ds4moe_timing_read(self.h, ms, cnt))
         return {TIMING_KINDS[i]: (ms[i], cnt[i]) for i in range(len(TIMING_KINDS)) if cnt[i]}
 

@@ -30,6 +30,8 @@ struct Layer {
     // weights (library-owned)
     const float *router;            // [NE][E]
     const float *router_bias;       // [NE] or nullptr
+    const uint16_t *router_hml;     // [3][NE][E] bf16 parts hi, mid, lo of the router (hi + mid + lo = router)
+    const float *router_norm;       // [NE] Euclidean norm of each router row, rounded up
     const uint16_t *codebook;       // [256] device copy
     const uint8_t *iq2_qs[2];       // gate, up: [NE][F][nbe][64]
     const uint16_t *iq2_d[2];       // [NE][F][nbe]
@@ -51,7 +53,6 @@ struct Work {
     float *hbuf;          // [min(max_tokens, 4)*(k+1)][F] fp32 activations between gate/up and down (GEMV)
     // batched (GEMM) path
     uint16_t *hbuf16;     // [max_tokens*k][F] fp16 routed activations, row = slot t*k + j
-    uint16_t *hsum;       // [max_tokens*k][F/16] fp16 sums of 16 consecutive hbuf16 values
     uint16_t *x16;        // [max_tokens][E] fp16 copy of x
     uint16_t *xhi, *xlo;  // [max_tokens][E] bf16 high / low parts of fp32 x (fp32 activations only)
     uint16_t *hsh_hi, *hsh_lo;  // [max_tokens][F] shared-expert activations, bf16 high / low parts
@@ -64,6 +65,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 
 __device__ __forceinline__ float half_to_f32(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
 }
 
 template <typename T>
@@ -82,6 +91,7 @@ hipError_t launch_repack_q2k(const uint8_t *canon, int64_t n_blocks, uint8_t *qs
 hipError_t launch_dequant_iq2(const Layer &L, int which, int expert, float *dst, hipStream_t s);
 hipError_t launch_dequant_q2k(const Layer &L, int expert, float *dst, hipStream_t s);
 
+hipError_t launch_router_prep(const float *router, int NE, int E, uint16_t *hml, float *norm, hipStream_t s);
 hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s,
                         hipEvent_t *ev /* nullable: [2] around the route kernels */);
 hipError_t launch_route_export(const Layer &L, const Work &W, int n_tok, int32_t *idx, float *w,
@@ -95,13 +105,17 @@ hipError_t launch_gemv_down_shared(const Layer &L, const Work &W, int n_tok, flo
 // Timing brackets recorded by ds4moe_forward when timing is enabled.
 enum TimingKind {
     TK_ROUTE = 0, TK_GU_ROUTED = 1, TK_GU_SHARED = 2, TK_DN_ROUTED = 3, TK_DN_SHARED = 4,
-    TK_GEMM_GU = 5, TK_GEMM_DN = 6, TK_FUSED = 7
+    TK_GEMM_GU_ROUTED = 5, TK_GEMM_DN_ROUTED = 6, TK_FUSED = 7, TK_GEMM_PREP = 8, TK_GEMM_GU_SHARED = 9,
+    TK_GEMM_DN_SHARED = 10, TK_COUNT = 11
 };
 
 bool gemm_enabled();
 int gemm_max_chunks(int n_tok, int NE, int k);   // upper bound of the routed chunk count
-hipError_t launch_gemm_gateup(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);
-hipError_t launch_gemm_down(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
+hipError_t launch_gemm_prep(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);
+hipError_t launch_gemm_gateup_routed(const Layer &L, const Work &W, int n_tok, hipStream_t s);
+hipError_t launch_gemm_gateup_shared(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);
+hipError_t launch_gemm_down_routed(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
+hipError_t launch_gemm_down_shared(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
 
 int decode_grid(int act_bf16);
 hipError_t launch_decode_fused(const Layer &L, const Work &W, const void *x, float *out, int grid,

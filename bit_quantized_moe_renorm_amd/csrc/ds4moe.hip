@@ -35,7 +35,7 @@ bool pow2_dim(int v) { return v == 256 || v == 512 || v == 1024 || v == 2048 || 
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-constexpr int TIMING_SLOTS = 8;
+constexpr int TIMING_SLOTS = TK_COUNT;
 constexpr int TIMING_EVENTS = 4096;
 
 }  // namespace
@@ -134,6 +134,8 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     };
     float *router = (float *)A(NE * E * 4);
     float *bias = d->router_bias ? (float *)A(NE * 4) : nullptr;
+    uint16_t *rhml = (uint16_t *)A(3 * NE * E * 2);
+    float *rnorm = (float *)A(NE * 4);
     uint16_t *cb = (uint16_t *)A(512);
     uint8_t *gq = (uint8_t *)A(gu_blocks * 64), *uq = (uint8_t *)A(gu_blocks * 64);
     uint16_t *gd = (uint16_t *)A(gu_blocks * 2), *ud = (uint16_t *)A(gu_blocks * 2);
@@ -152,7 +154,7 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     size_t o_logits = carve(T * NE * 4), o_idx = carve(T * k * 4), o_w = carve(T * k * 4);
     size_t o_off = carve((NE + 1) * 4), o_list = carve(T * k * 4), o_act = carve((NE + 1) * 4);
     size_t o_cnt = carve(16 * 256), o_h = carve(gemv_slots * F * 4), o_h16 = carve(T * k * F * 2);
-    size_t o_hsum = carve(T * k * (F / 16) * 2), o_x16 = carve(T * E * 2);
+    size_t o_x16 = carve(T * E * 2);
     const bool xf32 = d->act_dtype == DS4MOE_F32;
     size_t o_xhi = carve(xf32 ? T * E * 2 : 0), o_xlo = carve(xf32 ? T * E * 2 : 0);
     size_t o_shh = carve(d->n_shared ? T * F * 2 : 0), o_shl = carve(d->n_shared ? T * F * 2 : 0);
@@ -173,7 +175,6 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     W.counters = (int32_t *)(ws + o_cnt);
     W.hbuf = (float *)(ws + o_h);
     W.hbuf16 = (uint16_t *)(ws + o_h16);
-    W.hsum = (uint16_t *)(ws + o_hsum);
     W.x16 = (uint16_t *)(ws + o_x16);
     W.xhi = xf32 ? (uint16_t *)(ws + o_xhi) : nullptr;
     W.xlo = xf32 ? (uint16_t *)(ws + o_xlo) : nullptr;
@@ -193,6 +194,7 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     CK(hipMemsetAsync(ws, 0, off, s));
     CK(hipMemcpyAsync(router, d->router, NE * E * 4, hipMemcpyDeviceToDevice, s));
     if (bias) CK(hipMemcpyAsync(bias, d->router_bias, NE * 4, hipMemcpyDeviceToDevice, s));
+    CK(launch_router_prep(router, (int)NE, (int)E, rhml, rnorm, s));
     CK(hipMemcpyAsync(cb, d->codebook, 512, hipMemcpyHostToDevice, s));
     if (d->n_shared) {
         CK(hipMemcpyAsync(sg, d->sh_gate, F * E * 2, hipMemcpyDeviceToDevice, s));
@@ -205,6 +207,7 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     CK(hipStreamSynchronize(s));
 #undef CK
     L.router = router, L.router_bias = bias, L.codebook = cb;
+    L.router_hml = rhml, L.router_norm = rnorm;
     L.iq2_qs[0] = gq, L.iq2_qs[1] = uq, L.iq2_d[0] = gd, L.iq2_d[1] = ud;
     L.q2k_qs = dq, L.q2k_sc = dsc, L.q2k_dd = ddd;
     L.sh_gate = sg, L.sh_up = su, L.sh_down = sd;
@@ -303,13 +306,30 @@ int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *
         }
         return rc;
     }
-    tb = h->tbegin(TK_GEMM_GU, s);
-    rc = check_launch(h, launch_gemm_gateup(h->L, h->W, x, n_tok, s), "gemm gate/up");
+    // batched path: activation copies and chunk table, then the four grouped GEMMs
+    tb = h->tbegin(TK_GEMM_PREP, s);
+    rc = check_launch(h, launch_gemm_prep(h->L, h->W, x, n_tok, s), "gemm prep");
     h->tend(tb, s);
     if (rc) return rc;
-    tb = h->tbegin(TK_GEMM_DN, s);
-    rc = check_launch(h, launch_gemm_down(h->L, h->W, n_tok, out, s), "gemm down");
+    tb = h->tbegin(TK_GEMM_GU_ROUTED, s);
+    rc = check_launch(h, launch_gemm_gateup_routed(h->L, h->W, n_tok, s), "gemm routed gate/up");
     h->tend(tb, s);
+    if (rc) return rc;
+    if (h->L.n_shared) {
+        tb = h->tbegin(TK_GEMM_GU_SHARED, s);
+        rc = check_launch(h, launch_gemm_gateup_shared(h->L, h->W, x, n_tok, s), "gemm shared gate/up");
+        h->tend(tb, s);
+        if (rc) return rc;
+    }
+    tb = h->tbegin(TK_GEMM_DN_ROUTED, s);
+    rc = check_launch(h, launch_gemm_down_routed(h->L, h->W, n_tok, out, s), "gemm routed down");
+    h->tend(tb, s);
+    if (rc) return rc;
+    if (h->L.n_shared) {
+        tb = h->tbegin(TK_GEMM_DN_SHARED, s);
+        rc = check_launch(h, launch_gemm_down_shared(h->L, h->W, n_tok, out, s), "gemm shared down");
+        h->tend(tb, s);
+    }
     return rc;
 }
 

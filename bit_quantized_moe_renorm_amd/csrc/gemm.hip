@@ -9,15 +9,11 @@
 // 4(l/16)..+3 of that same column, so every per-row factor (block scale d,
 // sub-block scale, Q2_K d / dmin) is lane-local.
 //
-// Exactness of the decoded operands ("Redis 作者出手！ds4...", section 2.3):
-//   IQ2 gate/up: B = +-(2c+1)(2ls+1), integers <= 217, exact in fp16; the fp16
-//     block scale d and the format's constant 1/64 are applied to the fp32
-//     partial sum of each 256-K block.
-//   Q2_K down:   B = sc * q (<= 45, exact); the block's d multiplies that sum and
-//     dmin multiplies the min term sum_s m_s * hsum_s, computed by a 16x16x16
-//     MFMA from per-16-row sums of h written by the gate/up epilogue.
-// Activations are rounded to fp16 for the routed MFMAs (x and h); overflow of
-// the fp16 range turns into inf in the output rather than a silent error.  The
+// Numerics: the routed experts' B operand is the dequantized weight rounded
+// to fp16 (IQ2: signed level (2c+1) times fp16(d (2ls+1) / 64); Q2_K:
+// fma(q, fp16(d sc), fp16(-dmin m)); "Redis 作者出手！ds4...", section 2.3), and
+// their activations (x, and h = silu(gate) * up) are rounded to fp16; fp16
+// overflow turns into inf in the output rather than a silent error.  The
 // shared expert keeps its bf16 weights and takes bf16 activations split into a
 // high and a low part (two MFMAs), so its only rounding is fp32 accumulation.
 #include "common.h"
@@ -57,22 +53,7 @@ __device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(h
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
 __device__ __forceinline__ uint16_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
-
-// Sum over the 16 lanes that share l / 16 (the 16 weight rows of one C column block).
-__device__ __forceinline__ float row16_sum(float v) {
-    v += __shfl_xor(v, 8, 16);
-    v += __shfl_xor(v, 4, 16);
-    v += __shfl_xor(v, 2, 16);
-    v += __shfl_xor(v, 1, 16);
-    return v;
-}
 
 // ---------------------------------------------------------------- routing -> chunks
 // Splits every expert's token list into chunks of at most CH_TOK slots:
@@ -133,129 +114,182 @@ __device__ __forceinline__ uint4 stage_get(const uint8_t *stg, int i, int rl, in
     return *reinterpret_cast<const uint4 *>(stg + (16 * i + rl) * STG_PITCH + grp * 16);
 }
 
-// ---------------------------------------------------------------- routed gate/up
-// grid: (n_ff / GU_ROWS, max chunks).  Wave w covers n_ff rows f0..f0+31 of
-// both gate and up (B fragments: gate f0, gate f0+16, up f0, up f0+16) for all
-// tokens of the chunk (up to 4 token tiles), over the whole n_embd.
-__global__ __launch_bounds__(256, 2) void k_gemm_gateup_routed(Layer L, Work W) {
-    const int c = blockIdx.y;
-    if (c >= *W.nchunks) return;
-    const int4 ch = W.chunks[c];
-    const int e = ch.x, beg = ch.y, cnt = ch.z;
-    __shared__ uint4 T[256 * IQ2_REPL];
-    __shared__ __align__(16) uint8_t stg[2][STG_BYTES];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rl = lane & 15, grp = lane >> 4;
-    const int E = L.n_embd, F = L.n_ff, k = L.top_k, nbe = L.nbe;
-    const int nt = (cnt + 15) >> 4;
-    const int nkc = E / 32;
+// ---------------------------------------------------------------- routed experts: block-staged GEMMs
+// Both routed kernels work one 256-K block at a time.  The block of A (64
+// token rows x 256 K, fp16) sits in an LDS stage (double-buffered, one barrier
+// per block), and the MFMA K order is permuted inside the block: in step c
+// (0..7) lane group g = l / 16 supplies K 64 g + 8 c..+8.  Each lane therefore
+// needs only its own quarter of every weight row block: IQ2 sub-blocks 2g and
+// 2g + 1 (16 bytes), Q2_K qs bytes 16 g..16 g+15 (16 bytes) and scale bytes
+// 4 g..4 g+3, loaded once per block as one vector per fragment.
+//
+// The B operand is the dequantized weight rounded to fp16 (relative error at
+// most 2^-11 per weight): IQ2 = signed level (2c+1) times fp16(d (2ls+1) / 64),
+// Q2_K = fma(q, fp16(d sc), fp16(-dmin m)) in packed fp16, so the MFMAs
+// accumulate the whole K range into one fp32 accumulator per tile.
+constexpr int RB_WAVES = 16;                      // waves per routed workgroup (1 workgroup per CU)
+constexpr int RB_THREADS = 64 * RB_WAVES;
+constexpr int GU_FR = 1;                          // gate/up: 16-row fragments per matrix per wave
+constexpr int GU_NF = 2 * GU_FR;                  // fragments per wave (gate ones, then up ones)
+constexpr int DN_NF = 2;                          // down: 16-row fragments per wave
+constexpr int RB_PITCH = 2 * QK + 16;             // stage row: 256 fp16 + 16 B pad (conflict-free A reads)
+constexpr int RB_STAGE = CH_TOK * RB_PITCH;       // 33792 bytes
+constexpr int RGU_ROWS = RB_WAVES * 16 * GU_FR;   // n_ff rows per gate/up workgroup
+constexpr int RDN_ROWS = RB_WAVES * 16 * DN_NF;   // n_embd rows per down workgroup
+constexpr int LD_V = CH_TOK * QK * 2 / 16 / RB_THREADS;  // 16-byte vectors per thread per stage
+constexpr int LD_PER_ROW = 32 / LD_V;             // threads per token row
 
-    // A loader: token row tid / 4 of the chunk
-    const int sr = tid >> 2;
-    const uint16_t *xrow = nullptr;
-    if (sr < cnt) xrow = W.x16 + (int64_t)(W.list[beg + sr] / k) * E + 8 * (tid & 3);
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
-    const int f0 = blockIdx.x * GU_ROWS + wave * 32;
-    const uint2 *wq[4];
-    const uint16_t *wd[4];
-#pragma unroll
-    for (int fi = 0; fi < 4; ++fi) {
-        const int m = fi >> 1, f = f0 + 16 * (fi & 1) + rl;
-        const int64_t rb = ((int64_t)e * F + f) * nbe;
-        wq[fi] = reinterpret_cast<const uint2 *>(L.iq2_qs[m] + rb * 64);  // K-chunk kc: wq[fi][kc]
-        wd[fi] = L.iq2_d[m] + rb;
+// Block stage loader: thread t moves LD_V x 16 bytes: token row t / LD_PER_ROW,
+// K 8 LD_V (t % LD_PER_ROW)..+8 LD_V.
+struct BlockLoader {
+    const uint16_t *src;   // row start + K offset, or nullptr for rows past the chunk
+    int lds_off;
+    __device__ void init(const uint16_t *row, int tid) {
+        const int p = tid % LD_PER_ROW;
+        src = row ? row + 8 * LD_V * p : nullptr;
+        lds_off = (tid / LD_PER_ROW) * RB_PITCH + 16 * LD_V * p;
     }
-
-    uint4 xv[PF];
-    uint2 wr[PF][4];
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
+    __device__ void load(int bi, uint4 (&r)[LD_V]) const {
 #pragma unroll
-    for (int s = 0; s < PF; ++s) {
-        xv[s] = (xrow && s < nkc) ? *reinterpret_cast<const uint4 *>(xrow + 32 * s) : z4;
-#pragma unroll
-        for (int fi = 0; fi < 4; ++fi) wr[s][fi] = (s < nkc) ? wq[fi][s] : make_uint2(0, 0);
+        for (int j = 0; j < LD_V; ++j)
+            r[j] = src ? *reinterpret_cast<const uint4 *>(src + QK * bi + 8 * j) : make_uint4(0, 0, 0, 0);
     }
-    iq2_build_lut<true>(T, L.codebook, tid, 256);
-    stage_put(stg[0], tid, xv[0]);
-    xv[0] = (xrow && PF < nkc) ? *reinterpret_cast<const uint4 *>(xrow + 32 * PF) : z4;
-    __syncthreads();
+    __device__ void store(uint8_t *stg, const uint4 (&r)[LD_V]) const {
+#pragma unroll
+        for (int j = 0; j < LD_V; ++j) *reinterpret_cast<uint4 *>(stg + lds_off + 16 * j) = r[j];
+    }
+};
+// A fragment for step c of token tile i: row 16 i + rl, K 64 grp + 8 c.
+__device__ __forceinline__ half8 block_a(const uint8_t *stg, int i, int c, int rl, int grp) {
+    return as_half8(*reinterpret_cast<const uint4 *>(stg + (16 * i + rl) * RB_PITCH + 128 * grp + 16 * c));
+}
 
-    floatx4 acc[4][4], blk[4][4];
+// Main loop and epilogue of the routed gate/up GEMM for a chunk of NT token
+// tiles (NT is a template parameter so the step bodies have no branches).
+template <int NT>
+__device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &W, const uint4 *T, uint8_t *stg0,
+                                                    uint8_t *stg1, const BlockLoader &ld, uint4 (&xr)[LD_V],
+                                                    const uint8_t *qg, const uint16_t *dg, int fq, int fd, int f0,
+                                                    int beg, int cnt, int rl, int grp) {
+    const int F = L.n_ff, nbe = L.nbe;
+    // gate and up planes sit at a fixed distance from each other
+    const int64_t qdu = L.iq2_qs[1] - L.iq2_qs[0], ddu = L.iq2_d[1] - L.iq2_d[0];
+    auto wload = [&](int fi, int bi) {
+        return *reinterpret_cast<const uint4 *>(qg + ((fi >= GU_FR) ? qdu : 0) + (fi % GU_FR) * fq + 64 * bi);
+    };
+    auto dload = [&](int fi, int bi) { return dg[((fi >= GU_FR) ? ddu : 0) + (fi % GU_FR) * fd + bi]; };
+    uint4 wcur[GU_NF], wnext[GU_NF];
+    uint16_t dcur[GU_NF], dnext[GU_NF];
+#pragma unroll
+    for (int fi = 0; fi < GU_NF; ++fi) wcur[fi] = wload(fi, 0), dcur[fi] = dload(fi, 0);
+
+    floatx4 acc[NT][GU_NF];
     const floatx4 zf = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int fi = 0; fi < 4; ++fi) acc[i][fi] = zf, blk[i][fi] = zf;
+        for (int fi = 0; fi < GU_NF; ++fi) acc[i][fi] = zf;
 
     for (int bi = 0; bi < nbe; ++bi) {
-        float dsc[4];
+        const bool more = bi + 1 < nbe;
+        if (more) {
+            ld.load(bi + 1, xr);
 #pragma unroll
-        for (int fi = 0; fi < 4; ++fi) dsc[fi] = half_to_f32(wd[fi][bi]) * 0.015625f;  // d / 64
+            for (int fi = 0; fi < GU_NF; ++fi) wnext[fi] = wload(fi, bi + 1), dnext[fi] = dload(fi, bi + 1);
+        }
+        const uint8_t *cur = (bi & 1) ? stg1 : stg0;
+        half2v scl[GU_NF];
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
-            const int kc = bi * 8 + cc;
-            const int sl = cc & (PF - 1);
-            const uint8_t *cur = stg[kc & 1];
-            // decode the four B fragments of this K-chunk
-            half8 b[4];
+            uint4 lv[GU_NF];
 #pragma unroll
-            for (int fi = 0; fi < 4; ++fi) {
-                const uint32_t ib = wr[sl][fi].x, sw = wr[sl][fi].y;
-                const uint4 lv = iq2_group_levels(T, (ib >> (8 * grp)) & 0xFFu, (sw >> (7 * grp)) & 0x7Fu, rl);
-                const _Float16 s = (_Float16)(float)(2u * (sw >> 28) + 1u);
-                b[fi] = as_half8(lv) * s;
+            for (int fi = 0; fi < GU_NF; ++fi) {
+                const uint32_t ib = (cc < 4) ? wcur[fi].x : wcur[fi].z;
+                lv[fi] = T[((ib >> (8 * (cc & 3))) & 0xFFu) * IQ2_REPL + rl];
             }
-            // refill the weight ring for K-chunk kc + PF
+            half8 b[GU_NF];
 #pragma unroll
-            for (int fi = 0; fi < 4; ++fi) wr[sl][fi] = (kc + PF < nkc) ? wq[fi][kc + PF] : make_uint2(0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i < nt) {
-                    const half8 a = as_half8(stage_get(cur, i, rl, grp));
-#pragma unroll
-                    for (int fi = 0; fi < 4; ++fi) blk[i][fi] = mfma_f16(a, b[fi], cc == 0 ? zf : blk[i][fi]);
+            for (int fi = 0; fi < GU_NF; ++fi) {
+                const uint32_t sw = (cc < 4) ? wcur[fi].y : wcur[fi].w;
+                if ((cc & 3) == 0) {
+                    const _Float16 s = (_Float16)(half_to_f32(dcur[fi]) * (0.015625f * (float)(2u * (sw >> 28) + 1u)));
+                    scl[fi] = half2v{s, s};
                 }
+                const uint4 sg = iq2_apply_signs(lv[fi], (sw >> (7 * (cc & 3))) & 0x7Fu);
+                b[fi] = as_half8(sg) * __builtin_shufflevector(scl[fi], scl[fi], 0, 1, 0, 1, 0, 1, 0, 1);
             }
-            // stage K-chunk kc + 1 (loaded PF - 1 chunks ago) into the other buffer
-            const int sn = (cc + 1) & (PF - 1);
-            if (kc + 1 < nkc) {
-                stage_put(stg[(kc + 1) & 1], tid, xv[sn]);
-                xv[sn] = (xrow && kc + 1 + PF < nkc) ? *reinterpret_cast<const uint4 *>(xrow + 32 * (kc + 1 + PF)) : z4;
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const half8 a = block_a(cur, i, cc, rl, grp);
+#pragma unroll
+                for (int fi = 0; fi < GU_NF; ++fi) acc[i][fi] = mfma_f16(a, b[fi], acc[i][fi]);
             }
-            __syncthreads();
         }
+        if (more) {
+            ld.store((bi & 1) ? stg0 : stg1, xr);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (i < nt)
-#pragma unroll
-                for (int fi = 0; fi < 4; ++fi) acc[i][fi] += dsc[fi] * blk[i][fi];
+            for (int fi = 0; fi < GU_NF; ++fi) wcur[fi] = wnext[fi], dcur[fi] = dnext[fi];
+        }
+        __syncthreads();
     }
 
-    // epilogue: h = silu(gate) * up -> fp16 slot rows; per-16-row sums for the Q2_K min term
-    const int FS = F / 16;
+    // epilogue: h = silu(gate) * up -> fp16 slot rows
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (i >= nt) continue;
+    for (int i = 0; i < NT; ++i) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int tt = 16 * i + 4 * grp + v;
-            const int q = (tt < cnt) ? W.list[beg + tt] : -1;
+            if (tt >= cnt) continue;
+            const int q = W.list[beg + tt];
 #pragma unroll
-            for (int fp = 0; fp < 2; ++fp) {
-                const float h = silu(acc[i][fp][v]) * acc[i][fp + 2][v];
-                const uint16_t hb = f16_bits(h);
-                const float hs = row16_sum(half_to_f32(hb));
-                const int f = f0 + 16 * fp;
-                if (q >= 0) {
-                    W.hbuf16[(int64_t)q * F + f + rl] = hb;
-                    if (rl == 0) W.hsum[(int64_t)q * FS + f / 16] = f16_bits(hs);
-                }
+            for (int fp = 0; fp < GU_FR; ++fp) {
+                const float h = silu(acc[i][fp][v]) * acc[i][fp + GU_FR][v];
+                W.hbuf16[(int64_t)q * F + f0 + 16 * fp + rl] = f16_bits(h);
             }
         }
     }
 }
 
-// ---------------------------------------------------------------- routed down + weighted scatter
+// grid: (n_ff / RGU_ROWS, max chunks), RB_THREADS threads.  Wave w covers
+// n_ff rows f0..f0+16 GU_FR-1 of gate and up for all tokens of the chunk
+// (1..4 token tiles), over the whole n_embd.
+__global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_gateup_routed(Layer L, Work W) {
+    const int c = blockIdx.y;
+    if (c >= *W.nchunks) return;
+    const int4 ch = W.chunks[c];
+    const int e = ch.x, beg = ch.y, cnt = ch.z;
+    __shared__ uint4 T[256 * IQ2_REPL];
+    __shared__ __align__(16) uint8_t stg[2][RB_STAGE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rl = lane & 15, grp = lane >> 4;
+    const int E = L.n_embd, F = L.n_ff, k = L.top_k, nbe = L.nbe;
+
+    BlockLoader ld;
+    {
+        const int sr = tid / LD_PER_ROW;
+        ld.init(sr < cnt ? W.x16 + (int64_t)(W.list[beg + sr] / k) * E : nullptr, tid);
+    }
+    const int f0 = blockIdx.x * RGU_ROWS + wave * 16 * GU_FR;
+    // fragment fi: matrix fi / GU_FR (gate, up), rows f0 + 16 (fi % GU_FR) + rl
+    const int64_t rb = ((int64_t)e * F + f0 + rl) * nbe;
+    const uint8_t *qg = L.iq2_qs[0] + rb * 64 + 16 * grp;  // + 64 bi (up: + iq2_qs[1] - iq2_qs[0])
+    const uint16_t *dg = L.iq2_d[0] + rb;                  // + bi
+    const int fq = 16 * nbe * 64, fd = 16 * nbe;
+    uint4 xr[LD_V];
+    ld.load(0, xr);
+    iq2_build_lut<true>(T, L.codebook, tid, RB_THREADS);
+    ld.store(stg[0], xr);
+    __syncthreads();
+    switch ((cnt + 15) >> 4) {
+        case 1: gateup_routed_tiles<1>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp); break;
+        case 2: gateup_routed_tiles<2>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp); break;
+        case 3: gateup_routed_tiles<3>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp); break;
+        default: gateup_routed_tiles<4>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp); break;
+    }
+}
+
 // Q2_K B decode: a table of the four 2-bit values of each qs byte as fp16
 // (8 bytes per entry), 16 replicas interleaved per entry; lane l reads replica l % 16.
 constexpr int QT_REPL = 16;
@@ -272,129 +306,91 @@ __device__ __forceinline__ void q2k_build_table(uint2 *QT, int tid, int nthreads
     }
 }
 
-// grid: (n_embd / DN_ROWS, max chunks).  Wave w covers n_embd rows
-// r0..r0+63 (4 B fragments) for all tokens of the chunk, over the whole n_ff.
-__global__ __launch_bounds__(256, 2) void k_gemm_down_routed(Layer L, Work W, float *__restrict__ out) {
-    const int c = blockIdx.y;
-    if (c >= *W.nchunks) return;
-    const int4 ch = W.chunks[c];
-    const int e = ch.x, beg = ch.y, cnt = ch.z;
-    __shared__ uint2 QT[256 * QT_REPL];
-    __shared__ __align__(16) uint8_t stg[2][STG_BYTES];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rl = lane & 15, grp = lane >> 4;
-    const int E = L.n_embd, F = L.n_ff, nbf = L.nbf;
-    const int nt = (cnt + 15) >> 4;
-    const int nkc = F / 32, FS = F / 16;
-
-    const int sr = tid >> 2;
-    const uint16_t *hrow = nullptr;
-    if (sr < cnt) hrow = W.hbuf16 + (int64_t)W.list[beg + sr] * F + 8 * (tid & 3);
-    // A rows of the min-term MFMA: token 16 i + rl of each tile
-    const uint16_t *hs[4];
+template <int NT>
+__device__ __forceinline__ void down_routed_tiles(const Layer &L, const Work &W, float *__restrict__ out,
+                                                  const uint2 *QT, uint8_t *stg0, uint8_t *stg1, const BlockLoader &ld,
+                                                  uint4 (&xr)[LD_V], const uint8_t *qb, const uint8_t *sb,
+                                                  const uint32_t *db, int fq, int fs, int fd, bool active, int r0,
+                                                  int beg, int cnt, int rl, int grp) {
+    const int E = L.n_embd, nbf = L.nbf;
+    uint4 qcur[DN_NF], qnext[DN_NF];
+    uint32_t scur[DN_NF], snext[DN_NF], dcur[DN_NF], dnext[DN_NF];
+    if (active)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int tt = 16 * i + rl;
-        hs[i] = (tt < cnt) ? W.hsum + (int64_t)W.list[beg + tt] * FS + 4 * grp : nullptr;
-    }
+        for (int fi = 0; fi < DN_NF; ++fi) {
+            qcur[fi] = *reinterpret_cast<const uint4 *>(qb + fi * fq);
+            scur[fi] = *reinterpret_cast<const uint32_t *>(sb + fi * fs);
+            dcur[fi] = db[fi * fd];
+        }
 
-    const int r0 = blockIdx.x * DN_ROWS + wave * 64;
-    const uint16_t *wq[4];
-    const uint4 *wsc[4];
-    const uint32_t *wdd[4];
-#pragma unroll
-    for (int fi = 0; fi < 4; ++fi) {
-        const int64_t rb = ((int64_t)e * E + r0 + 16 * fi + rl) * nbf;
-        wq[fi] = reinterpret_cast<const uint16_t *>(L.q2k_qs + rb * 64) + grp;  // K-chunk kc: wq[fi][4 kc]
-        wsc[fi] = reinterpret_cast<const uint4 *>(L.q2k_sc + rb * 16);
-        wdd[fi] = L.q2k_dd + rb;
-    }
-
-    uint4 xv[PF];
-    uint16_t wr[PF][4];
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int s = 0; s < PF; ++s) {
-        xv[s] = (hrow && s < nkc) ? *reinterpret_cast<const uint4 *>(hrow + 32 * s) : z4;
-#pragma unroll
-        for (int fi = 0; fi < 4; ++fi) wr[s][fi] = (s < nkc) ? wq[fi][4 * s] : (uint16_t)0;
-    }
-    q2k_build_table(QT, tid, 256);
-    stage_put(stg[0], tid, xv[0]);
-    xv[0] = (hrow && PF < nkc) ? *reinterpret_cast<const uint4 *>(hrow + 32 * PF) : z4;
-    __syncthreads();
-
-    floatx4 acc[4][4], blk[4][4];
+    floatx4 acc[NT][DN_NF];
     const floatx4 zf = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int fi = 0; fi < 4; ++fi) acc[i][fi] = zf, blk[i][fi] = zf;
+        for (int fi = 0; fi < DN_NF; ++fi) acc[i][fi] = zf;
 
     for (int bi = 0; bi < nbf; ++bi) {
-        uint4 scv[4];
-        uint32_t ddv[4];
+        const bool more = bi + 1 < nbf;
+        if (more) {
+            ld.load(bi + 1, xr);
+            if (active)
 #pragma unroll
-        for (int fi = 0; fi < 4; ++fi) scv[fi] = wsc[fi][bi], ddv[fi] = wdd[fi][bi];
-        uint2 hsv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hsv[i] = hs[i] ? *reinterpret_cast<const uint2 *>(hs[i] + 16 * bi) : make_uint2(0, 0);
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-            const int kc = bi * 8 + cc;
-            const int sl = cc & (PF - 1);
-            const uint8_t *cur = stg[kc & 1];
-            half8 b[4];
-#pragma unroll
-            for (int fi = 0; fi < 4; ++fi) {
-                const uint32_t qq = wr[sl][fi];
-                const uint2 lo = QT[(qq & 0xFFu) * QT_REPL + rl], hi = QT[(qq >> 8) * QT_REPL + rl];
-                // scale nibble of the 16-weight sub-block: byte 2 cc + grp / 2 of the block's scales
-                const uint32_t scw = (cc < 2) ? scv[fi].x : (cc < 4) ? scv[fi].y : (cc < 6) ? scv[fi].z : scv[fi].w;
-                const uint32_t scb = (scw >> (16 * (cc & 1) + 8 * (grp >> 1))) & 0xFu;
-                b[fi] = as_half8(make_uint4(lo.x, lo.y, hi.x, hi.y)) * (_Float16)(float)scb;
-            }
-#pragma unroll
-            for (int fi = 0; fi < 4; ++fi) wr[sl][fi] = (kc + PF < nkc) ? wq[fi][4 * (kc + PF)] : (uint16_t)0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i < nt) {
-                    const half8 a = as_half8(stage_get(cur, i, rl, grp));
-#pragma unroll
-                    for (int fi = 0; fi < 4; ++fi) blk[i][fi] = mfma_f16(a, b[fi], cc == 0 ? zf : blk[i][fi]);
+                for (int fi = 0; fi < DN_NF; ++fi) {
+                    qnext[fi] = *reinterpret_cast<const uint4 *>(qb + fi * fq + 64 * (bi + 1));
+                    snext[fi] = *reinterpret_cast<const uint32_t *>(sb + fi * fs + 16 * (bi + 1));
+                    dnext[fi] = db[fi * fd + bi + 1];
                 }
-            }
-            const int sn = (cc + 1) & (PF - 1);
-            if (kc + 1 < nkc) {
-                stage_put(stg[(kc + 1) & 1], tid, xv[sn]);
-                xv[sn] = (hrow && kc + 1 + PF < nkc) ? *reinterpret_cast<const uint4 *>(hrow + 32 * (kc + 1 + PF)) : z4;
-            }
-            __syncthreads();
         }
-        // min term: sum over the block's 16 sub-blocks of m_s * hsum_s (16x16x16 MFMA, K = sub-blocks)
+        if (active) {
+            const uint8_t *cur = (bi & 1) ? stg1 : stg0;
+            half8 dsc[DN_NF], msc[DN_NF];
 #pragma unroll
-        for (int fi = 0; fi < 4; ++fi) {
-            const uint32_t mw = (grp == 0) ? scv[fi].x : (grp == 1) ? scv[fi].y : (grp == 2) ? scv[fi].z : scv[fi].w;
-            half4 bm;
+            for (int cc = 0; cc < 8; ++cc) {
+                uint2 lo[DN_NF], hi[DN_NF];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bm[j] = (_Float16)(float)((mw >> (8 * j + 4)) & 0xFu);
-            const float d = half_to_f32((uint16_t)(ddv[fi] & 0xFFFFu));
-            const float dmin = half_to_f32((uint16_t)(ddv[fi] >> 16));
+                for (int fi = 0; fi < DN_NF; ++fi) {
+                    const uint32_t dw = (cc < 2) ? qcur[fi].x : (cc < 4) ? qcur[fi].y : (cc < 6) ? qcur[fi].z : qcur[fi].w;
+                    const int sh = 16 * (cc & 1);
+                    lo[fi] = QT[((dw >> sh) & 0xFFu) * QT_REPL + rl];
+                    hi[fi] = QT[((dw >> (sh + 8)) & 0xFFu) * QT_REPL + rl];
+                }
+                half8 b[DN_NF];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i < nt) {
-                    const half4 am = __builtin_bit_cast(half4, hsv[i]);
-                    const floatx4 mn = __builtin_amdgcn_mfma_f32_16x16x16f16(am, bm, zf, 0, 0, 0);
-                    acc[i][fi] += d * blk[i][fi] - dmin * mn;
+                for (int fi = 0; fi < DN_NF; ++fi) {
+                    if ((cc & 1) == 0) {
+                        // sub-block 4 grp + cc / 2: scale and min nibbles of its scale byte
+                        const uint32_t sb8 = (scur[fi] >> (8 * (cc >> 1))) & 0xFFu;
+                        const float d = half_to_f32((uint16_t)(dcur[fi] & 0xFFFFu));
+                        const float dmin = half_to_f32((uint16_t)(dcur[fi] >> 16));
+                        const _Float16 ds = (_Float16)(d * (float)(sb8 & 0xFu));
+                        const _Float16 ms = (_Float16)(-dmin * (float)(sb8 >> 4));
+                        dsc[fi] = half8{ds, ds, ds, ds, ds, ds, ds, ds};
+                        msc[fi] = half8{ms, ms, ms, ms, ms, ms, ms, ms};
+                    }
+                    const half8 qv = as_half8(make_uint4(lo[fi].x, lo[fi].y, hi[fi].x, hi[fi].y));
+                    b[fi] = __builtin_elementwise_fma(qv, dsc[fi], msc[fi]);
+                }
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    const half8 a = block_a(cur, i, cc, rl, grp);
+#pragma unroll
+                    for (int fi = 0; fi < DN_NF; ++fi) acc[i][fi] = mfma_f16(a, b[fi], acc[i][fi]);
                 }
             }
         }
+        if (more) {
+            ld.store((bi & 1) ? stg0 : stg1, xr);
+#pragma unroll
+            for (int fi = 0; fi < DN_NF; ++fi) qcur[fi] = qnext[fi], scur[fi] = snext[fi], dcur[fi] = dnext[fi];
+        }
+        __syncthreads();
     }
+    if (!active) return;
 
     // epilogue: out[token][row] += w * y
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (i >= nt) continue;
+    for (int i = 0; i < NT; ++i) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int tt = 16 * i + 4 * grp + v;
@@ -403,8 +399,48 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_routed(Layer L, Work W, fl
             const float wgt = W.w[q];
             float *orow = out + (int64_t)(q / L.top_k) * E + r0 + rl;
 #pragma unroll
-            for (int fi = 0; fi < 4; ++fi) atomicAdd(orow + 16 * fi, wgt * acc[i][fi][v]);
+            for (int fi = 0; fi < DN_NF; ++fi) atomicAdd(orow + 16 * fi, wgt * acc[i][fi][v]);
         }
+    }
+}
+
+// grid: (ceil(n_embd / RDN_ROWS), max chunks), RB_THREADS threads.  Wave w
+// covers n_embd rows r0..r0+16 DN_NF-1 for all tokens of the chunk over the
+// whole n_ff; waves whose rows lie past n_embd only help with the staging.
+__global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_down_routed(Layer L, Work W, float *__restrict__ out) {
+    const int c = blockIdx.y;
+    if (c >= *W.nchunks) return;
+    const int4 ch = W.chunks[c];
+    const int e = ch.x, beg = ch.y, cnt = ch.z;
+    __shared__ uint2 QT[256 * QT_REPL];
+    __shared__ __align__(16) uint8_t stg[2][RB_STAGE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rl = lane & 15, grp = lane >> 4;
+    const int E = L.n_embd, F = L.n_ff, nbf = L.nbf;
+
+    BlockLoader ld;
+    {
+        const int sr = tid / LD_PER_ROW;
+        ld.init(sr < cnt ? W.hbuf16 + (int64_t)W.list[beg + sr] * F : nullptr, tid);
+    }
+    const int r0 = blockIdx.x * RDN_ROWS + wave * 16 * DN_NF;
+    const bool active = r0 < E;
+    // fragment fi = rows r0 + 16 fi + rl; one base per plane, fragments 16 rows apart
+    const int64_t rb = ((int64_t)e * E + (active ? r0 + rl : 0)) * nbf;
+    const uint8_t *qb = L.q2k_qs + rb * 64 + 16 * grp;   // + fi * fq + 64 bi
+    const uint8_t *sb = L.q2k_sc + rb * 16 + 4 * grp;    // + fi * fs + 16 bi
+    const uint32_t *db = L.q2k_dd + rb;                  // + fi * fd + bi
+    const int fq = 16 * nbf * 64, fs = 16 * nbf * 16, fd = 16 * nbf;
+    uint4 xr[LD_V];
+    ld.load(0, xr);
+    q2k_build_table(QT, tid, RB_THREADS);
+    ld.store(stg[0], xr);
+    __syncthreads();
+    switch ((cnt + 15) >> 4) {
+        case 1: down_routed_tiles<1>(L, W, out, QT, stg[0], stg[1], ld, xr, qb, sb, db, fq, fs, fd, active, r0, beg, cnt, rl, grp); break;
+        case 2: down_routed_tiles<2>(L, W, out, QT, stg[0], stg[1], ld, xr, qb, sb, db, fq, fs, fd, active, r0, beg, cnt, rl, grp); break;
+        case 3: down_routed_tiles<3>(L, W, out, QT, stg[0], stg[1], ld, xr, qb, sb, db, fq, fs, fd, active, r0, beg, cnt, rl, grp); break;
+        default: down_routed_tiles<4>(L, W, out, QT, stg[0], stg[1], ld, xr, qb, sb, db, fq, fs, fd, active, r0, beg, cnt, rl, grp); break;
     }
 }
 
@@ -603,34 +639,43 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_shared(Layer L, Work W, in
 }
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_gemm_gateup(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s) {
+hipError_t launch_gemm_prep(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s) {
     const int64_t nx = (int64_t)n_tok * L.n_embd;
     const int pg = (int)std::min<int64_t>((nx + 255) / 256, 4096);
-    const bool xb = L.act_dtype == 1;
-    if (xb)
+    if (L.act_dtype == 1)
         hipLaunchKernelGGL(k_prep_x<true>, dim3(pg), dim3(256), 0, s, x, nx, W.x16, nullptr, nullptr);
     else
         hipLaunchKernelGGL(k_prep_x<false>, dim3(pg), dim3(256), 0, s, x, nx, W.x16, W.xhi, W.xlo);
     hipLaunchKernelGGL(k_build_chunks, dim3(1), dim3(256), 0, s, L.n_expert, W);
-    const int mc = gemm_max_chunks(n_tok, L.n_expert, L.top_k);
-    hipLaunchKernelGGL(k_gemm_gateup_routed, dim3(L.n_ff / GU_ROWS, mc), dim3(256), 0, s, L, W);
-    if (L.n_shared) {
-        const uint16_t *xh = xb ? static_cast<const uint16_t *>(x) : W.xhi;
-        const dim3 g(L.n_ff / GU_ROWS, (n_tok + CH_TOK - 1) / CH_TOK);
-        if (xb)
-            hipLaunchKernelGGL(k_gemm_gateup_shared<false>, g, dim3(256), 0, s, L, W, xh, nullptr, n_tok);
-        else
-            hipLaunchKernelGGL(k_gemm_gateup_shared<true>, g, dim3(256), 0, s, L, W, xh, W.xlo, n_tok);
-    }
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_down(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s) {
+hipError_t launch_gemm_gateup_routed(const Layer &L, const Work &W, int n_tok, hipStream_t s) {
     const int mc = gemm_max_chunks(n_tok, L.n_expert, L.top_k);
-    hipLaunchKernelGGL(k_gemm_down_routed, dim3(L.n_embd / DN_ROWS, mc), dim3(256), 0, s, L, W, out);
-    if (L.n_shared)
-        hipLaunchKernelGGL(k_gemm_down_shared, dim3(L.n_embd / DN_ROWS, (n_tok + CH_TOK - 1) / CH_TOK), dim3(256), 0, s,
-                           L, W, n_tok, out);
+    hipLaunchKernelGGL(k_gemm_gateup_routed, dim3(L.n_ff / RGU_ROWS, mc), dim3(RB_THREADS), 0, s, L, W);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_gateup_shared(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s) {
+    const dim3 g(L.n_ff / GU_ROWS, (n_tok + CH_TOK - 1) / CH_TOK);
+    if (L.act_dtype == 1)
+        hipLaunchKernelGGL(k_gemm_gateup_shared<false>, g, dim3(256), 0, s, L, W, static_cast<const uint16_t *>(x),
+                           nullptr, n_tok);
+    else
+        hipLaunchKernelGGL(k_gemm_gateup_shared<true>, g, dim3(256), 0, s, L, W, W.xhi, W.xlo, n_tok);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_down_routed(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s) {
+    const int mc = gemm_max_chunks(n_tok, L.n_expert, L.top_k);
+    hipLaunchKernelGGL(k_gemm_down_routed, dim3((L.n_embd + RDN_ROWS - 1) / RDN_ROWS, mc), dim3(RB_THREADS), 0, s, L, W,
+                       out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_down_shared(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s) {
+    hipLaunchKernelGGL(k_gemm_down_shared, dim3(L.n_embd / DN_ROWS, (n_tok + CH_TOK - 1) / CH_TOK), dim3(256), 0, s,
+                       L, W, n_tok, out);
     return hipGetLastError();
 }
 

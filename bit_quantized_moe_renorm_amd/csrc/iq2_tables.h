@@ -55,10 +55,9 @@ __device__ __forceinline__ uint32_t rotr(uint32_t v) {
     return r;
 }
 
-// Signed levels of one group: idx = codebook index, s7 = stored sign bits of
-// weights 0..6.  Returns 4 dwords of packed pairs (w0|w1, w2|w3, w4|w5, w6|w7).
-__device__ __forceinline__ uint4 iq2_group_levels(const uint4 *T, uint32_t idx, uint32_t s7, int rep) {
-    uint4 L = T[idx * IQ2_REPL + rep];
+// Apply the signs of one group to its unsigned levels L (4 dwords of packed
+// pairs w0|w1 .. w6|w7): s7 = stored sign bits of weights 0..6.
+__device__ __forceinline__ uint4 iq2_apply_signs(uint4 L, uint32_t s7) {
     // 8th sign: the group holds an even number of negatives (bit 7 = parity;
     // bits 8-9 receive the rest of the count and are never selected below)
     const uint32_t s8 = s7 | (__builtin_popcount(s7) << 7);
@@ -73,6 +72,12 @@ __device__ __forceinline__ uint4 iq2_group_levels(const uint4 *T, uint32_t idx, 
     L.z ^= rotr<21>(S) & M;
     L.w ^= rotr<23>(S) & M;
     return L;
+}
+
+// Signed levels of one group: idx = codebook index, s7 = stored sign bits of
+// weights 0..6.  Returns 4 dwords of packed pairs (w0|w1, w2|w3, w4|w5, w6|w7).
+__device__ __forceinline__ uint4 iq2_group_levels(const uint4 *T, uint32_t idx, uint32_t s7, int rep) {
+    return iq2_apply_signs(T[idx * IQ2_REPL + rep], s7);
 }
 
 }  // namespace ds4

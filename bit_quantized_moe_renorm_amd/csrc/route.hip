@@ -184,32 +184,59 @@ __global__ __launch_bounds__(256) void k_topk(int n_tok, int NE, int k, Work W) 
 }
 
 // Per-expert token lists for any n_tok, by one workgroup of 1024 threads:
-// a histogram gives the offsets; each chunk of 2048 tokens is marked in a
-// per-expert bitmap, and each expert's set bits are emitted in ascending order.
+// a histogram and a scan give the offsets and the active experts; each chunk
+// of 2048 tokens is marked in a per-expert bitmap (with the chunk's expert
+// indices staged in LDS), and each expert's set bits are emitted in ascending
+// token order as list entries t*k + j.
 constexpr int BK_CHUNK = 2048;
 constexpr int BK_WORDS = BK_CHUNK / 32;
+
+// Exclusive prefix sum over the first 256 threads (4 waves) of the workgroup;
+// every thread of the workgroup gets the total.  Uses wtot[4] of LDS.
+__device__ __forceinline__ int scan256(int v, int tid, int *wtot, int &total) {
+    const int lane = tid & 63, wave = tid >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (tid < 256 && lane == 63) wtot[wave] = x;
+    __syncthreads();
+    int pre = 0;
+    for (int w = 0; w < wave && w < 4; ++w) pre += wtot[w];
+    total = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    __syncthreads();
+    return pre + x - v;
+}
+
 __global__ __launch_bounds__(1024) void k_bucket(int n_tok, int NE, int k, Work W) {
     __shared__ uint32_t bitmap[MAX_EXPERT * BK_WORDS];  // 64 KB
-    __shared__ int cnt[MAX_EXPERT + 1];
+    __shared__ uint8_t eidx[BK_CHUNK * MAX_TOPK];       // 16 KB: expert of every slot of the chunk
+    __shared__ int cnt[MAX_EXPERT];
     __shared__ int base[MAX_EXPERT];
     __shared__ int part[MAX_EXPERT * 4];
+    __shared__ int wtot[4];
     const int tid = threadIdx.x;
     const int nq = n_tok * k;
-    for (int e = tid; e < NE; e += 1024) cnt[e] = 0;
+    for (int e = tid; e < MAX_EXPERT; e += 1024) cnt[e] = 0;
     __syncthreads();
     for (int q = tid; q < nq; q += 1024) atomicAdd(&cnt[W.idx[q]], 1);
     __syncthreads();
-    if (tid == 0) {
-        int run = 0, u = 0;
-        for (int e = 0; e < NE; ++e) {
-            int c = cnt[e];
-            base[e] = run;
-            W.offsets[e] = run;
-            if (c) W.active[1 + u++] = e;
-            run += c;
+    {
+        const int c = (tid < NE) ? cnt[tid] : 0;
+        int total, nact;
+        const int off = scan256(c, tid, wtot, total);
+        const int apos = scan256(c > 0 ? 1 : 0, tid, wtot, nact);
+        if (tid < NE) {
+            base[tid] = off;
+            W.offsets[tid] = off;
+            if (c > 0) W.active[1 + apos] = tid;
         }
-        W.offsets[NE] = run;
-        W.active[0] = u;
+        if (tid == 0) {
+            W.offsets[NE] = total;
+            W.active[0] = nact;
+        }
     }
     __syncthreads();
     for (int c0 = 0; c0 < n_tok; c0 += BK_CHUNK) {
@@ -217,8 +244,10 @@ __global__ __launch_bounds__(1024) void k_bucket(int n_tok, int NE, int k, Work 
         for (int i = tid; i < NE * BK_WORDS; i += 1024) bitmap[i] = 0u;
         __syncthreads();
         for (int q = c0 * k + tid; q < c1 * k; q += 1024) {
-            int t = q / k - c0;
-            atomicOr(&bitmap[W.idx[q] * BK_WORDS + (t >> 5)], 1u << (t & 31));
+            const int e = W.idx[q];
+            const int t = q / k - c0;
+            eidx[q - c0 * k] = (uint8_t)e;
+            atomicOr(&bitmap[e * BK_WORDS + (t >> 5)], 1u << (t & 31));
         }
         __syncthreads();
         // 4 threads per expert row, 16 words each
@@ -235,13 +264,13 @@ __global__ __launch_bounds__(1024) void k_bucket(int n_tok, int NE, int k, Work 
                 const int word = pr * (BK_WORDS / 4) + wd;
                 uint32_t bits = bitmap[e * BK_WORDS + word];
                 while (bits) {
-                    int b = __ffs(bits) - 1;
+                    const int b = __ffs(bits) - 1;
                     bits &= bits - 1;
-                    int t = c0 + word * 32 + b;
+                    const int tl = word * 32 + b;
                     int j = 0;
                     for (int jj = 0; jj < k; ++jj)
-                        if (W.idx[(int64_t)t * k + jj] == e) j = jj;
-                    W.list[pos++] = t * k + j;
+                        if (eidx[tl * k + jj] == (uint8_t)e) j = jj;
+                    W.list[pos++] = (c0 + tl) * k + j;
                 }
             }
         }
@@ -251,8 +280,246 @@ __global__ __launch_bounds__(1024) void k_bucket(int n_tok, int NE, int k, Work 
     }
 }
 
+// ---------------------------------------------------------------- batched router
+// For many tokens the router runs as an estimate plus an exact recomputation:
+//  1. estimate: the fp32 router is split once into bf16 parts hi + mid + lo
+//     and the logits are accumulated by bf16 MFMAs (products exact, fp32 sums
+//     over 256-K chunks, chunk sums in fp64).  Each MFMA adds at most 32
+//     roundings of at most 2^-23 relative to its running magnitude, 24 MFMAs
+//     per chunk, so |estimate - exact| <= 800 * 2^-23 * sum_i |x_i| |w_i| (1 + 2^-7)
+//     <= RT_BOUND * ||x|| * ||w_e|| (Cauchy-Schwarz), plus an absolute 1e-30
+//     for flushed subnormal products.
+//  2. per token, the k-th largest lower bound theta; every expert of the exact
+//     top-k has an upper bound >= theta minus a few fp32 ulps (fp32 rounding
+//     is monotone, and experts whose exact logits differ by more than an ulp
+//     keep their order), so only experts above that are candidates.
+//  3. the candidates' logits are recomputed in fp64 and rounded to fp32 exactly
+//     as the single-token path does, and the top-k and the renormalised
+//     weights are taken among them.
+constexpr double RT_BOUND = 1.0e-4;
+
+// One workgroup per expert: bf16 parts and the row norm (rounded up).
+__global__ __launch_bounds__(256) void k_router_prep(const float *__restrict__ R, int NE, int E,
+                                                     uint16_t *__restrict__ hml, float *__restrict__ norm) {
+    __shared__ double red[4];
+    const int e = blockIdx.x, tid = threadIdx.x;
+    double ss = 0.0;
+    for (int i = tid; i < E; i += 256) {
+        const float w = R[(int64_t)e * E + i];
+        const uint16_t hi = f32_to_bf16_rne(w);
+        const float r1 = w - bf16_to_f32(hi);
+        const uint16_t mid = f32_to_bf16_rne(r1);
+        const float r2 = r1 - bf16_to_f32(mid);
+        const uint16_t lo = f32_to_bf16_rne(r2);
+        hml[((int64_t)0 * NE + e) * E + i] = hi;
+        hml[((int64_t)1 * NE + e) * E + i] = mid;
+        hml[((int64_t)2 * NE + e) * E + i] = lo;
+        ss = fma((double)w, (double)w, ss);
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    if (tid == 0) norm[e] = (float)(sqrt(red[0] + red[1] + red[2] + red[3]) * (1.0 + 1e-6));
+}
+
+hipError_t launch_router_prep(const float *router, int NE, int E, uint16_t *hml, float *norm, hipStream_t s) {
+    hipLaunchKernelGGL(k_router_prep, dim3(NE), dim3(256), 0, s, router, NE, E, hml, norm);
+    return hipGetLastError();
+}
+
+typedef __bf16 rt_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float rt_floatx4 __attribute__((ext_vector_type(4)));
+
+// Estimates for 32 tokens x 64 experts per workgroup; wave w takes experts
+// 16 w..16 w+15 (B: lane l holds expert l % 16, K 8 (l / 16)..+8) and two
+// 16-token tiles (A: token l % 16 of the tile, the same K).
+__global__ __launch_bounds__(256) void k_route_approx(const uint16_t *__restrict__ hml, const uint16_t *__restrict__ x,
+                                                      int n_tok, int NE, int E, float *__restrict__ est) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rl = lane & 15, grp = lane >> 4;
+    const int e = blockIdx.x * 64 + wave * 16 + rl;
+    const int t0 = blockIdx.y * 32;
+    const bool eok = e < NE;
+    const uint16_t *wp[3];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) wp[p] = hml + ((int64_t)p * NE + (eok ? e : 0)) * E + 8 * grp;
+    const uint16_t *xp[2];
+    bool tok[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int t = t0 + 16 * i + rl;
+        tok[i] = t < n_tok;
+        xp[i] = x + (int64_t)(tok[i] ? t : 0) * E + 8 * grp;
+    }
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
+    double acc[2][4] = {};
+    for (int k0 = 0; k0 < E; k0 += QK) {
+        rt_floatx4 part[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s = 0; s < QK / 32; ++s) {
+            const int kk = k0 + 32 * s;
+            uint4 a[2], b[3];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[i] = tok[i] ? *reinterpret_cast<const uint4 *>(xp[i] + kk) : z4;
+#pragma unroll
+            for (int p = 0; p < 3; ++p) b[p] = eok ? *reinterpret_cast<const uint4 *>(wp[p] + kk) : z4;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    part[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(rt_bf16x8, a[i]),
+                                                                      __builtin_bit_cast(rt_bf16x8, b[p]), part[i], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][v] += (double)part[i][v];
+    }
+    // C layout: lane (rl, grp) holds tokens 4 grp + v of each tile for expert rl
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int t = t0 + 16 * i + 4 * grp + v;
+            if (t < n_tok && eok) est[(int64_t)t * NE + e] = (float)acc[i][v];
+        }
+}
+
+// One wavefront per token: bounds, candidates, exact fp64 logits of the
+// candidates, top-k and renormalised weights.  Lane l holds x at 4 l + 256 m.
+constexpr int RS_MAXV = 4096 / 64;   // x values per lane (n_embd <= 4096)
+__global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ R, const float *__restrict__ bias,
+                                                      const float *__restrict__ rnorm, const uint16_t *__restrict__ x,
+                                                      int n_tok, int NE, int E, int k, Work W) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= n_tok) return;
+    const int nm = E / 256;
+    float xv[RS_MAXV];
+    double ss = 0.0;
+#pragma unroll
+    for (int m = 0; m < RS_MAXV / 4; ++m) {
+        if (m < nm) {
+            const uint2 r = *reinterpret_cast<const uint2 *>(x + (int64_t)t * E + 256 * m + 4 * lane);
+            xv[4 * m + 0] = bf16_to_f32((uint16_t)(r.x & 0xFFFF));
+            xv[4 * m + 1] = bf16_to_f32((uint16_t)(r.x >> 16));
+            xv[4 * m + 2] = bf16_to_f32((uint16_t)(r.y & 0xFFFF));
+            xv[4 * m + 3] = bf16_to_f32((uint16_t)(r.y >> 16));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ss = fma((double)xv[4 * m + j], (double)xv[4 * m + j], ss);
+        }
+    }
+    const double xn = sqrt(wave_sum(ss)) * (1.0 + 1e-12);
+    // bounds of every expert (lane l: experts l + 64 i)
+    double lb[4], ub[4], bb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        if (e < NE) {
+            bb[i] = bias ? (double)bias[e] : 0.0;
+            const double a = (double)W.logits[(int64_t)t * NE + e] + bb[i];
+            const double del = RT_BOUND * xn * (double)rnorm[e] + 1e-30;
+            lb[i] = a - del;
+            ub[i] = a + del;
+        } else {
+            bb[i] = 0.0, lb[i] = -INFINITY, ub[i] = -INFINITY;
+        }
+    }
+    // theta = k-th largest lower bound
+    double theta = -INFINITY;
+    {
+        bool taken[4] = {false, false, false, false};
+        for (int j = 0; j < k; ++j) {
+            double best = -INFINITY;
+            int bi = -1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (!taken[i] && lb[i] > best) best = lb[i], bi = i;
+            double m = best;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off, 64));
+            theta = m;
+            // the lowest lane holding the maximum gives it up
+            const uint64_t holders = __ballot(bi >= 0 && best == m);
+            const int who = __ffsll((unsigned long long)holders) - 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (lane == who && bi == i) taken[i] = true;
+        }
+    }
+    const double cut = theta - (fabs(theta) * 0x1p-20 + 1e-30);
+    // exact logits of the candidates
+    uint64_t key[4];
+    float Lv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        key[i] = 0ull;
+        Lv[i] = 0.f;
+        uint64_t cm = __ballot(ub[i] >= cut);
+        while (cm) {
+            const int l = __ffsll((unsigned long long)cm) - 1;
+            cm &= cm - 1;
+            const int e = l + 64 * i;
+            const float *row = R + (int64_t)e * E + 4 * lane;
+            double s = 0.0;
+#pragma unroll
+            for (int m = 0; m < RS_MAXV / 4; ++m) {
+                if (m < nm) {
+                    const float4 r = *reinterpret_cast<const float4 *>(row + 256 * m);
+                    s = fma((double)xv[4 * m + 0], (double)r.x, s);
+                    s = fma((double)xv[4 * m + 1], (double)r.y, s);
+                    s = fma((double)xv[4 * m + 2], (double)r.z, s);
+                    s = fma((double)xv[4 * m + 3], (double)r.w, s);
+                }
+            }
+            s = wave_sum(s);
+            if (lane == l) {
+                Lv[i] = (float)(s + bb[i]);
+                key[i] = topk_key(Lv[i], e);
+            }
+        }
+    }
+    // top-k among the candidates, renormalised weights
+    float sel_L[MAX_TOPK];
+    int sel_e[MAX_TOPK];
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max_u64(best);
+        const int e = 0xFFFF - (int)(best & 0xFFFFu);
+        sel_e[j] = e;
+        float Le = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (lane + 64 * i == e) Le = Lv[i], key[i] = 0ull;
+        sel_L[j] = __shfl(Le, e & 63, 64);
+    }
+    if (lane < k) {
+        double m = (double)sel_L[0], z = 0.0, num = 0.0;
+        int e = 0;
+        for (int j = 0; j < k; ++j) {
+            const double ex = exp((double)sel_L[j] - m);
+            z += ex;
+            if (j == lane) num = ex, e = sel_e[j];
+        }
+        W.idx[(int64_t)t * k + lane] = e;
+        W.w[(int64_t)t * k + lane] = (float)(num / z);
+    }
+}
+
 hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s, hipEvent_t *ev) {
     const int NE = L.n_expert;
+    if (n_tok > ROUTE_SMALL_MAX && L.act_dtype == 1) {
+        // batched: MFMA estimates, exact candidates, lists
+        const uint16_t *xb = static_cast<const uint16_t *>(x);
+        hipLaunchKernelGGL(k_route_approx, dim3((NE + 63) / 64, (n_tok + 31) / 32), dim3(256), 0, s, L.router_hml, xb,
+                           n_tok, NE, L.n_embd, W.logits);
+        hipLaunchKernelGGL(k_route_select, dim3((n_tok + 3) / 4), dim3(256), 0, s, L.router, L.router_bias,
+                           L.router_norm, xb, n_tok, NE, L.n_embd, L.top_k, W);
+        hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, s, n_tok, NE, L.top_k, W);
+        return hipGetLastError();
+    }
     dim3 grid((NE + RT_WAVES - 1) / RT_WAVES, (n_tok + RT_TOK - 1) / RT_TOK);
     const int fuse = n_tok <= ROUTE_SMALL_MAX;
     if (L.act_dtype == 1)

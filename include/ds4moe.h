@@ -168,9 +168,12 @@ int ds4moe_rmsnorm(const float *h, int32_t n_tok, int32_t n_embd, double eps, ui
  * accumulated milliseconds and launch counts (after synchronising the stream)
  * with ds4moe_timing_read.  kinds: 0 route (logits, top-k, lists), 1 routed
  * gate/up GEMV, 2 shared gate/up GEMV, 3 routed down GEMV, 4 shared down GEMV,
- * 5 grouped gate/up GEMM, 6 grouped down GEMM, 7 fused decode kernel.  ms and
- * counts have room for 8 entries each.  Enabling resets the counters.
+ * 5 routed gate/up GEMM, 6 routed down GEMM, 7 fused decode kernel, 8 batched
+ * path preparation (activation copies, chunk table), 9 shared gate/up GEMM,
+ * 10 shared down GEMM.  ms and counts have room for DS4MOE_TIMING_KINDS
+ * entries each.  Enabling resets the counters.
  */
+#define DS4MOE_TIMING_KINDS 11
 int ds4moe_timing_enable(ds4moe_t *h, int32_t enable);
 int ds4moe_timing_read(ds4moe_t *h, double *ms, int64_t *counts);
 

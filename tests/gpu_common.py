@@ -31,6 +31,14 @@ def host_layer(kind: str):
         return synth.make_layer(synth.TINY, seed=0)
     if kind == "ds4":
         return synth.make_layer(synth.DS4, seed=1)
+    if kind == "ds4_ties":
+        # pairs of identical router rows (2j, 2j+1): every logit has an exact twin
+        base = host_layer("ds4")
+        lay = synth.Layer(**{**base.__dict__})
+        r = base.router.copy()
+        r[1::2] = r[0::2]
+        lay.router = r
+        return lay
     if kind == "ds4_zipf":
         base = host_layer("ds4")
         lay = synth.Layer(**{**base.__dict__})
