@@ -241,6 +241,19 @@ def run_prefill(args):
     return res
 
 
+def copy_probe():
+    """A plain device copy of known size, for calibrating the HBM byte counters
+    (FETCH_SIZE / WRITE_SIZE) that the profiles of the block's kernels use."""
+    import torch
+    n = 64 << 20                      # 64 Mi fp32 = 256 MiB each way
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": 4 * n, "launches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +263,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", choices=("decode", "prefill"), default="decode")
     ap.add_argument("--tokens", type=int, default=2048, help="prefill tokens per call")
+    ap.add_argument("--copy-probe", action="store_true", help="only run the counter-calibration copy")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X only: this build runs the MoE block on a single GPU "
@@ -259,6 +273,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.workload == "prefill":
         if args.steps == 1000 and args.warmup == 100:   # defaults sized for decode
             args.steps, args.warmup = 50, 5

@@ -58,6 +58,9 @@ struct Work {
     uint16_t *hsh_hi, *hsh_lo;  // [max_tokens][F] shared-expert activations, bf16 high / low parts
     int4 *chunks;         // [gemm_max_chunks] (expert, first list position, count)
     int32_t *nchunks;     // number of valid chunks
+    int32_t *ecount;      // [MAX_EXPERT] tokens per expert (batched router)
+    float *rest;          // [4][max_tokens][NE] partial router estimates (batched router)
+    double *rhalf;        // [NE][2] fp64 half-row router sums (fused decode)
 };
 
 // ---------------------------------------------------------------- small device helpers

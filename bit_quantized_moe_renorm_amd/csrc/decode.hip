@@ -3,16 +3,18 @@
 // Generation is bandwidth-bound ("ds4 深度实战...", section 5.1) and the pages
 // fuse MoE routing with the expert computation into one GPU dispatch (same
 // page, section 2.3).  Here one persistent launch walks a fixed list of work
-// items in five phases:
-//   P0 router    : logits of 4 experts per item (fp64 accumulation, one wave per
-//                  expert); the wave that completes the last expert also does
-//                  top-k and renormalisation, then publishes "route ready";
-//   P1 shared g/u: 4 rows of the shared expert's gate and up per item;
-//   P2 routed g/u: 16 rows of one selected expert's IQ2 gate and up per item,
-//                  SiLU(g)*u kept in fp32 (waits for "route ready");
-//   P3 shared dn : rows of the shared down projection (waits for P1);
-//   P4 routed dn : rows of one selected expert's Q2_K down projection, scaled
-//                  by its routing weight (waits for that expert's P2 items).
+// items in five phases, in this order:
+//   router    : half an expert's logit per item (fp64 accumulation); the wave
+//               that completes the last half also does top-k and
+//               renormalisation, then publishes "route ready";
+//   routed g/u: 16 rows of one selected expert's IQ2 gate and up per item,
+//               SiLU(g)*u kept in fp32 (waits for "route ready");
+//   shared g/u: 4 rows of the shared expert's gate and up per item;
+//   routed dn : rows of one selected expert's Q2_K down projection, scaled
+//               by its routing weight (waits for that expert's g/u items);
+//   shared dn : rows of the shared down projection (waits for shared g/u).
+// The router runs alone first, so its 4 MB do not share HBM with the 50 MB
+// shared expert, which streams while the routed experts are processed.
 // Items are dealt round-robin over the workgroups in phase order, and the grid
 // is sized to what the GPU holds at once, so every wait is on an item that a
 // resident workgroup took earlier and that never waits on a later one.  Each
@@ -27,8 +29,7 @@
 // Consumers poll the counter with agent-scope loads and then read the data
 // with plain loads: no workgroup touches those lines earlier in the launch and
 // caches are invalidated between launches, so no stale copy can be hit.  The
-// last workgroup to leave resets the counters for the next call.  P1 needs no
-// routing, so the 50 MB shared expert streams while the router resolves.
+// counters hold 64-bit epochs and never need resetting.
 // The block output (routed + shared) is added into the residual with fp32
 // atomics.
 #include "common.h"
@@ -59,6 +60,8 @@ __device__ __forceinline__ unsigned long long *ctr(const Work &W, int slot) {
 
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_THREADS = 64 * DEC_WAVES;
+constexpr int DEC_WG_PER_CU = 2;  // resident workgroups per CU
+constexpr int DEC_REPL = 4;       // level-table replicas (lane l reads replica l % 4)
 constexpr int DEC_GU_NR = 4;  // routed gate/up row slots per wave
 constexpr int DEC_DN_NR = 4;  // routed down row slots per wave
 
@@ -129,62 +132,78 @@ __device__ __forceinline__ bool wait_items(const Work &W, unsigned long long *c,
     return ok;
 }
 
-__device__ __forceinline__ uint64_t dec_key(float L, int e) {
-    uint32_t u = __float_as_uint(L);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)(0xFFFF - e);
-}
 
 // ---------------------------------------------------------------- P0: router
-// Top-k + renormalised weights + per-expert lists for the single token, then
-// "route ready".  Run by the one wavefront that completed the last logit; kept
-// out of line so its fp64 exp does not raise the register budget of the rest.
-__device__ __noinline__ void dec_topk_publish(const Layer &L, const Work &W) {
+// Each router item is half an expert row (the two halves land in separate
+// fp64 slots of W.hbuf's router area, so nothing has to be cleared between
+// calls).  The wavefront that completes the last half rounds every logit to
+// fp32, takes the top-k with its renormalised weights, publishes "route
+// ready", and only then writes the per-expert lists kept for ds4moe_route.
+// Wave-wide maximum of an unsigned key by DPP (row shifts, then the two row
+// broadcasts); the result is read from the last lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true));  // row_shr:1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true));  // row_shr:2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true));  // row_shr:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true));  // row_shr:8
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false)); // row_bcast:15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false)); // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ void dec_topk_publish(const Layer &L, const Work &W, const double *part) {
     const int lane = threadIdx.x & 63;
     const int NE = L.n_expert, k = L.top_k;
-    uint64_t key[4];
+    // fp32 logits as order-preserving keys (0 = no expert); lane l holds experts l + 64 i.
+    // The halves were stored by other workgroups with write-through stores and
+    // this workgroup has not read those lines before: plain loads are coherent.
+    uint32_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int ee = lane + 64 * i;
-        key[i] = (ee < NE) ? dec_key(ld_shared(W.logits + ee), ee) : 0ull;
+        key[i] = 0u;
+        if (ee < NE) {
+            const double2 hh = *reinterpret_cast<const double2 *>(part + 2 * ee);
+            const float Lf = (float)(hh.x + hh.y + (L.router_bias ? (double)L.router_bias[ee] : 0.0));
+            const uint32_t u = __float_as_uint(Lf);
+            key[i] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+            if (key[i] == 0u) key[i] = 1u;  // keep 0 free for "taken"
+        }
     }
-    float selL[MAX_TOPK];
-    int selE[MAX_TOPK];
+    // lane j < k ends up holding the j-th selection: the largest key, and among
+    // equal keys the lowest expert index (lowest i, then lowest lane)
+    int myE = 0;
+    float myL = 0.f;
 #pragma unroll
     for (int j = 0; j < MAX_TOPK; ++j) {
         if (j >= k) break;
-        uint64_t best = key[0];
+        const uint32_t m = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+        int ee = -1;
 #pragma unroll
-        for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            uint64_t o = __shfl_xor(best, off, 64);
-            best = o > best ? o : best;
+        for (int i = 3; i >= 0; --i) {
+            const uint64_t b = __ballot(key[i] == m);
+            if (b) ee = 64 * i + (__ffsll((unsigned long long)b) - 1);
         }
-        const int ee = 0xFFFF - (int)(best & 0xFFFFu);
-        uint32_t u = (uint32_t)(best >> 32);
-        u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
-        selE[j] = ee;
-        selL[j] = __uint_as_float(u);
+        const uint32_t u = (m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m;
+        if (lane == j) myE = ee, myL = __uint_as_float(u);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (lane + 64 * i == ee) key[i] = 0ull;
+            if (lane + 64 * i == ee) key[i] = 0u;
     }
+    // one exp per lane, the denominator by a sum over the k lanes
+    const float L0 = __shfl(myL, 0, 64);
+    const double ex = (lane < k) ? exp((double)myL - (double)L0) : 0.0;
+    const double z = wave_sum(ex);
     if (lane < k) {
-        const double m = (double)selL[0];
-        double z = 0.0, num = 0.0;
-        int me = 0;
-#pragma unroll
-        for (int j = 0; j < MAX_TOPK; ++j) {
-            if (j >= k) break;
-            const double ex = exp((double)selL[j] - m);
-            z += ex;
-            if (j == lane) num = ex, me = selE[j];
-        }
-        st_shared(W.idx + lane, me);
-        st_shared(W.w + lane, (float)(num / z));
+        st_shared(W.idx + lane, myE);
+        st_shared(W.w + lane, (float)(ex / z));
     }
-    // per-expert lists for the single token (kept for ds4moe_route's export)
+    stores_done();
+    if (lane == 0) __hip_atomic_fetch_add(ctr(W, C_READY), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // per-expert lists for the single token (read only by ds4moe_route's export)
+    int selE[MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK; ++j) selE[j] = (j < k) ? __shfl(myE, j, 64) : 0;
     for (int ee = lane; ee <= NE; ee += 64) {
         int before = 0;
 #pragma unroll
@@ -193,88 +212,56 @@ __device__ __noinline__ void dec_topk_publish(const Layer &L, const Work &W) {
         W.offsets[ee] = before;
     }
     if (lane == 0) W.active[0] = k;
+    if (lane < k) {
+        int rank = 0;
 #pragma unroll
-    for (int j = 0; j < MAX_TOPK; ++j) {
-        if (j < k && lane == j) {
-            int rank = 0;
-#pragma unroll
-            for (int i = 0; i < MAX_TOPK; ++i)
-                if (i < k) rank += selE[i] < selE[j];
-            W.active[1 + rank] = selE[j];
-            W.list[rank] = j;
-        }
+        for (int i = 0; i < MAX_TOPK; ++i)
+            if (i < k) rank += selE[i] < myE;
+        W.active[1 + rank] = myE;
+        W.list[rank] = lane;
     }
-    stores_done();
-    if (lane == 0) __hip_atomic_fetch_add(ctr(W, C_READY), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Half h of expert e's logit: waves split the half row (E/2 elements).
 template <bool XBF16>
-__device__ void dec_route_item(const Layer &L, const Work &W, const void *__restrict__ x, int e, int *lds_flag,
+__device__ void dec_route_item(const Layer &L, const Work &W, const void *__restrict__ x, int item, int *lds_flag,
                                double *lds_part, const DecPlan &P) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd;
-    // wave w covers elements [w*E/4, (w+1)*E/4): E/1024 steps of 256
-    const int steps = E >> 10;
+    const int e = item >> 1, h = item & 1;
+    double *part = W.rhalf;
+    const int half = E >> 1, per_wave = half >> 2;   // E/8 elements per wave
+    const int base = h * half + wave * per_wave;
     double acc = 0.0;
-    {
-        float4 r[4];
-        float4 xv[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if (c < steps) {
-                const int i = wave * (E >> 2) + 256 * c + 4 * lane;
-                r[c] = *reinterpret_cast<const float4 *>(L.router + (int64_t)e * E + i);
-                if (XBF16) {
-                    const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(x) + i);
-                    xv[c] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
-                                        __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
-                } else {
-                    xv[c] = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + i);
-                }
-            }
+    for (int i = 4 * lane; i < per_wave; i += 256) {
+        const float4 r = *reinterpret_cast<const float4 *>(L.router + (int64_t)e * E + base + i);
+        float4 xv;
+        if (XBF16) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(x) + base + i);
+            xv = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                             __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+        } else {
+            xv = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + base + i);
         }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if (c < steps) {
-                acc = fma((double)xv[c].x, (double)r[c].x, acc);
-                acc = fma((double)xv[c].y, (double)r[c].y, acc);
-                acc = fma((double)xv[c].z, (double)r[c].z, acc);
-                acc = fma((double)xv[c].w, (double)r[c].w, acc);
-            }
-        }
-        // E < 1024: wave 0 takes the whole row in 256-element steps
-        if (steps == 0 && wave == 0) {
-            for (int i = 4 * lane; i < E; i += 256) {
-                const float4 rr = *reinterpret_cast<const float4 *>(L.router + (int64_t)e * E + i);
-                float4 xx;
-                if (XBF16) {
-                    const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(x) + i);
-                    xx = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
-                                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
-                } else {
-                    xx = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + i);
-                }
-                acc = fma((double)xx.x, (double)rr.x, acc);
-                acc = fma((double)xx.y, (double)rr.y, acc);
-                acc = fma((double)xx.z, (double)rr.z, acc);
-                acc = fma((double)xx.w, (double)rr.w, acc);
-            }
-        }
+        acc = fma((double)xv.x, (double)r.x, acc);
+        acc = fma((double)xv.y, (double)r.y, acc);
+        acc = fma((double)xv.z, (double)r.z, acc);
+        acc = fma((double)xv.w, (double)r.w, acc);
     }
     acc = wave_sum(acc);
     if (lane == 0) lds_part[wave] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
-        const double s = lds_part[0] + lds_part[1] + lds_part[2] + lds_part[3];
-        st_shared(W.logits + e, (float)(s + (L.router_bias ? (double)L.router_bias[e] : 0.0)));
+        const double sum = lds_part[0] + lds_part[1] + lds_part[2] + lds_part[3];
+        __hip_atomic_store(part + 2 * e + h, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // count the expert; the workgroup that completes the last one does top-k
+    // count the half; the workgroup that completes the last one does top-k
     const unsigned long long prev = publish_item(ctr(W, C_ROUTE));
     if (threadIdx.x == 0) *lds_flag = (prev == (P.ep + 1) * (unsigned long long)P.n_route - 1ull);
     __syncthreads();
     const int last = *lds_flag;
     __syncthreads();
-    if (last && wave == 0) dec_topk_publish(L, W);
+    if (last && wave == 0) dec_topk_publish(L, W, part);
 }
 
 // ---------------------------------------------------------------- P1: shared gate/up
@@ -331,50 +318,40 @@ __device__ void dec_shgu_item(const Layer &L, const Work &W, const void *__restr
 }
 
 // ---------------------------------------------------------------- P2: routed gate/up (IQ2)
+// The token's x, staged once per workgroup in LDS (bf16 or fp32 as given);
+// a routed gate/up lane reads the 8 values of one group at a time.
 template <bool XBF16>
 struct DecX;
 template <>
 struct DecX<true> {
-    uint32_t v[32];
-    __device__ __forceinline__ void load(const void *x, int off) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + off);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint4 r = p[i];
-            v[4 * i] = r.x, v[4 * i + 1] = r.y, v[4 * i + 2] = r.z, v[4 * i + 3] = r.w;
-        }
-    }
-    __device__ __forceinline__ float dot8(const uint4 &Lv, int o, float s) const {
-        s = dec_dot2(Lv.x, v[o], s);
-        s = dec_dot2(Lv.y, v[o + 1], s);
-        s = dec_dot2(Lv.z, v[o + 2], s);
-        s = dec_dot2(Lv.w, v[o + 3], s);
+    const uint4 *xs;   // LDS, 8 bf16 per uint4
+    __device__ __forceinline__ float dot8(const uint4 &Lv, int grp8, float s) const {
+        const uint4 v = xs[grp8];
+        s = dec_dot2(Lv.x, v.x, s);
+        s = dec_dot2(Lv.y, v.y, s);
+        s = dec_dot2(Lv.z, v.z, s);
+        s = dec_dot2(Lv.w, v.w, s);
         return s;
     }
 };
 template <>
 struct DecX<false> {
-    float v[64];
-    __device__ __forceinline__ void load(const void *x, int off) {
-        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float4 r = p[i];
-            v[4 * i] = r.x, v[4 * i + 1] = r.y, v[4 * i + 2] = r.z, v[4 * i + 3] = r.w;
-        }
-    }
-    __device__ __forceinline__ float dot8(const uint4 &Lv, int o, float s) const {
+    const float4 *xs;  // LDS, 4 fp32 per float4
+    __device__ __forceinline__ float dot8(const uint4 &Lv, int grp8, float s) const {
+        const float4 a = xs[2 * grp8], b = xs[2 * grp8 + 1];
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         const uint32_t l[4] = {Lv.x, Lv.y, Lv.z, Lv.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s = fmaf(__uint_as_float(l[i] << 16), v[2 * (o + i)], s);
-            s = fmaf(__uint_as_float(l[i] & 0xFFFF0000u), v[2 * (o + i) + 1], s);
+            s = fmaf(__uint_as_float(l[i] << 16), v[2 * i], s);
+            s = fmaf(__uint_as_float(l[i] & 0xFFFF0000u), v[2 * i + 1], s);
         }
         return s;
     }
 };
 
 // 64 IQ2 weights of one lane (two canonical sub-blocks) against x, before d/64.
+// (the lane's 64 weights are groups 8 c .. 8 c + 7 of the row; xc points at group 8 c)
 template <bool XBF16>
 __device__ __forceinline__ float dec_iq2_dot(const uint4 *T, uint4 q, const DecX<XBF16> &xc, int rep) {
     float acc = 0.0f;
@@ -385,8 +362,8 @@ __device__ __forceinline__ float dec_iq2_dot(const uint4 *T, uint4 q, const DecX
         float s = 0.0f;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const uint4 Lv = iq2_group_levels(T, (ib >> (8 * g)) & 0xFFu, (sw >> (7 * g)) & 0x7Fu, rep);
-            s = xc.dot8(Lv, 16 * sb + 4 * g, s);
+            const uint4 Lv = iq2_group_levels<DEC_REPL>(T, (ib >> (8 * g)) & 0xFFu, (sw >> (7 * g)) & 0x7Fu, rep);
+            s = xc.dot8(Lv, 4 * sb + g, s);
         }
         acc = fmaf((float)(2u * (sw >> 28) + 1u), s, acc);
     }
@@ -414,42 +391,50 @@ __device__ __forceinline__ bool route_cached(const Layer &L, const Work &W, cons
     return true;
 }
 
-template <bool XBF16>
-__device__ void dec_rgu_item(const Layer &L, const Work &W, const void *__restrict__ x, const uint4 *T, int item,
-                             const DecPlan &P, int *lds_flag, RouteCache *rc) {
+// Weights of one routed gate/up item for this lane: DEC_GU_NR rows of gate and up.
+struct RguW {
+    uint4 qg[DEC_GU_NR], qu[DEC_GU_NR];
+    float dg[DEC_GU_NR], du[DEC_GU_NR];
+};
+
+__device__ __forceinline__ void dec_rgu_load(const Layer &L, const DecPlan &P, const RouteCache *rc, int item,
+                                             RguW &w) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd, F = L.n_ff;
     const int lpr = E >> 6, rpw = 64 / lpr;
     const int c = lane & (lpr - 1);
     const int j = item / P.rgu_per_slot, tile = item - j * P.rgu_per_slot;
-    const int rows_per_wave = DEC_GU_NR * rpw;
-    const int f0 = (tile * DEC_WAVES + wave) * rows_per_wave + lane / lpr;
-    DecX<XBF16> xc;
-    xc.load(x, 64 * c);
-    if (!route_cached(L, W, P, rc, lds_flag)) return;
+    const int f0 = (tile * DEC_WAVES + wave) * (DEC_GU_NR * rpw) + lane / lpr;
     const int e = rc->idx[j];
-    uint4 qg[DEC_GU_NR], qu[DEC_GU_NR];
-    float dg[DEC_GU_NR], du[DEC_GU_NR];
 #pragma unroll
     for (int r = 0; r < DEC_GU_NR; ++r) {
+        // rows past n_ff (if any) read row n_ff - 1 with a zero scale
         const int f = f0 + r * rpw;
-        if (f < F) {
-            const int64_t rb = ((int64_t)e * F + f) * L.nbe;
-            qg[r] = *reinterpret_cast<const uint4 *>(L.iq2_qs[0] + rb * 64 + c * 16);
-            qu[r] = *reinterpret_cast<const uint4 *>(L.iq2_qs[1] + rb * 64 + c * 16);
-            dg[r] = half_to_f32(L.iq2_d[0][rb + (c >> 2)]);
-            du[r] = half_to_f32(L.iq2_d[1][rb + (c >> 2)]);
-        } else {
-            qg[r] = qu[r] = make_uint4(0, 0, 0, 0);
-            dg[r] = du[r] = 0.0f;
-        }
+        const int64_t rb = ((int64_t)e * F + min(f, F - 1)) * L.nbe;
+        w.qg[r] = *reinterpret_cast<const uint4 *>(L.iq2_qs[0] + rb * 64 + c * 16);
+        w.qu[r] = *reinterpret_cast<const uint4 *>(L.iq2_qs[1] + rb * 64 + c * 16);
+        w.dg[r] = (f < F) ? half_to_f32(L.iq2_d[0][rb + (c >> 2)]) : 0.0f;
+        w.du[r] = (f < F) ? half_to_f32(L.iq2_d[1][rb + (c >> 2)]) : 0.0f;
     }
-    const int rep = lane & (IQ2_REPL - 1);
+}
+
+template <bool XBF16>
+__device__ __forceinline__ void dec_rgu_compute(const Layer &L, const Work &W, const void *xl, const uint4 *T, int item,
+                                                const DecPlan &P, const RguW &w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int E = L.n_embd, F = L.n_ff;
+    const int lpr = E >> 6, rpw = 64 / lpr;
+    const int c = lane & (lpr - 1);
+    const int j = item / P.rgu_per_slot, tile = item - j * P.rgu_per_slot;
+    const int f0 = (tile * DEC_WAVES + wave) * (DEC_GU_NR * rpw) + lane / lpr;
+    DecX<XBF16> xc;
+    xc.xs = reinterpret_cast<decltype(xc.xs)>(xl) + (XBF16 ? 8 * c : 16 * c);
+    const int rep = lane & (DEC_REPL - 1);
 #pragma unroll
     for (int r = 0; r < DEC_GU_NR; ++r) {
         const int f = f0 + r * rpw;
-        float g = dec_iq2_dot<XBF16>(T, qg[r], xc, rep) * dg[r];
-        float u = dec_iq2_dot<XBF16>(T, qu[r], xc, rep) * du[r];
+        float g = dec_iq2_dot<XBF16>(T, w.qg[r], xc, rep) * w.dg[r];
+        float u = dec_iq2_dot<XBF16>(T, w.qu[r], xc, rep) * w.du[r];
         g = dec_group_sum(g, lpr) * 0.015625f;
         u = dec_group_sum(u, lpr) * 0.015625f;
         if (c == 0 && f < F) st_shared(W.hbuf + (int64_t)j * F + f, dec_silu(g) * u);
@@ -533,34 +518,43 @@ __device__ __forceinline__ float dec_q2k_dot(uint4 qs, uint32_t sc, uint32_t dd,
     return half_to_f32((uint16_t)(dd & 0xFFFFu)) * A - half_to_f32((uint16_t)(dd >> 16)) * B;
 }
 
-__device__ void dec_rdn_item(const Layer &L, const Work &W, float *__restrict__ out, int item, const DecPlan &P,
-                             int *lds_flag, RouteCache *rc) {
+// Weights of one routed down item for this lane: DEC_DN_NR rows.
+struct RdnW {
+    uint4 qs[DEC_DN_NR];
+    uint32_t sc[DEC_DN_NR], dd[DEC_DN_NR];
+};
+
+__device__ __forceinline__ void dec_rdn_load(const Layer &L, const DecPlan &P, const RouteCache *rc, int item,
+                                             RdnW &w) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd, F = L.n_ff;
     const int lpr = F >> 6, rpw = 64 / lpr;
     const int c = lane & (lpr - 1);
     const int j = item / P.rdn_per_slot, tile = item - j * P.rdn_per_slot;
-    const int rows_per_wave = DEC_DN_NR * rpw;
-    const int r0 = (tile * DEC_WAVES + wave) * rows_per_wave + lane / lpr;
-    if (!route_cached(L, W, P, rc, lds_flag)) return;
+    const int r0 = (tile * DEC_WAVES + wave) * (DEC_DN_NR * rpw) + lane / lpr;
     const int e = rc->idx[j];
-    const float wgt = rc->w[j];
-    if (!wait_items(W, ctr(W, C_GU + j), (P.ep + 1) * (unsigned long long)P.rgu_per_slot, lds_flag)) return;
-    uint4 qs[DEC_DN_NR];
-    uint32_t sc[DEC_DN_NR], dd[DEC_DN_NR];
 #pragma unroll
     for (int r = 0; r < DEC_DN_NR; ++r) {
+        // rows past n_embd (if any) read row n_embd - 1 with zero scales
         const int row = r0 + r * rpw;
-        if (row < E) {
-            const int64_t rb = ((int64_t)e * E + row) * L.nbf;
-            qs[r] = *reinterpret_cast<const uint4 *>(L.q2k_qs + rb * 64 + c * 16);
-            sc[r] = *reinterpret_cast<const uint32_t *>(L.q2k_sc + rb * 16 + c * 4);
-            dd[r] = L.q2k_dd[rb + (c >> 2)];
-        } else {
-            qs[r] = make_uint4(0, 0, 0, 0);
-            sc[r] = dd[r] = 0u;
-        }
+        const int64_t rb = ((int64_t)e * E + min(row, E - 1)) * L.nbf;
+        w.qs[r] = *reinterpret_cast<const uint4 *>(L.q2k_qs + rb * 64 + c * 16);
+        w.sc[r] = *reinterpret_cast<const uint32_t *>(L.q2k_sc + rb * 16 + c * 4);
+        w.dd[r] = (row < E) ? L.q2k_dd[rb + (c >> 2)] : 0u;
     }
+}
+
+// Returns false if the wait for the slot's gate/up items expired.
+__device__ __forceinline__ bool dec_rdn_compute(const Layer &L, const Work &W, float *__restrict__ out, int item,
+                                                const DecPlan &P, int *lds_flag, const RouteCache *rc, const RdnW &w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int E = L.n_embd, F = L.n_ff;
+    const int lpr = F >> 6, rpw = 64 / lpr;
+    const int c = lane & (lpr - 1);
+    const int j = item / P.rdn_per_slot, tile = item - j * P.rdn_per_slot;
+    const int r0 = (tile * DEC_WAVES + wave) * (DEC_DN_NR * rpw) + lane / lpr;
+    const float wgt = rc->w[j];
+    if (!wait_items(W, ctr(W, C_GU + j), (P.ep + 1) * (unsigned long long)P.rgu_per_slot, lds_flag)) return false;
     float hv[64], hsum[4];
     // plain loads: these lines are first touched now, after every producer finished
     const float4 *hp = reinterpret_cast<const float4 *>(W.hbuf + (int64_t)j * F + 64 * c);
@@ -579,37 +573,84 @@ __device__ void dec_rdn_item(const Layer &L, const Work &W, float *__restrict__ 
 #pragma unroll
     for (int r = 0; r < DEC_DN_NR; ++r) {
         const int row = r0 + r * rpw;
-        float y = dec_q2k_dot(qs[r], sc[r], dd[r], hv, hsum);
+        float y = dec_q2k_dot(w.qs[r], w.sc[r], w.dd[r], hv, hsum);
         y = dec_group_sum(y, lpr);
         if (c == 0 && row < E) atomicAdd(out + row, wgt * y);
     }
+    return true;
 }
 
 // ---------------------------------------------------------------- the persistent kernel
 template <bool XBF16>
-__global__ __launch_bounds__(DEC_THREADS, 2) void k_decode_fused(Layer L, Work W, const void *__restrict__ x,
+__global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Layer L, Work W, const void *__restrict__ x,
                                                              float *__restrict__ out, DecPlan P) {
-    __shared__ uint4 T[256 * IQ2_REPL];
+    __shared__ uint4 T[256 * DEC_REPL];
+    __shared__ uint4 xl[4096 * (XBF16 ? 2 : 4) / 16];   // the token's x (n_embd <= 4096)
     __shared__ int lds_flag;
     __shared__ double lds_part[DEC_WAVES];
     __shared__ RouteCache rc;
     if (threadIdx.x == 0) rc.ready = 0;
-    iq2_build_lut<false>(T, L.codebook, threadIdx.x, DEC_THREADS);
     __syncthreads();
     const int G = gridDim.x;
-    const int b0 = P.n_route, b1 = b0 + P.n_shgu, b2 = b1 + P.n_rgu, b3 = b2 + P.n_shdn;
-    for (int it = blockIdx.x; it < P.total; it += G) {
-        if (it < b0) dec_route_item<XBF16>(L, W, x, it, &lds_flag, lds_part, P);
-        else if (it < b1) dec_shgu_item<XBF16>(L, W, x, it - b0);
-        else if (it < b2) dec_rgu_item<XBF16>(L, W, x, T, it - b1, P, &lds_flag, &rc);
-        else if (it < b3) {
-            switch (P.shdn_cpr) {
-                case 1: dec_shdn_item<1>(L, W, out, it - b2, P, &lds_flag); break;
-                case 2: dec_shdn_item<2>(L, W, out, it - b2, P, &lds_flag); break;
-                case 4: dec_shdn_item<4>(L, W, out, it - b2, P, &lds_flag); break;
-                default: dec_shdn_item<8>(L, W, out, it - b2, P, &lds_flag); break;
-            }
-        } else dec_rdn_item(L, W, out, it - b3, P, &lds_flag, &rc);
+    // item order: router, routed gate/up, shared gate/up, routed down, shared down;
+    // every wait is on an earlier phase
+    const int b0 = P.n_route, b1 = b0 + P.n_rgu, b2 = b1 + P.n_shgu, b3 = b2 + P.n_rdn;
+    // one loop per phase (the same items in the same order as a single loop
+    // over all of them), so that each phase's registers are allocated on their own
+    int it = blockIdx.x;
+    for (; it < b0; it += G) dec_route_item<XBF16>(L, W, x, it, &lds_flag, lds_part, P);
+    // the IQ2 level table is built after the workgroup's router item
+    iq2_build_lut<false, DEC_REPL>(T, L.codebook, threadIdx.x, DEC_THREADS);
+    {
+        const int nv = L.n_embd * (XBF16 ? 2 : 4) / 16;
+        for (int i = threadIdx.x; i < nv; i += DEC_THREADS) xl[i] = reinterpret_cast<const uint4 *>(x)[i];
+    }
+    __syncthreads();
+    bool ok = true;
+    // routed gate/up: the next item's weights are in flight while this one is computed
+    if (it < b1) ok = route_cached(L, W, P, &rc, &lds_flag);
+    if (ok && it < b1) {
+        RguW wa, wb;   // two named buffers, alternating (no copies)
+        dec_rgu_load(L, P, &rc, it - b0, wa);
+        for (;;) {
+            bool more = it + G < b1;
+            if (more) dec_rgu_load(L, P, &rc, it + G - b0, wb);
+            dec_rgu_compute<XBF16>(L, W, xl, T, it - b0, P, wa);
+            it += G;
+            if (!more) break;
+            more = it + G < b1;
+            if (more) dec_rgu_load(L, P, &rc, it + G - b0, wa);
+            dec_rgu_compute<XBF16>(L, W, xl, T, it - b0, P, wb);
+            it += G;
+            if (!more) break;
+        }
+    }
+    for (; ok && it < b2; it += G) dec_shgu_item<XBF16>(L, W, x, it - b1);
+    // routed down: the same pipelining; weights do not wait for the gate/up phase
+    if (ok && it < b3) ok = route_cached(L, W, P, &rc, &lds_flag);
+    if (ok && it < b3) {
+        RdnW wa, wb;
+        dec_rdn_load(L, P, &rc, it - b2, wa);
+        for (;;) {
+            bool more = it + G < b3;
+            if (more) dec_rdn_load(L, P, &rc, it + G - b2, wb);
+            if (!dec_rdn_compute(L, W, out, it - b2, P, &lds_flag, &rc, wa)) { ok = false; break; }
+            it += G;
+            if (!more) break;
+            more = it + G < b3;
+            if (more) dec_rdn_load(L, P, &rc, it + G - b2, wa);
+            if (!dec_rdn_compute(L, W, out, it - b2, P, &lds_flag, &rc, wb)) { ok = false; break; }
+            it += G;
+            if (!more) break;
+        }
+    }
+    for (; ok && it < P.total; it += G) {
+        switch (P.shdn_cpr) {
+            case 1: dec_shdn_item<1>(L, W, out, it - b3, P, &lds_flag); break;
+            case 2: dec_shdn_item<2>(L, W, out, it - b3, P, &lds_flag); break;
+            case 4: dec_shdn_item<4>(L, W, out, it - b3, P, &lds_flag); break;
+            default: dec_shdn_item<8>(L, W, out, it - b3, P, &lds_flag); break;
+        }
     }
     // a bounded wait expired somewhere: make the failure visible in the output
     if (blockIdx.x == 0 && threadIdx.x == 0 &&
@@ -620,7 +661,7 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void k_decode_fused(Layer L, Work W
 static DecPlan make_plan(const Layer &L) {
     DecPlan P{};
     const int E = L.n_embd, F = L.n_ff, k = L.top_k;
-    P.n_route = L.n_expert;  // one expert per item
+    P.n_route = 2 * L.n_expert;  // half an expert row per item
     P.n_shgu = L.n_shared ? (F + DEC_WAVES - 1) / DEC_WAVES : 0;
     const int rows_gu_item = DEC_WAVES * DEC_GU_NR * (64 / (E >> 6));
     P.rgu_per_slot = (F + rows_gu_item - 1) / rows_gu_item;
@@ -647,7 +688,7 @@ int decode_grid(int act_bf16) {
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&k_decode_fused<false>),
                                                      DEC_THREADS, 0);
     if (e != hipSuccess) return 0;
-    per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
+    per_cu = per_cu < 1 ? 1 : (per_cu > DEC_WG_PER_CU ? DEC_WG_PER_CU : per_cu);
     return ncu * per_cu;
 }
 

@@ -30,9 +30,9 @@ __device__ __forceinline__ uint32_t iq2_level_f16(uint32_t c) {
     return (c == 0) ? 0x3C00u : (c == 1) ? 0x4200u : (c == 2) ? 0x4500u : 0x4700u;
 }
 
-// Build the replicated table (entry e, replica r at uint4 index e*16 + r): each
-// thread loads whole codebook entries once and writes their 8 replicas.
-template <bool FP16>
+// Build the replicated table (entry e, replica r at uint4 index e*R + r): each
+// thread loads whole codebook entries once and writes their R replicas.
+template <bool FP16, int R = IQ2_REPL>
 __device__ __forceinline__ void iq2_build_lut(uint4 *T, const uint16_t *__restrict__ codebook, int tid, int nthreads) {
     for (int e = tid; e < 256; e += nthreads) {
         const uint32_t c = codebook[e];
@@ -41,7 +41,7 @@ __device__ __forceinline__ void iq2_build_lut(uint4 *T, const uint16_t *__restri
         for (int k = 0; k < 8; ++k) v[k] = FP16 ? iq2_level_f16((c >> (2 * k)) & 3u) : iq2_level_bf16((c >> (2 * k)) & 3u);
         const uint4 q = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
 #pragma unroll
-        for (int r = 0; r < IQ2_REPL; ++r) T[e * IQ2_REPL + r] = q;
+        for (int r = 0; r < R; ++r) T[e * R + r] = q;
     }
 }
 
@@ -76,8 +76,9 @@ __device__ __forceinline__ uint4 iq2_apply_signs(uint4 L, uint32_t s7) {
 
 // Signed levels of one group: idx = codebook index, s7 = stored sign bits of
 // weights 0..6.  Returns 4 dwords of packed pairs (w0|w1, w2|w3, w4|w5, w6|w7).
+template <int R = IQ2_REPL>
 __device__ __forceinline__ uint4 iq2_group_levels(const uint4 *T, uint32_t idx, uint32_t s7, int rep) {
-    return iq2_apply_signs(T[idx * IQ2_REPL + rep], s7);
+    return iq2_apply_signs(T[idx * R + rep], s7);
 }
 
 }  // namespace ds4

@@ -330,58 +330,76 @@ hipError_t launch_router_prep(const float *router, int NE, int E, uint16_t *hml,
 typedef __bf16 rt_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float rt_floatx4 __attribute__((ext_vector_type(4)));
 
-// Estimates for 32 tokens x 64 experts per workgroup; wave w takes experts
-// 16 w..16 w+15 (B: lane l holds expert l % 16, K 8 (l / 16)..+8) and two
-// 16-token tiles (A: token l % 16 of the tile, the same K).
+// Estimates, split over K: workgroup (expert tile, token tile, K quarter)
+// covers 64 experts x 64 tokens x n_embd / 4; wave w takes experts
+// 16 w..16 w+15 (B: lane l holds expert l % 16, K 8 (l / 16)..+8, for each of
+// the three router parts) and the four 16-token tiles (A: token l % 16 of the
+// tile, the same K).  The quarter sums go to est[quarter][token][expert] and
+// are added in fp64 by the selection.  The first workgroup also clears the
+// per-expert counters that the selection fills.
+constexpr int RA_SPLIT = 4;
 __global__ __launch_bounds__(256) void k_route_approx(const uint16_t *__restrict__ hml, const uint16_t *__restrict__ x,
-                                                      int n_tok, int NE, int E, float *__restrict__ est) {
+                                                      int n_tok, int NE, int E, float *__restrict__ est,
+                                                      int32_t *__restrict__ ecount) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rl = lane & 15, grp = lane >> 4;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+        for (int i = threadIdx.x; i < NE; i += 256) ecount[i] = 0;
     const int e = blockIdx.x * 64 + wave * 16 + rl;
-    const int t0 = blockIdx.y * 32;
+    const int t0 = blockIdx.y * 64;
     const bool eok = e < NE;
+    const int kq = E / RA_SPLIT, kb = blockIdx.z * kq;
     const uint16_t *wp[3];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) wp[p] = hml + ((int64_t)p * NE + (eok ? e : 0)) * E + 8 * grp;
-    const uint16_t *xp[2];
-    bool tok[2];
+    for (int p = 0; p < 3; ++p) wp[p] = hml + ((int64_t)p * NE + (eok ? e : 0)) * E + kb + 8 * grp;
+    const uint16_t *xp[4];
+    bool tok[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
         const int t = t0 + 16 * i + rl;
         tok[i] = t < n_tok;
-        xp[i] = x + (int64_t)(tok[i] ? t : 0) * E + 8 * grp;
+        xp[i] = x + (int64_t)(tok[i] ? t : 0) * E + kb + 8 * grp;
     }
     const uint4 z4 = make_uint4(0, 0, 0, 0);
-    double acc[2][4] = {};
-    for (int k0 = 0; k0 < E; k0 += QK) {
-        rt_floatx4 part[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    double acc[4][4] = {};
+    for (int k0 = 0; k0 < kq; k0 += QK) {
+        rt_floatx4 part[4];
 #pragma unroll
-        for (int s = 0; s < QK / 32; ++s) {
-            const int kk = k0 + 32 * s;
-            uint4 a[2], b[3];
+        for (int i = 0; i < 4; ++i) part[i] = rt_floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = tok[i] ? *reinterpret_cast<const uint4 *>(xp[i] + kk) : z4;
+        for (int h = 0; h < 2; ++h) {
+            uint4 a[4][4], b[4][3];
 #pragma unroll
-            for (int p = 0; p < 3; ++p) b[p] = eok ? *reinterpret_cast<const uint4 *>(wp[p] + kk) : z4;
+            for (int s = 0; s < 4; ++s) {
+                const int kk = k0 + 128 * h + 32 * s;
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < 4; ++i) a[s][i] = tok[i] ? *reinterpret_cast<const uint4 *>(xp[i] + kk) : z4;
 #pragma unroll
-                for (int p = 0; p < 3; ++p)
-                    part[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(rt_bf16x8, a[i]),
-                                                                      __builtin_bit_cast(rt_bf16x8, b[p]), part[i], 0, 0, 0);
+                for (int p = 0; p < 3; ++p) b[s][p] = eok ? *reinterpret_cast<const uint4 *>(wp[p] + kk) : z4;
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int p = 0; p < 3; ++p)
+                        part[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(rt_bf16x8, a[s][i]),
+                                                                          __builtin_bit_cast(rt_bf16x8, b[s][p]),
+                                                                          part[i], 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[i][v] += (double)part[i][v];
     }
     // C layout: lane (rl, grp) holds tokens 4 grp + v of each tile for expert rl
+    float *eq = est + (int64_t)blockIdx.z * n_tok * NE;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int t = t0 + 16 * i + 4 * grp + v;
-            if (t < n_tok && eok) est[(int64_t)t * NE + e] = (float)acc[i][v];
+            if (t < n_tok && eok) eq[(int64_t)t * NE + e] = (float)acc[i][v];
         }
 }
 
@@ -417,7 +435,9 @@ __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ 
         const int e = lane + 64 * i;
         if (e < NE) {
             bb[i] = bias ? (double)bias[e] : 0.0;
-            const double a = (double)W.logits[(int64_t)t * NE + e] + bb[i];
+            double a = bb[i];
+#pragma unroll
+            for (int qd = 0; qd < RA_SPLIT; ++qd) a += (double)W.rest[((int64_t)qd * n_tok + t) * NE + e];
             const double del = RT_BOUND * xn * (double)rnorm[e] + 1e-30;
             lb[i] = a - del;
             ub[i] = a + del;
@@ -448,37 +468,61 @@ __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ 
         }
     }
     const double cut = theta - (fabs(theta) * 0x1p-20 + 1e-30);
-    // exact logits of the candidates
+    // exact logits of the candidates, up to 8 dot products at a time
     uint64_t key[4];
     float Lv[4];
 #pragma unroll
+    for (int i = 0; i < 4; ++i) key[i] = 0ull, Lv[i] = 0.f;
+    int cand[8];
+    int nc = 0;
+    auto flush = [&]() {
+        double sacc[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sacc[c] = 0.0;
+#pragma unroll
+        for (int m = 0; m < RS_MAXV / 4; ++m) {
+            if (m < nm) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    if (c < nc) {
+                        const float4 r = *reinterpret_cast<const float4 *>(R + (int64_t)cand[c] * E + 256 * m + 4 * lane);
+                        sacc[c] = fma((double)xv[4 * m + 0], (double)r.x, sacc[c]);
+                        sacc[c] = fma((double)xv[4 * m + 1], (double)r.y, sacc[c]);
+                        sacc[c] = fma((double)xv[4 * m + 2], (double)r.z, sacc[c]);
+                        sacc[c] = fma((double)xv[4 * m + 3], (double)r.w, sacc[c]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            if (c < nc) {
+                const double sv = wave_sum(sacc[c]);
+                const int e = cand[c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (lane + 64 * i == e) {
+                        Lv[i] = (float)(sv + bb[i]);
+                        key[i] = topk_key(Lv[i], e);
+                    }
+            }
+        }
+        nc = 0;
+    };
+#pragma unroll
     for (int i = 0; i < 4; ++i) {
-        key[i] = 0ull;
-        Lv[i] = 0.f;
         uint64_t cm = __ballot(ub[i] >= cut);
         while (cm) {
             const int l = __ffsll((unsigned long long)cm) - 1;
             cm &= cm - 1;
-            const int e = l + 64 * i;
-            const float *row = R + (int64_t)e * E + 4 * lane;
-            double s = 0.0;
 #pragma unroll
-            for (int m = 0; m < RS_MAXV / 4; ++m) {
-                if (m < nm) {
-                    const float4 r = *reinterpret_cast<const float4 *>(row + 256 * m);
-                    s = fma((double)xv[4 * m + 0], (double)r.x, s);
-                    s = fma((double)xv[4 * m + 1], (double)r.y, s);
-                    s = fma((double)xv[4 * m + 2], (double)r.z, s);
-                    s = fma((double)xv[4 * m + 3], (double)r.w, s);
-                }
-            }
-            s = wave_sum(s);
-            if (lane == l) {
-                Lv[i] = (float)(s + bb[i]);
-                key[i] = topk_key(Lv[i], e);
-            }
+            for (int c = 0; c < 8; ++c)
+                if (c == nc) cand[c] = l + 64 * i;
+            ++nc;
+            if (nc == 8) flush();
         }
     }
+    if (nc > 0) flush();
     // top-k among the candidates, renormalised weights
     float sel_L[MAX_TOPK];
     int sel_e[MAX_TOPK];
@@ -505,19 +549,61 @@ __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ 
         }
         W.idx[(int64_t)t * k + lane] = e;
         W.w[(int64_t)t * k + lane] = (float)(num / z);
+        atomicAdd(&W.ecount[e], 1);
+    }
+}
+
+// Per-expert lists after the batched selection: one workgroup per expert.
+// The expert's offset and its rank among the active experts come from the
+// counts of the lower experts; its entries t*k + j are emitted in ascending t
+// by a workgroup-wide scan over the tokens.
+__global__ __launch_bounds__(256) void k_fill_lists(int n_tok, int NE, int k, Work W) {
+    __shared__ int wtot[4];
+    const int e = blockIdx.x, tid = threadIdx.x;
+    int total, off, nact, apos;
+    {
+        const int c = (tid < NE) ? W.ecount[tid] : 0;
+        const int ex = scan256(c, tid, wtot, total);
+        const int ax = scan256(c > 0 ? 1 : 0, tid, wtot, nact);
+        __shared__ int mine[2];
+        if (tid == e) mine[0] = ex, mine[1] = ax;
+        __syncthreads();
+        off = mine[0], apos = mine[1];
+    }
+    const int cnt = W.ecount[e];
+    if (tid == 0) {
+        W.offsets[e] = off;
+        if (cnt > 0) W.active[1 + apos] = e;
+        if (e == NE - 1) {
+            W.offsets[NE] = total;
+            W.active[0] = nact;
+        }
+    }
+    if (cnt == 0) return;
+    int run = off;
+    for (int t0 = 0; t0 < n_tok; t0 += 256) {
+        const int t = t0 + tid;
+        int j = -1;
+        if (t < n_tok)
+            for (int jj = 0; jj < k; ++jj)
+                if (W.idx[(int64_t)t * k + jj] == e) j = jj;
+        int tot;
+        const int pos = scan256(j >= 0 ? 1 : 0, tid, wtot, tot);
+        if (j >= 0) W.list[run + pos] = t * k + j;
+        run += tot;
     }
 }
 
 hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s, hipEvent_t *ev) {
     const int NE = L.n_expert;
-    if (n_tok > ROUTE_SMALL_MAX && L.act_dtype == 1) {
+    if (n_tok > ROUTE_SMALL_MAX && L.act_dtype == 1 && L.n_embd % (4 * QK) == 0) {
         // batched: MFMA estimates, exact candidates, lists
         const uint16_t *xb = static_cast<const uint16_t *>(x);
-        hipLaunchKernelGGL(k_route_approx, dim3((NE + 63) / 64, (n_tok + 31) / 32), dim3(256), 0, s, L.router_hml, xb,
-                           n_tok, NE, L.n_embd, W.logits);
+        hipLaunchKernelGGL(k_route_approx, dim3((NE + 63) / 64, (n_tok + 63) / 64, RA_SPLIT), dim3(256), 0, s,
+                           L.router_hml, xb, n_tok, NE, L.n_embd, W.rest, W.ecount);
         hipLaunchKernelGGL(k_route_select, dim3((n_tok + 3) / 4), dim3(256), 0, s, L.router, L.router_bias,
                            L.router_norm, xb, n_tok, NE, L.n_embd, L.top_k, W);
-        hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, s, n_tok, NE, L.top_k, W);
+        hipLaunchKernelGGL(k_fill_lists, dim3(NE), dim3(256), 0, s, n_tok, NE, L.top_k, W);
         return hipGetLastError();
     }
     dim3 grid((NE + RT_WAVES - 1) / RT_WAVES, (n_tok + RT_TOK - 1) / RT_TOK);
