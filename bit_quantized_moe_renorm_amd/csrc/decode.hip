@@ -4,17 +4,16 @@
 // fuse MoE routing with the expert computation into one GPU dispatch (same
 // page, section 2.3).  Here one persistent launch walks a fixed list of work
 // items in five phases, in this order:
-//   router    : half an expert's logit per item (fp64 accumulation); the wave
-//               that completes the last half also does top-k and
-//               renormalisation, then publishes "route ready";
+//   router    : half an expert's logit per item (fp64 accumulation);
+//   shared g/u: 4 rows of the shared expert's gate and up per item (no
+//               routing needed, so it streams while the router is counted);
+//   routing   : every workgroup waits until all router halves are counted and
+//               takes the top-k and renormalised weights itself;
 //   routed g/u: 16 rows of one selected expert's IQ2 gate and up per item,
-//               SiLU(g)*u kept in fp32 (waits for "route ready");
-//   shared g/u: 4 rows of the shared expert's gate and up per item;
+//               SiLU(g)*u kept in fp32;
 //   routed dn : rows of one selected expert's Q2_K down projection, scaled
 //               by its routing weight (waits for that expert's g/u items);
 //   shared dn : rows of the shared down projection (waits for shared g/u).
-// The router runs alone first, so its 4 MB do not share HBM with the 50 MB
-// shared expert, which streams while the routed experts are processed.
 // Items are dealt round-robin over the workgroups in phase order, and the grid
 // is sized to what the GPU holds at once, so every wait is on an item that a
 // resident workgroup took earlier and that never waits on a later one.  Each
@@ -53,7 +52,7 @@ __device__ __forceinline__ float dec_group_sum(float v, int lpr) {
 // `ep` of a handle waits for (ep + 1) times the per-call count, so nothing has
 // to be reset at the end of a launch.
 constexpr int CSTRIDE = 32;  // in uint64
-constexpr int C_ROUTE = 1, C_READY = 2, C_SHGU = 3, C_ERR = 4, C_GU = 5;  // C_GU + slot; slot units
+constexpr int C_ROUTE = 1, C_SHGU = 3, C_ERR = 4, C_GU = 5;  // C_GU + slot; slot units
 __device__ __forceinline__ unsigned long long *ctr(const Work &W, int slot) {
     return reinterpret_cast<unsigned long long *>(W.counters) + slot * CSTRIDE;
 }
@@ -61,7 +60,7 @@ __device__ __forceinline__ unsigned long long *ctr(const Work &W, int slot) {
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_THREADS = 64 * DEC_WAVES;
 constexpr int DEC_WG_PER_CU = 2;  // resident workgroups per CU
-constexpr int DEC_REPL = 4;       // level-table replicas (lane l reads replica l % 4)
+constexpr int DEC_REPL = IQ2_REPL;  // level-table replicas (lane l reads replica l % 16)
 constexpr int DEC_GU_NR = 4;  // routed gate/up row slots per wave
 constexpr int DEC_DN_NR = 4;  // routed down row slots per wave
 
@@ -111,12 +110,13 @@ __device__ __forceinline__ unsigned long long publish_item(unsigned long long *c
 
 // Wait (one poller per workgroup, with backoff) until *c >= target.  Returns
 // false, and flags the error, if the bounded wait expired.
+template <int SLEEP = 8>
 __device__ __forceinline__ bool wait_items(const Work &W, unsigned long long *c, unsigned long long target,
                                            int *lds_flag) {
     if (threadIdx.x == 0) {
         int ok = 1, spins = 0;
         while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(8);
+            __builtin_amdgcn_s_sleep(SLEEP);
             if (++spins > SPIN_LIMIT) {
                 __hip_atomic_store(ctr(W, C_ERR), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ok = 0;
@@ -151,12 +151,24 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-__device__ __forceinline__ void dec_topk_publish(const Layer &L, const Work &W, const double *part) {
+// Routing of the token, computed by every workgroup for itself (wave 0) once
+// all router halves are counted: fp32 logits from the fp64 halves, top-k with
+// the lowest index first among equal logits, renormalised weights.  Workgroup
+// 0 also writes it (and the per-expert lists) to the workspace for
+// ds4moe_route's export.
+struct RouteCache {
+    int idx[MAX_TOPK];
+    float w[MAX_TOPK];
+};
+
+__device__ __forceinline__ void dec_topk_local(const Layer &L, const Work &W, const double *part, RouteCache *rc,
+                                               bool write_global) {
     const int lane = threadIdx.x & 63;
     const int NE = L.n_expert, k = L.top_k;
     // fp32 logits as order-preserving keys (0 = no expert); lane l holds experts l + 64 i.
     // The halves were stored by other workgroups with write-through stores and
-    // this workgroup has not read those lines before: plain loads are coherent.
+    // no workgroup reads those lines before the count is complete: plain loads
+    // are coherent.
     uint32_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -170,8 +182,7 @@ __device__ __forceinline__ void dec_topk_publish(const Layer &L, const Work &W, 
             if (key[i] == 0u) key[i] = 1u;  // keep 0 free for "taken"
         }
     }
-    // lane j < k ends up holding the j-th selection: the largest key, and among
-    // equal keys the lowest expert index (lowest i, then lowest lane)
+    // lane j < k ends up holding the j-th selection
     int myE = 0;
     float myL = 0.f;
 #pragma unroll
@@ -181,8 +192,8 @@ __device__ __forceinline__ void dec_topk_publish(const Layer &L, const Work &W, 
         int ee = -1;
 #pragma unroll
         for (int i = 3; i >= 0; --i) {
-            const uint64_t b = __ballot(key[i] == m);
-            if (b) ee = 64 * i + (__ffsll((unsigned long long)b) - 1);
+            const uint64_t bb = __ballot(key[i] == m);
+            if (bb) ee = 64 * i + (__ffsll((unsigned long long)bb) - 1);
         }
         const uint32_t u = (m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m;
         if (lane == j) myE = ee, myL = __uint_as_float(u);
@@ -194,13 +205,16 @@ __device__ __forceinline__ void dec_topk_publish(const Layer &L, const Work &W, 
     const float L0 = __shfl(myL, 0, 64);
     const double ex = (lane < k) ? exp((double)myL - (double)L0) : 0.0;
     const double z = wave_sum(ex);
+    const float wj = (float)(ex / z);
     if (lane < k) {
-        st_shared(W.idx + lane, myE);
-        st_shared(W.w + lane, (float)(ex / z));
+        rc->idx[lane] = myE;
+        rc->w[lane] = wj;
     }
-    stores_done();
-    if (lane == 0) __hip_atomic_fetch_add(ctr(W, C_READY), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // per-expert lists for the single token (read only by ds4moe_route's export)
+    if (!write_global) return;
+    if (lane < k) {
+        W.idx[lane] = myE;
+        W.w[lane] = wj;
+    }
     int selE[MAX_TOPK];
 #pragma unroll
     for (int j = 0; j < MAX_TOPK; ++j) selE[j] = (j < k) ? __shfl(myE, j, 64) : 0;
@@ -255,13 +269,10 @@ __device__ void dec_route_item(const Layer &L, const Work &W, const void *__rest
         const double sum = lds_part[0] + lds_part[1] + lds_part[2] + lds_part[3];
         __hip_atomic_store(part + 2 * e + h, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // count the half; the workgroup that completes the last one does top-k
-    const unsigned long long prev = publish_item(ctr(W, C_ROUTE));
-    if (threadIdx.x == 0) *lds_flag = (prev == (P.ep + 1) * (unsigned long long)P.n_route - 1ull);
+    // count the half (the increment's result is not needed)
+    stores_done();
     __syncthreads();
-    const int last = *lds_flag;
-    __syncthreads();
-    if (last && wave == 0) dec_topk_publish(L, W, part);
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr(W, C_ROUTE), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- P1: shared gate/up
@@ -318,33 +329,46 @@ __device__ void dec_shgu_item(const Layer &L, const Work &W, const void *__restr
 }
 
 // ---------------------------------------------------------------- P2: routed gate/up (IQ2)
-// The token's x, staged once per workgroup in LDS (bf16 or fp32 as given);
-// a routed gate/up lane reads the 8 values of one group at a time.
+// The lane's 64 values of x (its column chunk of every routed gate/up row), in
+// registers for the whole phase.
 template <bool XBF16>
 struct DecX;
 template <>
 struct DecX<true> {
-    const uint4 *xs;   // LDS, 8 bf16 per uint4
+    uint32_t v[32];
+    __device__ __forceinline__ void load(const void *x, int off) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + off);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 r = p[i];
+            v[4 * i] = r.x, v[4 * i + 1] = r.y, v[4 * i + 2] = r.z, v[4 * i + 3] = r.w;
+        }
+    }
     __device__ __forceinline__ float dot8(const uint4 &Lv, int grp8, float s) const {
-        const uint4 v = xs[grp8];
-        s = dec_dot2(Lv.x, v.x, s);
-        s = dec_dot2(Lv.y, v.y, s);
-        s = dec_dot2(Lv.z, v.z, s);
-        s = dec_dot2(Lv.w, v.w, s);
+        s = dec_dot2(Lv.x, v[4 * grp8], s);
+        s = dec_dot2(Lv.y, v[4 * grp8 + 1], s);
+        s = dec_dot2(Lv.z, v[4 * grp8 + 2], s);
+        s = dec_dot2(Lv.w, v[4 * grp8 + 3], s);
         return s;
     }
 };
 template <>
 struct DecX<false> {
-    const float4 *xs;  // LDS, 4 fp32 per float4
+    float v[64];
+    __device__ __forceinline__ void load(const void *x, int off) {
+        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float4 r = p[i];
+            v[4 * i] = r.x, v[4 * i + 1] = r.y, v[4 * i + 2] = r.z, v[4 * i + 3] = r.w;
+        }
+    }
     __device__ __forceinline__ float dot8(const uint4 &Lv, int grp8, float s) const {
-        const float4 a = xs[2 * grp8], b = xs[2 * grp8 + 1];
-        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         const uint32_t l[4] = {Lv.x, Lv.y, Lv.z, Lv.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s = fmaf(__uint_as_float(l[i] << 16), v[2 * i], s);
-            s = fmaf(__uint_as_float(l[i] & 0xFFFF0000u), v[2 * i + 1], s);
+            s = fmaf(__uint_as_float(l[i] << 16), v[8 * grp8 + 2 * i], s);
+            s = fmaf(__uint_as_float(l[i] & 0xFFFF0000u), v[8 * grp8 + 2 * i + 1], s);
         }
         return s;
     }
@@ -370,23 +394,12 @@ __device__ __forceinline__ float dec_iq2_dot(const uint4 *T, uint4 q, const DecX
     return acc;
 }
 
-// Routing of the token, read once per workgroup after "route ready".
-struct RouteCache {
-    int ready;
-    int idx[MAX_TOPK];
-    float w[MAX_TOPK];
-};
-
-__device__ __forceinline__ bool route_cached(const Layer &L, const Work &W, const DecPlan &P, RouteCache *rc,
-                                             int *lds_flag) {
-    if (rc->ready) return true;
-    if (!wait_items(W, ctr(W, C_READY), P.ep + 1, lds_flag)) return false;
-    if (threadIdx.x < L.top_k) {
-        rc->idx[threadIdx.x] = ld_shared(W.idx + threadIdx.x);
-        rc->w[threadIdx.x] = ld_shared(W.w + threadIdx.x);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) rc->ready = 1;
+// Wait until every router half is counted, then route locally.  Returns
+// false if the bounded wait expired.
+__device__ __forceinline__ bool dec_route_wait(const Layer &L, const Work &W, const DecPlan &P, RouteCache *rc,
+                                               int *lds_flag) {
+    if (!wait_items(W, ctr(W, C_ROUTE), (P.ep + 1) * (unsigned long long)P.n_route, lds_flag)) return false;
+    if (threadIdx.x < 64) dec_topk_local(L, W, W.rhalf, rc, blockIdx.x == 0);
     __syncthreads();
     return true;
 }
@@ -419,16 +432,14 @@ __device__ __forceinline__ void dec_rgu_load(const Layer &L, const DecPlan &P, c
 }
 
 template <bool XBF16>
-__device__ __forceinline__ void dec_rgu_compute(const Layer &L, const Work &W, const void *xl, const uint4 *T, int item,
-                                                const DecPlan &P, const RguW &w) {
+__device__ __forceinline__ void dec_rgu_compute(const Layer &L, const Work &W, const DecX<XBF16> &xc, const uint4 *T,
+                                                int item, const DecPlan &P, const RguW &w) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd, F = L.n_ff;
     const int lpr = E >> 6, rpw = 64 / lpr;
     const int c = lane & (lpr - 1);
     const int j = item / P.rgu_per_slot, tile = item - j * P.rgu_per_slot;
     const int f0 = (tile * DEC_WAVES + wave) * (DEC_GU_NR * rpw) + lane / lpr;
-    DecX<XBF16> xc;
-    xc.xs = reinterpret_cast<decltype(xc.xs)>(xl) + (XBF16 ? 8 * c : 16 * c);
     const int rep = lane & (DEC_REPL - 1);
 #pragma unroll
     for (int r = 0; r < DEC_GU_NR; ++r) {
@@ -585,49 +596,56 @@ template <bool XBF16>
 __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Layer L, Work W, const void *__restrict__ x,
                                                              float *__restrict__ out, DecPlan P) {
     __shared__ uint4 T[256 * DEC_REPL];
-    __shared__ uint4 xl[4096 * (XBF16 ? 2 : 4) / 16];   // the token's x (n_embd <= 4096)
     __shared__ int lds_flag;
     __shared__ double lds_part[DEC_WAVES];
     __shared__ RouteCache rc;
-    if (threadIdx.x == 0) rc.ready = 0;
-    __syncthreads();
     const int G = gridDim.x;
-    // item order: router, routed gate/up, shared gate/up, routed down, shared down;
+    // item order: router, shared gate/up, routed gate/up, routed down, shared down;
     // every wait is on an earlier phase
-    const int b0 = P.n_route, b1 = b0 + P.n_rgu, b2 = b1 + P.n_shgu, b3 = b2 + P.n_rdn;
+    const int b0 = P.n_route, b1 = b0 + P.n_shgu, b2 = b1 + P.n_rgu, b3 = b2 + P.n_rdn;
     // one loop per phase (the same items in the same order as a single loop
     // over all of them), so that each phase's registers are allocated on their own
+    // loads that depend on nothing are issued before the router item: this
+    // thread's codebook entry and the lane's slice of x for the routed gate/up
+    // (lane c of a routed gate/up row holds x[64 c .. 64 c + 63])
+    const uint32_t cb = L.codebook[threadIdx.x & 255];
+    DecX<XBF16> xc;
+    xc.load(x, 64 * ((threadIdx.x & 63) & ((L.n_embd >> 6) - 1)));
     int it = blockIdx.x;
     for (; it < b0; it += G) dec_route_item<XBF16>(L, W, x, it, &lds_flag, lds_part, P);
-    // the IQ2 level table is built after the workgroup's router item
-    iq2_build_lut<false, DEC_REPL>(T, L.codebook, threadIdx.x, DEC_THREADS);
+    // the IQ2 level table (entry e, replica r at e * DEC_REPL + r)
     {
-        const int nv = L.n_embd * (XBF16 ? 2 : 4) / 16;
-        for (int i = threadIdx.x; i < nv; i += DEC_THREADS) xl[i] = reinterpret_cast<const uint4 *>(x)[i];
+        uint32_t v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = iq2_level_bf16((cb >> (2 * q)) & 3u);
+        const uint4 ent = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+        static_assert(DEC_THREADS == 256, "one codebook entry per thread");
+#pragma unroll
+        for (int r = 0; r < DEC_REPL; ++r) T[threadIdx.x * DEC_REPL + ((r + threadIdx.x) & (DEC_REPL - 1))] = ent;
     }
     __syncthreads();
-    bool ok = true;
+    // the shared expert's gate/up needs no routing: it streams while the
+    // router halves are counted
+    for (; it < b1; it += G) dec_shgu_item<XBF16>(L, W, x, it - b0);
+    bool ok = dec_route_wait(L, W, P, &rc, &lds_flag);
     // routed gate/up: the next item's weights are in flight while this one is computed
-    if (it < b1) ok = route_cached(L, W, P, &rc, &lds_flag);
-    if (ok && it < b1) {
+    if (ok && it < b2) {
         RguW wa, wb;   // two named buffers, alternating (no copies)
-        dec_rgu_load(L, P, &rc, it - b0, wa);
+        dec_rgu_load(L, P, &rc, it - b1, wa);
         for (;;) {
-            bool more = it + G < b1;
-            if (more) dec_rgu_load(L, P, &rc, it + G - b0, wb);
-            dec_rgu_compute<XBF16>(L, W, xl, T, it - b0, P, wa);
+            bool more = it + G < b2;
+            if (more) dec_rgu_load(L, P, &rc, it + G - b1, wb);
+            dec_rgu_compute<XBF16>(L, W, xc, T, it - b1, P, wa);
             it += G;
             if (!more) break;
-            more = it + G < b1;
-            if (more) dec_rgu_load(L, P, &rc, it + G - b0, wa);
-            dec_rgu_compute<XBF16>(L, W, xl, T, it - b0, P, wb);
+            more = it + G < b2;
+            if (more) dec_rgu_load(L, P, &rc, it + G - b1, wa);
+            dec_rgu_compute<XBF16>(L, W, xc, T, it - b1, P, wb);
             it += G;
             if (!more) break;
         }
     }
-    for (; ok && it < b2; it += G) dec_shgu_item<XBF16>(L, W, x, it - b1);
     // routed down: the same pipelining; weights do not wait for the gate/up phase
-    if (ok && it < b3) ok = route_cached(L, W, P, &rc, &lds_flag);
     if (ok && it < b3) {
         RdnW wa, wb;
         dec_rdn_load(L, P, &rc, it - b2, wa);
