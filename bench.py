@@ -57,6 +57,32 @@ def kernel_bytes_decode(spec):
     return parts
 
 
+def profile_traffic(name):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
+    summary under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by what the
+    counter reads for a copy of known size), or None if there is none or the
+    kernel's sources changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", name)
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    tb = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    srcs = re.search(r"^kernel_sources: (.+)$", text, re.M)
+    sha = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", text, re.M)
+    if not (tb and srcs and sha):
+        return None
+    h = hashlib.sha256()
+    for f in srcs.group(1).split():
+        try:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        except OSError:
+            return None
+    return int(tb.group(1)) if h.hexdigest() == sha.group(1) else None
+
+
 def cpu_baseline_decode(layer, x_np, budget_s=12.0):
     """The oracle (as it stands) on the host cores, on a bounded sample of the same
     token stream: batches of 16 tokens until about budget_s seconds have passed."""
@@ -101,13 +127,19 @@ def run_decode(args):
 
     for i in range(args.warmup):
         step(i)
-    # pass 1 (the value): K steps back to back, bracketed by synchronisation only
+    # pass 1 (the value): K steps back to back, bracketed by synchronisation;
+    # HIP events on the launch stream around the same region give the fused
+    # kernel's average duration (one launch per step, nothing else queued)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
         step(args.warmup + i)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    region_us = 1000.0 * ev0.elapsed_time(ev1) / args.steps
     # pass 2 (kernel durations): the same K steps with HIP events recorded by the
     # library around each kernel on the caller's stream (an event pair per launch
     # adds about 4 us of stream time, so pass 1 alone gives the throughput)
@@ -132,9 +164,12 @@ def run_decode(args):
     per_kernel = {k: {"avg_us": round(avg_us[k], 3), "bytes": kb[k],
                       "GB_s": round(kb[k] / (avg_us[k] * 1e-6) / 1e9, 1)} for k in avg_us if k in kb}
     log("[bench] per-kernel: " + json.dumps(per_kernel))
-    # the kernel with the most algorithmic bytes is the dominant one
+    # the kernel with the most algorithmic bytes is the dominant one; its
+    # duration is the timed region's events divided by the launches in it
     dom = max(per_kernel, key=lambda k: per_kernel[k]["bytes"])
-    achieved = per_kernel[dom]["GB_s"]
+    achieved = round(kb[dom] / (region_us * 1e-6) / 1e9, 1)
+    traffic = profile_traffic("decode_b1_ds4_k_decode_fused.md") if dom == "fused" else None
+    log(f"[bench] {dom}: {region_us:.2f} us per launch over the timed region (events), {achieved} GB/s algorithmic")
 
     tok_s = args.steps / wall
     ms_step = 1000.0 * wall / args.steps
@@ -157,7 +192,9 @@ def run_decode(args):
                    "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
                    "per_kernel": per_kernel},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "traffic_unit": "bytes per launch",
+                     "algorithmic_bytes_per_launch": kb[dom], "avg_launch_us": round(region_us, 3)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(layer, x_np)
