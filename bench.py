@@ -278,6 +278,98 @@ def run_prefill(args):
     return res
 
 
+def run_stack(args):
+    """The layer stack: L DS4-shape layers with seeds 4000 + l, each RMSNorm
+    (unit gain, eps 1e-6) -> MoE block -> residual add on an fp32 stream.
+    Decode: 256 steps of one token through all layers.  Prefill: 4096 tokens
+    in 512-token chunks through all layers."""
+    import torch
+
+    import bit_quantized_moe_renorm_amd as m
+    from bit_quantized_moe_renorm_amd import synth
+
+    spec = synth.DS4
+    L, chunk, n_pre, n_dec = args.layers, 512, 4096, 256
+    devs = []
+    t0 = time.perf_counter()
+    for l in range(L):
+        lay = synth.make_layer(spec, seed=4000 + l)
+        w = m.upload_layer(lay)
+        devs.append(m.MoELayer(spec, w, max_tokens=chunk))
+        del w, lay
+        torch.cuda.synchronize()
+        log(f"[bench] stack: layer {l + 1}/{L} resident ({time.perf_counter() - t0:.0f} s)")
+    torch.cuda.empty_cache()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    # decode b = 1
+    h = torch.from_numpy(synth.residual(41, n_dec + 8, spec.n_embd)).cuda()
+    xb = torch.empty((1, spec.n_embd), dtype=torch.bfloat16, device="cuda")
+
+    def token(t):
+        ht = h[t:t + 1]
+        for dev in devs:
+            m.rmsnorm(ht, out=xb, stream=stream)
+            dev.forward(xb, ht, stream)
+
+    for t in range(8):                      # warm-up tokens
+        token(n_dec + t)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for t in range(n_dec):
+        token(t)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dec_s = ev0.elapsed_time(ev1) * 1e-3
+    dec_tok_s = n_dec / dec_s
+    layer_bytes = touched_bytes(spec, spec.top_k)
+    dec_gbs = L * layer_bytes * n_dec / dec_s / 1e9
+    log(f"[bench] stack of {L} decode b=1: {dec_tok_s:.1f} tok/s, {1e6 * dec_s / n_dec / L:.2f} us per layer-token, "
+        f"{dec_gbs:.0f} GB/s touched-expert bytes = {100 * dec_gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s")
+
+    # prefill: 4096 tokens in 512-token chunks
+    hp = torch.from_numpy(synth.residual(42, n_pre, spec.n_embd)).cuda()
+    xp = torch.empty((chunk, spec.n_embd), dtype=torch.bfloat16, device="cuda")
+
+    def prefill():
+        for c0 in range(0, n_pre, chunk):
+            hc = hp[c0:c0 + chunk]
+            for dev in devs:
+                m.rmsnorm(hc, out=xp, stream=stream)
+                dev.forward(xp, hc, stream)
+
+    prefill()                               # warm-up pass (the stream's values are not checked here)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    prefill()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    pre_s = ev0.elapsed_time(ev1) * 1e-3
+    fl = sum(flops_prefill(spec, chunk).values()) * (n_pre // chunk) * L
+    pre_tok_s = n_pre / pre_s
+    log(f"[bench] stack of {L} prefill {n_pre} in {chunk}-token chunks: {pre_tok_s:.0f} tok/s, "
+        f"{fl / pre_s / 1e12:.0f} TFLOP/s = {100 * fl / pre_s / 1e12 / BF16_PEAK_TFLOPS:.1f}% of bf16 peak")
+    for dev in devs:
+        dev.close()
+    return {
+        "metric": METRIC, "value": round(dec_tok_s, 2), "unit": "tok/s", "n_gpus": 1,
+        "steps": n_dec, "warmup": 8, "ms_per_step": round(1e3 * dec_s / n_dec, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"stack of {L} DS4-shape MoE layers (seeds 4000..{4000 + L - 1}), RMSNorm -> MoE -> "
+                               "residual add per layer, decode b=1 over 256 steps; prefill 4096 tokens in "
+                               "512-token chunks",
+                   "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)", "layers": L,
+                   "decode_layer_us": round(1e6 * dec_s / n_dec / L, 3),
+                   "decode_hbm_GB_s": round(dec_gbs, 1), "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                   "prefill_tok_s": round(pre_tok_s, 1), "prefill_TFLOP_s": round(fl / pre_s / 1e12, 1),
+                   "prefill_mfma_frac": round(fl / pre_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "fused", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+
+
 def copy_probe():
     """A plain device copy of known size, for calibrating the HBM byte counters
     (FETCH_SIZE / WRITE_SIZE) that the profiles of the block's kernels use."""
@@ -298,7 +390,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "prefill"), default="decode")
+    ap.add_argument("--workload", choices=("decode", "prefill", "stack"), default="decode")
+    ap.add_argument("--layers", type=int, default=43, help="stack workload: number of layers")
     ap.add_argument("--tokens", type=int, default=2048, help="prefill tokens per call")
     ap.add_argument("--copy-probe", action="store_true", help="only run the counter-calibration copy")
     args = ap.parse_args()
@@ -317,6 +410,8 @@ def main():
         if args.steps == 1000 and args.warmup == 100:   # defaults sized for decode
             args.steps, args.warmup = 50, 5
         res = run_prefill(args)
+    elif args.workload == "stack":
+        res = run_stack(args)
     else:
         res = run_decode(args)
     print(json.dumps(res), flush=True)

@@ -154,3 +154,26 @@ def rmsnorm(h: np.ndarray, eps: float = 1e-6):
     x64 = np.empty((n, E), np.float64)
     lib().oracle_rmsnorm(_p(h), n, E, eps, _p(xb), _p(x64))
     return xb, x64
+
+
+def stack(layers, h0: np.ndarray, eps: float = 1e-6):
+    """A stack of MoE layers on the residual stream h (fp32 [n, E]).
+
+    Each layer normalises h (RMSNorm with unit gain, ``rmsnorm`` above), runs
+    the MoE block on the bf16 result and adds it to h: h <- h + MoE(x), the sum
+    in fp64 and stored in fp32, the residual stream's type at the block's
+    boundary.  The pages describe the model's hyper-connection mixing rather
+    than a per-layer norm for this block; the stack is the plainest one around
+    it.  Returns (h after the last layer, [x_l bf16 bits], [idx_l], [logits_l]).
+    """
+    h = np.ascontiguousarray(h0, dtype=np.float32).copy()
+    xs, idxs, logits = [], [], []
+    for layer in layers:
+        xb, _ = rmsnorm(h, eps)
+        lg, idx, _, _ = route(xb, layer.router, layer.router_bias, layer.spec.top_k)
+        y, _, _ = forward(layer, xb)
+        h = (h.astype(np.float64) + y).astype(np.float32)
+        xs.append(xb)
+        idxs.append(idx)
+        logits.append(lg)
+    return h, xs, idxs, logits

@@ -138,3 +138,42 @@ def test_forward_rejects_bad_shapes(oracle_lib):
     lib = oracle_lib.lib()
     rc = lib.oracle_forward(100, 256, 8, 2, *([None] * 10), 0, None, 0, None, None, None)
     assert rc == -1
+
+
+def test_stack_of_silent_layers_keeps_the_residual(oracle_lib, tiny):
+    """Layers whose block contributes exactly zero (routed scales 0, no shared
+    expert) leave the residual stream unchanged, and every layer sees the same
+    normalised input."""
+    lay = copy.deepcopy(tiny)
+    lay.gate[..., 0:2] = 0
+    lay.up[..., 0:2] = 0
+    lay.down[..., 80:84] = 0
+    lay.sh_gate = lay.sh_up = lay.sh_down = None
+    h0 = synth.residual(3, 4, 256)
+    h, xs, idxs, _ = oracle_lib.stack([lay, lay, lay], h0)
+    assert np.array_equal(h, h0)
+    x0, _ = oracle_lib.rmsnorm(h0, 1e-6)
+    assert all(np.array_equal(x, x0) for x in xs)
+    assert all(np.array_equal(i, idxs[0]) for i in idxs)
+
+
+def test_stack_norm_before_block_and_residual_add(oracle_lib, tiny):
+    """With eps = 0 the norm is exactly scale-invariant (a power-of-two scale),
+    so the first layer's contribution does not change when h0 is doubled:
+    h1(2 h0) - 2 h0 == h1(h0) - h0 up to the fp32 rounding of the stream.  A
+    norm applied after the block, or a dropped residual, breaks this."""
+    lay2 = synth.make_layer(synth.TINY, seed=5)
+    h0 = synth.residual(4, 4, 256)
+    a, _, _, _ = oracle_lib.stack([tiny], h0, eps=0.0)
+    b, _, _, _ = oracle_lib.stack([tiny], 2 * h0, eps=0.0)
+    da = a.astype(np.float64) - h0
+    db = b.astype(np.float64) - 2 * h0.astype(np.float64)
+    # each stream value is one fp32 rounding of an fp64 sum: half an ulp each
+    ulp = np.spacing(np.maximum(np.abs(a), np.abs(b))).astype(np.float64)
+    assert np.all(np.abs(da - db) <= ulp)
+    assert np.max(np.abs(da)) > 1e-3          # the block does contribute
+    # two layers: the second sees the first layer's updated stream
+    _, xs, _, _ = oracle_lib.stack([tiny, lay2], h0)
+    h1, _, _, _ = oracle_lib.stack([tiny], h0)
+    x1, _ = oracle_lib.rmsnorm(h1, 1e-6)
+    assert np.array_equal(xs[1], x1)
