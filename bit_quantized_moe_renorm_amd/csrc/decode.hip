@@ -60,7 +60,6 @@ __device__ __forceinline__ unsigned long long *ctr(const Work &W, int slot) {
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_THREADS = 64 * DEC_WAVES;
 constexpr int DEC_WG_PER_CU = 2;  // resident workgroups per CU
-constexpr int DEC_REPL = IQ2_REPL;  // level-table replicas (lane l reads replica l % 16)
 constexpr int DEC_GU_NR = 4;  // routed gate/up row slots per wave
 constexpr int DEC_DN_NR = 4;  // routed down row slots per wave
 
@@ -329,66 +328,101 @@ __device__ void dec_shgu_item(const Layer &L, const Work &W, const void *__restr
 }
 
 // ---------------------------------------------------------------- P2: routed gate/up (IQ2)
-// The lane's 64 values of x (its column chunk of every routed gate/up row), in
-// registers for the whole phase.
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+__device__ __forceinline__ float dec_dot2h(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+__device__ __forceinline__ uint32_t dec_pack_f16(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+
+// The lane's 64 values of x (its column chunk of every routed gate/up row) as
+// fp16 pairs, in registers for the whole phase, times 2^-k with k chosen from
+// the chunk's largest magnitude so no value overflows fp16 (the partial dot
+// products are scaled back by 2^k).  bf16 x converts exactly (fp16 has the
+// longer mantissa) except below fp16's normal range, whose share of a dot
+// product is under 2^-14 of the chunk's largest term; fp32 x is split into
+// an fp16 high part and an fp16 low part, 22 bits in all.
 template <bool XBF16>
-struct DecX;
-template <>
-struct DecX<true> {
-    uint32_t v[32];
+struct DecX {
+    static constexpr int NP = XBF16 ? 1 : 2;  // parts
+    uint32_t v[NP][32];
+    float scale;
     __device__ __forceinline__ void load(const void *x, int off) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + off);
+        float f[64];
+        if (XBF16) {
+            const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + off);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint4 r = p[i];
-            v[4 * i] = r.x, v[4 * i + 1] = r.y, v[4 * i + 2] = r.z, v[4 * i + 3] = r.w;
+            for (int i = 0; i < 8; ++i) {
+                const uint4 r = p[i];
+                const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f[8 * i + 2 * q] = __uint_as_float(w[q] << 16);
+                    f[8 * i + 2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+                }
+            }
+        } else {
+            const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float4 r = p[i];
+                f[4 * i] = r.x, f[4 * i + 1] = r.y, f[4 * i + 2] = r.z, f[4 * i + 3] = r.w;
+            }
+        }
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) mx = fmaxf(mx, fabsf(f[i]));
+        // 2^-k with mx * 2^-k < 2^15
+        const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFFu) - 127;
+        const int k = ex > 14 ? ex - 14 : 0;
+        const float down = __uint_as_float((uint32_t)(127 - k) << 23);
+        scale = __uint_as_float((uint32_t)(127 + k) << 23);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const float a = f[2 * i] * down, b = f[2 * i + 1] * down;
+            v[0][i] = dec_pack_f16(a, b);
+            if (!XBF16) {
+                const float ah = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[0][i] & 0xFFFFu));
+                const float bh = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[0][i] >> 16));
+                v[NP - 1][i] = dec_pack_f16(a - ah, b - bh);
+            }
         }
     }
+    // 8 weights (4 fp16 pairs) of group grp8 against the matching x
     __device__ __forceinline__ float dot8(const uint4 &Lv, int grp8, float s) const {
-        s = dec_dot2(Lv.x, v[4 * grp8], s);
-        s = dec_dot2(Lv.y, v[4 * grp8 + 1], s);
-        s = dec_dot2(Lv.z, v[4 * grp8 + 2], s);
-        s = dec_dot2(Lv.w, v[4 * grp8 + 3], s);
-        return s;
-    }
-};
-template <>
-struct DecX<false> {
-    float v[64];
-    __device__ __forceinline__ void load(const void *x, int off) {
-        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float4 r = p[i];
-            v[4 * i] = r.x, v[4 * i + 1] = r.y, v[4 * i + 2] = r.z, v[4 * i + 3] = r.w;
-        }
-    }
-    __device__ __forceinline__ float dot8(const uint4 &Lv, int grp8, float s) const {
-        const uint32_t l[4] = {Lv.x, Lv.y, Lv.z, Lv.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s = fmaf(__uint_as_float(l[i] << 16), v[8 * grp8 + 2 * i], s);
-            s = fmaf(__uint_as_float(l[i] & 0xFFFF0000u), v[8 * grp8 + 2 * i + 1], s);
+        for (int p = 0; p < NP; ++p) {
+            s = dec_dot2h(Lv.x, v[p][4 * grp8], s);
+            s = dec_dot2h(Lv.y, v[p][4 * grp8 + 1], s);
+            s = dec_dot2h(Lv.z, v[p][4 * grp8 + 2], s);
+            s = dec_dot2h(Lv.w, v[p][4 * grp8 + 3], s);
         }
         return s;
     }
 };
 
-// 64 IQ2 weights of one lane (two canonical sub-blocks) against x, before d/64.
-// (the lane's 64 weights are groups 8 c .. 8 c + 7 of the row; xc points at group 8 c)
+// 64 IQ2 weights of one lane (two canonical sub-blocks) against x, before d/64
+// and before the lane's x scale.  TL / TS: the level-byte and sign-byte tables
+// (entry e, replica r at e * IQ2B_REPL + r).
 template <bool XBF16>
-__device__ __forceinline__ float dec_iq2_dot(const uint4 *T, uint4 q, const DecX<XBF16> &xc, int rep) {
+__device__ __forceinline__ float dec_iq2_dot(const uint2 *TL, const uint2 *TS, uint4 q, const DecX<XBF16> &xc,
+                                             int rep) {
     float acc = 0.0f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
         const uint32_t ib = sb ? q.z : q.x;   // 4 codebook indices
         const uint32_t sw = sb ? q.w : q.y;   // signs (7 x 4) | ls << 28
-        float s = 0.0f;
+        uint2 lv[4], sv[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const uint4 Lv = iq2_group_levels<DEC_REPL>(T, (ib >> (8 * g)) & 0xFFu, (sw >> (7 * g)) & 0x7Fu, rep);
-            s = xc.dot8(Lv, 4 * sb + g, s);
+            lv[g] = TL[((ib >> (8 * g)) & 0xFFu) * IQ2B_REPL + rep];
+            sv[g] = TS[((sw >> (7 * g)) & 0x7Fu) * IQ2B_REPL + rep];
         }
+        float s = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            s = xc.dot8(iq2_expand_f16(make_uint2(lv[g].x ^ sv[g].x, lv[g].y ^ sv[g].y)), 4 * sb + g, s);
         acc = fmaf((float)(2u * (sw >> 28) + 1u), s, acc);
     }
     return acc;
@@ -404,10 +438,22 @@ __device__ __forceinline__ bool dec_route_wait(const Layer &L, const Work &W, co
     return true;
 }
 
-// Weights of one routed gate/up item for this lane: DEC_GU_NR rows of gate and up.
+// Load at a 32-bit byte offset from a workgroup-uniform base.  Every plane
+// read this way is below 4 GiB (the largest, an expert matrix plane, holds at
+// most 256 x 4096 x 4096 / 4 bytes), and a zero-extended 32-bit offset lets
+// the compiler keep the base in scalar registers and one offset per lane.
+template <class T>
+__device__ __forceinline__ T ld_at(const void *base, uint32_t off) {
+    return *reinterpret_cast<const T *>(reinterpret_cast<const uint8_t *>(base) + off);
+}
+
+// Weights of one routed gate/up item for this lane: DEC_GU_NR rows of gate and
+// up, with their fp16 scales d as loaded.  Nothing here looks at the loaded
+// values: the item after the current one is loaded while the current one is
+// computed, and any use of a value would wait for every load in flight.
 struct RguW {
     uint4 qg[DEC_GU_NR], qu[DEC_GU_NR];
-    float dg[DEC_GU_NR], du[DEC_GU_NR];
+    uint32_t dg[DEC_GU_NR], du[DEC_GU_NR];
 };
 
 __device__ __forceinline__ void dec_rgu_load(const Layer &L, const DecPlan &P, const RouteCache *rc, int item,
@@ -421,31 +467,31 @@ __device__ __forceinline__ void dec_rgu_load(const Layer &L, const DecPlan &P, c
     const int e = rc->idx[j];
 #pragma unroll
     for (int r = 0; r < DEC_GU_NR; ++r) {
-        // rows past n_ff (if any) read row n_ff - 1 with a zero scale
+        // rows past n_ff (if any) read row n_ff - 1; the computation drops them
         const int f = f0 + r * rpw;
-        const int64_t rb = ((int64_t)e * F + min(f, F - 1)) * L.nbe;
-        w.qg[r] = *reinterpret_cast<const uint4 *>(L.iq2_qs[0] + rb * 64 + c * 16);
-        w.qu[r] = *reinterpret_cast<const uint4 *>(L.iq2_qs[1] + rb * 64 + c * 16);
-        w.dg[r] = (f < F) ? half_to_f32(L.iq2_d[0][rb + (c >> 2)]) : 0.0f;
-        w.du[r] = (f < F) ? half_to_f32(L.iq2_d[1][rb + (c >> 2)]) : 0.0f;
+        const uint32_t rb = ((uint32_t)e * F + min(f, F - 1)) * L.nbe;
+        w.qg[r] = ld_at<uint4>(L.iq2_qs[0], rb * 64u + c * 16u);
+        w.qu[r] = ld_at<uint4>(L.iq2_qs[1], rb * 64u + c * 16u);
+        w.dg[r] = ld_at<uint16_t>(L.iq2_d[0], 2u * (rb + (c >> 2)));
+        w.du[r] = ld_at<uint16_t>(L.iq2_d[1], 2u * (rb + (c >> 2)));
     }
 }
 
 template <bool XBF16>
-__device__ __forceinline__ void dec_rgu_compute(const Layer &L, const Work &W, const DecX<XBF16> &xc, const uint4 *T,
-                                                int item, const DecPlan &P, const RguW &w) {
+__device__ __forceinline__ void dec_rgu_compute(const Layer &L, const Work &W, const DecX<XBF16> &xc, const uint2 *TL,
+                                                const uint2 *TS, int item, const DecPlan &P, const RguW &w) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd, F = L.n_ff;
     const int lpr = E >> 6, rpw = 64 / lpr;
     const int c = lane & (lpr - 1);
     const int j = item / P.rgu_per_slot, tile = item - j * P.rgu_per_slot;
     const int f0 = (tile * DEC_WAVES + wave) * (DEC_GU_NR * rpw) + lane / lpr;
-    const int rep = lane & (DEC_REPL - 1);
+    const int rep = lane & (IQ2B_REPL - 1);
 #pragma unroll
     for (int r = 0; r < DEC_GU_NR; ++r) {
         const int f = f0 + r * rpw;
-        float g = dec_iq2_dot<XBF16>(T, w.qg[r], xc, rep) * w.dg[r];
-        float u = dec_iq2_dot<XBF16>(T, w.qu[r], xc, rep) * w.du[r];
+        float g = dec_iq2_dot<XBF16>(TL, TS, w.qg[r], xc, rep) * (half_to_f32((uint16_t)w.dg[r]) * xc.scale);
+        float u = dec_iq2_dot<XBF16>(TL, TS, w.qu[r], xc, rep) * (half_to_f32((uint16_t)w.du[r]) * xc.scale);
         g = dec_group_sum(g, lpr) * 0.015625f;
         u = dec_group_sum(u, lpr) * 0.015625f;
         if (c == 0 && f < F) st_shared(W.hbuf + (int64_t)j * F + f, dec_silu(g) * u);
@@ -546,12 +592,12 @@ __device__ __forceinline__ void dec_rdn_load(const Layer &L, const DecPlan &P, c
     const int e = rc->idx[j];
 #pragma unroll
     for (int r = 0; r < DEC_DN_NR; ++r) {
-        // rows past n_embd (if any) read row n_embd - 1 with zero scales
+        // rows past n_embd (if any) read row n_embd - 1; the computation drops them
         const int row = r0 + r * rpw;
-        const int64_t rb = ((int64_t)e * E + min(row, E - 1)) * L.nbf;
-        w.qs[r] = *reinterpret_cast<const uint4 *>(L.q2k_qs + rb * 64 + c * 16);
-        w.sc[r] = *reinterpret_cast<const uint32_t *>(L.q2k_sc + rb * 16 + c * 4);
-        w.dd[r] = (row < E) ? L.q2k_dd[rb + (c >> 2)] : 0u;
+        const uint32_t rb = ((uint32_t)e * E + min(row, E - 1)) * L.nbf;
+        w.qs[r] = ld_at<uint4>(L.q2k_qs, rb * 64u + c * 16u);
+        w.sc[r] = ld_at<uint32_t>(L.q2k_sc, rb * 16u + c * 4u);
+        w.dd[r] = ld_at<uint32_t>(L.q2k_dd, 4u * (rb + (c >> 2)));
     }
 }
 
@@ -595,7 +641,8 @@ __device__ __forceinline__ bool dec_rdn_compute(const Layer &L, const Work &W, f
 template <bool XBF16>
 __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Layer L, Work W, const void *__restrict__ x,
                                                              float *__restrict__ out, DecPlan P) {
-    __shared__ uint4 T[256 * DEC_REPL];
+    __shared__ uint2 TL[256 * IQ2B_REPL];  // level bytes per codebook entry
+    __shared__ uint2 TS[128 * IQ2B_REPL];  // sign bytes per pattern of 7 stored signs
     __shared__ int lds_flag;
     __shared__ double lds_part[DEC_WAVES];
     __shared__ RouteCache rc;
@@ -613,15 +660,19 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
     xc.load(x, 64 * ((threadIdx.x & 63) & ((L.n_embd >> 6) - 1)));
     int it = blockIdx.x;
     for (; it < b0; it += G) dec_route_item<XBF16>(L, W, x, it, &lds_flag, lds_part, P);
-    // the IQ2 level table (entry e, replica r at e * DEC_REPL + r)
+    // the IQ2 byte tables (entry e, replica r at e * IQ2B_REPL + r)
     {
-        uint32_t v[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = iq2_level_bf16((cb >> (2 * q)) & 3u);
-        const uint4 ent = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
         static_assert(DEC_THREADS == 256, "one codebook entry per thread");
+        const uint2 ent = iq2_level_bytes(cb);
 #pragma unroll
-        for (int r = 0; r < DEC_REPL; ++r) T[threadIdx.x * DEC_REPL + ((r + threadIdx.x) & (DEC_REPL - 1))] = ent;
+        for (int r = 0; r < IQ2B_REPL; ++r)
+            TL[threadIdx.x * IQ2B_REPL + ((r + threadIdx.x) & (IQ2B_REPL - 1))] = ent;
+        if (threadIdx.x < 128) {
+            const uint2 sg = iq2_sign_bytes(threadIdx.x);
+#pragma unroll
+            for (int r = 0; r < IQ2B_REPL; ++r)
+                TS[threadIdx.x * IQ2B_REPL + ((r + threadIdx.x) & (IQ2B_REPL - 1))] = sg;
+        }
     }
     __syncthreads();
     // the shared expert's gate/up needs no routing: it streams while the
@@ -635,12 +686,12 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
         for (;;) {
             bool more = it + G < b2;
             if (more) dec_rgu_load(L, P, &rc, it + G - b1, wb);
-            dec_rgu_compute<XBF16>(L, W, xc, T, it - b1, P, wa);
+            dec_rgu_compute<XBF16>(L, W, xc, TL, TS, it - b1, P, wa);
             it += G;
             if (!more) break;
             more = it + G < b2;
             if (more) dec_rgu_load(L, P, &rc, it + G - b1, wa);
-            dec_rgu_compute<XBF16>(L, W, xc, T, it - b1, P, wb);
+            dec_rgu_compute<XBF16>(L, W, xc, TL, TS, it - b1, P, wb);
             it += G;
             if (!more) break;
         }

@@ -81,4 +81,37 @@ __device__ __forceinline__ uint4 iq2_group_levels(const uint4 *T, uint32_t idx, 
     return iq2_apply_signs(T[idx * R + rep], s7);
 }
 
+// ---------------------------------------------------------------- byte tables
+// For fp16 dot products a group fits in 8 bytes.  The levels 1, 3, 5, 7 are
+// fp16 numbers whose low byte is zero (0x3C00, 0x4200, 0x4500, 0x4700), and
+// the fp16 sign is bit 7 of the high byte.  So one table holds each codebook
+// entry's 8 level bytes and another each sign pattern's 8 sign bytes (the 8th
+// sign from the parity of the 7 stored ones).  A group's signed levels are
+// the XOR of the two 8-byte words, spread into 4 fp16 pairs by v_perm.
+constexpr int IQ2B_REPL = 16;  // replicas of both byte tables (8 bytes each)
+
+__device__ __forceinline__ uint32_t iq2_level_f16hi(uint32_t c) {
+    return (c == 0) ? 0x3Cu : (c == 1) ? 0x42u : (c == 2) ? 0x45u : 0x47u;
+}
+// Level bytes of codebook entry cb (coordinate i in bits 2i..2i+1): byte i.
+__device__ __forceinline__ uint2 iq2_level_bytes(uint32_t cb) {
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = iq2_level_f16hi((cb >> (2 * i)) & 3u);
+    return make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+}
+// Sign bytes of the 7 stored sign bits s7: bit 7 of byte i is weight i's sign.
+__device__ __forceinline__ uint2 iq2_sign_bytes(uint32_t s7) {
+    const uint32_t s8 = s7 | ((__builtin_popcount(s7) & 1u) << 7);
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = ((s8 >> i) & 1u) << 7;
+    return make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+}
+// 8 signed level bytes -> 4 fp16 pairs (weights 2j | 2j+1 << 16 in dword j).
+__device__ __forceinline__ uint4 iq2_expand_f16(uint2 v) {
+    return make_uint4(__builtin_amdgcn_perm(0u, v.x, 0x010C000Cu), __builtin_amdgcn_perm(0u, v.x, 0x030C020Cu),
+                      __builtin_amdgcn_perm(0u, v.y, 0x010C000Cu), __builtin_amdgcn_perm(0u, v.y, 0x030C020Cu));
+}
+
 }  // namespace ds4
