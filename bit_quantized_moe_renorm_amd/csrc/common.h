@@ -60,7 +60,10 @@ struct Work {
     int32_t *nchunks;     // number of valid chunks
     int32_t *ecount;      // [MAX_EXPERT] tokens per expert (batched router)
     float *rest;          // [4][max_tokens][NE] partial router estimates (batched router)
-    double *rhalf;        // [NE][2] fp64 half-row router sums (fused decode)
+    unsigned long long *rtag;  // [NE][2][2] fused decode: each fp64 half-row router sum as two 32-bit
+                               // halves, each tagged with the call's epoch in its upper 32 bits
+    unsigned long long *htag;  // [k+1][F] fused decode: SwiGLU outputs of the routed slots and the
+                               // shared expert (fp32 bits), each tagged like rtag
 };
 
 // ---------------------------------------------------------------- small device helpers

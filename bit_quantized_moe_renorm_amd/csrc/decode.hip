@@ -52,9 +52,18 @@ __device__ __forceinline__ float dec_group_sum(float v, int lpr) {
 // `ep` of a handle waits for (ep + 1) times the per-call count, so nothing has
 // to be reset at the end of a launch.
 constexpr int CSTRIDE = 32;  // in uint64
-constexpr int C_ROUTE = 1, C_SHGU = 3, C_ERR = 4, C_GU = 5;  // C_GU + slot; slot units
+constexpr int C_SHGU = 3, C_ERR = 4, C_GU = 5;  // C_GU + slot; slot units
 __device__ __forceinline__ unsigned long long *ctr(const Work &W, int slot) {
     return reinterpret_cast<unsigned long long *>(W.counters) + slot * CSTRIDE;
+}
+
+// Load at a 32-bit byte offset from a workgroup-uniform base.  Every plane
+// read this way is below 4 GiB (the largest, an expert matrix plane, holds at
+// most 256 x 4096 x 4096 / 4 bytes), and a zero-extended 32-bit offset lets
+// the compiler keep the base in scalar registers and one offset per lane.
+template <class T>
+__device__ __forceinline__ T ld_at(const void *base, uint32_t off) {
+    return *reinterpret_cast<const T *>(reinterpret_cast<const uint8_t *>(base) + off);
 }
 
 constexpr int DEC_WAVES = 4;
@@ -88,6 +97,13 @@ __device__ __forceinline__ void st_shared(float *p, float v) {
 }
 __device__ __forceinline__ void st_shared(int *p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One tagged word: fp32 bits below, the call's tag above.  A 64-bit store is
+// seen whole or not at all, so a reader that finds the tag has the value.
+__device__ __forceinline__ void st_tagged(unsigned long long *p, float v, uint32_t tag) {
+    __hip_atomic_store(p, ((unsigned long long)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // This wavefront's shared stores are complete.
@@ -160,22 +176,19 @@ struct RouteCache {
     float w[MAX_TOPK];
 };
 
-__device__ __forceinline__ void dec_topk_local(const Layer &L, const Work &W, const double *part, RouteCache *rc,
+__device__ __forceinline__ void dec_topk_local(const Layer &L, const Work &W, const double *lg, RouteCache *rc,
                                                bool write_global) {
     const int lane = threadIdx.x & 63;
     const int NE = L.n_expert, k = L.top_k;
-    // fp32 logits as order-preserving keys (0 = no expert); lane l holds experts l + 64 i.
-    // The halves were stored by other workgroups with write-through stores and
-    // no workgroup reads those lines before the count is complete: plain loads
-    // are coherent.
+    // fp32 logits as order-preserving keys (0 = no expert); lane l holds
+    // experts l + 64 i, whose fp64 logits (both halves and the bias) are lg[i]
     uint32_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int ee = lane + 64 * i;
         key[i] = 0u;
         if (ee < NE) {
-            const double2 hh = *reinterpret_cast<const double2 *>(part + 2 * ee);
-            const float Lf = (float)(hh.x + hh.y + (L.router_bias ? (double)L.router_bias[ee] : 0.0));
+            const float Lf = (float)lg[i];
             const uint32_t u = __float_as_uint(Lf);
             key[i] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
             if (key[i] == 0u) key[i] = 1u;  // keep 0 free for "taken"
@@ -237,12 +250,11 @@ __device__ __forceinline__ void dec_topk_local(const Layer &L, const Work &W, co
 
 // Half h of expert e's logit: waves split the half row (E/2 elements).
 template <bool XBF16>
-__device__ void dec_route_item(const Layer &L, const Work &W, const void *__restrict__ x, int item, int *lds_flag,
-                               double *lds_part, const DecPlan &P) {
+__device__ void dec_route_item(const Layer &L, const Work &W, const void *__restrict__ x, int item,
+                               double *lds_part, uint32_t tag) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd;
     const int e = item >> 1, h = item & 1;
-    double *part = W.rhalf;
     const int half = E >> 1, per_wave = half >> 2;   // E/8 elements per wave
     const int base = h * half + wave * per_wave;
     double acc = 0.0;
@@ -264,67 +276,83 @@ __device__ void dec_route_item(const Layer &L, const Work &W, const void *__rest
     acc = wave_sum(acc);
     if (lane == 0) lds_part[wave] = acc;
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x < 2) {
+        // the half-sum's two 32-bit halves, each in one 64-bit store with the
+        // call's tag above it: a reader that finds the tag has that half
         const double sum = lds_part[0] + lds_part[1] + lds_part[2] + lds_part[3];
-        __hip_atomic_store(part + 2 * e + h, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long bits = (unsigned long long)__double_as_longlong(sum);
+        const unsigned long long part = threadIdx.x ? (bits >> 32) : (bits & 0xFFFFFFFFull);
+        __hip_atomic_store(W.rtag + 4 * e + 2 * h + threadIdx.x, ((unsigned long long)tag << 32) | part,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // count the half (the increment's result is not needed)
-    stores_done();
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr(W, C_ROUTE), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- P1: shared gate/up
+// One shared gate/up item (one row of gate and up per wave): the weights and
+// the matching x chunks (chunk ch = lane + 64 c, 8 elements each), as loaded.
 template <bool XBF16>
-__device__ void dec_shgu_item(const Layer &L, const Work &W, const void *__restrict__ x, int item) {
+struct ShguW {
+    uint4 wg[8], wu[8];
+    uint4 xv[XBF16 ? 8 : 16];
+};
+template <bool XBF16>
+__device__ __forceinline__ void dec_shgu_load(const Layer &L, const void *__restrict__ x, int item, ShguW<XBF16> &w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int E = L.n_embd, F = L.n_ff;
+    const int nch = E >> 3;  // 16-byte chunks per row
+    // rows past n_ff and chunks past the row read valid data that the
+    // computation drops
+    const int f = min(item * DEC_WAVES + wave, F - 1);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t ch = min(lane + 64 * c, nch - 1);
+        w.wg[c] = ld_at<uint4>(L.sh_gate, 2u * ((uint32_t)f * E + ch * 8u));
+        w.wu[c] = ld_at<uint4>(L.sh_up, 2u * ((uint32_t)f * E + ch * 8u));
+        if (XBF16) {
+            w.xv[c] = ld_at<uint4>(x, 16u * ch);
+        } else {
+            w.xv[2 * c] = ld_at<uint4>(x, 32u * ch);
+            w.xv[2 * c + 1] = ld_at<uint4>(x, 32u * ch + 16u);
+        }
+    }
+}
+template <bool XBF16>
+__device__ __forceinline__ void dec_shgu_compute(const Layer &L, const Work &W, int item, const ShguW<XBF16> &w,
+                                                 uint32_t tag) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd, F = L.n_ff, k = L.top_k;
-    const int nch = E >> 3;  // 16-byte chunks per row
+    const int nch = E >> 3;
     const int f = item * DEC_WAVES + wave;
-    if (f < F) {
-        uint4 wg[8], wu[8];
+    float g = 0.0f, u = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int ch = lane + 64 * c;
-            if (ch < nch) {
-                wg[c] = *reinterpret_cast<const uint4 *>(L.sh_gate + (int64_t)f * E + ch * 8);
-                wu[c] = *reinterpret_cast<const uint4 *>(L.sh_up + (int64_t)f * E + ch * 8);
+    for (int c = 0; c < 8; ++c) {
+        if (lane + 64 * c < nch) {
+            if (XBF16) {
+                const uint4 xv = w.xv[c];
+                g = dec_dot2(w.wg[c].x, xv.x, g), g = dec_dot2(w.wg[c].y, xv.y, g);
+                g = dec_dot2(w.wg[c].z, xv.z, g), g = dec_dot2(w.wg[c].w, xv.w, g);
+                u = dec_dot2(w.wu[c].x, xv.x, u), u = dec_dot2(w.wu[c].y, xv.y, u);
+                u = dec_dot2(w.wu[c].z, xv.z, u), u = dec_dot2(w.wu[c].w, xv.w, u);
             } else {
-                wg[c] = wu[c] = make_uint4(0, 0, 0, 0);
-            }
-        }
-        float g = 0.0f, u = 0.0f;
+                const uint4 a = w.xv[2 * c], b = w.xv[2 * c + 1];
+                const float xf[8] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
+                                     __uint_as_float(a.w), __uint_as_float(b.x), __uint_as_float(b.y),
+                                     __uint_as_float(b.z), __uint_as_float(b.w)};
+                const uint32_t gw[4] = {w.wg[c].x, w.wg[c].y, w.wg[c].z, w.wg[c].w};
+                const uint32_t uw[4] = {w.wu[c].x, w.wu[c].y, w.wu[c].z, w.wu[c].w};
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int ch = lane + 64 * c;
-            if (ch < nch) {
-                if (XBF16) {
-                    const uint4 xv = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + ch * 8);
-                    g = dec_dot2(wg[c].x, xv.x, g), g = dec_dot2(wg[c].y, xv.y, g);
-                    g = dec_dot2(wg[c].z, xv.z, g), g = dec_dot2(wg[c].w, xv.w, g);
-                    u = dec_dot2(wu[c].x, xv.x, u), u = dec_dot2(wu[c].y, xv.y, u);
-                    u = dec_dot2(wu[c].z, xv.z, u), u = dec_dot2(wu[c].w, xv.w, u);
-                } else {
-                    const float4 *xp = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + ch * 8);
-                    const float4 a = xp[0], b = xp[1];
-                    const float xf[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-                    const uint32_t gw[4] = {wg[c].x, wg[c].y, wg[c].z, wg[c].w};
-                    const uint32_t uw[4] = {wu[c].x, wu[c].y, wu[c].z, wu[c].w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        g = fmaf(__uint_as_float(gw[i] << 16), xf[2 * i], g);
-                        g = fmaf(__uint_as_float(gw[i] & 0xFFFF0000u), xf[2 * i + 1], g);
-                        u = fmaf(__uint_as_float(uw[i] << 16), xf[2 * i], u);
-                        u = fmaf(__uint_as_float(uw[i] & 0xFFFF0000u), xf[2 * i + 1], u);
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    g = fmaf(__uint_as_float(gw[i] << 16), xf[2 * i], g);
+                    g = fmaf(__uint_as_float(gw[i] & 0xFFFF0000u), xf[2 * i + 1], g);
+                    u = fmaf(__uint_as_float(uw[i] << 16), xf[2 * i], u);
+                    u = fmaf(__uint_as_float(uw[i] & 0xFFFF0000u), xf[2 * i + 1], u);
                 }
             }
         }
-        g = wave_sum(g);
-        u = wave_sum(u);
-        if (lane == 0) st_shared(W.hbuf + (int64_t)k * F + f, dec_silu(g) * u);
     }
-    publish_item(ctr(W, C_SHGU));
+    g = wave_sum(g);
+    u = wave_sum(u);
+    if (lane == 0 && f < F) st_tagged(W.htag + (int64_t)k * F + f, dec_silu(g) * u, tag);
 }
 
 // ---------------------------------------------------------------- P2: routed gate/up (IQ2)
@@ -428,23 +456,63 @@ __device__ __forceinline__ float dec_iq2_dot(const uint2 *TL, const uint2 *TS, u
     return acc;
 }
 
-// Wait until every router half is counted, then route locally.  Returns
-// false if the bounded wait expired.
-__device__ __forceinline__ bool dec_route_wait(const Layer &L, const Work &W, const DecPlan &P, RouteCache *rc,
+// Wait until every router half-sum of this call is stored, then route
+// locally (wave 0).  Each lane polls the tagged words of its experts (l + 64 i)
+// with agent-scope loads until all carry this call's tag: the values come
+// with the tags, in one round trip once they are there.  Returns false if the
+// bounded wait expired.
+__device__ __forceinline__ bool dec_route_wait(const Layer &L, const Work &W, uint32_t tag, RouteCache *rc,
                                                int *lds_flag) {
-    if (!wait_items(W, ctr(W, C_ROUTE), (P.ep + 1) * (unsigned long long)P.n_route, lds_flag)) return false;
-    if (threadIdx.x < 64) dec_topk_local(L, W, W.rhalf, rc, blockIdx.x == 0);
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x, NE = L.n_expert;
+        float bias[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            bias[i] = L.router_bias ? L.router_bias[min(lane + 64 * i, NE - 1)] : 0.0f;
+        unsigned long long v[4][4];
+        uint32_t missing = 0;  // bit 4 i + q: word q of expert lane + 64 i not yet of this call
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v[i][q] = 0;
+                if (lane + 64 * i < NE) missing |= 1u << (4 * i + q);
+            }
+        int spins = 0, ok = 1;
+        while (true) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (missing & (1u << (4 * i + q))) {
+                        v[i][q] = __hip_atomic_load(W.rtag + 4 * (lane + 64 * i) + q, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+                        if ((uint32_t)(v[i][q] >> 32) == tag) missing &= ~(1u << (4 * i + q));
+                    }
+            if (!__any(missing != 0)) break;
+            __builtin_amdgcn_s_sleep(4);
+            if (++spins > SPIN_LIMIT) {
+                if (lane == 0) __hip_atomic_store(ctr(W, C_ERR), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = 0;
+                break;
+            }
+        }
+        if (ok) {
+            double lg[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const double h0 = __longlong_as_double((long long)((v[i][0] & 0xFFFFFFFFull) | (v[i][1] << 32)));
+                const double h1 = __longlong_as_double((long long)((v[i][2] & 0xFFFFFFFFull) | (v[i][3] << 32)));
+                lg[i] = h0 + h1 + (double)bias[i];
+            }
+            dec_topk_local(L, W, lg, rc, blockIdx.x == 0);
+        }
+        if (lane == 0) *lds_flag = ok;
+    }
     __syncthreads();
-    return true;
-}
-
-// Load at a 32-bit byte offset from a workgroup-uniform base.  Every plane
-// read this way is below 4 GiB (the largest, an expert matrix plane, holds at
-// most 256 x 4096 x 4096 / 4 bytes), and a zero-extended 32-bit offset lets
-// the compiler keep the base in scalar registers and one offset per lane.
-template <class T>
-__device__ __forceinline__ T ld_at(const void *base, uint32_t off) {
-    return *reinterpret_cast<const T *>(reinterpret_cast<const uint8_t *>(base) + off);
+    const bool ok = *lds_flag != 0;
+    __syncthreads();
+    return ok;
 }
 
 // Weights of one routed gate/up item for this lane: DEC_GU_NR rows of gate and
@@ -479,7 +547,8 @@ __device__ __forceinline__ void dec_rgu_load(const Layer &L, const DecPlan &P, c
 
 template <bool XBF16>
 __device__ __forceinline__ void dec_rgu_compute(const Layer &L, const Work &W, const DecX<XBF16> &xc, const uint2 *TL,
-                                                const uint2 *TS, int item, const DecPlan &P, const RguW &w) {
+                                                const uint2 *TS, int item, const DecPlan &P, const RguW &w,
+                                                uint32_t tag) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd, F = L.n_ff;
     const int lpr = E >> 6, rpw = 64 / lpr;
@@ -494,54 +563,124 @@ __device__ __forceinline__ void dec_rgu_compute(const Layer &L, const Work &W, c
         float u = dec_iq2_dot<XBF16>(TL, TS, w.qu[r], xc, rep) * (half_to_f32((uint16_t)w.du[r]) * xc.scale);
         g = dec_group_sum(g, lpr) * 0.015625f;
         u = dec_group_sum(u, lpr) * 0.015625f;
-        if (c == 0 && f < F) st_shared(W.hbuf + (int64_t)j * F + f, dec_silu(g) * u);
+        if (c == 0 && f < F) st_tagged(W.htag + (int64_t)j * F + f, dec_silu(g) * u, tag);
     }
-    publish_item(ctr(W, C_GU + j));
+}
+
+// ---------------------------------------------------------------- h vectors in LDS
+// h vector float4 u (elements 4u .. 4u+3, in chunk c = u / 16) sits at slot
+// 16 c + ((u % 16) ^ (c % 16)): the 16 lanes reading float4 i of their
+// 64-element chunks hit 16 different bank quads, and so do lanes reading
+// consecutive 8-element chunks.
+__device__ __forceinline__ int h_slot(int u) { return (u & ~15) | ((u & 15) ^ ((u >> 4) & 15)); }
+
+// Staging h vector `slot` of this call into H in two parts.  dec_h_issue
+// loads the thread's tagged words (float4 u = thread + 256 q of h) early, so
+// their round trip overlaps other work; dec_h_finish polls again whatever did
+// not carry this call's tag yet, then stores the values.  dec_h_finish
+// returns false, for the whole workgroup, if the bounded wait expired.
+struct HPre {
+    unsigned long long v[4][4];
+};
+__device__ __forceinline__ void dec_h_issue(const Work &W, int F, int slot, HPre &p) {
+    const unsigned long long *src = W.htag + (int64_t)slot * F;
+    const int n4 = F >> 2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        // past the vector: re-read its last float4, ignored below
+        const int u = min((int)threadIdx.x + 256 * q, n4 - 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            p.v[q][e] = __hip_atomic_load(src + 4 * u + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+__device__ __forceinline__ bool dec_h_finish(const Work &W, int F, int slot, uint32_t tag, float4 *H, HPre &p) {
+    const unsigned long long *src = W.htag + (int64_t)slot * F;
+    const int n4 = F >> 2;  // float4 of h
+    // the previous item's reads of H are over
+    __syncthreads();
+    int ok = 1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int u = threadIdx.x + 256 * q;
+        if (ok && u < n4) {
+            unsigned long long *v = p.v[q];
+            uint32_t missing = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if ((uint32_t)(v[e] >> 32) != tag) missing |= 1u << e;
+            int spins = 0;
+            while (missing) {
+                __builtin_amdgcn_s_sleep(4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (missing & (1u << e)) {
+                        v[e] = __hip_atomic_load(src + 4 * u + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if ((uint32_t)(v[e] >> 32) == tag) missing &= ~(1u << e);
+                    }
+                if (missing && ++spins > SPIN_LIMIT) {
+                    __hip_atomic_store(ctr(W, C_ERR), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    ok = 0;
+                    break;
+                }
+            }
+            if (ok)
+                H[h_slot(u)] = make_float4(__uint_as_float((uint32_t)v[0]), __uint_as_float((uint32_t)v[1]),
+                                           __uint_as_float((uint32_t)v[2]), __uint_as_float((uint32_t)v[3]));
+        }
+    }
+    return __syncthreads_and(ok) != 0;
+}
+// Both parts at once.
+__device__ __forceinline__ bool dec_stage_h(const Work &W, int F, int slot, uint32_t tag, float4 *H) {
+    HPre p;
+    dec_h_issue(W, F, slot, p);
+    return dec_h_finish(W, F, slot, tag, H, p);
 }
 
 // ---------------------------------------------------------------- P3: shared down
 // CPR = 16-byte chunks per lane per row (F / 512, at least 1); 16 chunk loads in
 // flight per wave, i.e. 16 / CPR rows per wave.
 template <int CPR>
-__device__ void dec_shdn_item(const Layer &L, const Work &W, float *__restrict__ out, int item, const DecPlan &P,
-                              int *lds_flag) {
+__device__ void dec_shdn_item(const Layer &L, const Work &W, float *__restrict__ out, int item, uint32_t tag,
+                              float4 *H, int &hid, bool &ok) {
     constexpr int RPW = 16 / CPR;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd, F = L.n_ff, k = L.top_k;
     const int nch = F >> 3;
     const int r0 = (item * DEC_WAVES + wave) * RPW;
-    // the weights do not depend on the gate/up phase: issue them first
+    // the weights do not depend on the gate/up phase: issue them first (rows
+    // and chunks past the matrix read valid data that is dropped below)
     uint4 wv[RPW][CPR];
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr)
 #pragma unroll
         for (int c = 0; c < CPR; ++c) {
-            const int row = r0 + rr, ch = lane + 64 * c;
-            wv[rr][c] = (row < E && ch < nch) ? *reinterpret_cast<const uint4 *>(L.sh_down + (int64_t)row * F + ch * 8)
-                                              : make_uint4(0, 0, 0, 0);
+            const uint32_t row = min(r0 + rr, E - 1), ch = min(lane + 64 * c, nch - 1);
+            wv[rr][c] = ld_at<uint4>(L.sh_down, 2u * (row * F + ch * 8u));
         }
-    if (!wait_items(W, ctr(W, C_SHGU), (P.ep + 1) * (unsigned long long)P.n_shgu, lds_flag)) return;
-    const float *hs = W.hbuf + (int64_t)k * F;
+    // the shared h vector in LDS (its gate/up items, once all stored)
+    if (hid != k) {
+        if (!dec_stage_h(W, F, k, tag, H)) {
+            ok = false;
+            return;
+        }
+        hid = k;
+    }
     float hv[CPR][8];
 #pragma unroll
     for (int c = 0; c < CPR; ++c) {
-        const int ch = lane + 64 * c;
-        if (ch < nch) {
-            // plain loads: these lines are first touched now, after every producer finished
-            const float4 *p = reinterpret_cast<const float4 *>(hs + ch * 8);
-            const float4 a = p[0], b = p[1];
-            hv[c][0] = a.x, hv[c][1] = a.y, hv[c][2] = a.z, hv[c][3] = a.w;
-            hv[c][4] = b.x, hv[c][5] = b.y, hv[c][6] = b.z, hv[c][7] = b.w;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) hv[c][i] = 0.0f;
-        }
+        const int ch = min(lane + 64 * c, nch - 1);
+        const float4 a = H[h_slot(2 * ch)], b = H[h_slot(2 * ch + 1)];
+        hv[c][0] = a.x, hv[c][1] = a.y, hv[c][2] = a.z, hv[c][3] = a.w;
+        hv[c][4] = b.x, hv[c][5] = b.y, hv[c][6] = b.z, hv[c][7] = b.w;
     }
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
         float y = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPR; ++c) {
+            if (lane + 64 * c >= nch) continue;
             const uint32_t a[4] = {wv[rr][c].x, wv[rr][c].y, wv[rr][c].z, wv[rr][c].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -556,24 +695,6 @@ __device__ void dec_shdn_item(const Layer &L, const Work &W, float *__restrict__
 }
 
 // ---------------------------------------------------------------- P4: routed down (Q2_K)
-__device__ __forceinline__ float dec_q2k_dot(uint4 qs, uint32_t sc, uint32_t dd, const float *hv, const float *hsum) {
-    const uint32_t Q[4] = {qs.x, qs.y, qs.z, qs.w};
-    float A = 0.0f, B = 0.0f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        float dot = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t tq = (Q[s] >> (2 * u)) & 0x03030303u;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) dot = fmaf((float)((tq >> (8 * b)) & 0xFFu), hv[16 * s + 4 * b + u], dot);
-        }
-        const uint32_t scb = (sc >> (8 * s)) & 0xFFu;
-        A = fmaf((float)(scb & 15u), dot, A);
-        B = fmaf((float)(scb >> 4), hsum[s], B);
-    }
-    return half_to_f32((uint16_t)(dd & 0xFFFFu)) * A - half_to_f32((uint16_t)(dd >> 16)) * B;
-}
 
 // Weights of one routed down item for this lane: DEC_DN_NR rows.
 struct RdnW {
@@ -601,9 +722,11 @@ __device__ __forceinline__ void dec_rdn_load(const Layer &L, const DecPlan &P, c
     }
 }
 
-// Returns false if the wait for the slot's gate/up items expired.
-__device__ __forceinline__ bool dec_rdn_compute(const Layer &L, const Work &W, float *__restrict__ out, int item,
-                                                const DecPlan &P, int *lds_flag, const RouteCache *rc, const RdnW &w) {
+// H holds the slot's h vector (staged by the caller).  Each Q2_K row of the
+// lane (64 weights: 4 sub-blocks of 16, weight 16 s + 4 b + u in bits 2u of
+// byte b of word s) is d * sum_s sc_s dot_s - dmin * sum_s m_s hsum_s.
+__device__ __forceinline__ void dec_rdn_compute(const Layer &L, float *__restrict__ out, int item, const DecPlan &P,
+                                                const RouteCache *rc, const RdnW &w, const float4 *H) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd, F = L.n_ff;
     const int lpr = F >> 6, rpw = 64 / lpr;
@@ -611,30 +734,51 @@ __device__ __forceinline__ bool dec_rdn_compute(const Layer &L, const Work &W, f
     const int j = item / P.rdn_per_slot, tile = item - j * P.rdn_per_slot;
     const int r0 = (tile * DEC_WAVES + wave) * (DEC_DN_NR * rpw) + lane / lpr;
     const float wgt = rc->w[j];
-    if (!wait_items(W, ctr(W, C_GU + j), (P.ep + 1) * (unsigned long long)P.rgu_per_slot, lds_flag)) return false;
-    float hv[64], hsum[4];
-    // plain loads: these lines are first touched now, after every producer finished
-    const float4 *hp = reinterpret_cast<const float4 *>(W.hbuf + (int64_t)j * F + 64 * c);
+    float A[DEC_DN_NR], B[DEC_DN_NR];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float4 v = hp[i];
-        hv[4 * i] = v.x, hv[4 * i + 1] = v.y, hv[4 * i + 2] = v.z, hv[4 * i + 3] = v.w;
-    }
+    for (int r = 0; r < DEC_DN_NR; ++r) A[r] = 0.0f, B[r] = 0.0f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        float a = 0.0f;
+        float hv[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) a += hv[16 * s + i];
-        hsum[s] = a;
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = H[h_slot(16 * c + 4 * s + q)];
+            hv[4 * q] = v.x, hv[4 * q + 1] = v.y, hv[4 * q + 2] = v.z, hv[4 * q + 3] = v.w;
+        }
+        float hsum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) hsum += hv[q];
+#pragma unroll
+        for (int r = 0; r < DEC_DN_NR; ++r) {
+            const uint32_t Q = s == 0 ? w.qs[r].x : s == 1 ? w.qs[r].y : s == 2 ? w.qs[r].z : w.qs[r].w;
+            float dot = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t tq = (Q >> (2 * u)) & 0x03030303u;
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) dot = fmaf((float)((tq >> (8 * bb)) & 0xFFu), hv[4 * bb + u], dot);
+            }
+            const uint32_t scb = (w.sc[r] >> (8 * s)) & 0xFFu;
+            A[r] = fmaf((float)(scb & 15u), dot, A[r]);
+            B[r] = fmaf((float)(scb >> 4), hsum, B[r]);
+        }
     }
 #pragma unroll
     for (int r = 0; r < DEC_DN_NR; ++r) {
         const int row = r0 + r * rpw;
-        float y = dec_q2k_dot(w.qs[r], w.sc[r], w.dd[r], hv, hsum);
+        const uint32_t dd = w.dd[r];
+        float y = half_to_f32((uint16_t)(dd & 0xFFFFu)) * A[r] - half_to_f32((uint16_t)(dd >> 16)) * B[r];
         y = dec_group_sum(y, lpr);
         if (c == 0 && row < E) atomicAdd(out + row, wgt * y);
     }
-    return true;
+}
+
+// Routed down items are handed out so that each workgroup's units are
+// consecutive (slot-major), so they mostly share one h vector: local item
+// l = G m + o (o < G) is unit o q + min(o, r) + m, with n = q G + r units.
+__device__ __forceinline__ int dec_rdn_unit(int l, int G, int n) {
+    const int o = l % G, q = n / G, r = n % G;
+    return o * q + min(o, r) + l / G;
 }
 
 // ---------------------------------------------------------------- the persistent kernel
@@ -646,6 +790,7 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
     __shared__ int lds_flag;
     __shared__ double lds_part[DEC_WAVES];
     __shared__ RouteCache rc;
+    __shared__ float4 H[1024];             // an h vector (n_ff <= 4096) staged for the down projections
     const int G = gridDim.x;
     // item order: router, shared gate/up, routed gate/up, routed down, shared down;
     // every wait is on an earlier phase
@@ -659,7 +804,8 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
     DecX<XBF16> xc;
     xc.load(x, 64 * ((threadIdx.x & 63) & ((L.n_embd >> 6) - 1)));
     int it = blockIdx.x;
-    for (; it < b0; it += G) dec_route_item<XBF16>(L, W, x, it, &lds_flag, lds_part, P);
+    const uint32_t tag = (uint32_t)(P.ep % 0xFFFFFFFFull) + 1u;  // never 0, the workspace's initial value
+    for (; it < b0; it += G) dec_route_item<XBF16>(L, W, x, it, lds_part, tag);
     // the IQ2 byte tables (entry e, replica r at e * IQ2B_REPL + r)
     {
         static_assert(DEC_THREADS == 256, "one codebook entry per thread");
@@ -675,50 +821,72 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
         }
     }
     __syncthreads();
-    // the shared expert's gate/up needs no routing: it streams while the
-    // router halves are counted
-    for (; it < b1; it += G) dec_shgu_item<XBF16>(L, W, x, it - b0);
-    bool ok = dec_route_wait(L, W, P, &rc, &lds_flag);
+    // the first shared gate/up item's weights stream while the routing is
+    // polled (the polls' round trip ends once they are in); then the first
+    // routed gate/up item's weights stream while the shared items are computed
+    ShguW<XBF16> sg;
+    if (it < b1) dec_shgu_load<XBF16>(L, x, it - b0, sg);
+    bool ok = dec_route_wait(L, W, tag, &rc, &lds_flag);
+    int it_r = it;
+    while (it_r < b1) it_r += G;
+    RguW wa, wb;   // two named buffers, alternating (no copies)
+    if (ok && it_r < b2) dec_rgu_load(L, P, &rc, it_r - b1, wa);
+    for (bool first = true; it < b1; it += G, first = false) {
+        if (!first) dec_shgu_load<XBF16>(L, x, it - b0, sg);
+        dec_shgu_compute<XBF16>(L, W, it - b0, sg, tag);
+    }
     // routed gate/up: the next item's weights are in flight while this one is computed
     if (ok && it < b2) {
-        RguW wa, wb;   // two named buffers, alternating (no copies)
-        dec_rgu_load(L, P, &rc, it - b1, wa);
         for (;;) {
             bool more = it + G < b2;
             if (more) dec_rgu_load(L, P, &rc, it + G - b1, wb);
-            dec_rgu_compute<XBF16>(L, W, xc, TL, TS, it - b1, P, wa);
+            dec_rgu_compute<XBF16>(L, W, xc, TL, TS, it - b1, P, wa, tag);
             it += G;
             if (!more) break;
             more = it + G < b2;
             if (more) dec_rgu_load(L, P, &rc, it + G - b1, wa);
-            dec_rgu_compute<XBF16>(L, W, xc, TL, TS, it - b1, P, wb);
+            dec_rgu_compute<XBF16>(L, W, xc, TL, TS, it - b1, P, wb, tag);
             it += G;
             if (!more) break;
         }
     }
-    // routed down: the same pipelining; weights do not wait for the gate/up phase
+    // routed down: each workgroup takes consecutive units (slot-major), so
+    // its units mostly share one h vector, staged in LDS when the slot
+    // changes (before the next unit's prefetch, so the staging's polls do not
+    // wait for it); pipelined like routed gate/up otherwise
+    int hid = -1;  // the h vector H holds (slot, or top_k for the shared one)
     if (ok && it < b3) {
-        RdnW wa, wb;
-        dec_rdn_load(L, P, &rc, it - b2, wa);
+        RdnW da, db;
+        dec_rdn_load(L, P, &rc, dec_rdn_unit(it - b2, G, P.n_rdn), da);
         for (;;) {
+            int u = dec_rdn_unit(it - b2, G, P.n_rdn);
+            if (u / P.rdn_per_slot != hid) {
+                hid = u / P.rdn_per_slot;
+                if (!(ok = dec_stage_h(W, L.n_ff, hid, tag, H))) break;
+            }
             bool more = it + G < b3;
-            if (more) dec_rdn_load(L, P, &rc, it + G - b2, wb);
-            if (!dec_rdn_compute(L, W, out, it - b2, P, &lds_flag, &rc, wa)) { ok = false; break; }
+            if (more) dec_rdn_load(L, P, &rc, dec_rdn_unit(it + G - b2, G, P.n_rdn), db);
+            dec_rdn_compute(L, out, u, P, &rc, da, H);
             it += G;
             if (!more) break;
+            u = dec_rdn_unit(it - b2, G, P.n_rdn);
+            if (u / P.rdn_per_slot != hid) {
+                hid = u / P.rdn_per_slot;
+                if (!(ok = dec_stage_h(W, L.n_ff, hid, tag, H))) break;
+            }
             more = it + G < b3;
-            if (more) dec_rdn_load(L, P, &rc, it + G - b2, wa);
-            if (!dec_rdn_compute(L, W, out, it - b2, P, &lds_flag, &rc, wb)) { ok = false; break; }
+            if (more) dec_rdn_load(L, P, &rc, dec_rdn_unit(it + G - b2, G, P.n_rdn), da);
+            dec_rdn_compute(L, out, u, P, &rc, db, H);
             it += G;
             if (!more) break;
         }
     }
-    for (; ok && it < P.total; it += G) {
+    for (int d = it - b3; ok && d < P.n_shdn; d += G) {
         switch (P.shdn_cpr) {
-            case 1: dec_shdn_item<1>(L, W, out, it - b3, P, &lds_flag); break;
-            case 2: dec_shdn_item<2>(L, W, out, it - b3, P, &lds_flag); break;
-            case 4: dec_shdn_item<4>(L, W, out, it - b3, P, &lds_flag); break;
-            default: dec_shdn_item<8>(L, W, out, it - b3, P, &lds_flag); break;
+            case 1: dec_shdn_item<1>(L, W, out, d, tag, H, hid, ok); break;
+            case 2: dec_shdn_item<2>(L, W, out, d, tag, H, hid, ok); break;
+            case 4: dec_shdn_item<4>(L, W, out, d, tag, H, hid, ok); break;
+            default: dec_shdn_item<8>(L, W, out, d, tag, H, hid, ok); break;
         }
     }
     // a bounded wait expired somewhere: make the failure visible in the output

@@ -159,7 +159,8 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     size_t o_xhi = carve(xf32 ? T * E * 2 : 0), o_xlo = carve(xf32 ? T * E * 2 : 0);
     size_t o_shh = carve(d->n_shared ? T * F * 2 : 0), o_shl = carve(d->n_shared ? T * F * 2 : 0);
     size_t o_chunks = carve((size_t)gemm_max_chunks((int)T, (int)NE, (int)k) * 16), o_nch = carve(4);
-    size_t o_ecnt = carve(MAX_EXPERT * 4), o_rest = carve(4 * T * NE * 4), o_rhalf = carve(NE * 2 * 8);
+    size_t o_ecnt = carve(MAX_EXPERT * 4), o_rest = carve(4 * T * NE * 4), o_rtag = carve(NE * 4 * 8);
+    size_t o_htag = carve((size_t)(k + 1) * F * 8);
     char *ws = (char *)A(off);
     if (err != hipSuccess) {
         delete h;
@@ -185,7 +186,8 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     W.nchunks = (int32_t *)(ws + o_nch);
     W.ecount = (int32_t *)(ws + o_ecnt);
     W.rest = (float *)(ws + o_rest);
-    W.rhalf = (double *)(ws + o_rhalf);
+    W.rtag = (unsigned long long *)(ws + o_rtag);
+    W.htag = (unsigned long long *)(ws + o_htag);
 
 #define CK(call)                                                                                      \
     do {                                                                                              \
