@@ -461,7 +461,7 @@ __device__ __forceinline__ float dec_iq2_dot(const uint2 *TL, const uint2 *TS, u
 // with agent-scope loads until all carry this call's tag: the values come
 // with the tags, in one round trip once they are there.  Returns false if the
 // bounded wait expired.
-__device__ __forceinline__ bool dec_route_wait(const Layer &L, const Work &W, uint32_t tag, RouteCache *rc,
+__device__ __forceinline__ void dec_route_poll(const Layer &L, const Work &W, uint32_t tag, RouteCache *rc,
                                                int *lds_flag) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x, NE = L.n_expert;
@@ -509,6 +509,10 @@ __device__ __forceinline__ bool dec_route_wait(const Layer &L, const Work &W, ui
         }
         if (lane == 0) *lds_flag = ok;
     }
+}
+__device__ __forceinline__ bool dec_route_wait(const Layer &L, const Work &W, uint32_t tag, RouteCache *rc,
+                                               int *lds_flag) {
+    dec_route_poll(L, W, tag, rc, lds_flag);
     __syncthreads();
     const bool ok = *lds_flag != 0;
     __syncthreads();
@@ -824,9 +828,16 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
     // the first shared gate/up item's weights stream while the routing is
     // polled (the polls' round trip ends once they are in); then the first
     // routed gate/up item's weights stream while the shared items are computed
+    // (wave 0 polls first and loads its row after: its polls do not queue
+    // behind its own weights)
     ShguW<XBF16> sg;
-    if (it < b1) dec_shgu_load<XBF16>(L, x, it - b0, sg);
-    bool ok = dec_route_wait(L, W, tag, &rc, &lds_flag);
+    const bool wave0 = threadIdx.x < 64;
+    if (!wave0 && it < b1) dec_shgu_load<XBF16>(L, x, it - b0, sg);
+    dec_route_poll(L, W, tag, &rc, &lds_flag);
+    if (wave0 && it < b1) dec_shgu_load<XBF16>(L, x, it - b0, sg);
+    __syncthreads();
+    bool ok = lds_flag != 0;
+    __syncthreads();
     int it_r = it;
     while (it_r < b1) it_r += G;
     RguW wa, wb;   // two named buffers, alternating (no copies)
