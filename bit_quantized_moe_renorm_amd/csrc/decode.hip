@@ -5,30 +5,30 @@
 // page, section 2.3).  Here one persistent launch walks a fixed list of work
 // items in five phases, in this order:
 //   router    : half an expert's logit per item (fp64 accumulation);
-//   shared g/u: 4 rows of the shared expert's gate and up per item (no
-//               routing needed, so it streams while the router is counted);
-//   routing   : every workgroup waits until all router halves are counted and
-//               takes the top-k and renormalised weights itself;
+//   routing   : every workgroup polls until all router halves of this call
+//               are stored and takes the top-k and renormalised weights itself
+//               (the shared expert's first gate/up rows stream meanwhile);
+//   shared g/u: one row of the shared expert's gate and up per wave;
 //   routed g/u: 16 rows of one selected expert's IQ2 gate and up per item,
 //               SiLU(g)*u kept in fp32;
 //   routed dn : rows of one selected expert's Q2_K down projection, scaled
-//               by its routing weight (waits for that expert's g/u items);
-//   shared dn : rows of the shared down projection (waits for shared g/u).
-// Items are dealt round-robin over the workgroups in phase order, and the grid
-// is sized to what the GPU holds at once, so every wait is on an item that a
-// resident workgroup took earlier and that never waits on a later one.  Each
-// wait is also bounded: if it ever expires (the GPU shared with other work),
-// the kernel poisons the output with NaN instead of hanging.
+//               by its routing weight, from that slot's h vector in LDS;
+//   shared dn : rows of the shared down projection.
+// Items are dealt round-robin over the workgroups in phase order (routed down
+// units in consecutive runs, so a workgroup's units mostly share one h
+// vector), and the grid is sized to what the GPU holds at once, so every wait
+// is on data that a resident workgroup produces earlier in its own list and
+// that never waits on a later one.  Each wait is also bounded: if it ever
+// expires (the GPU shared with other work), the kernel poisons the output with
+// NaN instead of hanging.
 //
-// Hand-offs avoid cache-maintenance fences (an L2 write-back or invalidate per
-// hand-off costs more than the whole block).  Data another workgroup will read
-// (logits, routing, the h vectors) is written with agent-scope stores, which
-// write through to the device's point of coherence; the producer waits for
-// its stores to complete and then bumps a counter with an agent-scope atomic.
-// Consumers poll the counter with agent-scope loads and then read the data
-// with plain loads: no workgroup touches those lines earlier in the launch and
-// caches are invalidated between launches, so no stale copy can be hit.  The
-// counters hold 64-bit epochs and never need resetting.
+// Hand-offs need no fences, counters or drains.  Every value another
+// workgroup reads (the router half-sums, the h vectors) is stored as 64-bit
+// words, each holding 32 bits of data under a 32-bit tag that identifies the
+// call; a 64-bit store is seen whole or not at all.  Consumers poll the words
+// with agent-scope loads (which read the device's point of coherence) until
+// all of them carry this call's tag, and have the values in the same round
+// trip.  Tags only change between calls, so nothing is reset.
 // The block output (routed + shared) is added into the residual with fp32
 // atomics.
 #include "common.h"
@@ -47,12 +47,10 @@ __device__ __forceinline__ float dec_group_sum(float v, int lpr) {
     return v;
 }
 
-// Phase counters: 64-bit, each in its own 256-byte slot of W.counters (slot 0
-// belongs to the multi-kernel router).  They only ever increase: call number
-// `ep` of a handle waits for (ep + 1) times the per-call count, so nothing has
-// to be reset at the end of a launch.
+// The error flag, set when a bounded wait expires: a 64-bit word in its own
+// 256-byte slot of W.counters (slot 0 belongs to the multi-kernel router).
 constexpr int CSTRIDE = 32;  // in uint64
-constexpr int C_SHGU = 3, C_ERR = 4, C_GU = 5;  // C_GU + slot; slot units
+constexpr int C_ERR = 4;
 __device__ __forceinline__ unsigned long long *ctr(const Work &W, int slot) {
     return reinterpret_cast<unsigned long long *>(W.counters) + slot * CSTRIDE;
 }
@@ -82,23 +80,6 @@ struct DecPlan {
 
 constexpr int SPIN_LIMIT = 1 << 20;      // polls before giving up (about a second)
 
-// Loads of data produced by other workgroups in this launch (small items).
-__device__ __forceinline__ float ld_shared(const float *p) {
-    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ int ld_shared(const int *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Store that other workgroups (any XCD) can read after the hand-off.
-__device__ __forceinline__ void st_shared(float *p, float v) {
-    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_shared(int *p, int v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // One tagged word: fp32 bits below, the call's tag above.  A 64-bit store is
 // seen whole or not at all, so a reader that finds the tag has the value.
 __device__ __forceinline__ void st_tagged(unsigned long long *p, float v, uint32_t tag) {
@@ -106,54 +87,7 @@ __device__ __forceinline__ void st_tagged(unsigned long long *p, float v, uint32
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// This wavefront's shared stores are complete.
-__device__ __forceinline__ void stores_done() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// The workgroup's shared stores are complete; then count the item (once).
-// Returns the counter value before the increment (valid in thread 0).
-__device__ __forceinline__ unsigned long long publish_item(unsigned long long *c) {
-    stores_done();
-    __syncthreads();
-    unsigned long long prev = 0;
-    if (threadIdx.x == 0) prev = __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return prev;
-}
-
-// Wait (one poller per workgroup, with backoff) until *c >= target.  Returns
-// false, and flags the error, if the bounded wait expired.
-template <int SLEEP = 8>
-__device__ __forceinline__ bool wait_items(const Work &W, unsigned long long *c, unsigned long long target,
-                                           int *lds_flag) {
-    if (threadIdx.x == 0) {
-        int ok = 1, spins = 0;
-        while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(SLEEP);
-            if (++spins > SPIN_LIMIT) {
-                __hip_atomic_store(ctr(W, C_ERR), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ok = 0;
-                break;
-            }
-        }
-        *lds_flag = ok;
-    }
-    __syncthreads();
-    const bool ok = *lds_flag != 0;
-    __syncthreads();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    return ok;
-}
-
-
 // ---------------------------------------------------------------- P0: router
-// Each router item is half an expert row (the two halves land in separate
-// fp64 slots of W.hbuf's router area, so nothing has to be cleared between
-// calls).  The wavefront that completes the last half rounds every logit to
-// fp32, takes the top-k with its renormalised weights, publishes "route
-// ready", and only then writes the per-expert lists kept for ds4moe_route.
 // Wave-wide maximum of an unsigned key by DPP (row shifts, then the two row
 // broadcasts); the result is read from the last lane.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
