@@ -3,7 +3,7 @@
 // Generation is bandwidth-bound ("ds4 深度实战...", section 5.1) and the pages
 // fuse MoE routing with the expert computation into one GPU dispatch (same
 // page, section 2.3).  Here one persistent launch walks a fixed list of work
-// items in five phases, in this order:
+// items in these phases, in this order:
 //   router    : half an expert's logit per item (fp64 accumulation);
 //   routing   : every workgroup polls until all router halves of this call
 //               are stored and takes the top-k and renormalised weights itself
@@ -11,12 +11,15 @@
 //   shared g/u: one row of the shared expert's gate and up per wave;
 //   routed g/u: 16 rows of one selected expert's IQ2 gate and up per item,
 //               SiLU(g)*u kept in fp32;
+//   shared dn : rows of the shared down projection;
 //   routed dn : rows of one selected expert's Q2_K down projection, scaled
-//               by its routing weight, from that slot's h vector in LDS;
-//   shared dn : rows of the shared down projection.
+//               by its routing weight, from that slot's h vector staged in
+//               LDS as fp16 pairs.
 // Items are dealt round-robin over the workgroups in phase order (routed down
 // units in consecutive runs, so a workgroup's units mostly share one h
-// vector), and the grid is sized to what the GPU holds at once, so every wait
+// vector); shared down comes before routed down so that the workgroups with
+// fewer routed gate/up items stream it while the others still decode IQ2
+// weights.  The grid is sized to what the GPU holds at once, so every wait
 // is on data that a resident workgroup produces earlier in its own list and
 // that never waits on a later one.  Each wait is also bounded: if it ever
 // expires (the GPU shared with other work), the kernel poisons the output with
@@ -660,11 +663,97 @@ __device__ __forceinline__ void dec_rdn_load(const Layer &L, const DecPlan &P, c
     }
 }
 
-// H holds the slot's h vector (staged by the caller).  Each Q2_K row of the
-// lane (64 weights: 4 sub-blocks of 16, weight 16 s + 4 b + u in bits 2u of
-// byte b of word s) is d * sum_s sc_s dot_s - dmin * sum_s m_s hsum_s.
-__device__ __forceinline__ void dec_rdn_compute(const Layer &L, float *__restrict__ out, int item, const DecPlan &P,
-                                                const RouteCache *rc, const RdnW &w, const float4 *H) {
+// A routed slot's h vector staged in LDS for the Q2_K down projections, as
+// fp16 pairs laid out for the reading lanes.  Lane chunk c (h[64 c .. 64 c +
+// 63]) has per sub-block s (16 values, weight 4 b + u at bits 2u of byte b of
+// the sub-block's qs word) two 16-byte units, one per byte pair k = b / 2:
+// unit (2 s + k) * lpr + c holds, for u = 0..3, the pair
+// (h[64 c + 16 s + 8 k + u], h[64 c + 16 s + 8 k + 4 + u]) * 2^-e_c * 4^-u.
+// The 4^-u matches the weights, which enter the dot products as fp16
+// subnormals q * 4^u * 2^-24 (the byte masked in place: no shifts, no offset
+// to subtract); e_c puts the chunk's largest value in [2^14, 2^15), and
+// Hsc[c] = 2^(24 + e_c) undoes both.  Hsum[s * lpr + c] is the sub-block's
+// plain fp32 sum of h, for the min term.  Consecutive lanes read consecutive
+// units: no bank conflicts.
+__device__ __forceinline__ bool dec_stage_h16(const Work &W, int F, int slot, uint32_t tag, uint4 *Hq, float *Hsc,
+                                              float *Hsum) {
+    const unsigned long long *src = W.htag + (int64_t)slot * F;
+    const int np = F >> 3, lpr = F >> 6;  // thread steps of 8 values; lanes per row
+    unsigned long long v[2][8];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        // past the vector: re-read its last 8 values, ignored below
+        const int p = min((int)threadIdx.x + 256 * q, np - 1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v[q][e] = __hip_atomic_load(src + 8 * p + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the previous unit's reads of the staged vector are over
+    __syncthreads();
+    int ok = 1;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int p = threadIdx.x + 256 * q;
+        if (256 * q >= np) break;  // uniform
+        const bool mine = p < np;  // np is a multiple of 32: whole groups of 8 lanes agree
+        uint32_t missing = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (mine && (uint32_t)(v[q][e] >> 32) != tag) missing |= 1u << e;
+        int spins = 0;
+        while (ok && missing) {
+            __builtin_amdgcn_s_sleep(4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (missing & (1u << e)) {
+                    v[q][e] = __hip_atomic_load(src + 8 * p + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if ((uint32_t)(v[q][e] >> 32) == tag) missing &= ~(1u << e);
+                }
+            if (missing && ++spins > SPIN_LIMIT) {
+                __hip_atomic_store(ctr(W, C_ERR), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = 0;
+            }
+        }
+        float h[8];
+        float mx = 0.0f, hs = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            h[e] = __uint_as_float((uint32_t)v[q][e]);
+            mx = fmaxf(mx, fabsf(h[e]));
+            hs += h[e];
+        }
+        // chunk c = p / 8 is 8 consecutive lanes; sub-block s = (p / 2) % 4 is 2
+        mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+        hs += __shfl_xor(hs, 1, 64);
+        if (mine) {
+            const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFFu) - 127;
+            const int e = min(max(ex - 14, -100), 100);
+            uint32_t pr[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                // 2^-e * 4^-u, exact
+                const float down = __uint_as_float((uint32_t)(127 - e - 2 * u) << 23);
+                pr[u] = dec_pack_f16(h[u] * down, h[4 + u] * down);
+            }
+            Hq[(p & 7) * lpr + (p >> 3)] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+            if ((p & 7) == 0) Hsc[p >> 3] = __uint_as_float((uint32_t)(127 + 24 + e) << 23);
+            if ((p & 1) == 0) Hsum[((p >> 1) & 3) * lpr + (p >> 3)] = hs;
+        }
+    }
+    return __syncthreads_and(ok) != 0;
+}
+
+// One routed down unit from the staged h vector: each Q2_K row of the lane (64
+// weights: 4 sub-blocks of 16) is d * sum_s sc_s dot_s - dmin * sum_s m_s hsum_s.
+// The 2-bit codes of byte pair k become fp16 pairs by one byte permute (bytes
+// 2k, 2k+1 into the low bytes of the two halves) and, per position u, one mask
+// (bits 2u, 2u+1 of each low byte): the subnormal q * 4^u * 2^-24, whose
+// product with the staged h * 2^-e * 4^-u is exact.
+__device__ __forceinline__ void dec_rdn_compute16(const Layer &L, float *__restrict__ out, int item, const DecPlan &P,
+                                                  const RouteCache *rc, const RdnW &w, const uint4 *Hq,
+                                                  const float *Hsc, const float *Hsum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd, F = L.n_ff;
     const int lpr = F >> 6, rpw = 64 / lpr;
@@ -672,32 +761,30 @@ __device__ __forceinline__ void dec_rdn_compute(const Layer &L, float *__restric
     const int j = item / P.rdn_per_slot, tile = item - j * P.rdn_per_slot;
     const int r0 = (tile * DEC_WAVES + wave) * (DEC_DN_NR * rpw) + lane / lpr;
     const float wgt = rc->w[j];
+    const float hsc = Hsc[c];
     float A[DEC_DN_NR], B[DEC_DN_NR];
 #pragma unroll
     for (int r = 0; r < DEC_DN_NR; ++r) A[r] = 0.0f, B[r] = 0.0f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        float hv[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 v = H[h_slot(16 * c + 4 * s + q)];
-            hv[4 * q] = v.x, hv[4 * q + 1] = v.y, hv[4 * q + 2] = v.z, hv[4 * q + 3] = v.w;
-        }
-        float hsum = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) hsum += hv[q];
+        const uint4 h0 = Hq[(2 * s) * lpr + c], h1 = Hq[(2 * s + 1) * lpr + c];
+        const float hsum = Hsum[s * lpr + c];
 #pragma unroll
         for (int r = 0; r < DEC_DN_NR; ++r) {
             const uint32_t Q = s == 0 ? w.qs[r].x : s == 1 ? w.qs[r].y : s == 2 ? w.qs[r].z : w.qs[r].w;
-            float dot = 0.0f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t tq = (Q >> (2 * u)) & 0x03030303u;
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb) dot = fmaf((float)((tq >> (8 * bb)) & 0xFFu), hv[4 * bb + u], dot);
-            }
+            const uint32_t P0 = __builtin_amdgcn_perm(0u, Q, 0x0C010C00u);  // bytes 0, 1
+            const uint32_t P1 = __builtin_amdgcn_perm(0u, Q, 0x0C030C02u);  // bytes 2, 3
+            float d0 = 0.0f, d1 = 0.0f;
+            d0 = dec_dot2h(P0 & 0x00030003u, h0.x, d0);
+            d1 = dec_dot2h(P1 & 0x00030003u, h1.x, d1);
+            d0 = dec_dot2h(P0 & 0x000C000Cu, h0.y, d0);
+            d1 = dec_dot2h(P1 & 0x000C000Cu, h1.y, d1);
+            d0 = dec_dot2h(P0 & 0x00300030u, h0.z, d0);
+            d1 = dec_dot2h(P1 & 0x00300030u, h1.z, d1);
+            d0 = dec_dot2h(P0 & 0x00C000C0u, h0.w, d0);
+            d1 = dec_dot2h(P1 & 0x00C000C0u, h1.w, d1);
             const uint32_t scb = (w.sc[r] >> (8 * s)) & 0xFFu;
-            A[r] = fmaf((float)(scb & 15u), dot, A[r]);
+            A[r] = fmaf((float)(scb & 15u), d0 + d1, A[r]);
             B[r] = fmaf((float)(scb >> 4), hsum, B[r]);
         }
     }
@@ -705,7 +792,7 @@ __device__ __forceinline__ void dec_rdn_compute(const Layer &L, float *__restric
     for (int r = 0; r < DEC_DN_NR; ++r) {
         const int row = r0 + r * rpw;
         const uint32_t dd = w.dd[r];
-        float y = half_to_f32((uint16_t)(dd & 0xFFFFu)) * A[r] - half_to_f32((uint16_t)(dd >> 16)) * B[r];
+        float y = half_to_f32((uint16_t)(dd & 0xFFFFu)) * (A[r] * hsc) - half_to_f32((uint16_t)(dd >> 16)) * B[r];
         y = dec_group_sum(y, lpr);
         if (c == 0 && row < E) atomicAdd(out + row, wgt * y);
     }
@@ -719,6 +806,14 @@ __device__ __forceinline__ int dec_rdn_unit(int l, int G, int n) {
     return o * q + min(o, r) + l / G;
 }
 
+// Loads the weights of a workgroup's first two routed down items (it_d and
+// it_d + G, if they exist) into da and db.
+__device__ __forceinline__ void dec_rdn_preload(const Layer &L, const DecPlan &P, const RouteCache *rc, int it_d,
+                                                int b3, int b4, int G, RdnW &da, RdnW &db) {
+    if (it_d < b4) dec_rdn_load(L, P, rc, dec_rdn_unit(it_d - b3, G, P.n_rdn), da);
+    if (it_d + G < b4) dec_rdn_load(L, P, rc, dec_rdn_unit(it_d + G - b3, G, P.n_rdn), db);
+}
+
 // ---------------------------------------------------------------- the persistent kernel
 template <bool XBF16>
 __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Layer L, Work W, const void *__restrict__ x,
@@ -728,11 +823,15 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
     __shared__ int lds_flag;
     __shared__ double lds_part[DEC_WAVES];
     __shared__ RouteCache rc;
-    __shared__ float4 H[1024];             // an h vector (n_ff <= 4096) staged for the down projections
+    __shared__ float4 H[1024];             // the shared h vector (n_ff <= 4096) for the shared down projections
+    __shared__ uint4 Hq[512];              // a routed h vector as fp16 pairs (n_ff <= 4096)
+    __shared__ float Hsc[64], Hsum[256];   // its per-chunk scales and per-sub-block sums
     const int G = gridDim.x;
-    // item order: router, shared gate/up, routed gate/up, routed down, shared down;
-    // every wait is on an earlier phase
-    const int b0 = P.n_route, b1 = b0 + P.n_shgu, b2 = b1 + P.n_rgu, b3 = b2 + P.n_rdn;
+    // item order: router, shared gate/up, routed gate/up, shared down, routed
+    // down; every wait is on an earlier phase.  Shared down comes before routed
+    // down so that the workgroups with one routed gate/up item (fewer than the
+    // others) stream it while the others are still decoding IQ2 weights.
+    const int b0 = P.n_route, b1 = b0 + P.n_shgu, b2 = b1 + P.n_rgu, b3 = b2 + P.n_shdn, b4 = b3 + P.n_rdn;
     // one loop per phase (the same items in the same order as a single loop
     // over all of them), so that each phase's registers are allocated on their own
     // loads that depend on nothing are issued before the router item: this
@@ -780,58 +879,69 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
         if (!first) dec_shgu_load<XBF16>(L, x, it - b0, sg);
         dec_shgu_compute<XBF16>(L, W, it - b0, sg, tag);
     }
-    // routed gate/up: the next item's weights are in flight while this one is computed
+    // routed gate/up: the next item's weights are in flight while this one is
+    // computed; the last item's computation covers the loads of the first two
+    // routed down items instead (they depend on the routing alone)
+    int it_d = blockIdx.x;  // this workgroup's first routed down item
+    while (it_d < b3) it_d += G;
+    RdnW da, db;
+    bool rdn_pre = false;
     if (ok && it < b2) {
         for (;;) {
             bool more = it + G < b2;
-            if (more) dec_rgu_load(L, P, &rc, it + G - b1, wb);
+            if (more)
+                dec_rgu_load(L, P, &rc, it + G - b1, wb);
+            else
+                dec_rdn_preload(L, P, &rc, it_d, b3, b4, G, da, db), rdn_pre = true;
             dec_rgu_compute<XBF16>(L, W, xc, TL, TS, it - b1, P, wa, tag);
             it += G;
             if (!more) break;
             more = it + G < b2;
-            if (more) dec_rgu_load(L, P, &rc, it + G - b1, wa);
+            if (more)
+                dec_rgu_load(L, P, &rc, it + G - b1, wa);
+            else
+                dec_rdn_preload(L, P, &rc, it_d, b3, b4, G, da, db), rdn_pre = true;
             dec_rgu_compute<XBF16>(L, W, xc, TL, TS, it - b1, P, wb, tag);
             it += G;
             if (!more) break;
         }
     }
-    // routed down: each workgroup takes consecutive units (slot-major), so
-    // its units mostly share one h vector, staged in LDS when the slot
-    // changes (before the next unit's prefetch, so the staging's polls do not
-    // wait for it); pipelined like routed gate/up otherwise
     int hid = -1;  // the h vector H holds (slot, or top_k for the shared one)
-    if (ok && it < b3) {
-        RdnW da, db;
-        dec_rdn_load(L, P, &rc, dec_rdn_unit(it - b2, G, P.n_rdn), da);
-        for (;;) {
-            int u = dec_rdn_unit(it - b2, G, P.n_rdn);
-            if (u / P.rdn_per_slot != hid) {
-                hid = u / P.rdn_per_slot;
-                if (!(ok = dec_stage_h(W, L.n_ff, hid, tag, H))) break;
-            }
-            bool more = it + G < b3;
-            if (more) dec_rdn_load(L, P, &rc, dec_rdn_unit(it + G - b2, G, P.n_rdn), db);
-            dec_rdn_compute(L, out, u, P, &rc, da, H);
-            it += G;
-            if (!more) break;
-            u = dec_rdn_unit(it - b2, G, P.n_rdn);
-            if (u / P.rdn_per_slot != hid) {
-                hid = u / P.rdn_per_slot;
-                if (!(ok = dec_stage_h(W, L.n_ff, hid, tag, H))) break;
-            }
-            more = it + G < b3;
-            if (more) dec_rdn_load(L, P, &rc, dec_rdn_unit(it + G - b2, G, P.n_rdn), da);
-            dec_rdn_compute(L, out, u, P, &rc, db, H);
-            it += G;
-            if (!more) break;
+    for (; ok && it < b3; it += G) {
+        switch (P.shdn_cpr) {
+            case 1: dec_shdn_item<1>(L, W, out, it - b2, tag, H, hid, ok); break;
+            case 2: dec_shdn_item<2>(L, W, out, it - b2, tag, H, hid, ok); break;
+            case 4: dec_shdn_item<4>(L, W, out, it - b2, tag, H, hid, ok); break;
+            default: dec_shdn_item<8>(L, W, out, it - b2, tag, H, hid, ok); break;
         }
     }
-    for (int d = it - b3; ok && d < P.n_shdn; d += G) {
-        switch (P.shdn_cpr) {
-            case 1: dec_shdn_item<1>(L, W, out, d, tag, H, hid, ok); break;
-            case 2: dec_shdn_item<2>(L, W, out, d, tag, H, hid, ok); break;
-            case 4: dec_shdn_item<4>(L, W, out, d, tag, H, hid, ok); break;
-            default: dec_shdn_item<8>(L, W, out, d, tag, H, hid, ok); break;
+    // routed down: each workgroup takes consecutive units (slot-major), so
+    // its units mostly share one h vector, staged in LDS when the slot
+    // changes (before the next unit's load is issued, so the staging's polls
+    // do not wait for it); the first two units' weights were loaded ahead
+    if (ok && it < b4) {
+        if (!rdn_pre) dec_rdn_preload(L, P, &rc, it_d, b3, b4, G, da, db);
+        bool ahead = true;  // db already holds item it + G
+        for (;;) {
+            int u = dec_rdn_unit(it - b3, G, P.n_rdn);
+            if (u / P.rdn_per_slot != hid) {
+                hid = u / P.rdn_per_slot;
+                if (!(ok = dec_stage_h16(W, L.n_ff, hid, tag, Hq, Hsc, Hsum))) break;
+            }
+            if (!ahead && it + G < b4) dec_rdn_load(L, P, &rc, dec_rdn_unit(it + G - b3, G, P.n_rdn), db);
+            ahead = false;
+            dec_rdn_compute16(L, out, u, P, &rc, da, Hq, Hsc, Hsum);
+            it += G;
+            if (it >= b4) break;
+            u = dec_rdn_unit(it - b3, G, P.n_rdn);
+            if (u / P.rdn_per_slot != hid) {
+                hid = u / P.rdn_per_slot;
+                if (!(ok = dec_stage_h16(W, L.n_ff, hid, tag, Hq, Hsc, Hsum))) break;
+            }
+            if (it + G < b4) dec_rdn_load(L, P, &rc, dec_rdn_unit(it + G - b3, G, P.n_rdn), da);
+            dec_rdn_compute16(L, out, u, P, &rc, db, Hq, Hsc, Hsum);
+            it += G;
+            if (it >= b4) break;
         }
     }
     // a bounded wait expired somewhere: make the failure visible in the output

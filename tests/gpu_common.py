@@ -13,6 +13,14 @@ REL_TOL = 2e-3
 # a few fp32 roundings per dot product, far below the bar.  A tighter check
 # catches wiring mistakes the loose bar would let through.
 GEMV_TOL = 1e-5
+# The fused single-token decode rounds each routed SwiGLU output h to fp16
+# (11-bit significand, under a power-of-two scale per 64-value chunk that puts
+# the chunk's largest value at the top of fp16's range) before the Q2_K down
+# projections.  The rounding error of one h is at most 2^-12 of |h|; over the
+# 2048 terms of a down row they add up like a random walk, to about
+# 2^-12 / sqrt(3) ~ 1.4e-4 of the rms term, ~5e-5 of max|out| on the DS4 shapes.
+# The check takes 4x that.
+FUSED_TOL = 2e-4
 
 
 def log(*a):

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 from bit_quantized_moe_renorm_amd import synth
-from gpu_common import GEMV_TOL, REL_TOL, device_layer, host_layer, log, rel_err
+from gpu_common import FUSED_TOL, GEMV_TOL, REL_TOL, device_layer, host_layer, log, rel_err
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -141,7 +141,8 @@ def test_forward_ds4_gemv(n):
     ref, _, _ = oracle.forward(lay, x)
     err = rel_err(got, ref)
     log(f"[gpu] ds4 gemv n={n} rel err {err:.3e}")
-    assert err <= REL_TOL and err <= GEMV_TOL
+    # one token takes the fused decode launch
+    assert err <= REL_TOL and err <= (FUSED_TOL if n == 1 else GEMV_TOL)
 
 
 def test_forward_tiny_fused_decode():
@@ -154,7 +155,7 @@ def test_forward_tiny_fused_decode():
         ref, _, _ = oracle.forward(lay, x[t:t + 1])
         err = rel_err(got, ref)
         log(f"[gpu] tiny fused token {t} rel err {err:.3e}")
-        assert err <= GEMV_TOL
+        assert err <= FUSED_TOL
 
 
 def test_forward_ds4_fused_decode_many_tokens():
@@ -166,7 +167,7 @@ def test_forward_ds4_fused_decode_many_tokens():
     ref, _, _ = oracle.forward(lay, x)
     err = rel_err(got, ref)
     log(f"[gpu] ds4 fused 24 tokens rel err {err:.3e}")
-    assert err <= REL_TOL and err <= GEMV_TOL
+    assert err <= REL_TOL and err <= FUSED_TOL
 
 
 def test_forward_fused_zipf_bias():
@@ -175,16 +176,16 @@ def test_forward_fused_zipf_bias():
     x = synth.activations(1, 4, 4096, start=7)
     got = np.stack([_forward(dev, x[t:t + 1], m.PATH_AUTO)[0] for t in range(4)])
     ref, _, _ = oracle.forward(lay, x)
-    assert rel_err(got, ref) <= GEMV_TOL
+    assert rel_err(got, ref) <= FUSED_TOL
 
 
 def test_forward_accumulates_into_residual():
     lay = host_layer("ds4")
     x = synth.activations(1, 1, 4096, start=3)
     r = synth.residual(5, 1, 4096)
-    got = _forward(device_layer("ds4"), x, m.PATH_GEMV, out0=r)
+    got = _forward(device_layer("ds4"), x, m.PATH_GEMV, out0=r)  # one token: the fused decode
     ref, _, _ = oracle.forward(lay, x)
-    assert rel_err(got - r, ref) <= GEMV_TOL
+    assert rel_err(got - r, ref) <= FUSED_TOL
     got2 = _forward(device_layer("ds4"), np.concatenate([x, x]), m.PATH_GEMV, out0=np.concatenate([r, r]))
     assert rel_err(got2[1] - r[0], ref[0]) <= GEMV_TOL
 
