@@ -3,7 +3,7 @@
 // Generation is bandwidth-bound ("ds4 深度实战...", section 5.1) and the pages
 // fuse MoE routing with the expert computation into one GPU dispatch (same
 // page, section 2.3).  Here one persistent launch walks a fixed list of work
-// items in these phases, in this order:
+// items in five phases, in this order:
 //   router    : half an expert's logit per item (fp64 accumulation);
 //   routing   : every workgroup polls until all router halves of this call
 //               are stored and takes the top-k and renormalised weights itself
@@ -11,15 +11,12 @@
 //   shared g/u: one row of the shared expert's gate and up per wave;
 //   routed g/u: 16 rows of one selected expert's IQ2 gate and up per item,
 //               SiLU(g)*u kept in fp32;
-//   shared dn : rows of the shared down projection;
 //   routed dn : rows of one selected expert's Q2_K down projection, scaled
-//               by its routing weight, from that slot's h vector staged in
-//               LDS as fp16 pairs.
+//               by its routing weight, from that slot's h vector in LDS;
+//   shared dn : rows of the shared down projection.
 // Items are dealt round-robin over the workgroups in phase order (routed down
 // units in consecutive runs, so a workgroup's units mostly share one h
-// vector); shared down comes before routed down so that the workgroups with
-// fewer routed gate/up items stream it while the others still decode IQ2
-// weights.  The grid is sized to what the GPU holds at once, so every wait
+// vector), and the grid is sized to what the GPU holds at once, so every wait
 // is on data that a resident workgroup produces earlier in its own list and
 // that never waits on a later one.  Each wait is also bounded: if it ever
 // expires (the GPU shared with other work), the kernel poisons the output with
@@ -49,6 +46,23 @@ __device__ __forceinline__ float dec_group_sum(float v, int lpr) {
     for (int off = lpr >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
     return v;
 }
+// Sum over each group of lpr consecutive lanes (lpr a power of two up to 64),
+// left in the group's last lane, by DPP alone (row shifts, then the two row
+// broadcasts): plain VALU work that never waits on LDS traffic in flight.
+template <int CTRL, int ROW_MASK, bool BOUND_CTRL>
+__device__ __forceinline__ float dec_dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, BOUND_CTRL));
+}
+__device__ __forceinline__ float dec_group_sum_last(float v, int lpr) {
+    if (lpr > 1) v += dec_dpp<0x111, 0xF, true>(v);    // row_shr:1
+    if (lpr > 2) v += dec_dpp<0x112, 0xF, true>(v);    // row_shr:2
+    if (lpr > 4) v += dec_dpp<0x114, 0xF, true>(v);    // row_shr:4
+    if (lpr > 8) v += dec_dpp<0x118, 0xF, true>(v);    // row_shr:8
+    if (lpr > 16) v += dec_dpp<0x142, 0xA, false>(v);  // row_bcast:15
+    if (lpr > 32) v += dec_dpp<0x143, 0xC, false>(v);  // row_bcast:31
+    return v;
+}
+
 
 // The error flag, set when a bounded wait expires: a 64-bit word in its own
 // 256-byte slot of W.counters (slot 0 belongs to the multi-kernel router).
@@ -187,7 +201,7 @@ __device__ __forceinline__ void dec_topk_local(const Layer &L, const Work &W, co
 
 // Half h of expert e's logit: waves split the half row (E/2 elements).
 template <bool XBF16>
-__device__ void dec_route_item(const Layer &L, const Work &W, const void *__restrict__ x, int item,
+__device__ __forceinline__ void dec_route_item(const Layer &L, const Work &W, const void *__restrict__ x, int item,
                                double *lds_part, uint32_t tag) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd;
@@ -367,30 +381,35 @@ struct DecX {
     }
 };
 
-// 64 IQ2 weights of one lane (two canonical sub-blocks) against x, before d/64
-// and before the lane's x scale.  TL / TS: the level-byte and sign-byte tables
-// (entry e, replica r at e * IQ2B_REPL + r).
-template <bool XBF16>
-__device__ __forceinline__ float dec_iq2_dot(const uint2 *TL, const uint2 *TS, uint4 q, const DecX<XBF16> &xc,
-                                             int rep) {
-    float acc = 0.0f;
+// One canonical IQ2 sub-block (32 weights: 4 codebook indices in word ib, 7
+// sign bits per group of 8 and the 4-bit scale in word sw) of one lane.  The
+// table lookups (TL / TS: level bytes and sign bytes, entry e, replica r at
+// e * IQ2B_REPL + r) are issued one sub-block ahead of the arithmetic that
+// uses them, so the LDS latency overlaps the previous sub-block's dot products.
+struct Iq2Tab {
+    uint2 lv[4], sv[4];
+};
+__device__ __forceinline__ void dec_iq2_fetch(const uint2 *TL, const uint2 *TS, uint32_t ib, uint32_t sw, int rep,
+                                              Iq2Tab &t) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-        const uint32_t ib = sb ? q.z : q.x;   // 4 codebook indices
-        const uint32_t sw = sb ? q.w : q.y;   // signs (7 x 4) | ls << 28
-        uint2 lv[4], sv[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            lv[g] = TL[((ib >> (8 * g)) & 0xFFu) * IQ2B_REPL + rep];
-            sv[g] = TS[((sw >> (7 * g)) & 0x7Fu) * IQ2B_REPL + rep];
-        }
-        float s = 0.0f;
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-            s = xc.dot8(iq2_expand_f16(make_uint2(lv[g].x ^ sv[g].x, lv[g].y ^ sv[g].y)), 4 * sb + g, s);
-        acc = fmaf((float)(2u * (sw >> 28) + 1u), s, acc);
+    for (int g = 0; g < 4; ++g) {
+        t.lv[g] = TL[((ib >> (8 * g)) & 0xFFu) * IQ2B_REPL + rep];
+        t.sv[g] = TS[((sw >> (7 * g)) & 0x7Fu) * IQ2B_REPL + rep];
     }
-    return acc;
+}
+// The sub-block's dot product with x (x groups 4 sb .. 4 sb + 3 of the lane's
+// chunk), times its odd scale 2 ls + 1; before d/64 and the lane's x scale.
+// Two accumulators halve the chain of dependent dot products.
+template <bool XBF16>
+__device__ __forceinline__ float dec_iq2_sub(const Iq2Tab &t, uint32_t sw, const DecX<XBF16> &xc, int sb) {
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; g += 2) {
+        s0 = xc.dot8(iq2_expand_f16(make_uint2(t.lv[g].x ^ t.sv[g].x, t.lv[g].y ^ t.sv[g].y)), 4 * sb + g, s0);
+        s1 = xc.dot8(iq2_expand_f16(make_uint2(t.lv[g + 1].x ^ t.sv[g + 1].x, t.lv[g + 1].y ^ t.sv[g + 1].y)),
+                     4 * sb + g + 1, s1);
+    }
+    return (float)(2u * (sw >> 28) + 1u) * (s0 + s1);
 }
 
 // Wait until every router half-sum of this call is stored, then route
@@ -486,6 +505,13 @@ __device__ __forceinline__ void dec_rgu_load(const Layer &L, const DecPlan &P, c
     }
 }
 
+// Word pair (codebook indices, signs and scale) of sub-block n of an item's
+// lane data: row n / 4, gate (n / 2 even) or up, canonical sub-block n % 2.
+__device__ __forceinline__ uint2 dec_rgu_words(const RguW &w, int n) {
+    const uint4 q = ((n >> 1) & 1) ? w.qu[n >> 2] : w.qg[n >> 2];
+    return (n & 1) ? make_uint2(q.z, q.w) : make_uint2(q.x, q.y);
+}
+
 template <bool XBF16>
 __device__ __forceinline__ void dec_rgu_compute(const Layer &L, const Work &W, const DecX<XBF16> &xc, const uint2 *TL,
                                                 const uint2 *TS, int item, const DecPlan &P, const RguW &w,
@@ -497,14 +523,41 @@ __device__ __forceinline__ void dec_rgu_compute(const Layer &L, const Work &W, c
     const int j = item / P.rgu_per_slot, tile = item - j * P.rgu_per_slot;
     const int f0 = (tile * DEC_WAVES + wave) * (DEC_GU_NR * rpw) + lane / lpr;
     const int rep = lane & (IQ2B_REPL - 1);
+    // sub-block n (of NS) is row n / 4, gate or up, canonical sub-block n % 2;
+    // its lookups are issued while sub-block n - 1 is computed, into two named
+    // buffers by parity (no selects between them), and each scheduling barrier
+    // keeps the lookups after it (their registers) from being hoisted
+    constexpr int NS = 4 * DEC_GU_NR;
+    Iq2Tab t0, t1;
+    {
+        const uint2 q = dec_rgu_words(w, 0);
+        dec_iq2_fetch(TL, TS, q.x, q.y, rep, t0);
+    }
+    float a[2];
 #pragma unroll
-    for (int r = 0; r < DEC_GU_NR; ++r) {
-        const int f = f0 + r * rpw;
-        float g = dec_iq2_dot<XBF16>(TL, TS, w.qg[r], xc, rep) * (half_to_f32((uint16_t)w.dg[r]) * xc.scale);
-        float u = dec_iq2_dot<XBF16>(TL, TS, w.qu[r], xc, rep) * (half_to_f32((uint16_t)w.du[r]) * xc.scale);
-        g = dec_group_sum(g, lpr) * 0.015625f;
-        u = dec_group_sum(u, lpr) * 0.015625f;
-        if (c == 0 && f < F) st_tagged(W.htag + (int64_t)j * F + f, dec_silu(g) * u, tag);
+    for (int n = 0; n < NS; n += 2) {
+        {
+            const uint2 q = dec_rgu_words(w, n + 1);
+            dec_iq2_fetch(TL, TS, q.x, q.y, rep, t1);
+        }
+        a[(n >> 1) & 1] = dec_iq2_sub<XBF16>(t0, dec_rgu_words(w, n).y, xc, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (n + 2 < NS) {
+            const uint2 q = dec_rgu_words(w, n + 2);
+            dec_iq2_fetch(TL, TS, q.x, q.y, rep, t0);
+        }
+        a[(n >> 1) & 1] += dec_iq2_sub<XBF16>(t1, dec_rgu_words(w, n + 1).y, xc, 1);
+        if ((n & 3) == 2) {
+            // row r complete: gate in a[0], up in a[1], summed over the row's
+            // lanes into its last one
+            const int r = n >> 2, f = f0 + r * rpw;
+            float g = a[0] * (half_to_f32((uint16_t)w.dg[r]) * xc.scale);
+            float u = a[1] * (half_to_f32((uint16_t)w.du[r]) * xc.scale);
+            g = dec_group_sum_last(g, lpr) * 0.015625f;
+            u = dec_group_sum_last(u, lpr) * 0.015625f;
+            if (c == lpr - 1 && f < F) st_tagged(W.htag + (int64_t)j * F + f, dec_silu(g) * u, tag);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -583,15 +636,20 @@ __device__ __forceinline__ bool dec_stage_h(const Work &W, int F, int slot, uint
 // CPR = 16-byte chunks per lane per row (F / 512, at least 1); 16 chunk loads in
 // flight per wave, i.e. 16 / CPR rows per wave.
 template <int CPR>
-__device__ void dec_shdn_item(const Layer &L, const Work &W, float *__restrict__ out, int item, uint32_t tag,
+__device__ __forceinline__ void dec_shdn_item(const Layer &L, const Work &W, float *__restrict__ out, int item, uint32_t tag,
                               float4 *H, int &hid, bool &ok) {
     constexpr int RPW = 16 / CPR;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd, F = L.n_ff, k = L.top_k;
     const int nch = F >> 3;
     const int r0 = (item * DEC_WAVES + wave) * RPW;
-    // the weights do not depend on the gate/up phase: issue them first (rows
-    // and chunks past the matrix read valid data that is dropped below)
+    // the shared h vector's words are requested first (when not staged yet),
+    // then the weights (rows and chunks past the matrix read valid data that
+    // is dropped below): the h round trip overlaps the weights' and its wait
+    // does not include them
+    const bool stage = hid != k;
+    HPre hp;
+    if (stage) dec_h_issue(W, F, k, hp);
     uint4 wv[RPW][CPR];
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr)
@@ -601,8 +659,8 @@ __device__ void dec_shdn_item(const Layer &L, const Work &W, float *__restrict__
             wv[rr][c] = ld_at<uint4>(L.sh_down, 2u * (row * F + ch * 8u));
         }
     // the shared h vector in LDS (its gate/up items, once all stored)
-    if (hid != k) {
-        if (!dec_stage_h(W, F, k, tag, H)) {
+    if (stage) {
+        if (!dec_h_finish(W, F, k, tag, H, hp)) {
             ok = false;
             return;
         }
@@ -663,6 +721,57 @@ __device__ __forceinline__ void dec_rdn_load(const Layer &L, const DecPlan &P, c
     }
 }
 
+// H holds the slot's h vector (staged by the caller).  Each Q2_K row of the
+// lane (64 weights: 4 sub-blocks of 16, weight 16 s + 4 b + u in bits 2u of
+// byte b of word s) is d * sum_s sc_s dot_s - dmin * sum_s m_s hsum_s.
+__device__ __forceinline__ void dec_rdn_compute(const Layer &L, float *__restrict__ out, int item, const DecPlan &P,
+                                                const RouteCache *rc, const RdnW &w, const float4 *H) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int E = L.n_embd, F = L.n_ff;
+    const int lpr = F >> 6, rpw = 64 / lpr;
+    const int c = lane & (lpr - 1);
+    const int j = item / P.rdn_per_slot, tile = item - j * P.rdn_per_slot;
+    const int r0 = (tile * DEC_WAVES + wave) * (DEC_DN_NR * rpw) + lane / lpr;
+    const float wgt = rc->w[j];
+    float A[DEC_DN_NR], B[DEC_DN_NR];
+#pragma unroll
+    for (int r = 0; r < DEC_DN_NR; ++r) A[r] = 0.0f, B[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        float hv[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = H[h_slot(16 * c + 4 * s + q)];
+            hv[4 * q] = v.x, hv[4 * q + 1] = v.y, hv[4 * q + 2] = v.z, hv[4 * q + 3] = v.w;
+        }
+        float hsum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) hsum += hv[q];
+#pragma unroll
+        for (int r = 0; r < DEC_DN_NR; ++r) {
+            const uint32_t Q = s == 0 ? w.qs[r].x : s == 1 ? w.qs[r].y : s == 2 ? w.qs[r].z : w.qs[r].w;
+            float dot = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t tq = (Q >> (2 * u)) & 0x03030303u;
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) dot = fmaf((float)((tq >> (8 * bb)) & 0xFFu), hv[4 * bb + u], dot);
+            }
+            const uint32_t scb = (w.sc[r] >> (8 * s)) & 0xFFu;
+            A[r] = fmaf((float)(scb & 15u), dot, A[r]);
+            B[r] = fmaf((float)(scb >> 4), hsum, B[r]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < DEC_DN_NR; ++r) {
+        const int row = r0 + r * rpw;
+        const uint32_t dd = w.dd[r];
+        float y = half_to_f32((uint16_t)(dd & 0xFFFFu)) * A[r] - half_to_f32((uint16_t)(dd >> 16)) * B[r];
+        y = dec_group_sum(y, lpr);
+        if (c == 0 && row < E) atomicAdd(out + row, wgt * y);
+    }
+}
+
 // A routed slot's h vector staged in LDS for the Q2_K down projections, as
 // fp16 pairs laid out for the reading lanes.  Lane chunk c (h[64 c .. 64 c +
 // 63]) has per sub-block s (16 values, weight 4 b + u at bits 2u of byte b of
@@ -675,19 +784,31 @@ __device__ __forceinline__ void dec_rdn_load(const Layer &L, const DecPlan &P, c
 // Hsc[c] = 2^(24 + e_c) undoes both.  Hsum[s * lpr + c] is the sub-block's
 // plain fp32 sum of h, for the min term.  Consecutive lanes read consecutive
 // units: no bank conflicts.
-__device__ __forceinline__ bool dec_stage_h16(const Work &W, int F, int slot, uint32_t tag, uint4 *Hq, float *Hsc,
-                                              float *Hsum) {
-    const unsigned long long *src = W.htag + (int64_t)slot * F;
-    const int np = F >> 3, lpr = F >> 6;  // thread steps of 8 values; lanes per row
+// In two parts: dec_h16_issue loads the thread's tagged words early, so
+// their round trip overlaps other loads issued after them; dec_h16_finish
+// polls again whatever did not carry this call's tag yet, converts and
+// stores.  dec_h16_finish returns false, for the whole workgroup, if the
+// bounded wait expired.
+struct H16Pre {
     unsigned long long v[2][8];
+};
+__device__ __forceinline__ void dec_h16_issue(const Work &W, int F, int slot, H16Pre &pre) {
+    const unsigned long long *src = W.htag + (int64_t)slot * F;
+    const int np = F >> 3;  // thread steps of 8 values
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         // past the vector: re-read its last 8 values, ignored below
         const int p = min((int)threadIdx.x + 256 * q, np - 1);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            v[q][e] = __hip_atomic_load(src + 8 * p + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pre.v[q][e] = __hip_atomic_load(src + 8 * p + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+__device__ __forceinline__ bool dec_h16_finish(const Work &W, int F, int slot, uint32_t tag, uint4 *Hq, float *Hsc,
+                                               float *Hsum, H16Pre &pre) {
+    const unsigned long long *src = W.htag + (int64_t)slot * F;
+    const int np = F >> 3, lpr = F >> 6;  // thread steps of 8 values; lanes per row
+    unsigned long long (&v)[2][8] = pre.v;
     // the previous unit's reads of the staged vector are over
     __syncthreads();
     int ok = 1;
@@ -743,6 +864,13 @@ __device__ __forceinline__ bool dec_stage_h16(const Work &W, int F, int slot, ui
         }
     }
     return __syncthreads_and(ok) != 0;
+}
+// Both parts at once.
+__device__ __forceinline__ bool dec_stage_h16(const Work &W, int F, int slot, uint32_t tag, uint4 *Hq, float *Hsc,
+                                              float *Hsum) {
+    H16Pre pre;
+    dec_h16_issue(W, F, slot, pre);
+    return dec_h16_finish(W, F, slot, tag, Hq, Hsc, Hsum, pre);
 }
 
 // One routed down unit from the staged h vector: each Q2_K row of the lane (64
@@ -806,14 +934,6 @@ __device__ __forceinline__ int dec_rdn_unit(int l, int G, int n) {
     return o * q + min(o, r) + l / G;
 }
 
-// Loads the weights of a workgroup's first two routed down items (it_d and
-// it_d + G, if they exist) into da and db.
-__device__ __forceinline__ void dec_rdn_preload(const Layer &L, const DecPlan &P, const RouteCache *rc, int it_d,
-                                                int b3, int b4, int G, RdnW &da, RdnW &db) {
-    if (it_d < b4) dec_rdn_load(L, P, rc, dec_rdn_unit(it_d - b3, G, P.n_rdn), da);
-    if (it_d + G < b4) dec_rdn_load(L, P, rc, dec_rdn_unit(it_d + G - b3, G, P.n_rdn), db);
-}
-
 // ---------------------------------------------------------------- the persistent kernel
 template <bool XBF16>
 __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Layer L, Work W, const void *__restrict__ x,
@@ -823,7 +943,7 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
     __shared__ int lds_flag;
     __shared__ double lds_part[DEC_WAVES];
     __shared__ RouteCache rc;
-    __shared__ float4 H[1024];             // the shared h vector (n_ff <= 4096) for the shared down projections
+    __shared__ float4 H[1024];             // the shared h vector (n_ff <= 4096) for the shared down projection
     __shared__ uint4 Hq[512];              // a routed h vector as fp16 pairs (n_ff <= 4096)
     __shared__ float Hsc[64], Hsum[256];   // its per-chunk scales and per-sub-block sums
     const int G = gridDim.x;
@@ -880,31 +1000,26 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
         dec_shgu_compute<XBF16>(L, W, it - b0, sg, tag);
     }
     // routed gate/up: the next item's weights are in flight while this one is
-    // computed; the last item's computation covers the loads of the first two
-    // routed down items instead (they depend on the routing alone)
-    int it_d = blockIdx.x;  // this workgroup's first routed down item
-    while (it_d < b3) it_d += G;
-    RdnW da, db;
-    bool rdn_pre = false;
+    // computed.  A workgroup's last item runs at a raised wave priority: the
+    // two workgroups of a CU share its SIMDs, the older one's waves win equal
+    // priority, and the younger one (one item fewer) would otherwise wait for
+    // both of the older one's items, delaying the slots later units need.
     if (ok && it < b2) {
         for (;;) {
             bool more = it + G < b2;
-            if (more)
-                dec_rgu_load(L, P, &rc, it + G - b1, wb);
-            else
-                dec_rdn_preload(L, P, &rc, it_d, b3, b4, G, da, db), rdn_pre = true;
+            if (more) dec_rgu_load(L, P, &rc, it + G - b1, wb);
+            if (!more) __builtin_amdgcn_s_setprio(1);
             dec_rgu_compute<XBF16>(L, W, xc, TL, TS, it - b1, P, wa, tag);
             it += G;
             if (!more) break;
             more = it + G < b2;
-            if (more)
-                dec_rgu_load(L, P, &rc, it + G - b1, wa);
-            else
-                dec_rdn_preload(L, P, &rc, it_d, b3, b4, G, da, db), rdn_pre = true;
+            if (more) dec_rgu_load(L, P, &rc, it + G - b1, wa);
+            if (!more) __builtin_amdgcn_s_setprio(1);
             dec_rgu_compute<XBF16>(L, W, xc, TL, TS, it - b1, P, wb, tag);
             it += G;
             if (!more) break;
         }
+        __builtin_amdgcn_s_setprio(0);
     }
     int hid = -1;  // the h vector H holds (slot, or top_k for the shared one)
     for (; ok && it < b3; it += G) {
@@ -917,31 +1032,41 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
     }
     // routed down: each workgroup takes consecutive units (slot-major), so
     // its units mostly share one h vector, staged in LDS when the slot
-    // changes (before the next unit's load is issued, so the staging's polls
-    // do not wait for it); the first two units' weights were loaded ahead
+    // changes (before the next unit's prefetch, so the staging's polls do not
+    // wait for it); pipelined like routed gate/up otherwise
     if (ok && it < b4) {
-        if (!rdn_pre) dec_rdn_preload(L, P, &rc, it_d, b3, b4, G, da, db);
-        bool ahead = true;  // db already holds item it + G
-        for (;;) {
+        RdnW da, db;
+        {
+            // the first unit's h vector (H holds no routed one yet): its words
+            // are requested before the unit's weights
+            const int u = dec_rdn_unit(it - b3, G, P.n_rdn);
+            hid = u / P.rdn_per_slot;
+            H16Pre hp;
+            dec_h16_issue(W, L.n_ff, hid, hp);
+            dec_rdn_load(L, P, &rc, u, da);
+            ok = dec_h16_finish(W, L.n_ff, hid, tag, Hq, Hsc, Hsum, hp);
+        }
+        for (; ok;) {
             int u = dec_rdn_unit(it - b3, G, P.n_rdn);
             if (u / P.rdn_per_slot != hid) {
                 hid = u / P.rdn_per_slot;
                 if (!(ok = dec_stage_h16(W, L.n_ff, hid, tag, Hq, Hsc, Hsum))) break;
             }
-            if (!ahead && it + G < b4) dec_rdn_load(L, P, &rc, dec_rdn_unit(it + G - b3, G, P.n_rdn), db);
-            ahead = false;
+            bool more = it + G < b4;
+            if (more) dec_rdn_load(L, P, &rc, dec_rdn_unit(it + G - b3, G, P.n_rdn), db);
             dec_rdn_compute16(L, out, u, P, &rc, da, Hq, Hsc, Hsum);
             it += G;
-            if (it >= b4) break;
+            if (!more) break;
             u = dec_rdn_unit(it - b3, G, P.n_rdn);
             if (u / P.rdn_per_slot != hid) {
                 hid = u / P.rdn_per_slot;
                 if (!(ok = dec_stage_h16(W, L.n_ff, hid, tag, Hq, Hsc, Hsum))) break;
             }
-            if (it + G < b4) dec_rdn_load(L, P, &rc, dec_rdn_unit(it + G - b3, G, P.n_rdn), da);
+            more = it + G < b4;
+            if (more) dec_rdn_load(L, P, &rc, dec_rdn_unit(it + G - b3, G, P.n_rdn), da);
             dec_rdn_compute16(L, out, u, P, &rc, db, Hq, Hsc, Hsum);
             it += G;
-            if (it >= b4) break;
+            if (!more) break;
         }
     }
     // a bounded wait expired somewhere: make the failure visible in the output
