@@ -22,6 +22,7 @@ namespace ds4 {
 constexpr int QK = 256;
 constexpr int MAX_TOPK = 8;
 constexpr int MAX_EXPERT = 256;
+constexpr int RT_COPIES = 8;  // copies of the fused decode's router hand-off words (one per XCD)
 constexpr int GEMV_MAX_TOK = 4;   // GEMV path keeps up to this many tokens' x in registers
 
 struct Layer {
@@ -60,8 +61,9 @@ struct Work {
     int32_t *nchunks;     // number of valid chunks
     int32_t *ecount;      // [MAX_EXPERT] tokens per expert (batched router)
     float *rest;          // [4][max_tokens][NE] partial router estimates (batched router)
-    unsigned long long *rtag;  // [NE][2][2] fused decode: each fp64 half-row router sum as two 32-bit
-                               // halves, each tagged with the call's epoch in its upper 32 bits
+    unsigned long long *rtag;  // [RT_COPIES][2][2][MAX_EXPERT] fused decode: each fp64 half-row router
+                               // sum as two 32-bit halves, each tagged with the call's epoch in its
+                               // upper 32 bits
     unsigned long long *htag;  // [k+1][F] fused decode: SwiGLU outputs of the routed slots and the
                                // shared expert (fp32 bits), each tagged like rtag
 };

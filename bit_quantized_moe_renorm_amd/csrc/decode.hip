@@ -97,6 +97,13 @@ struct DecPlan {
 
 constexpr int SPIN_LIMIT = 1 << 20;      // polls before giving up (about a second)
 
+// An agent-scope read of a tagged word (the device's point of coherence),
+// as a global rather than a flat access.
+__device__ __forceinline__ unsigned long long poll_load(const unsigned long long *p) {
+    return __hip_atomic_load((const __attribute__((address_space(1))) unsigned long long *)p, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // One tagged word: fp32 bits below, the call's tag above.  A 64-bit store is
 // seen whole or not at all, so a reader that finds the tag has the value.
 __device__ __forceinline__ void st_tagged(unsigned long long *p, float v, uint32_t tag) {
@@ -436,15 +443,18 @@ __device__ __forceinline__ void dec_route_poll(const Layer &L, const Work &W, ui
             }
         int spins = 0, ok = 1;
         while (true) {
+            // all 16 words in flight at once (a word that already carries the
+            // tag reads the same again), then the tags
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    if (missing & (1u << (4 * i + q))) {
-                        v[i][q] = __hip_atomic_load(W.rtag + 4 * (lane + 64 * i) + q, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-                        if ((uint32_t)(v[i][q] >> 32) == tag) missing &= ~(1u << (4 * i + q));
-                    }
+                    v[i][q] = poll_load(W.rtag + 4 * min(lane + 64 * i, NE - 1) + q);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if ((uint32_t)(v[i][q] >> 32) == tag) missing &= ~(1u << (4 * i + q));
             if (!__any(missing != 0)) break;
             __builtin_amdgcn_s_sleep(4);
             if (++spins > SPIN_LIMIT) {
@@ -585,7 +595,7 @@ __device__ __forceinline__ void dec_h_issue(const Work &W, int F, int slot, HPre
         const int u = min((int)threadIdx.x + 256 * q, n4 - 1);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            p.v[q][e] = __hip_atomic_load(src + 4 * u + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            p.v[q][e] = poll_load(src + 4 * u + e);
     }
 }
 __device__ __forceinline__ bool dec_h_finish(const Work &W, int F, int slot, uint32_t tag, float4 *H, HPre &p) {
@@ -607,11 +617,10 @@ __device__ __forceinline__ bool dec_h_finish(const Work &W, int F, int slot, uin
             while (missing) {
                 __builtin_amdgcn_s_sleep(4);
 #pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = poll_load(src + 4 * u + e);
+#pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (missing & (1u << e)) {
-                        v[e] = __hip_atomic_load(src + 4 * u + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        if ((uint32_t)(v[e] >> 32) == tag) missing &= ~(1u << e);
-                    }
+                    if ((uint32_t)(v[e] >> 32) == tag) missing &= ~(1u << e);
                 if (missing && ++spins > SPIN_LIMIT) {
                     __hip_atomic_store(ctr(W, C_ERR), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     ok = 0;
@@ -801,7 +810,7 @@ __device__ __forceinline__ void dec_h16_issue(const Work &W, int F, int slot, H1
         const int p = min((int)threadIdx.x + 256 * q, np - 1);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            pre.v[q][e] = __hip_atomic_load(src + 8 * p + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pre.v[q][e] = poll_load(src + 8 * p + e);
     }
 }
 __device__ __forceinline__ bool dec_h16_finish(const Work &W, int F, int slot, uint32_t tag, uint4 *Hq, float *Hsc,
@@ -825,11 +834,10 @@ __device__ __forceinline__ bool dec_h16_finish(const Work &W, int F, int slot, u
         while (ok && missing) {
             __builtin_amdgcn_s_sleep(4);
 #pragma unroll
+            for (int e = 0; e < 8; ++e) v[q][e] = poll_load(src + 8 * p + e);
+#pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (missing & (1u << e)) {
-                    v[q][e] = __hip_atomic_load(src + 8 * p + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if ((uint32_t)(v[q][e] >> 32) == tag) missing &= ~(1u << e);
-                }
+                if ((uint32_t)(v[q][e] >> 32) == tag) missing &= ~(1u << e);
             if (missing && ++spins > SPIN_LIMIT) {
                 __hip_atomic_store(ctr(W, C_ERR), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ok = 0;
