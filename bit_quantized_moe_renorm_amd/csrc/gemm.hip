@@ -142,19 +142,21 @@ constexpr int LD_PER_ROW = 32 / LD_V;             // threads per token row
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 // Block stage loader: thread t moves LD_V x 16 bytes: token row t / LD_PER_ROW,
-// K 8 LD_V (t % LD_PER_ROW)..+8 LD_V.
+// K 8 LD_V (t % LD_PER_ROW)..+8 LD_V.  Every load is unconditional (a load
+// under a condition leaves a path without it, and the first use after the
+// join would then wait for every load in flight): rows past the chunk read
+// the chunk's last row, whose products land in accumulator rows never stored.
 struct BlockLoader {
-    const uint16_t *src;   // row start + K offset, or nullptr for rows past the chunk
+    const uint16_t *src;   // row start + K offset
     int lds_off;
     __device__ void init(const uint16_t *row, int tid) {
         const int p = tid % LD_PER_ROW;
-        src = row ? row + 8 * LD_V * p : nullptr;
+        src = row + 8 * LD_V * p;
         lds_off = (tid / LD_PER_ROW) * RB_PITCH + 16 * LD_V * p;
     }
     __device__ void load(int bi, uint4 (&r)[LD_V]) const {
 #pragma unroll
-        for (int j = 0; j < LD_V; ++j)
-            r[j] = src ? *reinterpret_cast<const uint4 *>(src + QK * bi + 8 * j) : make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < LD_V; ++j) r[j] = *reinterpret_cast<const uint4 *>(src + QK * bi + 8 * j);
     }
     __device__ void store(uint8_t *stg, const uint4 (&r)[LD_V]) const {
 #pragma unroll
@@ -194,10 +196,12 @@ __device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &
 
     for (int bi = 0; bi < nbe; ++bi) {
         const bool more = bi + 1 < nbe;
-        if (more) {
-            ld.load(bi + 1, xr);
+        {
+            // the next block (the last one again past the end: unused), unconditionally
+            const int bn = min(bi + 1, nbe - 1);
+            ld.load(bn, xr);
 #pragma unroll
-            for (int fi = 0; fi < GU_NF; ++fi) wnext[fi] = wload(fi, bi + 1), dnext[fi] = dload(fi, bi + 1);
+            for (int fi = 0; fi < GU_NF; ++fi) wnext[fi] = wload(fi, bn), dnext[fi] = dload(fi, bn);
         }
         const uint8_t *cur = (bi & 1) ? stg1 : stg0;
         half2v scl[GU_NF];
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_gateup_routed(Layer L, W
     BlockLoader ld;
     {
         const int sr = tid / LD_PER_ROW;
-        ld.init(sr < cnt ? W.x16 + (int64_t)(W.list[beg + sr] / k) * E : nullptr, tid);
+        ld.init(W.x16 + (int64_t)(W.list[beg + min(sr, cnt - 1)] / k) * E, tid);
     }
     const int f0 = blockIdx.x * RGU_ROWS + wave * 16 * GU_FR;
     // fragment fi: matrix fi / GU_FR (gate, up), rows f0 + 16 (fi % GU_FR) + rl
@@ -313,9 +317,9 @@ __device__ __forceinline__ void down_routed_tiles(const Layer &L, const Work &W,
                                                   const uint32_t *db, int fq, int fs, int fd, bool active, int r0,
                                                   int beg, int cnt, int rl, int grp) {
     const int E = L.n_embd, nbf = L.nbf;
+    // loads are unconditional (inactive waves read row 0: in bounds, unused)
     uint4 qcur[DN_NF], qnext[DN_NF];
     uint32_t scur[DN_NF], snext[DN_NF], dcur[DN_NF], dnext[DN_NF];
-    if (active)
 #pragma unroll
         for (int fi = 0; fi < DN_NF; ++fi) {
             qcur[fi] = *reinterpret_cast<const uint4 *>(qb + fi * fq);
@@ -332,15 +336,16 @@ __device__ __forceinline__ void down_routed_tiles(const Layer &L, const Work &W,
 
     for (int bi = 0; bi < nbf; ++bi) {
         const bool more = bi + 1 < nbf;
-        if (more) {
-            ld.load(bi + 1, xr);
-            if (active)
+        {
+            // the next block (the last one again past the end: unused), unconditionally
+            const int bn = min(bi + 1, nbf - 1);
+            ld.load(bn, xr);
 #pragma unroll
-                for (int fi = 0; fi < DN_NF; ++fi) {
-                    qnext[fi] = *reinterpret_cast<const uint4 *>(qb + fi * fq + 64 * (bi + 1));
-                    snext[fi] = *reinterpret_cast<const uint32_t *>(sb + fi * fs + 16 * (bi + 1));
-                    dnext[fi] = db[fi * fd + bi + 1];
-                }
+            for (int fi = 0; fi < DN_NF; ++fi) {
+                qnext[fi] = *reinterpret_cast<const uint4 *>(qb + fi * fq + 64 * bn);
+                snext[fi] = *reinterpret_cast<const uint32_t *>(sb + fi * fs + 16 * bn);
+                dnext[fi] = db[fi * fd + bn];
+            }
         }
         if (active) {
             const uint8_t *cur = (bi & 1) ? stg1 : stg0;
@@ -421,7 +426,7 @@ __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_down_routed(Layer L, Wor
     BlockLoader ld;
     {
         const int sr = tid / LD_PER_ROW;
-        ld.init(sr < cnt ? W.hbuf16 + (int64_t)W.list[beg + sr] * F : nullptr, tid);
+        ld.init(W.hbuf16 + (int64_t)W.list[beg + min(sr, cnt - 1)] * F, tid);
     }
     const int r0 = blockIdx.x * RDN_ROWS + wave * 16 * DN_NF;
     const bool active = r0 < E;
@@ -458,9 +463,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gateup_shared(Layer L, Work W, 
     const int E = L.n_embd, F = L.n_ff;
     const int nt = (cnt + 15) >> 4;
     const int nkc = E / 32;
+    // unconditional loads from clamped addresses (see the shared down kernel)
     const int sr = tid >> 2;
-    const int64_t xo = (int64_t)(t0 + sr) * E + 8 * (tid & 3);
-    const bool xok = sr < cnt;
+    const int64_t xo = (int64_t)(t0 + min(sr, cnt - 1)) * E + 8 * (tid & 3);
 
     const int f0 = blockIdx.x * GU_ROWS + wave * 32;
     const uint4 *wp[4];
@@ -471,18 +476,21 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gateup_shared(Layer L, Work W, 
     }
     constexpr int SPF = 2;
     uint4 xh[SPF], xl[SPF], wr[SPF][4];
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int s = 0; s < SPF; ++s) {
-        xh[s] = (xok && s < nkc) ? *reinterpret_cast<const uint4 *>(xhi + xo + 32 * s) : z4;
-        xl[s] = (SPLIT && xok && s < nkc) ? *reinterpret_cast<const uint4 *>(xlo + xo + 32 * s) : z4;
+        const int kq = min(s, nkc - 1);
+        xh[s] = *reinterpret_cast<const uint4 *>(xhi + xo + 32 * kq);
+        if (SPLIT) xl[s] = *reinterpret_cast<const uint4 *>(xlo + xo + 32 * kq);
 #pragma unroll
-        for (int fi = 0; fi < 4; ++fi) wr[s][fi] = (s < nkc) ? wp[fi][4 * s] : z4;
+        for (int fi = 0; fi < 4; ++fi) wr[s][fi] = wp[fi][4 * kq];
     }
     stage_put(stg[0][0], tid, xh[0]);
     if (SPLIT) stage_put(stg[0][1], tid, xl[0]);
-    xh[0] = (xok && SPF < nkc) ? *reinterpret_cast<const uint4 *>(xhi + xo + 32 * SPF) : z4;
-    if (SPLIT) xl[0] = (xok && SPF < nkc) ? *reinterpret_cast<const uint4 *>(xlo + xo + 32 * SPF) : z4;
+    {
+        const int kq = min(SPF, nkc - 1);
+        xh[0] = *reinterpret_cast<const uint4 *>(xhi + xo + 32 * kq);
+        if (SPLIT) xl[0] = *reinterpret_cast<const uint4 *>(xlo + xo + 32 * kq);
+    }
     __syncthreads();
 
     floatx4 acc[4][4];
@@ -501,7 +509,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gateup_shared(Layer L, Work W, 
 #pragma unroll
             for (int fi = 0; fi < 4; ++fi) {
                 b[fi] = wr[s][fi];
-                wr[s][fi] = (kc + SPF < nkc) ? wp[fi][4 * (kc + SPF)] : z4;
+                wr[s][fi] = wp[fi][4 * min(kc + SPF, nkc - 1)];
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -520,9 +528,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gateup_shared(Layer L, Work W, 
             if (kc + 1 < nkc) {
                 stage_put(stg[(kc + 1) & 1][0], tid, xh[sn]);
                 if (SPLIT) stage_put(stg[(kc + 1) & 1][1], tid, xl[sn]);
-                xh[sn] = (xok && kc + 1 + SPF < nkc) ? *reinterpret_cast<const uint4 *>(xhi + xo + 32 * (kc + 1 + SPF)) : z4;
-                if (SPLIT)
-                    xl[sn] = (xok && kc + 1 + SPF < nkc) ? *reinterpret_cast<const uint4 *>(xlo + xo + 32 * (kc + 1 + SPF)) : z4;
+                const int kq = min(kc + 1 + SPF, nkc - 1);
+                xh[sn] = *reinterpret_cast<const uint4 *>(xhi + xo + 32 * kq);
+                if (SPLIT) xl[sn] = *reinterpret_cast<const uint4 *>(xlo + xo + 32 * kq);
             }
             __syncthreads();
         }
@@ -559,9 +567,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_shared(Layer L, Work W, in
     const int E = L.n_embd, F = L.n_ff;
     const int nt = (cnt + 15) >> 4;
     const int nkc = F / 32;
+    // loads never depend on a condition (a select between a load and a zero
+    // vector becomes a flat load from a stack slot, waited on at once): rows
+    // past the chunk read the chunk's last row (their results are dropped),
+    // and prefetches past the last K chunk re-read it (unused)
     const int sr = tid >> 2;
-    const int64_t ho = (int64_t)(t0 + sr) * F + 8 * (tid & 3);
-    const bool hok = sr < cnt;
+    const int64_t ho = (int64_t)(t0 + min(sr, cnt - 1)) * F + 8 * (tid & 3);
 
     const int r0 = blockIdx.x * DN_ROWS + wave * 64;
     const uint4 *wp[4];
@@ -570,18 +581,21 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_shared(Layer L, Work W, in
         wp[fi] = reinterpret_cast<const uint4 *>(L.sh_down + (int64_t)(r0 + 16 * fi + rl) * F + 8 * grp);
     constexpr int SPF = 2;
     uint4 xh[SPF], xl[SPF], wr[SPF][4];
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int s = 0; s < SPF; ++s) {
-        xh[s] = (hok && s < nkc) ? *reinterpret_cast<const uint4 *>(W.hsh_hi + ho + 32 * s) : z4;
-        xl[s] = (hok && s < nkc) ? *reinterpret_cast<const uint4 *>(W.hsh_lo + ho + 32 * s) : z4;
+        const int kq = min(s, nkc - 1);
+        xh[s] = *reinterpret_cast<const uint4 *>(W.hsh_hi + ho + 32 * kq);
+        xl[s] = *reinterpret_cast<const uint4 *>(W.hsh_lo + ho + 32 * kq);
 #pragma unroll
-        for (int fi = 0; fi < 4; ++fi) wr[s][fi] = (s < nkc) ? wp[fi][4 * s] : z4;
+        for (int fi = 0; fi < 4; ++fi) wr[s][fi] = wp[fi][4 * kq];
     }
     stage_put(stg[0][0], tid, xh[0]);
     stage_put(stg[0][1], tid, xl[0]);
-    xh[0] = (hok && SPF < nkc) ? *reinterpret_cast<const uint4 *>(W.hsh_hi + ho + 32 * SPF) : z4;
-    xl[0] = (hok && SPF < nkc) ? *reinterpret_cast<const uint4 *>(W.hsh_lo + ho + 32 * SPF) : z4;
+    {
+        const int kq = min(SPF, nkc - 1);
+        xh[0] = *reinterpret_cast<const uint4 *>(W.hsh_hi + ho + 32 * kq);
+        xl[0] = *reinterpret_cast<const uint4 *>(W.hsh_lo + ho + 32 * kq);
+    }
     __syncthreads();
 
     floatx4 acc[4][4];
@@ -600,26 +614,33 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_shared(Layer L, Work W, in
 #pragma unroll
             for (int fi = 0; fi < 4; ++fi) {
                 b[fi] = wr[s][fi];
-                wr[s][fi] = (kc + SPF < nkc) ? wp[fi][4 * (kc + SPF)] : z4;
+                wr[s][fi] = wp[fi][4 * min(kc + SPF, nkc - 1)];
             }
+            // the high parts for every tile, then the low parts: no MFMA
+            // waits on the one just issued
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (i < nt) {
                     const uint4 a = stage_get(stg[kc & 1][0], i, rl, grp);
+#pragma unroll
+                    for (int fi = 0; fi < 4; ++fi) acc[i][fi] = mfma_bf16(a, b[fi], acc[i][fi]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i < nt) {
                     const uint4 al = stage_get(stg[kc & 1][1], i, rl, grp);
 #pragma unroll
-                    for (int fi = 0; fi < 4; ++fi) {
-                        acc[i][fi] = mfma_bf16(a, b[fi], acc[i][fi]);
-                        acc[i][fi] = mfma_bf16(al, b[fi], acc[i][fi]);
-                    }
+                    for (int fi = 0; fi < 4; ++fi) acc[i][fi] = mfma_bf16(al, b[fi], acc[i][fi]);
                 }
             }
             const int sn = (s + 1) & (SPF - 1);
             if (kc + 1 < nkc) {
                 stage_put(stg[(kc + 1) & 1][0], tid, xh[sn]);
                 stage_put(stg[(kc + 1) & 1][1], tid, xl[sn]);
-                xh[sn] = (hok && kc + 1 + SPF < nkc) ? *reinterpret_cast<const uint4 *>(W.hsh_hi + ho + 32 * (kc + 1 + SPF)) : z4;
-                xl[sn] = (hok && kc + 1 + SPF < nkc) ? *reinterpret_cast<const uint4 *>(W.hsh_lo + ho + 32 * (kc + 1 + SPF)) : z4;
+                const int kq = min(kc + 1 + SPF, nkc - 1);
+                xh[sn] = *reinterpret_cast<const uint4 *>(W.hsh_hi + ho + 32 * kq);
+                xl[sn] = *reinterpret_cast<const uint4 *>(W.hsh_lo + ho + 32 * kq);
             }
             __syncthreads();
         }
@@ -631,9 +652,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_shared(Layer L, Work W, in
         for (int v = 0; v < 4; ++v) {
             const int tt = 16 * i + 4 * grp + v;
             if (tt >= cnt) continue;
+            // each output element gets exactly one shared contribution, and
+            // nothing else writes out meanwhile: a plain read-modify-write
             float *orow = out + (int64_t)(t0 + tt) * E + r0 + rl;
 #pragma unroll
-            for (int fi = 0; fi < 4; ++fi) atomicAdd(orow + 16 * fi, acc[i][fi][v]);
+            for (int fi = 0; fi < 4; ++fi) orow[16 * fi] += acc[i][fi][v];
         }
     }
 }
