@@ -474,65 +474,111 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gateup_shared(Layer L, Work W, 
         const uint16_t *base = (fi >> 1) ? L.sh_up : L.sh_gate;
         wp[fi] = reinterpret_cast<const uint4 *>(base + (int64_t)(f0 + 16 * (fi & 1) + rl) * E + 8 * grp);  // kc: wp[fi][4 kc]
     }
-    constexpr int SPF = 2;
-    uint4 xh[SPF], xl[SPF], wr[SPF][4];
-#pragma unroll
-    for (int s = 0; s < SPF; ++s) {
-        const int kq = min(s, nkc - 1);
-        xh[s] = *reinterpret_cast<const uint4 *>(xhi + xo + 32 * kq);
-        if (SPLIT) xl[s] = *reinterpret_cast<const uint4 *>(xlo + xo + 32 * kq);
-#pragma unroll
-        for (int fi = 0; fi < 4; ++fi) wr[s][fi] = wp[fi][4 * kq];
-    }
-    stage_put(stg[0][0], tid, xh[0]);
-    if (SPLIT) stage_put(stg[0][1], tid, xl[0]);
-    {
-        const int kq = min(SPF, nkc - 1);
-        xh[0] = *reinterpret_cast<const uint4 *>(xhi + xo + 32 * kq);
-        if (SPLIT) xl[0] = *reinterpret_cast<const uint4 *>(xlo + xo + 32 * kq);
-    }
-    __syncthreads();
-
     floatx4 acc[4][4];
     const floatx4 zf = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int fi = 0; fi < 4; ++fi) acc[i][fi] = zf;
-
-    for (int k0 = 0; k0 < nkc; k0 += SPF) {
+    if constexpr (!SPLIT) {
+        // one part of x: the stage's second plane holds the next K chunk, so
+        // each barrier covers two chunks (n_embd / 32 is even)
+        uint4 xh[2], wr[2][4];
 #pragma unroll
-        for (int s = 0; s < SPF; ++s) {
-            const int kc = k0 + s;
-            if (kc >= nkc) break;
-            uint4 b[4];
+        for (int s = 0; s < 2; ++s) {
+            xh[s] = *reinterpret_cast<const uint4 *>(xhi + xo + 32 * s);
 #pragma unroll
-            for (int fi = 0; fi < 4; ++fi) {
-                b[fi] = wr[s][fi];
-                wr[s][fi] = wp[fi][4 * min(kc + SPF, nkc - 1)];
-            }
+            for (int fi = 0; fi < 4; ++fi) wr[s][fi] = wp[fi][4 * s];
+        }
+        stage_put(stg[0][0], tid, xh[0]);
+        stage_put(stg[0][1], tid, xh[1]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i < nt) {
-                    const uint4 a = stage_get(stg[kc & 1][0], i, rl, grp);
+        for (int s = 0; s < 2; ++s) xh[s] = *reinterpret_cast<const uint4 *>(xhi + xo + 32 * min(2 + s, nkc - 1));
+        __syncthreads();
+        for (int k0 = 0; k0 < nkc; k0 += 2) {
+            const int buf = (k0 >> 1) & 1;
+            uint4 b[2][4];
 #pragma unroll
-                    for (int fi = 0; fi < 4; ++fi) acc[i][fi] = mfma_bf16(a, b[fi], acc[i][fi]);
-                    if (SPLIT) {
-                        const uint4 al = stage_get(stg[kc & 1][1], i, rl, grp);
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
-                        for (int fi = 0; fi < 4; ++fi) acc[i][fi] = mfma_bf16(al, b[fi], acc[i][fi]);
+                for (int fi = 0; fi < 4; ++fi) {
+                    b[s][fi] = wr[s][fi];
+                    wr[s][fi] = wp[fi][4 * min(k0 + 2 + s, nkc - 1)];
+                }
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (i < nt) {
+                        const uint4 a = stage_get(stg[buf][s], i, rl, grp);
+#pragma unroll
+                        for (int fi = 0; fi < 4; ++fi) acc[i][fi] = mfma_bf16(a, b[s][fi], acc[i][fi]);
                     }
                 }
-            }
-            const int sn = (s + 1) & (SPF - 1);
-            if (kc + 1 < nkc) {
-                stage_put(stg[(kc + 1) & 1][0], tid, xh[sn]);
-                if (SPLIT) stage_put(stg[(kc + 1) & 1][1], tid, xl[sn]);
-                const int kq = min(kc + 1 + SPF, nkc - 1);
-                xh[sn] = *reinterpret_cast<const uint4 *>(xhi + xo + 32 * kq);
-                if (SPLIT) xl[sn] = *reinterpret_cast<const uint4 *>(xlo + xo + 32 * kq);
+            if (k0 + 2 < nkc) {
+                stage_put(stg[buf ^ 1][0], tid, xh[0]);
+                stage_put(stg[buf ^ 1][1], tid, xh[1]);
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    xh[s] = *reinterpret_cast<const uint4 *>(xhi + xo + 32 * min(k0 + 4 + s, nkc - 1));
             }
             __syncthreads();
+        }
+    } else {
+        constexpr int SPF = 2;
+        uint4 xh[SPF], xl[SPF], wr[SPF][4];
+    #pragma unroll
+        for (int s = 0; s < SPF; ++s) {
+            const int kq = min(s, nkc - 1);
+            xh[s] = *reinterpret_cast<const uint4 *>(xhi + xo + 32 * kq);
+            if (SPLIT) xl[s] = *reinterpret_cast<const uint4 *>(xlo + xo + 32 * kq);
+    #pragma unroll
+            for (int fi = 0; fi < 4; ++fi) wr[s][fi] = wp[fi][4 * kq];
+        }
+        stage_put(stg[0][0], tid, xh[0]);
+        if (SPLIT) stage_put(stg[0][1], tid, xl[0]);
+        {
+            const int kq = min(SPF, nkc - 1);
+            xh[0] = *reinterpret_cast<const uint4 *>(xhi + xo + 32 * kq);
+            if (SPLIT) xl[0] = *reinterpret_cast<const uint4 *>(xlo + xo + 32 * kq);
+        }
+        __syncthreads();
+
+
+        for (int k0 = 0; k0 < nkc; k0 += SPF) {
+    #pragma unroll
+            for (int s = 0; s < SPF; ++s) {
+                const int kc = k0 + s;
+                if (kc >= nkc) break;
+                uint4 b[4];
+    #pragma unroll
+                for (int fi = 0; fi < 4; ++fi) {
+                    b[fi] = wr[s][fi];
+                    wr[s][fi] = wp[fi][4 * min(kc + SPF, nkc - 1)];
+                }
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (i < nt) {
+                        const uint4 a = stage_get(stg[kc & 1][0], i, rl, grp);
+    #pragma unroll
+                        for (int fi = 0; fi < 4; ++fi) acc[i][fi] = mfma_bf16(a, b[fi], acc[i][fi]);
+                        if (SPLIT) {
+                            const uint4 al = stage_get(stg[kc & 1][1], i, rl, grp);
+    #pragma unroll
+                            for (int fi = 0; fi < 4; ++fi) acc[i][fi] = mfma_bf16(al, b[fi], acc[i][fi]);
+                        }
+                    }
+                }
+                const int sn = (s + 1) & (SPF - 1);
+                if (kc + 1 < nkc) {
+                    stage_put(stg[(kc + 1) & 1][0], tid, xh[sn]);
+                    if (SPLIT) stage_put(stg[(kc + 1) & 1][1], tid, xl[sn]);
+                    const int kq = min(kc + 1 + SPF, nkc - 1);
+                    xh[sn] = *reinterpret_cast<const uint4 *>(xhi + xo + 32 * kq);
+                    if (SPLIT) xl[sn] = *reinterpret_cast<const uint4 *>(xlo + xo + 32 * kq);
+                }
+                __syncthreads();
+            }
         }
     }
     // h = silu(gate) * up, stored as bf16 high and low parts
