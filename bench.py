@@ -308,10 +308,7 @@ def run_stack(args):
     xb = torch.empty((1, spec.n_embd), dtype=torch.bfloat16, device="cuda")
 
     def token(t):
-        ht = h[t:t + 1]
-        for dev in devs:
-            m.rmsnorm(ht, out=xb, stream=stream)
-            dev.forward(xb, ht, stream)
+        m.forward_stack(devs, h[t:t + 1], x=xb, stream=stream)
 
     for t in range(8):                      # warm-up tokens
         token(n_dec + t)
@@ -334,10 +331,7 @@ def run_stack(args):
 
     def prefill():
         for c0 in range(0, n_pre, chunk):
-            hc = hp[c0:c0 + chunk]
-            for dev in devs:
-                m.rmsnorm(hc, out=xp, stream=stream)
-                dev.forward(xp, hc, stream)
+            m.forward_stack(devs, hp[c0:c0 + chunk], x=xp, stream=stream)
 
     prefill()                               # warm-up pass (the stream's values are not checked here)
     torch.cuda.synchronize()

@@ -24,8 +24,8 @@ TIMING_KINDS = ("route", "gateup_routed", "gateup_shared", "down_routed", "down_
                 "gemm_down_routed", "fused", "gemm_prep", "gemm_gateup_shared", "gemm_down_shared")
 
 SYMBOLS = ("ds4moe_create", "ds4moe_route", "ds4moe_forward", "ds4moe_set_path", "ds4moe_dequantize",
-           "ds4moe_rmsnorm", "ds4moe_timing_enable", "ds4moe_timing_read", "ds4moe_destroy",
-           "ds4moe_last_error")
+           "ds4moe_rmsnorm", "ds4moe_forward_stack", "ds4moe_timing_enable", "ds4moe_timing_read",
+           "ds4moe_destroy", "ds4moe_last_error")
 
 
 class Ds4MoeError(RuntimeError):
@@ -65,6 +65,7 @@ def load_library(path: Optional[Path] = None) -> ctypes.CDLL:
     L.ds4moe_set_path.argtypes = [P, i32]
     L.ds4moe_dequantize.argtypes = [P, i32, i32, P, P]
     L.ds4moe_rmsnorm.argtypes = [P, i32, i32, ctypes.c_double, P, P]
+    L.ds4moe_forward_stack.argtypes = [P, i32, P, i32, ctypes.c_double, P, P]
     L.ds4moe_timing_enable.argtypes = [P, i32]
     L.ds4moe_timing_read.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     L.ds4moe_destroy.argtypes = [P]
@@ -177,6 +178,19 @@ def rmsnorm(h, eps: float = 1e-6, out=None, stream=None):
         out = torch.empty((n, E), dtype=torch.bfloat16, device=h.device)
     _check(load_library().ds4moe_rmsnorm(_ptr(h), n, E, eps, _ptr(out), _stream(stream)))
     return out
+
+
+def forward_stack(layers, h, eps: float = 1e-6, x=None, stream=None):
+    """For each layer in order: x = RMSNorm(h), h += MoE(x), all enqueued by
+    one library call (h fp32 [n, E] on the GPU, updated in place; x optional
+    bf16 [n, E] scratch).  Returns h."""
+    import torch
+    n, E = h.shape
+    if x is None:
+        x = torch.empty((n, E), dtype=torch.bfloat16, device=h.device)
+    hs = (ctypes.c_void_p * len(layers))(*[lay.h.value for lay in layers])
+    _check(load_library().ds4moe_forward_stack(hs, len(layers), _ptr(h), n, eps, _ptr(x), _stream(stream)))
+    return h
 
 
 def upload_layer(layer, device="cuda"):

@@ -360,6 +360,33 @@ int ds4moe_rmsnorm(const float *hin, int32_t n_tok, int32_t n_embd, double eps, 
     return DS4MOE_OK;
 }
 
+int ds4moe_forward_stack(ds4moe_t *const *layers, int32_t n_layers, float *h, int32_t n_tok, double eps,
+                         uint16_t *x_bf16, void *stream) {
+    if (!layers || n_layers < 1) return fail(DS4MOE_EINVAL, "forward_stack: no layers");
+    if (n_tok < 0 || !(eps >= 0.0)) return fail(DS4MOE_EINVAL, "forward_stack: n_tok %d, eps %g", n_tok, eps);
+    if (n_tok > 0 && (!h || !x_bf16)) return fail(DS4MOE_EINVAL, "forward_stack: NULL h or x");
+    // every layer is checked before anything is enqueued
+    for (int l = 0; l < n_layers; ++l) {
+        ds4moe *d = layers[l];
+        int rc = common_checks(d, x_bf16, n_tok, "forward_stack");
+        if (rc) return fail(rc, "forward_stack: layer %d: %s", l, g_err.c_str());
+        if (d->L.act_dtype != DS4MOE_BF16)
+            return fail(DS4MOE_EINVAL, "forward_stack: layer %d takes fp32 activations (needs bf16)", l);
+        if (d->L.n_embd != layers[0]->L.n_embd)
+            return fail(DS4MOE_EINVAL, "forward_stack: layer %d has n_embd %d, layer 0 %d", l, d->L.n_embd,
+                        layers[0]->L.n_embd);
+    }
+    if (n_tok == 0) return DS4MOE_OK;
+    const int E = layers[0]->L.n_embd;
+    for (int l = 0; l < n_layers; ++l) {
+        hipError_t e = launch_rmsnorm(h, n_tok, E, eps, x_bf16, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(DS4MOE_EHIP, "forward_stack: layer %d rmsnorm: %s", l, hipGetErrorString(e));
+        int rc = ds4moe_forward(layers[l], x_bf16, n_tok, h, stream);
+        if (rc) return fail(rc, "forward_stack: layer %d: %s", l, g_err.c_str());
+    }
+    return DS4MOE_OK;
+}
+
 int ds4moe_timing_enable(ds4moe_t *h, int32_t enable) {
     if (!h) return fail(DS4MOE_EINVAL, "timing_enable: NULL handle");
     if (enable && h->events.empty()) {

@@ -163,6 +163,25 @@ int ds4moe_rmsnorm(const float *h, int32_t n_tok, int32_t n_embd, double eps, ui
                    void *stream);
 
 /*
+ * A stack of layers on one residual stream: the per-layer loop of the
+ * inference pseudo-code ("ds4 深度实战...", section 3.2) with attention left
+ * out and a unit-gain RMSNorm in front of each MoE block.  For
+ * l = 0 .. n_layers-1,
+ *   x = RMSNorm(h)  (exactly as ds4moe_rmsnorm with eps), then
+ *   h += MoE_l(x)   (exactly as ds4moe_forward on layers[l]).
+ * h: device fp32 [n_tok][n_embd], updated in place.  x_bf16: device scratch
+ * of n_tok * n_embd bf16 values, caller-owned, overwritten.  Every layer must
+ * take bf16 activations, share n_embd and allow n_tok tokens.  All launches
+ * are enqueued from this one host call (two per layer at n_tok = 1), so the
+ * host does not pace the device.  Errors: every layer is validated before
+ * anything is enqueued (DS4MOE_EINVAL / DS4MOE_EPOISONED, nothing enqueued);
+ * a launch failure at layer l returns DS4MOE_EHIP with layers before l
+ * already enqueued, and the message names l.
+ */
+int ds4moe_forward_stack(ds4moe_t *const *layers, int32_t n_layers, float *h, int32_t n_tok, double eps,
+                         uint16_t *x_bf16, void *stream);
+
+/*
  * Per-kernel timing for benchmarks.  When enabled, ds4moe_forward records HIP
  * events around each kernel it launches on the caller's stream; read back the
  * accumulated milliseconds and launch counts (after synchronising the stream)

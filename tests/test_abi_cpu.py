@@ -66,6 +66,13 @@ def test_validation_without_gpu(lib):
     assert lib.ds4moe_rmsnorm(None, -1, 16, 1e-6, None, None) == m.EINVAL
     assert lib.ds4moe_rmsnorm(None, 1, 0, 1e-6, None, None) == m.EINVAL
     assert lib.ds4moe_rmsnorm(None, 0, 16, 1e-6, None, None) == m.OK
+    # forward_stack: no layers, a NULL layer handle, bad eps
+    assert lib.ds4moe_forward_stack(None, 1, None, 1, 1e-6, None, None) == m.EINVAL
+    one_null = (ctypes.c_void_p * 1)(None)
+    assert lib.ds4moe_forward_stack(one_null, 0, None, 1, 1e-6, None, None) == m.EINVAL
+    assert lib.ds4moe_forward_stack(one_null, 1, 1, 1, 1e-6, 1, None) == m.EINVAL
+    assert b"layer 0" in lib.ds4moe_last_error()
+    assert lib.ds4moe_forward_stack(one_null, 1, 1, 1, -1.0, 1, None) == m.EINVAL
 
 
 def test_binding_has_no_fallback(tmp_path):

@@ -9,6 +9,8 @@ change it: each logit moves by at most |router row| . |x_gpu - x_ref|, so the
 selected set (and its order) is checked for every token whose logit gaps exceed
 those bounds.
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -28,15 +30,16 @@ N_LAYERS, N_TOK = 3, 4
 SEED0 = 4000  # layer l uses seed 4000 + l
 
 
-def _layers():
-    return [synth.make_layer(synth.DS4, seed=SEED0 + l) for l in range(N_LAYERS)]
+@functools.lru_cache(maxsize=1)
+def _case():
+    layers = [synth.make_layer(synth.DS4, seed=SEED0 + l) for l in range(N_LAYERS)]
+    h0 = synth.residual(40, N_TOK, 4096)
+    return layers, h0, oracle.stack(layers, h0)
 
 
 @pytest.mark.parametrize("per_token", [True, False], ids=["decode_b1", "batch4"])
 def test_stack_matches_oracle(per_token):
-    layers = _layers()
-    h0 = synth.residual(40, N_TOK, 4096)
-    ref_h, ref_x, ref_idx, ref_logits = oracle.stack(layers, h0)
+    layers, h0, (ref_h, ref_x, ref_idx, ref_logits) = _case()
 
     devs = []
     for l, lay in enumerate(layers):
@@ -91,6 +94,33 @@ def test_stack_matches_oracle(per_token):
     contrib_ref = ref_h.astype(np.float64) - h0
     err = rel_err(contrib_gpu, contrib_ref)
     log(f"[gpu] stack of {N_LAYERS} ({'decode b=1' if per_token else 'batch of 4'}): "
+        f"rel err of the accumulated block outputs {err:.3e}")
+    assert err <= REL_TOL
+    assert np.all(np.isfinite(got_h))
+
+
+@pytest.mark.parametrize("per_token", [True, False], ids=["decode_b1", "batch4"])
+def test_forward_stack_matches_oracle(per_token):
+    """The whole stack from one library call per token (or per batch)."""
+    layers, h0, (ref_h, _, _, _) = _case()
+    devs = []
+    for l, lay in enumerate(layers):
+        log(f"[gpu] forward_stack: create layer {l} (seed {SEED0 + l})")
+        w = m.upload_layer(lay)
+        devs.append(m.MoELayer(lay.spec, w, max_tokens=N_TOK))
+        del w
+    h = torch.from_numpy(h0.copy()).cuda()
+    if per_token:
+        for t in range(N_TOK):
+            m.forward_stack(devs, h[t:t + 1])
+    else:
+        m.forward_stack(devs, h)
+    torch.cuda.synchronize()
+    got_h = h.cpu().numpy()
+    for dev in devs:
+        dev.close()
+    err = rel_err(got_h.astype(np.float64) - h0, ref_h.astype(np.float64) - h0)
+    log(f"[gpu] forward_stack of {N_LAYERS} ({'decode b=1' if per_token else 'batch of 4'}): "
         f"rel err of the accumulated block outputs {err:.3e}")
     assert err <= REL_TOL
     assert np.all(np.isfinite(got_h))
