@@ -80,6 +80,21 @@ template <class T>
 __device__ __forceinline__ T ld_at(const void *base, uint32_t off) {
     return *reinterpret_cast<const T *>(reinterpret_cast<const uint8_t *>(base) + off);
 }
+// Weights are read once per call: non-temporal loads (common.h).
+template <typename T>
+__device__ __forceinline__ T ld_nt(const void *base, uint32_t off);
+template <>
+__device__ __forceinline__ uint4 ld_nt<uint4>(const void *base, uint32_t off) {
+    return ld_nt16(reinterpret_cast<const uint8_t *>(base) + off);
+}
+template <>
+__device__ __forceinline__ uint32_t ld_nt<uint32_t>(const void *base, uint32_t off) {
+    return ld_nt4(reinterpret_cast<const uint8_t *>(base) + off);
+}
+template <>
+__device__ __forceinline__ uint16_t ld_nt<uint16_t>(const void *base, uint32_t off) {
+    return ld_nt2(reinterpret_cast<const uint8_t *>(base) + off);
+}
 
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_THREADS = 64 * DEC_WAVES;
@@ -217,7 +232,7 @@ __device__ __forceinline__ void dec_route_item(const Layer &L, const Work &W, co
     const int base = h * half + wave * per_wave;
     double acc = 0.0;
     for (int i = 4 * lane; i < per_wave; i += 256) {
-        const float4 r = *reinterpret_cast<const float4 *>(L.router + (int64_t)e * E + base + i);
+        const float4 r = ld_nt_f4(L.router + (int64_t)e * E + base + i);
         float4 xv;
         if (XBF16) {
             const uint2 v = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(x) + base + i);
@@ -264,8 +279,8 @@ __device__ __forceinline__ void dec_shgu_load(const Layer &L, const void *__rest
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const uint32_t ch = min(lane + 64 * c, nch - 1);
-        w.wg[c] = ld_at<uint4>(L.sh_gate, 2u * ((uint32_t)f * E + ch * 8u));
-        w.wu[c] = ld_at<uint4>(L.sh_up, 2u * ((uint32_t)f * E + ch * 8u));
+        w.wg[c] = ld_nt<uint4>(L.sh_gate, 2u * ((uint32_t)f * E + ch * 8u));
+        w.wu[c] = ld_nt<uint4>(L.sh_up, 2u * ((uint32_t)f * E + ch * 8u));
         if (XBF16) {
             w.xv[c] = ld_at<uint4>(x, 16u * ch);
         } else {
@@ -508,10 +523,10 @@ __device__ __forceinline__ void dec_rgu_load(const Layer &L, const DecPlan &P, c
         // rows past n_ff (if any) read row n_ff - 1; the computation drops them
         const int f = f0 + r * rpw;
         const uint32_t rb = ((uint32_t)e * F + min(f, F - 1)) * L.nbe;
-        w.qg[r] = ld_at<uint4>(L.iq2_qs[0], rb * 64u + c * 16u);
-        w.qu[r] = ld_at<uint4>(L.iq2_qs[1], rb * 64u + c * 16u);
-        w.dg[r] = ld_at<uint16_t>(L.iq2_d[0], 2u * (rb + (c >> 2)));
-        w.du[r] = ld_at<uint16_t>(L.iq2_d[1], 2u * (rb + (c >> 2)));
+        w.qg[r] = ld_nt<uint4>(L.iq2_qs[0], rb * 64u + c * 16u);
+        w.qu[r] = ld_nt<uint4>(L.iq2_qs[1], rb * 64u + c * 16u);
+        w.dg[r] = ld_nt<uint16_t>(L.iq2_d[0], 2u * (rb + (c >> 2)));
+        w.du[r] = ld_nt<uint16_t>(L.iq2_d[1], 2u * (rb + (c >> 2)));
     }
 }
 
@@ -665,7 +680,7 @@ __device__ __forceinline__ void dec_shdn_item(const Layer &L, const Work &W, flo
 #pragma unroll
         for (int c = 0; c < CPR; ++c) {
             const uint32_t row = min(r0 + rr, E - 1), ch = min(lane + 64 * c, nch - 1);
-            wv[rr][c] = ld_at<uint4>(L.sh_down, 2u * (row * F + ch * 8u));
+            wv[rr][c] = ld_nt<uint4>(L.sh_down, 2u * (row * F + ch * 8u));
         }
     // the shared h vector in LDS (its gate/up items, once all stored)
     if (stage) {
@@ -724,9 +739,9 @@ __device__ __forceinline__ void dec_rdn_load(const Layer &L, const DecPlan &P, c
         // rows past n_embd (if any) read row n_embd - 1; the computation drops them
         const int row = r0 + r * rpw;
         const uint32_t rb = ((uint32_t)e * E + min(row, E - 1)) * L.nbf;
-        w.qs[r] = ld_at<uint4>(L.q2k_qs, rb * 64u + c * 16u);
-        w.sc[r] = ld_at<uint32_t>(L.q2k_sc, rb * 16u + c * 4u);
-        w.dd[r] = ld_at<uint32_t>(L.q2k_dd, 4u * (rb + (c >> 2)));
+        w.qs[r] = ld_nt<uint4>(L.q2k_qs, rb * 64u + c * 16u);
+        w.sc[r] = ld_nt<uint32_t>(L.q2k_sc, rb * 16u + c * 4u);
+        w.dd[r] = ld_nt<uint32_t>(L.q2k_dd, 4u * (rb + (c >> 2)));
     }
 }
 

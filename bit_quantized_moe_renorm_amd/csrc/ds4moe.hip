@@ -159,7 +159,7 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     size_t o_xhi = carve(xf32 ? T * E * 2 : 0), o_xlo = carve(xf32 ? T * E * 2 : 0);
     size_t o_shh = carve(d->n_shared ? T * F * 2 : 0), o_shl = carve(d->n_shared ? T * F * 2 : 0);
     size_t o_chunks = carve((size_t)gemm_max_chunks((int)T, (int)NE, (int)k) * 16), o_nch = carve(4);
-    size_t o_ecnt = carve(MAX_EXPERT * 4), o_rest = carve(4 * T * NE * 4), o_rtag = carve((size_t)RT_COPIES * 4 * MAX_EXPERT * 8);
+    size_t o_ecnt = carve(MAX_EXPERT * 4), o_rest = carve(4 * T * NE * 4), o_rtag = carve(4 * MAX_EXPERT * 8);
     size_t o_htag = carve((size_t)(k + 1) * F * 8);
     char *ws = (char *)A(off);
     if (err != hipSuccess) {

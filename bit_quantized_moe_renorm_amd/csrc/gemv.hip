@@ -125,10 +125,10 @@ __global__ __launch_bounds__(512) void k_gemv_gateup_routed(Layer L, Work W, con
         const int f = f0 + r * rpw;
         if (f < F) {
             const int64_t rb = ((int64_t)e * F + f) * L.nbe;
-            qg[r] = *reinterpret_cast<const uint4 *>(L.iq2_qs[0] + rb * 64 + c * 16);
-            qu[r] = *reinterpret_cast<const uint4 *>(L.iq2_qs[1] + rb * 64 + c * 16);
-            dg[r] = half_to_f32(L.iq2_d[0][rb + (c >> 2)]);
-            du[r] = half_to_f32(L.iq2_d[1][rb + (c >> 2)]);
+            qg[r] = ld_nt16(L.iq2_qs[0] + rb * 64 + c * 16);
+            qu[r] = ld_nt16(L.iq2_qs[1] + rb * 64 + c * 16);
+            dg[r] = half_to_f32(ld_nt2(L.iq2_d[0] + rb + (c >> 2)));
+            du[r] = half_to_f32(ld_nt2(L.iq2_d[1] + rb + (c >> 2)));
         } else {
             qg[r] = qu[r] = make_uint4(0, 0, 0, 0);
             dg[r] = du[r] = 0.0f;
@@ -183,8 +183,8 @@ __global__ __launch_bounds__(256) void k_gemv_gateup_shared(Layer L, Work W, con
             const int ch = lane + 64 * it;
             const int f = f0 + r;
             if (ch < nch && f < F) {
-                wg[r][it] = *reinterpret_cast<const uint4 *>(L.sh_gate + (int64_t)f * E + ch * 8);
-                wu[r][it] = *reinterpret_cast<const uint4 *>(L.sh_up + (int64_t)f * E + ch * 8);
+                wg[r][it] = ld_nt16(L.sh_gate + (int64_t)f * E + ch * 8);
+                wu[r][it] = ld_nt16(L.sh_up + (int64_t)f * E + ch * 8);
             } else {
                 wg[r][it] = wu[r][it] = make_uint4(0, 0, 0, 0);
             }
@@ -285,9 +285,9 @@ __global__ __launch_bounds__(256) void k_gemv_down_routed(Layer L, Work W, float
         const int row = r0 + r * rpw;
         if (row < E) {
             const int64_t rb = ((int64_t)e * E + row) * L.nbf;
-            qs[r] = *reinterpret_cast<const uint4 *>(L.q2k_qs + rb * 64 + c * 16);
-            sc[r] = *reinterpret_cast<const uint32_t *>(L.q2k_sc + rb * 16 + c * 4);
-            dd[r] = L.q2k_dd[rb + (c >> 2)];
+            qs[r] = ld_nt16(L.q2k_qs + rb * 64 + c * 16);
+            sc[r] = ld_nt4(L.q2k_sc + rb * 16 + c * 4);
+            dd[r] = ld_nt4(L.q2k_dd + rb + (c >> 2));
         } else {
             qs[r] = make_uint4(0, 0, 0, 0);
             sc[r] = dd[r] = 0u;
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(256) void k_gemv_down_shared(Layer L, Work W, int n
             const int ch = lane + 64 * it;
             const int row = r0 + r;
             wd[r][it] = (ch < nch && row < E)
-                            ? *reinterpret_cast<const uint4 *>(L.sh_down + (int64_t)row * F + ch * 8)
+                            ? ld_nt16(L.sh_down + (int64_t)row * F + ch * 8)
                             : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
