@@ -202,8 +202,11 @@ def test_forward_gemv_rejects_large_batches():
 
 
 # ------------------------------------------------------------------ RMSNorm
-def test_rmsnorm_matches_oracle():
-    h = (synth.residual(7, 33, 4096) * 3).astype(np.float32)
+@pytest.mark.parametrize("n_tok,n_embd", [(33, 4096), (1, 4096), (3, 3072), (5, 1000), (2, 256)])
+def test_rmsnorm_matches_oracle(n_tok, n_embd):
+    """Bit-exact against the oracle: rows of 1024 k floats take the vector
+    kernel, the others the strided one."""
+    h = (synth.residual(7, n_tok, n_embd) * 3).astype(np.float32)
     got = m.rmsnorm(torch.from_numpy(h).cuda()).cpu().view(torch.int16).numpy().view(np.uint16)
     ref, _ = oracle.rmsnorm(h, 1e-6)
     assert np.array_equal(got, ref)
