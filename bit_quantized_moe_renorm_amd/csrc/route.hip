@@ -352,45 +352,62 @@ __global__ __launch_bounds__(256) void k_route_approx(const uint16_t *__restrict
     const uint16_t *wp[3];
 #pragma unroll
     for (int p = 0; p < 3; ++p) wp[p] = hml + ((int64_t)p * NE + (eok ? e : 0)) * E + kb + 8 * grp;
+    // every load is unconditional: tokens past n_tok read token 0 and experts
+    // past NE read expert 0 (in bounds); their products land in accumulator
+    // rows and columns that are never stored
     const uint16_t *xp[4];
-    bool tok[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int t = t0 + 16 * i + rl;
-        tok[i] = t < n_tok;
-        xp[i] = x + (int64_t)(tok[i] ? t : 0) * E + kb + 8 * grp;
+        xp[i] = x + (int64_t)(t < n_tok ? t : 0) * E + kb + 8 * grp;
     }
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
     double acc[4][4] = {};
-    for (int k0 = 0; k0 < kq; k0 += QK) {
-        rt_floatx4 part[4];
+    // 32-K steps, two per stage; the next stage's loads are in flight while
+    // this one's MFMAs run (named buffers alternate, no copies).  The fp32
+    // MFMA sums go into the fp64 accumulators every 256 K.
+    struct Stage {
+        uint4 a[2][4], b[2][3];
+    };
+    auto load = [&](int st, Stage &g) __attribute__((always_inline)) {
+        const int s0 = min(st, kq / 64 - 1) * 64;  // past the end: the last stage again, unused
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part[i] = rt_floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 2; ++s) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint4 a[4][4], b[4][3];
+            for (int i = 0; i < 4; ++i) g.a[s][i] = *reinterpret_cast<const uint4 *>(xp[i] + s0 + 32 * s);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int kk = k0 + 128 * h + 32 * s;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) a[s][i] = tok[i] ? *reinterpret_cast<const uint4 *>(xp[i] + kk) : z4;
-#pragma unroll
-                for (int p = 0; p < 3; ++p) b[s][p] = eok ? *reinterpret_cast<const uint4 *>(wp[p] + kk) : z4;
-            }
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int p = 0; p < 3; ++p)
-                        part[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(rt_bf16x8, a[s][i]),
-                                                                          __builtin_bit_cast(rt_bf16x8, b[s][p]),
-                                                                          part[i], 0, 0, 0);
+            for (int p = 0; p < 3; ++p) g.b[s][p] = *reinterpret_cast<const uint4 *>(wp[p] + s0 + 32 * s);
         }
+    };
+    rt_floatx4 part[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) part[i] = rt_floatx4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int st, const Stage &g) __attribute__((always_inline)) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[i][v] += (double)part[i][v];
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    part[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(rt_bf16x8, g.a[s][i]),
+                                                                      __builtin_bit_cast(rt_bf16x8, g.b[s][p]),
+                                                                      part[i], 0, 0, 0);
+        if ((st & 3) == 3) {  // 256 K done
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[i][v] += (double)part[i][v];
+                part[i] = rt_floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    };
+    const int nst = kq / 64;  // a multiple of 4: the launch requires n_embd % 1024 == 0
+    Stage g0, g1;
+    load(0, g0);
+    for (int st = 0; st < nst; st += 2) {
+        load(st + 1, g1);
+        compute(st, g0);
+        load(st + 2, g0);
+        compute(st + 1, g1);
     }
     // C layout: lane (rl, grp) holds tokens 4 grp + v of each tile for expert rl
     float *eq = est + (int64_t)blockIdx.z * n_tok * NE;
@@ -415,17 +432,21 @@ __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ 
     const int nm = E / 256;
     float xv[RS_MAXV];
     double ss = 0.0;
+    // loads are unconditional (chunks past n_embd re-read the last one and
+    // are zeroed), so they are all in flight at once
+    uint2 xr[RS_MAXV / 4];
+#pragma unroll
+    for (int m = 0; m < RS_MAXV / 4; ++m)
+        xr[m] = *reinterpret_cast<const uint2 *>(x + (int64_t)t * E + 256 * min(m, nm - 1) + 4 * lane);
 #pragma unroll
     for (int m = 0; m < RS_MAXV / 4; ++m) {
-        if (m < nm) {
-            const uint2 r = *reinterpret_cast<const uint2 *>(x + (int64_t)t * E + 256 * m + 4 * lane);
-            xv[4 * m + 0] = bf16_to_f32((uint16_t)(r.x & 0xFFFF));
-            xv[4 * m + 1] = bf16_to_f32((uint16_t)(r.x >> 16));
-            xv[4 * m + 2] = bf16_to_f32((uint16_t)(r.y & 0xFFFF));
-            xv[4 * m + 3] = bf16_to_f32((uint16_t)(r.y >> 16));
+        const bool in = m < nm;
+        xv[4 * m + 0] = in ? bf16_to_f32((uint16_t)(xr[m].x & 0xFFFF)) : 0.0f;
+        xv[4 * m + 1] = in ? bf16_to_f32((uint16_t)(xr[m].x >> 16)) : 0.0f;
+        xv[4 * m + 2] = in ? bf16_to_f32((uint16_t)(xr[m].y & 0xFFFF)) : 0.0f;
+        xv[4 * m + 3] = in ? bf16_to_f32((uint16_t)(xr[m].y >> 16)) : 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ss = fma((double)xv[4 * m + j], (double)xv[4 * m + j], ss);
-        }
+        for (int j = 0; j < 4; ++j) ss = fma((double)xv[4 * m + j], (double)xv[4 * m + j], ss);
     }
     const double xn = sqrt(wave_sum(ss)) * (1.0 + 1e-12);
     // bounds of every expert (lane l: experts l + 64 i)
@@ -468,61 +489,51 @@ __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ 
         }
     }
     const double cut = theta - (fabs(theta) * 0x1p-20 + 1e-30);
-    // exact logits of the candidates, up to 8 dot products at a time
+    // candidates (upper bound at or above the cut), in ascending expert order,
+    // into this wave's LDS list (a wave's LDS accesses complete in order)
+    __shared__ int clist[4][MAX_EXPERT];
+    int *cl = clist[threadIdx.x >> 6];
+    int ncand = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool in = ub[i] >= cut;
+        const uint64_t cm = __ballot(in);
+        if (in) cl[ncand + __popcll(cm & ((1ull << lane) - 1ull))] = lane + 64 * i;
+        ncand += __popcll(cm);
+    }
+    // exact logits of the candidates, one row at a time: its 16-byte chunks
+    // are all in flight at once (chunks past n_embd re-read the last one,
+    // where xv is zero)
     uint64_t key[4];
     float Lv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) key[i] = 0ull, Lv[i] = 0.f;
-    int cand[8];
-    int nc = 0;
-    auto flush = [&]() {
-        double sacc[8];
+    for (int c = 0; c < ncand; ++c) {
+        const int e = cl[c];
+        const float *rp = R + (int64_t)e * E + 4 * lane;
+        float4 r[RS_MAXV / 4];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) sacc[c] = 0.0;
+        for (int m = 0; m < RS_MAXV / 4; ++m) r[m] = *reinterpret_cast<const float4 *>(rp + 256 * min(m, nm - 1));
+        double s0 = 0.0, s1 = 0.0;
 #pragma unroll
-        for (int m = 0; m < RS_MAXV / 4; ++m) {
-            if (m < nm) {
+        for (int m = 0; m < RS_MAXV / 4; m += 2) {
+            s0 = fma((double)xv[4 * m + 0], (double)r[m].x, s0);
+            s0 = fma((double)xv[4 * m + 1], (double)r[m].y, s0);
+            s0 = fma((double)xv[4 * m + 2], (double)r[m].z, s0);
+            s0 = fma((double)xv[4 * m + 3], (double)r[m].w, s0);
+            s1 = fma((double)xv[4 * m + 4], (double)r[m + 1].x, s1);
+            s1 = fma((double)xv[4 * m + 5], (double)r[m + 1].y, s1);
+            s1 = fma((double)xv[4 * m + 6], (double)r[m + 1].z, s1);
+            s1 = fma((double)xv[4 * m + 7], (double)r[m + 1].w, s1);
+        }
+        const double sv = wave_sum(s0 + s1);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    if (c < nc) {
-                        const float4 r = *reinterpret_cast<const float4 *>(R + (int64_t)cand[c] * E + 256 * m + 4 * lane);
-                        sacc[c] = fma((double)xv[4 * m + 0], (double)r.x, sacc[c]);
-                        sacc[c] = fma((double)xv[4 * m + 1], (double)r.y, sacc[c]);
-                        sacc[c] = fma((double)xv[4 * m + 2], (double)r.z, sacc[c]);
-                        sacc[c] = fma((double)xv[4 * m + 3], (double)r.w, sacc[c]);
-                    }
-                }
+        for (int i = 0; i < 4; ++i)
+            if (lane + 64 * i == e) {
+                Lv[i] = (float)(sv + bb[i]);
+                key[i] = topk_key(Lv[i], e);
             }
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            if (c < nc) {
-                const double sv = wave_sum(sacc[c]);
-                const int e = cand[c];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (lane + 64 * i == e) {
-                        Lv[i] = (float)(sv + bb[i]);
-                        key[i] = topk_key(Lv[i], e);
-                    }
-            }
-        }
-        nc = 0;
-    };
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint64_t cm = __ballot(ub[i] >= cut);
-        while (cm) {
-            const int l = __ffsll((unsigned long long)cm) - 1;
-            cm &= cm - 1;
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                if (c == nc) cand[c] = l + 64 * i;
-            ++nc;
-            if (nc == 8) flush();
-        }
     }
-    if (nc > 0) flush();
     // top-k among the candidates, renormalised weights
     float sel_L[MAX_TOPK];
     int sel_e[MAX_TOPK];
