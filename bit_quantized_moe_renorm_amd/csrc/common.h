@@ -63,6 +63,8 @@ struct Work {
     unsigned long long *rtag;  // [MAX_EXPERT][2][2] fused decode: each fp64 half-row router
                                // sum as two 32-bit halves, each tagged with the call's epoch in its
                                // upper 32 bits
+    unsigned long long *ltag;  // [64][MAX_EXPERT] small-batch router: fp32 logit bits under the call's tag
+    unsigned long long *itag;  // [64][MAX_TOPK] small-batch router: selected expert under the call's tag
     unsigned long long *htag;  // [k+1][F] fused decode: SwiGLU outputs of the routed slots and the
                                // shared expert (fp32 bits), each tagged like rtag
 };
@@ -119,8 +121,10 @@ hipError_t launch_dequant_iq2(const Layer &L, int which, int expert, float *dst,
 hipError_t launch_dequant_q2k(const Layer &L, int expert, float *dst, hipStream_t s);
 
 hipError_t launch_router_prep(const float *router, int NE, int E, uint16_t *hml, float *norm, hipStream_t s);
+// ep: this handle's count of routing launches so far (the small-batch router's
+// hand-off tag is ep + 1, never 0)
 hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s,
-                        hipEvent_t *ev /* nullable: [2] around the route kernels */);
+                        unsigned long long ep);
 hipError_t launch_route_export(const Layer &L, const Work &W, int n_tok, int32_t *idx, float *w,
                                int32_t *offsets, int32_t *tokens, hipStream_t s);
 

@@ -46,6 +46,7 @@ struct ds4moe {
     int path = DS4MOE_PATH_AUTO;
     int decode_grid = 0;    // workgroups of the persistent decode kernel
     unsigned long long decode_calls = 0;  // fused launches so far (the phase counters' epoch)
+    unsigned long long route_calls = 0;   // routing launches so far (the router hand-off tag)
     bool poisoned = false;
     int device = 0;
     std::vector<void *> allocs;
@@ -161,6 +162,7 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     size_t o_chunks = carve((size_t)gemm_max_chunks((int)T, (int)NE, (int)k) * 16), o_nch = carve(4);
     size_t o_ecnt = carve(MAX_EXPERT * 4), o_rest = carve(4 * T * NE * 4), o_rtag = carve(4 * MAX_EXPERT * 8);
     size_t o_htag = carve((size_t)(k + 1) * F * 8);
+    size_t o_ltag = carve(64 * MAX_EXPERT * 8), o_itag = carve(64 * MAX_TOPK * 8);
     char *ws = (char *)A(off);
     if (err != hipSuccess) {
         delete h;
@@ -188,6 +190,8 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     W.rest = (float *)(ws + o_rest);
     W.rtag = (unsigned long long *)(ws + o_rtag);
     W.htag = (unsigned long long *)(ws + o_htag);
+    W.ltag = (unsigned long long *)(ws + o_ltag);
+    W.itag = (unsigned long long *)(ws + o_itag);
 
 #define CK(call)                                                                                      \
     do {                                                                                              \
@@ -258,7 +262,7 @@ int ds4moe_route(ds4moe_t *h, const void *x, int32_t n_tok, int32_t *topk_idx, f
     if (n_tok == 0) return DS4MOE_OK;
     hipStream_t s = (hipStream_t)stream;
     int tb = h->tbegin(TK_ROUTE, s);
-    rc = check_launch(h, launch_route(h->L, h->W, x, n_tok, s, nullptr), "route");
+    rc = check_launch(h, launch_route(h->L, h->W, x, n_tok, s, h->route_calls++), "route");
     h->tend(tb, s);
     if (rc) return rc;
     return check_launch(h, launch_route_export(h->L, h->W, n_tok, topk_idx, topk_w, expert_offsets, expert_tokens, s),
@@ -287,7 +291,7 @@ int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *
         return rc;
     }
     int tb = h->tbegin(TK_ROUTE, s);
-    rc = check_launch(h, launch_route(h->L, h->W, x, n_tok, s, nullptr), "route");
+    rc = check_launch(h, launch_route(h->L, h->W, x, n_tok, s, h->route_calls++), "route");
     h->tend(tb, s);
     if (rc) return rc;
     if (path == DS4MOE_PATH_GEMV) {

@@ -13,7 +13,7 @@
 
 namespace ds4 {
 
-constexpr int RT_WAVES = 4;         // experts per workgroup (one per wave)
+constexpr int RT_WAVES = 4;         // waves per router workgroup (one K quarter each)
 constexpr int RT_TOK = 16;          // tokens per workgroup
 constexpr int ROUTE_SMALL_MAX = 64; // fused top-k/bucketing in the last workgroup up to this n_tok
 
@@ -38,6 +38,12 @@ __device__ __forceinline__ uint64_t topk_key(float L, int e) {
     return ((uint64_t)u << 32) | (uint32_t)(0xFFFF - e);
 }
 
+// The logit a key was made from.
+__device__ __forceinline__ float key_logit(uint64_t key) {
+    const uint32_t u = (uint32_t)(key >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -45,6 +51,75 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
         v = o > v ? o : v;
     }
     return v;
+}
+
+// Small-batch hand-offs between workgroups use 64-bit words: 32 data bits
+// under the call's 32-bit tag (never 0, the workspace's initial value),
+// stored and polled at agent scope.  A word is seen whole or not at all, so a
+// consumer that finds the tag has the value: no fences (which would write
+// back and invalidate the L2) and nothing to reset.
+constexpr int RT_SPIN = 1 << 20;  // polls of one word before giving up (about a second)
+__device__ __forceinline__ unsigned long long rt_poll(const unsigned long long *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void rt_put(unsigned long long *p, uint32_t tag, uint32_t v) {
+    __hip_atomic_store(p, ((unsigned long long)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until word p carries the tag (bounded); false if the wait expired.
+__device__ __forceinline__ bool rt_wait(const unsigned long long *p, uint32_t tag, unsigned long long &v) {
+    for (int spins = 0; (uint32_t)(v >> 32) != tag; ++spins) {
+        if (spins > RT_SPIN) return false;
+        __builtin_amdgcn_s_sleep(2);
+        v = rt_poll(p);
+    }
+    return true;
+}
+
+// Top-k + renormalised weights for token t, by one wavefront, from the tagged
+// logits of this call; the selection also goes to the tagged itag words.  An
+// expired wait poisons the token's weights with NaN.
+__device__ void topk_tagged(const unsigned long long *__restrict__ ltag, int t, int NE, int k, uint32_t tag,
+                            int32_t *__restrict__ idx, float *__restrict__ w, unsigned long long *__restrict__ itag) {
+    const int lane = threadIdx.x & 63;
+    unsigned long long v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = rt_poll(ltag + (int64_t)t * MAX_EXPERT + min(lane + 64 * i, NE - 1));
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ok &= rt_wait(ltag + (int64_t)t * MAX_EXPERT + min(lane + 64 * i, NE - 1), tag, v[i]);
+    uint64_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = (e < NE) ? topk_key(__uint_as_float((uint32_t)v[i]), e) : 0ull;
+    }
+    const bool bad = __ballot(!ok) != 0ull;
+    float sel_L[MAX_TOPK];
+    int sel_e[MAX_TOPK];
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max_u64(best);
+        int e = 0xFFFF - (int)(best & 0xFFFFu);
+        sel_e[j] = e;
+        sel_L[j] = key_logit(best);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (lane + 64 * i == e) key[i] = 0ull;
+    }
+    if (lane < k) {
+        double m = (double)sel_L[0], z = 0.0, num = 0.0;
+        int e = 0;
+        for (int j = 0; j < k; ++j) {
+            const double ex = exp((double)sel_L[j] - m);
+            z += ex;
+            if (j == lane) num = ex, e = sel_e[j];
+        }
+        idx[(int64_t)t * k + lane] = e;
+        w[(int64_t)t * k + lane] = bad ? __builtin_nanf("") : (float)(num / z);
+        rt_put(itag + (int64_t)t * MAX_TOPK + lane, tag, (uint32_t)e);
+    }
 }
 
 // Top-k + renormalised weights for token t, by one wavefront.
@@ -66,7 +141,7 @@ __device__ void topk_token(const float *__restrict__ logits, int t, int NE, int 
         best = wave_max_u64(best);
         int e = 0xFFFF - (int)(best & 0xFFFFu);
         sel_e[j] = e;
-        sel_L[j] = logits[(int64_t)t * NE + e];
+        sel_L[j] = key_logit(best);  // no reload: the key holds the logit
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (lane + 64 * i == e) key[i] = 0ull;
@@ -87,93 +162,142 @@ __device__ void topk_token(const float *__restrict__ logits, int t, int NE, int 
     }
 }
 
-// Per-expert lists for small n_tok by one workgroup: counts, offsets, active
-// experts, and the list entries t*k+j in ascending t within each expert.
-__device__ void bucket_small(const int32_t *__restrict__ idx, int n_tok, int k, int NE, const Work &W) {
-    __shared__ int cnt[MAX_EXPERT + 1];
-    __shared__ int act[MAX_EXPERT + 1];
-    const int tid = threadIdx.x;
+// Per-expert lists for small n_tok by one workgroup of 256 threads: counts,
+// offsets, active experts, and the list entries t*k+j in ascending t within
+// each expert.  The tagged selections are read into LDS once; every scan
+// after that is over LDS.
+constexpr int BS_MAXQ = ROUTE_SMALL_MAX * MAX_TOPK;
+__device__ void bucket_small(const unsigned long long *__restrict__ itag, uint32_t tag, int n_tok, int k, int NE,
+                             const Work &W) {
+    __shared__ int sidx[BS_MAXQ];
+    __shared__ int cnt[MAX_EXPERT];
+    __shared__ int wtot[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nq = n_tok * k;
-    for (int e = tid; e < NE; e += blockDim.x) cnt[e] = 0;
-    __syncthreads();
-    for (int q = tid; q < nq; q += blockDim.x) atomicAdd(&cnt[idx[q]], 1);
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0, u = 0;
-        for (int e = 0; e < NE; ++e) {
-            int c = cnt[e];
-            cnt[e] = run;
-            W.offsets[e] = run;
-            if (c) act[u++] = e;
-            run += c;
-        }
-        W.offsets[NE] = run;
-        W.active[0] = u;
-        for (int i = 0; i < u; ++i) W.active[1 + i] = act[i];
+    for (int q = tid; q < nq; q += 256) {
+        const unsigned long long *p = itag + (int64_t)(q / k) * MAX_TOPK + q % k;
+        unsigned long long v = rt_poll(p);
+        sidx[q] = rt_wait(p, tag, v) ? (int)(uint32_t)v : 0;  // an expired wait already poisoned the weights
     }
+    cnt[tid] = 0;
     __syncthreads();
-    for (int e = tid; e < NE; e += blockDim.x) {
-        int pos = cnt[e];
+    for (int q = tid; q < nq; q += 256) atomicAdd(&cnt[sidx[q]], 1);
+    __syncthreads();
+    // exclusive scan over the experts (thread e holds expert e) and the
+    // compaction of the active ones, by wave scans
+    const int c = tid < NE ? cnt[tid] : 0;
+    int v = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    const uint64_t am = __ballot(c > 0);
+    if (lane == 63) wtot[wave] = v;
+    __shared__ int wact[4];
+    if (lane == 0) wact[wave] = __popcll(am);
+    __syncthreads();
+    int pre = 0, apre = 0;
+    for (int w = 0; w < wave; ++w) pre += wtot[w], apre += wact[w];
+    const int start = pre + v - c;
+    if (tid < NE) {
+        W.offsets[tid] = start;
+        if (c > 0) W.active[1 + apre + __popcll(am & ((1ull << lane) - 1ull))] = tid;
+    }
+    if (tid == 255) {
+        W.offsets[NE] = pre + v;
+        W.active[0] = apre + __popcll(am);
+    }
+    // list entries of expert tid, ascending
+    if (tid < NE && c > 0) {
+        int pos = start;
         for (int q = 0; q < nq; ++q)
-            if (idx[q] == e) W.list[pos++] = q;
+            if (sidx[q] == tid) W.list[pos++] = q;
     }
 }
 
-// Logits for RT_WAVES experts x RT_TOK tokens per workgroup, fp64 accumulation.
-// With fuse_tail, the last workgroup to finish also does top-k and bucketing.
+// Logits of one expert (blockIdx.x) for RT_TOK tokens per workgroup, fp64
+// accumulation.  Wave w covers K quarter w; lane l holds 4 values at
+// 4 l + 256 j of it (j < 4: n_embd <= 4096).  All of a wave's loads are in
+// flight together (unconditional: tokens past the tile's end re-read its last
+// token, chunks past the quarter re-read its first; neither is summed), and
+// the quarters are added in order by wave 0.
+// With fuse_tail, the last workgroup of each token tile takes the tile's top-k,
+// and the last of those builds the per-expert lists.
+constexpr int RT_KCH = 4;  // 256-value chunks per wave at most
 template <bool XBF16>
 __global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ R, const float *__restrict__ bias,
                                                       const void *__restrict__ x, int n_tok, int NE, int E,
-                                                      int k, Work W, int fuse_tail) {
+                                                      int k, Work W, int fuse_tail, uint32_t tag) {
+    __shared__ double part[RT_WAVES][RT_TOK];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e = blockIdx.x * RT_WAVES + wave;
+    const int e = blockIdx.x;
     const int t0 = blockIdx.y * RT_TOK;
     const int nt = min(RT_TOK, n_tok - t0);
-    if (e < NE) {
+    const int kq = E / RT_WAVES, kb = wave * kq;
+    {
         double acc[RT_TOK];
 #pragma unroll
         for (int t = 0; t < RT_TOK; ++t) acc[t] = 0.0;
-        for (int i = 4 * lane; i < E; i += 256) {
-            float4 r = *reinterpret_cast<const float4 *>(R + (int64_t)e * E + i);
+        float4 r[RT_KCH];
+        double xv[RT_KCH][RT_TOK][4];
 #pragma unroll
-            for (int t = 0; t < RT_TOK; ++t) {
-                if (t < nt) {
-                    double xv[4];
-                    load_x4<XBF16>(x, (int64_t)(t0 + t) * E + i, xv);
-                    acc[t] = fma(xv[0], (double)r.x, acc[t]);
-                    acc[t] = fma(xv[1], (double)r.y, acc[t]);
-                    acc[t] = fma(xv[2], (double)r.z, acc[t]);
-                    acc[t] = fma(xv[3], (double)r.w, acc[t]);
+        for (int j = 0; j < RT_KCH; ++j) {
+            const int off = 4 * lane + 256 * j;
+            const int i = kb + (off < kq ? off : 0);
+            r[j] = *reinterpret_cast<const float4 *>(R + (int64_t)e * E + i);
+#pragma unroll
+            for (int t = 0; t < RT_TOK; ++t) load_x4<XBF16>(x, (int64_t)(t0 + min(t, nt - 1)) * E + i, xv[j][t]);
+        }
+#pragma unroll
+        for (int j = 0; j < RT_KCH; ++j) {
+            if (4 * lane + 256 * j < kq) {
+#pragma unroll
+                for (int t = 0; t < RT_TOK; ++t) {
+                    acc[t] = fma(xv[j][t][0], (double)r[j].x, acc[t]);
+                    acc[t] = fma(xv[j][t][1], (double)r[j].y, acc[t]);
+                    acc[t] = fma(xv[j][t][2], (double)r[j].z, acc[t]);
+                    acc[t] = fma(xv[j][t][3], (double)r[j].w, acc[t]);
                 }
             }
         }
-        const double b = bias ? (double)bias[e] : 0.0;
 #pragma unroll
         for (int t = 0; t < RT_TOK; ++t) {
-            if (t < nt) {
-                double s = wave_sum(acc[t]);
-                if (lane == 0) W.logits[(int64_t)(t0 + t) * NE + e] = (float)(s + b);
-            }
+            const double s = wave_sum(acc[t]);
+            if (lane == 0) part[wave][t] = s;
         }
     }
+    __syncthreads();
+    if (wave == 0 && lane < nt) {
+        const double b = bias ? (double)bias[e] : 0.0;
+        double s = part[0][lane];
+#pragma unroll
+        for (int w = 1; w < RT_WAVES; ++w) s += part[w][lane];
+        const float L = (float)(s + b);
+        if (fuse_tail)
+            rt_put(W.ltag + (int64_t)(t0 + lane) * MAX_EXPERT + e, tag, __float_as_uint(L));
+        else
+            W.logits[(int64_t)(t0 + lane) * NE + e] = L;
+    }
     if (!fuse_tail) return;
-    // last-workgroup epilogue: release our logits, take a ticket
+    // tickets (slot 0 of the counters: word 0 for the lists, word 1 + y for
+    // token tile y; each last taker resets its word).  A ticket needs no
+    // fence: the tail polls the tagged words, whose stores were all issued
+    // before the ticket was taken, so every wait ends.
     __shared__ int last;
-    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) last = atomicAdd(&W.counters[1 + blockIdx.y], 1) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!last) return;
+    for (int t = t0 + wave; t < t0 + nt; t += RT_WAVES) topk_tagged(W.ltag, t, NE, k, tag, W.idx, W.w, W.itag);
     __syncthreads();
     if (threadIdx.x == 0) {
-        int total = gridDim.x * gridDim.y;
-        int ticket = atomicAdd(&W.counters[0], 1);
-        last = (ticket == total - 1);
+        W.counters[1 + blockIdx.y] = 0;
+        last = atomicAdd(&W.counters[0], 1) == (int)gridDim.y - 1;
     }
     __syncthreads();
     if (!last) return;
-    __threadfence();
-    const int nw = blockDim.x >> 6;
-    for (int t = wave; t < n_tok; t += nw) topk_token(W.logits, t, NE, k, W.idx, W.w);
-    __threadfence();
-    __syncthreads();
-    bucket_small(W.idx, n_tok, k, NE, W);
+    bucket_small(W.itag, tag, n_tok, k, NE, W);
     if (threadIdx.x == 0) W.counters[0] = 0;
 }
 
@@ -605,7 +729,9 @@ __global__ __launch_bounds__(256) void k_fill_lists(int n_tok, int NE, int k, Wo
     }
 }
 
-hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s, hipEvent_t *ev) {
+hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s,
+                        unsigned long long ep) {
+    const uint32_t tag = (uint32_t)(ep % 0xFFFFFFFFull) + 1u;
     const int NE = L.n_expert;
     if (n_tok > ROUTE_SMALL_MAX && L.act_dtype == 1 && L.n_embd % (4 * QK) == 0) {
         // batched: MFMA estimates, exact candidates, lists
@@ -617,14 +743,14 @@ hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok,
         hipLaunchKernelGGL(k_fill_lists, dim3(NE), dim3(256), 0, s, n_tok, NE, L.top_k, W);
         return hipGetLastError();
     }
-    dim3 grid((NE + RT_WAVES - 1) / RT_WAVES, (n_tok + RT_TOK - 1) / RT_TOK);
+    dim3 grid(NE, (n_tok + RT_TOK - 1) / RT_TOK);
     const int fuse = n_tok <= ROUTE_SMALL_MAX;
     if (L.act_dtype == 1)
         hipLaunchKernelGGL(k_route_logits<true>, grid, dim3(256), 0, s, L.router, L.router_bias, x, n_tok, NE,
-                           L.n_embd, L.top_k, W, fuse);
+                           L.n_embd, L.top_k, W, fuse, tag);
     else
         hipLaunchKernelGGL(k_route_logits<false>, grid, dim3(256), 0, s, L.router, L.router_bias, x, n_tok, NE,
-                           L.n_embd, L.top_k, W, fuse);
+                           L.n_embd, L.top_k, W, fuse, tag);
     if (!fuse) {
         hipLaunchKernelGGL(k_topk, dim3((n_tok + 3) / 4), dim3(256), 0, s, n_tok, NE, L.top_k, W);
         hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, s, n_tok, NE, L.top_k, W);
