@@ -56,6 +56,7 @@ struct Work {
     uint16_t *x16;        // [max_tokens][E] fp16 copy of x
     uint16_t *xhi, *xlo;  // [max_tokens][E] bf16 high / low parts of fp32 x (fp32 activations only)
     uint16_t *hsh_hi, *hsh_lo;  // [max_tokens][F] shared-expert activations, bf16 high / low parts
+    float *part;          // [PART_ROWS][max(2F, E)] batched GEMMs: partial sums over K splits
     int4 *chunks;         // [gemm_max_chunks] (expert, first list position, count)
     int32_t *nchunks;     // number of valid chunks
     int32_t *ecount;      // [MAX_EXPERT] tokens per expert (batched router)
@@ -142,6 +143,7 @@ enum TimingKind {
 
 bool gemm_enabled();
 int gemm_max_chunks(int n_tok, int NE, int k);   // upper bound of the routed chunk count
+constexpr int PART_ROWS = 2048;  // K splits times rows (tokens or slots) of a split GEMM launch, at most
 hipError_t launch_gemm_prep(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);
 hipError_t launch_gemm_gateup_routed(const Layer &L, const Work &W, int n_tok, hipStream_t s);
 hipError_t launch_gemm_gateup_shared(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);

@@ -159,6 +159,7 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     const bool xf32 = d->act_dtype == DS4MOE_F32;
     size_t o_xhi = carve(xf32 ? T * E * 2 : 0), o_xlo = carve(xf32 ? T * E * 2 : 0);
     size_t o_shh = carve(d->n_shared ? T * F * 2 : 0), o_shl = carve(d->n_shared ? T * F * 2 : 0);
+    size_t o_part = carve((size_t)PART_ROWS * std::max<int64_t>(2 * F, E) * 4);
     size_t o_chunks = carve((size_t)gemm_max_chunks((int)T, (int)NE, (int)k) * 16), o_nch = carve(4);
     size_t o_ecnt = carve(MAX_EXPERT * 4), o_rest = carve(4 * T * NE * 4), o_rtag = carve(4 * MAX_EXPERT * 8);
     size_t o_htag = carve((size_t)(k + 1) * F * 8);
@@ -184,6 +185,7 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     W.xlo = xf32 ? (uint16_t *)(ws + o_xlo) : nullptr;
     W.hsh_hi = d->n_shared ? (uint16_t *)(ws + o_shh) : nullptr;
     W.hsh_lo = d->n_shared ? (uint16_t *)(ws + o_shl) : nullptr;
+    W.part = (float *)(ws + o_part);
     W.chunks = (int4 *)(ws + o_chunks);
     W.nchunks = (int32_t *)(ws + o_nch);
     W.ecount = (int32_t *)(ws + o_ecnt);
@@ -275,7 +277,9 @@ int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *
     if (n_tok > 0 && !out) return fail(DS4MOE_EINVAL, "forward: NULL out");
     if (n_tok == 0) return DS4MOE_OK;
     int path = h->path;
-    if (path == DS4MOE_PATH_AUTO) path = (n_tok <= GEMV_MAX_TOK) ? DS4MOE_PATH_GEMV : DS4MOE_PATH_GEMM;
+    // one token: the fused decode kernel; more: the grouped GEMMs, which at 2-4
+    // tokens (K split over more workgroups) also beat the GEMV kernels
+    if (path == DS4MOE_PATH_AUTO) path = (n_tok == 1) ? DS4MOE_PATH_GEMV : DS4MOE_PATH_GEMM;
     if (path == DS4MOE_PATH_GEMV && n_tok > GEMV_MAX_TOK)
         return fail(DS4MOE_EUNSUPPORTED, "forward: GEMV path takes at most %d tokens (got %d)", GEMV_MAX_TOK, n_tok);
     if (path == DS4MOE_PATH_GEMM && !gemm_available())

@@ -174,8 +174,9 @@ template <int NT>
 __device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &W, const uint4 *T, uint8_t *stg0,
                                                     uint8_t *stg1, const BlockLoader &ld, uint4 (&xr)[LD_V],
                                                     const uint8_t *qg, const uint16_t *dg, int fq, int fd, int f0,
-                                                    int beg, int cnt, int rl, int grp) {
-    const int F = L.n_ff, nbe = L.nbe;
+                                                    int beg, int cnt, int rl, int grp, int nbe, float *part,
+                                                    int nq) {
+    const int F = L.n_ff;
     // gate and up planes sit at a fixed distance from each other
     const int64_t qdu = L.iq2_qs[1] - L.iq2_qs[0], ddu = L.iq2_d[1] - L.iq2_d[0];
     auto wload = [&](int fi, int bi) {
@@ -239,6 +240,24 @@ __device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &
         __syncthreads();
     }
 
+    if (part) {
+        // this K range's gate and up sums, slot-major
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int tt = 16 * i + 4 * grp + v;
+                if (tt >= cnt) continue;
+                float *prow = part + ((int64_t)blockIdx.z * nq + W.list[beg + tt]) * (2 * F) + f0 + rl;
+#pragma unroll
+                for (int fp = 0; fp < GU_FR; ++fp) {
+                    prow[16 * fp] = acc[i][fp][v];
+                    prow[F + 16 * fp] = acc[i][fp + GU_FR][v];
+                }
+            }
+        }
+        return;
+    }
     // epilogue: h = silu(gate) * up -> fp16 slot rows
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
@@ -259,7 +278,10 @@ __device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &
 // grid: (n_ff / RGU_ROWS, max chunks), RB_THREADS threads.  Wave w covers
 // n_ff rows f0..f0+16 GU_FR-1 of gate and up for all tokens of the chunk
 // (1..4 token tiles), over the whole n_embd.
-__global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_gateup_routed(Layer L, Work W) {
+// blockIdx.z = K split: 256-K blocks bps z .. bps z + bps - 1.  With part (more
+// than one split) the raw sums go to part[z][slot][2 n_ff] for
+// k_routed_gu_reduce; nq = slots of the call.
+__global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_gateup_routed(Layer L, Work W, int bps, float *part, int nq) {
     const int c = blockIdx.y;
     if (c >= *W.nchunks) return;
     const int4 ch = W.chunks[c];
@@ -268,18 +290,18 @@ __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_gateup_routed(Layer L, W
     __shared__ __align__(16) uint8_t stg[2][RB_STAGE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rl = lane & 15, grp = lane >> 4;
-    const int E = L.n_embd, F = L.n_ff, k = L.top_k, nbe = L.nbe;
+    const int E = L.n_embd, F = L.n_ff, k = L.top_k, nbe = L.nbe, b0 = blockIdx.z * bps;
 
     BlockLoader ld;
     {
         const int sr = tid / LD_PER_ROW;
-        ld.init(W.x16 + (int64_t)(W.list[beg + min(sr, cnt - 1)] / k) * E, tid);
+        ld.init(W.x16 + (int64_t)(W.list[beg + min(sr, cnt - 1)] / k) * E + QK * b0, tid);
     }
     const int f0 = blockIdx.x * RGU_ROWS + wave * 16 * GU_FR;
     // fragment fi: matrix fi / GU_FR (gate, up), rows f0 + 16 (fi % GU_FR) + rl
     const int64_t rb = ((int64_t)e * F + f0 + rl) * nbe;
-    const uint8_t *qg = L.iq2_qs[0] + rb * 64 + 16 * grp;  // + 64 bi (up: + iq2_qs[1] - iq2_qs[0])
-    const uint16_t *dg = L.iq2_d[0] + rb;                  // + bi
+    const uint8_t *qg = L.iq2_qs[0] + (rb + b0) * 64 + 16 * grp;  // + 64 bi (up: + iq2_qs[1] - iq2_qs[0])
+    const uint16_t *dg = L.iq2_d[0] + rb + b0;                    // + bi
     const int fq = 16 * nbe * 64, fd = 16 * nbe;
     uint4 xr[LD_V];
     ld.load(0, xr);
@@ -287,10 +309,10 @@ __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_gateup_routed(Layer L, W
     ld.store(stg[0], xr);
     __syncthreads();
     switch ((cnt + 15) >> 4) {
-        case 1: gateup_routed_tiles<1>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp); break;
-        case 2: gateup_routed_tiles<2>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp); break;
-        case 3: gateup_routed_tiles<3>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp); break;
-        default: gateup_routed_tiles<4>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp); break;
+        case 1: gateup_routed_tiles<1>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
+        case 2: gateup_routed_tiles<2>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
+        case 3: gateup_routed_tiles<3>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
+        default: gateup_routed_tiles<4>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
     }
 }
 
@@ -315,8 +337,8 @@ __device__ __forceinline__ void down_routed_tiles(const Layer &L, const Work &W,
                                                   const uint2 *QT, uint8_t *stg0, uint8_t *stg1, const BlockLoader &ld,
                                                   uint4 (&xr)[LD_V], const uint8_t *qb, const uint8_t *sb,
                                                   const uint32_t *db, int fq, int fs, int fd, bool active, int r0,
-                                                  int beg, int cnt, int rl, int grp) {
-    const int E = L.n_embd, nbf = L.nbf;
+                                                  int beg, int cnt, int rl, int grp, int nbf) {
+    const int E = L.n_embd;
     // loads are unconditional (inactive waves read row 0: in bounds, unused)
     uint4 qcur[DN_NF], qnext[DN_NF];
     uint32_t scur[DN_NF], snext[DN_NF], dcur[DN_NF], dnext[DN_NF];
@@ -412,7 +434,9 @@ __device__ __forceinline__ void down_routed_tiles(const Layer &L, const Work &W,
 // grid: (ceil(n_embd / RDN_ROWS), max chunks), RB_THREADS threads.  Wave w
 // covers n_embd rows r0..r0+16 DN_NF-1 for all tokens of the chunk over the
 // whole n_ff; waves whose rows lie past n_embd only help with the staging.
-__global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_down_routed(Layer L, Work W, float *__restrict__ out) {
+// blockIdx.z = K split (256-K blocks bps z ..): every split adds its share of
+// w y into out with the same atomics.
+__global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_down_routed(Layer L, Work W, float *__restrict__ out, int bps) {
     const int c = blockIdx.y;
     if (c >= *W.nchunks) return;
     const int4 ch = W.chunks[c];
@@ -421,20 +445,20 @@ __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_down_routed(Layer L, Wor
     __shared__ __align__(16) uint8_t stg[2][RB_STAGE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rl = lane & 15, grp = lane >> 4;
-    const int E = L.n_embd, F = L.n_ff, nbf = L.nbf;
+    const int E = L.n_embd, F = L.n_ff, nbf = L.nbf, b0 = blockIdx.z * bps;
 
     BlockLoader ld;
     {
         const int sr = tid / LD_PER_ROW;
-        ld.init(W.hbuf16 + (int64_t)W.list[beg + min(sr, cnt - 1)] * F, tid);
+        ld.init(W.hbuf16 + (int64_t)W.list[beg + min(sr, cnt - 1)] * F + QK * b0, tid);
     }
     const int r0 = blockIdx.x * RDN_ROWS + wave * 16 * DN_NF;
     const bool active = r0 < E;
     // fragment fi = rows r0 + 16 fi + rl; one base per plane, fragments 16 rows apart
     const int64_t rb = ((int64_t)e * E + (active ? r0 + rl : 0)) * nbf;
-    const uint8_t *qb = L.q2k_qs + rb * 64 + 16 * grp;   // + fi * fq + 64 bi
-    const uint8_t *sb = L.q2k_sc + rb * 16 + 4 * grp;    // + fi * fs + 16 bi
-    const uint32_t *db = L.q2k_dd + rb;                  // + fi * fd + bi
+    const uint8_t *qb = L.q2k_qs + (rb + b0) * 64 + 16 * grp;   // + fi * fq + 64 bi
+    const uint8_t *sb = L.q2k_sc + (rb + b0) * 16 + 4 * grp;    // + fi * fs + 16 bi
+    const uint32_t *db = L.q2k_dd + rb + b0;                    // + fi * fd + bi
     const int fq = 16 * nbf * 64, fs = 16 * nbf * 16, fd = 16 * nbf;
     uint4 xr[LD_V];
     ld.load(0, xr);
@@ -442,19 +466,24 @@ __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_down_routed(Layer L, Wor
     ld.store(stg[0], xr);
     __syncthreads();
     switch ((cnt + 15) >> 4) {
-        case 1: down_routed_tiles<1>(L, W, out, QT, stg[0], stg[1], ld, xr, qb, sb, db, fq, fs, fd, active, r0, beg, cnt, rl, grp); break;
-        case 2: down_routed_tiles<2>(L, W, out, QT, stg[0], stg[1], ld, xr, qb, sb, db, fq, fs, fd, active, r0, beg, cnt, rl, grp); break;
-        case 3: down_routed_tiles<3>(L, W, out, QT, stg[0], stg[1], ld, xr, qb, sb, db, fq, fs, fd, active, r0, beg, cnt, rl, grp); break;
-        default: down_routed_tiles<4>(L, W, out, QT, stg[0], stg[1], ld, xr, qb, sb, db, fq, fs, fd, active, r0, beg, cnt, rl, grp); break;
+        case 1: down_routed_tiles<1>(L, W, out, QT, stg[0], stg[1], ld, xr, qb, sb, db, fq, fs, fd, active, r0, beg, cnt, rl, grp, bps); break;
+        case 2: down_routed_tiles<2>(L, W, out, QT, stg[0], stg[1], ld, xr, qb, sb, db, fq, fs, fd, active, r0, beg, cnt, rl, grp, bps); break;
+        case 3: down_routed_tiles<3>(L, W, out, QT, stg[0], stg[1], ld, xr, qb, sb, db, fq, fs, fd, active, r0, beg, cnt, rl, grp, bps); break;
+        default: down_routed_tiles<4>(L, W, out, QT, stg[0], stg[1], ld, xr, qb, sb, db, fq, fs, fd, active, r0, beg, cnt, rl, grp, bps); break;
     }
 }
 
 // ---------------------------------------------------------------- shared expert gate/up
 // grid: (n_ff / GU_ROWS, ceil(n_tok / CH_TOK)).  bf16 weights straight from
 // memory; A = x as bf16 (SPLIT: high and low bf16 parts of fp32 x).
+// blockIdx.z = K split: this workgroup covers K chunks kcs z .. kcs z + kcs - 1
+// (32 values each).  With part, its raw gate and up sums go to
+// part[z][token][2 n_ff] for k_shared_gu_reduce; without (one split), h is
+// stored directly.
 template <bool SPLIT>
 __global__ __launch_bounds__(256, 2) void k_gemm_gateup_shared(Layer L, Work W, const uint16_t *__restrict__ xhi,
-                                                               const uint16_t *__restrict__ xlo, int n_tok) {
+                                                               const uint16_t *__restrict__ xlo, int n_tok, int kcs,
+                                                               float *__restrict__ part) {
     const int t0 = blockIdx.y * CH_TOK;
     const int cnt = min(CH_TOK, n_tok - t0);
     __shared__ __align__(16) uint8_t stg[2][2][STG_BYTES];
@@ -462,17 +491,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gateup_shared(Layer L, Work W, 
     const int rl = lane & 15, grp = lane >> 4;
     const int E = L.n_embd, F = L.n_ff;
     const int nt = (cnt + 15) >> 4;
-    const int nkc = E / 32;
+    const int nkc = kcs, kc0 = blockIdx.z * kcs;
     // unconditional loads from clamped addresses (see the shared down kernel)
     const int sr = tid >> 2;
-    const int64_t xo = (int64_t)(t0 + min(sr, cnt - 1)) * E + 8 * (tid & 3);
+    const int64_t xo = (int64_t)(t0 + min(sr, cnt - 1)) * E + 8 * (tid & 3) + 32 * kc0;
 
     const int f0 = blockIdx.x * GU_ROWS + wave * 32;
     const uint4 *wp[4];
 #pragma unroll
     for (int fi = 0; fi < 4; ++fi) {
         const uint16_t *base = (fi >> 1) ? L.sh_up : L.sh_gate;
-        wp[fi] = reinterpret_cast<const uint4 *>(base + (int64_t)(f0 + 16 * (fi & 1) + rl) * E + 8 * grp);  // kc: wp[fi][4 kc]
+        wp[fi] = reinterpret_cast<const uint4 *>(base + (int64_t)(f0 + 16 * (fi & 1) + rl) * E + 8 * grp) +
+                 4 * kc0;  // kc: wp[fi][4 kc]
     }
     floatx4 acc[4][4];
     const floatx4 zf = {0.f, 0.f, 0.f, 0.f};
@@ -482,7 +512,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gateup_shared(Layer L, Work W, 
         for (int fi = 0; fi < 4; ++fi) acc[i][fi] = zf;
     if constexpr (!SPLIT) {
         // one part of x: the stage's second plane holds the next K chunk, so
-        // each barrier covers two chunks (n_embd / 32 is even)
+        // each barrier covers two chunks (kcs is even)
         uint4 xh[2], wr[2][4];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -581,6 +611,25 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gateup_shared(Layer L, Work W, 
             }
         }
     }
+    if (part) {
+        // this K range's gate and up sums
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i >= nt) continue;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int tt = 16 * i + 4 * grp + v;
+                if (tt >= cnt) continue;
+                float *prow = part + ((int64_t)blockIdx.z * n_tok + t0 + tt) * (2 * F) + f0 + rl;
+#pragma unroll
+                for (int fp = 0; fp < 2; ++fp) {
+                    prow[16 * fp] = acc[i][fp][v];
+                    prow[F + 16 * fp] = acc[i][fp + 2][v];
+                }
+            }
+        }
+        return;
+    }
     // h = silu(gate) * up, stored as bf16 high and low parts
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -604,7 +653,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gateup_shared(Layer L, Work W, 
 // ---------------------------------------------------------------- shared expert down
 // grid: (n_embd / DN_ROWS, ceil(n_tok / CH_TOK)).  A = h (high and low bf16
 // parts), B = bf16 rows of the shared down matrix; out[token][row] += y.
-__global__ __launch_bounds__(256, 2) void k_gemm_down_shared(Layer L, Work W, int n_tok, float *__restrict__ out) {
+// blockIdx.z = K split as in the shared gate/up GEMM; with part, this K
+// range's sums go to part[z][token][n_embd] for k_shared_dn_reduce.
+__global__ __launch_bounds__(256, 2) void k_gemm_down_shared(Layer L, Work W, int n_tok, float *__restrict__ out,
+                                                             int kcs, float *__restrict__ part) {
     const int t0 = blockIdx.y * CH_TOK;
     const int cnt = min(CH_TOK, n_tok - t0);
     __shared__ __align__(16) uint8_t stg[2][2][STG_BYTES];
@@ -612,19 +664,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_shared(Layer L, Work W, in
     const int rl = lane & 15, grp = lane >> 4;
     const int E = L.n_embd, F = L.n_ff;
     const int nt = (cnt + 15) >> 4;
-    const int nkc = F / 32;
+    const int nkc = kcs, kc0 = blockIdx.z * kcs;
     // loads never depend on a condition (a select between a load and a zero
     // vector becomes a flat load from a stack slot, waited on at once): rows
     // past the chunk read the chunk's last row (their results are dropped),
     // and prefetches past the last K chunk re-read it (unused)
     const int sr = tid >> 2;
-    const int64_t ho = (int64_t)(t0 + min(sr, cnt - 1)) * F + 8 * (tid & 3);
+    const int64_t ho = (int64_t)(t0 + min(sr, cnt - 1)) * F + 8 * (tid & 3) + 32 * kc0;
 
     const int r0 = blockIdx.x * DN_ROWS + wave * 64;
     const uint4 *wp[4];
 #pragma unroll
     for (int fi = 0; fi < 4; ++fi)
-        wp[fi] = reinterpret_cast<const uint4 *>(L.sh_down + (int64_t)(r0 + 16 * fi + rl) * F + 8 * grp);
+        wp[fi] = reinterpret_cast<const uint4 *>(L.sh_down + (int64_t)(r0 + 16 * fi + rl) * F + 8 * grp) + 4 * kc0;
     constexpr int SPF = 2;
     uint4 xh[SPF], xl[SPF], wr[SPF][4];
 #pragma unroll
@@ -698,6 +750,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_shared(Layer L, Work W, in
         for (int v = 0; v < 4; ++v) {
             const int tt = 16 * i + 4 * grp + v;
             if (tt >= cnt) continue;
+            if (part) {
+                float *prow = part + ((int64_t)blockIdx.z * n_tok + t0 + tt) * E + r0 + rl;
+#pragma unroll
+                for (int fi = 0; fi < 4; ++fi) prow[16 * fi] = acc[i][fi][v];
+                continue;
+            }
             // each output element gets exactly one shared contribution, and
             // nothing else writes out meanwhile: a plain read-modify-write
             float *orow = out + (int64_t)(t0 + tt) * E + r0 + rl;
@@ -705,6 +763,74 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_shared(Layer L, Work W, in
             for (int fi = 0; fi < 4; ++fi) orow[16 * fi] += acc[i][fi][v];
         }
     }
+}
+
+// ---------------------------------------------------------------- K-split reductions
+// h[t][f] = silu(sum_z gate) * sum_z up over the ks splits in order, as bf16 high
+// and low parts.
+__global__ __launch_bounds__(256) void k_shared_gu_reduce(Work W, const float *__restrict__ part, int n_tok, int F,
+                                                          int ks) {
+    const int64_t n = (int64_t)n_tok * F;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t t = i / F, f = i - t * F;
+        float g = 0.0f, u = 0.0f;
+        for (int z = 0; z < ks; ++z) {
+            const float *p = part + ((int64_t)z * n_tok + t) * (2 * F);
+            g += p[f];
+            u += p[F + f];
+        }
+        const float h = silu(g) * u;
+        const uint16_t hi = f32_to_bf16_rne(h);
+        W.hsh_hi[i] = hi;
+        W.hsh_lo[i] = f32_to_bf16_rne(h - bf16_to_f32(hi));
+    }
+}
+// out[t][r] += sum_z part[z][t][r] over the ks splits in order.
+__global__ __launch_bounds__(256) void k_shared_dn_reduce(const float *__restrict__ part, int n_tok, int E, int ks,
+                                                          float *__restrict__ out) {
+    const int64_t n = (int64_t)n_tok * E;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        float s = 0.0f;
+        for (int z = 0; z < ks; ++z) s += part[(int64_t)z * n + i];
+        out[i] += s;
+    }
+}
+
+// h[q][f] = silu(sum_z gate) * sum_z up over the ks splits in order, as fp16,
+// for the nq routed slots.
+__global__ __launch_bounds__(256) void k_routed_gu_reduce(Work W, const float *__restrict__ part, int nq, int F, int ks) {
+    const int64_t n = (int64_t)nq * F;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t q = i / F, f = i - q * F;
+        float g = 0.0f, u = 0.0f;
+        for (int z = 0; z < ks; ++z) {
+            const float *p = part + ((int64_t)z * nq + q) * (2 * F);
+            g += p[f];
+            u += p[F + f];
+        }
+        W.hbuf16[i] = f16_bits(silu(g) * u);
+    }
+}
+
+// K splits for a routed GEMM of wgs workgroups (the grid's chunk rows are an
+// upper bound of the work) over nb 256-K blocks: none from 256 workgroups up
+// (at 8 tokens splits measured no faster), else about 512 workgroups in all,
+// at least 2 blocks per split, at most 8 splits; rows (the slots when the
+// splits write partial sums, else 0) times splits within the partial-sum buffer.
+static int routed_ksplit(int wgs, int nb, int rows) {
+    int ks = 1;
+    if (wgs >= 256) return ks;
+    while (wgs * ks < 512 && ks < 8 && nb / (2 * ks) >= 2 && 2 * ks * rows <= PART_ROWS) ks *= 2;
+    return ks;
+}
+
+// K splits for a shared-expert GEMM of wgs workgroups over nkc K chunks: about
+// 512 workgroups in all, at least 2 chunks per split, at most 16 splits, and
+// splits times tokens within the partial-sum buffer.
+static int shared_ksplit(int wgs, int nkc, int n_tok) {
+    int ks = 1;
+    while (wgs * ks < 512 && ks < 16 && nkc / (2 * ks) >= 2 && 2 * ks * n_tok <= PART_ROWS) ks *= 2;
+    return ks;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -720,31 +846,51 @@ hipError_t launch_gemm_prep(const Layer &L, const Work &W, const void *x, int n_
 }
 
 hipError_t launch_gemm_gateup_routed(const Layer &L, const Work &W, int n_tok, hipStream_t s) {
-    const int mc = gemm_max_chunks(n_tok, L.n_expert, L.top_k);
-    hipLaunchKernelGGL(k_gemm_gateup_routed, dim3(L.n_ff / RGU_ROWS, mc), dim3(RB_THREADS), 0, s, L, W);
+    const int mc = gemm_max_chunks(n_tok, L.n_expert, L.top_k), gx = L.n_ff / RGU_ROWS, nq = n_tok * L.top_k;
+    const int ks = routed_ksplit(gx * mc, L.nbe, nq);
+    float *part = ks > 1 ? W.part : nullptr;
+    hipLaunchKernelGGL(k_gemm_gateup_routed, dim3(gx, mc, ks), dim3(RB_THREADS), 0, s, L, W, L.nbe / ks, part, nq);
+    if (ks > 1) {
+        const int nb = (int)std::min<int64_t>(((int64_t)nq * L.n_ff + 255) / 256, 2048);
+        hipLaunchKernelGGL(k_routed_gu_reduce, dim3(nb), dim3(256), 0, s, W, W.part, nq, L.n_ff, ks);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_gateup_shared(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s) {
-    const dim3 g(L.n_ff / GU_ROWS, (n_tok + CH_TOK - 1) / CH_TOK);
+    const int gx = L.n_ff / GU_ROWS, gy = (n_tok + CH_TOK - 1) / CH_TOK, nkc = L.n_embd / 32;
+    const int ks = shared_ksplit(gx * gy, nkc, n_tok);
+    const dim3 g(gx, gy, ks);
+    float *part = ks > 1 ? W.part : nullptr;
     if (L.act_dtype == 1)
         hipLaunchKernelGGL(k_gemm_gateup_shared<false>, g, dim3(256), 0, s, L, W, static_cast<const uint16_t *>(x),
-                           nullptr, n_tok);
+                           nullptr, n_tok, nkc / ks, part);
     else
-        hipLaunchKernelGGL(k_gemm_gateup_shared<true>, g, dim3(256), 0, s, L, W, W.xhi, W.xlo, n_tok);
+        hipLaunchKernelGGL(k_gemm_gateup_shared<true>, g, dim3(256), 0, s, L, W, W.xhi, W.xlo, n_tok, nkc / ks,
+                           part);
+    if (ks > 1) {
+        const int nb = (int)std::min<int64_t>(((int64_t)n_tok * L.n_ff + 255) / 256, 2048);
+        hipLaunchKernelGGL(k_shared_gu_reduce, dim3(nb), dim3(256), 0, s, W, W.part, n_tok, L.n_ff, ks);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_down_routed(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s) {
-    const int mc = gemm_max_chunks(n_tok, L.n_expert, L.top_k);
-    hipLaunchKernelGGL(k_gemm_down_routed, dim3((L.n_embd + RDN_ROWS - 1) / RDN_ROWS, mc), dim3(RB_THREADS), 0, s, L, W,
-                       out);
+    const int mc = gemm_max_chunks(n_tok, L.n_expert, L.top_k), gx = (L.n_embd + RDN_ROWS - 1) / RDN_ROWS;
+    const int ks = routed_ksplit(gx * mc, L.nbf, 0);
+    hipLaunchKernelGGL(k_gemm_down_routed, dim3(gx, mc, ks), dim3(RB_THREADS), 0, s, L, W, out, L.nbf / ks);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_down_shared(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s) {
-    hipLaunchKernelGGL(k_gemm_down_shared, dim3(L.n_embd / DN_ROWS, (n_tok + CH_TOK - 1) / CH_TOK), dim3(256), 0, s,
-                       L, W, n_tok, out);
+    const int gx = L.n_embd / DN_ROWS, gy = (n_tok + CH_TOK - 1) / CH_TOK, nkc = L.n_ff / 32;
+    const int ks = shared_ksplit(gx * gy, nkc, n_tok);
+    float *part = ks > 1 ? W.part : nullptr;
+    hipLaunchKernelGGL(k_gemm_down_shared, dim3(gx, gy, ks), dim3(256), 0, s, L, W, n_tok, out, nkc / ks, part);
+    if (ks > 1) {
+        const int nb = (int)std::min<int64_t>(((int64_t)n_tok * L.n_embd + 255) / 256, 2048);
+        hipLaunchKernelGGL(k_shared_dn_reduce, dim3(nb), dim3(256), 0, s, W.part, n_tok, L.n_embd, ks, out);
+    }
     return hipGetLastError();
 }
 
