@@ -278,8 +278,12 @@ int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *
     if (n_tok == 0) return DS4MOE_OK;
     int path = h->path;
     // one token: the fused decode kernel; more: the grouped GEMMs, which at 2-4
-    // tokens (K split over more workgroups) also beat the GEMV kernels
-    if (path == DS4MOE_PATH_AUTO) path = (n_tok == 1) ? DS4MOE_PATH_GEMV : DS4MOE_PATH_GEMM;
+    // tokens (K split over more workgroups) also beat the GEMV kernels.  fp32
+    // activations of up to 4 tokens keep the GEMV kernels, which do not round
+    // them to fp16.
+    if (path == DS4MOE_PATH_AUTO)
+        path = (n_tok == 1 || (n_tok <= GEMV_MAX_TOK && h->L.act_dtype == DS4MOE_F32)) ? DS4MOE_PATH_GEMV
+                                                                                      : DS4MOE_PATH_GEMM;
     if (path == DS4MOE_PATH_GEMV && n_tok > GEMV_MAX_TOK)
         return fail(DS4MOE_EUNSUPPORTED, "forward: GEMV path takes at most %d tokens (got %d)", GEMV_MAX_TOK, n_tok);
     if (path == DS4MOE_PATH_GEMM && !gemm_available())

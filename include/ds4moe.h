@@ -71,7 +71,7 @@ enum { DS4MOE_F32 = 0, DS4MOE_BF16 = 1 };
 
 /* Kernel path selection for ds4moe_forward (ds4moe_set_path). */
 enum {
-    DS4MOE_PATH_AUTO = 0,    /* the fused decode kernel for one token, grouped MFMA GEMM above */
+    DS4MOE_PATH_AUTO = 0,    /* one token: fused decode; 2-4 fp32 tokens: GEMV; else grouped MFMA GEMM */
     DS4MOE_PATH_GEMV = 1,    /* dequant-fused GEMV kernels (decode); n_tok <= 4 only,
                                 else ds4moe_forward returns DS4MOE_EUNSUPPORTED */
     DS4MOE_PATH_GEMM = 2     /* grouped dequant MFMA GEMM kernels (prefill), any n_tok */
