@@ -491,14 +491,6 @@ __device__ __forceinline__ void dec_route_poll(const Layer &L, const Work &W, ui
         if (lane == 0) *lds_flag = ok;
     }
 }
-__device__ __forceinline__ bool dec_route_wait(const Layer &L, const Work &W, uint32_t tag, RouteCache *rc,
-                                               int *lds_flag) {
-    dec_route_poll(L, W, tag, rc, lds_flag);
-    __syncthreads();
-    const bool ok = *lds_flag != 0;
-    __syncthreads();
-    return ok;
-}
 
 // Weights of one routed gate/up item for this lane: DEC_GU_NR rows of gate and
 // up, with their fp16 scales d as loaded.  Nothing here looks at the loaded
@@ -649,12 +641,6 @@ __device__ __forceinline__ bool dec_h_finish(const Work &W, int F, int slot, uin
     }
     return __syncthreads_and(ok) != 0;
 }
-// Both parts at once.
-__device__ __forceinline__ bool dec_stage_h(const Work &W, int F, int slot, uint32_t tag, float4 *H) {
-    HPre p;
-    dec_h_issue(W, F, slot, p);
-    return dec_h_finish(W, F, slot, tag, H, p);
-}
 
 // ---------------------------------------------------------------- P3: shared down
 // CPR = 16-byte chunks per lane per row (F / 512, at least 1); 16 chunk loads in
@@ -742,57 +728,6 @@ __device__ __forceinline__ void dec_rdn_load(const Layer &L, const DecPlan &P, c
         w.qs[r] = ld_nt<uint4>(L.q2k_qs, rb * 64u + c * 16u);
         w.sc[r] = ld_nt<uint32_t>(L.q2k_sc, rb * 16u + c * 4u);
         w.dd[r] = ld_nt<uint32_t>(L.q2k_dd, 4u * (rb + (c >> 2)));
-    }
-}
-
-// H holds the slot's h vector (staged by the caller).  Each Q2_K row of the
-// lane (64 weights: 4 sub-blocks of 16, weight 16 s + 4 b + u in bits 2u of
-// byte b of word s) is d * sum_s sc_s dot_s - dmin * sum_s m_s hsum_s.
-__device__ __forceinline__ void dec_rdn_compute(const Layer &L, float *__restrict__ out, int item, const DecPlan &P,
-                                                const RouteCache *rc, const RdnW &w, const float4 *H) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int E = L.n_embd, F = L.n_ff;
-    const int lpr = F >> 6, rpw = 64 / lpr;
-    const int c = lane & (lpr - 1);
-    const int j = item / P.rdn_per_slot, tile = item - j * P.rdn_per_slot;
-    const int r0 = (tile * DEC_WAVES + wave) * (DEC_DN_NR * rpw) + lane / lpr;
-    const float wgt = rc->w[j];
-    float A[DEC_DN_NR], B[DEC_DN_NR];
-#pragma unroll
-    for (int r = 0; r < DEC_DN_NR; ++r) A[r] = 0.0f, B[r] = 0.0f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        float hv[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 v = H[h_slot(16 * c + 4 * s + q)];
-            hv[4 * q] = v.x, hv[4 * q + 1] = v.y, hv[4 * q + 2] = v.z, hv[4 * q + 3] = v.w;
-        }
-        float hsum = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) hsum += hv[q];
-#pragma unroll
-        for (int r = 0; r < DEC_DN_NR; ++r) {
-            const uint32_t Q = s == 0 ? w.qs[r].x : s == 1 ? w.qs[r].y : s == 2 ? w.qs[r].z : w.qs[r].w;
-            float dot = 0.0f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t tq = (Q >> (2 * u)) & 0x03030303u;
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb) dot = fmaf((float)((tq >> (8 * bb)) & 0xFFu), hv[4 * bb + u], dot);
-            }
-            const uint32_t scb = (w.sc[r] >> (8 * s)) & 0xFFu;
-            A[r] = fmaf((float)(scb & 15u), dot, A[r]);
-            B[r] = fmaf((float)(scb >> 4), hsum, B[r]);
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < DEC_DN_NR; ++r) {
-        const int row = r0 + r * rpw;
-        const uint32_t dd = w.dd[r];
-        float y = half_to_f32((uint16_t)(dd & 0xFFFFu)) * A[r] - half_to_f32((uint16_t)(dd >> 16)) * B[r];
-        y = dec_group_sum(y, lpr);
-        if (c == 0 && row < E) atomicAdd(out + row, wgt * y);
     }
 }
 
