@@ -183,10 +183,23 @@ __device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &
         return *reinterpret_cast<const uint4 *>(qg + ((fi >= GU_FR) ? qdu : 0) + (fi % GU_FR) * fq + 64 * bi);
     };
     auto dload = [&](int fi, int bi) { return dg[((fi >= GU_FR) ? ddu : 0) + (fi % GU_FR) * fd + bi]; };
-    uint4 wcur[GU_NF], wnext[GU_NF];
-    uint16_t dcur[GU_NF], dnext[GU_NF];
+    // weights LA blocks ahead in LA + 1 named buffers used in rotation (the
+    // loop is unrolled by LA + 1): a buffer is first read LA blocks after its
+    // loads are issued, and nothing copies a value that may still be in flight
+    // (a copy would wait for it).  Two blocks ahead for one or two token tiles,
+    // whose blocks compute in less than a load's latency, when there are at
+    // least 4 blocks; one otherwise (more tiles: their registers would not
+    // fit two)
+    constexpr int LAM = NT <= 2 ? 2 : 1;
+    const int LA = (LAM == 2 && nbe >= 4) ? 2 : 1;
+    uint4 w0[GU_NF], w1[GU_NF], w2[GU_NF];
+    uint16_t d0[GU_NF], d1[GU_NF], d2[GU_NF];
 #pragma unroll
-    for (int fi = 0; fi < GU_NF; ++fi) wcur[fi] = wload(fi, 0), dcur[fi] = dload(fi, 0);
+    for (int fi = 0; fi < GU_NF; ++fi) {
+        w0[fi] = wload(fi, 0), d0[fi] = dload(fi, 0);
+        // unconditionally (with one block ahead, block 0 loads it again)
+        w1[fi] = wload(fi, min(1, nbe - 1)), d1[fi] = dload(fi, min(1, nbe - 1));
+    }
 
     floatx4 acc[NT][GU_NF];
     const floatx4 zf = {0.f, 0.f, 0.f, 0.f};
@@ -195,14 +208,17 @@ __device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &
 #pragma unroll
         for (int fi = 0; fi < GU_NF; ++fi) acc[i][fi] = zf;
 
-    for (int bi = 0; bi < nbe; ++bi) {
+    // block bi from (wcur, dcur); block bi + LA's weights into (wl, dl)
+    auto block = [&](int bi, const uint4 (&wcur)[GU_NF], const uint16_t (&dcur)[GU_NF], uint4 (&wl)[GU_NF],
+                     uint16_t (&dl)[GU_NF]) __attribute__((always_inline)) {
         const bool more = bi + 1 < nbe;
         {
-            // the next block (the last one again past the end: unused), unconditionally
-            const int bn = min(bi + 1, nbe - 1);
-            ld.load(bn, xr);
+            // the next block's x, then the weights LA blocks ahead (the last
+            // block again past the end: unused), unconditionally
+            ld.load(min(bi + 1, nbe - 1), xr);
+            const int b2 = min(bi + LA, nbe - 1);
 #pragma unroll
-            for (int fi = 0; fi < GU_NF; ++fi) wnext[fi] = wload(fi, bn), dnext[fi] = dload(fi, bn);
+            for (int fi = 0; fi < GU_NF; ++fi) wl[fi] = wload(fi, b2), dl[fi] = dload(fi, b2);
         }
         const uint8_t *cur = (bi & 1) ? stg1 : stg0;
         half2v scl[GU_NF];
@@ -232,12 +248,23 @@ __device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &
                 for (int fi = 0; fi < GU_NF; ++fi) acc[i][fi] = mfma_f16(a, b[fi], acc[i][fi]);
             }
         }
-        if (more) {
-            ld.store((bi & 1) ? stg0 : stg1, xr);
-#pragma unroll
-            for (int fi = 0; fi < GU_NF; ++fi) wcur[fi] = wnext[fi], dcur[fi] = dnext[fi];
-        }
+        if (more) ld.store((bi & 1) ? stg0 : stg1, xr);
         __syncthreads();
+    };
+    if (LAM == 2 && LA == 2) {
+        for (int bi = 0; bi < nbe; bi += 3) {
+            block(bi, w0, d0, w2, d2);
+            if (bi + 1 >= nbe) break;
+            block(bi + 1, w1, d1, w0, d0);
+            if (bi + 2 >= nbe) break;
+            block(bi + 2, w2, d2, w1, d1);
+        }
+    } else {
+        for (int bi = 0; bi < nbe; bi += 2) {
+            block(bi, w0, d0, w1, d1);
+            if (bi + 1 >= nbe) break;
+            block(bi + 1, w1, d1, w0, d0);
+        }
     }
 
     if (part) {
