@@ -57,8 +57,9 @@ __device__ __forceinline__ uint16_t f16_bits(float f) { return __builtin_bit_cas
 
 // ---------------------------------------------------------------- routing -> chunks
 // Splits every expert's token list into chunks of at most CH_TOK slots:
-// chunk = (expert, first list position, count), experts ascending.
-__global__ __launch_bounds__(256) void k_build_chunks(int NE, Work W) {
+// chunk = (expert, first list position, count), experts ascending.  By one
+// workgroup of 256 threads (thread e: expert e).
+__device__ void build_chunks(int NE, const Work &W) {
     __shared__ int wsum[4];
     const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
     int beg = 0, m = 0;
@@ -86,9 +87,12 @@ __global__ __launch_bounds__(256) void k_build_chunks(int NE, Work W) {
 // ---------------------------------------------------------------- activation copies
 // x (bf16 or fp32) -> fp16 for the routed GEMMs; for fp32 x also the bf16 high
 // and low parts used by the shared expert.
+// Workgroup 0 also builds the chunk table (one launch instead of two).
 template <bool XBF16>
 __global__ __launch_bounds__(256) void k_prep_x(const void *__restrict__ x, int64_t n, uint16_t *__restrict__ x16,
-                                                uint16_t *__restrict__ xhi, uint16_t *__restrict__ xlo) {
+                                                uint16_t *__restrict__ xhi, uint16_t *__restrict__ xlo, int NE,
+                                                Work W) {
+    if (blockIdx.x == 0) build_chunks(NE, W);
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
         float v;
         if (XBF16) {
@@ -865,10 +869,9 @@ hipError_t launch_gemm_prep(const Layer &L, const Work &W, const void *x, int n_
     const int64_t nx = (int64_t)n_tok * L.n_embd;
     const int pg = (int)std::min<int64_t>((nx + 255) / 256, 4096);
     if (L.act_dtype == 1)
-        hipLaunchKernelGGL(k_prep_x<true>, dim3(pg), dim3(256), 0, s, x, nx, W.x16, nullptr, nullptr);
+        hipLaunchKernelGGL(k_prep_x<true>, dim3(pg), dim3(256), 0, s, x, nx, W.x16, nullptr, nullptr, L.n_expert, W);
     else
-        hipLaunchKernelGGL(k_prep_x<false>, dim3(pg), dim3(256), 0, s, x, nx, W.x16, W.xhi, W.xlo);
-    hipLaunchKernelGGL(k_build_chunks, dim3(1), dim3(256), 0, s, L.n_expert, W);
+        hipLaunchKernelGGL(k_prep_x<false>, dim3(pg), dim3(256), 0, s, x, nx, W.x16, W.xhi, W.xlo, L.n_expert, W);
     return hipGetLastError();
 }
 
