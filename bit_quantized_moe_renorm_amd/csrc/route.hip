@@ -478,43 +478,55 @@ __global__ __launch_bounds__(256) void k_route_approx(const uint16_t *__restrict
     for (int p = 0; p < 3; ++p) wp[p] = hml + ((int64_t)p * NE + (eok ? e : 0)) * E + kb + 8 * grp;
     // every load is unconditional: tokens past n_tok read token 0 and experts
     // past NE read expert 0 (in bounds); their products land in accumulator
-    // rows and columns that are never stored
-    const uint16_t *xp[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * i + rl;
-        xp[i] = x + (int64_t)(t < n_tok ? t : 0) * E + kb + 8 * grp;
-    }
+    // rows and columns that are never stored.
+    // x (64 tokens x 64 K per stage) is staged in LDS once for the four waves,
+    // double-buffered with one barrier per stage: thread t moves 32 bytes of
+    // row t / 4, 16-byte units 2 (t % 4) and 2 (t % 4) + 1.  Unit u of row r
+    // sits at position u ^ (r & 7), so a step's A reads hit distinct banks.
+    __shared__ uint4 xs[2][64 * 8];
+    const int sr = threadIdx.x >> 2, su = 2 * (threadIdx.x & 3);
+    const uint16_t *xsrc = x + (int64_t)(t0 + sr < n_tok ? t0 + sr : 0) * E + kb + 8 * su;
     double acc[4][4] = {};
-    // 32-K steps, two per stage; the next stage's loads are in flight while
-    // this one's MFMAs run (named buffers alternate, no copies).  The fp32
-    // MFMA sums go into the fp64 accumulators every 256 K.
+    // router parts: 32-K steps, two per stage, one stage ahead in named
+    // buffers that alternate (no copies).  The fp32 MFMA sums go into the fp64
+    // accumulators every 256 K.
     struct Stage {
-        uint4 a[2][4], b[2][3];
+        uint4 b[2][3];
     };
-    auto load = [&](int st, Stage &g) __attribute__((always_inline)) {
-        const int s0 = min(st, kq / 64 - 1) * 64;  // past the end: the last stage again, unused
+    const int nst = kq / 64;  // a multiple of 4: the launch requires n_embd % 1024 == 0
+    auto loadb = [&](int st, Stage &g) __attribute__((always_inline)) {
+        const int s0 = min(st, nst - 1) * 64;  // past the end: the last stage again, unused
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) g.a[s][i] = *reinterpret_cast<const uint4 *>(xp[i] + s0 + 32 * s);
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int p = 0; p < 3; ++p) g.b[s][p] = *reinterpret_cast<const uint4 *>(wp[p] + s0 + 32 * s);
-        }
+    };
+    uint4 xr0, xr1;  // x of the next stage, on its way to LDS
+    auto loadx = [&](int st) __attribute__((always_inline)) {
+        const int s0 = min(st, nst - 1) * 64;
+        xr0 = *reinterpret_cast<const uint4 *>(xsrc + s0);
+        xr1 = *reinterpret_cast<const uint4 *>(xsrc + s0 + 8);
+    };
+    auto storex = [&](int buf) __attribute__((always_inline)) {
+        xs[buf][sr * 8 + (su ^ (sr & 7))] = xr0;
+        xs[buf][sr * 8 + ((su + 1) ^ (sr & 7))] = xr1;
     };
     rt_floatx4 part[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) part[i] = rt_floatx4{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](int st, const Stage &g) __attribute__((always_inline)) {
+        const uint4 *xb = xs[st & 1];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
+                const uint4 a = xb[(16 * i + rl) * 8 + ((4 * s + grp) ^ (rl & 7))];
 #pragma unroll
                 for (int p = 0; p < 3; ++p)
-                    part[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(rt_bf16x8, g.a[s][i]),
+                    part[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(rt_bf16x8, a),
                                                                       __builtin_bit_cast(rt_bf16x8, g.b[s][p]),
                                                                       part[i], 0, 0, 0);
+            }
         if ((st & 3) == 3) {  // 256 K done
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -524,14 +536,26 @@ __global__ __launch_bounds__(256) void k_route_approx(const uint16_t *__restrict
             }
         }
     };
-    const int nst = kq / 64;  // a multiple of 4: the launch requires n_embd % 1024 == 0
+    // one stage: compute st; put x of st + 1 (loaded a stage ago) into the
+    // other buffer, whose readers finished before the last barrier; load x
+    // and the router parts of st + 2
+    auto stage = [&](int st, Stage &g) __attribute__((always_inline)) {
+        compute(st, g);
+        if (st + 1 < nst) storex((st + 1) & 1);
+        loadx(st + 2);
+        loadb(st + 2, g);
+        __syncthreads();
+    };
     Stage g0, g1;
-    load(0, g0);
+    loadx(0);
+    loadb(0, g0);
+    storex(0);
+    loadx(1);
+    loadb(1, g1);
+    __syncthreads();
     for (int st = 0; st < nst; st += 2) {
-        load(st + 1, g1);
-        compute(st, g0);
-        load(st + 2, g0);
-        compute(st + 1, g1);
+        stage(st, g0);
+        stage(st + 1, g1);
     }
     // C layout: lane (rl, grp) holds tokens 4 grp + v of each tile for expert rl
     float *eq = est + (int64_t)blockIdx.z * n_tok * NE;
