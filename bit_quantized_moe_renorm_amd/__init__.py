@@ -188,7 +188,8 @@ def forward_stack(layers, h, eps: float = 1e-6, x=None, stream=None):
     n, E = h.shape
     if x is None:
         x = torch.empty((n, E), dtype=torch.bfloat16, device=h.device)
-    hs = (ctypes.c_void_p * len(layers))(*[lay.h.value for lay in layers])
+    # a closed layer passes NULL, which the library rejects (DS4MOE_EINVAL)
+    hs = (ctypes.c_void_p * len(layers))(*[lay.h.value if lay.h else None for lay in layers])
     _check(load_library().ds4moe_forward_stack(hs, len(layers), _ptr(h), n, eps, _ptr(x), _stream(stream)))
     return h
 
