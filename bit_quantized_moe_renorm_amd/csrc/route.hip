@@ -14,7 +14,7 @@
 namespace ds4 {
 
 constexpr int RT_WAVES = 4;         // waves per router workgroup (one K quarter each)
-constexpr int RT_TOK = 16;          // tokens per workgroup
+constexpr int RT_TOK = 16;          // tokens per router workgroup (8 for calls of up to 8 tokens)
 constexpr int ROUTE_SMALL_MAX = 64; // fused top-k/bucketing in the last workgroup up to this n_tok
 
 template <bool XBF16>
@@ -216,7 +216,7 @@ __device__ void bucket_small(const unsigned long long *__restrict__ itag, uint32
     }
 }
 
-// Logits of one expert (blockIdx.x) for RT_TOK tokens per workgroup, fp64
+// Logits of one expert (blockIdx.x) for TT tokens per workgroup, fp64
 // accumulation.  Wave w covers K quarter w; lane l holds 4 values at
 // 4 l + 256 j of it (j < 4: n_embd <= 4096).  All of a wave's loads are in
 // flight together (unconditional: tokens past the tile's end re-read its last
@@ -225,35 +225,35 @@ __device__ void bucket_small(const unsigned long long *__restrict__ itag, uint32
 // With fuse_tail, the last workgroup of each token tile takes the tile's top-k,
 // and the last of those builds the per-expert lists.
 constexpr int RT_KCH = 4;  // 256-value chunks per wave at most
-template <bool XBF16>
+template <bool XBF16, int TT>
 __global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ R, const float *__restrict__ bias,
                                                       const void *__restrict__ x, int n_tok, int NE, int E,
                                                       int k, Work W, int fuse_tail, uint32_t tag) {
-    __shared__ double part[RT_WAVES][RT_TOK];
+    __shared__ double part[RT_WAVES][TT];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int e = blockIdx.x;
-    const int t0 = blockIdx.y * RT_TOK;
-    const int nt = min(RT_TOK, n_tok - t0);
+    const int t0 = blockIdx.y * TT;
+    const int nt = min(TT, n_tok - t0);
     const int kq = E / RT_WAVES, kb = wave * kq;
     {
-        double acc[RT_TOK];
+        double acc[TT];
 #pragma unroll
-        for (int t = 0; t < RT_TOK; ++t) acc[t] = 0.0;
+        for (int t = 0; t < TT; ++t) acc[t] = 0.0;
         float4 r[RT_KCH];
-        double xv[RT_KCH][RT_TOK][4];
+        double xv[RT_KCH][TT][4];
 #pragma unroll
         for (int j = 0; j < RT_KCH; ++j) {
             const int off = 4 * lane + 256 * j;
             const int i = kb + (off < kq ? off : 0);
             r[j] = *reinterpret_cast<const float4 *>(R + (int64_t)e * E + i);
 #pragma unroll
-            for (int t = 0; t < RT_TOK; ++t) load_x4<XBF16>(x, (int64_t)(t0 + min(t, nt - 1)) * E + i, xv[j][t]);
+            for (int t = 0; t < TT; ++t) load_x4<XBF16>(x, (int64_t)(t0 + min(t, nt - 1)) * E + i, xv[j][t]);
         }
 #pragma unroll
         for (int j = 0; j < RT_KCH; ++j) {
             if (4 * lane + 256 * j < kq) {
 #pragma unroll
-                for (int t = 0; t < RT_TOK; ++t) {
+                for (int t = 0; t < TT; ++t) {
                     acc[t] = fma(xv[j][t][0], (double)r[j].x, acc[t]);
                     acc[t] = fma(xv[j][t][1], (double)r[j].y, acc[t]);
                     acc[t] = fma(xv[j][t][2], (double)r[j].z, acc[t]);
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ 
             }
         }
 #pragma unroll
-        for (int t = 0; t < RT_TOK; ++t) {
+        for (int t = 0; t < TT; ++t) {
             const double s = wave_sum(acc[t]);
             if (lane == 0) part[wave][t] = s;
         }
@@ -767,14 +767,27 @@ hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok,
         hipLaunchKernelGGL(k_fill_lists, dim3(NE), dim3(256), 0, s, n_tok, NE, L.top_k, W);
         return hipGetLastError();
     }
-    dim3 grid(NE, (n_tok + RT_TOK - 1) / RT_TOK);
     const int fuse = n_tok <= ROUTE_SMALL_MAX;
-    if (L.act_dtype == 1)
-        hipLaunchKernelGGL(k_route_logits<true>, grid, dim3(256), 0, s, L.router, L.router_bias, x, n_tok, NE,
-                           L.n_embd, L.top_k, W, fuse, tag);
-    else
-        hipLaunchKernelGGL(k_route_logits<false>, grid, dim3(256), 0, s, L.router, L.router_bias, x, n_tok, NE,
-                           L.n_embd, L.top_k, W, fuse, tag);
+    // 8-token tiles for calls of up to 8 tokens (a 16-token tile would load and
+    // multiply clamped copies of the last token)
+    const bool small = n_tok <= 8;
+    const int tt = small ? 8 : RT_TOK;
+    const dim3 grid(NE, (n_tok + tt - 1) / tt);
+    if (L.act_dtype == 1) {
+        if (small)
+            hipLaunchKernelGGL((k_route_logits<true, 8>), grid, dim3(256), 0, s, L.router, L.router_bias, x, n_tok,
+                               NE, L.n_embd, L.top_k, W, fuse, tag);
+        else
+            hipLaunchKernelGGL((k_route_logits<true, RT_TOK>), grid, dim3(256), 0, s, L.router, L.router_bias, x,
+                               n_tok, NE, L.n_embd, L.top_k, W, fuse, tag);
+    } else {
+        if (small)
+            hipLaunchKernelGGL((k_route_logits<false, 8>), grid, dim3(256), 0, s, L.router, L.router_bias, x, n_tok,
+                               NE, L.n_embd, L.top_k, W, fuse, tag);
+        else
+            hipLaunchKernelGGL((k_route_logits<false, RT_TOK>), grid, dim3(256), 0, s, L.router, L.router_bias, x,
+                               n_tok, NE, L.n_embd, L.top_k, W, fuse, tag);
+    }
     if (!fuse) {
         hipLaunchKernelGGL(k_topk, dim3((n_tok + 3) / 4), dim3(256), 0, s, n_tok, NE, L.top_k, W);
         hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, s, n_tok, NE, L.top_k, W);
