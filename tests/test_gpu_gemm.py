@@ -64,7 +64,7 @@ def test_gemm_tiny_multi_chunk_experts():
 
 @pytest.mark.parametrize("n", [5, 8, 16, 32])
 def test_gemm_zipf_batches(n):
-    """Decode batches under a Zipf-skewed router bias (AUTO takes the GEMM path above 4 tokens)."""
+    """Decode batches under a Zipf-skewed router bias (AUTO takes the GEMM path for bf16 batches)."""
     lay = host_layer("ds4_zipf")
     x = synth.activations(2, n, 4096)
     got = _run(device_layer("ds4_zipf"), x, m.PATH_AUTO)
