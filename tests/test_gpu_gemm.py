@@ -62,9 +62,11 @@ def test_gemm_tiny_multi_chunk_experts():
     assert err <= REL_TOL
 
 
-@pytest.mark.parametrize("n", [5, 8, 16, 32])
+@pytest.mark.parametrize("n", [2, 3, 5, 8, 16, 32])
 def test_gemm_zipf_batches(n):
-    """Decode batches under a Zipf-skewed router bias (AUTO takes the GEMM path for bf16 batches)."""
+    """Decode batches under a Zipf-skewed router bias (AUTO takes the GEMM path for bf16 batches).
+    2 and 3 tokens split the GEMMs' K range 8 ways, 5 tokens 4 ways, 8 and more not at all
+    (routed) while the shared expert still splits."""
     lay = host_layer("ds4_zipf")
     x = synth.activations(2, n, 4096)
     got = _run(device_layer("ds4_zipf"), x, m.PATH_AUTO)
