@@ -12,6 +12,10 @@ steps cycle through the copies, so consecutive uses of one copy are R * 97 MB
 apart and nothing is served from the 256 MB Infinity Cache: every step
 streams its weights from HBM, as in a stack of distinct layers.
 
+The default run also times the 2048-token prefill of the same layer (one
+call, and four calls of 512 tokens), nested under "prefill" with its own MFMA
+roofline and CPU baseline: the metric names both halves.
+
 Prints ONE JSON line on stdout; details go to stderr.
 """
 import argparse
@@ -83,23 +87,63 @@ def profile_traffic(name):
     return int(tb.group(1)) if h.hexdigest() == sha.group(1) else None
 
 
-def cpu_baseline_decode(layer, x_np, budget_s=12.0):
-    """The oracle (as it stands) on the host cores, on a bounded sample of the same
-    token stream: batches of 16 tokens until about budget_s seconds have passed."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(fn, n_tok):
+    t0 = time.perf_counter()
+    fn()
+    return n_tok / (time.perf_counter() - t0)
+
+
+def cpu_baseline(fn_all, n_all, fn_one, n_one, unit, sample, sample_one):
+    """The oracle (as it stands) on the host cores: fn_all covers n_all tokens
+    with every OpenMP thread (or returns how many it covered, when n_all is
+    None), fn_one n_one tokens with one thread."""
     import oracle
-    done, t0 = 0, time.perf_counter()
-    while True:
-        oracle.forward(layer, x_np[done:done + 16])
-        done += 16
-        el = time.perf_counter() - t0
-        if el >= budget_s or done + 16 > len(x_np):
-            break
-    return {"value": done / el, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {done} of the 1000 decode tokens, oracle.forward in batches of 16 "
-                      f"({el:.1f} s)"}
+    cores = oracle.num_threads()
+    t0 = time.perf_counter()
+    r = fn_all()
+    el = time.perf_counter() - t0
+    if n_all is None:
+        n_all = r
+    oracle.set_num_threads(1)
+    try:
+        one = _oracle_rate(fn_one, n_one)
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": round(n_all / el, 3), "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"{sample}: {n_all} tokens in {el:.1f} s", "cpu_model": cpu_model(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "one_thread": {"value": round(one, 3), "unit": unit, "sample": sample_one}}
 
 
-def run_decode(args):
+def cpu_baseline_decode(layer, x_np, budget_s=12.0):
+    """The oracle on a bounded sample of the decode token stream: batches of 16
+    tokens until about budget_s seconds have passed."""
+    import oracle
+
+    def run():
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.forward(layer, x_np[done:done + 16])
+            done += 16
+            if time.perf_counter() - t0 >= budget_s or done + 16 > len(x_np):
+                return done
+
+    return cpu_baseline(run, None, lambda: oracle.forward(layer, x_np[:1]), 1, "tok/s",
+                        "the first tokens of the 1000-token decode stream, oracle.forward in batches of 16",
+                        "token 0")
+
+
+def run_decode(args, layer=None):
     import numpy as np
     import torch
 
@@ -108,7 +152,8 @@ def run_decode(args):
 
     spec = synth.DS4
     t0 = time.perf_counter()
-    layer = synth.make_layer(spec, seed=1)
+    if layer is None:
+        layer = synth.make_layer(spec, seed=1)
     x_np = synth.activations(1, 1000, spec.n_embd)
     log(f"[bench] generated layer + 1000 tokens in {time.perf_counter() - t0:.1f} s")
     w = m.upload_layer(layer)
@@ -165,11 +210,16 @@ def run_decode(args):
                       "GB_s": round(kb[k] / (avg_us[k] * 1e-6) / 1e9, 1)} for k in avg_us if k in kb}
     log("[bench] per-kernel: " + json.dumps(per_kernel))
     # the kernel with the most algorithmic bytes is the dominant one; its
-    # duration is the timed region's events divided by the launches in it
+    # duration is the timed region's events divided by the launches in it.
+    # Algorithmic bytes: the touched expert bytes as stored (6 routed experts +
+    # the shared expert); the router's 4 MB counts in time, not in bytes.
     dom = max(per_kernel, key=lambda k: per_kernel[k]["bytes"])
-    achieved = round(kb[dom] / (region_us * 1e-6) / 1e9, 1)
+    alg_bytes = touched_bytes(spec, spec.top_k) if dom == "fused" else kb[dom]
+    achieved = round(alg_bytes / (region_us * 1e-6) / 1e9, 1)
+    achieved_router = round(kb[dom] / (region_us * 1e-6) / 1e9, 1)
     traffic = profile_traffic("decode_b1_ds4_k_decode_fused.md") if dom == "fused" else None
-    log(f"[bench] {dom}: {region_us:.2f} us per launch over the timed region (events), {achieved} GB/s algorithmic")
+    log(f"[bench] {dom}: {region_us:.2f} us per launch over the timed region (events), {achieved} GB/s "
+        f"algorithmic ({achieved_router} GB/s counting the router's bytes too)")
 
     tok_s = args.steps / wall
     ms_step = 1000.0 * wall / args.steps
@@ -194,7 +244,10 @@ def run_decode(args):
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "traffic_unit": "bytes per launch",
-                     "algorithmic_bytes_per_launch": kb[dom], "avg_launch_us": round(region_us, 3)},
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "bytes_per_launch_with_router": kb[dom], "achieved_with_router": achieved_router,
+                     "frac_with_router": round(achieved_router / HBM_PEAK_GBS, 4),
+                     "avg_launch_us": round(region_us, 3)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(layer, x_np)
@@ -214,7 +267,24 @@ def flops_prefill(spec, n):
             "gemm_down_routed": 2 * E * F * S, "gemm_down_shared": 2 * E * F * n}
 
 
-def run_prefill(args):
+def layer_flop(spec, n):
+    """Routed (selected) + shared matmul flops of a layer for n tokens; the
+    router's flops count in time, not in the numerator."""
+    fl = flops_prefill(spec, n)
+    return sum(v for k, v in fl.items() if k != "route")
+
+
+def distinct_experts(off):
+    import numpy as np
+    o = off.cpu().numpy()
+    return int(np.count_nonzero(o[1:] - o[:-1]))
+
+
+def run_prefill(args, layer=None, cpu=True):
+    """The 2048-token prefill of the DS4-shape layer (seed 1 weights, seed 1
+    tokens): one call of 2048 tokens (MFMA-bound; roofline against the bf16
+    peak) and the same tokens in four calls of 512 (HBM-bound: every call
+    streams nearly all 256 experts; reported against the HBM peak)."""
     import numpy as np
     import torch
 
@@ -223,7 +293,9 @@ def run_prefill(args):
 
     spec = synth.DS4
     n = args.tokens
-    layer = synth.make_layer(spec, seed=1)
+    steps, warmup = args.prefill_steps, args.prefill_warmup
+    if layer is None:
+        layer = synth.make_layer(spec, seed=1)
     x_np = synth.activations(1, n, spec.n_embd)
     w = m.upload_layer(layer)
     dev = m.MoELayer(spec, w, max_tokens=n)
@@ -232,16 +304,17 @@ def run_prefill(args):
     torch.cuda.empty_cache()
     x = m.to_device_x(x_np)
     out = torch.zeros((n, spec.n_embd), dtype=torch.float32, device="cuda")
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         dev.forward(x, out)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         dev.forward(x, out)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    u_one = distinct_experts(dev.last_routing(n)[2])
     dev.timing_enable(True)
-    for _ in range(args.steps):
+    for _ in range(steps):
         dev.forward(x, out)
     torch.cuda.synchronize()
     tim = dev.timing_read()
@@ -253,27 +326,81 @@ def run_prefill(args):
         d = {"avg_us": round(us, 2)}
         if kind in fl:
             d["TFLOP_s"] = round(fl[kind] / (us * 1e-6) / 1e12, 1)
+            if kind != "route":
+                d["mfma_frac"] = round(fl[kind] / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)
         per_kernel[kind] = d
     log("[bench] prefill per-kernel: " + json.dumps(per_kernel))
     dom = "gemm_gateup_routed"
     achieved = per_kernel[dom]["TFLOP_s"]
-    ms_step = 1000.0 * wall / args.steps
-    tok_s = n / (wall / args.steps)
-    total_tf = sum(fl.values()) / (wall / args.steps) / 1e12
-    log(f"[bench] prefill {n}: {ms_step:.3f} ms/step, {tok_s:.0f} tok/s, {total_tf:.0f} TFLOP/s whole layer")
+    step_s = wall / steps
+    tok_s = n / step_s
+    lf = layer_flop(spec, n)
+    layer_tf = lf / step_s / 1e12
+    nb = synth.layer_nbytes(spec)
+    bytes_one = u_one * nb["per_expert"] + nb["shared"]
+    log(f"[bench] prefill {n}: {1000 * step_s:.3f} ms/step, {tok_s:.0f} tok/s, {layer_tf:.0f} TFLOP/s whole layer "
+        f"= {100 * layer_tf / BF16_PEAK_TFLOPS:.1f}% of bf16 peak; {dom} {achieved} TFLOP/s")
+
+    # the same tokens in calls of 512: memory-bound
+    chunk = 512
+    devc = m.MoELayer(spec, m.upload_layer(layer), max_tokens=chunk)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    outc = torch.zeros_like(out)
+
+    def chunked():
+        for c0 in range(0, n, chunk):
+            devc.forward(x[c0:c0 + chunk], outc[c0:c0 + chunk])
+
+    for _ in range(warmup):
+        chunked()
+    us = []
+    for c0 in range(0, n, chunk):
+        devc.forward(x[c0:c0 + chunk], outc[c0:c0 + chunk])
+        us.append(distinct_experts(devc.last_routing(chunk)[2]))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        chunked()
+    torch.cuda.synchronize()
+    wall_c = time.perf_counter() - t0
+    call_s = wall_c / steps / (n // chunk)
+    bytes_c = float(np.mean(us)) * nb["per_expert"] + nb["shared"]
+    gbs_c = bytes_c / call_s / 1e9
+    tf_c = layer_flop(spec, chunk) / call_s / 1e12
+    log(f"[bench] prefill {n} in {chunk}-token calls: {1e6 * call_s:.1f} us per call, {chunk / call_s:.0f} tok/s, "
+        f"{float(np.mean(us)):.1f} experts touched, {gbs_c:.0f} GB/s = {100 * gbs_c / HBM_PEAK_GBS:.1f}% of 8 TB/s, "
+        f"{tf_c:.0f} TFLOP/s")
+    devc.close()
+
     res = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16/bf16 MFMA, fp32 accumulate",
-        "data": "synthetic",
+        "steps": steps, "warmup": warmup, "ms_per_step": round(1000 * step_s, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16/fp16 MFMA, fp32 accumulate", "data": "synthetic",
         "config": {"workload": f"DS4-shape MoE layer prefill of {n} tokens in one call (n_embd 4096, n_ff 2048, "
                                "256 experts, top-6, 1 shared; IQ2-style gate/up, Q2_K-style down; seed 1)",
                    "global_batch": n, "seq_len": n, "parallelism": "none (1 GPU)",
-                   "layer_TFLOP_s": round(total_tf, 1), "layer_flop": sum(fl.values()),
+                   "layer_TFLOP_s": round(layer_tf, 1), "layer_flop": lf,
+                   "layer_mfma_frac": round(layer_tf / BF16_PEAK_TFLOPS, 4),
+                   "distinct_experts": u_one, "touched_expert_bytes": bytes_one,
+                   "layer_hbm_frac": round(bytes_one / step_s / 1e9 / HBM_PEAK_GBS, 4),
                    "per_kernel": per_kernel},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flop_per_launch": fl[dom], "avg_launch_us": per_kernel[dom]["avg_us"]},
+        "chunks_512": {"us_per_call": round(1e6 * call_s, 2), "tok_s": round(chunk / call_s, 1),
+                       "distinct_experts": round(float(np.mean(us)), 2), "touched_expert_bytes": round(bytes_c),
+                       "GB_s": round(gbs_c, 1), "hbm_frac": round(gbs_c / HBM_PEAK_GBS, 4),
+                       "TFLOP_s": round(tf_c, 1), "mfma_frac": round(tf_c / BF16_PEAK_TFLOPS, 4)},
     }
+    if cpu:
+        import oracle
+        ns = args.prefill_cpu_tokens
+        res["cpu_baseline"] = cpu_baseline(
+            lambda: oracle.forward(layer, x_np[:ns]), ns, lambda: oracle.forward(layer, x_np[:4]), 4, "tok/s",
+            f"oracle.forward on the first {ns} of the {n} prefill tokens in one call", "first 4 prefill tokens")
+        log(f"[bench] prefill cpu baseline: {res['cpu_baseline']}")
     dev.close()
     return res
 
@@ -282,7 +409,11 @@ def run_stack(args):
     """The layer stack: L DS4-shape layers with seeds 4000 + l, each RMSNorm
     (unit gain, eps 1e-6) -> MoE block -> residual add on an fp32 stream.
     Decode: 256 steps of one token through all layers.  Prefill: 4096 tokens
-    in 512-token chunks through all layers."""
+    in 512-token chunks through all layers.  After the timed runs, a
+    teacher-forced check: a few decode tokens run layer by layer, and for
+    every layer the oracle takes the GPU's own x_l and recomputes the routing
+    and the block output; its time is the CPU baseline."""
+    import numpy as np
     import torch
 
     import bit_quantized_moe_renorm_amd as m
@@ -290,12 +421,13 @@ def run_stack(args):
 
     spec = synth.DS4
     L, chunk, n_pre, n_dec = args.layers, 512, 4096, 256
-    devs = []
+    devs, hosts = [], []
     t0 = time.perf_counter()
     for l in range(L):
         lay = synth.make_layer(spec, seed=4000 + l)
         w = m.upload_layer(lay)
         devs.append(m.MoELayer(spec, w, max_tokens=chunk))
+        hosts.append(lay if not args.no_cpu_baseline else None)
         del w, lay
         torch.cuda.synchronize()
         log(f"[bench] stack: layer {l + 1}/{L} resident ({time.perf_counter() - t0:.0f} s)")
@@ -340,13 +472,15 @@ def run_stack(args):
     ev1.record(stream)
     torch.cuda.synchronize()
     pre_s = ev0.elapsed_time(ev1) * 1e-3
-    fl = sum(flops_prefill(spec, chunk).values()) * (n_pre // chunk) * L
+    fl = layer_flop(spec, chunk) * (n_pre // chunk) * L
     pre_tok_s = n_pre / pre_s
+    nb = synth.layer_nbytes(spec)
+    pre_bytes = L * (n_pre // chunk) * (spec.n_expert * nb["per_expert"] + nb["shared"])
     log(f"[bench] stack of {L} prefill {n_pre} in {chunk}-token chunks: {pre_tok_s:.0f} tok/s, "
-        f"{fl / pre_s / 1e12:.0f} TFLOP/s = {100 * fl / pre_s / 1e12 / BF16_PEAK_TFLOPS:.1f}% of bf16 peak")
-    for dev in devs:
-        dev.close()
-    return {
+        f"{fl / pre_s / 1e12:.0f} TFLOP/s = {100 * fl / pre_s / 1e12 / BF16_PEAK_TFLOPS:.1f}% of bf16 peak, "
+        f"{pre_bytes / pre_s / 1e9:.0f} GB/s = {100 * pre_bytes / pre_s / 1e9 / HBM_PEAK_GBS:.1f}% of 8 TB/s")
+
+    res = {
         "metric": METRIC, "value": round(dec_tok_s, 2), "unit": "tok/s", "n_gpus": 1,
         "steps": n_dec, "warmup": 8, "ms_per_step": round(1e3 * dec_s / n_dec, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -358,22 +492,68 @@ def run_stack(args):
                    "decode_layer_us": round(1e6 * dec_s / n_dec / L, 3),
                    "decode_hbm_GB_s": round(dec_gbs, 1), "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                    "prefill_tok_s": round(pre_tok_s, 1), "prefill_TFLOP_s": round(fl / pre_s / 1e12, 1),
-                   "prefill_mfma_frac": round(fl / pre_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "fused", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                   "prefill_mfma_frac": round(fl / pre_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+                   "prefill_hbm_GB_s": round(pre_bytes / pre_s / 1e9, 1),
+                   "prefill_hbm_frac": round(pre_bytes / pre_s / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "fused (decode, all layers)", "achieved": round(dec_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None},
     }
+    if not args.no_cpu_baseline:
+        import oracle
+        # teacher-forced: n_chk decode tokens layer by layer on the GPU, keeping
+        # every layer's x_l, block output and routing; the oracle recomputes
+        # each layer from the GPU's own x_l (its time is the CPU baseline)
+        n_chk = args.stack_check_tokens
+        hc = torch.from_numpy(synth.residual(45, n_chk, spec.n_embd)).cuda()
+        rec = []
+        for l, dev in enumerate(devs):
+            xs = m.rmsnorm(hc)
+            y = torch.zeros_like(hc)
+            idx = []
+            for t in range(n_chk):
+                dev.forward(xs[t:t + 1], y[t:t + 1])
+                idx.append(dev.last_routing(1)[0])
+            torch.cuda.synchronize()
+            rec.append((xs.view(torch.int16).cpu().numpy().view(np.uint16), y.cpu().numpy(),
+                        torch.cat(idx).cpu().numpy()))
+            hc = hc + y
+        worst, same = 0.0, 0
+
+        def check():
+            nonlocal worst, same
+            for l, (xl, yl, il) in enumerate(rec):
+                ref, ridx, _ = oracle.forward(hosts[l], xl)
+                d = np.max(np.abs(yl - ref)) / np.max(np.abs(ref))
+                worst = max(worst, float(d))
+                same += int(np.count_nonzero(np.all(il == ridx, axis=1)))
+
+        res["cpu_baseline"] = cpu_baseline(
+            check, n_chk, lambda: oracle.forward(hosts[0], rec[0][0][:1]), 1.0 / L, "tok/s",
+            f"oracle.forward on {n_chk} decode tokens through all {L} layers, teacher-forced on the GPU's x_l",
+            "one token through layer 0 (tok/s through the whole stack = this / layers)")
+        res["config"]["teacher_forced_check"] = {
+            "tokens": n_chk, "layers": L, "routing_equal": f"{same}/{n_chk * L}",
+            "max_rel_err_block_output": worst, "tolerance": 2e-3}
+        log(f"[bench] stack teacher-forced check: routing equal {same}/{n_chk * L}, worst block-output rel err "
+            f"{worst:.3e}; cpu baseline {res['cpu_baseline']}")
+    for dev in devs:
+        dev.close()
+    return res
 
 
 def run_batch(args):
-    """Small-batch decode (n = 8, 16, 32 tokens per call) of the DS4-shape layer
-    under a Zipf(1.1)-biased router, 8 layer replicas cycled so the weights
-    come from HBM.  Bytes per call: the distinct routed experts the call
-    touches (counted from its own routing) times an expert's bytes, plus the
-    shared expert and the router."""
+    """Small-batch decode (n = 2, 7, 8, 16, 32 tokens per call; 2 and 7 are
+    speculative verification shapes, the last token plus k = 1 or 6 drafted
+    ones) of the DS4-shape layer under a Zipf(1.1)-biased router, 8 layer
+    replicas cycled so the weights come from HBM.  Bytes per call: the
+    distinct routed experts the call touches (counted from its own routing)
+    times an expert's bytes, plus the shared expert."""
     import numpy as np
     import torch
 
     import bit_quantized_moe_renorm_amd as m
+    import oracle
     from bit_quantized_moe_renorm_amd import synth
 
     spec = synth.DS4
@@ -384,18 +564,17 @@ def run_batch(args):
         devs.append(m.MoELayer(spec, w, max_tokens=64))
         del w
     nb = synth.layer_nbytes(spec)
-    router_bytes = spec.n_expert * spec.n_embd * 4
     steps = 200
-    x = m.to_device_x(synth.activations(2, 32 * (steps + 8), spec.n_embd))
+    x_np = synth.activations(2, 32 * (steps + 8), spec.n_embd)
+    x = m.to_device_x(x_np)
     out = torch.zeros((32, spec.n_embd), dtype=torch.float32, device="cuda")
     rows = {}
-    for n in (8, 16, 32):
+    for n in (2, 7, 8, 16, 32):
         # distinct experts per call, from the library's own routing of the same tokens
         uniq = []
         for it in range(steps):
             _, _, off, _ = devs[0].route(x[n * it:n * it + n])
-            o = off.cpu().numpy()
-            uniq.append(int(np.count_nonzero(o[1:] - o[:-1])))
+            uniq.append(distinct_experts(off))
         for it in range(8):
             devs[it % len(devs)].forward(x[n * it:n * it + n], out[:n])
         torch.cuda.synchronize()
@@ -405,25 +584,34 @@ def run_batch(args):
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / steps
         u = float(np.mean(uniq))
-        gbs = (u * nb["per_expert"] + nb["shared"] + router_bytes) / dt / 1e9
-        rows[n] = {"us_per_call": round(dt * 1e6, 2), "tok_s": round(n / dt, 1), "distinct_experts": round(u, 2),
-                   "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        gbs = (u * nb["per_expert"] + nb["shared"]) / dt / 1e9
+        row = {"us_per_call": round(dt * 1e6, 2), "tok_s": round(n / dt, 1), "distinct_experts": round(u, 2),
+               "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if not args.no_cpu_baseline:
+            row["cpu_baseline"] = cpu_baseline(
+                lambda: oracle.forward(lay, x_np[:n]), n, lambda: oracle.forward(lay, x_np[:1]), 1, "tok/s",
+                f"oracle.forward on one call of {n} tokens (the first of the stream)", "one token")
+        rows[n] = row
         log(f"[bench] batch {n}: {dt * 1e6:.1f} us per call, {n / dt:.0f} tok/s, {u:.1f} distinct experts, "
             f"{gbs:.0f} GB/s = {100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s")
     for d in devs:
         d.close()
     r32 = rows[32]
-    return {
+    res = {
         "metric": METRIC, "value": r32["tok_s"], "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": 8,
         "ms_per_step": round(r32["us_per_call"] / 1000, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "DS4-shape MoE layer, small-batch decode of 8/16/32 tokens per call under a "
-                               "Zipf(1.1) router bias (seed 1; value = 32 tokens)", "global_batch": 32,
+        "config": {"workload": "DS4-shape MoE layer, small-batch decode of 2/7/8/16/32 tokens per call under a "
+                               "Zipf(1.1) router bias (seed 1; value = 32 tokens; 2 and 7 = MTP verification "
+                               "of k = 1 and 6 drafts)", "global_batch": 32,
                    "seq_len": 1, "parallelism": "none (1 GPU)", "replicas": args.replicas,
                    "per_batch": {str(k): v for k, v in rows.items()}},
         "roofline": {"bound": "hbm", "kernel": "whole call", "achieved": r32["GB_s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": r32["hbm_frac"], "traffic": None},
     }
+    if "cpu_baseline" in r32:
+        res["cpu_baseline"] = r32["cpu_baseline"]
+    return res
 
 
 def copy_probe():
@@ -446,9 +634,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="decode only (skip the nested prefill)")
     ap.add_argument("--workload", choices=("decode", "prefill", "stack", "batch"), default="decode")
     ap.add_argument("--layers", type=int, default=43, help="stack workload: number of layers")
     ap.add_argument("--tokens", type=int, default=2048, help="prefill tokens per call")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-warmup", type=int, default=3)
+    ap.add_argument("--prefill-cpu-tokens", type=int, default=256,
+                    help="prefill tokens the oracle runs for the CPU baseline")
+    ap.add_argument("--stack-check-tokens", type=int, default=2,
+                    help="decode tokens of the stack's teacher-forced check (and CPU baseline)")
     ap.add_argument("--copy-probe", action="store_true", help="only run the counter-calibration copy")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -463,15 +658,19 @@ def main():
         copy_probe()
         return
     if args.workload == "prefill":
-        if args.steps == 1000 and args.warmup == 100:   # defaults sized for decode
-            args.steps, args.warmup = 50, 5
-        res = run_prefill(args)
+        res = run_prefill(args, cpu=not args.no_cpu_baseline)
     elif args.workload == "stack":
         res = run_stack(args)
     elif args.workload == "batch":
         res = run_batch(args)
     else:
-        res = run_decode(args)
+        from bit_quantized_moe_renorm_amd import synth
+        layer = synth.make_layer(synth.DS4, seed=1)
+        res = run_decode(args, layer)
+        if not args.no_prefill:
+            pre = run_prefill(args, layer, cpu=not args.no_cpu_baseline)
+            res["prefill"] = {k: pre[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "dtype",
+                                                  "config", "roofline", "chunks_512", "cpu_baseline") if k in pre}
     print(json.dumps(res), flush=True)
 
 

@@ -25,6 +25,7 @@ TIMING_KINDS = ("route", "gateup_routed", "gateup_shared", "down_routed", "down_
 
 SYMBOLS = ("ds4moe_create", "ds4moe_route", "ds4moe_forward", "ds4moe_set_path", "ds4moe_dequantize",
            "ds4moe_rmsnorm", "ds4moe_forward_stack", "ds4moe_timing_enable", "ds4moe_timing_read",
+           "ds4moe_last_routing", "ds4moe_status", "ds4moe_set_wait_limit",
            "ds4moe_destroy", "ds4moe_last_error")
 
 
@@ -68,6 +69,9 @@ def load_library(path: Optional[Path] = None) -> ctypes.CDLL:
     L.ds4moe_forward_stack.argtypes = [P, i32, P, i32, ctypes.c_double, P, P]
     L.ds4moe_timing_enable.argtypes = [P, i32]
     L.ds4moe_timing_read.argtypes = [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.ds4moe_last_routing.argtypes = [P, i32, P, P, P, P, P]
+    L.ds4moe_status.argtypes = [P]
+    L.ds4moe_set_wait_limit.argtypes = [P, i32, i32]
     L.ds4moe_destroy.argtypes = [P]
     L.ds4moe_last_error.restype = ctypes.c_char_p
     for name in SYMBOLS:
@@ -91,6 +95,23 @@ def _stream(stream=None):
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def _check_tensor(name, t, dtype, shape, device=None):
+    """Raise before a raw pointer crosses the ABI: the library trusts sizes."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
 
 
 class MoELayer:
@@ -133,23 +154,58 @@ class MoELayer:
     def set_path(self, path: int):
         _check(load_library().ds4moe_set_path(self.h, path))
 
+    def _x_dtype(self):
+        import torch
+        return torch.bfloat16 if self.act_dtype == BF16 else torch.float32
+
+    def _check_x(self, x):
+        import torch
+        if not isinstance(x, torch.Tensor) or x.dim() != 2:
+            raise ValueError("x: expected a 2-D torch tensor [n_tok, n_embd]")
+        _check_tensor("x", x, self._x_dtype(), (x.shape[0], self.spec.n_embd))
+        return x.shape[0]
+
     def forward(self, x, out, stream=None):
-        """out += MoE(x) (x [n, E] bf16/fp32, out [n, E] fp32, both on the GPU)."""
-        n = x.shape[0]
+        """out += MoE(x) (x [n, E] of the handle's activation dtype, out [n, E] fp32, both on the GPU)."""
+        import torch
+        n = self._check_x(x)
+        _check_tensor("out", out, torch.float32, (n, self.spec.n_embd), x.device)
         _check(load_library().ds4moe_forward(self.h, _ptr(x), n, _ptr(out), _stream(stream)))
 
-    def route(self, x, stream=None):
-        """Returns (idx int32 [n,k], w fp32 [n,k], offsets int32 [NE+1], tokens int32 [n*k])."""
+    def _routing_buffers(self, n, dev):
         import torch
-        n, k, NE = x.shape[0], self.spec.top_k, self.spec.n_expert
-        dev = x.device
+        k, NE = self.spec.top_k, self.spec.n_expert
         idx = torch.empty((n, k), dtype=torch.int32, device=dev)
         w = torch.empty((n, k), dtype=torch.float32, device=dev)
         off = torch.empty((NE + 1,), dtype=torch.int32, device=dev)
         tok = torch.empty((max(n * k, 1),), dtype=torch.int32, device=dev)
+        return idx, w, off, tok
+
+    def route(self, x, stream=None):
+        """Returns (idx int32 [n,k], w fp32 [n,k], offsets int32 [NE+1], tokens int32 [n*k])."""
+        n = self._check_x(x)
+        idx, w, off, tok = self._routing_buffers(n, x.device)
         _check(load_library().ds4moe_route(self.h, _ptr(x), n, _ptr(idx), _ptr(w), _ptr(off), _ptr(tok),
                                            _stream(stream)))
-        return idx, w, off, tok[: n * k]
+        return idx, w, off, tok[: n * self.spec.top_k]
+
+    def last_routing(self, n, stream=None):
+        """The routing of the latest forward/route call on this layer (n = its token count),
+        as (idx, w, offsets, tokens) like ``route``."""
+        import torch
+        idx, w, off, tok = self._routing_buffers(n, torch.device("cuda", torch.cuda.current_device()))
+        _check(load_library().ds4moe_last_routing(self.h, n, _ptr(idx), _ptr(w), _ptr(off), _ptr(tok),
+                                                  _stream(stream)))
+        return idx, w, off, tok[: n * self.spec.top_k]
+
+    def status(self) -> int:
+        """OK, or EPOISONED once a bounded wait of an earlier call gave up (no synchronisation)."""
+        return load_library().ds4moe_status(self.h)
+
+    def set_wait_limit(self, max_polls: int, force_expire: bool = False):
+        """Test hook: polls before a bounded wait gives up (0 = default); force_expire makes
+        every wait give up."""
+        _check(load_library().ds4moe_set_wait_limit(self.h, max_polls, 1 if force_expire else 0))
 
     def dequantize(self, expert: int, which: int, stream=None):
         """fp32 matrix decoded from the library's repacked layout (0 gate, 1 up, 2 down)."""
@@ -174,8 +230,10 @@ def rmsnorm(h, eps: float = 1e-6, out=None, stream=None):
     """bf16 RMSNorm (unit gain) of fp32 h [n, E] on the GPU."""
     import torch
     n, E = h.shape
+    _check_tensor("h", h, torch.float32, (n, E))
     if out is None:
         out = torch.empty((n, E), dtype=torch.bfloat16, device=h.device)
+    _check_tensor("out", out, torch.bfloat16, (n, E), h.device)
     _check(load_library().ds4moe_rmsnorm(_ptr(h), n, E, eps, _ptr(out), _stream(stream)))
     return out
 
@@ -186,8 +244,10 @@ def forward_stack(layers, h, eps: float = 1e-6, x=None, stream=None):
     bf16 [n, E] scratch).  Returns h."""
     import torch
     n, E = h.shape
+    _check_tensor("h", h, torch.float32, (n, E))
     if x is None:
         x = torch.empty((n, E), dtype=torch.bfloat16, device=h.device)
+    _check_tensor("x", x, torch.bfloat16, (n, E), h.device)
     # a closed layer passes NULL, which the library rejects (DS4MOE_EINVAL)
     hs = (ctypes.c_void_p * len(layers))(*[lay.h.value if lay.h else None for lay in layers])
     _check(load_library().ds4moe_forward_stack(hs, len(layers), _ptr(h), n, eps, _ptr(x), _stream(stream)))

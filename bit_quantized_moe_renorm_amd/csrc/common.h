@@ -68,7 +68,22 @@ struct Work {
     unsigned long long *itag;  // [64][MAX_TOPK] small-batch router: selected expert under the call's tag
     unsigned long long *htag;  // [k+1][F] fused decode: SwiGLU outputs of the routed slots and the
                                // shared expert (fp32 bits), each tagged like rtag
+    // Bounded waits.  A wait that gives up stores its call's tag into *status,
+    // a host-visible word (pinned host memory mapped into the device address
+    // space), so the host sees the failure at its next call without
+    // synchronising.  Consumers wait for (producer tag) ^ want_xor: 0 in normal
+    // use; a nonzero value (set only by the test hook) makes every wait expire.
+    uint32_t *status;
+    int spin_limit;       // polls before a wait gives up
+    uint32_t want_xor;
 };
+
+constexpr int DEFAULT_SPIN_LIMIT = 1 << 20;  // about a second of polling
+
+// A bounded wait expired during the call tagged `tag`: record it for the host.
+__device__ __forceinline__ void report_wait_expired(const Work &W, uint32_t tag) {
+    __hip_atomic_store(W.status, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 
 // ---------------------------------------------------------------- small device helpers
 // Weights are read once per call: non-temporal loads (streaming cache

@@ -49,6 +49,8 @@ struct ds4moe {
     unsigned long long route_calls = 0;   // routing launches so far (the router hand-off tag)
     bool poisoned = false;
     int device = 0;
+    int32_t last_n_tok = -1;              // n_tok of the latest forward/route call (its routing is in W)
+    uint32_t *status_host = nullptr;      // pinned, mapped: nonzero = a bounded wait expired (that call's tag)
     std::vector<void *> allocs;
     // timing
     bool timing = false;
@@ -59,8 +61,9 @@ struct ds4moe {
     int64_t counts[TIMING_SLOTS] = {};
 
     ~ds4moe() {
-        for (void *p : allocs) hipFree(p);
-        for (hipEvent_t e : events) hipEventDestroy(e);
+        for (void *p : allocs) (void)hipFree(p);
+        for (hipEvent_t e : events) (void)hipEventDestroy(e);
+        if (status_host) (void)hipHostFree(status_host);
     }
     void *alloc(size_t bytes, hipError_t &err) {
         void *p = nullptr;
@@ -194,6 +197,21 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     W.htag = (unsigned long long *)(ws + o_htag);
     W.ltag = (unsigned long long *)(ws + o_ltag);
     W.itag = (unsigned long long *)(ws + o_itag);
+    // the host-visible status word of the bounded waits
+    if (hipHostMalloc((void **)&h->status_host, 256, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess) {
+        h->status_host = nullptr;
+        delete h;
+        hipGetLastError();
+        return fail(DS4MOE_ENOMEM, "create: pinned status word");
+    }
+    *(volatile uint32_t *)h->status_host = 0u;
+    if (hipHostGetDevicePointer((void **)&W.status, h->status_host, 0) != hipSuccess) {
+        delete h;
+        hipGetLastError();
+        return fail(DS4MOE_EHIP, "create: device address of the status word");
+    }
+    W.spin_limit = DEFAULT_SPIN_LIMIT;
+    W.want_xor = 0u;
 
 #define CK(call)                                                                                      \
     do {                                                                                              \
@@ -246,12 +264,42 @@ int ds4moe_set_path(ds4moe_t *h, int32_t path) {
     return DS4MOE_OK;
 }
 
+// A bounded wait of an earlier call gave up (its kernel recorded the call's
+// tag in the handle's host-visible status word): the handle is poisoned.
+static int poll_status(ds4moe *h, const char *what) {
+    if (h->poisoned) return fail(DS4MOE_EPOISONED, "%s: handle poisoned by an earlier error", what);
+    const uint32_t st = *(volatile const uint32_t *)h->status_host;
+    if (st) {
+        h->poisoned = true;
+        return fail(DS4MOE_EPOISONED, "%s: a bounded wait of an earlier call (tag %u) expired; handle poisoned",
+                    what, st);
+    }
+    return DS4MOE_OK;
+}
+
+// The hand-off tags come from host-side call counts, so a captured graph
+// would replay one call's tags: capture is refused.
+static int stream_checks(hipStream_t s, const char *what) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+        hipGetLastError();
+        return fail(DS4MOE_EINVAL, "%s: invalid stream", what);
+    }
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(DS4MOE_EUNSUPPORTED, "%s: the stream is being captured into a graph (not supported)", what);
+    return DS4MOE_OK;
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
 static int common_checks(ds4moe *h, const void *x, int32_t n_tok, const char *what) {
     if (!h) return fail(DS4MOE_EINVAL, "%s: NULL handle", what);
-    if (h->poisoned) return fail(DS4MOE_EPOISONED, "%s: handle poisoned by an earlier HIP error", what);
+    int rc = poll_status(h, what);
+    if (rc) return rc;
     if (n_tok < 0 || n_tok > h->L.max_tokens)
         return fail(DS4MOE_EINVAL, "%s: n_tok %d not in 0..max_tokens (%d)", what, n_tok, h->L.max_tokens);
     if (n_tok > 0 && !x) return fail(DS4MOE_EINVAL, "%s: NULL x", what);
+    if (n_tok > 0 && !aligned16(x)) return fail(DS4MOE_EINVAL, "%s: x is not 16-byte aligned", what);
     return DS4MOE_OK;
 }
 
@@ -263,6 +311,8 @@ int ds4moe_route(ds4moe_t *h, const void *x, int32_t n_tok, int32_t *topk_idx, f
         return fail(DS4MOE_EINVAL, "route: NULL output");
     if (n_tok == 0) return DS4MOE_OK;
     hipStream_t s = (hipStream_t)stream;
+    if ((rc = stream_checks(s, "route"))) return rc;
+    h->last_n_tok = n_tok;
     int tb = h->tbegin(TK_ROUTE, s);
     rc = check_launch(h, launch_route(h->L, h->W, x, n_tok, s, h->route_calls++), "route");
     h->tend(tb, s);
@@ -275,7 +325,9 @@ int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *
     int rc = common_checks(h, x, n_tok, "forward");
     if (rc) return rc;
     if (n_tok > 0 && !out) return fail(DS4MOE_EINVAL, "forward: NULL out");
+    if (n_tok > 0 && !aligned16(out)) return fail(DS4MOE_EINVAL, "forward: out is not 16-byte aligned");
     if (n_tok == 0) return DS4MOE_OK;
+    if ((rc = stream_checks((hipStream_t)stream, "forward"))) return rc;
     int path = h->path;
     // one token: the fused decode kernel; more: the grouped GEMMs, which at 2-4
     // tokens (K split over more workgroups) also beat the GEMV kernels.  fp32
@@ -289,6 +341,7 @@ int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *
     if (path == DS4MOE_PATH_GEMM && !gemm_available())
         return fail(DS4MOE_EUNSUPPORTED, "forward: the grouped GEMM path is not available in this build");
     hipStream_t s = (hipStream_t)stream;
+    h->last_n_tok = n_tok;
     if (path == DS4MOE_PATH_GEMV && n_tok == 1) {
         // the whole block for one token in one persistent launch
         int tf = h->tbegin(TK_FUSED, s);
@@ -377,6 +430,8 @@ int ds4moe_forward_stack(ds4moe_t *const *layers, int32_t n_layers, float *h, in
     if (!layers || n_layers < 1) return fail(DS4MOE_EINVAL, "forward_stack: no layers");
     if (n_tok < 0 || !(eps >= 0.0)) return fail(DS4MOE_EINVAL, "forward_stack: n_tok %d, eps %g", n_tok, eps);
     if (n_tok > 0 && (!h || !x_bf16)) return fail(DS4MOE_EINVAL, "forward_stack: NULL h or x");
+    if (n_tok > 0 && (!aligned16(h) || !aligned16(x_bf16)))
+        return fail(DS4MOE_EINVAL, "forward_stack: h or x is not 16-byte aligned");
     // every layer is checked before anything is enqueued
     for (int l = 0; l < n_layers; ++l) {
         ds4moe *d = layers[l];
@@ -389,6 +444,10 @@ int ds4moe_forward_stack(ds4moe_t *const *layers, int32_t n_layers, float *h, in
                         layers[0]->L.n_embd);
     }
     if (n_tok == 0) return DS4MOE_OK;
+    {
+        int rc = stream_checks((hipStream_t)stream, "forward_stack");
+        if (rc) return rc;
+    }
     const int E = layers[0]->L.n_embd;
     for (int l = 0; l < n_layers; ++l) {
         hipError_t e = launch_rmsnorm(h, n_tok, E, eps, x_bf16, (hipStream_t)stream);
@@ -396,6 +455,35 @@ int ds4moe_forward_stack(ds4moe_t *const *layers, int32_t n_layers, float *h, in
         int rc = ds4moe_forward(layers[l], x_bf16, n_tok, h, stream);
         if (rc) return fail(rc, "forward_stack: layer %d: %s", l, g_err.c_str());
     }
+    return DS4MOE_OK;
+}
+
+int ds4moe_last_routing(ds4moe_t *h, int32_t n_tok, int32_t *topk_idx, float *topk_w, int32_t *expert_offsets,
+                        int32_t *expert_tokens, void *stream) {
+    if (!h) return fail(DS4MOE_EINVAL, "last_routing: NULL handle");
+    int rc = poll_status(h, "last_routing");
+    if (rc) return rc;
+    if (h->last_n_tok < 1 || n_tok != h->last_n_tok)
+        return fail(DS4MOE_EINVAL, "last_routing: n_tok %d, the latest forward/route call had %d", n_tok,
+                    h->last_n_tok);
+    if (!topk_idx || !topk_w || !expert_offsets || !expert_tokens)
+        return fail(DS4MOE_EINVAL, "last_routing: NULL output");
+    hipStream_t s = (hipStream_t)stream;
+    if ((rc = stream_checks(s, "last_routing"))) return rc;
+    return check_launch(h, launch_route_export(h->L, h->W, n_tok, topk_idx, topk_w, expert_offsets, expert_tokens, s),
+                        "last_routing export");
+}
+
+int ds4moe_status(ds4moe_t *h) {
+    if (!h) return fail(DS4MOE_EINVAL, "status: NULL handle");
+    return poll_status(h, "status");
+}
+
+int ds4moe_set_wait_limit(ds4moe_t *h, int32_t max_polls, int32_t force_expire) {
+    if (!h) return fail(DS4MOE_EINVAL, "set_wait_limit: NULL handle");
+    if (max_polls < 0) return fail(DS4MOE_EINVAL, "set_wait_limit: max_polls %d", max_polls);
+    h->W.spin_limit = max_polls ? max_polls : DEFAULT_SPIN_LIMIT;
+    h->W.want_xor = force_expire ? 0x80000000u : 0u;
     return DS4MOE_OK;
 }
 

@@ -58,17 +58,23 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // stored and polled at agent scope.  A word is seen whole or not at all, so a
 // consumer that finds the tag has the value: no fences (which would write
 // back and invalidate the L2) and nothing to reset.
-constexpr int RT_SPIN = 1 << 20;  // polls of one word before giving up (about a second)
 __device__ __forceinline__ unsigned long long rt_poll(const unsigned long long *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void rt_put(unsigned long long *p, uint32_t tag, uint32_t v) {
     __hip_atomic_store(p, ((unsigned long long)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Waits until word p carries the tag (bounded); false if the wait expired.
-__device__ __forceinline__ bool rt_wait(const unsigned long long *p, uint32_t tag, unsigned long long &v) {
-    for (int spins = 0; (uint32_t)(v >> 32) != tag; ++spins) {
-        if (spins > RT_SPIN) return false;
+// Waits until word p carries the call's tag (bounded: W.spin_limit polls);
+// false, with the call's tag recorded in the host-visible status word, if the
+// wait expired.
+__device__ __forceinline__ bool rt_wait(const Work &W, const unsigned long long *p, uint32_t tag,
+                                        unsigned long long &v) {
+    const uint32_t want = tag ^ W.want_xor;
+    for (int spins = 0; (uint32_t)(v >> 32) != want; ++spins) {
+        if (spins > W.spin_limit) {
+            report_wait_expired(W, tag);
+            return false;
+        }
         __builtin_amdgcn_s_sleep(2);
         v = rt_poll(p);
     }
@@ -78,15 +84,16 @@ __device__ __forceinline__ bool rt_wait(const unsigned long long *p, uint32_t ta
 // Top-k + renormalised weights for token t, by one wavefront, from the tagged
 // logits of this call; the selection also goes to the tagged itag words.  An
 // expired wait poisons the token's weights with NaN.
-__device__ void topk_tagged(const unsigned long long *__restrict__ ltag, int t, int NE, int k, uint32_t tag,
-                            int32_t *__restrict__ idx, float *__restrict__ w, unsigned long long *__restrict__ itag) {
+__device__ void topk_tagged(const Work &W, const unsigned long long *__restrict__ ltag, int t, int NE, int k,
+                            uint32_t tag, int32_t *__restrict__ idx, float *__restrict__ w,
+                            unsigned long long *__restrict__ itag) {
     const int lane = threadIdx.x & 63;
     unsigned long long v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = rt_poll(ltag + (int64_t)t * MAX_EXPERT + min(lane + 64 * i, NE - 1));
     bool ok = true;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ok &= rt_wait(ltag + (int64_t)t * MAX_EXPERT + min(lane + 64 * i, NE - 1), tag, v[i]);
+    for (int i = 0; i < 4; ++i) ok &= rt_wait(W, ltag + (int64_t)t * MAX_EXPERT + min(lane + 64 * i, NE - 1), tag, v[i]);
     uint64_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -177,7 +184,7 @@ __device__ void bucket_small(const unsigned long long *__restrict__ itag, uint32
     for (int q = tid; q < nq; q += 256) {
         const unsigned long long *p = itag + (int64_t)(q / k) * MAX_TOPK + q % k;
         unsigned long long v = rt_poll(p);
-        sidx[q] = rt_wait(p, tag, v) ? (int)(uint32_t)v : 0;  // an expired wait already poisoned the weights
+        sidx[q] = rt_wait(W, p, tag, v) ? (int)(uint32_t)v : 0;  // an expired wait already poisoned the weights
     }
     cnt[tid] = 0;
     __syncthreads();
@@ -289,7 +296,7 @@ __global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ 
     if (threadIdx.x == 0) last = atomicAdd(&W.counters[1 + blockIdx.y], 1) == (int)gridDim.x - 1;
     __syncthreads();
     if (!last) return;
-    for (int t = t0 + wave; t < t0 + nt; t += RT_WAVES) topk_tagged(W.ltag, t, NE, k, tag, W.idx, W.w, W.itag);
+    for (int t = t0 + wave; t < t0 + nt; t += RT_WAVES) topk_tagged(W, W.ltag, t, NE, k, tag, W.idx, W.w, W.itag);
     __syncthreads();
     if (threadIdx.x == 0) {
         W.counters[1 + blockIdx.y] = 0;

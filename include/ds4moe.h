@@ -41,11 +41,21 @@
  * Arguments are validated before anything is enqueued; on a validation error
  * nothing is enqueued and ds4moe_last_error() describes it.  A HIP error
  * reported by a launch returns DS4MOE_EHIP and poisons the handle: later
- * calls on it return DS4MOE_EPOISONED.  No C++ exception crosses the ABI.
+ * calls on it return DS4MOE_EPOISONED.  Kernels that hand data between
+ * workgroups bound every wait; a wait that gives up writes NaN into the
+ * call's output and records the call in a host-visible status word of the
+ * handle, so the next call on the handle (or ds4moe_status) returns
+ * DS4MOE_EPOISONED without any host synchronisation.  No C++ exception
+ * crosses the ABI.
  *
  * Threading.  One handle serves one stream of calls at a time: calls on the
  * same handle must not overlap (they share the handle's workspace).  Distinct
  * handles are independent.
+ *
+ * Graph capture.  The hand-offs between workgroups are tagged with host-side
+ * call counts, which a captured graph would replay unchanged: route, forward,
+ * forward_stack and last_routing refuse a stream that is being captured
+ * (DS4MOE_EUNSUPPORTED, nothing enqueued).
  */
 #ifndef DS4MOE_H
 #define DS4MOE_H
@@ -109,7 +119,10 @@ typedef struct {
 } ds4moe_desc;
 
 /*
- * Create a layer handle.  Reads the caller's weights on `stream`, repacks the
+ * Create a layer handle: one routed-MoE layer with 256 (n_expert) routed
+ * experts, top-k routing and one shared expert ("Redis 作者出手！ds4...",
+ * section 2.1, the model constants; section 2.3, the two 2-bit block formats
+ * and the high-precision shared expert).  Reads the caller's weights on `stream`, repacks the
  * routed experts into the library's own device layout (same bytes per weight,
  * planes aligned for 128-bit loads), copies the router and shared expert,
  * allocates the workspace for max_tokens, synchronises `stream` and returns.
@@ -120,7 +133,11 @@ int ds4moe_create(const ds4moe_desc *desc, void *stream, ds4moe_t **out);
 
 /*
  * Router and token bucketing only (the front of ds4moe_forward), with the
- * results exposed.  x: device [n_tok][n_embd] of act_dtype.  Outputs, device:
+ * results exposed.  The router scores every expert and only the chosen ones
+ * are computed ("ds4 深度实战...", section 3.2 "MoE FFN"; section 3.3: experts
+ * are scheduled from the router's output); 6 of 256 per token ("Redis 作者出
+ * 手！ds4...", section 2.1).  The gating is softmax, top-k and renormalisation
+ * over the selected experts.  x: device [n_tok][n_embd] of act_dtype.  Outputs, device:
  *   topk_idx [n_tok][top_k] int32: selected experts, slot order = decreasing
  *            logit, lower index first among equal logits;
  *   topk_w   [n_tok][top_k] fp32: softmax probabilities renormalised over the
@@ -135,6 +152,9 @@ int ds4moe_route(ds4moe_t *h, const void *x, int32_t n_tok, int32_t *topk_idx, f
                  int32_t *expert_offsets, int32_t *expert_tokens, void *stream);
 
 /*
+ * The block ("ds4 深度实战...", section 3.2 "MoE FFN": route, compute only the
+ * chosen experts and the shared expert, merge their outputs; section 2.1: the
+ * routed gate/up in IQ2_XXS, down in Q2_K, shared expert at full precision).
  * out += MoE(x): x device [n_tok][n_embd] of act_dtype; out device fp32
  * [n_tok][n_embd], read and written (pass zeros for the bare block output).
  * 0 <= n_tok <= max_tokens; n_tok == 0 is a no-op.  x and out must not overlap;
@@ -148,13 +168,16 @@ int ds4moe_set_path(ds4moe_t *h, int32_t path);
 
 /*
  * Debug/test: decode one routed expert matrix from the library's repacked
- * layout.  which: 0 gate, 1 up ([n_ff][n_embd] fp32), 2 down ([n_embd][n_ff]
+ * layout ("Redis 作者出手！ds4...", section 2.3: block_iq2_xxs for gate/up,
+ * block_q2_K for down, each 256 weights per super-block).  which: 0 gate, 1 up ([n_ff][n_embd] fp32), 2 down ([n_embd][n_ff]
  * fp32).  dst: device, fp32, that many elements.
  */
 int ds4moe_dequantize(ds4moe_t *h, int32_t expert, int32_t which, float *dst, void *stream);
 
 /*
- * RMSNorm with unit gain between stacked layers:
+ * RMSNorm with unit gain between stacked layers (the stack of 43 layers,
+ * "Redis 作者出手！ds4...", section 2.1; the pages' model mixes layers through
+ * hyper-connections instead, which this block leaves out):
  *   x_bf16[t][i] = bf16_rne( h[t][i] / sqrt(mean_i h[t][i]^2 + eps) )
  * computed in fp64.  h: device fp32 [n_tok][n_embd]; x_bf16: device bf16 bits.
  * n_tok >= 0, 1 <= n_embd <= 65536, eps >= 0.
@@ -195,6 +218,34 @@ int ds4moe_forward_stack(ds4moe_t *const *layers, int32_t n_layers, float *h, in
 #define DS4MOE_TIMING_KINDS 11
 int ds4moe_timing_enable(ds4moe_t *h, int32_t enable);
 int ds4moe_timing_read(ds4moe_t *h, double *ms, int64_t *counts);
+
+/*
+ * The routing that the most recent ds4moe_forward or ds4moe_route call on h
+ * computed (for a one-token forward, the fused decode kernel's own top-k),
+ * copied into the caller's device buffers with the layouts of ds4moe_route.
+ * n_tok must equal that call's n_tok (EINVAL otherwise).  Stream-ordered
+ * after that call.  The same selection rule as ds4moe_route ("ds4 深度实战...",
+ * section 3.2).
+ */
+int ds4moe_last_routing(ds4moe_t *h, int32_t n_tok, int32_t *topk_idx, float *topk_w, int32_t *expert_offsets,
+                        int32_t *expert_tokens, void *stream);
+
+/*
+ * DS4MOE_OK, or DS4MOE_EPOISONED (the handle is then poisoned) if a bounded
+ * wait of an earlier call on h gave up or a HIP error poisoned it.  Reads the
+ * host-visible status word only: synchronise the stream first for a
+ * definitive answer about calls still in flight.
+ */
+int ds4moe_status(ds4moe_t *h);
+
+/*
+ * Test hook for the bounded waits of h's kernels: max_polls is the number of
+ * polls before a wait gives up (0 restores the default, about a second), and
+ * force_expire != 0 makes every wait look for a tag that no producer writes,
+ * so every wait gives up after max_polls polls while every kernel still runs
+ * to its end.  Host-only.
+ */
+int ds4moe_set_wait_limit(ds4moe_t *h, int32_t max_polls, int32_t force_expire);
 
 /* Free everything the handle owns (after the caller's stream work is done).  NULL is a no-op. */
 int ds4moe_destroy(ds4moe_t *h);

@@ -50,6 +50,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_forward.restype = i32
         L.oracle_rmsnorm.argtypes = [P, i64, i32, f64, P, P]
         L.oracle_num_threads.restype = i32
+        L.oracle_set_num_threads.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -60,6 +61,11 @@ def _p(a):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for later calls (results do not depend on it)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def dequant_iq2(blocks: np.ndarray, codebook: np.ndarray) -> np.ndarray:

@@ -493,3 +493,15 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Set the number of OpenMP threads for later calls (timing only: the results
+ * do not depend on it). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

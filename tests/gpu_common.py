@@ -47,6 +47,16 @@ def host_layer(kind: str):
         r[1::2] = r[0::2]
         lay.router = r
         return lay
+    if kind == "ds4_ties_half":
+        # router rows 4j+1 copy rows 4j: half the experts have an exact twin, so
+        # the k-th / (k+1)-th boundary often falls between two equal logits
+        # (whose experts have different weights)
+        base = host_layer("ds4")
+        lay = synth.Layer(**{**base.__dict__})
+        r = base.router.copy()
+        r[1::4] = r[0::4]
+        lay.router = r
+        return lay
     if kind == "ds4_zipf":
         base = host_layer("ds4")
         lay = synth.Layer(**{**base.__dict__})
@@ -70,3 +80,22 @@ def device_layer(kind: str, max_tokens: int = 64):
         _dev[key] = m.MoELayer(lay.spec, w, max_tokens=max_tokens, act_dtype=act)
         del w
     return _dev[key]
+
+
+def tie_split_tokens(kind: str, x_np, want: int):
+    """Indices of tokens (up to ``want``) whose oracle top-k boundary falls
+    between two experts with exactly equal fp32 logits: the k-th selected
+    expert has a twin outside the selection, so only the lower-index rule
+    decides which of the two is taken."""
+    import oracle
+    lay = host_layer(kind)
+    lg, idx, _, _ = oracle.route(x_np, lay.router, lay.router_bias, lay.spec.top_k)
+    out = []
+    for t in range(len(x_np)):
+        last = idx[t, -1]
+        twins = np.nonzero(lg[t] == lg[t, last])[0]
+        if any(e not in idx[t] for e in twins):
+            out.append(t)
+        if len(out) == want:
+            break
+    return np.array(out, dtype=np.int64)

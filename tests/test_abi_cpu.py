@@ -70,9 +70,18 @@ def test_validation_without_gpu(lib):
     assert lib.ds4moe_forward_stack(None, 1, None, 1, 1e-6, None, None) == m.EINVAL
     one_null = (ctypes.c_void_p * 1)(None)
     assert lib.ds4moe_forward_stack(one_null, 0, None, 1, 1e-6, None, None) == m.EINVAL
-    assert lib.ds4moe_forward_stack(one_null, 1, 1, 1, 1e-6, 1, None) == m.EINVAL
+    assert lib.ds4moe_forward_stack(one_null, 1, 256, 1, 1e-6, 256, None) == m.EINVAL
     assert b"layer 0" in lib.ds4moe_last_error()
-    assert lib.ds4moe_forward_stack(one_null, 1, 1, 1, -1.0, 1, None) == m.EINVAL
+    assert lib.ds4moe_forward_stack(one_null, 1, 256, 1, -1.0, 256, None) == m.EINVAL
+    # misaligned h or x (the kernels load 16 bytes at a time)
+    assert lib.ds4moe_forward_stack(one_null, 1, 258, 1, 1e-6, 256, None) == m.EINVAL
+    assert b"aligned" in lib.ds4moe_last_error()
+    assert lib.ds4moe_forward_stack(one_null, 1, 256, 1, 1e-6, 264, None) == m.EINVAL
+    assert b"aligned" in lib.ds4moe_last_error()
+    # the newer per-handle entry points reject a NULL handle too
+    assert lib.ds4moe_last_routing(None, 1, None, None, None, None, None) == m.EINVAL
+    assert lib.ds4moe_status(None) == m.EINVAL
+    assert lib.ds4moe_set_wait_limit(None, 4, 1) == m.EINVAL
 
 
 def test_binding_has_no_fallback(tmp_path):

@@ -62,11 +62,14 @@ def test_gemm_tiny_multi_chunk_experts():
     assert err <= REL_TOL
 
 
-@pytest.mark.parametrize("n", [2, 3, 5, 8, 16, 32])
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 7, 8, 16, 32])
 def test_gemm_zipf_batches(n):
     """Decode batches under a Zipf-skewed router bias (AUTO takes the GEMM path for bf16 batches).
     2 and 3 tokens split the GEMMs' K range 8 ways, 5 tokens 4 ways, 8 and more not at all
-    (routed) while the shared expert still splits."""
+    (routed) while the shared expert still splits.  2..8 tokens are also the shapes of
+    speculative (MTP) verification, which scores the last token plus k drafted ones in one
+    call ("ds4 深度实战...", section 4.2: the optional MTP download for multi-token
+    prediction / speculative decoding); 7 is k = 6."""
     lay = host_layer("ds4_zipf")
     x = synth.activations(2, n, 4096)
     got = _run(device_layer("ds4_zipf"), x, m.PATH_AUTO)
@@ -100,7 +103,8 @@ _PREFILL = {}
 
 
 def _prefill_outputs():
-    """2048-token prefill in one call and in chunks of 512 (cached)."""
+    """2048-token prefill in one call and in chunks of 512 (cached), and the
+    GEMV kernels' result (exact weights, fp32 activations, 4 tokens per call)."""
     if not _PREFILL:
         dev = device_layer("ds4", 2048)
         x = synth.activations(1, 2048, 4096)
@@ -109,27 +113,50 @@ def _prefill_outputs():
         _PREFILL["one"] = _run(dev, x, m.PATH_AUTO)
         log("[gpu] prefill 2048 in chunks of 512")
         _PREFILL["chunked"] = _run(dev, x, m.PATH_AUTO, chunk=512)
+        log("[gpu] prefill 2048 through the GEMV kernels, 4 tokens per call")
+        _PREFILL["gemv"] = _run(dev, x, m.PATH_GEMV, chunk=4)
     return _PREFILL
 
 
-def test_gemm_prefill_2048_sampled_tokens():
-    """Full-size prefill, checked against the oracle on a sample of tokens
-    (first, last, chunk edges and a seeded spread)."""
+def chunk_edge_rows(x_np, k, n_expert, call=2048, chunk=64):
+    """Tokens in the first and the last slot of every chunk of CH_TOK = 64
+    slots of every expert's list (the grouped GEMMs' work units, ragged tails
+    included), for calls of ``call`` tokens; from the oracle's routing."""
+    lay = host_layer("ds4")
+    rows = set()
+    for c0 in range(0, len(x_np), call):
+        _, idx, _, _ = oracle.route(x_np[c0:c0 + call], lay.router, lay.router_bias, k)
+        offs, toks = oracle.bucket(idx, n_expert)
+        for e in range(n_expert):
+            lst = toks[offs[e]:offs[e + 1]]
+            for s0 in range(0, len(lst), chunk):
+                part = lst[s0:s0 + chunk]
+                rows.add(c0 + int(part[0]))
+                rows.add(c0 + int(part[-1]))
+    return np.array(sorted(rows), dtype=np.int32)
+
+
+def test_gemm_prefill_2048_every_chunk():
+    """Full-size prefill against the oracle on the first and last token of
+    every expert's 64-slot chunk (so every work unit of the routed GEMMs,
+    with its ragged tail, is checked), in one call and in four calls of 512."""
     p = _prefill_outputs()
-    rng = np.random.default_rng(11)
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, 511, 512, 1023, 1024, 2046, 2047],
-                                     rng.choice(2048, 22, replace=False)])).astype(np.int32)
+    rows = np.union1d(chunk_edge_rows(p["x"], 6, 256), chunk_edge_rows(p["x"], 6, 256, call=512))
+    log(f"[gpu] prefill 2048: oracle on {len(rows)} chunk-edge tokens")
     ref, _, _ = oracle.forward(host_layer("ds4"), p["x"], rows=rows)
     err = rel_err(p["one"][rows], ref)
-    log(f"[gpu] prefill 2048: {len(rows)} sampled tokens, rel err {err:.3e}")
-    assert err <= REL_TOL
-    assert np.all(np.isfinite(p["one"]))
+    err512 = rel_err(p["chunked"][rows], ref)
+    log(f"[gpu] prefill 2048: rel err {err:.3e} (one call), {err512:.3e} (512-token calls)")
+    assert err <= REL_TOL and err512 <= REL_TOL
+    assert np.all(np.isfinite(p["one"])) and np.all(np.isfinite(p["chunked"]))
 
 
-def test_gemm_prefill_chunked_512_matches():
-    """Prefill in chunks of 512 tokens gives the single-call result (same
-    arithmetic per token; only the order of the output atomics differs)."""
+def test_gemm_prefill_2048_all_rows_against_gemv():
+    """All 2048 rows against the GEMV kernels (exact dequantised weights and
+    fp32 activations; within 1e-5 of the oracle in the GEMV tests), at the
+    same bar: a fault confined to some rows of the grouped GEMMs shows here."""
     p = _prefill_outputs()
-    err = rel_err(p["chunked"], p["one"])
-    log(f"[gpu] prefill 512-chunks vs one call rel diff {err:.3e}")
-    assert err <= 1e-5
+    err = rel_err(p["one"], p["gemv"])
+    err512 = rel_err(p["chunked"], p["gemv"])
+    log(f"[gpu] prefill 2048 vs GEMV kernels: rel diff {err:.3e} (one call), {err512:.3e} (512-token calls)")
+    assert err <= REL_TOL and err512 <= REL_TOL

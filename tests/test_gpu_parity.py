@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 from bit_quantized_moe_renorm_amd import synth
-from gpu_common import FUSED_TOL, GEMV_TOL, REL_TOL, device_layer, host_layer, log, rel_err
+from gpu_common import FUSED_TOL, GEMV_TOL, REL_TOL, device_layer, host_layer, log, rel_err, tie_split_tokens
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -98,6 +98,75 @@ def test_route_batched_exact_ties():
     _, ridx, _, _ = oracle.route(x, lay.router, lay.router_bias, lay.spec.top_k)
     # the tie rule is exercised: some token takes both experts of a pair
     assert any(len(set(r // 2)) < len(r) for r in ridx)
+
+
+def _tie_inputs(n):
+    x = synth.activations(21, 160, 4096)
+    t = tie_split_tokens("ds4_ties_half", x, n)
+    assert len(t) == n, "not enough tokens whose top-k boundary splits a tied pair"
+    return x[t]
+
+
+@pytest.mark.parametrize("n", [2, 8, 32])
+def test_route_small_batch_tie_boundary(n):
+    """The 2..64-token router (tagged top-k in the last workgroup of each token
+    tile): every token's k-th expert has an exactly tied twin outside the
+    selection, so only the lower-index rule picks between them."""
+    lay = host_layer("ds4_ties_half")
+    log(f"[gpu] route tie boundary n={n}")
+    _check_route("ties_half", _tie_inputs(n), device_layer("ds4_ties_half"), lay)
+
+
+def _check_last_routing(dev, lay, x_np, n):
+    idx, w, off, tok = dev.last_routing(n)
+    torch.cuda.synchronize()
+    _, ridx, _, rw64 = oracle.route(x_np, lay.router, lay.router_bias, lay.spec.top_k)
+    roff, rtok = oracle.bucket(ridx, lay.spec.n_expert)
+    idx, w, off, tok = idx.cpu().numpy(), w.cpu().numpy(), off.cpu().numpy(), tok.cpu().numpy()
+    assert np.array_equal(idx, ridx), (idx, ridx)
+    assert np.array_equal(off, roff) and np.array_equal(tok, rtok)
+    assert np.max(np.abs(w.astype(np.float64) - rw64)) <= 2.5e-7
+
+
+def test_fused_decode_tie_boundary():
+    """One-token forward (the fused decode kernel, which takes its own top-k):
+    its routing, read back with last_routing, is bit-exact against the oracle
+    on tokens whose k-th expert has a tied twin, and the output (the twins'
+    weights differ) is within the fused path's tolerance."""
+    lay = host_layer("ds4_ties_half")
+    dev = device_layer("ds4_ties_half")
+    xs = _tie_inputs(8)
+    for i in range(len(xs)):
+        got = _forward(dev, xs[i:i + 1], m.PATH_AUTO)
+        _check_last_routing(dev, lay, xs[i:i + 1], 1)
+        ref, _, _ = oracle.forward(lay, xs[i:i + 1])
+        err = rel_err(got, ref)
+        log(f"[gpu] fused tie-boundary token {i}: rel err {err:.3e}")
+        assert err <= FUSED_TOL
+
+
+def test_fused_decode_routing_matches_oracle():
+    """The fused decode kernel's own routing on ordinary tokens (no ties)."""
+    lay = host_layer("ds4")
+    dev = device_layer("ds4")
+    x = synth.activations(1, 6, 4096, start=200)
+    for t in range(6):
+        _forward(dev, x[t:t + 1], m.PATH_AUTO)
+        _check_last_routing(dev, lay, x[t:t + 1], 1)
+
+
+def test_batched_forward_tie_boundary():
+    """8 tie-boundary tokens through the batched path (small-batch router, then
+    the grouped GEMMs): routing bit-exact, output within the bar."""
+    lay = host_layer("ds4_ties_half")
+    dev = device_layer("ds4_ties_half")
+    xs = _tie_inputs(8)
+    got = _forward(dev, xs, m.PATH_AUTO)
+    _check_last_routing(dev, lay, xs, 8)
+    ref, _, _ = oracle.forward(lay, xs)
+    err = rel_err(got, ref)
+    log(f"[gpu] batched tie-boundary n=8 rel err {err:.3e}")
+    assert err <= REL_TOL
 
 
 def test_route_empty_and_errors():
