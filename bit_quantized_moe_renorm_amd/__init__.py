@@ -25,7 +25,7 @@ TIMING_KINDS = ("route", "gateup_routed", "gateup_shared", "down_routed", "down_
 
 SYMBOLS = ("ds4moe_create", "ds4moe_route", "ds4moe_forward", "ds4moe_set_path", "ds4moe_dequantize",
            "ds4moe_rmsnorm", "ds4moe_forward_stack", "ds4moe_timing_enable", "ds4moe_timing_read",
-           "ds4moe_last_routing", "ds4moe_status", "ds4moe_set_wait_limit",
+           "ds4moe_last_routing", "ds4moe_status", "ds4moe_set_wait_limit", "ds4moe_forward_static",
            "ds4moe_destroy", "ds4moe_last_error")
 
 
@@ -72,6 +72,7 @@ def load_library(path: Optional[Path] = None) -> ctypes.CDLL:
     L.ds4moe_last_routing.argtypes = [P, i32, P, P, P, P, P]
     L.ds4moe_status.argtypes = [P]
     L.ds4moe_set_wait_limit.argtypes = [P, i32, i32]
+    L.ds4moe_forward_static.argtypes = [P, P, i32, P, P]
     L.ds4moe_destroy.argtypes = [P]
     L.ds4moe_last_error.restype = ctypes.c_char_p
     for name in SYMBOLS:
@@ -171,6 +172,13 @@ class MoELayer:
         n = self._check_x(x)
         _check_tensor("out", out, torch.float32, (n, self.spec.n_embd), x.device)
         _check(load_library().ds4moe_forward(self.h, _ptr(x), n, _ptr(out), _stream(stream)))
+
+    def forward_static(self, x, out, stream=None):
+        """out += MoE(x) for 1..4 tokens with the library's static scratch (allocates nothing)."""
+        import torch
+        n = self._check_x(x)
+        _check_tensor("out", out, torch.float32, (n, self.spec.n_embd), x.device)
+        _check(load_library().ds4moe_forward_static(self.h, _ptr(x), n, _ptr(out), _stream(stream)))
 
     def _routing_buffers(self, n, dev):
         import torch

@@ -141,6 +141,7 @@ hipError_t launch_router_prep(const float *router, int NE, int E, uint16_t *hml,
 // hand-off tag is ep + 1, never 0)
 hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s,
                         unsigned long long ep);
+hipError_t launch_fill_u32(uint32_t *p, int n, uint32_t v, hipStream_t s);
 hipError_t launch_route_export(const Layer &L, const Work &W, int n_tok, int32_t *idx, float *w,
                                int32_t *offsets, int32_t *tokens, hipStream_t s);
 

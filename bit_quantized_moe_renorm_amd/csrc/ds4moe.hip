@@ -5,9 +5,11 @@
 // kernels on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -38,7 +40,25 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 constexpr int TIMING_SLOTS = TK_COUNT;
 constexpr int TIMING_EVENTS = 4096;
 
+// ---------------------------------------------------------------- static scratch
+// The scratch of ds4moe_forward_static: one array per GPU, in device memory
+// the library never allocates (the code object's own storage), holding the
+// routing results, the tagged hand-off words, the router's tickets and the
+// SwiGLU activations of calls of 1..4 tokens.  In host code its name is only a
+// stand-in: kernels get the address that hipGetSymbolAddress returned for the
+// device, looked up once per device with that device current.
+constexpr size_t STATIC_BYTES = DS4MOE_STATIC_SCRATCH_BYTES;
+constexpr int STATIC_MAX_TOK = DS4MOE_STATIC_MAX_TOKENS;
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+// Calls on a device's array: their hand-off tags, unique across the handles
+// that share it.
+std::atomic<unsigned long long> g_static_calls[MAX_DEVICES];
+
 }  // namespace
+
+static __device__ __align__(256) unsigned char scratch[STATIC_BYTES];
 
 struct ds4moe {
     Layer L{};
@@ -50,6 +70,9 @@ struct ds4moe {
     bool poisoned = false;
     int device = 0;
     int32_t last_n_tok = -1;              // n_tok of the latest forward/route call (its routing is in W)
+    bool last_static = false;             // ... made by ds4moe_forward_static (its routing is in Wst)
+    Work Wst{};                           // the workspace of ds4moe_forward_static, in the static scratch
+    size_t static_need = 0;               // bytes of it this layer needs
     uint32_t *status_host = nullptr;      // pinned, mapped: nonzero = a bounded wait expired (that call's tag)
     std::vector<void *> allocs;
     // timing
@@ -93,6 +116,26 @@ static int check_launch(ds4moe *h, hipError_t e, const char *what) {
         return fail(DS4MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
     }
     return DS4MOE_OK;
+}
+
+// Carve the forward_static workspace (1..4 tokens: the fused decode and the
+// GEMV path) out of the device's static scratch; returns the bytes it spans.
+static size_t carve_static(const Layer &L, char *base, Work &S) {
+    const size_t T = STATIC_MAX_TOK, NE = L.n_expert, k = L.top_k, F = L.n_ff;
+    size_t off = 0;
+    auto carve = [&](size_t bytes) { char *p = base + off; off += align256(bytes); return p; };
+    S.idx = (int32_t *)carve(T * k * 4);
+    S.w = (float *)carve(T * k * 4);
+    S.offsets = (int32_t *)carve((NE + 1) * 4);
+    S.list = (int32_t *)carve(T * k * 4);
+    S.active = (int32_t *)carve((NE + 1) * 4);
+    S.counters = (int32_t *)carve(256);
+    S.rtag = (unsigned long long *)carve(4 * MAX_EXPERT * 8);
+    S.htag = (unsigned long long *)carve((k + 1) * F * 8);
+    S.ltag = (unsigned long long *)carve(T * MAX_EXPERT * 8);
+    S.itag = (unsigned long long *)carve(T * MAX_TOPK * 8);
+    S.hbuf = (float *)carve(T * (k + 1) * F * 4);
+    return off;
 }
 
 extern "C" {
@@ -212,6 +255,28 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     }
     W.spin_limit = DEFAULT_SPIN_LIMIT;
     W.want_xor = 0u;
+    // the device's static scratch (ds4moe_forward_static): its address, looked
+    // up once per device with the device current
+    if (h->device < 0 || h->device >= MAX_DEVICES) {
+        delete h;
+        return fail(DS4MOE_EUNSUPPORTED, "create: device %d beyond the library's table", h->device);
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        if (!g_scratch_ptr[h->device]) {
+            void *p = nullptr;
+            hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) {
+                delete h;
+                hipGetLastError();
+                return fail(DS4MOE_EHIP, "create: address of the static scratch (%s)", hipGetErrorString(e));
+            }
+            g_scratch_ptr[h->device] = p;
+        }
+        h->Wst = Work{};
+        h->Wst.status = W.status;
+        h->static_need = carve_static(L, (char *)g_scratch_ptr[h->device], h->Wst);
+    }
 
 #define CK(call)                                                                                      \
     do {                                                                                              \
@@ -313,6 +378,7 @@ int ds4moe_route(ds4moe_t *h, const void *x, int32_t n_tok, int32_t *topk_idx, f
     hipStream_t s = (hipStream_t)stream;
     if ((rc = stream_checks(s, "route"))) return rc;
     h->last_n_tok = n_tok;
+    h->last_static = false;
     int tb = h->tbegin(TK_ROUTE, s);
     rc = check_launch(h, launch_route(h->L, h->W, x, n_tok, s, h->route_calls++), "route");
     h->tend(tb, s);
@@ -342,6 +408,7 @@ int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *
         return fail(DS4MOE_EUNSUPPORTED, "forward: the grouped GEMM path is not available in this build");
     hipStream_t s = (hipStream_t)stream;
     h->last_n_tok = n_tok;
+    h->last_static = false;
     if (path == DS4MOE_PATH_GEMV && n_tok == 1) {
         // the whole block for one token in one persistent launch
         int tf = h->tbegin(TK_FUSED, s);
@@ -401,6 +468,51 @@ int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *
         rc = check_launch(h, launch_gemm_down_shared(h->L, h->W, n_tok, out, s), "gemm shared down");
         h->tend(tb, s);
     }
+    return rc;
+}
+
+int ds4moe_forward_static(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *stream) {
+    int rc = common_checks(h, x, n_tok, "forward_static");
+    if (rc) return rc;
+    if (n_tok > STATIC_MAX_TOK)
+        return fail(DS4MOE_EINVAL, "forward_static: n_tok %d beyond the static scratch's %d tokens", n_tok,
+                    STATIC_MAX_TOK);
+    if (n_tok > 0 && !out) return fail(DS4MOE_EINVAL, "forward_static: NULL out");
+    if (n_tok > 0 && !aligned16(out)) return fail(DS4MOE_EINVAL, "forward_static: out is not 16-byte aligned");
+    if (n_tok == 0) return DS4MOE_OK;
+    if (h->static_need > STATIC_BYTES)
+        return fail(DS4MOE_EINVAL, "forward_static: this layer needs %zu bytes of scratch, the static array holds %zu",
+                    h->static_need, STATIC_BYTES);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
+        hipGetLastError();
+        return fail(DS4MOE_EINVAL, "forward_static: the handle's device %d is not the current device %d", h->device,
+                    dev);
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if ((rc = stream_checks(s, "forward_static"))) return rc;
+    Work S = h->Wst;
+    S.spin_limit = h->W.spin_limit;
+    S.want_xor = h->W.want_xor;
+    const unsigned long long ep = g_static_calls[dev].fetch_add(1);
+    h->last_n_tok = n_tok;
+    h->last_static = true;
+    if (n_tok == 1)
+        return check_launch(h, launch_decode_fused(h->L, S, x, out, h->decode_grid, ep, s), "forward_static decode");
+    // the router's tickets start at zero
+    rc = check_launch(h, launch_fill_u32((uint32_t *)S.counters, 64, 0u, s), "forward_static clear");
+    if (rc) return rc;
+    rc = check_launch(h, launch_route(h->L, S, x, n_tok, s, ep), "forward_static route");
+    if (rc) return rc;
+    if (h->L.n_shared) {
+        rc = check_launch(h, launch_gemv_gateup_shared(h->L, S, x, n_tok, s), "forward_static shared gate/up");
+        if (rc) return rc;
+    }
+    rc = check_launch(h, launch_gemv_gateup_routed(h->L, S, x, n_tok, s), "forward_static routed gate/up");
+    if (rc) return rc;
+    rc = check_launch(h, launch_gemv_down_routed(h->L, S, n_tok, out, s), "forward_static routed down");
+    if (rc) return rc;
+    if (h->L.n_shared) rc = check_launch(h, launch_gemv_down_shared(h->L, S, n_tok, out, s), "forward_static shared down");
     return rc;
 }
 
@@ -470,7 +582,8 @@ int ds4moe_last_routing(ds4moe_t *h, int32_t n_tok, int32_t *topk_idx, float *to
         return fail(DS4MOE_EINVAL, "last_routing: NULL output");
     hipStream_t s = (hipStream_t)stream;
     if ((rc = stream_checks(s, "last_routing"))) return rc;
-    return check_launch(h, launch_route_export(h->L, h->W, n_tok, topk_idx, topk_w, expert_offsets, expert_tokens, s),
+    return check_launch(h, launch_route_export(h->L, h->last_static ? h->Wst : h->W, n_tok, topk_idx, topk_w,
+                                               expert_offsets, expert_tokens, s),
                         "last_routing export");
 }
 

@@ -802,6 +802,16 @@ hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok,
     return hipGetLastError();
 }
 
+// Fill n 32-bit words with a value (counters that must start at zero).
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t *__restrict__ p, int n, uint32_t v) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t *p, int n, uint32_t v, hipStream_t s) {
+    hipLaunchKernelGGL(k_fill_u32, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
 // Copy the internal routing results into the caller's buffers.
 __global__ void k_route_export(int n_tok, int NE, int k, Work W, int32_t *__restrict__ idx, float *__restrict__ w,
                                int32_t *__restrict__ offsets, int32_t *__restrict__ tokens) {

@@ -163,6 +163,28 @@ int ds4moe_route(ds4moe_t *h, const void *x, int32_t n_tok, int32_t *topk_idx, f
  */
 int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture elsewhere in their program, tight serving loops, harnesses that
+ * forbid hipMalloc): out += MoE(x) for 1 <= n_tok <= DS4MOE_STATIC_MAX_TOKENS
+ * tokens, with the results of ds4moe_forward on the same inputs (one token:
+ * the fused decode kernel; 2..4: the dequant-fused GEMV kernels, whatever
+ * ds4moe_set_path says), but every scratch buffer of the call (routing
+ * results, tagged hand-off words, the router's tickets, SwiGLU activations)
+ * in the library's static device array of DS4MOE_STATIC_SCRATCH_BYTES, one
+ * per GPU, which each GPU holds until the process ends; the handle's own
+ * workspace is not touched.  Nothing is allocated.  The handle's device must
+ * be current.  n_tok > DS4MOE_STATIC_MAX_TOKENS returns DS4MOE_EINVAL
+ * (nothing enqueued); n_tok == 0 is a no-op.  Calls on one GPU share its
+ * array: calls that overlap on one GPU (on any handles, on different streams)
+ * race and must be serialised by the caller; consecutive stream-ordered calls
+ * are safe (their hand-off tags come from one per-GPU count).  x, out and the
+ * errors are as for ds4moe_forward; a stream under capture is refused.
+ */
+#define DS4MOE_STATIC_SCRATCH_BYTES (1u << 20)
+#define DS4MOE_STATIC_MAX_TOKENS 4
+int ds4moe_forward_static(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *stream);
+
 /* Choose the kernel path used by ds4moe_forward (DS4MOE_PATH_*).  Host-only. */
 int ds4moe_set_path(ds4moe_t *h, int32_t path);
 
