@@ -37,6 +37,7 @@ CODEBOOK_SEED = 0xC0DE_B00C
 QK = 256                    # weights per super-block
 IQ2_BLOCK_BYTES = 66        # fp16 d + 8 sub-blocks x (4 index bytes + 1 sign/scale word)
 Q2K_BLOCK_BYTES = 84        # scales[16] + qs[64] + fp16 d + fp16 dmin
+Q4K_BLOCK_BYTES = 144       # fp16 d + fp16 dmin + 16 six-bit scale/min fields + qs[128]
 
 _TID = dict(router=1, router_bias=2, gate=3, up=4, down=5, sh_gate=6, sh_up=7,
             sh_down=8, x=9, codebook=10, h0=11, zipf=12)
@@ -93,6 +94,21 @@ def q2k_blocks(rng: np.random.Generator, n_blocks: int) -> np.ndarray:
     return blk
 
 
+def q4k_blocks(rng: np.random.Generator, n_blocks: int) -> np.ndarray:
+    """``n_blocks`` random Q4_K-style super-blocks, shape ``[n_blocks, 144]`` uint8.
+
+    Bytes 0-1 hold ``d`` and 2-3 ``dmin`` (fp16, little endian), both in
+    [2^-14, 2^-13) (exponent field 1, the smallest normal binade: with 6-bit
+    scales and 4-bit quants the weights' spread is then close to the other
+    formats'); bytes 4-143 (the scale/min fields and the quants) are uniform
+    random.
+    """
+    blk = _raw_bytes(rng, n_blocks * Q4K_BLOCK_BYTES).reshape(n_blocks, Q4K_BLOCK_BYTES).copy()
+    dd = _fp16_in_binade(rng, 2 * n_blocks, 1)
+    blk[:, 0:4] = dd.view(np.uint8).reshape(n_blocks, 4)
+    return blk
+
+
 def codebook() -> np.ndarray:
     """The shared 256-entry codebook: uint16 per entry, 2 bits per coordinate."""
     return rng_for(CODEBOOK_SEED, "codebook").integers(0, 1 << 16, size=256, dtype=np.uint16)
@@ -121,6 +137,8 @@ class Layer:
     * ``down``: uint8 ``[n_expert, n_embd, n_ff/256, 84]``
     * ``codebook``: uint16 ``[256]``
     * ``sh_gate``, ``sh_up``: bf16 bits ``[n_ff, n_embd]``; ``sh_down``: bf16 bits ``[n_embd, n_ff]``
+    * ``fmt``: "q2" (the layout above) or "q4": gate, up and down are all Q4_K-style
+      blocks of 144 bytes, ``[n_expert, rows, cols/256, 144]``
     """
     spec: LayerSpec
     seed: int
@@ -134,6 +152,7 @@ class Layer:
     sh_up: Optional[np.ndarray]
     sh_down: Optional[np.ndarray]
     extra: dict = field(default_factory=dict)
+    fmt: str = "q2"
 
 
 def zipf_router_bias(seed: int, n_expert: int, s: float = 1.1) -> np.ndarray:
@@ -145,21 +164,27 @@ def zipf_router_bias(seed: int, n_expert: int, s: float = 1.1) -> np.ndarray:
     return (-s * np.log(ranks.astype(np.float64))).astype(np.float32)
 
 
-def make_layer(spec: LayerSpec, seed: int, zipf_bias: bool = False, shared: bool = True) -> Layer:
+def make_layer(spec: LayerSpec, seed: int, zipf_bias: bool = False, shared: bool = True, fmt: str = "q2") -> Layer:
     E, F, NE = spec.n_embd, spec.n_ff, spec.n_expert
-    assert E % QK == 0 and F % QK == 0
+    assert E % QK == 0 and F % QK == 0 and fmt in ("q2", "q4")
     router = (rng_for(seed, "router").standard_normal((NE, E)) * 0.02).astype(np.float32)
     bias = zipf_router_bias(seed, NE) if zipf_bias else None
-    gate = iq2_blocks(rng_for(seed, "gate"), NE * F * (E // QK)).reshape(NE, F, E // QK, IQ2_BLOCK_BYTES)
-    up = iq2_blocks(rng_for(seed, "up"), NE * F * (E // QK)).reshape(NE, F, E // QK, IQ2_BLOCK_BYTES)
-    down = q2k_blocks(rng_for(seed, "down"), NE * E * (F // QK)).reshape(NE, E, F // QK, Q2K_BLOCK_BYTES)
+    if fmt == "q4":
+        B = Q4K_BLOCK_BYTES
+        gate = q4k_blocks(rng_for(seed, "gate"), NE * F * (E // QK)).reshape(NE, F, E // QK, B)
+        up = q4k_blocks(rng_for(seed, "up"), NE * F * (E // QK)).reshape(NE, F, E // QK, B)
+        down = q4k_blocks(rng_for(seed, "down"), NE * E * (F // QK)).reshape(NE, E, F // QK, B)
+    else:
+        gate = iq2_blocks(rng_for(seed, "gate"), NE * F * (E // QK)).reshape(NE, F, E // QK, IQ2_BLOCK_BYTES)
+        up = iq2_blocks(rng_for(seed, "up"), NE * F * (E // QK)).reshape(NE, F, E // QK, IQ2_BLOCK_BYTES)
+        down = q2k_blocks(rng_for(seed, "down"), NE * E * (F // QK)).reshape(NE, E, F // QK, Q2K_BLOCK_BYTES)
     if shared and spec.n_shared:
         sg = f32_to_bf16_bits((rng_for(seed, "sh_gate").standard_normal((F, E)) * 0.02).astype(np.float32))
         su = f32_to_bf16_bits((rng_for(seed, "sh_up").standard_normal((F, E)) * 0.02).astype(np.float32))
         sd = f32_to_bf16_bits((rng_for(seed, "sh_down").standard_normal((E, F)) * 0.02).astype(np.float32))
     else:
         sg = su = sd = None
-    return Layer(spec, seed, router, bias, gate, up, down, codebook(), sg, su, sd)
+    return Layer(spec, seed, router, bias, gate, up, down, codebook(), sg, su, sd, fmt=fmt)
 
 
 def activations(seed: int, n_tok: int, n_embd: int, bf16: bool = True, start: int = 0) -> np.ndarray:
@@ -178,10 +203,10 @@ def residual(seed: int, n_tok: int, n_embd: int) -> np.ndarray:
     return rng_for(seed, "h0").standard_normal((n_tok, n_embd)).astype(np.float32)
 
 
-def layer_nbytes(spec: LayerSpec) -> dict:
+def layer_nbytes(spec: LayerSpec, fmt: str = "q2") -> dict:
     """Stored bytes of one layer's tensors (quantised experts as stored)."""
     E, F, NE = spec.n_embd, spec.n_ff, spec.n_expert
-    per_gate = F * (E // QK) * IQ2_BLOCK_BYTES
-    per_down = E * (F // QK) * Q2K_BLOCK_BYTES
+    per_gate = F * (E // QK) * (Q4K_BLOCK_BYTES if fmt == "q4" else IQ2_BLOCK_BYTES)
+    per_down = E * (F // QK) * (Q4K_BLOCK_BYTES if fmt == "q4" else Q2K_BLOCK_BYTES)
     return dict(per_expert=2 * per_gate + per_down, gate=per_gate, down=per_down,
                 shared=3 * E * F * 2 * spec.n_shared, router=NE * E * 4)

@@ -42,10 +42,11 @@ def lib() -> ctypes.CDLL:
         i64, i32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
         L.oracle_dequant_iq2.argtypes = [P, i64, P, P]
         L.oracle_dequant_q2k.argtypes = [P, i64, P]
+        L.oracle_dequant_q4k.argtypes = [P, i64, P]
         L.oracle_route.argtypes = [P, i32, i64, i32, P, P, i32, i32, P, P, P, P]
         L.oracle_route.restype = i32
         L.oracle_bucket.argtypes = [P, i64, i32, i32, P, P]
-        L.oracle_forward.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, i32, P, i64,
+        L.oracle_forward.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, i32, P, i64,
                                      P, P, P]
         L.oracle_forward.restype = i32
         L.oracle_rmsnorm.argtypes = [P, i64, i32, f64, P, P]
@@ -90,8 +91,25 @@ def dequant_q2k(blocks: np.ndarray) -> np.ndarray:
     return out
 
 
+def dequant_q4k(blocks: np.ndarray) -> np.ndarray:
+    """Decode Q4_K-style blocks ``[..., 144]`` to fp32 ``[..., 256]``."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint8)
+    assert b.shape[-1] == 144
+    n = b.size // 144
+    out = np.empty(b.shape[:-1] + (256,), dtype=np.float32)
+    lib().oracle_dequant_q4k(_p(b), n, _p(out))
+    return out
+
+
+def _fmt(layer) -> int:
+    return 1 if getattr(layer, "fmt", "q2") == "q4" else 0
+
+
 def dequant_matrix(layer, expert: int, which: str) -> np.ndarray:
     """fp32 matrix of one routed expert: gate/up ``[n_ff, n_embd]``, down ``[n_embd, n_ff]``."""
+    if _fmt(layer):
+        blk = getattr(layer, which)[expert]
+        return dequant_q4k(blk).reshape(blk.shape[0], -1)
     if which in ("gate", "up"):
         blk = getattr(layer, which)[expert]
         return dequant_iq2(blk, layer.codebook).reshape(blk.shape[0], -1)
@@ -144,7 +162,7 @@ def forward(layer, x, rows=None):
     out = np.empty((len(rows), E), np.float64)
     idx = np.empty((len(rows), s.top_k), np.int32)
     w = np.empty((len(rows), s.top_k), np.float64)
-    rc = lib().oracle_forward(E, s.n_ff, s.n_expert, s.top_k, _p(layer.router), _p(layer.router_bias),
+    rc = lib().oracle_forward(E, s.n_ff, s.n_expert, s.top_k, _fmt(layer), _p(layer.router), _p(layer.router_bias),
                               _p(layer.gate), _p(layer.up), _p(layer.down), _p(layer.codebook),
                               _p(layer.sh_gate), _p(layer.sh_up), _p(layer.sh_down), _p(x), isbf,
                               _p(rows), len(rows), _p(out), _p(idx), _p(w))

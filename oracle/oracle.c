@@ -8,8 +8,9 @@
  *
  * What it computes (every function below cites the passage it follows):
  *
- *  - the two routed-expert block formats, decoded one weight at a time into
- *    fp32 (every decoded value is exact in fp32 for the value ranges used);
+ *  - the routed-expert block formats (IQ2-style gate/up with Q2_K-style down,
+ *    or Q4_K-style for all three), decoded one weight at a time into fp32
+ *    (every decoded value is exact in fp32 for the value ranges used);
  *  - the router: fp64-accumulated logits rounded to fp32, a softmax over all
  *    experts, the top-k experts (lower index wins exact ties) and the weights
  *    renormalised over the selected experts;
@@ -158,6 +159,45 @@ void oracle_dequant_q2k(const uint8_t *blocks, int64_t n_blocks, float *out)
             int sc = blk[s] & 15;
             int m = blk[s] >> 4;
             int q = (blk[16 + i / 4] >> (2 * (i % 4))) & 3;
+            out[QK * b + i] = (float)(d * sc * q - dmin * m);
+        }
+    }
+}
+
+/*
+ * Q4_K-style super-block, 144 bytes per 256 weights: the routed experts of the
+ * q4 model ([P1] section 2.1: the q2-q4 variant keeps its last 6 layers at q4;
+ * [P5] section 3.1 names the format Q4 (Q4_K)).  The pages give no layout, so
+ * the packing is the stand-in fixed for this block:
+ *   bytes 0-1 fp16 d, bytes 2-3 fp16 dmin (little endian);
+ *   bytes 4-15 a little-endian stream of sixteen 6-bit fields, field j at
+ *   stream bits 6j..6j+5: for j < 8 the scale sc of sub-block j (weights
+ *   32j..32j+31), for j >= 8 the min m of sub-block j-8;
+ *   bytes 16-143 the 4-bit quants: weight i's q is bits 4(i%2)..4(i%2)+3 of
+ *   byte 16 + i/2.
+ *   w = d * sc * q - dmin * m
+ */
+static int q4k_field(const uint8_t *blk, int j)
+{
+    int v = 0;
+    for (int b = 0; b < 6; ++b) {
+        int bit = 6 * j + b;
+        v |= ((blk[4 + bit / 8] >> (bit % 8)) & 1) << b;
+    }
+    return v;
+}
+
+void oracle_dequant_q4k(const uint8_t *blocks, int64_t n_blocks, float *out)
+{
+    for (int64_t b = 0; b < n_blocks; ++b) {
+        const uint8_t *blk = blocks + 144 * b;
+        double d = half_value(rd16(blk));
+        double dmin = half_value(rd16(blk + 2));
+        for (int i = 0; i < QK; ++i) {
+            int s = i / 32;
+            int sc = q4k_field(blk, s);
+            int m = q4k_field(blk, 8 + s);
+            int q = (blk[16 + i / 2] >> (4 * (i % 2))) & 15;
             out[QK * b + i] = (float)(d * sc * q - dmin * m);
         }
     }
@@ -355,21 +395,23 @@ static void ffn_bf16(const uint16_t *wg, const uint16_t *wu, const uint16_t *wd,
  * time; the work is spread over experts with OpenMP and summed per token in
  * slot order, so the result does not depend on the thread count.
  *
- * gate, up: [n_expert][n_ff][n_embd/256] IQ2 blocks; down: [n_expert][n_embd][n_ff/256]
- * Q2_K blocks; sh_*: bf16 bits or NULL when there is no shared expert.
+ * expert_format 0: gate, up are [n_expert][n_ff][n_embd/256] IQ2 blocks and down is
+ * [n_expert][n_embd][n_ff/256] Q2_K blocks; expert_format 1: all three are Q4_K
+ * blocks in the same shapes.  sh_*: bf16 bits or NULL when there is no shared expert.
  * out: [n_rows][n_embd] fp64, overwritten.  Optional outputs (NULL to skip):
  * idx_out [n_rows][top_k], w_out [n_rows][top_k] fp64.
  * Returns 0, -1 on bad sizes, -2 on allocation failure.
  */
-int oracle_forward(int n_embd, int n_ff, int n_expert, int top_k, const float *router,
+int oracle_forward(int n_embd, int n_ff, int n_expert, int top_k, int expert_format, const float *router,
                    const float *bias, const uint8_t *gate, const uint8_t *up, const uint8_t *down,
                    const uint16_t *codebook, const uint16_t *sh_gate, const uint16_t *sh_up,
                    const uint16_t *sh_down, const void *x, int x_is_bf16, const int32_t *rows,
                    int64_t n_rows, double *out, int32_t *idx_out, double *w_out)
 {
     if (n_embd % QK || n_ff % QK || n_embd <= 0 || n_ff <= 0 || top_k <= 0 || top_k > n_expert ||
-        n_rows < 0)
+        n_rows < 0 || (expert_format != 0 && expert_format != 1))
         return -1;
+    const int gu_bytes = expert_format ? 144 : 66, dn_bytes = expert_format ? 144 : 84;
     const int64_t gate_blocks = (int64_t)n_ff * (n_embd / QK);
     const int64_t down_blocks = (int64_t)n_embd * (n_ff / QK);
 
@@ -417,9 +459,15 @@ int oracle_forward(int n_embd, int n_ff, int n_expert, int top_k, const float *r
 #pragma omp atomic write
             bad = 1;
         } else {
-            oracle_dequant_iq2(gate + (int64_t)e * gate_blocks * 66, gate_blocks, codebook, wg);
-            oracle_dequant_iq2(up + (int64_t)e * gate_blocks * 66, gate_blocks, codebook, wu);
-            oracle_dequant_q2k(down + (int64_t)e * down_blocks * 84, down_blocks, wd);
+            if (expert_format == 1) {
+                oracle_dequant_q4k(gate + (int64_t)e * gate_blocks * gu_bytes, gate_blocks, wg);
+                oracle_dequant_q4k(up + (int64_t)e * gate_blocks * gu_bytes, gate_blocks, wu);
+                oracle_dequant_q4k(down + (int64_t)e * down_blocks * dn_bytes, down_blocks, wd);
+            } else {
+                oracle_dequant_iq2(gate + (int64_t)e * gate_blocks * gu_bytes, gate_blocks, codebook, wg);
+                oracle_dequant_iq2(up + (int64_t)e * gate_blocks * gu_bytes, gate_blocks, codebook, wu);
+                oracle_dequant_q2k(down + (int64_t)e * down_blocks * dn_bytes, down_blocks, wd);
+            }
             for (int64_t q = 0; q < n_rows * top_k; ++q)
                 if (idx[q] == e)
                     ffn_f32(wg, wu, wd, xs + (q / top_k) * n_embd, n_embd, n_ff, h, ys + q * n_embd);
