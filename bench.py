@@ -614,6 +614,103 @@ def run_batch(args):
     return res
 
 
+def run_q4(args):
+    """Decode b = 1 through a DS4-shape layer whose routed experts are
+    Q4_K-style (the q4 model's format, 14.2 MB per expert): one forward call
+    per token (router, then the dequant-fused GEMV kernels), replicas cycled
+    so the weights come from HBM.  Bytes: 6 touched experts + the shared
+    expert, as stored."""
+    import torch
+
+    import bit_quantized_moe_renorm_amd as m
+    import oracle
+    from bit_quantized_moe_renorm_amd import synth
+
+    spec = synth.DS4
+    lay = synth.make_layer(spec, seed=1, fmt="q4")
+    x_np = synth.activations(1, 1000, spec.n_embd)
+    w = m.upload_layer(lay)
+    R = max(1, min(args.replicas, 8))
+    reps = [m.MoELayer(spec, w, max_tokens=4) for _ in range(R)]
+    del w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    x = m.to_device_x(x_np)
+    out = torch.zeros((1000, spec.n_embd), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    steps = min(args.steps, 1000)
+
+    def step(i):
+        t = i % 1000
+        reps[i % R].forward(x[t:t + 1], out[t:t + 1], stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for r in reps:
+        r.timing_enable(True)
+    for i in range(steps):
+        step(args.warmup + steps + i)
+    torch.cuda.synchronize()
+    tot = {}
+    for r in reps:
+        for kind, (ms, cnt) in r.timing_read().items():
+            a = tot.setdefault(kind, [0.0, 0])
+            a[0] += ms
+            a[1] += cnt
+        r.timing_enable(False)
+    nb = synth.layer_nbytes(spec, "q4")
+    E, F, k = spec.n_embd, spec.n_ff, spec.top_k
+    kbytes = {"route": nb["router"], "gateup_shared": 2 * E * F * 2, "q4_gateup_routed": k * 2 * nb["gate"],
+              "q4_down_routed": k * nb["down"], "down_shared": E * F * 2}
+    per_kernel = {}
+    for kind, (ms, cnt) in tot.items():
+        us = 1000.0 * ms / cnt
+        d = {"avg_us": round(us, 3)}
+        if kind in kbytes:
+            d["bytes"] = kbytes[kind]
+            d["GB_s"] = round(kbytes[kind] / (us * 1e-6) / 1e9, 1)
+        per_kernel[kind] = d
+    log("[bench] q4 per-kernel: " + json.dumps(per_kernel))
+    layer_bytes = k * nb["per_expert"] + nb["shared"]
+    step_s = wall / steps
+    gbs = layer_bytes / step_s / 1e9
+    dom = "q4_gateup_routed"
+    log(f"[bench] q4 decode b=1: {1e6 * step_s:.2f} us/token, {1 / step_s:.0f} tok/s, {gbs:.0f} GB/s touched "
+        f"= {100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s")
+    res = {
+        "metric": METRIC, "value": round(1 / step_s, 1), "unit": "tok/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(1000 * step_s, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "DS4-shape MoE layer with Q4_K-style routed experts (q4 model), decode b=1, "
+                               "seed 1, 1000-token stream", "global_batch": 1, "seq_len": 1,
+                   "parallelism": "none (1 GPU)", "replicas": R, "touched_expert_bytes_per_token": layer_bytes,
+                   "layer_GB_s": round(gbs, 1), "layer_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                   "per_kernel": per_kernel},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": per_kernel[dom]["GB_s"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(per_kernel[dom]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": kbytes[dom], "avg_launch_us": per_kernel[dom]["avg_us"]},
+    }
+    if not args.no_cpu_baseline:
+        def run():
+            done, t1 = 0, time.perf_counter()
+            while time.perf_counter() - t1 < 10.0 and done + 4 <= 1000:
+                oracle.forward(lay, x_np[done:done + 4])
+                done += 4
+            return done
+        res["cpu_baseline"] = cpu_baseline(run, None, lambda: oracle.forward(lay, x_np[:1]), 1, "tok/s",
+                                           "the first tokens of the decode stream, oracle.forward in batches of 4",
+                                           "token 0")
+    for r in reps:
+        r.close()
+    return res
+
+
 def copy_probe():
     """A plain device copy of known size, for calibrating the HBM byte counters
     (FETCH_SIZE / WRITE_SIZE) that the profiles of the block's kernels use."""
@@ -635,7 +732,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode only (skip the nested prefill)")
-    ap.add_argument("--workload", choices=("decode", "prefill", "stack", "batch"), default="decode")
+    ap.add_argument("--workload", choices=("decode", "prefill", "stack", "batch", "q4"), default="decode")
     ap.add_argument("--layers", type=int, default=43, help="stack workload: number of layers")
     ap.add_argument("--tokens", type=int, default=2048, help="prefill tokens per call")
     ap.add_argument("--prefill-steps", type=int, default=20)
@@ -663,6 +760,8 @@ def main():
         res = run_stack(args)
     elif args.workload == "batch":
         res = run_batch(args)
+    elif args.workload == "q4":
+        res = run_q4(args)
     else:
         from bit_quantized_moe_renorm_amd import synth
         layer = synth.make_layer(synth.DS4, seed=1)

@@ -18,10 +18,12 @@ LIB_PATH = _PKG / "libds4moe.so"
 
 OK, EINVAL, ENOMEM, EHIP, EUNSUPPORTED, EPOISONED = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
+FMT_Q2, FMT_Q4 = 0, 1
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 TIMING_KINDS = ("route", "gateup_routed", "gateup_shared", "down_routed", "down_shared", "gemm_gateup_routed",
-                "gemm_down_routed", "fused", "gemm_prep", "gemm_gateup_shared", "gemm_down_shared")
+                "gemm_down_routed", "fused", "gemm_prep", "gemm_gateup_shared", "gemm_down_shared",
+                "q4_gateup_routed", "q4_down_routed")
 
 SYMBOLS = ("ds4moe_create", "ds4moe_route", "ds4moe_forward", "ds4moe_set_path", "ds4moe_dequantize",
            "ds4moe_rmsnorm", "ds4moe_forward_stack", "ds4moe_timing_enable", "ds4moe_timing_read",
@@ -41,7 +43,8 @@ class Desc(ctypes.Structure):
                 ("max_tokens", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("up", ctypes.c_void_p), ("down", ctypes.c_void_p), ("codebook", ctypes.c_void_p),
-                ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p)]
+                ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p),
+                ("expert_format", ctypes.c_int32)]
 
 
 _lib = None
@@ -121,7 +124,8 @@ class MoELayer:
     ``weights`` holds device tensors in the canonical block layout:
     router fp32 [NE, E], router_bias fp32 [NE] or None, gate/up uint8
     [NE, F, E/256, 66], down uint8 [NE, E, F/256, 84], codebook (host, 256
-    uint16 values), sh_gate/sh_up/sh_down bf16 or None.
+    uint16 values), sh_gate/sh_up/sh_down bf16 or None; with ``fmt`` "q4"
+    (weights["fmt"]) gate, up and down are uint8 [..., 144] Q4_K-style blocks.
     """
 
     def __init__(self, spec, weights: dict, max_tokens: int, act_dtype: int = BF16, stream=None):
@@ -129,17 +133,19 @@ class MoELayer:
         L = load_library()
         cb = np.ascontiguousarray(weights["codebook"], dtype=np.uint16)
         self._cb = cb
+        fmt = FMT_Q4 if weights.get("fmt", "q2") == "q4" else FMT_Q2
         d = Desc(ABI_VERSION, spec.n_embd, spec.n_ff, spec.n_expert, spec.top_k,
                  1 if weights.get("sh_gate") is not None else 0, max_tokens, act_dtype,
                  _ptr(weights["router"]), _ptr(weights.get("router_bias")), _ptr(weights["gate"]),
                  _ptr(weights["up"]), _ptr(weights["down"]), cb.ctypes.data,
-                 _ptr(weights.get("sh_gate")), _ptr(weights.get("sh_up")), _ptr(weights.get("sh_down")))
+                 _ptr(weights.get("sh_gate")), _ptr(weights.get("sh_up")), _ptr(weights.get("sh_down")), fmt)
         h = ctypes.c_void_p()
         _check(L.ds4moe_create(ctypes.byref(d), _stream(stream), ctypes.byref(h)))
         self.h = h
         self.spec = spec
         self.max_tokens = max_tokens
         self.act_dtype = act_dtype
+        self.fmt = fmt
 
     def close(self):
         if getattr(self, "h", None):
@@ -276,7 +282,7 @@ def upload_layer(layer, device="cuda"):
         return x.to(device)
 
     return dict(router=t(layer.router), router_bias=t(layer.router_bias), gate=t(layer.gate), up=t(layer.up),
-                down=t(layer.down), codebook=layer.codebook,
+                down=t(layer.down), codebook=layer.codebook, fmt=getattr(layer, "fmt", "q2"),
                 sh_gate=t(None if layer.sh_gate is None else layer.sh_gate.view(np.int16), torch.bfloat16),
                 sh_up=t(None if layer.sh_up is None else layer.sh_up.view(np.int16), torch.bfloat16),
                 sh_down=t(None if layer.sh_down is None else layer.sh_down.view(np.int16), torch.bfloat16))

@@ -39,6 +39,9 @@ struct Layer {
     const uint8_t *q2k_sc;          // [NE][E][nbf][16]
     const uint32_t *q2k_dd;         // [NE][E][nbf]
     const uint16_t *sh_gate, *sh_up, *sh_down;
+    int fmt;                        // 0: IQ2 gate/up + Q2_K down; 1: Q4_K gate, up and down
+    const uint8_t *q4_qs[3];        // Q4_K gate, up, down: [NE][rows][blocks][128] quants
+    const uint4 *q4_meta[3];        //   and [NE][rows][blocks] 16-byte d | dmin | 6-bit fields
 };
 
 // Workspace (device), carved from one allocation at create time.
@@ -154,7 +157,7 @@ hipError_t launch_gemv_down_shared(const Layer &L, const Work &W, int n_tok, flo
 enum TimingKind {
     TK_ROUTE = 0, TK_GU_ROUTED = 1, TK_GU_SHARED = 2, TK_DN_ROUTED = 3, TK_DN_SHARED = 4,
     TK_GEMM_GU_ROUTED = 5, TK_GEMM_DN_ROUTED = 6, TK_FUSED = 7, TK_GEMM_PREP = 8, TK_GEMM_GU_SHARED = 9,
-    TK_GEMM_DN_SHARED = 10, TK_COUNT = 11
+    TK_GEMM_DN_SHARED = 10, TK_Q4_GU_ROUTED = 11, TK_Q4_DN_ROUTED = 12, TK_COUNT = 13
 };
 
 bool gemm_enabled();
@@ -171,5 +174,10 @@ hipError_t launch_decode_fused(const Layer &L, const Work &W, const void *x, flo
                                unsigned long long ep, hipStream_t s);
 
 hipError_t launch_rmsnorm(const float *h, int n_tok, int n_embd, double eps, uint16_t *x, hipStream_t s);
+
+hipError_t launch_repack_q4k(const uint8_t *canon, int64_t n_blocks, uint4 *meta, uint8_t *qs, hipStream_t s);
+hipError_t launch_dequant_q4k(const Layer &L, int which, int expert, float *dst, hipStream_t s);
+hipError_t launch_q4_gateup_routed(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);
+hipError_t launch_q4_down_routed(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
 
 }  // namespace ds4

@@ -138,6 +138,37 @@ static size_t carve_static(const Layer &L, char *base, Work &S) {
     return off;
 }
 
+// One call of at most GEMV_MAX_TOK tokens on a q4 layer: router, shared
+// gate/up, routed gate/up (Q4_K), routed down (Q4_K), shared down.
+static int run_q4_chunk(ds4moe *h, const Work &W, const void *x, int n, float *out, unsigned long long ep,
+                        hipStream_t s, bool timed) {
+    const Layer &L = h->L;
+    int tb = timed ? h->tbegin(TK_ROUTE, s) : -1;
+    int rc = check_launch(h, launch_route(L, W, x, n, s, ep), "q4 route");
+    h->tend(tb, s);
+    if (rc) return rc;
+    if (L.n_shared) {
+        tb = timed ? h->tbegin(TK_GU_SHARED, s) : -1;
+        rc = check_launch(h, launch_gemv_gateup_shared(L, W, x, n, s), "q4 shared gate/up");
+        h->tend(tb, s);
+        if (rc) return rc;
+    }
+    tb = timed ? h->tbegin(TK_Q4_GU_ROUTED, s) : -1;
+    rc = check_launch(h, launch_q4_gateup_routed(L, W, x, n, s), "q4 routed gate/up");
+    h->tend(tb, s);
+    if (rc) return rc;
+    tb = timed ? h->tbegin(TK_Q4_DN_ROUTED, s) : -1;
+    rc = check_launch(h, launch_q4_down_routed(L, W, n, out, s), "q4 routed down");
+    h->tend(tb, s);
+    if (rc) return rc;
+    if (L.n_shared) {
+        tb = timed ? h->tbegin(TK_DN_SHARED, s) : -1;
+        rc = check_launch(h, launch_gemv_down_shared(L, W, n, out, s), "q4 shared down");
+        h->tend(tb, s);
+    }
+    return rc;
+}
+
 extern "C" {
 
 const char *ds4moe_last_error(void) { return g_err.c_str(); }
@@ -158,7 +189,10 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
         return fail(DS4MOE_EINVAL, "create: max_tokens %d not in 1..2^20", d->max_tokens);
     if (d->act_dtype != DS4MOE_F32 && d->act_dtype != DS4MOE_BF16)
         return fail(DS4MOE_EINVAL, "create: act_dtype %d", d->act_dtype);
-    if (!d->router || !d->gate || !d->up || !d->down || !d->codebook)
+    if (d->expert_format != DS4MOE_FMT_Q2 && d->expert_format != DS4MOE_FMT_Q4)
+        return fail(DS4MOE_EINVAL, "create: expert_format %d", d->expert_format);
+    const bool q4 = d->expert_format == DS4MOE_FMT_Q4;
+    if (!d->router || !d->gate || !d->up || !d->down || (!q4 && !d->codebook))
         return fail(DS4MOE_EINVAL, "create: NULL router/gate/up/down/codebook");
     if (d->n_shared && (!d->sh_gate || !d->sh_up || !d->sh_down))
         return fail(DS4MOE_EINVAL, "create: n_shared = 1 but a shared-expert pointer is NULL");
@@ -184,10 +218,21 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     uint16_t *rhml = (uint16_t *)A(3 * NE * E * 2);
     float *rnorm = (float *)A(NE * 4);
     uint16_t *cb = (uint16_t *)A(512);
-    uint8_t *gq = (uint8_t *)A(gu_blocks * 64), *uq = (uint8_t *)A(gu_blocks * 64);
-    uint16_t *gd = (uint16_t *)A(gu_blocks * 2), *ud = (uint16_t *)A(gu_blocks * 2);
-    uint8_t *dq = (uint8_t *)A(dn_blocks * 64), *dsc = (uint8_t *)A(dn_blocks * 16);
-    uint32_t *ddd = (uint32_t *)A(dn_blocks * 4);
+    // the routed planes of the layer's format (the other format's stay NULL)
+    uint8_t *gq = nullptr, *uq = nullptr, *dq = nullptr, *dsc = nullptr;
+    uint16_t *gd = nullptr, *ud = nullptr;
+    uint32_t *ddd = nullptr;
+    uint8_t *q4q[3] = {nullptr, nullptr, nullptr};
+    uint4 *q4m[3] = {nullptr, nullptr, nullptr};
+    if (q4) {
+        const int64_t nbk[3] = {gu_blocks, gu_blocks, dn_blocks};
+        for (int i = 0; i < 3; ++i) q4q[i] = (uint8_t *)A(nbk[i] * 128), q4m[i] = (uint4 *)A(nbk[i] * 16);
+    } else {
+        gq = (uint8_t *)A(gu_blocks * 64), uq = (uint8_t *)A(gu_blocks * 64);
+        gd = (uint16_t *)A(gu_blocks * 2), ud = (uint16_t *)A(gu_blocks * 2);
+        dq = (uint8_t *)A(dn_blocks * 64), dsc = (uint8_t *)A(dn_blocks * 16);
+        ddd = (uint32_t *)A(dn_blocks * 4);
+    }
     uint16_t *sg = nullptr, *su = nullptr, *sd = nullptr;
     if (d->n_shared) {
         sg = (uint16_t *)A(F * E * 2);
@@ -290,15 +335,25 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     CK(hipMemcpyAsync(router, d->router, NE * E * 4, hipMemcpyDeviceToDevice, s));
     if (bias) CK(hipMemcpyAsync(bias, d->router_bias, NE * 4, hipMemcpyDeviceToDevice, s));
     CK(launch_router_prep(router, (int)NE, (int)E, rhml, rnorm, s));
-    CK(hipMemcpyAsync(cb, d->codebook, 512, hipMemcpyHostToDevice, s));
+    if (!q4) CK(hipMemcpyAsync(cb, d->codebook, 512, hipMemcpyHostToDevice, s));
     if (d->n_shared) {
         CK(hipMemcpyAsync(sg, d->sh_gate, F * E * 2, hipMemcpyDeviceToDevice, s));
         CK(hipMemcpyAsync(su, d->sh_up, F * E * 2, hipMemcpyDeviceToDevice, s));
         CK(hipMemcpyAsync(sd, d->sh_down, E * F * 2, hipMemcpyDeviceToDevice, s));
     }
-    CK(launch_repack_iq2((const uint8_t *)d->gate, gu_blocks, gq, gd, s));
-    CK(launch_repack_iq2((const uint8_t *)d->up, gu_blocks, uq, ud, s));
-    CK(launch_repack_q2k((const uint8_t *)d->down, dn_blocks, dq, dsc, ddd, s));
+    if (q4) {
+        if (((uintptr_t)d->gate | (uintptr_t)d->up | (uintptr_t)d->down) & 15u) {
+            delete h;
+            return fail(DS4MOE_EINVAL, "create: Q4_K weights must be 16-byte aligned");
+        }
+        CK(launch_repack_q4k((const uint8_t *)d->gate, gu_blocks, q4m[0], q4q[0], s));
+        CK(launch_repack_q4k((const uint8_t *)d->up, gu_blocks, q4m[1], q4q[1], s));
+        CK(launch_repack_q4k((const uint8_t *)d->down, dn_blocks, q4m[2], q4q[2], s));
+    } else {
+        CK(launch_repack_iq2((const uint8_t *)d->gate, gu_blocks, gq, gd, s));
+        CK(launch_repack_iq2((const uint8_t *)d->up, gu_blocks, uq, ud, s));
+        CK(launch_repack_q2k((const uint8_t *)d->down, dn_blocks, dq, dsc, ddd, s));
+    }
     CK(hipStreamSynchronize(s));
 #undef CK
     L.router = router, L.router_bias = bias, L.codebook = cb;
@@ -306,6 +361,8 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     L.iq2_qs[0] = gq, L.iq2_qs[1] = uq, L.iq2_d[0] = gd, L.iq2_d[1] = ud;
     L.q2k_qs = dq, L.q2k_sc = dsc, L.q2k_dd = ddd;
     L.sh_gate = sg, L.sh_up = su, L.sh_down = sd;
+    L.fmt = q4 ? 1 : 0;
+    for (int i = 0; i < 3; ++i) L.q4_qs[i] = q4q[i], L.q4_meta[i] = q4m[i];
     h->decode_grid = decode_grid(d->act_dtype == DS4MOE_BF16);
     if (h->decode_grid <= 0) {
         delete h;
@@ -325,6 +382,8 @@ int ds4moe_destroy(ds4moe_t *h) {
 int ds4moe_set_path(ds4moe_t *h, int32_t path) {
     if (!h) return fail(DS4MOE_EINVAL, "set_path: NULL handle");
     if (path < DS4MOE_PATH_AUTO || path > DS4MOE_PATH_GEMM) return fail(DS4MOE_EINVAL, "set_path: %d", path);
+    if (path == DS4MOE_PATH_GEMM && h->L.fmt == 1)
+        return fail(DS4MOE_EUNSUPPORTED, "set_path: a q4 layer has no grouped GEMM path");
     h->path = path;
     return DS4MOE_OK;
 }
@@ -394,6 +453,22 @@ int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *
     if (n_tok > 0 && !aligned16(out)) return fail(DS4MOE_EINVAL, "forward: out is not 16-byte aligned");
     if (n_tok == 0) return DS4MOE_OK;
     if ((rc = stream_checks((hipStream_t)stream, "forward"))) return rc;
+    if (h->L.fmt == 1) {
+        // q4: the GEMV kernels (set_path refuses the GEMM path), in chunks of
+        // up to GEMV_MAX_TOK tokens; the routing of a call of more tokens is
+        // not kept for ds4moe_last_routing
+        hipStream_t s = (hipStream_t)stream;
+        h->last_n_tok = n_tok <= GEMV_MAX_TOK ? n_tok : -1;
+        h->last_static = false;
+        const size_t xb = h->L.act_dtype == DS4MOE_BF16 ? 2 : 4;
+        for (int c0 = 0; c0 < n_tok; c0 += GEMV_MAX_TOK) {
+            const int nc = std::min(GEMV_MAX_TOK, n_tok - c0);
+            const void *xc = (const char *)x + (size_t)c0 * h->L.n_embd * xb;
+            float *oc = out + (size_t)c0 * h->L.n_embd;
+            if ((rc = run_q4_chunk(h, h->W, xc, nc, oc, h->route_calls++, s, true))) return rc;
+        }
+        return DS4MOE_OK;
+    }
     int path = h->path;
     // one token: the fused decode kernel; more: the grouped GEMMs, which at 2-4
     // tokens (K split over more workgroups) also beat the GEMV kernels.  fp32
@@ -497,6 +572,12 @@ int ds4moe_forward_static(ds4moe_t *h, const void *x, int32_t n_tok, float *out,
     const unsigned long long ep = g_static_calls[dev].fetch_add(1);
     h->last_n_tok = n_tok;
     h->last_static = true;
+    if (h->L.fmt == 1) {
+        // the router's tickets start at zero
+        rc = check_launch(h, launch_fill_u32((uint32_t *)S.counters, 64, 0u, s), "forward_static clear");
+        if (rc) return rc;
+        return run_q4_chunk(h, S, x, n_tok, out, ep, s, false);
+    }
     if (n_tok == 1)
         return check_launch(h, launch_decode_fused(h->L, S, x, out, h->decode_grid, ep, s), "forward_static decode");
     // the router's tickets start at zero
@@ -523,7 +604,9 @@ int ds4moe_dequantize(ds4moe_t *h, int32_t expert, int32_t which, float *dst, vo
     if (which < 0 || which > 2) return fail(DS4MOE_EINVAL, "dequantize: which %d", which);
     if (!dst) return fail(DS4MOE_EINVAL, "dequantize: NULL dst");
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = (which < 2) ? launch_dequant_iq2(h->L, which, expert, dst, s) : launch_dequant_q2k(h->L, expert, dst, s);
+    hipError_t e = h->L.fmt == 1 ? launch_dequant_q4k(h->L, which, expert, dst, s)
+                   : (which < 2)  ? launch_dequant_iq2(h->L, which, expert, dst, s)
+                                  : launch_dequant_q2k(h->L, expert, dst, s);
     return check_launch(h, e, "dequantize");
 }
 

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define DS4MOE_ABI_VERSION 1
+#define DS4MOE_ABI_VERSION 2
 
 enum {
     DS4MOE_OK = 0,
@@ -78,6 +78,12 @@ enum {
 };
 
 enum { DS4MOE_F32 = 0, DS4MOE_BF16 = 1 };
+
+/* Routed-expert block formats (ds4moe_desc.expert_format). */
+enum {
+    DS4MOE_FMT_Q2 = 0, /* gate/up IQ2-style (66 B / 256 weights), down Q2_K-style (84 B) */
+    DS4MOE_FMT_Q4 = 1  /* gate, up and down Q4_K-style (144 B / 256 weights) */
+};
 
 /* Kernel path selection for ds4moe_forward (ds4moe_set_path). */
 enum {
@@ -103,6 +109,17 @@ typedef struct ds4moe ds4moe_t; /* opaque; one per MoE layer */
  *   codebook:    host, uint16 [256].
  *   sh_gate, sh_up: device, bf16 [n_ff][n_embd]; sh_down: device, bf16 [n_embd][n_ff];
  *                all NULL when n_shared == 0.
+ *   expert_format: DS4MOE_FMT_Q2 (the layouts above) or DS4MOE_FMT_Q4: gate, up
+ *                and down are all Q4_K-style blocks, [n_expert][rows][cols/256][144
+ *                bytes]: fp16 d, fp16 dmin, sixteen 6-bit fields as a little-
+ *                endian bit stream (field j at bits 6j..6j+5: sc of sub-block j
+ *                for j < 8, m of sub-block j-8 for j >= 8; sub-block = 32 weights),
+ *                then 128 bytes of 4-bit quants (weight i in nibble i%2 of byte
+ *                i/2, low nibble first); w = d sc q - dmin m.  The q4 model keeps
+ *                its routed experts in Q4_K ("ds4 深度实战...", section 2.1; the
+ *                pages give no layout: this one is a stand-in).  codebook is
+ *                unused.  A q4 layer runs the dequant-fused GEMV kernels for
+ *                every call, in chunks of up to 4 tokens.
  */
 typedef struct {
     int32_t abi_version; /* DS4MOE_ABI_VERSION */
@@ -116,6 +133,7 @@ typedef struct {
     const uint16_t *sh_gate;
     const uint16_t *sh_up;
     const uint16_t *sh_down;
+    int32_t expert_format; /* DS4MOE_FMT_Q2 or DS4MOE_FMT_Q4 */
 } ds4moe_desc;
 
 /*
@@ -191,7 +209,8 @@ int ds4moe_set_path(ds4moe_t *h, int32_t path);
 /*
  * Debug/test: decode one routed expert matrix from the library's repacked
  * layout ("Redis 作者出手！ds4...", section 2.3: block_iq2_xxs for gate/up,
- * block_q2_K for down, each 256 weights per super-block).  which: 0 gate, 1 up ([n_ff][n_embd] fp32), 2 down ([n_embd][n_ff]
+ * block_q2_K for down, each 256 weights per super-block; Q4_K-style for all
+ * three in a q4 layer).  which: 0 gate, 1 up ([n_ff][n_embd] fp32), 2 down ([n_embd][n_ff]
  * fp32).  dst: device, fp32, that many elements.
  */
 int ds4moe_dequantize(ds4moe_t *h, int32_t expert, int32_t which, float *dst, void *stream);
@@ -234,10 +253,11 @@ int ds4moe_forward_stack(ds4moe_t *const *layers, int32_t n_layers, float *h, in
  * gate/up GEMV, 2 shared gate/up GEMV, 3 routed down GEMV, 4 shared down GEMV,
  * 5 routed gate/up GEMM, 6 routed down GEMM, 7 fused decode kernel, 8 batched
  * path preparation (activation copies, chunk table), 9 shared gate/up GEMM,
- * 10 shared down GEMM.  ms and counts have room for DS4MOE_TIMING_KINDS
- * entries each.  Enabling resets the counters.
+ * 10 shared down GEMM, 11 routed gate/up Q4_K GEMV, 12 routed down Q4_K
+ * GEMV.  ms and counts have room for DS4MOE_TIMING_KINDS entries each.
+ * Enabling resets the counters.
  */
-#define DS4MOE_TIMING_KINDS 11
+#define DS4MOE_TIMING_KINDS 13
 int ds4moe_timing_enable(ds4moe_t *h, int32_t enable);
 int ds4moe_timing_read(ds4moe_t *h, double *ms, int64_t *counts);
 

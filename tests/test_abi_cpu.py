@@ -43,17 +43,21 @@ def test_validation_without_gpu(lib):
     # NULL description
     assert lib.ds4moe_create(None, None, ctypes.byref(h)) == m.EINVAL
     # bad sizes: n_embd not a supported power of two
-    d = m.Desc(m.ABI_VERSION, 300, 256, 8, 2, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None)
+    d = m.Desc(m.ABI_VERSION, 300, 256, 8, 2, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 0)
     assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
     assert b"n_embd" in lib.ds4moe_last_error()
     # top_k > n_expert
-    d = m.Desc(m.ABI_VERSION, 256, 256, 4, 6, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None)
+    d = m.Desc(m.ABI_VERSION, 256, 256, 4, 6, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 0)
     assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
     # wrong ABI version
-    d = m.Desc(99, 256, 256, 8, 2, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None)
+    d = m.Desc(99, 256, 256, 8, 2, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 0)
     assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
+    # unknown expert format
+    d = m.Desc(m.ABI_VERSION, 256, 256, 8, 2, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 7)
+    assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
+    assert b"expert_format" in lib.ds4moe_last_error()
     # shared expert requested but missing
-    d = m.Desc(m.ABI_VERSION, 256, 256, 8, 2, 1, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None)
+    d = m.Desc(m.ABI_VERSION, 256, 256, 8, 2, 1, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 0)
     assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
     # NULL handle on every per-handle entry point
     assert lib.ds4moe_forward(None, None, 1, None, None) == m.EINVAL
