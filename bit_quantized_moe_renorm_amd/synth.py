@@ -40,7 +40,8 @@ Q2K_BLOCK_BYTES = 84        # scales[16] + qs[64] + fp16 d + fp16 dmin
 Q4K_BLOCK_BYTES = 144       # fp16 d + fp16 dmin + 16 six-bit scale/min fields + qs[128]
 
 _TID = dict(router=1, router_bias=2, gate=3, up=4, down=5, sh_gate=6, sh_up=7,
-            sh_down=8, x=9, codebook=10, h0=11, zipf=12)
+            sh_down=8, x=9, codebook=10, h0=11, zipf=12, hash=13, ids=14)
+N_VOCAB = 129280            # DS4_N_VOCAB, the model's vocabulary size
 
 
 def rng_for(seed: int, what: str) -> np.random.Generator:
@@ -153,6 +154,7 @@ class Layer:
     sh_down: Optional[np.ndarray]
     extra: dict = field(default_factory=dict)
     fmt: str = "q2"
+    hash_table: Optional[np.ndarray] = None   # int32 [n_vocab, top_k] for a hash-routed layer
 
 
 def zipf_router_bias(seed: int, n_expert: int, s: float = 1.1) -> np.ndarray:
@@ -185,6 +187,20 @@ def make_layer(spec: LayerSpec, seed: int, zipf_bias: bool = False, shared: bool
     else:
         sg = su = sd = None
     return Layer(spec, seed, router, bias, gate, up, down, codebook(), sg, su, sd, fmt=fmt)
+
+
+def hash_table(seed: int, n_vocab: int, n_expert: int, top_k: int) -> np.ndarray:
+    """Per-token-id expert table of a hash-routed layer, int32 ``[n_vocab, top_k]``:
+    row v holds top_k distinct experts drawn uniformly (the model's own table
+    is part of its weights, which the pages do not give)."""
+    rng = rng_for(seed, "hash")
+    keys = rng.random((n_vocab, n_expert))
+    return np.argsort(keys, axis=1)[:, :top_k].astype(np.int32)
+
+
+def token_ids(seed: int, n_tok: int, n_vocab: int = N_VOCAB, start: int = 0) -> np.ndarray:
+    """Rows ``start .. start+n_tok`` of the seed's uniform token-id stream (int32)."""
+    return rng_for(seed, "ids").integers(0, n_vocab, size=start + n_tok, dtype=np.int64)[start:].astype(np.int32)
 
 
 def activations(seed: int, n_tok: int, n_embd: int, bf16: bool = True, start: int = 0) -> np.ndarray:

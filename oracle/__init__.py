@@ -47,7 +47,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_route.restype = i32
         L.oracle_bucket.argtypes = [P, i64, i32, i32, P, P]
         L.oracle_forward.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, i32, P, i64,
-                                     P, P, P]
+                                     P, P, i64, P, P, P]
+        L.oracle_route_hashed.argtypes = [P, i32, i64, i32, P, P, i32, i32, P, P, i64, P, P, P, P]
+        L.oracle_route_hashed.restype = i32
         L.oracle_forward.restype = i32
         L.oracle_rmsnorm.argtypes = [P, i64, i32, f64, P, P]
         L.oracle_num_threads.restype = i32
@@ -142,6 +144,27 @@ def route(x, router, bias, top_k):
     return logits, idx, w, w64
 
 
+def route_hashed(x, router, bias, top_k, token_ids, table):
+    """Hash routing: experts from ``table[token_ids[t]]`` (slot order), weights the
+    softmax renormalised over them.  Returns (logits, idx, w, w64) like ``route``."""
+    x, isbf = _x(x)
+    n, E = x.shape
+    router = np.ascontiguousarray(router, dtype=np.float32)
+    NE = router.shape[0]
+    bias = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+    tab = np.ascontiguousarray(table, dtype=np.int32)
+    assert ids.shape == (n,) and tab.shape[1] == top_k
+    logits = np.empty((n, NE), np.float32)
+    idx = np.empty((n, top_k), np.int32)
+    w = np.empty((n, top_k), np.float32)
+    w64 = np.empty((n, top_k), np.float64)
+    rc = lib().oracle_route_hashed(_p(x), isbf, n, E, _p(router), _p(bias), NE, top_k, _p(ids), _p(tab),
+                                   tab.shape[0], _p(logits), _p(idx), _p(w), _p(w64))
+    assert rc == 0, rc
+    return logits, idx, w, w64
+
+
 def bucket(idx: np.ndarray, n_expert: int):
     """Per-expert token lists: (offsets int32 [NE+1], tokens int32 [n*k])."""
     idx = np.ascontiguousarray(idx, dtype=np.int32)
@@ -152,8 +175,9 @@ def bucket(idx: np.ndarray, n_expert: int):
     return offsets, tokens
 
 
-def forward(layer, x, rows=None):
-    """MoE(x) for the tokens in ``rows`` (default all): returns (out fp64 [r, E], idx, w64)."""
+def forward(layer, x, rows=None, token_ids=None):
+    """MoE(x) for the tokens in ``rows`` (default all): returns (out fp64 [r, E], idx, w64).
+    A hash-routed layer (``layer.hash_table`` set) needs the tokens' ids."""
     x, isbf = _x(x)
     n, E = x.shape
     s = layer.spec
@@ -162,10 +186,17 @@ def forward(layer, x, rows=None):
     out = np.empty((len(rows), E), np.float64)
     idx = np.empty((len(rows), s.top_k), np.int32)
     w = np.empty((len(rows), s.top_k), np.float64)
+    tab = getattr(layer, "hash_table", None)
+    ids = None
+    if tab is not None:
+        assert token_ids is not None and len(token_ids) == n, "a hash-routed layer needs the token ids"
+        tab = np.ascontiguousarray(tab, dtype=np.int32)
+        ids = np.ascontiguousarray(token_ids, dtype=np.int32)
     rc = lib().oracle_forward(E, s.n_ff, s.n_expert, s.top_k, _fmt(layer), _p(layer.router), _p(layer.router_bias),
                               _p(layer.gate), _p(layer.up), _p(layer.down), _p(layer.codebook),
                               _p(layer.sh_gate), _p(layer.sh_up), _p(layer.sh_down), _p(x), isbf,
-                              _p(rows), len(rows), _p(out), _p(idx), _p(w))
+                              _p(rows), len(rows), _p(ids), _p(tab), 0 if tab is None else tab.shape[0],
+                              _p(out), _p(idx), _p(w))
     assert rc == 0, rc
     return out, idx, w
 
@@ -180,7 +211,7 @@ def rmsnorm(h: np.ndarray, eps: float = 1e-6):
     return xb, x64
 
 
-def stack(layers, h0: np.ndarray, eps: float = 1e-6):
+def stack(layers, h0: np.ndarray, eps: float = 1e-6, token_ids=None):
     """A stack of MoE layers on the residual stream h (fp32 [n, E]).
 
     Each layer normalises h (RMSNorm with unit gain, ``rmsnorm`` above), runs
@@ -188,14 +219,20 @@ def stack(layers, h0: np.ndarray, eps: float = 1e-6):
     in fp64 and stored in fp32, the residual stream's type at the block's
     boundary.  The pages describe the model's hyper-connection mixing rather
     than a per-layer norm for this block; the stack is the plainest one around
-    it.  Returns (h after the last layer, [x_l bf16 bits], [idx_l], [logits_l]).
+    it.  A hash-routed layer (``hash_table`` set) routes by the tokens' ids,
+    ``token_ids`` [n].  Returns (h after the last layer, [x_l bf16 bits],
+    [idx_l], [logits_l]).
     """
     h = np.ascontiguousarray(h0, dtype=np.float32).copy()
     xs, idxs, logits = [], [], []
     for layer in layers:
         xb, _ = rmsnorm(h, eps)
-        lg, idx, _, _ = route(xb, layer.router, layer.router_bias, layer.spec.top_k)
-        y, _, _ = forward(layer, xb)
+        if getattr(layer, "hash_table", None) is not None:
+            lg, idx, _, _ = route_hashed(xb, layer.router, layer.router_bias, layer.spec.top_k, token_ids,
+                                         layer.hash_table)
+        else:
+            lg, idx, _, _ = route(xb, layer.router, layer.router_bias, layer.spec.top_k)
+        y, _, _ = forward(layer, xb, token_ids=token_ids)
         h = (h.astype(np.float64) + y).astype(np.float32)
         xs.append(xb)
         idxs.append(idx)

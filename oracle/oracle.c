@@ -14,6 +14,9 @@
  *  - the router: fp64-accumulated logits rounded to fp32, a softmax over all
  *    experts, the top-k experts (lower index wins exact ties) and the weights
  *    renormalised over the selected experts;
+ *  - hash routing for the model's hash layers: the experts looked up from a
+ *    per-token-id table, the weights the router's softmax renormalised over
+ *    them (the pages give only the layer count; this is the reading used);
  *  - per-expert token lists (ascending token order);
  *  - the block output: for each token, the weighted sum of its selected
  *    experts' SwiGLU feed-forward outputs plus the shared expert's output,
@@ -266,6 +269,52 @@ static void route_token(const double *xt, int n_embd, const float *router, const
 }
 
 /*
+ * Hash routing ([P5] section 2.1: DS4_N_HASH_LAYER = 3, the model's hash
+ * layers; the pages give nothing more).  Reading used: in a hash layer the k
+ * experts of a token are not chosen by the logits but looked up from a fixed
+ * table by the token's id, table[id][0..k-1] (k distinct experts, in slot
+ * order); the weights are still the router's softmax probabilities,
+ * renormalised over those k experts: w[j] = p[table[id][j]] / sum_j p[...].
+ * logits and p are as in route_token.  Returns 0, or -1 if id is outside
+ * [0, n_vocab).
+ */
+static int route_token_hashed(const double *xt, int n_embd, const float *router, const float *bias,
+                              int n_expert, int top_k, const int32_t *table, int64_t n_vocab, int32_t id,
+                              float *logits, double *p, int32_t *idx, double *w)
+{
+    if (id < 0 || id >= n_vocab)
+        return -1;
+    for (int e = 0; e < n_expert; ++e) {
+        double s = 0.0;
+        const float *r = router + (int64_t)e * n_embd;
+        for (int i = 0; i < n_embd; ++i)
+            s += xt[i] * (double)r[i];
+        if (bias)
+            s += (double)bias[e];
+        logits[e] = (float)s;
+    }
+    double mx = -INFINITY;
+    for (int e = 0; e < n_expert; ++e)
+        if ((double)logits[e] > mx)
+            mx = logits[e];
+    double z = 0.0;
+    for (int e = 0; e < n_expert; ++e) {
+        p[e] = exp((double)logits[e] - mx);
+        z += p[e];
+    }
+    for (int e = 0; e < n_expert; ++e)
+        p[e] /= z;
+    double sum = 0.0;
+    for (int j = 0; j < top_k; ++j) {
+        idx[j] = table[(int64_t)id * top_k + j];
+        sum += p[idx[j]];
+    }
+    for (int j = 0; j < top_k; ++j)
+        w[j] = p[idx[j]] / sum;
+    return 0;
+}
+
+/*
  * Route n_tok tokens.  x: [n_tok][n_embd] bf16 bits (x_is_bf16) or fp32.
  * router: [n_expert][n_embd] fp32; bias: [n_expert] fp32 or NULL.
  * Outputs (any may be NULL): logits [n_tok][n_expert] fp32, idx [n_tok][top_k],
@@ -311,6 +360,55 @@ int oracle_route(const void *x, int x_is_bf16, int64_t n_tok, int n_embd, const 
         free(wt);
     }
     return bad ? -2 : 0;
+}
+
+/*
+ * Hash-routed tokens (route_token_hashed): as oracle_route, with token_ids
+ * [n_tok] and table [n_vocab][top_k].  Returns 0, -1 on bad sizes, -3 if an
+ * id is out of range.
+ */
+int oracle_route_hashed(const void *x, int x_is_bf16, int64_t n_tok, int n_embd, const float *router,
+                        const float *bias, int n_expert, int top_k, const int32_t *token_ids,
+                        const int32_t *table, int64_t n_vocab, float *logits, int32_t *idx, float *w,
+                        double *w64)
+{
+    if (n_tok < 0 || n_embd <= 0 || n_expert <= 0 || top_k <= 0 || top_k > n_expert || n_vocab <= 0)
+        return -1;
+    int bad = 0;
+    for (int64_t t = 0; t < n_tok; ++t) {
+        double *xt = malloc(sizeof(double) * n_embd);
+        double *p = malloc(sizeof(double) * n_expert);
+        float *lg = malloc(sizeof(float) * n_expert);
+        int32_t *id = malloc(sizeof(int32_t) * top_k);
+        double *wt = malloc(sizeof(double) * top_k);
+        if (!xt || !p || !lg || !id || !wt) {
+            bad = -2;
+        } else {
+            for (int i = 0; i < n_embd; ++i)
+                xt[i] = x_value(x, x_is_bf16, t * n_embd + i);
+            if (route_token_hashed(xt, n_embd, router, bias, n_expert, top_k, table, n_vocab, token_ids[t], lg,
+                                   p, id, wt))
+                bad = -3;
+            else
+                for (int j = 0; j < top_k; ++j) {
+                    if (logits)
+                        for (int e = 0; e < n_expert; ++e)
+                            logits[t * n_expert + e] = lg[e];
+                    if (idx)
+                        idx[t * top_k + j] = id[j];
+                    if (w)
+                        w[t * top_k + j] = (float)wt[j];
+                    if (w64)
+                        w64[t * top_k + j] = wt[j];
+                }
+        }
+        free(xt);
+        free(p);
+        free(lg);
+        free(id);
+        free(wt);
+    }
+    return bad;
 }
 
 /*
@@ -400,13 +498,17 @@ static void ffn_bf16(const uint16_t *wg, const uint16_t *wu, const uint16_t *wd,
  * blocks in the same shapes.  sh_*: bf16 bits or NULL when there is no shared expert.
  * out: [n_rows][n_embd] fp64, overwritten.  Optional outputs (NULL to skip):
  * idx_out [n_rows][top_k], w_out [n_rows][top_k] fp64.
- * Returns 0, -1 on bad sizes, -2 on allocation failure.
+ * hash_table (NULL for a learned-routing layer): [n_vocab][top_k], with
+ * token_ids [n_tok] (indexed by the row's token): the layer routes by
+ * route_token_hashed.
+ * Returns 0, -1 on bad sizes, -2 on allocation failure, -3 on a token id out of range.
  */
 int oracle_forward(int n_embd, int n_ff, int n_expert, int top_k, int expert_format, const float *router,
                    const float *bias, const uint8_t *gate, const uint8_t *up, const uint8_t *down,
                    const uint16_t *codebook, const uint16_t *sh_gate, const uint16_t *sh_up,
                    const uint16_t *sh_down, const void *x, int x_is_bf16, const int32_t *rows,
-                   int64_t n_rows, double *out, int32_t *idx_out, double *w_out)
+                   int64_t n_rows, const int32_t *token_ids, const int32_t *hash_table, int64_t n_vocab,
+                   double *out, int32_t *idx_out, double *w_out)
 {
     if (n_embd % QK || n_ff % QK || n_embd <= 0 || n_ff <= 0 || top_k <= 0 || top_k > n_expert ||
         n_rows < 0 || (expert_format != 0 && expert_format != 1))
@@ -435,6 +537,12 @@ int oracle_forward(int n_embd, int n_ff, int n_expert, int top_k, int expert_for
         if (!lg || !p) {
 #pragma omp atomic write
             bad = 1;
+        } else if (hash_table) {
+            if (route_token_hashed(xs + r * n_embd, n_embd, router, bias, n_expert, top_k, hash_table, n_vocab,
+                                   token_ids[rows[r]], lg, p, idx + r * top_k, w + r * top_k)) {
+#pragma omp atomic write
+                bad = 3;
+            }
         } else {
             route_token(xs + r * n_embd, n_embd, router, bias, n_expert, top_k, lg, p, idx + r * top_k,
                         w + r * top_k);
@@ -507,7 +615,7 @@ int oracle_forward(int n_embd, int n_ff, int n_expert, int top_k, int expert_for
     free(idx);
     free(w);
     free(ys);
-    return bad ? -2 : 0;
+    return bad == 3 ? -3 : bad ? -2 : 0;
 }
 
 /*

@@ -136,10 +136,10 @@ def test_rmsnorm_pins(oracle_lib):
 
 def test_forward_rejects_bad_shapes(oracle_lib):
     lib = oracle_lib.lib()
-    rc = lib.oracle_forward(100, 256, 8, 2, 0, *([None] * 10), 0, None, 0, None, None, None)
+    rc = lib.oracle_forward(100, 256, 8, 2, 0, *([None] * 10), 0, None, 0, None, None, 0, None, None, None)
     assert rc == -1
     # an unknown expert format
-    rc = lib.oracle_forward(256, 256, 8, 2, 2, *([None] * 10), 0, None, 0, None, None, None)
+    rc = lib.oracle_forward(256, 256, 8, 2, 2, *([None] * 10), 0, None, 0, None, None, 0, None, None, None)
     assert rc == -1
 
 
