@@ -257,6 +257,54 @@ def run_decode(args, layer=None):
     return res
 
 
+def run_decode_hash(args, layer):
+    """The same decode stream through a hash-routed layer (the experts of each
+    token from its id's table row): the block's time when only the k table
+    experts' router rows are read.  Token ids: the seed's uniform id stream."""
+    import torch
+
+    import bit_quantized_moe_renorm_amd as m
+    from bit_quantized_moe_renorm_amd import synth
+
+    spec = synth.DS4
+    lay = synth.Layer(**{**layer.__dict__})
+    lay.hash_table = synth.hash_table(1, synth.N_VOCAB, spec.n_expert, spec.top_k)
+    w = m.upload_layer(lay)
+    reps = [m.MoELayer(spec, w, max_tokens=1) for _ in range(args.replicas)]
+    del w
+    x = m.to_device_x(synth.activations(1, 1000, spec.n_embd))
+    ids = m.to_device_ids(synth.token_ids(1, 1000))
+    out = torch.zeros((1000, spec.n_embd), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    R = len(reps)
+
+    def step(i):
+        t = i % 1000
+        reps[i % R].forward(x[t:t + 1], out[t:t + 1], stream, ids=ids[t:t + 1])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for r in reps:
+        assert r.status() == m.OK
+        r.close()
+    us = 1e6 * wall / args.steps
+    gbs = touched_bytes(spec, spec.top_k) / (wall / args.steps) / 1e9
+    log(f"[bench] hash-routed layer decode b=1: {args.steps / wall:.0f} tok/s, {us:.2f} us/token, "
+        f"touched-expert {gbs:.0f} GB/s = {100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s")
+    return {"value": round(args.steps / wall, 1), "unit": "tok/s", "us_per_token": round(us, 3),
+            "steps": args.steps, "warmup": args.warmup,
+            "workload": "the decode stream above through a hash-routed layer (same weights; table of "
+                        f"{synth.N_VOCAB} x {spec.top_k} experts, seed 1; token ids uniform, seed 1)",
+            "layer_GB_s": round(gbs, 1), "layer_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "router_bytes_read": spec.top_k * spec.n_embd * 4}
+
+
 def flops_prefill(spec, n):
     """Algorithmic floating-point operations of each batched-path kernel for n tokens
     (2 per multiply-add; the Q2_K min term and the shared expert's low-part
@@ -421,10 +469,13 @@ def run_stack(args):
 
     spec = synth.DS4
     L, chunk, n_pre, n_dec = args.layers, 512, 4096, 256
+    n_hash = min(args.hash_layers, L)
     devs, hosts = [], []
     t0 = time.perf_counter()
     for l in range(L):
         lay = synth.make_layer(spec, seed=4000 + l)
+        if l < n_hash:
+            lay.hash_table = synth.hash_table(4000 + l, synth.N_VOCAB, spec.n_expert, spec.top_k)
         w = m.upload_layer(lay)
         devs.append(m.MoELayer(spec, w, max_tokens=chunk))
         hosts.append(lay if not args.no_cpu_baseline else None)
@@ -437,10 +488,11 @@ def run_stack(args):
 
     # decode b = 1
     h = torch.from_numpy(synth.residual(41, n_dec + 8, spec.n_embd)).cuda()
+    ids_dec = m.to_device_ids(synth.token_ids(41, n_dec + 8))
     xb = torch.empty((1, spec.n_embd), dtype=torch.bfloat16, device="cuda")
 
     def token(t):
-        m.forward_stack(devs, h[t:t + 1], x=xb, stream=stream)
+        m.forward_stack(devs, h[t:t + 1], x=xb, stream=stream, ids=ids_dec[t:t + 1])
 
     for t in range(8):                      # warm-up tokens
         token(n_dec + t)
@@ -459,11 +511,12 @@ def run_stack(args):
 
     # prefill: 4096 tokens in 512-token chunks
     hp = torch.from_numpy(synth.residual(42, n_pre, spec.n_embd)).cuda()
+    ids_pre = m.to_device_ids(synth.token_ids(42, n_pre))
     xp = torch.empty((chunk, spec.n_embd), dtype=torch.bfloat16, device="cuda")
 
     def prefill():
         for c0 in range(0, n_pre, chunk):
-            m.forward_stack(devs, hp[c0:c0 + chunk], x=xp, stream=stream)
+            m.forward_stack(devs, hp[c0:c0 + chunk], x=xp, stream=stream, ids=ids_pre[c0:c0 + chunk])
 
     prefill()                               # warm-up pass (the stream's values are not checked here)
     torch.cuda.synchronize()
@@ -485,9 +538,11 @@ def run_stack(args):
         "steps": n_dec, "warmup": 8, "ms_per_step": round(1e3 * dec_s / n_dec, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"stack of {L} DS4-shape MoE layers (seeds 4000..{4000 + L - 1}), RMSNorm -> MoE -> "
+        "config": {"workload": f"stack of {L} DS4-shape MoE layers (seeds 4000..{4000 + L - 1}; the first "
+                               f"{n_hash} hash-routed by token id), RMSNorm -> MoE -> "
                                "residual add per layer, decode b=1 over 256 steps; prefill 4096 tokens in "
                                "512-token chunks",
+                   "hash_layers": n_hash,
                    "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)", "layers": L,
                    "decode_layer_us": round(1e6 * dec_s / n_dec / L, 3),
                    "decode_hbm_GB_s": round(dec_gbs, 1), "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
@@ -506,13 +561,15 @@ def run_stack(args):
         # each layer from the GPU's own x_l (its time is the CPU baseline)
         n_chk = args.stack_check_tokens
         hc = torch.from_numpy(synth.residual(45, n_chk, spec.n_embd)).cuda()
+        ids_np = synth.token_ids(45, n_chk)
+        ids_chk = m.to_device_ids(ids_np)
         rec = []
         for l, dev in enumerate(devs):
             xs = m.rmsnorm(hc)
             y = torch.zeros_like(hc)
             idx = []
             for t in range(n_chk):
-                dev.forward(xs[t:t + 1], y[t:t + 1])
+                dev.forward(xs[t:t + 1], y[t:t + 1], ids=ids_chk[t:t + 1])
                 idx.append(dev.last_routing(1)[0])
             torch.cuda.synchronize()
             rec.append((xs.view(torch.int16).cpu().numpy().view(np.uint16), y.cpu().numpy(),
@@ -523,15 +580,15 @@ def run_stack(args):
         def check():
             nonlocal worst, same
             for l, (xl, yl, il) in enumerate(rec):
-                ref, ridx, _ = oracle.forward(hosts[l], xl)
+                ref, ridx, _ = oracle.forward(hosts[l], xl, token_ids=ids_np)
                 d = np.max(np.abs(yl - ref)) / np.max(np.abs(ref))
                 worst = max(worst, float(d))
                 same += int(np.count_nonzero(np.all(il == ridx, axis=1)))
 
         res["cpu_baseline"] = cpu_baseline(
-            check, n_chk, lambda: oracle.forward(hosts[0], rec[0][0][:1]), 1.0 / L, "tok/s",
+            check, n_chk, lambda: oracle.forward(hosts[-1], rec[-1][0][:1]), 1.0 / L, "tok/s",
             f"oracle.forward on {n_chk} decode tokens through all {L} layers, teacher-forced on the GPU's x_l",
-            "one token through layer 0 (tok/s through the whole stack = this / layers)")
+            "one token through the last layer (tok/s through the whole stack = this / layers)")
         res["config"]["teacher_forced_check"] = {
             "tokens": n_chk, "layers": L, "routing_equal": f"{same}/{n_chk * L}",
             "max_rel_err_block_output": worst, "tolerance": 2e-3}
@@ -734,6 +791,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="decode only (skip the nested prefill)")
     ap.add_argument("--workload", choices=("decode", "prefill", "stack", "batch", "q4"), default="decode")
     ap.add_argument("--layers", type=int, default=43, help="stack workload: number of layers")
+    ap.add_argument("--hash-layers", type=int, default=3,
+                    help="stack workload: the first layers that are hash-routed (the model has 3)")
     ap.add_argument("--tokens", type=int, default=2048, help="prefill tokens per call")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=3)
@@ -766,6 +825,7 @@ def main():
         from bit_quantized_moe_renorm_amd import synth
         layer = synth.make_layer(synth.DS4, seed=1)
         res = run_decode(args, layer)
+        res["hash_layer_decode"] = run_decode_hash(args, layer)
         if not args.no_prefill:
             pre = run_prefill(args, layer, cpu=not args.no_cpu_baseline)
             res["prefill"] = {k: pre[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "dtype",

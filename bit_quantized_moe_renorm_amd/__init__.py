@@ -20,7 +20,7 @@ OK, EINVAL, ENOMEM, EHIP, EUNSUPPORTED, EPOISONED = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 FMT_Q2, FMT_Q4 = 0, 1
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 TIMING_KINDS = ("route", "gateup_routed", "gateup_shared", "down_routed", "down_shared", "gemm_gateup_routed",
                 "gemm_down_routed", "fused", "gemm_prep", "gemm_gateup_shared", "gemm_down_shared",
                 "q4_gateup_routed", "q4_down_routed")
@@ -28,6 +28,7 @@ TIMING_KINDS = ("route", "gateup_routed", "gateup_shared", "down_routed", "down_
 SYMBOLS = ("ds4moe_create", "ds4moe_route", "ds4moe_forward", "ds4moe_set_path", "ds4moe_dequantize",
            "ds4moe_rmsnorm", "ds4moe_forward_stack", "ds4moe_timing_enable", "ds4moe_timing_read",
            "ds4moe_last_routing", "ds4moe_status", "ds4moe_set_wait_limit", "ds4moe_forward_static",
+           "ds4moe_route_ids", "ds4moe_forward_ids", "ds4moe_forward_stack_ids",
            "ds4moe_destroy", "ds4moe_last_error")
 
 
@@ -44,7 +45,7 @@ class Desc(ctypes.Structure):
                 ("router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("up", ctypes.c_void_p), ("down", ctypes.c_void_p), ("codebook", ctypes.c_void_p),
                 ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p),
-                ("expert_format", ctypes.c_int32)]
+                ("expert_format", ctypes.c_int32), ("hash_table", ctypes.c_void_p), ("n_vocab", ctypes.c_int64)]
 
 
 _lib = None
@@ -76,6 +77,9 @@ def load_library(path: Optional[Path] = None) -> ctypes.CDLL:
     L.ds4moe_status.argtypes = [P]
     L.ds4moe_set_wait_limit.argtypes = [P, i32, i32]
     L.ds4moe_forward_static.argtypes = [P, P, i32, P, P]
+    L.ds4moe_route_ids.argtypes = [P, P, P, i32, P, P, P, P, P]
+    L.ds4moe_forward_ids.argtypes = [P, P, P, i32, P, P]
+    L.ds4moe_forward_stack_ids.argtypes = [P, i32, P, P, i32, ctypes.c_double, P, P]
     L.ds4moe_destroy.argtypes = [P]
     L.ds4moe_last_error.restype = ctypes.c_char_p
     for name in SYMBOLS:
@@ -125,7 +129,9 @@ class MoELayer:
     router fp32 [NE, E], router_bias fp32 [NE] or None, gate/up uint8
     [NE, F, E/256, 66], down uint8 [NE, E, F/256, 84], codebook (host, 256
     uint16 values), sh_gate/sh_up/sh_down bf16 or None; with ``fmt`` "q4"
-    (weights["fmt"]) gate, up and down are uint8 [..., 144] Q4_K-style blocks.
+    (weights["fmt"]) gate, up and down are uint8 [..., 144] Q4_K-style blocks;
+    ``hash_table`` (int32 [n_vocab, top_k] on the GPU, or None) makes it a
+    hash-routed layer, whose calls take the tokens' ids.
     """
 
     def __init__(self, spec, weights: dict, max_tokens: int, act_dtype: int = BF16, stream=None):
@@ -134,11 +140,13 @@ class MoELayer:
         cb = np.ascontiguousarray(weights["codebook"], dtype=np.uint16)
         self._cb = cb
         fmt = FMT_Q4 if weights.get("fmt", "q2") == "q4" else FMT_Q2
+        tab = weights.get("hash_table")
         d = Desc(ABI_VERSION, spec.n_embd, spec.n_ff, spec.n_expert, spec.top_k,
                  1 if weights.get("sh_gate") is not None else 0, max_tokens, act_dtype,
                  _ptr(weights["router"]), _ptr(weights.get("router_bias")), _ptr(weights["gate"]),
                  _ptr(weights["up"]), _ptr(weights["down"]), cb.ctypes.data,
-                 _ptr(weights.get("sh_gate")), _ptr(weights.get("sh_up")), _ptr(weights.get("sh_down")), fmt)
+                 _ptr(weights.get("sh_gate")), _ptr(weights.get("sh_up")), _ptr(weights.get("sh_down")), fmt,
+                 _ptr(tab), 0 if tab is None else tab.shape[0])
         h = ctypes.c_void_p()
         _check(L.ds4moe_create(ctypes.byref(d), _stream(stream), ctypes.byref(h)))
         self.h = h
@@ -146,6 +154,7 @@ class MoELayer:
         self.max_tokens = max_tokens
         self.act_dtype = act_dtype
         self.fmt = fmt
+        self.hashed = tab is not None
 
     def close(self):
         if getattr(self, "h", None):
@@ -172,12 +181,24 @@ class MoELayer:
         _check_tensor("x", x, self._x_dtype(), (x.shape[0], self.spec.n_embd))
         return x.shape[0]
 
-    def forward(self, x, out, stream=None):
-        """out += MoE(x) (x [n, E] of the handle's activation dtype, out [n, E] fp32, both on the GPU)."""
+    def _check_ids(self, ids, n, dev):
+        import torch
+        if ids is not None:
+            _check_tensor("token_ids", ids, torch.int32, (n,), dev)
+        return ids
+
+    def forward(self, x, out, stream=None, ids=None):
+        """out += MoE(x) (x [n, E] of the handle's activation dtype, out [n, E] fp32, both on the GPU);
+        ``ids`` (int32 [n] on the GPU) are the tokens' ids, which a hash-routed layer needs."""
         import torch
         n = self._check_x(x)
         _check_tensor("out", out, torch.float32, (n, self.spec.n_embd), x.device)
-        _check(load_library().ds4moe_forward(self.h, _ptr(x), n, _ptr(out), _stream(stream)))
+        L = load_library()
+        if ids is None:
+            _check(L.ds4moe_forward(self.h, _ptr(x), n, _ptr(out), _stream(stream)))
+        else:
+            self._check_ids(ids, n, x.device)
+            _check(L.ds4moe_forward_ids(self.h, _ptr(x), _ptr(ids), n, _ptr(out), _stream(stream)))
 
     def forward_static(self, x, out, stream=None):
         """out += MoE(x) for 1..4 tokens with the library's static scratch (allocates nothing)."""
@@ -195,12 +216,18 @@ class MoELayer:
         tok = torch.empty((max(n * k, 1),), dtype=torch.int32, device=dev)
         return idx, w, off, tok
 
-    def route(self, x, stream=None):
-        """Returns (idx int32 [n,k], w fp32 [n,k], offsets int32 [NE+1], tokens int32 [n*k])."""
+    def route(self, x, stream=None, ids=None):
+        """Returns (idx int32 [n,k], w fp32 [n,k], offsets int32 [NE+1], tokens int32 [n*k]);
+        ``ids`` as for ``forward``."""
         n = self._check_x(x)
         idx, w, off, tok = self._routing_buffers(n, x.device)
-        _check(load_library().ds4moe_route(self.h, _ptr(x), n, _ptr(idx), _ptr(w), _ptr(off), _ptr(tok),
-                                           _stream(stream)))
+        L = load_library()
+        if ids is None:
+            _check(L.ds4moe_route(self.h, _ptr(x), n, _ptr(idx), _ptr(w), _ptr(off), _ptr(tok), _stream(stream)))
+        else:
+            self._check_ids(ids, n, x.device)
+            _check(L.ds4moe_route_ids(self.h, _ptr(x), _ptr(ids), n, _ptr(idx), _ptr(w), _ptr(off), _ptr(tok),
+                                      _stream(stream)))
         return idx, w, off, tok[: n * self.spec.top_k]
 
     def last_routing(self, n, stream=None):
@@ -252,10 +279,11 @@ def rmsnorm(h, eps: float = 1e-6, out=None, stream=None):
     return out
 
 
-def forward_stack(layers, h, eps: float = 1e-6, x=None, stream=None):
+def forward_stack(layers, h, eps: float = 1e-6, x=None, stream=None, ids=None):
     """For each layer in order: x = RMSNorm(h), h += MoE(x), all enqueued by
     one library call (h fp32 [n, E] on the GPU, updated in place; x optional
-    bf16 [n, E] scratch).  Returns h."""
+    bf16 [n, E] scratch; ``ids`` int32 [n] on the GPU, the tokens' ids, needed
+    when a layer is hash-routed).  Returns h."""
     import torch
     n, E = h.shape
     _check_tensor("h", h, torch.float32, (n, E))
@@ -264,7 +292,12 @@ def forward_stack(layers, h, eps: float = 1e-6, x=None, stream=None):
     _check_tensor("x", x, torch.bfloat16, (n, E), h.device)
     # a closed layer passes NULL, which the library rejects (DS4MOE_EINVAL)
     hs = (ctypes.c_void_p * len(layers))(*[lay.h.value if lay.h else None for lay in layers])
-    _check(load_library().ds4moe_forward_stack(hs, len(layers), _ptr(h), n, eps, _ptr(x), _stream(stream)))
+    if ids is None:
+        _check(load_library().ds4moe_forward_stack(hs, len(layers), _ptr(h), n, eps, _ptr(x), _stream(stream)))
+    else:
+        _check_tensor("token_ids", ids, torch.int32, (n,), h.device)
+        _check(load_library().ds4moe_forward_stack_ids(hs, len(layers), _ptr(h), _ptr(ids), n, eps, _ptr(x),
+                                                       _stream(stream)))
     return h
 
 
@@ -285,7 +318,15 @@ def upload_layer(layer, device="cuda"):
                 down=t(layer.down), codebook=layer.codebook, fmt=getattr(layer, "fmt", "q2"),
                 sh_gate=t(None if layer.sh_gate is None else layer.sh_gate.view(np.int16), torch.bfloat16),
                 sh_up=t(None if layer.sh_up is None else layer.sh_up.view(np.int16), torch.bfloat16),
-                sh_down=t(None if layer.sh_down is None else layer.sh_down.view(np.int16), torch.bfloat16))
+                sh_down=t(None if layer.sh_down is None else layer.sh_down.view(np.int16), torch.bfloat16),
+                hash_table=t(getattr(layer, "hash_table", None)))
+
+
+def to_device_ids(ids_np, device="cuda"):
+    """Token ids (int32 numpy) as a device tensor."""
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).to(device)
 
 
 def to_device_x(x_np, device="cuda"):

@@ -42,6 +42,10 @@ struct Layer {
     int fmt;                        // 0: IQ2 gate/up + Q2_K down; 1: Q4_K gate, up and down
     const uint8_t *q4_qs[3];        // Q4_K gate, up, down: [NE][rows][blocks][128] quants
     const uint4 *q4_meta[3];        //   and [NE][rows][blocks] 16-byte d | dmin | 6-bit fields
+    // hash-routed layer: the experts of a token are row `id` of this table
+    // ([n_vocab][top_k], library-owned), nullptr for a learned-routing layer
+    const int32_t *hash_table;
+    int n_vocab;
 };
 
 // Workspace (device), carved from one allocation at create time.
@@ -79,6 +83,8 @@ struct Work {
     uint32_t *status;
     int spin_limit;       // polls before a wait gives up
     uint32_t want_xor;
+    // per call: the tokens' ids ([n_tok], device) for a hash-routed layer
+    const int32_t *ids;
 };
 
 constexpr int DEFAULT_SPIN_LIMIT = 1 << 20;  // about a second of polling
@@ -86,6 +92,12 @@ constexpr int DEFAULT_SPIN_LIMIT = 1 << 20;  // about a second of polling
 // A bounded wait expired during the call tagged `tag`: record it for the host.
 __device__ __forceinline__ void report_wait_expired(const Work &W, uint32_t tag) {
     __hip_atomic_store(W.status, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// A hash-routed call met a token id outside [0, n_vocab): record its tag in
+// the status word's second slot.
+__device__ __forceinline__ void report_bad_id(const Work &W, uint32_t tag) {
+    __hip_atomic_store(W.status + 1, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // ---------------------------------------------------------------- small device helpers

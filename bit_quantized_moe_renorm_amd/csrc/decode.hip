@@ -4,7 +4,8 @@
 // fuse MoE routing with the expert computation into one GPU dispatch (same
 // page, section 2.3).  Here one persistent launch walks a fixed list of work
 // items in five phases, in this order:
-//   router    : half an expert's logit per item (fp64 accumulation);
+//   router    : half an expert's logit per item (fp64 accumulation); a hash
+//               layer scores only the k experts of the token's table row;
 //   routing   : every workgroup polls until all router halves of this call
 //               are stored and takes the top-k and renormalised weights itself
 //               (the shared expert's first gate/up rows stream meanwhile);
@@ -98,7 +99,7 @@ constexpr int DEC_DN_NR = 4;  // routed down row slots per wave
 
 struct DecPlan {
     unsigned long long ep;  // calls already made on this workspace
-    int n_route, n_shgu, n_rgu, n_shdn, n_rdn;
+    int n_route, n_shgu, n_rgu, n_shdn, n_rdn;   // n_route: 2 items per expert scored
     int rgu_per_slot, rdn_per_slot;
     int shdn_cpr;
     int total;
@@ -141,6 +142,50 @@ struct RouteCache {
     float w[MAX_TOPK];
 };
 
+// The weights and the export of a routing whose lane j < k holds slot j's
+// expert and fp32 logit: one exp per lane (relative to the largest of the k
+// logits, slot 0's for a top-k selection), the denominator by a sum over the
+// k lanes.
+__device__ __forceinline__ void dec_route_finish(const Layer &L, const Work &W, int myE, float myL, RouteCache *rc,
+                                                 bool write_global) {
+    const int lane = threadIdx.x & 63;
+    const int NE = L.n_expert, k = L.top_k;
+    float M = (lane < k) ? myL : -INFINITY;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const double ex = (lane < k) ? exp((double)myL - (double)M) : 0.0;
+    const double z = wave_sum(ex);
+    const float wj = (float)(ex / z);
+    if (lane < k) {
+        rc->idx[lane] = myE;
+        rc->w[lane] = wj;
+    }
+    if (!write_global) return;
+    if (lane < k) {
+        W.idx[lane] = myE;
+        W.w[lane] = wj;
+    }
+    int selE[MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK; ++j) selE[j] = (j < k) ? __shfl(myE, j, 64) : 0;
+    for (int ee = lane; ee <= NE; ee += 64) {
+        int before = 0;
+#pragma unroll
+        for (int j = 0; j < MAX_TOPK; ++j)
+            if (j < k) before += selE[j] < ee;
+        W.offsets[ee] = before;
+    }
+    if (lane == 0) W.active[0] = k;
+    if (lane < k) {
+        int rank = 0;
+#pragma unroll
+        for (int i = 0; i < MAX_TOPK; ++i)
+            if (i < k) rank += selE[i] < myE;
+        W.active[1 + rank] = myE;
+        W.list[rank] = lane;
+    }
+}
+
 __device__ __forceinline__ void dec_topk_local(const Layer &L, const Work &W, const double *lg, RouteCache *rc,
                                                bool write_global) {
     const int lane = threadIdx.x & 63;
@@ -178,48 +223,15 @@ __device__ __forceinline__ void dec_topk_local(const Layer &L, const Work &W, co
         for (int i = 0; i < 4; ++i)
             if (lane + 64 * i == ee) key[i] = 0u;
     }
-    // one exp per lane, the denominator by a sum over the k lanes
-    const float L0 = __shfl(myL, 0, 64);
-    const double ex = (lane < k) ? exp((double)myL - (double)L0) : 0.0;
-    const double z = wave_sum(ex);
-    const float wj = (float)(ex / z);
-    if (lane < k) {
-        rc->idx[lane] = myE;
-        rc->w[lane] = wj;
-    }
-    if (!write_global) return;
-    if (lane < k) {
-        W.idx[lane] = myE;
-        W.w[lane] = wj;
-    }
-    int selE[MAX_TOPK];
-#pragma unroll
-    for (int j = 0; j < MAX_TOPK; ++j) selE[j] = (j < k) ? __shfl(myE, j, 64) : 0;
-    for (int ee = lane; ee <= NE; ee += 64) {
-        int before = 0;
-#pragma unroll
-        for (int j = 0; j < MAX_TOPK; ++j)
-            if (j < k) before += selE[j] < ee;
-        W.offsets[ee] = before;
-    }
-    if (lane == 0) W.active[0] = k;
-    if (lane < k) {
-        int rank = 0;
-#pragma unroll
-        for (int i = 0; i < MAX_TOPK; ++i)
-            if (i < k) rank += selE[i] < myE;
-        W.active[1 + rank] = myE;
-        W.list[rank] = lane;
-    }
+    dec_route_finish(L, W, myE, myL, rc, write_global);
 }
 
 // Half h of expert e's logit: waves split the half row (E/2 elements).
 template <bool XBF16>
-__device__ __forceinline__ void dec_route_item(const Layer &L, const Work &W, const void *__restrict__ x, int item,
-                               double *lds_part, uint32_t tag) {
+__device__ __forceinline__ void dec_route_item(const Layer &L, const Work &W, const void *__restrict__ x, int e,
+                                               int h, double *lds_part, uint32_t tag) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = L.n_embd;
-    const int e = item >> 1, h = item & 1;
     const int half = E >> 1, per_wave = half >> 2;   // E/8 elements per wave
     const int base = h * half + wave * per_wave;
     double acc = 0.0;
@@ -480,6 +492,50 @@ __device__ __forceinline__ void dec_route_poll(const Layer &L, const Work &W, ui
                 lg[i] = h0 + h1 + (double)bias[i];
             }
             dec_topk_local(L, W, lg, rc, blockIdx.x == 0);
+        }
+        if (lane == 0) *lds_flag = ok;
+    }
+}
+
+// The routing of a hash layer's token: lane j < k polls the four tagged
+// words of slot j's expert (row `trow` of the table), then the weights are
+// taken over those k logits.  A bad id (decided by every workgroup alike from
+// the same word) skips the wait and fails the call.
+__device__ __forceinline__ void dec_route_poll_hashed(const Layer &L, const Work &W, uint32_t tag,
+                                                      const int32_t *trow, bool bad_id, RouteCache *rc,
+                                                      int *lds_flag) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x, k = L.top_k;
+        int ok = 1;
+        if (bad_id) {
+            if (lane == 0) report_bad_id(W, tag);
+            ok = 0;
+        } else {
+            const int e = trow[min(lane, k - 1)];
+            const float b = L.router_bias ? L.router_bias[e] : 0.0f;
+            unsigned long long v[4] = {0, 0, 0, 0};
+            uint32_t missing = lane < k ? 0xFu : 0u;
+            const uint32_t want = tag ^ W.want_xor;
+            int spins = 0;
+            while (true) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = poll_load(W.rtag + 4 * e + q);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if ((uint32_t)(v[q] >> 32) == want) missing &= ~(1u << q);
+                if (!__any(missing != 0)) break;
+                __builtin_amdgcn_s_sleep(4);
+                if (++spins > W.spin_limit) {
+                    if (lane == 0) report_wait_expired(W, tag);
+                    ok = 0;
+                    break;
+                }
+            }
+            if (ok) {
+                const double h0 = __longlong_as_double((long long)((v[0] & 0xFFFFFFFFull) | (v[1] << 32)));
+                const double h1 = __longlong_as_double((long long)((v[2] & 0xFFFFFFFFull) | (v[3] << 32)));
+                dec_route_finish(L, W, e, (float)(h0 + h1 + (double)b), rc, blockIdx.x == 0);
+            }
         }
         if (lane == 0) *lds_flag = ok;
     }
@@ -915,7 +971,12 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
     xc.load(x, 64 * ((threadIdx.x & 63) & ((L.n_embd >> 6) - 1)));
     int it = blockIdx.x;
     const uint32_t tag = (uint32_t)(P.ep % 0xFFFFFFFFull) + 1u;  // never 0, the workspace's initial value
-    for (; it < b0; it += G) dec_route_item<XBF16>(L, W, x, it, lds_part, tag);
+    // a hash layer scores only the k experts of the token's table row
+    const bool hashed = L.hash_table != nullptr;
+    const int id = hashed ? W.ids[0] : 0;
+    const bool bad_id = hashed && (id < 0 || id >= L.n_vocab);
+    const int32_t *trow = hashed ? L.hash_table + (int64_t)(bad_id ? 0 : id) * L.top_k : nullptr;
+    for (; it < b0; it += G) dec_route_item<XBF16>(L, W, x, hashed ? trow[it >> 1] : it >> 1, it & 1, lds_part, tag);
     // the IQ2 byte tables (entry e, replica r at e * IQ2B_REPL + r)
     {
         static_assert(DEC_THREADS == 256, "one codebook entry per thread");
@@ -939,7 +1000,10 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
     ShguW<XBF16> sg;
     const bool wave0 = threadIdx.x < 64;
     if (!wave0 && it < b1) dec_shgu_load<XBF16>(L, x, it - b0, sg);
-    dec_route_poll(L, W, tag, &rc, &lds_flag);
+    if (hashed)
+        dec_route_poll_hashed(L, W, tag, trow, bad_id, &rc, &lds_flag);
+    else
+        dec_route_poll(L, W, tag, &rc, &lds_flag);
     if (wave0 && it < b1) dec_shgu_load<XBF16>(L, x, it - b0, sg);
     __syncthreads();
     bool ok = lds_flag != 0;
@@ -1022,8 +1086,8 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
             if (!more) break;
         }
     }
-    // a bounded wait of this workgroup expired (and was reported for the host):
-    // the call's output is poisoned too.  An exchange at the device's point of
+    // a bounded wait of this workgroup expired, or the token's id is out of
+    // range (either was reported for the host): the call's output is poisoned too.  An exchange at the device's point of
     // coherence, where the other contributions are added: whatever lands
     // before or after it, out[0] ends as NaN.
     if (!ok && threadIdx.x == 0) atomicExch(out, __builtin_nanf(""));
@@ -1032,7 +1096,8 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
 static DecPlan make_plan(const Layer &L) {
     DecPlan P{};
     const int E = L.n_embd, F = L.n_ff, k = L.top_k;
-    P.n_route = 2 * L.n_expert;  // half an expert row per item
+    // half an expert row per item: every expert, or the k of a hash layer's table row
+    P.n_route = 2 * (L.hash_table ? L.top_k : L.n_expert);
     P.n_shgu = L.n_shared ? (F + DEC_WAVES - 1) / DEC_WAVES : 0;
     const int rows_gu_item = DEC_WAVES * DEC_GU_NR * (64 / (E >> 6));
     P.rgu_per_slot = (F + rows_gu_item - 1) / rows_gu_item;

@@ -68,6 +68,7 @@ struct ds4moe {
     unsigned long long decode_calls = 0;  // fused launches so far (the phase counters' epoch)
     unsigned long long route_calls = 0;   // routing launches so far (the router hand-off tag)
     bool poisoned = false;
+    std::string poison_why;               // what poisoned it, repeated by every later call
     int device = 0;
     int32_t last_n_tok = -1;              // n_tok of the latest forward/route call (its routing is in W)
     bool last_static = false;             // ... made by ds4moe_forward_static (its routing is in Wst)
@@ -113,6 +114,7 @@ static bool gemm_available() { return ds4::gemm_enabled(); }
 static int check_launch(ds4moe *h, hipError_t e, const char *what) {
     if (e != hipSuccess) {
         h->poisoned = true;
+        h->poison_why = std::string(what) + ": " + hipGetErrorString(e);
         return fail(DS4MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
     }
     return DS4MOE_OK;
@@ -196,6 +198,11 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
         return fail(DS4MOE_EINVAL, "create: NULL router/gate/up/down/codebook");
     if (d->n_shared && (!d->sh_gate || !d->sh_up || !d->sh_down))
         return fail(DS4MOE_EINVAL, "create: n_shared = 1 but a shared-expert pointer is NULL");
+    if (d->hash_table) {
+        if (d->n_vocab < 1 || d->n_vocab > (int64_t)(INT32_MAX / d->top_k))
+            return fail(DS4MOE_EINVAL, "create: n_vocab %lld for a hash table", (long long)d->n_vocab);
+        if ((uintptr_t)d->hash_table & 3u) return fail(DS4MOE_EINVAL, "create: hash_table is not 4-byte aligned");
+    }
 
     hipStream_t s = (hipStream_t)stream;
     ds4moe *h = new (std::nothrow) ds4moe();
@@ -218,6 +225,8 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     uint16_t *rhml = (uint16_t *)A(3 * NE * E * 2);
     float *rnorm = (float *)A(NE * 4);
     uint16_t *cb = (uint16_t *)A(512);
+    const int64_t n_hash = d->hash_table ? d->n_vocab * k : 0;
+    int32_t *htab = d->hash_table ? (int32_t *)A(n_hash * 4) : nullptr;
     // the routed planes of the layer's format (the other format's stay NULL)
     uint8_t *gq = nullptr, *uq = nullptr, *dq = nullptr, *dsc = nullptr;
     uint16_t *gd = nullptr, *ud = nullptr;
@@ -292,7 +301,8 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
         hipGetLastError();
         return fail(DS4MOE_ENOMEM, "create: pinned status word");
     }
-    *(volatile uint32_t *)h->status_host = 0u;
+    ((volatile uint32_t *)h->status_host)[0] = 0u;  // a bounded wait expired (that call's tag)
+    ((volatile uint32_t *)h->status_host)[1] = 0u;  // a token id out of range (that call's tag)
     if (hipHostGetDevicePointer((void **)&W.status, h->status_host, 0) != hipSuccess) {
         delete h;
         hipGetLastError();
@@ -332,6 +342,12 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
         }                                                                                             \
     } while (0)
     CK(hipMemsetAsync(ws, 0, off, s));
+    std::vector<int32_t> host_table;
+    if (htab) {
+        host_table.resize((size_t)n_hash);
+        CK(hipMemcpyAsync(htab, d->hash_table, n_hash * 4, hipMemcpyDeviceToDevice, s));
+        CK(hipMemcpyAsync(host_table.data(), d->hash_table, n_hash * 4, hipMemcpyDeviceToHost, s));
+    }
     CK(hipMemcpyAsync(router, d->router, NE * E * 4, hipMemcpyDeviceToDevice, s));
     if (bias) CK(hipMemcpyAsync(bias, d->router_bias, NE * 4, hipMemcpyDeviceToDevice, s));
     CK(launch_router_prep(router, (int)NE, (int)E, rhml, rnorm, s));
@@ -356,6 +372,21 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     }
     CK(hipStreamSynchronize(s));
 #undef CK
+    // every table row: k distinct experts in range (the kernels index with them unchecked)
+    for (int64_t v = 0; v < (int64_t)host_table.size() / k; ++v) {
+        const int32_t *r = host_table.data() + v * k;
+        for (int j = 0; j < k; ++j) {
+            bool dup = false;
+            for (int i = 0; i < j; ++i) dup |= r[i] == r[j];
+            if (r[j] < 0 || r[j] >= NE || dup) {
+                delete h;
+                return fail(DS4MOE_EINVAL, "create: hash_table row %lld slot %d: expert %d %s", (long long)v, j, r[j],
+                            dup ? "repeated" : "out of range");
+            }
+        }
+    }
+    L.hash_table = htab;
+    L.n_vocab = htab ? (int)d->n_vocab : 0;
     L.router = router, L.router_bias = bias, L.codebook = cb;
     L.router_hml = rhml, L.router_norm = rnorm;
     L.iq2_qs[0] = gq, L.iq2_qs[1] = uq, L.iq2_d[0] = gd, L.iq2_d[1] = ud;
@@ -388,16 +419,23 @@ int ds4moe_set_path(ds4moe_t *h, int32_t path) {
     return DS4MOE_OK;
 }
 
-// A bounded wait of an earlier call gave up (its kernel recorded the call's
-// tag in the handle's host-visible status word): the handle is poisoned.
+// A bounded wait of an earlier call gave up, or a hash-routed call met a token
+// id out of range (its kernel recorded the call's tag in the handle's
+// host-visible status words): the handle is poisoned.
 static int poll_status(ds4moe *h, const char *what) {
-    if (h->poisoned) return fail(DS4MOE_EPOISONED, "%s: handle poisoned by an earlier error", what);
-    const uint32_t st = *(volatile const uint32_t *)h->status_host;
-    if (st) {
-        h->poisoned = true;
-        return fail(DS4MOE_EPOISONED, "%s: a bounded wait of an earlier call (tag %u) expired; handle poisoned",
-                    what, st);
+    if (!h->poisoned) {
+        char buf[160];
+        const uint32_t st = ((volatile const uint32_t *)h->status_host)[0];
+        const uint32_t bad = ((volatile const uint32_t *)h->status_host)[1];
+        if (st) {
+            snprintf(buf, sizeof buf, "a bounded wait of an earlier call (tag %u) expired", st);
+            h->poisoned = true, h->poison_why = buf;
+        } else if (bad) {
+            snprintf(buf, sizeof buf, "an earlier call (tag %u) had a token id outside 0..n_vocab-1", bad);
+            h->poisoned = true, h->poison_why = buf;
+        }
     }
+    if (h->poisoned) return fail(DS4MOE_EPOISONED, "%s: handle poisoned (%s)", what, h->poison_why.c_str());
     return DS4MOE_OK;
 }
 
@@ -427,10 +465,19 @@ static int common_checks(ds4moe *h, const void *x, int32_t n_tok, const char *wh
     return DS4MOE_OK;
 }
 
-int ds4moe_route(ds4moe_t *h, const void *x, int32_t n_tok, int32_t *topk_idx, float *topk_w,
-                 int32_t *expert_offsets, int32_t *expert_tokens, void *stream) {
+// A hash-routed layer needs the tokens' ids (a learned one ignores them).
+static int id_checks(ds4moe *h, const int32_t *ids, int32_t n_tok, const char *what) {
+    if (!h->L.hash_table || n_tok == 0) return DS4MOE_OK;
+    if (!ids) return fail(DS4MOE_EINVAL, "%s: a hash-routed layer needs token ids (the *_ids entry points)", what);
+    if ((uintptr_t)ids & 3u) return fail(DS4MOE_EINVAL, "%s: token_ids is not 4-byte aligned", what);
+    return DS4MOE_OK;
+}
+
+static int route_impl(ds4moe_t *h, const void *x, const int32_t *ids, int32_t n_tok, int32_t *topk_idx,
+                      float *topk_w, int32_t *expert_offsets, int32_t *expert_tokens, void *stream) {
     int rc = common_checks(h, x, n_tok, "route");
     if (rc) return rc;
+    if ((rc = id_checks(h, ids, n_tok, "route"))) return rc;
     if (n_tok > 0 && (!topk_idx || !topk_w || !expert_offsets || !expert_tokens))
         return fail(DS4MOE_EINVAL, "route: NULL output");
     if (n_tok == 0) return DS4MOE_OK;
@@ -438,17 +485,30 @@ int ds4moe_route(ds4moe_t *h, const void *x, int32_t n_tok, int32_t *topk_idx, f
     if ((rc = stream_checks(s, "route"))) return rc;
     h->last_n_tok = n_tok;
     h->last_static = false;
+    Work W = h->W;
+    W.ids = ids;
     int tb = h->tbegin(TK_ROUTE, s);
-    rc = check_launch(h, launch_route(h->L, h->W, x, n_tok, s, h->route_calls++), "route");
+    rc = check_launch(h, launch_route(h->L, W, x, n_tok, s, h->route_calls++), "route");
     h->tend(tb, s);
     if (rc) return rc;
-    return check_launch(h, launch_route_export(h->L, h->W, n_tok, topk_idx, topk_w, expert_offsets, expert_tokens, s),
+    return check_launch(h, launch_route_export(h->L, W, n_tok, topk_idx, topk_w, expert_offsets, expert_tokens, s),
                         "route export");
 }
 
-int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *stream) {
+int ds4moe_route(ds4moe_t *h, const void *x, int32_t n_tok, int32_t *topk_idx, float *topk_w,
+                 int32_t *expert_offsets, int32_t *expert_tokens, void *stream) {
+    return route_impl(h, x, nullptr, n_tok, topk_idx, topk_w, expert_offsets, expert_tokens, stream);
+}
+
+int ds4moe_route_ids(ds4moe_t *h, const void *x, const int32_t *token_ids, int32_t n_tok, int32_t *topk_idx,
+                     float *topk_w, int32_t *expert_offsets, int32_t *expert_tokens, void *stream) {
+    return route_impl(h, x, token_ids, n_tok, topk_idx, topk_w, expert_offsets, expert_tokens, stream);
+}
+
+static int forward_impl(ds4moe_t *h, const void *x, const int32_t *ids, int32_t n_tok, float *out, void *stream) {
     int rc = common_checks(h, x, n_tok, "forward");
     if (rc) return rc;
+    if ((rc = id_checks(h, ids, n_tok, "forward"))) return rc;
     if (n_tok > 0 && !out) return fail(DS4MOE_EINVAL, "forward: NULL out");
     if (n_tok > 0 && !aligned16(out)) return fail(DS4MOE_EINVAL, "forward: out is not 16-byte aligned");
     if (n_tok == 0) return DS4MOE_OK;
@@ -465,7 +525,9 @@ int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *
             const int nc = std::min(GEMV_MAX_TOK, n_tok - c0);
             const void *xc = (const char *)x + (size_t)c0 * h->L.n_embd * xb;
             float *oc = out + (size_t)c0 * h->L.n_embd;
-            if ((rc = run_q4_chunk(h, h->W, xc, nc, oc, h->route_calls++, s, true))) return rc;
+            Work Wc = h->W;
+            Wc.ids = ids ? ids + c0 : nullptr;
+            if ((rc = run_q4_chunk(h, Wc, xc, nc, oc, h->route_calls++, s, true))) return rc;
         }
         return DS4MOE_OK;
     }
@@ -484,71 +546,84 @@ int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *
     hipStream_t s = (hipStream_t)stream;
     h->last_n_tok = n_tok;
     h->last_static = false;
+    Work W = h->W;
+    W.ids = ids;
     if (path == DS4MOE_PATH_GEMV && n_tok == 1) {
         // the whole block for one token in one persistent launch
         int tf = h->tbegin(TK_FUSED, s);
-        rc = check_launch(h, launch_decode_fused(h->L, h->W, x, out, h->decode_grid, h->decode_calls, s),
+        rc = check_launch(h, launch_decode_fused(h->L, W, x, out, h->decode_grid, h->decode_calls, s),
                           "fused decode");
         h->decode_calls += 1;
         h->tend(tf, s);
         return rc;
     }
     int tb = h->tbegin(TK_ROUTE, s);
-    rc = check_launch(h, launch_route(h->L, h->W, x, n_tok, s, h->route_calls++), "route");
+    rc = check_launch(h, launch_route(h->L, W, x, n_tok, s, h->route_calls++), "route");
     h->tend(tb, s);
     if (rc) return rc;
     if (path == DS4MOE_PATH_GEMV) {
         if (h->L.n_shared) {
             tb = h->tbegin(TK_GU_SHARED, s);
-            rc = check_launch(h, launch_gemv_gateup_shared(h->L, h->W, x, n_tok, s), "gemv shared gate/up");
+            rc = check_launch(h, launch_gemv_gateup_shared(h->L, W, x, n_tok, s), "gemv shared gate/up");
             h->tend(tb, s);
             if (rc) return rc;
         }
         tb = h->tbegin(TK_GU_ROUTED, s);
-        rc = check_launch(h, launch_gemv_gateup_routed(h->L, h->W, x, n_tok, s), "gemv routed gate/up");
+        rc = check_launch(h, launch_gemv_gateup_routed(h->L, W, x, n_tok, s), "gemv routed gate/up");
         h->tend(tb, s);
         if (rc) return rc;
         tb = h->tbegin(TK_DN_ROUTED, s);
-        rc = check_launch(h, launch_gemv_down_routed(h->L, h->W, n_tok, out, s), "gemv routed down");
+        rc = check_launch(h, launch_gemv_down_routed(h->L, W, n_tok, out, s), "gemv routed down");
         h->tend(tb, s);
         if (rc) return rc;
         if (h->L.n_shared) {
             tb = h->tbegin(TK_DN_SHARED, s);
-            rc = check_launch(h, launch_gemv_down_shared(h->L, h->W, n_tok, out, s), "gemv shared down");
+            rc = check_launch(h, launch_gemv_down_shared(h->L, W, n_tok, out, s), "gemv shared down");
             h->tend(tb, s);
         }
         return rc;
     }
     // batched path: activation copies and chunk table, then the four grouped GEMMs
     tb = h->tbegin(TK_GEMM_PREP, s);
-    rc = check_launch(h, launch_gemm_prep(h->L, h->W, x, n_tok, s), "gemm prep");
+    rc = check_launch(h, launch_gemm_prep(h->L, W, x, n_tok, s), "gemm prep");
     h->tend(tb, s);
     if (rc) return rc;
     tb = h->tbegin(TK_GEMM_GU_ROUTED, s);
-    rc = check_launch(h, launch_gemm_gateup_routed(h->L, h->W, n_tok, s), "gemm routed gate/up");
+    rc = check_launch(h, launch_gemm_gateup_routed(h->L, W, n_tok, s), "gemm routed gate/up");
     h->tend(tb, s);
     if (rc) return rc;
     if (h->L.n_shared) {
         tb = h->tbegin(TK_GEMM_GU_SHARED, s);
-        rc = check_launch(h, launch_gemm_gateup_shared(h->L, h->W, x, n_tok, s), "gemm shared gate/up");
+        rc = check_launch(h, launch_gemm_gateup_shared(h->L, W, x, n_tok, s), "gemm shared gate/up");
         h->tend(tb, s);
         if (rc) return rc;
     }
     tb = h->tbegin(TK_GEMM_DN_ROUTED, s);
-    rc = check_launch(h, launch_gemm_down_routed(h->L, h->W, n_tok, out, s), "gemm routed down");
+    rc = check_launch(h, launch_gemm_down_routed(h->L, W, n_tok, out, s), "gemm routed down");
     h->tend(tb, s);
     if (rc) return rc;
     if (h->L.n_shared) {
         tb = h->tbegin(TK_GEMM_DN_SHARED, s);
-        rc = check_launch(h, launch_gemm_down_shared(h->L, h->W, n_tok, out, s), "gemm shared down");
+        rc = check_launch(h, launch_gemm_down_shared(h->L, W, n_tok, out, s), "gemm shared down");
         h->tend(tb, s);
     }
     return rc;
 }
 
+int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *stream) {
+    return forward_impl(h, x, nullptr, n_tok, out, stream);
+}
+
+int ds4moe_forward_ids(ds4moe_t *h, const void *x, const int32_t *token_ids, int32_t n_tok, float *out,
+                       void *stream) {
+    return forward_impl(h, x, token_ids, n_tok, out, stream);
+}
+
 int ds4moe_forward_static(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *stream) {
     int rc = common_checks(h, x, n_tok, "forward_static");
     if (rc) return rc;
+    if (h->L.hash_table)
+        return fail(DS4MOE_EUNSUPPORTED, "forward_static: a hash-routed layer takes token ids (ds4moe_forward_ids)");
     if (n_tok > STATIC_MAX_TOK)
         return fail(DS4MOE_EINVAL, "forward_static: n_tok %d beyond the static scratch's %d tokens", n_tok,
                     STATIC_MAX_TOK);
@@ -620,8 +695,8 @@ int ds4moe_rmsnorm(const float *hin, int32_t n_tok, int32_t n_embd, double eps, 
     return DS4MOE_OK;
 }
 
-int ds4moe_forward_stack(ds4moe_t *const *layers, int32_t n_layers, float *h, int32_t n_tok, double eps,
-                         uint16_t *x_bf16, void *stream) {
+static int forward_stack_impl(ds4moe_t *const *layers, int32_t n_layers, float *h, const int32_t *ids,
+                              int32_t n_tok, double eps, uint16_t *x_bf16, void *stream) {
     if (!layers || n_layers < 1) return fail(DS4MOE_EINVAL, "forward_stack: no layers");
     if (n_tok < 0 || !(eps >= 0.0)) return fail(DS4MOE_EINVAL, "forward_stack: n_tok %d, eps %g", n_tok, eps);
     if (n_tok > 0 && (!h || !x_bf16)) return fail(DS4MOE_EINVAL, "forward_stack: NULL h or x");
@@ -637,6 +712,7 @@ int ds4moe_forward_stack(ds4moe_t *const *layers, int32_t n_layers, float *h, in
         if (d->L.n_embd != layers[0]->L.n_embd)
             return fail(DS4MOE_EINVAL, "forward_stack: layer %d has n_embd %d, layer 0 %d", l, d->L.n_embd,
                         layers[0]->L.n_embd);
+        if ((rc = id_checks(d, ids, n_tok, "forward_stack"))) return fail(rc, "forward_stack: layer %d: %s", l, g_err.c_str());
     }
     if (n_tok == 0) return DS4MOE_OK;
     {
@@ -647,10 +723,20 @@ int ds4moe_forward_stack(ds4moe_t *const *layers, int32_t n_layers, float *h, in
     for (int l = 0; l < n_layers; ++l) {
         hipError_t e = launch_rmsnorm(h, n_tok, E, eps, x_bf16, (hipStream_t)stream);
         if (e != hipSuccess) return fail(DS4MOE_EHIP, "forward_stack: layer %d rmsnorm: %s", l, hipGetErrorString(e));
-        int rc = ds4moe_forward(layers[l], x_bf16, n_tok, h, stream);
+        int rc = forward_impl(layers[l], x_bf16, ids, n_tok, h, stream);
         if (rc) return fail(rc, "forward_stack: layer %d: %s", l, g_err.c_str());
     }
     return DS4MOE_OK;
+}
+
+int ds4moe_forward_stack(ds4moe_t *const *layers, int32_t n_layers, float *h, int32_t n_tok, double eps,
+                         uint16_t *x_bf16, void *stream) {
+    return forward_stack_impl(layers, n_layers, h, nullptr, n_tok, eps, x_bf16, stream);
+}
+
+int ds4moe_forward_stack_ids(ds4moe_t *const *layers, int32_t n_layers, float *h, const int32_t *token_ids,
+                             int32_t n_tok, double eps, uint16_t *x_bf16, void *stream) {
+    return forward_stack_impl(layers, n_layers, h, token_ids, n_tok, eps, x_bf16, stream);
 }
 
 int ds4moe_last_routing(ds4moe_t *h, int32_t n_tok, int32_t *topk_idx, float *topk_w, int32_t *expert_offsets,

@@ -760,10 +760,77 @@ __global__ __launch_bounds__(256) void k_fill_lists(int n_tok, int NE, int k, Wo
     }
 }
 
+// ---------------------------------------------------------------- hash-routed layers
+// A hash layer takes a token's experts from row `id` of its table, in slot
+// order, and weights them by the softmax over all logits renormalised over
+// those experts.  The renormalisation cancels every other expert:
+// p_j / sum_i p_i = exp(L_j - M) / sum_i exp(L_i - M) over the k table experts
+// alone (M: their largest logit), so only k router rows are read per token.
+// One workgroup per token; wave w computes the logits of slots w, w + 4
+// (fp64 accumulation, rounded to fp32 as in the learned router).  An id
+// outside [0, n_vocab) poisons the token's weights with NaN (its experts are
+// then row 0's, so every later access stays in bounds) and records the call
+// in the host-visible status word.
+template <bool XBF16>
+__global__ __launch_bounds__(256) void k_route_hashed(const float *__restrict__ R, const float *__restrict__ bias,
+                                                      const void *__restrict__ x, const int32_t *__restrict__ table,
+                                                      int n_vocab, int E, int k, Work W, uint32_t tag) {
+    __shared__ float Ls[MAX_TOPK];
+    __shared__ int Es[MAX_TOPK];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x;
+    const int id = W.ids[t];
+    const bool bad = id < 0 || id >= n_vocab;
+    const int32_t *row = table + (int64_t)(bad ? 0 : id) * k;
+    for (int j = wave; j < k; j += RT_WAVES) {
+        const int e = row[j];
+        double acc = 0.0;
+        for (int i = 4 * lane; i < E; i += 256) {
+            const float4 r = *reinterpret_cast<const float4 *>(R + (int64_t)e * E + i);
+            double xv[4];
+            load_x4<XBF16>(x, (int64_t)t * E + i, xv);
+            acc = fma(xv[0], (double)r.x, acc);
+            acc = fma(xv[1], (double)r.y, acc);
+            acc = fma(xv[2], (double)r.z, acc);
+            acc = fma(xv[3], (double)r.w, acc);
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) {
+            Ls[j] = (float)(acc + (bias ? (double)bias[e] : 0.0));
+            Es[j] = e;
+        }
+    }
+    __syncthreads();
+    if (wave == 0 && lane < k) {
+        float m = Ls[0];
+        for (int j = 1; j < k; ++j) m = fmaxf(m, Ls[j]);
+        double z = 0.0, num = 0.0;
+        for (int j = 0; j < k; ++j) {
+            const double ex = exp((double)Ls[j] - (double)m);
+            z += ex;
+            if (j == lane) num = ex;
+        }
+        W.idx[(int64_t)t * k + lane] = Es[lane];
+        W.w[(int64_t)t * k + lane] = bad ? __builtin_nanf("") : (float)(num / z);
+    }
+    if (bad && threadIdx.x == 0) report_bad_id(W, tag);
+}
+
 hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s,
                         unsigned long long ep) {
     const uint32_t tag = (uint32_t)(ep % 0xFFFFFFFFull) + 1u;
     const int NE = L.n_expert;
+    if (L.hash_table) {
+        // table lookups and k logits per token, then the per-expert lists
+        if (L.act_dtype == 1)
+            hipLaunchKernelGGL(k_route_hashed<true>, dim3(n_tok), dim3(256), 0, s, L.router, L.router_bias, x,
+                               L.hash_table, L.n_vocab, L.n_embd, L.top_k, W, tag);
+        else
+            hipLaunchKernelGGL(k_route_hashed<false>, dim3(n_tok), dim3(256), 0, s, L.router, L.router_bias, x,
+                               L.hash_table, L.n_vocab, L.n_embd, L.top_k, W, tag);
+        hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, s, n_tok, NE, L.top_k, W);
+        return hipGetLastError();
+    }
     if (n_tok > ROUTE_SMALL_MAX && L.act_dtype == 1 && L.n_embd % (4 * QK) == 0) {
         // batched: MFMA estimates, exact candidates, lists
         const uint16_t *xb = static_cast<const uint16_t *>(x);

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define DS4MOE_ABI_VERSION 2
+#define DS4MOE_ABI_VERSION 3
 
 enum {
     DS4MOE_OK = 0,
@@ -74,7 +74,8 @@ enum {
     DS4MOE_ENOMEM = -2,       /* device allocation failed in ds4moe_create */
     DS4MOE_EHIP = -3,         /* a HIP call failed; the handle is poisoned */
     DS4MOE_EUNSUPPORTED = -4, /* valid but unsupported combination */
-    DS4MOE_EPOISONED = -5     /* handle unusable after an earlier HIP error */
+    DS4MOE_EPOISONED = -5     /* handle unusable after an earlier HIP error, an expired
+                                 bounded wait or a token id out of range */
 };
 
 enum { DS4MOE_F32 = 0, DS4MOE_BF16 = 1 };
@@ -120,6 +121,15 @@ typedef struct ds4moe ds4moe_t; /* opaque; one per MoE layer */
  *                pages give no layout: this one is a stand-in).  codebook is
  *                unused.  A q4 layer runs the dequant-fused GEMV kernels for
  *                every call, in chunks of up to 4 tokens.
+ *   hash_table, n_vocab: a hash-routed layer (the model's hash layers,
+ *                DS4_N_HASH_LAYER = 3 in the model constants of "Redis 作者出手！
+ *                ds4...", section 2.1; the pages say nothing more, so this is a
+ *                reading): token t's experts are row token_ids[t] of the table,
+ *                in slot order, and their weights are the router's softmax
+ *                renormalised over them.  Each row must hold top_k distinct
+ *                experts in 0..n_expert-1 (checked at create: EINVAL); 1 <=
+ *                n_vocab <= INT32_MAX / top_k; 4-byte aligned.  The table is
+ *                copied.  Such a layer is called through the *_ids entry points.
  */
 typedef struct {
     int32_t abi_version; /* DS4MOE_ABI_VERSION */
@@ -134,6 +144,8 @@ typedef struct {
     const uint16_t *sh_up;
     const uint16_t *sh_down;
     int32_t expert_format; /* DS4MOE_FMT_Q2 or DS4MOE_FMT_Q4 */
+    const int32_t *hash_table; /* device int32 [n_vocab][top_k], or NULL (learned routing) */
+    int64_t n_vocab;           /* rows of hash_table (ignored when it is NULL) */
 } ds4moe_desc;
 
 /*
@@ -170,6 +182,23 @@ int ds4moe_route(ds4moe_t *h, const void *x, int32_t n_tok, int32_t *topk_idx, f
                  int32_t *expert_offsets, int32_t *expert_tokens, void *stream);
 
 /*
+ * ds4moe_route with the tokens' ids, for a hash-routed layer (the model's
+ * hash layers: "Redis 作者出手！ds4...", section 2.1, DS4_N_HASH_LAYER).
+ * token_ids: device int32 [n_tok], 4-byte aligned, each in 0..n_vocab-1;
+ * ignored (may be NULL) for a learned-routing layer, which it routes exactly
+ * as ds4moe_route.  On a hash layer topk_idx[t] is the table's row
+ * token_ids[t] in slot order and topk_w[t] the softmax over all logits
+ * renormalised over those experts, which depends on their k logits alone
+ * (only those k router rows are read).  An id out of range cannot be seen
+ * without synchronising: that token's weights (and its block output) become
+ * NaN, and the handle reports DS4MOE_EPOISONED from its next call on.  The
+ * plain entry points (route, forward, forward_stack) refuse a hash layer
+ * with DS4MOE_EINVAL, and ds4moe_forward_static with DS4MOE_EUNSUPPORTED.
+ */
+int ds4moe_route_ids(ds4moe_t *h, const void *x, const int32_t *token_ids, int32_t n_tok, int32_t *topk_idx,
+                     float *topk_w, int32_t *expert_offsets, int32_t *expert_tokens, void *stream);
+
+/*
  * The block ("ds4 深度实战...", section 3.2 "MoE FFN": route, compute only the
  * chosen experts and the shared expert, merge their outputs; section 2.1: the
  * routed gate/up in IQ2_XXS, down in Q2_K, shared expert at full precision).
@@ -180,6 +209,14 @@ int ds4moe_route(ds4moe_t *h, const void *x, int32_t n_tok, int32_t *topk_idx, f
  * fp32 atomics, so the summation order (last bits) may vary between runs.
  */
 int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *stream);
+
+/*
+ * ds4moe_forward with the tokens' ids (token_ids as for ds4moe_route_ids):
+ * the block of a hash-routed layer, with the same kernels as ds4moe_forward
+ * after the routing; a learned-routing layer ignores the ids.
+ */
+int ds4moe_forward_ids(ds4moe_t *h, const void *x, const int32_t *token_ids, int32_t n_tok, float *out,
+                       void *stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph
@@ -244,6 +281,15 @@ int ds4moe_rmsnorm(const float *h, int32_t n_tok, int32_t n_embd, double eps, ui
  */
 int ds4moe_forward_stack(ds4moe_t *const *layers, int32_t n_layers, float *h, int32_t n_tok, double eps,
                          uint16_t *x_bf16, void *stream);
+
+/*
+ * ds4moe_forward_stack with the tokens' ids, for stacks holding hash-routed
+ * layers (the model's first layers; "Redis 作者出手！ds4...", section 2.1,
+ * DS4_N_HASH_LAYER = 3): every layer runs as ds4moe_forward_ids with the same
+ * token_ids (device int32 [n_tok]); NULL is allowed when no layer hashes.
+ */
+int ds4moe_forward_stack_ids(ds4moe_t *const *layers, int32_t n_layers, float *h, const int32_t *token_ids,
+                             int32_t n_tok, double eps, uint16_t *x_bf16, void *stream);
 
 /*
  * Per-kernel timing for benchmarks.  When enabled, ds4moe_forward records HIP

@@ -57,6 +57,17 @@ def host_layer(kind: str):
         r[1::4] = r[0::4]
         lay.router = r
         return lay
+    if kind == "tiny_hash":
+        base = host_layer("tiny")
+        lay = synth.Layer(**{**base.__dict__})
+        lay.hash_table = synth.hash_table(0, 1000, base.spec.n_expert, base.spec.top_k)
+        return lay
+    if kind == "ds4_hash":
+        # a hash layer of the model's shape: a table over the full vocabulary
+        base = host_layer("ds4")
+        lay = synth.Layer(**{**base.__dict__})
+        lay.hash_table = synth.hash_table(1, synth.N_VOCAB, base.spec.n_expert, base.spec.top_k)
+        return lay
     if kind == "ds4_zipf":
         base = host_layer("ds4")
         lay = synth.Layer(**{**base.__dict__})
@@ -76,7 +87,7 @@ def device_layer(kind: str, max_tokens: int = 64):
         lay = host_layer(kind)
         log(f"[gpu] create layer {kind} max_tokens={max_tokens}")
         w = m.upload_layer(lay)
-        act = m.F32 if kind == "tiny" else m.BF16
+        act = m.F32 if kind.startswith("tiny") else m.BF16
         _dev[key] = m.MoELayer(lay.spec, w, max_tokens=max_tokens, act_dtype=act)
         del w
     return _dev[key]

@@ -1,0 +1,268 @@
+"""Hash-routed layers on the GPU against the oracle, through the C ABI.
+
+A hash layer takes each token's experts from row token_ids[t] of its table
+and weights them by the router's softmax renormalised over them (the
+reading of the model's hash layers that the oracle pins).  Checked here:
+the routing (experts and per-expert lists bit-exact, weights within fp32
+rounding), the block output on every kernel path (fused decode, GEMV, grouped
+GEMM, q4 GEMV in chunks), stacks mixing hash and learned layers, and the
+error handling (ids missing, out of range, bad tables).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from bit_quantized_moe_renorm_amd import synth
+from gpu_common import FUSED_TOL, GEMV_TOL, REL_TOL, device_layer, host_layer, log, rel_err
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import bit_quantized_moe_renorm_amd as m  # noqa: E402
+
+
+def _vocab(lay):
+    return lay.hash_table.shape[0]
+
+
+def _inputs(kind, n, seed=3):
+    lay = host_layer(kind)
+    x = synth.activations(seed, n, lay.spec.n_embd, bf16=not kind.startswith("tiny"))
+    ids = synth.token_ids(seed, n, _vocab(lay))
+    return lay, x, ids
+
+
+def _check_route(kind, n, max_tokens=64):
+    lay, x_np, ids_np = _inputs(kind, n)
+    dev = device_layer(kind, max_tokens)
+    log(f"[gpu] hash route {kind} n={n}")
+    idx, w, off, tok = dev.route(m.to_device_x(x_np), ids=m.to_device_ids(ids_np))
+    torch.cuda.synchronize()
+    _, ridx, _, rw64 = oracle.route_hashed(x_np, lay.router, lay.router_bias, lay.spec.top_k, ids_np,
+                                           lay.hash_table)
+    roff, rtok = oracle.bucket(ridx, lay.spec.n_expert)
+    idx, w, off, tok = idx.cpu().numpy(), w.cpu().numpy(), off.cpu().numpy(), tok.cpu().numpy()
+    assert np.array_equal(idx, ridx)
+    assert np.array_equal(off, roff) and np.array_equal(tok, rtok)
+    assert np.max(np.abs(w.astype(np.float64) - rw64)) <= 2.5e-7
+    assert dev.status() == m.OK
+
+
+@pytest.mark.parametrize("kind,n", [("tiny_hash", 1), ("tiny_hash", 5), ("ds4_hash", 1), ("ds4_hash", 3),
+                                    ("ds4_hash", 8), ("ds4_hash", 64)])
+def test_hash_route_matches_oracle(kind, n):
+    _check_route(kind, n)
+
+
+def test_hash_route_prefill_2048():
+    _check_route("ds4_hash", 2048, max_tokens=2048)
+
+
+def _forward(dev, x_np, ids_np, path=m.PATH_AUTO):
+    dev.set_path(path)
+    x = m.to_device_x(x_np)
+    out = torch.zeros((x.shape[0], dev.spec.n_embd), dtype=torch.float32, device="cuda")
+    dev.forward(x, out, ids=m.to_device_ids(ids_np))
+    torch.cuda.synchronize()
+    dev.set_path(m.PATH_AUTO)
+    assert dev.status() == m.OK
+    return out.cpu().numpy()
+
+
+def test_hash_fused_decode_tiny():
+    lay, x, ids = _inputs("tiny_hash", 6)
+    dev = device_layer("tiny_hash")
+    for t in range(6):
+        got = _forward(dev, x[t:t + 1], ids[t:t + 1])
+        ref, _, _ = oracle.forward(lay, x[t:t + 1], token_ids=ids[t:t + 1])
+        err = rel_err(got, ref)
+        log(f"[gpu] hash fused tiny token {t} id {ids[t]}: rel err {err:.2e}")
+        assert err <= FUSED_TOL
+
+
+def test_hash_fused_decode_ds4_and_routing_export():
+    """One token at a time through the fused kernel; the routing it exports
+    (ds4moe_last_routing) is the table row and the renormalised weights."""
+    lay, x, ids = _inputs("ds4_hash", 8)
+    dev = device_layer("ds4_hash")
+    ref, ridx, rw = oracle.forward(lay, x, token_ids=ids)
+    for t in range(8):
+        got = _forward(dev, x[t:t + 1], ids[t:t + 1])
+        err = rel_err(got, ref[t:t + 1])
+        log(f"[gpu] hash fused ds4 token {t} id {ids[t]}: rel err {err:.2e}")
+        assert err <= FUSED_TOL
+        idx, w, off, tok = (a.cpu().numpy() for a in dev.last_routing(1))
+        assert np.array_equal(idx[0], ridx[t]) and np.array_equal(idx[0], lay.hash_table[ids[t]])
+        assert np.max(np.abs(w[0] - rw[t])) <= 2.5e-7
+        roff, rtok = oracle.bucket(ridx[t:t + 1], 256)
+        assert np.array_equal(off, roff) and np.array_equal(tok, rtok)
+
+
+def test_hash_gemv_tiny():
+    lay, x, ids = _inputs("tiny_hash", 4)
+    got = _forward(device_layer("tiny_hash"), x, ids, m.PATH_GEMV)
+    ref, _, _ = oracle.forward(lay, x, token_ids=ids)
+    assert rel_err(got, ref) <= GEMV_TOL
+
+
+@pytest.mark.parametrize("n,path", [(3, m.PATH_GEMV), (2, m.PATH_AUTO), (7, m.PATH_AUTO), (64, m.PATH_AUTO)])
+def test_hash_forward_ds4(n, path):
+    lay, x, ids = _inputs("ds4_hash", n)
+    log(f"[gpu] hash forward ds4 n={n} path={path}")
+    got = _forward(device_layer("ds4_hash"), x, ids, path)
+    ref, _, _ = oracle.forward(lay, x, token_ids=ids)
+    err = rel_err(got, ref)
+    log(f"[gpu]   rel err {err:.2e}")
+    assert err <= REL_TOL
+
+
+def test_hash_forward_prefill_512_sampled():
+    """A 512-token call on the grouped GEMM path; the oracle computes 40
+    sampled rows, the tile edges among them."""
+    lay, x, ids = _inputs("ds4_hash", 512, seed=4)
+    got = _forward(device_layer("ds4_hash", 512), x, ids)
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, 63, 64, 255, 256, 510, 511],
+                                     np.random.default_rng(4).choice(512, 30, replace=False)])).astype(np.int32)
+    ref, _, _ = oracle.forward(lay, x, rows, token_ids=ids)
+    err = rel_err(got[rows], ref)
+    log(f"[gpu] hash prefill 512 rows {len(rows)}: rel err {err:.2e}")
+    assert err <= REL_TOL
+
+
+def test_hash_same_x_different_ids():
+    """Two copies of one activation row under two ids: the outputs are the two
+    table rows' mixtures (on the GPU as in the oracle)."""
+    lay = host_layer("ds4_hash")
+    x = np.repeat(synth.activations(5, 1, 4096), 2, axis=0)
+    ids = np.array([11, 70000], np.int32)
+    assert set(lay.hash_table[11]) != set(lay.hash_table[70000])
+    got = _forward(device_layer("ds4_hash"), x, ids)
+    ref, _, _ = oracle.forward(lay, x, token_ids=ids)
+    assert rel_err(got, ref) <= REL_TOL
+    assert rel_err(got[0], got[1]) > 1e-2
+
+
+def test_learned_layer_ignores_ids():
+    lay = host_layer("ds4")
+    dev = device_layer("ds4")
+    x_np = synth.activations(1, 3, 4096)
+    x = m.to_device_x(x_np)
+    a = [t.cpu().numpy() for t in dev.route(x)]
+    b = [t.cpu().numpy() for t in dev.route(x, ids=m.to_device_ids(np.array([5, -7, 10 ** 6], np.int32)))]
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+    assert dev.status() == m.OK
+
+
+def test_hash_q4_layer_in_chunks():
+    """A q4 hash layer: 7 tokens run as GEMV chunks of 4 + 3, each with its
+    own slice of the ids."""
+    base = synth.make_layer(synth.DS4, seed=1, fmt="q4")
+    base.hash_table = host_layer("ds4_hash").hash_table
+    x = synth.activations(6, 7, 4096)
+    ids = synth.token_ids(6, 7, synth.N_VOCAB)
+    log("[gpu] create q4 hash layer")
+    dev = m.MoELayer(base.spec, m.upload_layer(base), max_tokens=8, act_dtype=m.BF16)
+    got = _forward(dev, x, ids)
+    ref, _, _ = oracle.forward(base, x, token_ids=ids)
+    err = rel_err(got, ref)
+    log(f"[gpu] q4 hash n=7: rel err {err:.2e}")
+    assert err <= REL_TOL
+    dev.close()
+
+
+def test_hash_stack_with_learned_layers():
+    """Three hash layers then two learned ones, one library call, against the
+    oracle's stack taken one layer at a time from the GPU's own inputs
+    (teacher-forced: a last-bit difference cannot flip a later routing)."""
+    kinds = ["ds4_hash", "ds4_hash", "ds4_hash", "ds4", "ds4"]
+    devs = [device_layer(k, 64) for k in kinds]
+    h0 = synth.residual(7, 4, 4096)
+    ids = synth.token_ids(7, 4, synth.N_VOCAB)
+    h = torch.from_numpy(h0.copy()).cuda()
+    d_ids = m.to_device_ids(ids)
+    m.forward_stack(devs, h, ids=d_ids)
+    torch.cuda.synchronize()
+    got = h.cpu().numpy()
+    # layer by layer on the GPU, each layer's input checked against the oracle
+    hg = torch.from_numpy(h0.copy()).cuda()
+    for i, (k, dev) in enumerate(zip(kinds, devs)):
+        x = m.rmsnorm(hg)
+        before = hg.cpu().numpy().astype(np.float64)
+        out = torch.zeros_like(hg)
+        dev.forward(x, out, ids=d_ids)
+        torch.cuda.synchronize()
+        x_np = x.cpu().view(torch.int16).numpy().view(np.uint16)
+        ref, ridx, _ = oracle.forward(host_layer(k), x_np, token_ids=ids if k == "ds4_hash" else None)
+        err = rel_err(out.cpu().numpy(), ref)
+        log(f"[gpu] stack layer {i} ({k}): rel err {err:.2e}")
+        assert err <= REL_TOL
+        if k == "ds4_hash":
+            assert np.array_equal(ridx, host_layer(k).hash_table[ids])
+        hg += out
+        assert np.all(np.isfinite(before))
+    assert rel_err(got - h0, hg.cpu().numpy() - h0) <= REL_TOL
+
+
+def test_hash_errors():
+    lay, x_np, ids_np = _inputs("ds4_hash", 3)
+    dev = device_layer("ds4_hash")
+    x = m.to_device_x(x_np)
+    out = torch.zeros((3, 4096), dtype=torch.float32, device="cuda")
+    with pytest.raises(m.Ds4MoeError) as ei:
+        dev.forward(x, out)                                    # ids missing
+    assert ei.value.code == m.EINVAL and "token ids" in str(ei.value)
+    with pytest.raises(m.Ds4MoeError) as ei:
+        dev.route(x)
+    assert ei.value.code == m.EINVAL
+    with pytest.raises(m.Ds4MoeError) as ei:
+        dev.forward_static(x[:1], out[:1])
+    assert ei.value.code == m.EUNSUPPORTED
+    with pytest.raises(m.Ds4MoeError) as ei:
+        m.forward_stack([dev], torch.zeros((3, 4096), dtype=torch.float32, device="cuda"))
+    assert ei.value.code == m.EINVAL
+    assert dev.status() == m.OK
+
+
+@pytest.mark.parametrize("n", [1, 3])
+def test_hash_bad_id_poisons_handle(n):
+    """An id outside 0..n_vocab-1: that call's output turns NaN (no
+    out-of-range read happens) and the handle reports EPOISONED."""
+    lay = host_layer("ds4_hash")
+    dev = m.MoELayer(lay.spec, m.upload_layer(lay), max_tokens=8, act_dtype=m.BF16)
+    x = m.to_device_x(synth.activations(3, n, 4096))
+    ids = synth.token_ids(3, n, synth.N_VOCAB)
+    out = torch.zeros((n, 4096), dtype=torch.float32, device="cuda")
+    dev.forward(x, out, ids=m.to_device_ids(ids))
+    torch.cuda.synchronize()
+    assert dev.status() == m.OK and bool(torch.isfinite(out).all())
+    bad = ids.copy()
+    bad[-1] = synth.N_VOCAB                                    # one past the end
+    log(f"[gpu] hash bad id n={n}")
+    out.zero_()
+    dev.forward(x, out, ids=m.to_device_ids(bad))
+    torch.cuda.synchronize()
+    assert not bool(torch.isfinite(out).all())
+    assert dev.status() == m.EPOISONED
+    with pytest.raises(m.Ds4MoeError) as ei:
+        dev.forward(x, out, ids=m.to_device_ids(ids))
+    assert ei.value.code == m.EPOISONED and "token id" in str(ei.value)
+    dev.close()
+
+
+def test_hash_table_validated_at_create():
+    lay = host_layer("tiny_hash")
+    for bad_val, what in ((8, "out of range"), (-1, "out of range"), (None, "repeated")):
+        tab = lay.hash_table.copy()
+        if bad_val is None:
+            tab[17, 1] = tab[17, 0]
+        else:
+            tab[17, 1] = bad_val
+        w = m.upload_layer(lay)
+        w["hash_table"] = m.to_device_ids(tab.reshape(-1)).view(tab.shape)
+        with pytest.raises(m.Ds4MoeError) as ei:
+            m.MoELayer(lay.spec, w, max_tokens=4, act_dtype=m.F32)
+        assert ei.value.code == m.EINVAL and what in str(ei.value) and "row 17" in str(ei.value)
