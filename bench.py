@@ -789,6 +789,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode only (skip the nested prefill)")
+    ap.add_argument("--no-hash-decode", action="store_true",
+                    help="skip the hash-routed layer's decode figure (its launches are the same kernel)")
     ap.add_argument("--workload", choices=("decode", "prefill", "stack", "batch", "q4"), default="decode")
     ap.add_argument("--layers", type=int, default=43, help="stack workload: number of layers")
     ap.add_argument("--hash-layers", type=int, default=3,
@@ -825,7 +827,8 @@ def main():
         from bit_quantized_moe_renorm_amd import synth
         layer = synth.make_layer(synth.DS4, seed=1)
         res = run_decode(args, layer)
-        res["hash_layer_decode"] = run_decode_hash(args, layer)
+        if not args.no_hash_decode:
+            res["hash_layer_decode"] = run_decode_hash(args, layer)
         if not args.no_prefill:
             pre = run_prefill(args, layer, cpu=not args.no_cpu_baseline)
             res["prefill"] = {k: pre[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "dtype",

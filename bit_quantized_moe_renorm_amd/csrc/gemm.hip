@@ -306,6 +306,26 @@ __device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &
     }
 }
 
+// XCD-aware tile order for the routed GEMMs.  Workgroups go to the 8 XCDs
+// round-robin by linear id, so the gx row groups of one chunk (consecutive
+// ids), which all read that chunk's activation rows, would sit on 8 XCDs with
+// 8 separate L2s and each fetch the rows from memory.  Here, within each run
+// of 8 gx ids, id 8 m + j takes row group m of chunk 8 g + j: a chunk's row
+// groups share one XCD's L2.  Ids past the last whole run keep the plain
+// order.  The map is a bijection of the (gx, gy) grid, per K split.
+__device__ __forceinline__ void xcd_tile(int gx, int gy, int &tx, int &ty) {
+    const int lin = blockIdx.x + gx * blockIdx.y;
+    const int run = 8 * gx;
+    if (lin < (gy / 8) * run) {
+        const int g = lin / run, r = lin - g * run;
+        ty = 8 * g + (r & 7);
+        tx = r >> 3;
+    } else {
+        ty = lin / gx;
+        tx = lin - ty * gx;
+    }
+}
+
 // grid: (n_ff / RGU_ROWS, max chunks), RB_THREADS threads.  Wave w covers
 // n_ff rows f0..f0+16 GU_FR-1 of gate and up for all tokens of the chunk
 // (1..4 token tiles), over the whole n_embd.
@@ -313,7 +333,8 @@ __device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &
 // than one split) the raw sums go to part[z][slot][2 n_ff] for
 // k_routed_gu_reduce; nq = slots of the call.
 __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_gateup_routed(Layer L, Work W, int bps, float *part, int nq) {
-    const int c = blockIdx.y;
+    int tx, c;
+    xcd_tile(gridDim.x, gridDim.y, tx, c);
     if (c >= *W.nchunks) return;
     const int4 ch = W.chunks[c];
     const int e = ch.x, beg = ch.y, cnt = ch.z;
@@ -328,7 +349,7 @@ __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_gateup_routed(Layer L, W
         const int sr = tid / LD_PER_ROW;
         ld.init(W.x16 + (int64_t)(W.list[beg + min(sr, cnt - 1)] / k) * E + QK * b0, tid);
     }
-    const int f0 = blockIdx.x * RGU_ROWS + wave * 16 * GU_FR;
+    const int f0 = tx * RGU_ROWS + wave * 16 * GU_FR;
     // fragment fi: matrix fi / GU_FR (gate, up), rows f0 + 16 (fi % GU_FR) + rl
     const int64_t rb = ((int64_t)e * F + f0 + rl) * nbe;
     const uint8_t *qg = L.iq2_qs[0] + (rb + b0) * 64 + 16 * grp;  // + 64 bi (up: + iq2_qs[1] - iq2_qs[0])
@@ -468,7 +489,8 @@ __device__ __forceinline__ void down_routed_tiles(const Layer &L, const Work &W,
 // blockIdx.z = K split (256-K blocks bps z ..): every split adds its share of
 // w y into out with the same atomics.
 __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_down_routed(Layer L, Work W, float *__restrict__ out, int bps) {
-    const int c = blockIdx.y;
+    int tx, c;
+    xcd_tile(gridDim.x, gridDim.y, tx, c);
     if (c >= *W.nchunks) return;
     const int4 ch = W.chunks[c];
     const int e = ch.x, beg = ch.y, cnt = ch.z;
@@ -483,7 +505,7 @@ __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_down_routed(Layer L, Wor
         const int sr = tid / LD_PER_ROW;
         ld.init(W.hbuf16 + (int64_t)W.list[beg + min(sr, cnt - 1)] * F + QK * b0, tid);
     }
-    const int r0 = blockIdx.x * RDN_ROWS + wave * 16 * DN_NF;
+    const int r0 = tx * RDN_ROWS + wave * 16 * DN_NF;
     const bool active = r0 < E;
     // fragment fi = rows r0 + 16 fi + rl; one base per plane, fragments 16 rows apart
     const int64_t rb = ((int64_t)e * E + (active ? r0 + rl : 0)) * nbf;
