@@ -23,12 +23,13 @@ PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
 ABI_VERSION = 3
 TIMING_KINDS = ("route", "gateup_routed", "gateup_shared", "down_routed", "down_shared", "gemm_gateup_routed",
                 "gemm_down_routed", "fused", "gemm_prep", "gemm_gateup_shared", "gemm_down_shared",
-                "q4_gateup_routed", "q4_down_routed")
+                "q4_gateup_routed", "q4_down_routed", "cache")
 
 SYMBOLS = ("ds4moe_create", "ds4moe_route", "ds4moe_forward", "ds4moe_set_path", "ds4moe_dequantize",
            "ds4moe_rmsnorm", "ds4moe_forward_stack", "ds4moe_timing_enable", "ds4moe_timing_read",
            "ds4moe_last_routing", "ds4moe_status", "ds4moe_set_wait_limit", "ds4moe_forward_static",
-           "ds4moe_route_ids", "ds4moe_forward_ids", "ds4moe_forward_stack_ids",
+           "ds4moe_route_ids", "ds4moe_forward_ids", "ds4moe_forward_stack_ids", "ds4moe_cache_stats",
+           "ds4moe_cache_slots",
            "ds4moe_destroy", "ds4moe_last_error")
 
 
@@ -45,7 +46,8 @@ class Desc(ctypes.Structure):
                 ("router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("gate", ctypes.c_void_p),
                 ("up", ctypes.c_void_p), ("down", ctypes.c_void_p), ("codebook", ctypes.c_void_p),
                 ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p),
-                ("expert_format", ctypes.c_int32), ("hash_table", ctypes.c_void_p), ("n_vocab", ctypes.c_int64)]
+                ("expert_format", ctypes.c_int32), ("hash_table", ctypes.c_void_p), ("n_vocab", ctypes.c_int64),
+                ("expert_cache_slots", ctypes.c_int32)]
 
 
 _lib = None
@@ -80,6 +82,8 @@ def load_library(path: Optional[Path] = None) -> ctypes.CDLL:
     L.ds4moe_route_ids.argtypes = [P, P, P, i32, P, P, P, P, P]
     L.ds4moe_forward_ids.argtypes = [P, P, P, i32, P, P]
     L.ds4moe_forward_stack_ids.argtypes = [P, i32, P, P, i32, ctypes.c_double, P, P]
+    L.ds4moe_cache_stats.argtypes = [P, ctypes.POINTER(ctypes.c_int64), P]
+    L.ds4moe_cache_slots.argtypes = [P, ctypes.POINTER(ctypes.c_int32), P]
     L.ds4moe_destroy.argtypes = [P]
     L.ds4moe_last_error.restype = ctypes.c_char_p
     for name in SYMBOLS:
@@ -131,10 +135,12 @@ class MoELayer:
     uint16 values), sh_gate/sh_up/sh_down bf16 or None; with ``fmt`` "q4"
     (weights["fmt"]) gate, up and down are uint8 [..., 144] Q4_K-style blocks;
     ``hash_table`` (int32 [n_vocab, top_k] on the GPU, or None) makes it a
-    hash-routed layer, whose calls take the tokens' ids.
+    hash-routed layer, whose calls take the tokens' ids.  ``cache_slots`` > 0 keeps
+    the routed experts in pinned host memory with that many of them in an HBM cache.
     """
 
-    def __init__(self, spec, weights: dict, max_tokens: int, act_dtype: int = BF16, stream=None):
+    def __init__(self, spec, weights: dict, max_tokens: int, act_dtype: int = BF16, stream=None,
+                 cache_slots: int = 0):
         import numpy as np
         L = load_library()
         cb = np.ascontiguousarray(weights["codebook"], dtype=np.uint16)
@@ -146,7 +152,7 @@ class MoELayer:
                  _ptr(weights["router"]), _ptr(weights.get("router_bias")), _ptr(weights["gate"]),
                  _ptr(weights["up"]), _ptr(weights["down"]), cb.ctypes.data,
                  _ptr(weights.get("sh_gate")), _ptr(weights.get("sh_up")), _ptr(weights.get("sh_down")), fmt,
-                 _ptr(tab), 0 if tab is None else tab.shape[0])
+                 _ptr(tab), 0 if tab is None else tab.shape[0], cache_slots)
         h = ctypes.c_void_p()
         _check(L.ds4moe_create(ctypes.byref(d), _stream(stream), ctypes.byref(h)))
         self.h = h
@@ -155,6 +161,7 @@ class MoELayer:
         self.act_dtype = act_dtype
         self.fmt = fmt
         self.hashed = tab is not None
+        self.cache_slots = cache_slots
 
     def close(self):
         if getattr(self, "h", None):
@@ -256,6 +263,18 @@ class MoELayer:
         dst = torch.empty(shape, dtype=torch.float32, device="cuda")
         _check(load_library().ds4moe_dequantize(self.h, expert, which, _ptr(dst), _stream(stream)))
         return dst
+
+    def cache_stats(self, stream=None):
+        """HBM expert cache counters: dict(calls, hits, misses, bytes) (synchronises)."""
+        v = (ctypes.c_int64 * 4)()
+        _check(load_library().ds4moe_cache_stats(self.h, v, _stream(stream)))
+        return dict(calls=v[0], hits=v[1], misses=v[2], bytes=v[3])
+
+    def cache_slots_held(self, stream=None):
+        """The expert each HBM cache slot holds (-1: empty), as a list (synchronises)."""
+        v = (ctypes.c_int32 * self.cache_slots)()
+        _check(load_library().ds4moe_cache_slots(self.h, v, _stream(stream)))
+        return list(v)
 
     def timing_enable(self, on: bool = True):
         _check(load_library().ds4moe_timing_enable(self.h, 1 if on else 0))

@@ -46,6 +46,35 @@ struct Layer {
     // ([n_vocab][top_k], library-owned), nullptr for a learned-routing layer
     const int32_t *hash_table;
     int n_vocab;
+    // host-resident experts: the HBM slot holding each expert's weights
+    // ([n_expert], set for the call by the cache update), nullptr when every
+    // expert is resident in HBM (slot = expert)
+    const int32_t *slot_of;
+};
+
+// The weight slot of expert e in the routed planes.
+__device__ __forceinline__ int expert_slot(const Layer &L, int e) { return L.slot_of ? L.slot_of[e] : e; }
+
+// HBM expert cache of a layer whose routed experts live in host memory
+// (device memory, library-owned; every pointer a device address).
+struct ExpertCache {
+    int32_t *slot_of;       // [n_expert]: slot holding the expert, -1 if none
+    int32_t *slot_expert;   // [slots]: expert held, -1 if empty
+    uint32_t *slot_last;    // [slots]: cache clock of its last use (0 = never)
+    uint32_t *clock;        // calls so far
+    int32_t *miss_slot;     // [slots]: slots to fill in this call, in miss order
+    int32_t *miss_count;
+    unsigned long long *stats;  // calls, hits, misses, bytes loaded
+    int slots;
+};
+
+// The routed planes of one expert, as (host-resident source, HBM slot base,
+// bytes per expert): 7 planes for the 2-bit format, 6 for Q4_K.
+struct ExpertPlanes {
+    int n;
+    const uint8_t *host[7];
+    uint8_t *hbm[7];
+    int64_t bytes[7];
 };
 
 // Workspace (device), carved from one allocation at create time.
@@ -156,6 +185,9 @@ hipError_t launch_router_prep(const float *router, int NE, int E, uint16_t *hml,
 // hand-off tag is ep + 1, never 0)
 hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s,
                         unsigned long long ep);
+hipError_t launch_cache_update(const Layer &L, const Work &W, const ExpertCache &C, int64_t expert_bytes,
+                               hipStream_t s);
+hipError_t launch_cache_fill(const ExpertPlanes &P, const ExpertCache &C, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, int n, uint32_t v, hipStream_t s);
 hipError_t launch_route_export(const Layer &L, const Work &W, int n_tok, int32_t *idx, float *w,
                                int32_t *offsets, int32_t *tokens, hipStream_t s);
@@ -169,7 +201,7 @@ hipError_t launch_gemv_down_shared(const Layer &L, const Work &W, int n_tok, flo
 enum TimingKind {
     TK_ROUTE = 0, TK_GU_ROUTED = 1, TK_GU_SHARED = 2, TK_DN_ROUTED = 3, TK_DN_SHARED = 4,
     TK_GEMM_GU_ROUTED = 5, TK_GEMM_DN_ROUTED = 6, TK_FUSED = 7, TK_GEMM_PREP = 8, TK_GEMM_GU_SHARED = 9,
-    TK_GEMM_DN_SHARED = 10, TK_Q4_GU_ROUTED = 11, TK_Q4_DN_ROUTED = 12, TK_COUNT = 13
+    TK_GEMM_DN_SHARED = 10, TK_Q4_GU_ROUTED = 11, TK_Q4_DN_ROUTED = 12, TK_CACHE = 13, TK_COUNT = 14
 };
 
 bool gemm_enabled();

@@ -76,6 +76,13 @@ struct ds4moe {
     size_t static_need = 0;               // bytes of it this layer needs
     uint32_t *status_host = nullptr;      // pinned, mapped: nonzero = a bounded wait expired (that call's tag)
     std::vector<void *> allocs;
+    // host-resident experts (cache.slots > 0): the HBM cache, the planes it
+    // copies, and the layer as seen from the host store (for dequantize)
+    ExpertCache cache{};
+    ExpertPlanes planes{};
+    int64_t expert_bytes = 0;
+    Layer Lhost{};
+    std::vector<void *> host_allocs;      // pinned host memory of the backing store
     // timing
     bool timing = false;
     std::vector<hipEvent_t> events;  // pairs
@@ -88,6 +95,7 @@ struct ds4moe {
         for (void *p : allocs) (void)hipFree(p);
         for (hipEvent_t e : events) (void)hipEventDestroy(e);
         if (status_host) (void)hipHostFree(status_host);
+        for (void *p : host_allocs) (void)hipHostFree(p);
     }
     void *alloc(size_t bytes, hipError_t &err) {
         void *p = nullptr;
@@ -140,15 +148,12 @@ static size_t carve_static(const Layer &L, char *base, Work &S) {
     return off;
 }
 
-// One call of at most GEMV_MAX_TOK tokens on a q4 layer: router, shared
-// gate/up, routed gate/up (Q4_K), routed down (Q4_K), shared down.
-static int run_q4_chunk(ds4moe *h, const Work &W, const void *x, int n, float *out, unsigned long long ep,
-                        hipStream_t s, bool timed) {
+// The expert kernels of a q4 layer after the routing, for at most
+// GEMV_MAX_TOK tokens: shared gate/up, routed gate/up (Q4_K), routed down
+// (Q4_K), shared down.
+static int run_q4_experts(ds4moe *h, const Work &W, const void *x, int n, float *out, hipStream_t s, bool timed) {
     const Layer &L = h->L;
-    int tb = timed ? h->tbegin(TK_ROUTE, s) : -1;
-    int rc = check_launch(h, launch_route(L, W, x, n, s, ep), "q4 route");
-    h->tend(tb, s);
-    if (rc) return rc;
+    int tb, rc = DS4MOE_OK;
     if (L.n_shared) {
         tb = timed ? h->tbegin(TK_GU_SHARED, s) : -1;
         rc = check_launch(h, launch_gemv_gateup_shared(L, W, x, n, s), "q4 shared gate/up");
@@ -169,6 +174,17 @@ static int run_q4_chunk(ds4moe *h, const Work &W, const void *x, int n, float *o
         h->tend(tb, s);
     }
     return rc;
+}
+
+// One call of at most GEMV_MAX_TOK tokens on a q4 layer: router, then the
+// expert kernels.
+static int run_q4_chunk(ds4moe *h, const Work &W, const void *x, int n, float *out, unsigned long long ep,
+                        hipStream_t s, bool timed) {
+    int tb = timed ? h->tbegin(TK_ROUTE, s) : -1;
+    int rc = check_launch(h, launch_route(h->L, W, x, n, s, ep), "q4 route");
+    h->tend(tb, s);
+    if (rc) return rc;
+    return run_q4_experts(h, W, x, n, out, s, timed);
 }
 
 extern "C" {
@@ -198,6 +214,10 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
         return fail(DS4MOE_EINVAL, "create: NULL router/gate/up/down/codebook");
     if (d->n_shared && (!d->sh_gate || !d->sh_up || !d->sh_down))
         return fail(DS4MOE_EINVAL, "create: n_shared = 1 but a shared-expert pointer is NULL");
+    if (d->expert_cache_slots < 0 || d->expert_cache_slots > d->n_expert ||
+        (d->expert_cache_slots > 0 && d->expert_cache_slots < d->top_k))
+        return fail(DS4MOE_EINVAL, "create: expert_cache_slots %d not 0 or in top_k..n_expert (%d..%d)",
+                    d->expert_cache_slots, d->top_k, d->n_expert);
     if (d->hash_table) {
         if (d->n_vocab < 1 || d->n_vocab > (int64_t)(INT32_MAX / d->top_k))
             return fail(DS4MOE_EINVAL, "create: n_vocab %lld for a hash table", (long long)d->n_vocab);
@@ -233,14 +253,46 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     uint32_t *ddd = nullptr;
     uint8_t *q4q[3] = {nullptr, nullptr, nullptr};
     uint4 *q4m[3] = {nullptr, nullptr, nullptr};
+    // HBM holds the planes of every expert, or of `slots` experts when the
+    // routed experts live in host memory (their planes are then in pinned host
+    // memory, for all experts, in the same layout)
+    const int S = d->expert_cache_slots;
+    const int64_t NR = S ? S : NE;
+    const int64_t gu_pe = F * L.nbe, dn_pe = E * L.nbf;  // blocks per expert
     if (q4) {
-        const int64_t nbk[3] = {gu_blocks, gu_blocks, dn_blocks};
+        const int64_t nbk[3] = {gu_pe * NR, gu_pe * NR, dn_pe * NR};
         for (int i = 0; i < 3; ++i) q4q[i] = (uint8_t *)A(nbk[i] * 128), q4m[i] = (uint4 *)A(nbk[i] * 16);
     } else {
-        gq = (uint8_t *)A(gu_blocks * 64), uq = (uint8_t *)A(gu_blocks * 64);
-        gd = (uint16_t *)A(gu_blocks * 2), ud = (uint16_t *)A(gu_blocks * 2);
-        dq = (uint8_t *)A(dn_blocks * 64), dsc = (uint8_t *)A(dn_blocks * 16);
-        ddd = (uint32_t *)A(dn_blocks * 4);
+        gq = (uint8_t *)A(gu_pe * NR * 64), uq = (uint8_t *)A(gu_pe * NR * 64);
+        gd = (uint16_t *)A(gu_pe * NR * 2), ud = (uint16_t *)A(gu_pe * NR * 2);
+        dq = (uint8_t *)A(dn_pe * NR * 64), dsc = (uint8_t *)A(dn_pe * NR * 16);
+        ddd = (uint32_t *)A(dn_pe * NR * 4);
+    }
+    // pinned host store and cache state
+    bool host_ok = true;
+    auto H = [&](size_t bytes) -> uint8_t * {
+        void *p = nullptr, *dp = nullptr;
+        if (!host_ok || hipHostMalloc(&p, align256(bytes), hipHostMallocMapped) != hipSuccess) {
+            host_ok = false;
+            return nullptr;
+        }
+        h->host_allocs.push_back(p);
+        if (hipHostGetDevicePointer(&dp, p, 0) != hipSuccess) host_ok = false;
+        return (uint8_t *)dp;
+    };
+    uint8_t *hgq = nullptr, *huq = nullptr, *hgd = nullptr, *hud = nullptr, *hdq = nullptr, *hdsc = nullptr,
+            *hddd = nullptr, *hq4q[3] = {nullptr, nullptr, nullptr}, *hq4m[3] = {nullptr, nullptr, nullptr};
+    int32_t *cstate = nullptr;
+    if (S) {
+        if (q4) {
+            const int64_t nbk[3] = {gu_blocks, gu_blocks, dn_blocks};
+            for (int i = 0; i < 3; ++i) hq4q[i] = H(nbk[i] * 128), hq4m[i] = H(nbk[i] * 16);
+        } else {
+            hgq = H(gu_blocks * 64), huq = H(gu_blocks * 64), hgd = H(gu_blocks * 2), hud = H(gu_blocks * 2);
+            hdq = H(dn_blocks * 64), hdsc = H(dn_blocks * 16), hddd = H(dn_blocks * 4);
+        }
+        // slot_of [NE], slot_expert [S], slot_last [S], miss_slot [S], clock, miss_count, stats [4]
+        cstate = (int32_t *)A((NE + 3 * S + 2) * 4 + 64);
     }
     uint16_t *sg = nullptr, *su = nullptr, *sd = nullptr;
     if (d->n_shared) {
@@ -269,6 +321,23 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
         delete h;
         hipGetLastError();
         return fail(DS4MOE_ENOMEM, "create: device allocation failed (%s)", hipGetErrorString(err));
+    }
+    if (!host_ok) {
+        delete h;
+        hipGetLastError();
+        return fail(DS4MOE_ENOMEM, "create: pinned host memory for the host-resident experts");
+    }
+    if (S) {
+        ExpertCache &C = h->cache;
+        C.slots = S;
+        C.slot_of = cstate;
+        C.slot_expert = cstate + NE;
+        C.slot_last = (uint32_t *)(cstate + NE + S);
+        C.miss_slot = cstate + NE + 2 * S;
+        C.clock = (uint32_t *)(cstate + NE + 3 * S);
+        C.miss_count = cstate + NE + 3 * S + 1;
+        // 8-byte aligned, within the 64 bytes allocated past the counters
+        C.stats = (unsigned long long *)(((uintptr_t)(cstate + NE + 3 * S + 2) + 7) & ~(uintptr_t)7);
     }
     Work &W = h->W;
     W.logits = (float *)(ws + o_logits);
@@ -357,18 +426,27 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
         CK(hipMemcpyAsync(su, d->sh_up, F * E * 2, hipMemcpyDeviceToDevice, s));
         CK(hipMemcpyAsync(sd, d->sh_down, E * F * 2, hipMemcpyDeviceToDevice, s));
     }
+    if (S) {
+        // empty cache: no expert resident (-1), stamps, clock, counters 0
+        CK(hipMemsetAsync(cstate, 0xFF, (NE + S) * 4, s));
+        CK(hipMemsetAsync(cstate + NE + S, 0, (2 * S + 2) * 4 + 64, s));
+    }
+    // the repacked planes go to HBM, or to the host store (all experts)
     if (q4) {
         if (((uintptr_t)d->gate | (uintptr_t)d->up | (uintptr_t)d->down) & 15u) {
             delete h;
             return fail(DS4MOE_EINVAL, "create: Q4_K weights must be 16-byte aligned");
         }
-        CK(launch_repack_q4k((const uint8_t *)d->gate, gu_blocks, q4m[0], q4q[0], s));
-        CK(launch_repack_q4k((const uint8_t *)d->up, gu_blocks, q4m[1], q4q[1], s));
-        CK(launch_repack_q4k((const uint8_t *)d->down, dn_blocks, q4m[2], q4q[2], s));
+        uint8_t *tq[3], *tm[3];
+        for (int i = 0; i < 3; ++i) tq[i] = S ? hq4q[i] : q4q[i], tm[i] = S ? hq4m[i] : (uint8_t *)q4m[i];
+        CK(launch_repack_q4k((const uint8_t *)d->gate, gu_blocks, (uint4 *)tm[0], tq[0], s));
+        CK(launch_repack_q4k((const uint8_t *)d->up, gu_blocks, (uint4 *)tm[1], tq[1], s));
+        CK(launch_repack_q4k((const uint8_t *)d->down, dn_blocks, (uint4 *)tm[2], tq[2], s));
     } else {
-        CK(launch_repack_iq2((const uint8_t *)d->gate, gu_blocks, gq, gd, s));
-        CK(launch_repack_iq2((const uint8_t *)d->up, gu_blocks, uq, ud, s));
-        CK(launch_repack_q2k((const uint8_t *)d->down, dn_blocks, dq, dsc, ddd, s));
+        CK(launch_repack_iq2((const uint8_t *)d->gate, gu_blocks, S ? hgq : gq, S ? (uint16_t *)hgd : gd, s));
+        CK(launch_repack_iq2((const uint8_t *)d->up, gu_blocks, S ? huq : uq, S ? (uint16_t *)hud : ud, s));
+        CK(launch_repack_q2k((const uint8_t *)d->down, dn_blocks, S ? hdq : dq, S ? hdsc : dsc,
+                             S ? (uint32_t *)hddd : ddd, s));
     }
     CK(hipStreamSynchronize(s));
 #undef CK
@@ -394,6 +472,34 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     L.sh_gate = sg, L.sh_up = su, L.sh_down = sd;
     L.fmt = q4 ? 1 : 0;
     for (int i = 0; i < 3; ++i) L.q4_qs[i] = q4q[i], L.q4_meta[i] = q4m[i];
+    if (S) {
+        // the copy kernel's planes (host store -> HBM slot) and the layer as
+        // the host store holds it
+        ExpertPlanes &P = h->planes;
+        Layer &Lh = h->Lhost;
+        Lh = L;
+        if (q4) {
+            P.n = 6;
+            for (int i = 0; i < 3; ++i) {
+                const int64_t pe = i < 2 ? gu_pe : dn_pe;
+                P.host[2 * i] = hq4q[i], P.hbm[2 * i] = q4q[i], P.bytes[2 * i] = pe * 128;
+                P.host[2 * i + 1] = hq4m[i], P.hbm[2 * i + 1] = (uint8_t *)q4m[i], P.bytes[2 * i + 1] = pe * 16;
+                Lh.q4_qs[i] = hq4q[i], Lh.q4_meta[i] = (const uint4 *)hq4m[i];
+            }
+        } else {
+            P.n = 7;
+            const uint8_t *hs[7] = {hgq, hgd, huq, hud, hdq, hdsc, hddd};
+            uint8_t *ds[7] = {gq, (uint8_t *)gd, uq, (uint8_t *)ud, dq, dsc, (uint8_t *)ddd};
+            const int64_t bs[7] = {gu_pe * 64, gu_pe * 2, gu_pe * 64, gu_pe * 2, dn_pe * 64, dn_pe * 16, dn_pe * 4};
+            for (int i = 0; i < 7; ++i) P.host[i] = hs[i], P.hbm[i] = ds[i], P.bytes[i] = bs[i];
+            Lh.iq2_qs[0] = hgq, Lh.iq2_qs[1] = huq, Lh.iq2_d[0] = (const uint16_t *)hgd, Lh.iq2_d[1] = (const uint16_t *)hud;
+            Lh.q2k_qs = hdq, Lh.q2k_sc = hdsc, Lh.q2k_dd = (const uint32_t *)hddd;
+        }
+        h->expert_bytes = 0;
+        for (int i = 0; i < P.n; ++i) h->expert_bytes += P.bytes[i];
+        L.slot_of = h->cache.slot_of;
+        Lh.slot_of = nullptr;
+    }
     h->decode_grid = decode_grid(d->act_dtype == DS4MOE_BF16);
     if (h->decode_grid <= 0) {
         delete h;
@@ -505,6 +611,107 @@ int ds4moe_route_ids(ds4moe_t *h, const void *x, const int32_t *token_ids, int32
     return route_impl(h, x, token_ids, n_tok, topk_idx, topk_w, expert_offsets, expert_tokens, stream);
 }
 
+// The expert kernels after the routing, for n <= GEMV_MAX_TOK tokens: the
+// dequant-fused GEMV kernels.
+static int run_gemv(ds4moe *h, const Work &W, const void *x, int n, float *out, hipStream_t s) {
+    int rc = DS4MOE_OK, tb;
+    if (h->L.n_shared) {
+        tb = h->tbegin(TK_GU_SHARED, s);
+        rc = check_launch(h, launch_gemv_gateup_shared(h->L, W, x, n, s), "gemv shared gate/up");
+        h->tend(tb, s);
+        if (rc) return rc;
+    }
+    tb = h->tbegin(TK_GU_ROUTED, s);
+    rc = check_launch(h, launch_gemv_gateup_routed(h->L, W, x, n, s), "gemv routed gate/up");
+    h->tend(tb, s);
+    if (rc) return rc;
+    tb = h->tbegin(TK_DN_ROUTED, s);
+    rc = check_launch(h, launch_gemv_down_routed(h->L, W, n, out, s), "gemv routed down");
+    h->tend(tb, s);
+    if (rc) return rc;
+    if (h->L.n_shared) {
+        tb = h->tbegin(TK_DN_SHARED, s);
+        rc = check_launch(h, launch_gemv_down_shared(h->L, W, n, out, s), "gemv shared down");
+        h->tend(tb, s);
+    }
+    return rc;
+}
+
+// The expert kernels after the routing, any n: activation copies and chunk
+// table, then the four grouped GEMMs.
+static int run_gemm(ds4moe *h, const Work &W, const void *x, int n, float *out, hipStream_t s) {
+    int tb = h->tbegin(TK_GEMM_PREP, s);
+    int rc = check_launch(h, launch_gemm_prep(h->L, W, x, n, s), "gemm prep");
+    h->tend(tb, s);
+    if (rc) return rc;
+    tb = h->tbegin(TK_GEMM_GU_ROUTED, s);
+    rc = check_launch(h, launch_gemm_gateup_routed(h->L, W, n, s), "gemm routed gate/up");
+    h->tend(tb, s);
+    if (rc) return rc;
+    if (h->L.n_shared) {
+        tb = h->tbegin(TK_GEMM_GU_SHARED, s);
+        rc = check_launch(h, launch_gemm_gateup_shared(h->L, W, x, n, s), "gemm shared gate/up");
+        h->tend(tb, s);
+        if (rc) return rc;
+    }
+    tb = h->tbegin(TK_GEMM_DN_ROUTED, s);
+    rc = check_launch(h, launch_gemm_down_routed(h->L, W, n, out, s), "gemm routed down");
+    h->tend(tb, s);
+    if (rc) return rc;
+    if (h->L.n_shared) {
+        tb = h->tbegin(TK_GEMM_DN_SHARED, s);
+        rc = check_launch(h, launch_gemm_down_shared(h->L, W, n, out, s), "gemm shared down");
+        h->tend(tb, s);
+    }
+    return rc;
+}
+
+static int run_route(ds4moe *h, const Work &W, const void *x, int n, hipStream_t s) {
+    int tb = h->tbegin(TK_ROUTE, s);
+    int rc = check_launch(h, launch_route(h->L, W, x, n, s, h->route_calls++), "route");
+    h->tend(tb, s);
+    return rc;
+}
+
+// Host-resident experts: after the routing, the cache update and the copy of
+// the missed experts into their HBM slots.
+static int run_cache(ds4moe *h, const Work &W, hipStream_t s) {
+    int tb = h->tbegin(TK_CACHE, s);
+    int rc = check_launch(h, launch_cache_update(h->L, W, h->cache, h->expert_bytes, s), "cache update");
+    if (!rc) rc = check_launch(h, launch_cache_fill(h->planes, h->cache, s), "cache fill");
+    h->tend(tb, s);
+    return rc;
+}
+
+// A layer with host-resident experts: the call in sub-calls whose distinct
+// experts fit in the cache's slots (at most slots / top_k tokens each, unless
+// the slots hold every expert), each routed, cached and computed in turn.
+static int forward_cached(ds4moe *h, const void *x, const int32_t *ids, int n_tok, float *out, hipStream_t s) {
+    const Layer &L = h->L;
+    int chunk = h->cache.slots >= L.n_expert ? n_tok : std::max(1, h->cache.slots / L.top_k);
+    if (L.fmt == 1 || h->path == DS4MOE_PATH_GEMV) chunk = std::min(chunk, GEMV_MAX_TOK);
+    h->last_n_tok = chunk >= n_tok ? n_tok : -1;
+    h->last_static = false;
+    const size_t xb = L.act_dtype == DS4MOE_BF16 ? 2 : 4;
+    for (int c0 = 0; c0 < n_tok; c0 += chunk) {
+        const int n = std::min(chunk, n_tok - c0);
+        const void *xc = (const char *)x + (size_t)c0 * L.n_embd * xb;
+        float *oc = out + (size_t)c0 * L.n_embd;
+        Work W = h->W;
+        W.ids = ids ? ids + c0 : nullptr;
+        int rc = run_route(h, W, xc, n, s);
+        if (!rc) rc = run_cache(h, W, s);
+        if (rc) return rc;
+        bool gemv = n <= GEMV_MAX_TOK && (L.fmt == 1 || h->path == DS4MOE_PATH_GEMV ||
+                                          (h->path == DS4MOE_PATH_AUTO && (n == 1 || L.act_dtype == DS4MOE_F32)));
+        rc = L.fmt == 1 ? run_q4_experts(h, W, xc, n, oc, s, true)
+             : gemv     ? run_gemv(h, W, xc, n, oc, s)
+                        : run_gemm(h, W, xc, n, oc, s);
+        if (rc) return rc;
+    }
+    return DS4MOE_OK;
+}
+
 static int forward_impl(ds4moe_t *h, const void *x, const int32_t *ids, int32_t n_tok, float *out, void *stream) {
     int rc = common_checks(h, x, n_tok, "forward");
     if (rc) return rc;
@@ -513,11 +720,12 @@ static int forward_impl(ds4moe_t *h, const void *x, const int32_t *ids, int32_t 
     if (n_tok > 0 && !aligned16(out)) return fail(DS4MOE_EINVAL, "forward: out is not 16-byte aligned");
     if (n_tok == 0) return DS4MOE_OK;
     if ((rc = stream_checks((hipStream_t)stream, "forward"))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (h->cache.slots) return forward_cached(h, x, ids, n_tok, out, s);
     if (h->L.fmt == 1) {
         // q4: the GEMV kernels (set_path refuses the GEMM path), in chunks of
         // up to GEMV_MAX_TOK tokens; the routing of a call of more tokens is
         // not kept for ds4moe_last_routing
-        hipStream_t s = (hipStream_t)stream;
         h->last_n_tok = n_tok <= GEMV_MAX_TOK ? n_tok : -1;
         h->last_static = false;
         const size_t xb = h->L.act_dtype == DS4MOE_BF16 ? 2 : 4;
@@ -543,7 +751,6 @@ static int forward_impl(ds4moe_t *h, const void *x, const int32_t *ids, int32_t 
         return fail(DS4MOE_EUNSUPPORTED, "forward: GEMV path takes at most %d tokens (got %d)", GEMV_MAX_TOK, n_tok);
     if (path == DS4MOE_PATH_GEMM && !gemm_available())
         return fail(DS4MOE_EUNSUPPORTED, "forward: the grouped GEMM path is not available in this build");
-    hipStream_t s = (hipStream_t)stream;
     h->last_n_tok = n_tok;
     h->last_static = false;
     Work W = h->W;
@@ -557,57 +764,8 @@ static int forward_impl(ds4moe_t *h, const void *x, const int32_t *ids, int32_t 
         h->tend(tf, s);
         return rc;
     }
-    int tb = h->tbegin(TK_ROUTE, s);
-    rc = check_launch(h, launch_route(h->L, W, x, n_tok, s, h->route_calls++), "route");
-    h->tend(tb, s);
-    if (rc) return rc;
-    if (path == DS4MOE_PATH_GEMV) {
-        if (h->L.n_shared) {
-            tb = h->tbegin(TK_GU_SHARED, s);
-            rc = check_launch(h, launch_gemv_gateup_shared(h->L, W, x, n_tok, s), "gemv shared gate/up");
-            h->tend(tb, s);
-            if (rc) return rc;
-        }
-        tb = h->tbegin(TK_GU_ROUTED, s);
-        rc = check_launch(h, launch_gemv_gateup_routed(h->L, W, x, n_tok, s), "gemv routed gate/up");
-        h->tend(tb, s);
-        if (rc) return rc;
-        tb = h->tbegin(TK_DN_ROUTED, s);
-        rc = check_launch(h, launch_gemv_down_routed(h->L, W, n_tok, out, s), "gemv routed down");
-        h->tend(tb, s);
-        if (rc) return rc;
-        if (h->L.n_shared) {
-            tb = h->tbegin(TK_DN_SHARED, s);
-            rc = check_launch(h, launch_gemv_down_shared(h->L, W, n_tok, out, s), "gemv shared down");
-            h->tend(tb, s);
-        }
-        return rc;
-    }
-    // batched path: activation copies and chunk table, then the four grouped GEMMs
-    tb = h->tbegin(TK_GEMM_PREP, s);
-    rc = check_launch(h, launch_gemm_prep(h->L, W, x, n_tok, s), "gemm prep");
-    h->tend(tb, s);
-    if (rc) return rc;
-    tb = h->tbegin(TK_GEMM_GU_ROUTED, s);
-    rc = check_launch(h, launch_gemm_gateup_routed(h->L, W, n_tok, s), "gemm routed gate/up");
-    h->tend(tb, s);
-    if (rc) return rc;
-    if (h->L.n_shared) {
-        tb = h->tbegin(TK_GEMM_GU_SHARED, s);
-        rc = check_launch(h, launch_gemm_gateup_shared(h->L, W, x, n_tok, s), "gemm shared gate/up");
-        h->tend(tb, s);
-        if (rc) return rc;
-    }
-    tb = h->tbegin(TK_GEMM_DN_ROUTED, s);
-    rc = check_launch(h, launch_gemm_down_routed(h->L, W, n_tok, out, s), "gemm routed down");
-    h->tend(tb, s);
-    if (rc) return rc;
-    if (h->L.n_shared) {
-        tb = h->tbegin(TK_GEMM_DN_SHARED, s);
-        rc = check_launch(h, launch_gemm_down_shared(h->L, W, n_tok, out, s), "gemm shared down");
-        h->tend(tb, s);
-    }
-    return rc;
+    if ((rc = run_route(h, W, x, n_tok, s))) return rc;
+    return path == DS4MOE_PATH_GEMV ? run_gemv(h, W, x, n_tok, out, s) : run_gemm(h, W, x, n_tok, out, s);
 }
 
 int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *stream) {
@@ -624,6 +782,8 @@ int ds4moe_forward_static(ds4moe_t *h, const void *x, int32_t n_tok, float *out,
     if (rc) return rc;
     if (h->L.hash_table)
         return fail(DS4MOE_EUNSUPPORTED, "forward_static: a hash-routed layer takes token ids (ds4moe_forward_ids)");
+    if (h->cache.slots)
+        return fail(DS4MOE_EUNSUPPORTED, "forward_static: a layer with host-resident experts needs ds4moe_forward");
     if (n_tok > STATIC_MAX_TOK)
         return fail(DS4MOE_EINVAL, "forward_static: n_tok %d beyond the static scratch's %d tokens", n_tok,
                     STATIC_MAX_TOK);
@@ -679,9 +839,11 @@ int ds4moe_dequantize(ds4moe_t *h, int32_t expert, int32_t which, float *dst, vo
     if (which < 0 || which > 2) return fail(DS4MOE_EINVAL, "dequantize: which %d", which);
     if (!dst) return fail(DS4MOE_EINVAL, "dequantize: NULL dst");
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = h->L.fmt == 1 ? launch_dequant_q4k(h->L, which, expert, dst, s)
-                   : (which < 2)  ? launch_dequant_iq2(h->L, which, expert, dst, s)
-                                  : launch_dequant_q2k(h->L, expert, dst, s);
+    // with host-resident experts, decoded from the host store (every expert)
+    const Layer &L = h->cache.slots ? h->Lhost : h->L;
+    hipError_t e = L.fmt == 1 ? launch_dequant_q4k(L, which, expert, dst, s)
+                   : (which < 2) ? launch_dequant_iq2(L, which, expert, dst, s)
+                                 : launch_dequant_q2k(L, expert, dst, s);
     return check_launch(h, e, "dequantize");
 }
 
@@ -766,6 +928,33 @@ int ds4moe_set_wait_limit(ds4moe_t *h, int32_t max_polls, int32_t force_expire) 
     if (max_polls < 0) return fail(DS4MOE_EINVAL, "set_wait_limit: max_polls %d", max_polls);
     h->W.spin_limit = max_polls ? max_polls : DEFAULT_SPIN_LIMIT;
     h->W.want_xor = force_expire ? 0x80000000u : 0u;
+    return DS4MOE_OK;
+}
+
+int ds4moe_cache_stats(ds4moe_t *h, int64_t *stats, void *stream) {
+    if (!h || !stats) return fail(DS4MOE_EINVAL, "cache_stats: NULL argument");
+    if (!h->cache.slots) return fail(DS4MOE_EUNSUPPORTED, "cache_stats: the layer's experts are all resident in HBM");
+    hipStream_t s = (hipStream_t)stream;
+    unsigned long long v[4];
+    if (hipMemcpyAsync(v, h->cache.stats, sizeof v, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess) {
+        hipGetLastError();
+        return fail(DS4MOE_EHIP, "cache_stats: copy");
+    }
+    for (int i = 0; i < 4; ++i) stats[i] = (int64_t)v[i];
+    return DS4MOE_OK;
+}
+
+int ds4moe_cache_slots(ds4moe_t *h, int32_t *slot_expert, void *stream) {
+    if (!h || !slot_expert) return fail(DS4MOE_EINVAL, "cache_slots: NULL argument");
+    if (!h->cache.slots) return fail(DS4MOE_EUNSUPPORTED, "cache_slots: the layer's experts are all resident in HBM");
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(slot_expert, h->cache.slot_expert, (size_t)h->cache.slots * 4, hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess) {
+        hipGetLastError();
+        return fail(DS4MOE_EHIP, "cache_slots: copy");
+    }
     return DS4MOE_OK;
 }
 

@@ -351,7 +351,7 @@ __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_gateup_routed(Layer L, W
     }
     const int f0 = tx * RGU_ROWS + wave * 16 * GU_FR;
     // fragment fi: matrix fi / GU_FR (gate, up), rows f0 + 16 (fi % GU_FR) + rl
-    const int64_t rb = ((int64_t)e * F + f0 + rl) * nbe;
+    const int64_t rb = ((int64_t)expert_slot(L, e) * F + f0 + rl) * nbe;
     const uint8_t *qg = L.iq2_qs[0] + (rb + b0) * 64 + 16 * grp;  // + 64 bi (up: + iq2_qs[1] - iq2_qs[0])
     const uint16_t *dg = L.iq2_d[0] + rb + b0;                    // + bi
     const int fq = 16 * nbe * 64, fd = 16 * nbe;
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_down_routed(Layer L, Wor
     const int r0 = tx * RDN_ROWS + wave * 16 * DN_NF;
     const bool active = r0 < E;
     // fragment fi = rows r0 + 16 fi + rl; one base per plane, fragments 16 rows apart
-    const int64_t rb = ((int64_t)e * E + (active ? r0 + rl : 0)) * nbf;
+    const int64_t rb = ((int64_t)expert_slot(L, e) * E + (active ? r0 + rl : 0)) * nbf;
     const uint8_t *qb = L.q2k_qs + (rb + b0) * 64 + 16 * grp;   // + fi * fq + 64 bi
     const uint8_t *sb = L.q2k_sc + (rb + b0) * 16 + 4 * grp;    // + fi * fs + 16 bi
     const uint32_t *db = L.q2k_dd + rb + b0;                    // + fi * fd + bi

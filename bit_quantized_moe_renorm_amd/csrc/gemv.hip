@@ -109,6 +109,7 @@ __global__ __launch_bounds__(512) void k_gemv_gateup_routed(Layer L, Work W, con
     const int u = blockIdx.y;
     if (u >= U) return;
     const int e = W.active[1 + u];
+    const int es = expert_slot(L, e);  // the slot holding its weights
     const int beg = W.offsets[e];
     const int m = W.offsets[e + 1] - beg;
     const int E = L.n_embd, F = L.n_ff, k = L.top_k;
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(512) void k_gemv_gateup_routed(Layer L, Work W, con
     for (int r = 0; r < GU_NR; ++r) {
         const int f = f0 + r * rpw;
         if (f < F) {
-            const int64_t rb = ((int64_t)e * F + f) * L.nbe;
+            const int64_t rb = ((int64_t)es * F + f) * L.nbe;
             qg[r] = ld_nt16(L.iq2_qs[0] + rb * 64 + c * 16);
             qu[r] = ld_nt16(L.iq2_qs[1] + rb * 64 + c * 16);
             dg[r] = half_to_f32(ld_nt2(L.iq2_d[0] + rb + (c >> 2)));
@@ -270,6 +271,7 @@ __global__ __launch_bounds__(256) void k_gemv_down_routed(Layer L, Work W, float
     const int u = blockIdx.y;
     if (u >= U) return;
     const int e = W.active[1 + u];
+    const int es = expert_slot(L, e);  // the slot holding its weights
     const int beg = W.offsets[e];
     const int m = W.offsets[e + 1] - beg;
     const int E = L.n_embd, F = L.n_ff, k = L.top_k;
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(256) void k_gemv_down_routed(Layer L, Work W, float
     for (int r = 0; r < DN_NR; ++r) {
         const int row = r0 + r * rpw;
         if (row < E) {
-            const int64_t rb = ((int64_t)e * E + row) * L.nbf;
+            const int64_t rb = ((int64_t)es * E + row) * L.nbf;
             qs[r] = ld_nt16(L.q2k_qs + rb * 64 + c * 16);
             sc[r] = ld_nt4(L.q2k_sc + rb * 16 + c * 4);
             dd[r] = ld_nt4(L.q2k_dd + rb + (c >> 2));

@@ -111,6 +111,7 @@ __global__ __launch_bounds__(64 * Q4_WAVES) void k_q4_gateup_routed(Layer L, Wor
     const int u = blockIdx.y;
     if (u >= W.active[0]) return;
     const int e = W.active[1 + u];
+    const int es = expert_slot(L, e);  // the slot holding its weights
     const int beg = W.offsets[e], m = W.offsets[e + 1] - beg;
     const int E = L.n_embd, F = L.n_ff, k = L.top_k, nbe = L.nbe;
     const int lpr = E >> 6, rpw = 64 / lpr;
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(64 * Q4_WAVES) void k_q4_gateup_routed(Layer L, Wor
     for (int r = 0; r < Q4_GU_NR; ++r) {
         // rows past n_ff read row n_ff - 1 (dropped below)
         const int f = min(f0 + r * rpw, F - 1);
-        const int64_t blk = ((int64_t)e * F + f) * nbe + (c >> 2);
+        const int64_t blk = ((int64_t)es * F + f) * nbe + (c >> 2);
         const uint8_t *pg = L.q4_qs[0] + blk * 128 + 32 * (c & 3), *pu = L.q4_qs[1] + blk * 128 + 32 * (c & 3);
         qg[r][0] = ld_nt16(pg), qg[r][1] = ld_nt16(pg + 16);
         qu[r][0] = ld_nt16(pu), qu[r][1] = ld_nt16(pu + 16);
@@ -152,6 +153,7 @@ __global__ __launch_bounds__(64 * Q4_WAVES) void k_q4_down_routed(Layer L, Work 
     const int u = blockIdx.y;
     if (u >= W.active[0]) return;
     const int e = W.active[1 + u];
+    const int es = expert_slot(L, e);  // the slot holding its weights
     const int beg = W.offsets[e], m = W.offsets[e + 1] - beg;
     const int E = L.n_embd, F = L.n_ff, k = L.top_k, nbf = L.nbf;
     const int lpr = F >> 6, rpw = 64 / lpr;
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(64 * Q4_WAVES) void k_q4_down_routed(Layer L, Work 
 #pragma unroll
     for (int r = 0; r < Q4_DN_NR; ++r) {
         const int row = min(r0 + r * rpw, E - 1);
-        const int64_t blk = ((int64_t)e * E + row) * nbf + (c >> 2);
+        const int64_t blk = ((int64_t)es * E + row) * nbf + (c >> 2);
         const uint8_t *p = L.q4_qs[2] + blk * 128 + 32 * (c & 3);
         qd[r][0] = ld_nt16(p), qd[r][1] = ld_nt16(p + 16);
         md[r] = ld_nt16(L.q4_meta[2] + blk);

@@ -130,6 +130,24 @@ typedef struct ds4moe ds4moe_t; /* opaque; one per MoE layer */
  *                experts in 0..n_expert-1 (checked at create: EINVAL); 1 <=
  *                n_vocab <= INT32_MAX / top_k; 4-byte aligned.  The table is
  *                copied.  Such a layer is called through the *_ids entry points.
+ *   expert_cache_slots: 0 keeps every routed expert in HBM.  S in top_k..n_expert
+ *                keeps the routed experts in pinned host memory (copied there at
+ *                create, in the library's layout) and S of them in HBM: the
+ *                model's way to run when it does not fit in GPU memory, with the
+ *                non-routed weights resident and a routed expert loaded on a
+ *                miss ("DS-4 DwarfStar - DeepSeek V4 Flash 本地推理引擎", section
+ *                "SSD Streaming", how it works; "ds4 深度实战...", section 3.5).
+ *                Each call routes, then one workgroup updates the cache (the
+ *                call's resident experts are stamped, each missing expert takes
+ *                a slot the call does not use: empty ones first, then the least
+ *                recently used, lower slot first on equal stamps) and a copy
+ *                kernel pulls the missed experts over the host link into their
+ *                slots, all on the call's stream with no host synchronisation;
+ *                the expert kernels then read each expert at its slot.  A call
+ *                is run in sub-calls of at most S / top_k tokens (unless S ==
+ *                n_expert), so that its distinct experts fit; one token runs on
+ *                the GEMV kernels instead of the fused decode kernel.  The
+ *                results equal those of a layer with every expert in HBM.
  */
 typedef struct {
     int32_t abi_version; /* DS4MOE_ABI_VERSION */
@@ -146,6 +164,7 @@ typedef struct {
     int32_t expert_format; /* DS4MOE_FMT_Q2 or DS4MOE_FMT_Q4 */
     const int32_t *hash_table; /* device int32 [n_vocab][top_k], or NULL (learned routing) */
     int64_t n_vocab;           /* rows of hash_table (ignored when it is NULL) */
+    int32_t expert_cache_slots; /* 0: every routed expert in HBM; else host-resident experts, this many in HBM */
 } ds4moe_desc;
 
 /*
@@ -292,6 +311,17 @@ int ds4moe_forward_stack_ids(ds4moe_t *const *layers, int32_t n_layers, float *h
                              int32_t n_tok, double eps, uint16_t *x_bf16, void *stream);
 
 /*
+ * The HBM expert cache of a layer created with expert_cache_slots > 0
+ * (DS4MOE_EUNSUPPORTED otherwise).  ds4moe_cache_stats writes, to host
+ * stats[4]: calls (sub-calls) so far, expert hits, expert misses, and bytes
+ * copied from host memory.  ds4moe_cache_slots writes, to host
+ * slot_expert[expert_cache_slots], the expert each slot holds (-1: empty).
+ * Both enqueue a copy on `stream` and synchronise it.
+ */
+int ds4moe_cache_stats(ds4moe_t *h, int64_t *stats, void *stream);
+int ds4moe_cache_slots(ds4moe_t *h, int32_t *slot_expert, void *stream);
+
+/*
  * Per-kernel timing for benchmarks.  When enabled, ds4moe_forward records HIP
  * events around each kernel it launches on the caller's stream; read back the
  * accumulated milliseconds and launch counts (after synchronising the stream)
@@ -300,10 +330,10 @@ int ds4moe_forward_stack_ids(ds4moe_t *const *layers, int32_t n_layers, float *h
  * 5 routed gate/up GEMM, 6 routed down GEMM, 7 fused decode kernel, 8 batched
  * path preparation (activation copies, chunk table), 9 shared gate/up GEMM,
  * 10 shared down GEMM, 11 routed gate/up Q4_K GEMV, 12 routed down Q4_K
- * GEMV.  ms and counts have room for DS4MOE_TIMING_KINDS entries each.
+ * GEMV, 13 expert cache update and copy.  ms and counts have room for DS4MOE_TIMING_KINDS entries each.
  * Enabling resets the counters.
  */
-#define DS4MOE_TIMING_KINDS 13
+#define DS4MOE_TIMING_KINDS 14
 int ds4moe_timing_enable(ds4moe_t *h, int32_t enable);
 int ds4moe_timing_read(ds4moe_t *h, double *ms, int64_t *counts);
 

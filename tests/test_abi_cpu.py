@@ -43,21 +43,21 @@ def test_validation_without_gpu(lib):
     # NULL description
     assert lib.ds4moe_create(None, None, ctypes.byref(h)) == m.EINVAL
     # bad sizes: n_embd not a supported power of two
-    d = m.Desc(m.ABI_VERSION, 300, 256, 8, 2, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 0, None, 0)
+    d = m.Desc(m.ABI_VERSION, 300, 256, 8, 2, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 0, None, 0, 0)
     assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
     assert b"n_embd" in lib.ds4moe_last_error()
     # top_k > n_expert
-    d = m.Desc(m.ABI_VERSION, 256, 256, 4, 6, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 0, None, 0)
+    d = m.Desc(m.ABI_VERSION, 256, 256, 4, 6, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 0, None, 0, 0)
     assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
     # wrong ABI version
-    d = m.Desc(99, 256, 256, 8, 2, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 0, None, 0)
+    d = m.Desc(99, 256, 256, 8, 2, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 0, None, 0, 0)
     assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
     # unknown expert format
-    d = m.Desc(m.ABI_VERSION, 256, 256, 8, 2, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 7, None, 0)
+    d = m.Desc(m.ABI_VERSION, 256, 256, 8, 2, 0, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 7, None, 0, 0)
     assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
     assert b"expert_format" in lib.ds4moe_last_error()
     # shared expert requested but missing
-    d = m.Desc(m.ABI_VERSION, 256, 256, 8, 2, 1, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 0, None, 0)
+    d = m.Desc(m.ABI_VERSION, 256, 256, 8, 2, 1, 4, m.BF16, 1, None, 1, 1, 1, 1, None, None, None, 0, None, 0, 0)
     assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
     # NULL handle on every per-handle entry point
     assert lib.ds4moe_forward(None, None, 1, None, None) == m.EINVAL
@@ -92,7 +92,7 @@ def test_validation_without_gpu(lib):
     assert lib.ds4moe_forward_stack_ids(one_null, 1, 256, 256, 1, 1e-6, 256, None) == m.EINVAL
     assert b"layer 0" in lib.ds4moe_last_error()
     # a hash table needs 1 <= n_vocab <= INT32_MAX / top_k and 4-byte alignment
-    d = m.Desc(m.ABI_VERSION, 256, 256, 8, 2, 0, 4, m.BF16, 256, None, 256, 256, 256, 256, None, None, None, 0, 256, 0)
+    d = m.Desc(m.ABI_VERSION, 256, 256, 8, 2, 0, 4, m.BF16, 256, None, 256, 256, 256, 256, None, None, None, 0, 256, 0, 0)
     assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
     assert b"n_vocab" in lib.ds4moe_last_error()
     d.n_vocab = 2 ** 31
@@ -100,6 +100,15 @@ def test_validation_without_gpu(lib):
     d.n_vocab, d.hash_table = 1000, 258
     assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
     assert b"hash_table" in lib.ds4moe_last_error()
+    # expert cache slots: 0, or top_k..n_expert
+    d.hash_table, d.n_vocab = None, 0
+    for slots in (-1, 1, 9):
+        d.expert_cache_slots = slots
+        assert lib.ds4moe_create(ctypes.byref(d), None, ctypes.byref(h)) == m.EINVAL
+        assert b"expert_cache_slots" in lib.ds4moe_last_error()
+    v = (ctypes.c_int64 * 4)()
+    assert lib.ds4moe_cache_stats(None, v, None) == m.EINVAL
+    assert lib.ds4moe_cache_slots(None, None, None) == m.EINVAL
 
 
 def test_binding_has_no_fallback(tmp_path):
