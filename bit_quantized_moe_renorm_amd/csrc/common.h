@@ -214,8 +214,10 @@ hipError_t launch_gemm_down_routed(const Layer &L, const Work &W, int n_tok, flo
 hipError_t launch_gemm_down_shared(const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
 
 int decode_grid(int act_bf16);
+// pre_routed: the routing of the token is already in W (the router kernel ran
+// earlier on the stream), so the kernel skips its router phase.
 hipError_t launch_decode_fused(const Layer &L, const Work &W, const void *x, float *out, int grid,
-                               unsigned long long ep, hipStream_t s);
+                               unsigned long long ep, hipStream_t s, bool pre_routed = false);
 
 hipError_t launch_rmsnorm(const float *h, int n_tok, int n_embd, double eps, uint16_t *x, hipStream_t s);
 

@@ -101,6 +101,7 @@ struct DecPlan {
     unsigned long long ep;  // calls already made on this workspace
     int n_route, n_shgu, n_rgu, n_shdn, n_rdn;   // n_route: 2 items per expert scored
     int rgu_per_slot, rdn_per_slot;
+    int pre_routed;         // the routing is in W (idx, w, lists) from the router kernel: no router phase
     int shdn_cpr;
     int total;
 };
@@ -140,6 +141,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 struct RouteCache {
     int idx[MAX_TOPK];
     float w[MAX_TOPK];
+    int slot[MAX_TOPK];  // where each selected expert's weights are (expert_slot)
 };
 
 // The weights and the export of a routing whose lane j < k holds slot j's
@@ -159,6 +161,7 @@ __device__ __forceinline__ void dec_route_finish(const Layer &L, const Work &W, 
     if (lane < k) {
         rc->idx[lane] = myE;
         rc->w[lane] = wj;
+        rc->slot[lane] = expert_slot(L, myE);
     }
     if (!write_global) return;
     if (lane < k) {
@@ -558,7 +561,7 @@ __device__ __forceinline__ void dec_rgu_load(const Layer &L, const DecPlan &P, c
     const int c = lane & (lpr - 1);
     const int j = item / P.rgu_per_slot, tile = item - j * P.rgu_per_slot;
     const int f0 = (tile * DEC_WAVES + wave) * (DEC_GU_NR * rpw) + lane / lpr;
-    const int e = rc->idx[j];
+    const int e = rc->slot[j];
 #pragma unroll
     for (int r = 0; r < DEC_GU_NR; ++r) {
         // rows past n_ff (if any) read row n_ff - 1; the computation drops them
@@ -769,7 +772,7 @@ __device__ __forceinline__ void dec_rdn_load(const Layer &L, const DecPlan &P, c
     const int c = lane & (lpr - 1);
     const int j = item / P.rdn_per_slot, tile = item - j * P.rdn_per_slot;
     const int r0 = (tile * DEC_WAVES + wave) * (DEC_DN_NR * rpw) + lane / lpr;
-    const int e = rc->idx[j];
+    const int e = rc->slot[j];
 #pragma unroll
     for (int r = 0; r < DEC_DN_NR; ++r) {
         // rows past n_embd (if any) read row n_embd - 1; the computation drops them
@@ -1000,10 +1003,21 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
     ShguW<XBF16> sg;
     const bool wave0 = threadIdx.x < 64;
     if (!wave0 && it < b1) dec_shgu_load<XBF16>(L, x, it - b0, sg);
-    if (hashed)
+    if (P.pre_routed) {
+        // routed by the router kernel earlier on the stream (host-resident
+        // experts: the cache step ran in between and placed them)
+        if (threadIdx.x < L.top_k) {
+            const int ex = W.idx[threadIdx.x];
+            rc.idx[threadIdx.x] = ex;
+            rc.w[threadIdx.x] = W.w[threadIdx.x];
+            rc.slot[threadIdx.x] = expert_slot(L, ex);
+        }
+        if (threadIdx.x == 0) lds_flag = 1;
+    } else if (hashed) {
         dec_route_poll_hashed(L, W, tag, trow, bad_id, &rc, &lds_flag);
-    else
+    } else {
         dec_route_poll(L, W, tag, &rc, &lds_flag);
+    }
     if (wave0 && it < b1) dec_shgu_load<XBF16>(L, x, it - b0, sg);
     __syncthreads();
     bool ok = lds_flag != 0;
@@ -1098,6 +1112,7 @@ static DecPlan make_plan(const Layer &L) {
     const int E = L.n_embd, F = L.n_ff, k = L.top_k;
     // half an expert row per item: every expert, or the k of a hash layer's table row
     P.n_route = 2 * (L.hash_table ? L.top_k : L.n_expert);
+    P.pre_routed = 0;
     P.n_shgu = L.n_shared ? (F + DEC_WAVES - 1) / DEC_WAVES : 0;
     const int rows_gu_item = DEC_WAVES * DEC_GU_NR * (64 / (E >> 6));
     P.rgu_per_slot = (F + rows_gu_item - 1) / rows_gu_item;
@@ -1129,9 +1144,14 @@ int decode_grid(int act_bf16) {
 }
 
 hipError_t launch_decode_fused(const Layer &L, const Work &W, const void *x, float *out, int grid,
-                               unsigned long long ep, hipStream_t s) {
+                               unsigned long long ep, hipStream_t s, bool pre_routed) {
     DecPlan P = make_plan(L);
     P.ep = ep;
+    if (pre_routed) {
+        P.pre_routed = 1;
+        P.total -= P.n_route;
+        P.n_route = 0;
+    }
     Layer Lc = L;
     Work Wc = W;
     const void *xc = x;

@@ -702,8 +702,19 @@ static int forward_cached(ds4moe *h, const void *x, const int32_t *ids, int n_to
         int rc = run_route(h, W, xc, n, s);
         if (!rc) rc = run_cache(h, W, s);
         if (rc) return rc;
+        if (n == 1 && L.fmt == 0 && h->path == DS4MOE_PATH_AUTO) {
+            // one token: the fused decode kernel, taking the routing from the
+            // router kernel (its own router phase would come after the cache step)
+            int tf = h->tbegin(TK_FUSED, s);
+            rc = check_launch(h, launch_decode_fused(L, W, xc, oc, h->decode_grid, h->decode_calls, s, true),
+                              "fused decode");
+            h->decode_calls += 1;
+            h->tend(tf, s);
+            if (rc) return rc;
+            continue;
+        }
         bool gemv = n <= GEMV_MAX_TOK && (L.fmt == 1 || h->path == DS4MOE_PATH_GEMV ||
-                                          (h->path == DS4MOE_PATH_AUTO && (n == 1 || L.act_dtype == DS4MOE_F32)));
+                                          (h->path == DS4MOE_PATH_AUTO && L.act_dtype == DS4MOE_F32));
         rc = L.fmt == 1 ? run_q4_experts(h, W, xc, n, oc, s, true)
              : gemv     ? run_gemv(h, W, xc, n, oc, s)
                         : run_gemm(h, W, xc, n, oc, s);
