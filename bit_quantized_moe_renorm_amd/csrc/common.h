@@ -130,6 +130,15 @@ __device__ __forceinline__ void report_bad_id(const Work &W, uint32_t tag) {
 }
 
 // ---------------------------------------------------------------- small device helpers
+// Packed weights held across a loop over tokens: an empty asm that claims to
+// change them keeps the compiler from hoisting their unpacking out of the
+// loop (it would unpack every weight of the lane into registers, spill into
+// AGPRs and wait for the loads before the first token).
+__device__ __forceinline__ void keep_packed(uint4 &q) {
+    asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
+}
+__device__ __forceinline__ void keep_packed(uint32_t &q) { asm volatile("" : "+v"(q)); }
+
 // Weights are read once per call: non-temporal loads (streaming cache
 // policy).  A plain streaming read with 512 workgroups of 256 threads and four
 // 16-byte loads in flight per thread measured 7.2 TB/s with them on MI355X,

@@ -299,6 +299,8 @@ __global__ __launch_bounds__(256) void k_gemv_down_routed(Layer L, Work W, float
         const int q = W.list[beg + i];
         const int t = q / k;
         const float wgt = W.w[q];
+#pragma unroll
+        for (int r = 0; r < DN_NR; ++r) keep_packed(qs[r]), keep_packed(sc[r]), keep_packed(dd[r]);
         float hv[64], hs[4];
         const float4 *hp = reinterpret_cast<const float4 *>(W.hbuf + (int64_t)q * F + 64 * c);
 #pragma unroll

@@ -13,8 +13,8 @@
 // same bytes, each plane aligned for 128-bit loads.
 //
 // Decode (few tokens): dequant-fused GEMVs.  A lane covers 64 weights of a row
-// (a quarter block: two sub-blocks, 32 qs bytes); per sub-block it forms
-// sum q x in fp32 (the quants convert exactly) and applies
+// (a quarter block: two sub-blocks, 32 qs bytes), one sub-block at a time; per
+// sub-block it forms sum q x in fp32 (the quants convert exactly) and applies
 // d sc * sum q x - dmin m * sum x, the min term through the per-sub-block sums
 // of the input vector.  Weights are loaded once per expert and reused for all
 // of that expert's tokens, which are taken one at a time.
@@ -34,42 +34,49 @@ __device__ __forceinline__ uint32_t q4k_field(const uint4 &meta, int j) {
     return (uint32_t)(pair >> sh) & 63u;
 }
 
-// One lane's quarter block against 64 input values v (fp32) whose two
-// 32-value sums are vs[0], vs[1]: lane quarter qq = c & 3 covers sub-blocks
-// 2 qq and 2 qq + 1; qs = its 32 quant bytes.
-__device__ __forceinline__ float q4k_quarter_dot(const uint4 &meta, const uint4 &qa, const uint4 &qb, int qq,
-                                                 const float *v, const float *vs) {
-    const uint32_t Q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-    float r = 0.0f, mn = 0.0f;
+// One sub-block (32 weights) of a lane's quarter block: sum q x over its 16
+// quant bytes qw (weight 2 b + 8 wd in the low nibble of byte b of word wd,
+// its neighbour in the high nibble) and 32 input values v.
+__device__ __forceinline__ float q4k_sub_dot(const uint4 &qw, const float *v) {
+    const uint32_t Q[4] = {qw.x, qw.y, qw.z, qw.w};
+    float dot = 0.0f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        float dot = 0.0f;
+    for (int wd = 0; wd < 4; ++wd) {
+        const uint32_t lo = Q[wd] & 0x0F0F0F0Fu, hi = (Q[wd] >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-            const uint32_t w = Q[4 * h + wd];
-            const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int i = 32 * h + 8 * wd + 2 * b;  // weight index within the lane's 64
-                dot = fmaf((float)((lo >> (8 * b)) & 0xFFu), v[i], dot);
-                dot = fmaf((float)((hi >> (8 * b)) & 0xFFu), v[i + 1], dot);
-            }
+        for (int b = 0; b < 4; ++b) {
+            dot = fmaf((float)((lo >> (8 * b)) & 0xFFu), v[8 * wd + 2 * b], dot);
+            dot = fmaf((float)((hi >> (8 * b)) & 0xFFu), v[8 * wd + 2 * b + 1], dot);
         }
-        const int s = 2 * qq + h;
-        r = fmaf((float)q4k_field(meta, s), dot, r);
-        mn = fmaf((float)q4k_field(meta, 8 + s), vs[h], mn);
     }
-    const float d = half_to_f32((uint16_t)(meta.x & 0xFFFFu)), dmin = half_to_f32((uint16_t)(meta.x >> 16));
-    return d * r - dmin * mn;
+    return dot;
 }
 
-// 64 input values of a lane (fp32 or bf16 source) and their two 32-value sums.
+// A lane's quarter block (sub-blocks 2 qq and 2 qq + 1) is taken one
+// sub-block at a time, so a lane holds 32 input values, not 64: per row, r
+// accumulates sc * dot and mn accumulates m * (sum of the 32 inputs), and the
+// row's value is d r - dmin mn.
+struct Q4Acc {
+    float r, mn;
+};
+__device__ __forceinline__ void q4k_sub_acc(Q4Acc &a, const uint4 &meta, const uint4 &qw, int s, const float *v,
+                                            float vs) {
+    const float dot = q4k_sub_dot(qw, v);
+    a.r = fmaf((float)q4k_field(meta, s), dot, a.r);
+    a.mn = fmaf((float)q4k_field(meta, 8 + s), vs, a.mn);
+}
+__device__ __forceinline__ float q4k_acc_value(const Q4Acc &a, const uint4 &meta) {
+    const float d = half_to_f32((uint16_t)(meta.x & 0xFFFFu)), dmin = half_to_f32((uint16_t)(meta.x >> 16));
+    return d * a.r - dmin * a.mn;
+}
+
+// 32 input values of a lane (fp32 or bf16 source) and their sum, in order.
 template <bool XBF16>
-__device__ __forceinline__ void q4_load_vec(const void *src, int64_t off, float *v, float *vs) {
+__device__ __forceinline__ void q4_load_half(const void *src, int64_t off, float *v, float &vs) {
     if (XBF16) {
         const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(src) + off);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const uint4 r = p[i];
             const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
@@ -81,18 +88,15 @@ __device__ __forceinline__ void q4_load_vec(const void *src, int64_t off, float 
     } else {
         const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(src) + off);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 8; ++i) {
             const float4 r = p[i];
             v[4 * i] = r.x, v[4 * i + 1] = r.y, v[4 * i + 2] = r.z, v[4 * i + 3] = r.w;
         }
     }
+    float a = 0.0f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        float a = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) a += v[32 * h + i];
-        vs[h] = a;
-    }
+    for (int i = 0; i < 32; ++i) a += v[i];
+    vs = a;
 }
 
 __device__ __forceinline__ float q4_group_sum(float v, int lpr) {
@@ -133,15 +137,28 @@ __global__ __launch_bounds__(64 * Q4_WAVES) void k_q4_gateup_routed(Layer L, Wor
     }
     for (int i = 0; i < m; ++i) {
         const int q = W.list[beg + i];
-        float v[64], vs[2];
-        q4_load_vec<XBF16>(x, (int64_t)(q / k) * E + 64 * c, v, vs);
+#pragma unroll
+        for (int r = 0; r < Q4_GU_NR; ++r)
+            keep_packed(qg[r][0]), keep_packed(qg[r][1]), keep_packed(qu[r][0]), keep_packed(qu[r][1]),
+                keep_packed(mg[r]), keep_packed(mu[r]);
+        Q4Acc ag[Q4_GU_NR], au[Q4_GU_NR];
+#pragma unroll
+        for (int r = 0; r < Q4_GU_NR; ++r) ag[r] = au[r] = Q4Acc{0.0f, 0.0f};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            float v[32], vs;
+            q4_load_half<XBF16>(x, (int64_t)(q / k) * E + 64 * c + 32 * hh, v, vs);
+#pragma unroll
+            for (int r = 0; r < Q4_GU_NR; ++r) {
+                q4k_sub_acc(ag[r], mg[r], qg[r][hh], 2 * (c & 3) + hh, v, vs);
+                q4k_sub_acc(au[r], mu[r], qu[r][hh], 2 * (c & 3) + hh, v, vs);
+            }
+        }
 #pragma unroll
         for (int r = 0; r < Q4_GU_NR; ++r) {
             const int f = f0 + r * rpw;
-            float g = q4k_quarter_dot(mg[r], qg[r][0], qg[r][1], c & 3, v, vs);
-            float uu = q4k_quarter_dot(mu[r], qu[r][0], qu[r][1], c & 3, v, vs);
-            g = q4_group_sum(g, lpr);
-            uu = q4_group_sum(uu, lpr);
+            const float g = q4_group_sum(q4k_acc_value(ag[r], mg[r]), lpr);
+            const float uu = q4_group_sum(q4k_acc_value(au[r], mu[r]), lpr);
             if (c == 0 && f < F) W.hbuf[(int64_t)q * F + f] = q4_silu(g) * uu;
         }
     }
@@ -173,13 +190,22 @@ __global__ __launch_bounds__(64 * Q4_WAVES) void k_q4_down_routed(Layer L, Work 
     for (int i = 0; i < m; ++i) {
         const int q = W.list[beg + i];
         const float wgt = W.w[q];
-        float v[64], vs[2];
-        q4_load_vec<false>(W.hbuf, (int64_t)q * F + 64 * c, v, vs);
+#pragma unroll
+        for (int r = 0; r < Q4_DN_NR; ++r) keep_packed(qd[r][0]), keep_packed(qd[r][1]), keep_packed(md[r]);
+        Q4Acc ad[Q4_DN_NR];
+#pragma unroll
+        for (int r = 0; r < Q4_DN_NR; ++r) ad[r] = Q4Acc{0.0f, 0.0f};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            float v[32], vs;
+            q4_load_half<false>(W.hbuf, (int64_t)q * F + 64 * c + 32 * hh, v, vs);
+#pragma unroll
+            for (int r = 0; r < Q4_DN_NR; ++r) q4k_sub_acc(ad[r], md[r], qd[r][hh], 2 * (c & 3) + hh, v, vs);
+        }
 #pragma unroll
         for (int r = 0; r < Q4_DN_NR; ++r) {
             const int row = r0 + r * rpw;
-            float y = q4k_quarter_dot(md[r], qd[r][0], qd[r][1], c & 3, v, vs);
-            y = q4_group_sum(y, lpr);
+            const float y = q4_group_sum(q4k_acc_value(ad[r], md[r]), lpr);
             if (c == 0 && row < E) atomicAdd(out + (int64_t)(q / k) * E + row, wgt * y);
         }
     }
