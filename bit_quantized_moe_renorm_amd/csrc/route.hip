@@ -843,11 +843,18 @@ hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok,
     }
     const int fuse = n_tok <= ROUTE_SMALL_MAX;
     // 8-token tiles for calls of up to 8 tokens (a 16-token tile would load and
-    // multiply clamped copies of the last token)
+    // multiply clamped copies of the last token), a 1-token tile for one token
     const bool small = n_tok <= 8;
-    const int tt = small ? 8 : RT_TOK;
+    const int tt = n_tok == 1 ? 1 : small ? 8 : RT_TOK;
     const dim3 grid(NE, (n_tok + tt - 1) / tt);
-    if (L.act_dtype == 1) {
+    if (n_tok == 1) {
+        if (L.act_dtype == 1)
+            hipLaunchKernelGGL((k_route_logits<true, 1>), grid, dim3(256), 0, s, L.router, L.router_bias, x, n_tok,
+                               NE, L.n_embd, L.top_k, W, fuse, tag);
+        else
+            hipLaunchKernelGGL((k_route_logits<false, 1>), grid, dim3(256), 0, s, L.router, L.router_bias, x, n_tok,
+                               NE, L.n_embd, L.top_k, W, fuse, tag);
+    } else if (L.act_dtype == 1) {
         if (small)
             hipLaunchKernelGGL((k_route_logits<true, 8>), grid, dim3(256), 0, s, L.router, L.router_bias, x, n_tok,
                                NE, L.n_embd, L.top_k, W, fuse, tag);
