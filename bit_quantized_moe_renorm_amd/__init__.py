@@ -29,7 +29,7 @@ SYMBOLS = ("ds4moe_create", "ds4moe_route", "ds4moe_forward", "ds4moe_set_path",
            "ds4moe_rmsnorm", "ds4moe_forward_stack", "ds4moe_timing_enable", "ds4moe_timing_read",
            "ds4moe_last_routing", "ds4moe_status", "ds4moe_set_wait_limit", "ds4moe_forward_static",
            "ds4moe_route_ids", "ds4moe_forward_ids", "ds4moe_forward_stack_ids", "ds4moe_cache_stats",
-           "ds4moe_cache_slots",
+           "ds4moe_cache_slots", "ds4moe_debug_gemm_b",
            "ds4moe_destroy", "ds4moe_last_error")
 
 
@@ -82,6 +82,7 @@ def load_library(path: Optional[Path] = None) -> ctypes.CDLL:
     L.ds4moe_route_ids.argtypes = [P, P, P, i32, P, P, P, P, P]
     L.ds4moe_forward_ids.argtypes = [P, P, P, i32, P, P]
     L.ds4moe_forward_stack_ids.argtypes = [P, i32, P, P, i32, ctypes.c_double, P, P]
+    L.ds4moe_debug_gemm_b.argtypes = [P, i32, i32, P, P]
     L.ds4moe_cache_stats.argtypes = [P, ctypes.POINTER(ctypes.c_int64), P]
     L.ds4moe_cache_slots.argtypes = [P, ctypes.POINTER(ctypes.c_int32), P]
     L.ds4moe_destroy.argtypes = [P]
@@ -275,6 +276,15 @@ class MoELayer:
         v = (ctypes.c_int32 * self.cache_slots)()
         _check(load_library().ds4moe_cache_slots(self.h, v, _stream(stream)))
         return list(v)
+
+    def debug_gemm_b(self, expert: int, which: int, stream=None):
+        """The matrix as the grouped GEMMs feed it to the MFMAs (fp16 values as fp32)."""
+        import torch
+        s = self.spec
+        shape = (s.n_ff, s.n_embd) if which < 2 else (s.n_embd, s.n_ff)
+        dst = torch.empty(shape, dtype=torch.float32, device="cuda")
+        _check(load_library().ds4moe_debug_gemm_b(self.h, expert, which, _ptr(dst), _stream(stream)))
+        return dst
 
     def timing_enable(self, on: bool = True):
         _check(load_library().ds4moe_timing_enable(self.h, 1 if on else 0))

@@ -194,6 +194,7 @@ hipError_t launch_router_prep(const float *router, int NE, int E, uint16_t *hml,
 // hand-off tag is ep + 1, never 0)
 hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s,
                         unsigned long long ep);
+hipError_t launch_debug_gemm_b(const Layer &L, int which, int expert, float *dst, hipStream_t s);
 hipError_t launch_cache_update(const Layer &L, const Work &W, const ExpertCache &C, int64_t expert_bytes,
                                hipStream_t s);
 hipError_t launch_cache_fill(const ExpertPlanes &P, const ExpertCache &C, hipStream_t s);

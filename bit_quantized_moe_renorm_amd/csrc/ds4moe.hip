@@ -858,6 +858,17 @@ int ds4moe_dequantize(ds4moe_t *h, int32_t expert, int32_t which, float *dst, vo
     return check_launch(h, e, "dequantize");
 }
 
+int ds4moe_debug_gemm_b(ds4moe_t *h, int32_t expert, int32_t which, float *dst, void *stream) {
+    if (!h) return fail(DS4MOE_EINVAL, "debug_gemm_b: NULL handle");
+    if (h->poisoned) return fail(DS4MOE_EPOISONED, "debug_gemm_b: handle poisoned");
+    if (h->L.fmt == 1) return fail(DS4MOE_EUNSUPPORTED, "debug_gemm_b: a q4 layer has no grouped GEMM path");
+    if (expert < 0 || expert >= h->L.n_expert) return fail(DS4MOE_EINVAL, "debug_gemm_b: expert %d", expert);
+    if (which < 0 || which > 2) return fail(DS4MOE_EINVAL, "debug_gemm_b: which %d", which);
+    if (!dst) return fail(DS4MOE_EINVAL, "debug_gemm_b: NULL dst");
+    const Layer &L = h->cache.slots ? h->Lhost : h->L;
+    return check_launch(h, launch_debug_gemm_b(L, which, expert, dst, (hipStream_t)stream), "debug_gemm_b");
+}
+
 int ds4moe_rmsnorm(const float *hin, int32_t n_tok, int32_t n_embd, double eps, uint16_t *x_bf16, void *stream) {
     if (n_tok < 0 || n_embd < 1 || n_embd > 65536 || !(eps >= 0.0))
         return fail(DS4MOE_EINVAL, "rmsnorm: n_tok %d, n_embd %d, eps %g", n_tok, n_embd, eps);

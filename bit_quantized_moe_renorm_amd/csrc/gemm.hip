@@ -174,6 +174,26 @@ __device__ __forceinline__ half8 block_a(const uint8_t *stg, int i, int c, int r
 
 // Main loop and epilogue of the routed gate/up GEMM for a chunk of NT token
 // tiles (NT is a template parameter so the step bodies have no branches).
+// B operand of the routed gate/up GEMM: for the lane's 16-byte quarter w of
+// an IQ2 row block (sub-blocks 2 g and 2 g + 1: words x, y and z, w) and
+// step cc (0..7), the 8 weights K 64 g + 8 cc .. + 7 in fp16: the signed
+// table level times fp16(d (2 ls + 1) / 64), rounded once more in the
+// product.  scl caches the scale over a sub-block's 4 steps (set at cc % 4
+// == 0), so steps go in order.  The debug entry decodes through this same
+// function.
+__device__ __forceinline__ half8 iq2_b_operand(const uint4 *T, const uint4 &w, uint16_t d, int cc, int rl,
+                                               half2v &scl) {
+    const uint32_t ib = (cc < 4) ? w.x : w.z;
+    const uint4 lv = T[((ib >> (8 * (cc & 3))) & 0xFFu) * IQ2_REPL + rl];
+    const uint32_t sw = (cc < 4) ? w.y : w.w;
+    if ((cc & 3) == 0) {
+        const _Float16 s = (_Float16)(half_to_f32(d) * (0.015625f * (float)(2u * (sw >> 28) + 1u)));
+        scl = half2v{s, s};
+    }
+    const uint4 sg = iq2_apply_signs(lv, (sw >> (7 * (cc & 3))) & 0x7Fu);
+    return as_half8(sg) * __builtin_shufflevector(scl, scl, 0, 1, 0, 1, 0, 1, 0, 1);
+}
+
 template <int NT>
 __device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &W, const uint4 *T, uint8_t *stg0,
                                                     uint8_t *stg1, const BlockLoader &ld, uint4 (&xr)[LD_V],
@@ -228,23 +248,9 @@ __device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &
         half2v scl[GU_NF];
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
-            uint4 lv[GU_NF];
-#pragma unroll
-            for (int fi = 0; fi < GU_NF; ++fi) {
-                const uint32_t ib = (cc < 4) ? wcur[fi].x : wcur[fi].z;
-                lv[fi] = T[((ib >> (8 * (cc & 3))) & 0xFFu) * IQ2_REPL + rl];
-            }
             half8 b[GU_NF];
 #pragma unroll
-            for (int fi = 0; fi < GU_NF; ++fi) {
-                const uint32_t sw = (cc < 4) ? wcur[fi].y : wcur[fi].w;
-                if ((cc & 3) == 0) {
-                    const _Float16 s = (_Float16)(half_to_f32(dcur[fi]) * (0.015625f * (float)(2u * (sw >> 28) + 1u)));
-                    scl[fi] = half2v{s, s};
-                }
-                const uint4 sg = iq2_apply_signs(lv[fi], (sw >> (7 * (cc & 3))) & 0x7Fu);
-                b[fi] = as_half8(sg) * __builtin_shufflevector(scl[fi], scl[fi], 0, 1, 0, 1, 0, 1, 0, 1);
-            }
+            for (int fi = 0; fi < GU_NF; ++fi) b[fi] = iq2_b_operand(T, wcur[fi], dcur[fi], cc, rl, scl[fi]);
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
                 const half8 a = block_a(cur, i, cc, rl, grp);
@@ -384,6 +390,33 @@ __device__ __forceinline__ void q2k_build_table(uint2 *QT, int tid, int nthreads
     }
 }
 
+// B operand of the routed down GEMM: for the lane's 16 quant bytes q of a
+// Q2_K row block (weights 64 g .. 64 g + 63), its 4 scale bytes sc
+// (sub-blocks 4 g .. 4 g + 3) and dd = d | dmin << 16, step cc (0..7) gives
+// the 8 weights K 64 g + 8 cc .. + 7 in fp16 as fma(q, fp16(d sc),
+// fp16(-dmin m)).  dsc and msc cache the scale and min over a sub-block's 2
+// steps (set at even cc), so steps go in order.  The debug entry decodes
+// through this same function.
+__device__ __forceinline__ half8 q2k_b_operand(const uint2 *QT, const uint4 &q, uint32_t sc, uint32_t dd, int cc,
+                                               int rl, half8 &dsc, half8 &msc) {
+    const uint32_t dw = (cc < 2) ? q.x : (cc < 4) ? q.y : (cc < 6) ? q.z : q.w;
+    const int sh = 16 * (cc & 1);
+    const uint2 lo = QT[((dw >> sh) & 0xFFu) * QT_REPL + rl];
+    const uint2 hi = QT[((dw >> (sh + 8)) & 0xFFu) * QT_REPL + rl];
+    if ((cc & 1) == 0) {
+        // sub-block 4 g + cc / 2: scale and min nibbles of its scale byte
+        const uint32_t sb8 = (sc >> (8 * (cc >> 1))) & 0xFFu;
+        const float d = half_to_f32((uint16_t)(dd & 0xFFFFu));
+        const float dmin = half_to_f32((uint16_t)(dd >> 16));
+        const _Float16 ds = (_Float16)(d * (float)(sb8 & 0xFu));
+        const _Float16 ms = (_Float16)(-dmin * (float)(sb8 >> 4));
+        dsc = half8{ds, ds, ds, ds, ds, ds, ds, ds};
+        msc = half8{ms, ms, ms, ms, ms, ms, ms, ms};
+    }
+    const half8 qv = as_half8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    return __builtin_elementwise_fma(qv, dsc, msc);
+}
+
 template <int NT>
 __device__ __forceinline__ void down_routed_tiles(const Layer &L, const Work &W, float *__restrict__ out,
                                                   const uint2 *QT, uint8_t *stg0, uint8_t *stg1, const BlockLoader &ld,
@@ -426,30 +459,10 @@ __device__ __forceinline__ void down_routed_tiles(const Layer &L, const Work &W,
             half8 dsc[DN_NF], msc[DN_NF];
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) {
-                uint2 lo[DN_NF], hi[DN_NF];
-#pragma unroll
-                for (int fi = 0; fi < DN_NF; ++fi) {
-                    const uint32_t dw = (cc < 2) ? qcur[fi].x : (cc < 4) ? qcur[fi].y : (cc < 6) ? qcur[fi].z : qcur[fi].w;
-                    const int sh = 16 * (cc & 1);
-                    lo[fi] = QT[((dw >> sh) & 0xFFu) * QT_REPL + rl];
-                    hi[fi] = QT[((dw >> (sh + 8)) & 0xFFu) * QT_REPL + rl];
-                }
                 half8 b[DN_NF];
 #pragma unroll
-                for (int fi = 0; fi < DN_NF; ++fi) {
-                    if ((cc & 1) == 0) {
-                        // sub-block 4 grp + cc / 2: scale and min nibbles of its scale byte
-                        const uint32_t sb8 = (scur[fi] >> (8 * (cc >> 1))) & 0xFFu;
-                        const float d = half_to_f32((uint16_t)(dcur[fi] & 0xFFFFu));
-                        const float dmin = half_to_f32((uint16_t)(dcur[fi] >> 16));
-                        const _Float16 ds = (_Float16)(d * (float)(sb8 & 0xFu));
-                        const _Float16 ms = (_Float16)(-dmin * (float)(sb8 >> 4));
-                        dsc[fi] = half8{ds, ds, ds, ds, ds, ds, ds, ds};
-                        msc[fi] = half8{ms, ms, ms, ms, ms, ms, ms, ms};
-                    }
-                    const half8 qv = as_half8(make_uint4(lo[fi].x, lo[fi].y, hi[fi].x, hi[fi].y));
-                    b[fi] = __builtin_elementwise_fma(qv, dsc[fi], msc[fi]);
-                }
+                for (int fi = 0; fi < DN_NF; ++fi)
+                    b[fi] = q2k_b_operand(QT, qcur[fi], scur[fi], dcur[fi], cc, rl, dsc[fi], msc[fi]);
 #pragma unroll
                 for (int i = 0; i < NT; ++i) {
                     const half8 a = block_a(cur, i, cc, rl, grp);
@@ -943,6 +956,55 @@ hipError_t launch_gemm_down_shared(const Layer &L, const Work &W, int n_tok, flo
         const int nb = (int)std::min<int64_t>(((int64_t)n_tok * L.n_embd + 255) / 256, 2048);
         hipLaunchKernelGGL(k_shared_dn_reduce, dim3(nb), dim3(256), 0, s, W.part, n_tok, L.n_embd, ks, out);
     }
+    return hipGetLastError();
+}
+
+// Debug: one routed expert matrix exactly as the grouped GEMMs feed it to
+// the MFMAs, through iq2_b_operand and q2k_b_operand (which 0 gate, 1 up:
+// [n_ff][n_embd]; 2 down: [n_embd][n_ff]), each fp16 value widened to fp32.
+// One thread per (row, 256-K block, lane quarter g), its 8 steps in order.
+__global__ __launch_bounds__(256) void k_debug_gemm_b(Layer L, int which, int expert, float *__restrict__ dst) {
+    __shared__ uint4 T[256 * IQ2_REPL];
+    __shared__ uint2 QT[256 * QT_REPL];
+    const int tid = threadIdx.x;
+    if (which < 2)
+        iq2_build_lut<true>(T, L.codebook, tid, 256);
+    else
+        q2k_build_table(QT, tid, 256);
+    __syncthreads();
+    const int rows = which < 2 ? L.n_ff : L.n_embd, nb = which < 2 ? L.nbe : L.nbf;
+    const int64_t i = (int64_t)blockIdx.x * 256 + tid;
+    if (i >= (int64_t)rows * nb * 4) return;
+    const int g = (int)(i & 3);
+    const int64_t rbk = i >> 2;
+    const int row = (int)(rbk / nb), bi = (int)(rbk % nb);
+    const int rl = tid & 15;
+    const int64_t rb = ((int64_t)expert * rows + row) * nb + bi;
+    float *o = dst + (int64_t)row * nb * QK + (int64_t)bi * QK + 64 * g;
+    if (which < 2) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(L.iq2_qs[which] + rb * 64 + 16 * g);
+        const uint16_t d = L.iq2_d[which][rb];
+        half2v scl;
+        for (int cc = 0; cc < 8; ++cc) {
+            const half8 b = iq2_b_operand(T, w, d, cc, rl, scl);
+            for (int j = 0; j < 8; ++j) o[8 * cc + j] = (float)b[j];
+        }
+    } else {
+        const uint4 q = *reinterpret_cast<const uint4 *>(L.q2k_qs + rb * 64 + 16 * g);
+        const uint32_t sc = *reinterpret_cast<const uint32_t *>(L.q2k_sc + rb * 16 + 4 * g);
+        const uint32_t dd = L.q2k_dd[rb];
+        half8 dsc, msc;
+        for (int cc = 0; cc < 8; ++cc) {
+            const half8 b = q2k_b_operand(QT, q, sc, dd, cc, rl, dsc, msc);
+            for (int j = 0; j < 8; ++j) o[8 * cc + j] = (float)b[j];
+        }
+    }
+}
+
+hipError_t launch_debug_gemm_b(const Layer &L, int which, int expert, float *dst, hipStream_t s) {
+    const int rows = which < 2 ? L.n_ff : L.n_embd, nb = which < 2 ? L.nbe : L.nbf;
+    const int64_t n = (int64_t)rows * nb * 4;
+    hipLaunchKernelGGL(k_debug_gemm_b, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, L, which, expert, dst);
     return hipGetLastError();
 }
 

@@ -272,6 +272,17 @@ int ds4moe_set_path(ds4moe_t *h, int32_t path);
 int ds4moe_dequantize(ds4moe_t *h, int32_t expert, int32_t which, float *dst, void *stream);
 
 /*
+ * Debug/test: one routed expert matrix exactly as the grouped GEMM kernels
+ * feed it to the MFMAs, each fp16 value widened to fp32, through the same
+ * device code (which and dst as for ds4moe_dequantize).  The 2-bit weights
+ * are rounded to fp16 there: an IQ2 weight is its signed level times
+ * fp16(d (2 ls + 1) / 64), rounded again in the product; a Q2_K weight is
+ * fma(q, fp16(d sc), fp16(-dmin m)) in fp16.  DS4MOE_EUNSUPPORTED for a q4
+ * layer (its kernels keep the weights exact in fp32).
+ */
+int ds4moe_debug_gemm_b(ds4moe_t *h, int32_t expert, int32_t which, float *dst, void *stream);
+
+/*
  * RMSNorm with unit gain between stacked layers (the stack of 43 layers,
  * "Redis 作者出手！ds4...", section 2.1; the pages' model mixes layers through
  * hyper-connections instead, which this block leaves out):

@@ -120,3 +120,38 @@ def test_misaligned_and_mistyped_buffers():
     torch.cuda.synchronize()
     assert dev.status() == m.OK
     dev.close()
+
+
+def test_create_out_of_device_memory():
+    """With nearly all device memory taken, create fails with DS4MOE_ENOMEM
+    and releases what it had allocated: once the memory is back, the same
+    description creates a working layer."""
+    lay = host_layer("ds4")
+    w = m.upload_layer(lay)
+    torch.cuda.synchronize()
+    free, _ = torch.cuda.mem_get_info()
+    log(f"[gpu] taking {free / 2**30:.1f} GiB of device memory, all but 256 MiB")
+    hog = []
+    left = free - (256 << 20)
+    chunk = 16 << 30
+    while left > (64 << 20):
+        n = min(chunk, left)
+        try:
+            hog.append(torch.empty(n, dtype=torch.uint8, device="cuda"))
+            left -= n
+        except RuntimeError:
+            chunk //= 2
+            if chunk < (64 << 20):
+                break
+    with pytest.raises(m.Ds4MoeError) as ei:
+        m.MoELayer(lay.spec, w, max_tokens=64, act_dtype=m.BF16)
+    assert ei.value.code == m.ENOMEM
+    del hog
+    torch.cuda.empty_cache()
+    dev = m.MoELayer(lay.spec, w, max_tokens=64, act_dtype=m.BF16)
+    x = m.to_device_x(synth.activations(1, 1, 4096))
+    out = torch.zeros((1, 4096), dtype=torch.float32, device="cuda")
+    dev.forward(x, out)
+    torch.cuda.synchronize()
+    assert dev.status() == m.OK and bool(torch.isfinite(out).all())
+    dev.close()
