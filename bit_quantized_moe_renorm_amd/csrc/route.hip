@@ -14,7 +14,7 @@
 namespace ds4 {
 
 constexpr int RT_WAVES = 4;         // waves per router workgroup (one K quarter each)
-constexpr int RT_TOK = 16;          // tokens per router workgroup (8 for calls of up to 8 tokens)
+constexpr int RT_TOK = 16;          // tokens per router workgroup beyond 64 tokens (fp32 activations; bf16 ones take the batched router)
 constexpr int ROUTE_SMALL_MAX = 64; // fused top-k/bucketing in the last workgroup up to this n_tok
 
 template <bool XBF16>
@@ -842,33 +842,24 @@ hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok,
         return hipGetLastError();
     }
     const int fuse = n_tok <= ROUTE_SMALL_MAX;
-    // 8-token tiles for calls of up to 8 tokens (a 16-token tile would load and
-    // multiply clamped copies of the last token), a 1-token tile for one token
-    const bool small = n_tok <= 8;
-    const int tt = n_tok == 1 ? 1 : small ? 8 : RT_TOK;
+    // token tiles of 1, 2, 4 or 8 for calls of up to 8 tokens (a larger tile
+    // would load and multiply clamped copies of the last token), and 8 up to
+    // 64 tokens too: the 16-token tile takes 252 VGPRs (2 waves per SIMD), and
+    // 8-token tiles measured 44 -> 33 us at 16 tokens, 52 -> 47 at 32
+    const int tt = n_tok == 1 ? 1 : n_tok == 2 ? 2 : n_tok <= 4 ? 4 : fuse ? 8 : RT_TOK;
     const dim3 grid(NE, (n_tok + tt - 1) / tt);
-    if (n_tok == 1) {
-        if (L.act_dtype == 1)
-            hipLaunchKernelGGL((k_route_logits<true, 1>), grid, dim3(256), 0, s, L.router, L.router_bias, x, n_tok,
-                               NE, L.n_embd, L.top_k, W, fuse, tag);
-        else
-            hipLaunchKernelGGL((k_route_logits<false, 1>), grid, dim3(256), 0, s, L.router, L.router_bias, x, n_tok,
-                               NE, L.n_embd, L.top_k, W, fuse, tag);
-    } else if (L.act_dtype == 1) {
-        if (small)
-            hipLaunchKernelGGL((k_route_logits<true, 8>), grid, dim3(256), 0, s, L.router, L.router_bias, x, n_tok,
-                               NE, L.n_embd, L.top_k, W, fuse, tag);
-        else
-            hipLaunchKernelGGL((k_route_logits<true, RT_TOK>), grid, dim3(256), 0, s, L.router, L.router_bias, x,
-                               n_tok, NE, L.n_embd, L.top_k, W, fuse, tag);
-    } else {
-        if (small)
-            hipLaunchKernelGGL((k_route_logits<false, 8>), grid, dim3(256), 0, s, L.router, L.router_bias, x, n_tok,
-                               NE, L.n_embd, L.top_k, W, fuse, tag);
-        else
-            hipLaunchKernelGGL((k_route_logits<false, RT_TOK>), grid, dim3(256), 0, s, L.router, L.router_bias, x,
-                               n_tok, NE, L.n_embd, L.top_k, W, fuse, tag);
+    const bool bf = L.act_dtype == 1;
+#define DS4_ROUTE_LAUNCH(T)                                                                                   \
+    hipLaunchKernelGGL((bf ? k_route_logits<true, T> : k_route_logits<false, T>), grid, dim3(256), 0, s, L.router, \
+                       L.router_bias, x, n_tok, NE, L.n_embd, L.top_k, W, fuse, tag)
+    switch (tt) {
+        case 1: DS4_ROUTE_LAUNCH(1); break;
+        case 2: DS4_ROUTE_LAUNCH(2); break;
+        case 4: DS4_ROUTE_LAUNCH(4); break;
+        case 8: DS4_ROUTE_LAUNCH(8); break;
+        default: DS4_ROUTE_LAUNCH(RT_TOK); break;
     }
+#undef DS4_ROUTE_LAUNCH
     if (!fuse) {
         hipLaunchKernelGGL(k_topk, dim3((n_tok + 3) / 4), dim3(256), 0, s, n_tok, NE, L.top_k, W);
         hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, s, n_tok, NE, L.top_k, W);
