@@ -12,7 +12,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libds4moe.so"
 BUILD = ROOT / "_build"
-SOURCES = ["ds4moe.hip", "repack.hip", "route.hip", "gemv.hip", "decode.hip", "gemm.hip", "rmsnorm.hip", "q4k.hip", "cache.hip"]
+SOURCES = ["ds4moe.hip", "repack.hip", "route.hip", "gemv.hip", "decode.hip", "gemm.hip", "rmsnorm.hip", "q4k.hip", "cache.hip", "shared_blas.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -39,7 +39,9 @@ def build(jobs: int = 6) -> Path:
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB.with_suffix(".so.tmp")
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)]
+    # hipBLASLt runs the shared expert's dense GEMMs for large calls
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *map(str, objs), "-L/opt/rocm/lib", "-lhipblaslt",
+           "-Wl,-rpath,/opt/rocm/lib", "-o", str(tmp)]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB

@@ -194,6 +194,16 @@ hipError_t launch_router_prep(const float *router, int NE, int E, uint16_t *hml,
 // hand-off tag is ep + 1, never 0)
 hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s,
                         unsigned long long ep);
+// The shared expert of large bf16 calls on hipBLASLt (shared_blas.hip):
+// gate/up GEMM + SiLU split into W.hsh_hi / hsh_lo, then the down GEMMs
+// into out.  Requires sh_up == sh_gate + n_ff * n_embd.
+struct SharedBlas;
+constexpr int SBLAS_CHUNK = 2048;   // tokens per GEMM (the fp32 gate/up buffer holds one chunk)
+constexpr int SBLAS_MIN_TOK = 128;  // calls of fewer tokens keep the grouped kernels' shared tiles
+int sblas_create(SharedBlas **out, int n_ff);
+void sblas_destroy(SharedBlas *S);
+hipError_t sblas_gateup(SharedBlas *S, const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s);
+hipError_t sblas_down(SharedBlas *S, const Layer &L, const Work &W, int n_tok, float *out, hipStream_t s);
 hipError_t launch_debug_gemm_b(const Layer &L, int which, int expert, float *dst, hipStream_t s);
 hipError_t launch_cache_update(const Layer &L, const Work &W, const ExpertCache &C, int64_t expert_bytes,
                                hipStream_t s);

@@ -83,6 +83,7 @@ struct ds4moe {
     int64_t expert_bytes = 0;
     Layer Lhost{};
     std::vector<void *> host_allocs;      // pinned host memory of the backing store
+    SharedBlas *sblas = nullptr;          // the shared expert of large bf16 calls on hipBLASLt, if any
     // timing
     bool timing = false;
     std::vector<hipEvent_t> events;  // pairs
@@ -96,6 +97,7 @@ struct ds4moe {
         for (hipEvent_t e : events) (void)hipEventDestroy(e);
         if (status_host) (void)hipHostFree(status_host);
         for (void *p : host_allocs) (void)hipHostFree(p);
+        sblas_destroy(sblas);
     }
     void *alloc(size_t bytes, hipError_t &err) {
         void *p = nullptr;
@@ -296,8 +298,9 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     }
     uint16_t *sg = nullptr, *su = nullptr, *sd = nullptr;
     if (d->n_shared) {
-        sg = (uint16_t *)A(F * E * 2);
-        su = (uint16_t *)A(F * E * 2);
+        // gate and up adjacent: one [2 n_ff][n_embd] matrix for the library GEMM
+        sg = (uint16_t *)A(2 * F * E * 2);
+        su = sg ? sg + F * E : nullptr;
         sd = (uint16_t *)A(E * F * 2);
     }
     // workspace
@@ -500,6 +503,11 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
         L.slot_of = h->cache.slot_of;
         Lh.slot_of = nullptr;
     }
+    // the shared expert of large bf16 calls on hipBLASLt (without it, if the
+    // library cannot be set up: the grouped kernels cover every size)
+    if (d->n_shared && d->act_dtype == DS4MOE_BF16 && d->max_tokens >= SBLAS_MIN_TOK &&
+        sblas_create(&h->sblas, (int)F) != 0)
+        h->sblas = nullptr;
     h->decode_grid = decode_grid(d->act_dtype == DS4MOE_BF16);
     if (h->decode_grid <= 0) {
         delete h;
@@ -648,9 +656,11 @@ static int run_gemm(ds4moe *h, const Work &W, const void *x, int n, float *out, 
     rc = check_launch(h, launch_gemm_gateup_routed(h->L, W, n, s), "gemm routed gate/up");
     h->tend(tb, s);
     if (rc) return rc;
+    const bool blas = h->sblas && n >= SBLAS_MIN_TOK;
     if (h->L.n_shared) {
         tb = h->tbegin(TK_GEMM_GU_SHARED, s);
-        rc = check_launch(h, launch_gemm_gateup_shared(h->L, W, x, n, s), "gemm shared gate/up");
+        rc = check_launch(h, blas ? sblas_gateup(h->sblas, h->L, W, x, n, s) : launch_gemm_gateup_shared(h->L, W, x, n, s),
+                          "gemm shared gate/up");
         h->tend(tb, s);
         if (rc) return rc;
     }
@@ -660,7 +670,8 @@ static int run_gemm(ds4moe *h, const Work &W, const void *x, int n, float *out, 
     if (rc) return rc;
     if (h->L.n_shared) {
         tb = h->tbegin(TK_GEMM_DN_SHARED, s);
-        rc = check_launch(h, launch_gemm_down_shared(h->L, W, n, out, s), "gemm shared down");
+        rc = check_launch(h, blas ? sblas_down(h->sblas, h->L, W, n, out, s) : launch_gemm_down_shared(h->L, W, n, out, s),
+                          "gemm shared down");
         h->tend(tb, s);
     }
     return rc;
