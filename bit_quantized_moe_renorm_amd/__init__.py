@@ -19,11 +19,12 @@ LIB_PATH = _PKG / "libds4moe.so"
 OK, EINVAL, ENOMEM, EHIP, EUNSUPPORTED, EPOISONED = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 FMT_Q2, FMT_Q4 = 0, 1
-PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
-ABI_VERSION = 3
+PATH_AUTO, PATH_GEMV, PATH_GEMM, PATH_SMALL = 0, 1, 2, 3
+SMALL_MAX_TOKENS = 8
+ABI_VERSION = 4
 TIMING_KINDS = ("route", "gateup_routed", "gateup_shared", "down_routed", "down_shared", "gemm_gateup_routed",
                 "gemm_down_routed", "fused", "gemm_prep", "gemm_gateup_shared", "gemm_down_shared",
-                "q4_gateup_routed", "q4_down_routed", "cache")
+                "q4_gateup_routed", "q4_down_routed", "cache", "small_gateup", "small_down")
 
 SYMBOLS = ("ds4moe_create", "ds4moe_route", "ds4moe_forward", "ds4moe_set_path", "ds4moe_dequantize",
            "ds4moe_rmsnorm", "ds4moe_forward_stack", "ds4moe_timing_enable", "ds4moe_timing_read",

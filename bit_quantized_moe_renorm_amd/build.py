@@ -12,7 +12,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libds4moe.so"
 BUILD = ROOT / "_build"
-SOURCES = ["ds4moe.hip", "repack.hip", "route.hip", "gemv.hip", "decode.hip", "gemm.hip", "rmsnorm.hip", "q4k.hip", "cache.hip", "shared_blas.hip"]
+SOURCES = ["ds4moe.hip", "repack.hip", "route.hip", "gemv.hip", "decode.hip", "gemm.hip", "rmsnorm.hip", "q4k.hip", "cache.hip", "shared_blas.hip", "small.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -23,6 +23,8 @@ constexpr int QK = 256;
 constexpr int MAX_TOPK = 8;
 constexpr int MAX_EXPERT = 256;
 constexpr int GEMV_MAX_TOK = 4;   // GEMV path keeps up to this many tokens' x in registers
+constexpr int SMALL_MAX_TOK = 8;  // small-batch kernels: tokens per call at most (bf16 x, 2-bit experts)
+constexpr int SMALL_MAX_FF = 2048; // small-batch kernels: n_ff at most (h vectors staged in LDS)
 
 struct Layer {
     int n_embd, n_ff, n_expert, top_k, n_shared, max_tokens, act_dtype;
@@ -114,6 +116,9 @@ struct Work {
     uint32_t want_xor;
     // per call: the tokens' ids ([n_tok], device) for a hash-routed layer
     const int32_t *ids;
+    // small-batch path: two buffers of gate/up sums in turn, each
+    // [SMALL_MAX_TOK (k + 1)][2 F] fp32 (nullptr if the layer cannot take the path)
+    float *sgu;
 };
 
 constexpr int DEFAULT_SPIN_LIMIT = 1 << 20;  // about a second of polling
@@ -173,6 +178,47 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Wave-wide maximum of an unsigned key by DPP (row shifts, then the two row
+// broadcasts), read from the last lane: every lane gets it.  All 64 lanes
+// must be active.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true));  // row_shr:1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true));  // row_shr:2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true));  // row_shr:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true));  // row_shr:8
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false)); // row_bcast:15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false)); // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Order-preserving 32-bit key of an fp32 logit (larger logit, larger key),
+// never 0 (0 marks a taken or absent expert).
+__device__ __forceinline__ uint32_t logit_key32(float L) {
+    const uint32_t u = __float_as_uint(L);
+    const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return key ? key : 1u;
+}
+__device__ __forceinline__ float key32_logit(uint32_t m) {
+    return __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+}
+
+// One top-k round over the wave's keys (lane l holds experts l + 64 i in
+// key[i]): the largest key, at the lowest expert index among equal keys; that
+// expert's key is cleared.  Wave-uniform results.
+__device__ __forceinline__ void topk_round(uint32_t (&key)[4], uint32_t &m, int &e) {
+    const int lane = threadIdx.x & 63;
+    m = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+    e = -1;
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+        const uint64_t bb = __ballot(key[i] == m);
+        if (bb) e = 64 * i + (__ffsll((unsigned long long)bb) - 1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i == e) key[i] = 0u;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
@@ -221,7 +267,8 @@ hipError_t launch_gemv_down_shared(const Layer &L, const Work &W, int n_tok, flo
 enum TimingKind {
     TK_ROUTE = 0, TK_GU_ROUTED = 1, TK_GU_SHARED = 2, TK_DN_ROUTED = 3, TK_DN_SHARED = 4,
     TK_GEMM_GU_ROUTED = 5, TK_GEMM_DN_ROUTED = 6, TK_FUSED = 7, TK_GEMM_PREP = 8, TK_GEMM_GU_SHARED = 9,
-    TK_GEMM_DN_SHARED = 10, TK_Q4_GU_ROUTED = 11, TK_Q4_DN_ROUTED = 12, TK_CACHE = 13, TK_COUNT = 14
+    TK_GEMM_DN_SHARED = 10, TK_Q4_GU_ROUTED = 11, TK_Q4_DN_ROUTED = 12, TK_CACHE = 13, TK_SMALL_GU = 14,
+    TK_SMALL_DN = 15, TK_COUNT = 16
 };
 
 bool gemm_enabled();
@@ -238,6 +285,16 @@ int decode_grid(int act_bf16);
 // earlier on the stream), so the kernel skips its router phase.
 hipError_t launch_decode_fused(const Layer &L, const Work &W, const void *x, float *out, int grid,
                                unsigned long long ep, hipStream_t s, bool pre_routed = false);
+
+// Small batches (2..SMALL_MAX_TOK tokens, bf16 x, 2-bit experts), after the
+// router: gate/up sums into gu (small_sum_floats floats, zero on entry), then
+// the down projections into out, which also clear gz (the other buffer).
+int small_grid();  // workgroups per launch (one per CU), 0 if the kernels cannot run
+size_t small_sum_floats(const Layer &L);
+hipError_t launch_small_gateup(const Layer &L, const Work &W, const void *x, int n_tok, float *gu, int grid,
+                               hipStream_t s);
+hipError_t launch_small_down(const Layer &L, const Work &W, const float *gu, float *gz, int n_tok, float *out,
+                             int grid, hipStream_t s);
 
 hipError_t launch_rmsnorm(const float *h, int n_tok, int n_embd, double eps, uint16_t *x, hipStream_t s);
 

@@ -121,17 +121,6 @@ __device__ __forceinline__ void st_tagged(unsigned long long *p, float v, uint32
 }
 
 // ---------------------------------------------------------------- P0: router
-// Wave-wide maximum of an unsigned key by DPP (row shifts, then the two row
-// broadcasts); the result is read from the last lane.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true));  // row_shr:1
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true));  // row_shr:2
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true));  // row_shr:4
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true));  // row_shr:8
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false)); // row_bcast:15
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false)); // row_bcast:31
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
 
 // Routing of the token, computed by every workgroup for itself (wave 0) once
 // all router halves are counted: fp32 logits from the fp64 halves, top-k with
@@ -197,34 +186,17 @@ __device__ __forceinline__ void dec_topk_local(const Layer &L, const Work &W, co
     // experts l + 64 i, whose fp64 logits (both halves and the bias) are lg[i]
     uint32_t key[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ee = lane + 64 * i;
-        key[i] = 0u;
-        if (ee < NE) {
-            const float Lf = (float)lg[i];
-            const uint32_t u = __float_as_uint(Lf);
-            key[i] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-            if (key[i] == 0u) key[i] = 1u;  // keep 0 free for "taken"
-        }
-    }
+    for (int i = 0; i < 4; ++i) key[i] = lane + 64 * i < NE ? logit_key32((float)lg[i]) : 0u;
     // lane j < k ends up holding the j-th selection
     int myE = 0;
     float myL = 0.f;
 #pragma unroll
     for (int j = 0; j < MAX_TOPK; ++j) {
         if (j >= k) break;
-        const uint32_t m = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
-        int ee = -1;
-#pragma unroll
-        for (int i = 3; i >= 0; --i) {
-            const uint64_t bb = __ballot(key[i] == m);
-            if (bb) ee = 64 * i + (__ffsll((unsigned long long)bb) - 1);
-        }
-        const uint32_t u = (m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m;
-        if (lane == j) myE = ee, myL = __uint_as_float(u);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (lane + 64 * i == ee) key[i] = 0u;
+        uint32_t m;
+        int ee;
+        topk_round(key, m, ee);
+        if (lane == j) myE = ee, myL = key32_logit(m);
     }
     dec_route_finish(L, W, myE, myL, rc, write_global);
 }

@@ -38,6 +38,7 @@ bool pow2_dim(int v) { return v == 256 || v == 512 || v == 1024 || v == 2048 || 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 constexpr int TIMING_SLOTS = TK_COUNT;
+static_assert(TIMING_SLOTS == DS4MOE_TIMING_KINDS, "timing kinds of the ABI");
 constexpr int TIMING_EVENTS = 4096;
 
 // ---------------------------------------------------------------- static scratch
@@ -65,6 +66,8 @@ struct ds4moe {
     Work W{};
     int path = DS4MOE_PATH_AUTO;
     int decode_grid = 0;    // workgroups of the persistent decode kernel
+    int small_grid = 0;     // workgroups of the small-batch kernels (0: the layer has no small-batch path)
+    int small_parity = 0;   // which of the two gate/up sum buffers the next small-batch call uses
     unsigned long long decode_calls = 0;  // fused launches so far (the phase counters' epoch)
     unsigned long long route_calls = 0;   // routing launches so far (the router hand-off tag)
     bool poisoned = false;
@@ -319,6 +322,10 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     size_t o_ecnt = carve(MAX_EXPERT * 4), o_rest = carve(4 * T * NE * 4), o_rtag = carve(4 * MAX_EXPERT * 8);
     size_t o_htag = carve((size_t)(k + 1) * F * 8);
     size_t o_ltag = carve(64 * MAX_EXPERT * 8), o_itag = carve(64 * MAX_TOPK * 8);
+    // small batches (2..SMALL_MAX_TOK bf16 tokens, 2-bit experts, n_ff <= SMALL_MAX_FF): two
+    // gate/up sum buffers, zero at create like the whole workspace
+    const bool small_cap = !q4 && d->act_dtype == DS4MOE_BF16 && T >= 2 && F <= SMALL_MAX_FF;
+    size_t o_sgu = carve(small_cap ? 2 * small_sum_floats(L) * 4 : 0);
     char *ws = (char *)A(off);
     if (err != hipSuccess) {
         delete h;
@@ -366,6 +373,7 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     W.htag = (unsigned long long *)(ws + o_htag);
     W.ltag = (unsigned long long *)(ws + o_ltag);
     W.itag = (unsigned long long *)(ws + o_itag);
+    W.sgu = small_cap ? (float *)(ws + o_sgu) : nullptr;
     // the host-visible status word of the bounded waits
     if (hipHostMalloc((void **)&h->status_host, 256, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess) {
         h->status_host = nullptr;
@@ -509,6 +517,16 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
         sblas_create(&h->sblas, (int)F) != 0)
         h->sblas = nullptr;
     h->decode_grid = decode_grid(d->act_dtype == DS4MOE_BF16);
+    // the small-batch kernels stage at most two routed slots' and two shared
+    // K parts' h vectors per workgroup: a workgroup's range of down units must
+    // be shorter than one slot's or one part's (n_embd / 16 units).  Its cost
+    // share is at most TE (3 U + F / 256) / G shared-unit costs (routed down
+    // units cost 3, shared 1; U <= SMALL_MAX_TOK k slots), so G must exceed
+    // 3 U + F / 256.
+    if (small_cap) {
+        const int g = small_grid();
+        if (g >= 3 * SMALL_MAX_TOK * (int)k + (int)(F / 256) + 1) h->small_grid = g;
+    }
     if (h->decode_grid <= 0) {
         delete h;
         return fail(DS4MOE_EHIP, "create: cannot size the decode grid");
@@ -526,9 +544,14 @@ int ds4moe_destroy(ds4moe_t *h) {
 
 int ds4moe_set_path(ds4moe_t *h, int32_t path) {
     if (!h) return fail(DS4MOE_EINVAL, "set_path: NULL handle");
-    if (path < DS4MOE_PATH_AUTO || path > DS4MOE_PATH_GEMM) return fail(DS4MOE_EINVAL, "set_path: %d", path);
+    if (path < DS4MOE_PATH_AUTO || path > DS4MOE_PATH_SMALL) return fail(DS4MOE_EINVAL, "set_path: %d", path);
     if (path == DS4MOE_PATH_GEMM && h->L.fmt == 1)
         return fail(DS4MOE_EUNSUPPORTED, "set_path: a q4 layer has no grouped GEMM path");
+    if (path == DS4MOE_PATH_SMALL && !h->small_grid)
+        return fail(DS4MOE_EUNSUPPORTED,
+                    "set_path: the small-batch path needs bf16 activations, the 2-bit format, n_ff <= %d and "
+                    "max_tokens >= 2",
+                    SMALL_MAX_FF);
     h->path = path;
     return DS4MOE_OK;
 }
@@ -677,6 +700,26 @@ static int run_gemm(ds4moe *h, const Work &W, const void *x, int n, float *out, 
     return rc;
 }
 
+// The expert kernels after the routing for 2..SMALL_MAX_TOK bf16 tokens: the
+// two persistent small-batch kernels (gate/up sums into one buffer, then the
+// down projections, which also clear the other buffer for the next call).
+static bool small_ok(const ds4moe *h, int n) { return h->small_grid > 0 && n >= 2 && n <= SMALL_MAX_TOK; }
+
+static int run_small(ds4moe *h, const Work &W, const void *x, int n, float *out, hipStream_t s) {
+    const size_t zn = small_sum_floats(h->L);
+    float *gu = W.sgu + (size_t)h->small_parity * zn, *gz = W.sgu + (size_t)(1 - h->small_parity) * zn;
+    int tb = h->tbegin(TK_SMALL_GU, s);
+    int rc = check_launch(h, launch_small_gateup(h->L, W, x, n, gu, h->small_grid, s), "small-batch gate/up");
+    h->tend(tb, s);
+    if (rc) return rc;
+    tb = h->tbegin(TK_SMALL_DN, s);
+    rc = check_launch(h, launch_small_down(h->L, W, gu, gz, n, out, h->small_grid, s), "small-batch down");
+    h->tend(tb, s);
+    if (rc) return rc;
+    h->small_parity ^= 1;
+    return DS4MOE_OK;
+}
+
 static int run_route(ds4moe *h, const Work &W, const void *x, int n, hipStream_t s) {
     int tb = h->tbegin(TK_ROUTE, s);
     int rc = check_launch(h, launch_route(h->L, W, x, n, s, h->route_calls++), "route");
@@ -701,6 +744,7 @@ static int forward_cached(ds4moe *h, const void *x, const int32_t *ids, int n_to
     const Layer &L = h->L;
     int chunk = h->cache.slots >= L.n_expert ? n_tok : std::max(1, h->cache.slots / L.top_k);
     if (L.fmt == 1 || h->path == DS4MOE_PATH_GEMV) chunk = std::min(chunk, GEMV_MAX_TOK);
+    if (h->path == DS4MOE_PATH_SMALL) chunk = std::min(chunk, SMALL_MAX_TOK);
     h->last_n_tok = chunk >= n_tok ? n_tok : -1;
     h->last_static = false;
     const size_t xb = L.act_dtype == DS4MOE_BF16 ? 2 : 4;
@@ -713,7 +757,7 @@ static int forward_cached(ds4moe *h, const void *x, const int32_t *ids, int n_to
         int rc = run_route(h, W, xc, n, s);
         if (!rc) rc = run_cache(h, W, s);
         if (rc) return rc;
-        if (n == 1 && L.fmt == 0 && h->path == DS4MOE_PATH_AUTO) {
+        if (n == 1 && L.fmt == 0 && (h->path == DS4MOE_PATH_AUTO || h->path == DS4MOE_PATH_SMALL)) {
             // one token: the fused decode kernel, taking the routing from the
             // router kernel (its own router phase would come after the cache step)
             int tf = h->tbegin(TK_FUSED, s);
@@ -726,8 +770,10 @@ static int forward_cached(ds4moe *h, const void *x, const int32_t *ids, int n_to
         }
         bool gemv = n <= GEMV_MAX_TOK && (L.fmt == 1 || h->path == DS4MOE_PATH_GEMV ||
                                           (h->path == DS4MOE_PATH_AUTO && L.act_dtype == DS4MOE_F32));
+        const bool small = !gemv && small_ok(h, n) && (h->path == DS4MOE_PATH_AUTO || h->path == DS4MOE_PATH_SMALL);
         rc = L.fmt == 1 ? run_q4_experts(h, W, xc, n, oc, s, true)
              : gemv     ? run_gemv(h, W, xc, n, oc, s)
+             : small    ? run_small(h, W, xc, n, oc, s)
                         : run_gemm(h, W, xc, n, oc, s);
         if (rc) return rc;
     }
@@ -762,15 +808,18 @@ static int forward_impl(ds4moe_t *h, const void *x, const int32_t *ids, int32_t 
         return DS4MOE_OK;
     }
     int path = h->path;
-    // one token: the fused decode kernel; more: the grouped GEMMs, which at 2-4
-    // tokens (K split over more workgroups) also beat the GEMV kernels.  fp32
-    // activations of up to 4 tokens keep the GEMV kernels, which do not round
-    // them to fp16.
+    // one token: the fused decode kernel; 2..SMALL_MAX_TOK bf16 tokens: the
+    // small-batch kernels; more: the grouped GEMMs.  fp32 activations of up to
+    // 4 tokens keep the GEMV kernels, which do not round them to fp16.
     if (path == DS4MOE_PATH_AUTO)
-        path = (n_tok == 1 || (n_tok <= GEMV_MAX_TOK && h->L.act_dtype == DS4MOE_F32)) ? DS4MOE_PATH_GEMV
-                                                                                      : DS4MOE_PATH_GEMM;
+        path = n_tok == 1 || (n_tok <= GEMV_MAX_TOK && h->L.act_dtype == DS4MOE_F32) ? DS4MOE_PATH_GEMV
+               : small_ok(h, n_tok)                                                  ? DS4MOE_PATH_SMALL
+                                                                                     : DS4MOE_PATH_GEMM;
     if (path == DS4MOE_PATH_GEMV && n_tok > GEMV_MAX_TOK)
         return fail(DS4MOE_EUNSUPPORTED, "forward: GEMV path takes at most %d tokens (got %d)", GEMV_MAX_TOK, n_tok);
+    if (path == DS4MOE_PATH_SMALL && (n_tok < 2 || !small_ok(h, n_tok)))
+        return fail(DS4MOE_EUNSUPPORTED, "forward: the small-batch path takes 2..%d tokens (got %d)", SMALL_MAX_TOK,
+                    n_tok);
     if (path == DS4MOE_PATH_GEMM && !gemm_available())
         return fail(DS4MOE_EUNSUPPORTED, "forward: the grouped GEMM path is not available in this build");
     h->last_n_tok = n_tok;
@@ -787,7 +836,9 @@ static int forward_impl(ds4moe_t *h, const void *x, const int32_t *ids, int32_t 
         return rc;
     }
     if ((rc = run_route(h, W, x, n_tok, s))) return rc;
-    return path == DS4MOE_PATH_GEMV ? run_gemv(h, W, x, n_tok, out, s) : run_gemm(h, W, x, n_tok, out, s);
+    return path == DS4MOE_PATH_GEMV    ? run_gemv(h, W, x, n_tok, out, s)
+           : path == DS4MOE_PATH_SMALL ? run_small(h, W, x, n_tok, out, s)
+                                       : run_gemm(h, W, x, n_tok, out, s);
 }
 
 int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *stream) {

@@ -18,22 +18,17 @@
 // high and a low part (two MFMAs), so its only rounding is fp32 accumulation.
 #include "common.h"
 #include "iq2_tables.h"
+#include "mfma_ops.h"
 
 #include <algorithm>
 
 namespace ds4 {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH_TOK = 64;                     // tokens (routed: slots) per chunk
 constexpr int STG_PITCH = 80;                  // LDS stage row: 32 16-bit values + 16 B pad
 constexpr int STG_BYTES = CH_TOK * STG_PITCH;  // one K-chunk of A for a chunk of tokens
 constexpr int GU_ROWS = 128;                   // n_ff rows per gate/up workgroup (32 per wave)
 constexpr int DN_ROWS = 256;                   // n_embd rows per down workgroup (64 per wave)
-constexpr int PF = 4;                          // prefetch distance in K-chunks
 
 bool gemm_enabled() { return true; }
 
@@ -41,19 +36,6 @@ int gemm_max_chunks(int n_tok, int NE, int k) {
     const int nq = n_tok * k;
     return min(NE, nq) + (nq + CH_TOK - 1) / CH_TOK;
 }
-
-__device__ __forceinline__ floatx4 mfma_f16(half8 a, half8 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4 mfma_bf16(uint4 a, uint4 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                   0, 0, 0);
-}
-__device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
-
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
-
-__device__ __forceinline__ uint16_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
 // ---------------------------------------------------------------- routing -> chunks
 // Splits every expert's token list into chunks of at most CH_TOK slots:
@@ -143,8 +125,6 @@ constexpr int RDN_ROWS = RB_WAVES * 16 * DN_NF;   // n_embd rows per down workgr
 constexpr int LD_V = CH_TOK * QK * 2 / 16 / RB_THREADS;  // 16-byte vectors per thread per stage
 constexpr int LD_PER_ROW = 32 / LD_V;             // threads per token row
 
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-
 // Block stage loader: thread t moves LD_V x 16 bytes: token row t / LD_PER_ROW,
 // K 8 LD_V (t % LD_PER_ROW)..+8 LD_V.  Every load is unconditional (a load
 // under a condition leaves a path without it, and the first use after the
@@ -174,26 +154,6 @@ __device__ __forceinline__ half8 block_a(const uint8_t *stg, int i, int c, int r
 
 // Main loop and epilogue of the routed gate/up GEMM for a chunk of NT token
 // tiles (NT is a template parameter so the step bodies have no branches).
-// B operand of the routed gate/up GEMM: for the lane's 16-byte quarter w of
-// an IQ2 row block (sub-blocks 2 g and 2 g + 1: words x, y and z, w) and
-// step cc (0..7), the 8 weights K 64 g + 8 cc .. + 7 in fp16: the signed
-// table level times fp16(d (2 ls + 1) / 64), rounded once more in the
-// product.  scl caches the scale over a sub-block's 4 steps (set at cc % 4
-// == 0), so steps go in order.  The debug entry decodes through this same
-// function.
-__device__ __forceinline__ half8 iq2_b_operand(const uint4 *T, const uint4 &w, uint16_t d, int cc, int rl,
-                                               half2v &scl) {
-    const uint32_t ib = (cc < 4) ? w.x : w.z;
-    const uint4 lv = T[((ib >> (8 * (cc & 3))) & 0xFFu) * IQ2_REPL + rl];
-    const uint32_t sw = (cc < 4) ? w.y : w.w;
-    if ((cc & 3) == 0) {
-        const _Float16 s = (_Float16)(half_to_f32(d) * (0.015625f * (float)(2u * (sw >> 28) + 1u)));
-        scl = half2v{s, s};
-    }
-    const uint4 sg = iq2_apply_signs(lv, (sw >> (7 * (cc & 3))) & 0x7Fu);
-    return as_half8(sg) * __builtin_shufflevector(scl, scl, 0, 1, 0, 1, 0, 1, 0, 1);
-}
-
 template <int NT>
 __device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &W, const uint4 *T, uint8_t *stg0,
                                                     uint8_t *stg1, const BlockLoader &ld, uint4 (&xr)[LD_V],
@@ -372,49 +332,6 @@ __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_gateup_routed(Layer L, W
         case 3: gateup_routed_tiles<3>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
         default: gateup_routed_tiles<4>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
     }
-}
-
-// Q2_K B decode: a table of the four 2-bit values of each qs byte as fp16
-// (8 bytes per entry), 16 replicas interleaved per entry; lane l reads replica l % 16.
-constexpr int QT_REPL = 16;
-__device__ __forceinline__ void q2k_build_table(uint2 *QT, int tid, int nthreads) {
-    for (int i = tid; i < 256 * QT_REPL; i += nthreads) {
-        const uint32_t byte = (uint32_t)i / QT_REPL;
-        uint32_t h[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t q = (byte >> (2 * j)) & 3u;
-            h[j] = (q == 0) ? 0u : (q == 1) ? 0x3C00u : (q == 2) ? 0x4000u : 0x4200u;
-        }
-        QT[i] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-    }
-}
-
-// B operand of the routed down GEMM: for the lane's 16 quant bytes q of a
-// Q2_K row block (weights 64 g .. 64 g + 63), its 4 scale bytes sc
-// (sub-blocks 4 g .. 4 g + 3) and dd = d | dmin << 16, step cc (0..7) gives
-// the 8 weights K 64 g + 8 cc .. + 7 in fp16 as fma(q, fp16(d sc),
-// fp16(-dmin m)).  dsc and msc cache the scale and min over a sub-block's 2
-// steps (set at even cc), so steps go in order.  The debug entry decodes
-// through this same function.
-__device__ __forceinline__ half8 q2k_b_operand(const uint2 *QT, const uint4 &q, uint32_t sc, uint32_t dd, int cc,
-                                               int rl, half8 &dsc, half8 &msc) {
-    const uint32_t dw = (cc < 2) ? q.x : (cc < 4) ? q.y : (cc < 6) ? q.z : q.w;
-    const int sh = 16 * (cc & 1);
-    const uint2 lo = QT[((dw >> sh) & 0xFFu) * QT_REPL + rl];
-    const uint2 hi = QT[((dw >> (sh + 8)) & 0xFFu) * QT_REPL + rl];
-    if ((cc & 1) == 0) {
-        // sub-block 4 g + cc / 2: scale and min nibbles of its scale byte
-        const uint32_t sb8 = (sc >> (8 * (cc >> 1))) & 0xFFu;
-        const float d = half_to_f32((uint16_t)(dd & 0xFFFFu));
-        const float dmin = half_to_f32((uint16_t)(dd >> 16));
-        const _Float16 ds = (_Float16)(d * (float)(sb8 & 0xFu));
-        const _Float16 ms = (_Float16)(-dmin * (float)(sb8 >> 4));
-        dsc = half8{ds, ds, ds, ds, ds, ds, ds, ds};
-        msc = half8{ms, ms, ms, ms, ms, ms, ms, ms};
-    }
-    const half8 qv = as_half8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-    return __builtin_elementwise_fma(qv, dsc, msc);
 }
 
 template <int NT>

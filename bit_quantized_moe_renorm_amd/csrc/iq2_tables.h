@@ -30,19 +30,22 @@ __device__ __forceinline__ uint32_t iq2_level_f16(uint32_t c) {
     return (c == 0) ? 0x3C00u : (c == 1) ? 0x4200u : (c == 2) ? 0x4500u : 0x4700u;
 }
 
-// Build the replicated table (entry e, replica r at uint4 index e*R + r): each
-// thread loads whole codebook entries once and writes their R replicas.
+// One entry of the replicated table (entry e, replica r at uint4 index e*R +
+// r) from its codebook word c.
+template <bool FP16, int R = IQ2_REPL>
+__device__ __forceinline__ void iq2_lut_entry(uint4 *T, int e, uint32_t c) {
+    uint32_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = FP16 ? iq2_level_f16((c >> (2 * k)) & 3u) : iq2_level_bf16((c >> (2 * k)) & 3u);
+    const uint4 q = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+#pragma unroll
+    for (int r = 0; r < R; ++r) T[e * R + r] = q;
+}
+// Build the replicated table: each thread loads whole codebook entries once
+// and writes their R replicas.
 template <bool FP16, int R = IQ2_REPL>
 __device__ __forceinline__ void iq2_build_lut(uint4 *T, const uint16_t *__restrict__ codebook, int tid, int nthreads) {
-    for (int e = tid; e < 256; e += nthreads) {
-        const uint32_t c = codebook[e];
-        uint32_t v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = FP16 ? iq2_level_f16((c >> (2 * k)) & 3u) : iq2_level_bf16((c >> (2 * k)) & 3u);
-        const uint4 q = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
-#pragma unroll
-        for (int r = 0; r < R; ++r) T[e * R + r] = q;
-    }
+    for (int e = tid; e < 256; e += nthreads) iq2_lut_entry<FP16, R>(T, e, codebook[e]);
 }
 
 // Rotate right (v_alignbit_b32 with both sources equal).  Written as one

@@ -94,26 +94,17 @@ __device__ void topk_tagged(const Work &W, const unsigned long long *__restrict_
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ok &= rt_wait(W, ltag + (int64_t)t * MAX_EXPERT + min(lane + 64 * i, NE - 1), tag, v[i]);
-    uint64_t key[4];
+    // DPP maxima and ballots: no cross-lane round trip through LDS
+    uint32_t key[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = (e < NE) ? topk_key(__uint_as_float((uint32_t)v[i]), e) : 0ull;
-    }
+    for (int i = 0; i < 4; ++i) key[i] = lane + 64 * i < NE ? logit_key32(__uint_as_float((uint32_t)v[i])) : 0u;
     const bool bad = __ballot(!ok) != 0ull;
     float sel_L[MAX_TOPK];
     int sel_e[MAX_TOPK];
     for (int j = 0; j < k; ++j) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
-        int e = 0xFFFF - (int)(best & 0xFFFFu);
-        sel_e[j] = e;
-        sel_L[j] = key_logit(best);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (lane + 64 * i == e) key[i] = 0ull;
+        uint32_t m;
+        topk_round(key, m, sel_e[j]);
+        sel_L[j] = key32_logit(m);
     }
     if (lane < k) {
         double m = (double)sel_L[0], z = 0.0, num = 0.0;
@@ -133,25 +124,18 @@ __device__ void topk_tagged(const Work &W, const unsigned long long *__restrict_
 __device__ void topk_token(const float *__restrict__ logits, int t, int NE, int k, int32_t *__restrict__ idx,
                            float *__restrict__ w) {
     const int lane = threadIdx.x & 63;
-    uint64_t key[4];
+    uint32_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        int e = lane + 64 * i;
-        key[i] = (e < NE) ? topk_key(logits[(int64_t)t * NE + e], e) : 0ull;
+        const int e = lane + 64 * i;
+        key[i] = e < NE ? logit_key32(logits[(int64_t)t * NE + e]) : 0u;
     }
     float sel_L[MAX_TOPK];
     int sel_e[MAX_TOPK];
     for (int j = 0; j < k; ++j) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
-        int e = 0xFFFF - (int)(best & 0xFFFFu);
-        sel_e[j] = e;
-        sel_L[j] = key_logit(best);  // no reload: the key holds the logit
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (lane + 64 * i == e) key[i] = 0ull;
+        uint32_t m;
+        topk_round(key, m, sel_e[j]);
+        sel_L[j] = key32_logit(m);  // no reload: the key holds the logit
     }
     if (lane < k) {
         // every lane < k evaluates the common denominator; lane j also its numerator

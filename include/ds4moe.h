@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define DS4MOE_ABI_VERSION 3
+#define DS4MOE_ABI_VERSION 4
 
 enum {
     DS4MOE_OK = 0,
@@ -88,11 +88,19 @@ enum {
 
 /* Kernel path selection for ds4moe_forward (ds4moe_set_path). */
 enum {
-    DS4MOE_PATH_AUTO = 0,    /* one token: fused decode; 2-4 fp32 tokens: GEMV; else grouped MFMA GEMM */
+    DS4MOE_PATH_AUTO = 0,    /* one token: fused decode; 2-4 fp32 tokens: GEMV; 2..DS4MOE_SMALL_MAX_TOKENS
+                                bf16 tokens on a layer that has it: small-batch kernels; else grouped MFMA GEMM */
     DS4MOE_PATH_GEMV = 1,    /* dequant-fused GEMV kernels (decode); n_tok <= 4 only,
                                 else ds4moe_forward returns DS4MOE_EUNSUPPORTED */
-    DS4MOE_PATH_GEMM = 2     /* grouped dequant MFMA GEMM kernels (prefill), any n_tok */
+    DS4MOE_PATH_GEMM = 2,    /* grouped dequant MFMA GEMM kernels (prefill), any n_tok */
+    DS4MOE_PATH_SMALL = 3    /* small-batch kernels: the router, then two persistent MFMA launches that
+                                stream each selected expert once for all of its tokens (speculative
+                                verification batches, "ds4 深度实战...", sections 4.2 and 4.4).  Layers
+                                with bf16 activations, the 2-bit format, n_ff <= 2048 and max_tokens >= 2
+                                (else ds4moe_set_path returns DS4MOE_EUNSUPPORTED); ds4moe_forward takes
+                                2..DS4MOE_SMALL_MAX_TOKENS tokens on it (else DS4MOE_EUNSUPPORTED) */
 };
+#define DS4MOE_SMALL_MAX_TOKENS 8
 
 typedef struct ds4moe ds4moe_t; /* opaque; one per MoE layer */
 
@@ -341,10 +349,11 @@ int ds4moe_cache_slots(ds4moe_t *h, int32_t *slot_expert, void *stream);
  * 5 routed gate/up GEMM, 6 routed down GEMM, 7 fused decode kernel, 8 batched
  * path preparation (activation copies, chunk table), 9 shared gate/up GEMM,
  * 10 shared down GEMM, 11 routed gate/up Q4_K GEMV, 12 routed down Q4_K
- * GEMV, 13 expert cache update and copy.  ms and counts have room for DS4MOE_TIMING_KINDS entries each.
+ * GEMV, 13 expert cache update and copy, 14 small-batch gate/up kernel, 15
+ * small-batch down kernel.  ms and counts have room for DS4MOE_TIMING_KINDS entries each.
  * Enabling resets the counters.
  */
-#define DS4MOE_TIMING_KINDS 14
+#define DS4MOE_TIMING_KINDS 16
 int ds4moe_timing_enable(ds4moe_t *h, int32_t enable);
 int ds4moe_timing_read(ds4moe_t *h, double *ms, int64_t *counts);
 

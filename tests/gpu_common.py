@@ -68,6 +68,8 @@ def host_layer(kind: str):
         lay = synth.Layer(**{**base.__dict__})
         lay.hash_table = synth.hash_table(1, synth.N_VOCAB, base.spec.n_expert, base.spec.top_k)
         return lay
+    if kind == "tiny_noshared":
+        return synth.make_layer(synth.TINY, seed=5, shared=False)
     if kind == "ds4_zipf":
         base = host_layer("ds4")
         lay = synth.Layer(**{**base.__dict__})
@@ -79,15 +81,17 @@ def host_layer(kind: str):
 _dev = {}
 
 
-def device_layer(kind: str, max_tokens: int = 64):
-    """A MoELayer handle (cached per kind and max_tokens)."""
+def device_layer(kind: str, max_tokens: int = 64, act=None):
+    """A MoELayer handle (cached per kind, max_tokens and activation dtype;
+    by default fp32 activations for the tiny kinds, bf16 for the others)."""
     import bit_quantized_moe_renorm_amd as m
-    key = (kind, max_tokens)
+    if act is None:
+        act = m.F32 if kind.startswith("tiny") else m.BF16
+    key = (kind, max_tokens, act)
     if key not in _dev:
         lay = host_layer(kind)
-        log(f"[gpu] create layer {kind} max_tokens={max_tokens}")
+        log(f"[gpu] create layer {kind} max_tokens={max_tokens} act={act}")
         w = m.upload_layer(lay)
-        act = m.F32 if kind.startswith("tiny") else m.BF16
         _dev[key] = m.MoELayer(lay.spec, w, max_tokens=max_tokens, act_dtype=act)
         del w
     return _dev[key]

@@ -64,7 +64,8 @@ def test_gemm_tiny_multi_chunk_experts():
 
 @pytest.mark.parametrize("n", [2, 3, 4, 5, 7, 8, 16, 32])
 def test_gemm_zipf_batches(n):
-    """Decode batches under a Zipf-skewed router bias (AUTO takes the GEMM path for bf16 batches).
+    """Decode batches under a Zipf-skewed router bias, on the GEMM path (AUTO takes the
+    small-batch kernels up to 8 bf16 tokens, the GEMM path beyond).
     2 and 3 tokens split the GEMMs' K range 8 ways, 5 tokens 4 ways, 8 and more not at all
     (routed) while the shared expert still splits.  2..8 tokens are also the shapes of
     speculative (MTP) verification, which scores the last token plus k drafted ones in one
@@ -72,7 +73,7 @@ def test_gemm_zipf_batches(n):
     prediction / speculative decoding); 7 is k = 6."""
     lay = host_layer("ds4_zipf")
     x = synth.activations(2, n, 4096)
-    got = _run(device_layer("ds4_zipf"), x, m.PATH_AUTO)
+    got = _run(device_layer("ds4_zipf"), x, m.PATH_GEMM)
     ref, _, _ = oracle.forward(lay, x)
     err = rel_err(got, ref)
     log(f"[gpu] gemm zipf n={n} rel err {err:.3e}")
