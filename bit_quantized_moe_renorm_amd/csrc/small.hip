@@ -22,8 +22,10 @@
 //     will use: the two buffers alternate, so no buffer is cleared while it
 //     is read.
 // Units are split over the workgroups in contiguous ranges and dealt
-// round-robin to each workgroup's waves; a wave loads its next unit's weights
-// while it computes the current one.  A lane loads a quarter of a row block
+// round-robin to each workgroup's 12 waves; a wave computes each half of a
+// unit while the next half's weights are in flight (two register buffers,
+// three waves per SIMD: measured faster than 8 waves with a ring of four
+// buffers, and than 16 waves with one).  A lane loads a quarter of a row block
 // (IQ2, Q2_K) or 16 bytes of a row part (bf16), so one load instruction reads
 // each 128-byte line only in part and the next few read the rest: weights
 // are read with ordinary loads, which keep the line in L2 for them (a
@@ -40,8 +42,11 @@
 
 namespace ds4 {
 
-constexpr int SB_WAVES = 8;
+constexpr int SB_WAVES = 12;                        // one workgroup per CU, 3 waves per SIMD
 constexpr int SB_THREADS = 64 * SB_WAVES;
+constexpr int SB_XV = (SMALL_MAX_TOK * 4096 / 8 + SB_THREADS - 1) / SB_THREADS;  // x vectors (16 B) per thread at most
+constexpr int SB_HV = (SMALL_MAX_TOK * SMALL_MAX_FF / 8 + SB_THREADS - 1) / SB_THREADS;  // h groups of 8 per thread at most
+static_assert(SB_THREADS % 32 == 0, "a group of 32 lanes covers 32 consecutive vectors");
 constexpr int SB_SLOTS = SMALL_MAX_TOK * MAX_TOPK;  // (token, expert) selections at most
 constexpr int SB_XP = 2 * 4096 + 16;                // x row pitch in LDS, bytes (n_embd <= 4096; 16 B * odd)
 constexpr int SB_HP = 2 * SMALL_MAX_FF + 16;        // routed h row pitch, bytes
@@ -124,24 +129,19 @@ __device__ __forceinline__ void sb_range(int na, int ca, int nb, int cb, int &g0
     g1 = sb_units_below(C * (blockIdx.x + 1) / gridDim.x, na, ca, nb, cb);
 }
 
-// Maximum over each group of 32 consecutive lanes (left in every lane).
-__device__ __forceinline__ float sb_max32(float v) {
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+// Maximum of a non-negative value over each group of 32 consecutive lanes,
+// in the group's last lane (lane 31 or 63), by DPP row shifts and one row
+// broadcast: plain VALU work (no round trip through LDS).  All lanes active.
+__device__ __forceinline__ float sb_max32_last(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true)));  // row_shr:1
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, true)));  // row_shr:2
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, true)));  // row_shr:4
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, true)));  // row_shr:8
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false))); // row_bcast:15
     return v;
 }
 
 // ---------------------------------------------------------------- gate/up
-// One unit's weights for this lane: 16 uint4 (gate slots 0..7, up 8..15) and
-// the gate and up block scales d of the row's 16-byte group holding the
-// unit's blocks (element doff + s for block s; routed units only, shared
-// units load valid unused words there).
-struct SbW {
-    uint4 q[16];
-    uint4 dg, du;
-    int doff;
-};
-
 // 16-bit element j (0..7) of a 16-byte group.
 __device__ __forceinline__ uint32_t sb_u16_of(const uint4 &v, int j) {
     const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
@@ -154,13 +154,26 @@ __device__ __forceinline__ uint32_t sb_u32_of(const uint4 &a, const uint4 &b, in
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// Half h of a unit's weights for this lane: 4 gate uint4 (q[0..3]) and 4 up
+// uint4 (q[4..7]) -- a routed unit's blocks 4 h .. 4 h + 3, a shared unit's
+// steps 4 h .. 4 h + 3 -- and the gate and up block scales d of the row's
+// 16-byte group holding the unit's blocks (element doff + s for block s;
+// routed units only, shared units load valid unused words there).  A wave
+// computes one half while the next one's loads are in flight.
+struct SbW {
+    uint4 q[8];
+    uint4 dg, du;
+    int doff;
+};
+
 // Unit i: i < ns shared (tile i / nbe, 256-K part i % nbe; lane group g of
 // step s holds K 32 s + 8 g of the part, so a load reads 64 contiguous bytes
-// of each row); else routed (slot u, tile, part of bpu blocks).  Every load is issued whatever the unit
-// (addresses are selected, loads are never skipped), so the compiler's waits
-// count the same loads on every path; with `none` every address is the same
-// 16 bytes of the codebook (a cache hit, the values unused).
-__device__ __forceinline__ void sb_gu_load(const Layer &L, const SbRoute &R, int i, int ns, int TG, int pr,
+// of each row); else routed (slot u, tile, part of bpu blocks).  Every load
+// is issued whatever the unit (addresses are selected, loads are never
+// skipped), so the compiler's waits count the same loads on every path; with
+// `none` every address is the same 16 bytes of the codebook (a cache hit, the
+// values unused).
+__device__ __forceinline__ void sb_gu_load(const Layer &L, const SbRoute &R, int i, int h, int ns, int TG, int pr,
                                            int bpu, bool none, SbW &w) {
     const int lane = threadIdx.x & 63, rl = lane & 15, grp = lane >> 4;
     const int E = L.n_embd, F = L.n_ff, nbe = L.nbe;
@@ -194,73 +207,79 @@ __device__ __forceinline__ void sb_gu_load(const Layer &L, const SbRoute &R, int
         qs = 0;
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const int ss = min(s, last);
+    for (int s = 0; s < 4; ++s) {
+        const int ss = min(4 * h + s, last);
         w.q[s] = ld_at<uint4>(q0, ss * qs);
-        w.q[8 + s] = ld_at<uint4>(q1, ss * qs);
+        w.q[4 + s] = ld_at<uint4>(q1, ss * qs);
     }
     w.dg = ld_at<uint4>(d0, 0);
     w.du = ld_at<uint4>(d1, 0);
 }
 
+// Half h of unit i into the gate and up accumulators (16 tokens x 16 rows).
+// Lanes past the unit's tokens read its first token's x: their products land
+// in C rows never stored.
 __device__ __forceinline__ void sb_gu_compute(const Layer &L, const SbRoute &R, const uint4 *T, const uint8_t *xs,
-                                              const float *xsc, int i, int ns, int TG, int pr, int bpu, int n,
-                                              const SbW &w, float *__restrict__ gu) {
+                                              int i, int h, int ns, int TG, int pr, int bpu, int n, const SbW &w,
+                                              floatx4 &ag, floatx4 &au) {
     const int lane = threadIdx.x & 63, rl = lane & 15, grp = lane >> 4;
-    const int F = L.n_ff, k = L.top_k, nbe = L.nbe;
-    // Every step's LDS reads are issued a step ahead of its arithmetic, and
-    // even and odd steps accumulate separately, so neither the LDS latency nor
-    // the MFMA latency chains the steps.  Lanes past the unit's tokens read
-    // its first token's x: their products land in C rows never stored.
-    floatx4 ag[2] = {}, au[2] = {};
+    const int k = L.top_k, nbe = L.nbe;
     if (i < ns) {
-        const int tile = i / nbe, part = i - tile * nbe, f = 16 * tile + rl;
-        const uint8_t *xr = xs + (rl < n ? rl : 0) * SB_XP + 2 * (256 * part + 8 * grp);
-        half8 a = *reinterpret_cast<const half8 *>(xr);
+        const int tile = i / nbe, part = i - tile * nbe;
+        const uint8_t *xr = xs + (rl < n ? rl : 0) * SB_XP + 2 * (256 * part + 8 * grp) + 256 * h;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const half8 a = *reinterpret_cast<const half8 *>(xr + 64 * s);
+            ag = mfma_f16(a, sb_bf16_to_half8(w.q[s]), ag);
+            au = mfma_f16(a, sb_bf16_to_half8(w.q[4 + s]), au);
+        }
+        return;
+    }
+    const int r = i - ns, per = TG * pr;
+    const int u = r / per, part = (r - u * per) % pr;
+    const int beg = R.beg[u], cnt = R.cnt[u];
+    const int tq = R.lst[beg + (rl < cnt ? rl : 0)] / k;
+    const uint8_t *xr = xs + tq * SB_XP + 2 * (256 * part * bpu + 64 * grp);
+    half2v sg, su;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int b = 4 * h + s;  // block of the unit
+        if (b >= bpu) break;
+        const uint32_t dgb = sb_u16_of(w.dg, w.doff + b), dub = sb_u16_of(w.du, w.doff + b);
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
-            const half8 a1 = *reinterpret_cast<const half8 *>(xr + 64 * min(cc + 1, 7));
-            ag[cc & 1] = mfma_f16(a, sb_bf16_to_half8(w.q[cc]), ag[cc & 1]);
-            au[cc & 1] = mfma_f16(a, sb_bf16_to_half8(w.q[8 + cc]), au[cc & 1]);
-            a = a1;
+            const uint4 lg = iq2_b_lookup(T, w.q[s], cc, rl), lu = iq2_b_lookup(T, w.q[4 + s], cc, rl);
+            const half8 a = *reinterpret_cast<const half8 *>(xr + 512 * b + 16 * cc);
+            const half8 bg = iq2_b_finish(lg, w.q[s], (uint16_t)dgb, cc, sg);
+            const half8 bu = iq2_b_finish(lu, w.q[4 + s], (uint16_t)dub, cc, su);
+            ag = mfma_f16(a, bg, ag);
+            au = mfma_f16(a, bu, au);
         }
-        const floatx4 g4 = ag[0] + ag[1], u4 = au[0] + au[1];
+    }
+}
+
+// Unit i's sums, times the x scales, added into the buffer.
+__device__ __forceinline__ void sb_gu_store(const Layer &L, const SbRoute &R, const float *xsc, int i, int ns,
+                                            int TG, int pr, int n, const floatx4 &ag, const floatx4 &au,
+                                            float *__restrict__ gu) {
+    const int lane = threadIdx.x & 63, rl = lane & 15, grp = lane >> 4;
+    const int F = L.n_ff, k = L.top_k, nbe = L.nbe;
+    if (i < ns) {
+        const int f = 16 * (i / nbe) + rl;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int t = 4 * grp + v;
             if (t < n) {
                 float *row = gu + (int64_t)(SMALL_MAX_TOK * k + t) * 2 * F + f;
-                atomicAdd(row, g4[v] * xsc[t]);
-                atomicAdd(row + F, u4[v] * xsc[t]);
+                atomicAdd(row, ag[v] * xsc[t]);
+                atomicAdd(row + F, au[v] * xsc[t]);
             }
         }
         return;
     }
     const int r = i - ns, per = TG * pr;
-    const int u = r / per, rem = r - u * per, tile = rem / pr, part = rem - tile * pr, f = 16 * tile + rl;
+    const int u = r / per, f = 16 * ((r - u * per) / pr) + rl;
     const int beg = R.beg[u], cnt = R.cnt[u];
-    const int tq = R.lst[beg + (rl < cnt ? rl : 0)] / k;
-    const uint8_t *xr = xs + tq * SB_XP + 2 * (256 * part * bpu + 64 * grp);
-    // step st = 8 s + cc: block s of the unit, step cc of the block.  Past the
-    // unit's last step the look-ahead reads block 7 (registers holding a
-    // clamped copy) and x within the row: in range, unused.
-    uint4 lg = iq2_b_lookup(T, w.q[0], 0, rl), lu = iq2_b_lookup(T, w.q[8], 0, rl);
-    half8 a = *reinterpret_cast<const half8 *>(xr);
-    half2v sg, su;
-#pragma unroll
-    for (int st = 0; st < 64; ++st) {
-        const int s = st >> 3, cc = st & 7;
-        if (s >= bpu) break;
-        const int sn = min((st + 1) >> 3, 7), cn = (st + 1) & 7;
-        const uint4 lg1 = iq2_b_lookup(T, w.q[sn], cn, rl), lu1 = iq2_b_lookup(T, w.q[8 + sn], cn, rl);
-        const half8 a1 = *reinterpret_cast<const half8 *>(xr + 512 * sn + 16 * cn);
-        const half8 bg = iq2_b_finish(lg, w.q[s], (uint16_t)sb_u16_of(w.dg, w.doff + s), cc, sg);
-        const half8 bu = iq2_b_finish(lu, w.q[8 + s], (uint16_t)sb_u16_of(w.du, w.doff + s), cc, su);
-        ag[cc & 1] = mfma_f16(a, bg, ag[cc & 1]);
-        au[cc & 1] = mfma_f16(a, bu, au[cc & 1]);
-        lg = lg1, lu = lu1, a = a1;
-    }
-    const floatx4 g4 = ag[0] + ag[1], u4 = au[0] + au[1];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int ii = 4 * grp + v;
@@ -268,8 +287,8 @@ __device__ __forceinline__ void sb_gu_compute(const Layer &L, const SbRoute &R, 
             const int q = R.lst[beg + ii];
             const float sc = xsc[q / k];
             float *row = gu + (int64_t)q * 2 * F + f;
-            atomicAdd(row, g4[v] * sc);
-            atomicAdd(row + F, u4[v] * sc);
+            atomicAdd(row, ag[v] * sc);
+            atomicAdd(row + F, au[v] * sc);
         }
     }
 }
@@ -287,11 +306,11 @@ __global__ __launch_bounds__(SB_THREADS, 1) void k_small_gateup(Layer L, Work W,
     const int E = L.n_embd, F = L.n_ff, nbe = L.nbe;
     const int e8 = E >> 3, nv = n * e8;  // 16-byte vectors of x per token, in all
     // x and the codebook first (the thread's vectors tid + SB_THREADS j of x:
-    // n E / 8 <= 8 SB_THREADS)
+    // n E / 8 <= SB_XV SB_THREADS)
     const uint32_t cbw = tid < 256 ? L.codebook[tid] : 0u;
-    uint4 xr[SMALL_MAX_TOK];
+    uint4 xr[SB_XV];
 #pragma unroll
-    for (int j = 0; j < SMALL_MAX_TOK; ++j) {
+    for (int j = 0; j < SB_XV; ++j) {
         const int i = min(tid + SB_THREADS * j, nv - 1);
         xr[j] = *reinterpret_cast<const uint4 *>(x + 8 * (int64_t)i);
     }
@@ -303,11 +322,12 @@ __global__ __launch_bounds__(SB_THREADS, 1) void k_small_gateup(Layer L, Work W,
     int g0, g1;
     sb_range(ns, SB_GU_COST_SHARED, R.U * TG * pr, SB_GU_COST_ROUTED, g0, g1);
     int i = g0 + wave;
+    // the first half unit's weights stream while x and the table are staged
     SbW wa, wb;
-    sb_gu_load(L, R, i, ns, TG, pr, bpu, i >= g1, wa);
+    sb_gu_load(L, R, i, 0, ns, TG, pr, bpu, i >= g1, wa);
     // per-token maxima of |x| (32 consecutive vectors always belong to one token)
 #pragma unroll
-    for (int j = 0; j < SMALL_MAX_TOK; ++j) {
+    for (int j = 0; j < SB_XV; ++j) {
         const int iv = tid + SB_THREADS * j;
         if (SB_THREADS * j >= nv) break;
         const uint32_t a[4] = {xr[j].x, xr[j].y, xr[j].z, xr[j].w};
@@ -315,14 +335,14 @@ __global__ __launch_bounds__(SB_THREADS, 1) void k_small_gateup(Layer L, Work W,
 #pragma unroll
         for (int q = 0; q < 4; ++q) m = fmaxf(m, fmaxf(fabsf(bf16_to_f32((uint16_t)(a[q] & 0xFFFFu))),
                                                       fabsf(bf16_to_f32((uint16_t)(a[q] >> 16)))));
-        m = sb_max32(m);
-        if (iv < nv && (tid & 31) == 0) atomicMax(&xmax[iv / e8], __float_as_uint(m));
+        m = sb_max32_last(m);
+        if (iv < nv && (tid & 31) == 31) atomicMax(&xmax[iv / e8], __float_as_uint(m));
     }
     if (tid < 256) iq2_lut_entry<true>(T, tid, cbw);
     __syncthreads();
     if (tid < n) xsc[tid] = sb_pow2(sb_scale_exp(__uint_as_float(xmax[tid])));
 #pragma unroll
-    for (int j = 0; j < SMALL_MAX_TOK; ++j) {
+    for (int j = 0; j < SB_XV; ++j) {
         const int iv = tid + SB_THREADS * j;
         if (SB_THREADS * j >= nv) break;
         if (iv < nv) {
@@ -339,23 +359,27 @@ __global__ __launch_bounds__(SB_THREADS, 1) void k_small_gateup(Layer L, Work W,
         }
     }
     __syncthreads();
-    // the wave's units i, i + SB_WAVES, ..: the next unit's weights are in
-    // flight while the current one is computed (one call site of each, so the
-    // loop's code stays small; the copy waits for the next unit's loads).
+    // the wave's units i, i + SB_WAVES, .., by halves in two named buffers:
+    // each half is computed while the next one's loads are in flight
     for (; i < g1; i += SB_WAVES) {
-        sb_gu_load(L, R, i + SB_WAVES, ns, TG, pr, bpu, i + SB_WAVES >= g1, wb);
-        sb_gu_compute(L, R, T, xs, xsc, i, ns, TG, pr, bpu, n, wa, gu);
-        wa = wb;
+        sb_gu_load(L, R, i, 1, ns, TG, pr, bpu, false, wb);
+        floatx4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+        sb_gu_compute(L, R, T, xs, i, 0, ns, TG, pr, bpu, n, wa, ag, au);
+        const int nx = i + SB_WAVES;
+        sb_gu_load(L, R, nx, 0, ns, TG, pr, bpu, nx >= g1, wa);
+        sb_gu_compute(L, R, T, xs, i, 1, ns, TG, pr, bpu, n, wb, ag, au);
+        sb_gu_store(L, R, xsc, i, ns, TG, pr, n, ag, au, gu);
     }
 }
 
 // ---------------------------------------------------------------- down
-// One unit's weights for this lane: routed, per 256-K block b (nbf <= 8) the
-// lane's 16 qs bytes, 4 scale bytes and d | dmin; shared, per step the 8 bf16
-// weights (scales: valid unused words).
+// Half h of a unit's weights for this lane: routed, per 256-K block b = 4 h
+// .. 4 h + 3 (nbf <= 8) the lane's 16 qs bytes and 4 scale bytes, and the
+// row's words d | dmin; shared, per step 4 h .. 4 h + 3 the 8 bf16 weights
+// (scales: valid unused words).
 struct SbDW {
-    uint4 q[8];
-    uint32_t sc[8];
+    uint4 q[4];
+    uint32_t sc[4];
     uint4 dd0, dd1;  // d | dmin of the row's blocks: element doff + b of the two 16-byte groups
     int doff;
 };
@@ -363,8 +387,8 @@ struct SbDW {
 // Unit i: i < nr routed (slot i / TE, tile i % TE: 16 rows of n_embd, all of
 // n_ff); else shared, 256-K part major (part j / TE, tile j % TE, j = i - nr;
 // K as for the shared gate/up); `none` as for sb_gu_load.
-__device__ __forceinline__ void sb_dn_load(const Layer &L, const SbRoute &R, int i, int nr, int TE, bool none,
-                                           SbDW &w) {
+__device__ __forceinline__ void sb_dn_load(const Layer &L, const SbRoute &R, int i, int h, int nr, int TE,
+                                           bool none, SbDW &w) {
     const int lane = threadIdx.x & 63, rl = lane & 15, grp = lane >> 4;
     const int E = L.n_embd, F = L.n_ff, nbf = L.nbf;
     const uint8_t *q0, *s0, *d0, *d1;
@@ -394,8 +418,8 @@ __device__ __forceinline__ void sb_dn_load(const Layer &L, const SbRoute &R, int
         qs = ss = 0;
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const int b = min(s, last);
+    for (int s = 0; s < 4; ++s) {
+        const int b = min(4 * h + s, last);
         w.q[s] = ld_at<uint4>(q0, b * qs);
         w.sc[s] = ld_at<uint32_t>(s0, b * ss);
     }
@@ -403,91 +427,119 @@ __device__ __forceinline__ void sb_dn_load(const Layer &L, const SbRoute &R, int
     w.dd1 = ld_at<uint4>(d1, 0);
 }
 
+// Half h of unit i into the accumulator (16 tokens x 16 rows).
 __device__ __forceinline__ void sb_dn_compute(const Layer &L, const SbRoute &R, const uint2 *QT, const uint8_t *hr,
-                                              const float *hsc, int u0, const uint8_t *hsh, const float *shsc,
-                                              int kp0, int i, int nr, int TE, int n, const SbDW &w,
-                                              float *__restrict__ out) {
+                                              int u0, const uint8_t *hsh, int kp0, int i, int h, int nr, int TE,
+                                              int n, const SbDW &w, floatx4 &acc) {
     const int lane = threadIdx.x & 63, rl = lane & 15, grp = lane >> 4;
-    const int E = L.n_embd, k = L.top_k, nbf = L.nbf;
-    // LDS reads a step ahead and two accumulators, as in sb_gu_compute
-    floatx4 acc[2] = {};
+    const int nbf = L.nbf;
     if (i >= nr) {
-        const int j = i - nr, part = j / TE, tile = j - part * TE, row = 16 * tile + rl;
-        const uint8_t *hp = hsh + (rl < n ? rl : 0) * SB_SP + 2 * (256 * (part - kp0) + 8 * grp);
-        half8 a = *reinterpret_cast<const half8 *>(hp);
+        const int j = i - nr, part = j / TE;
+        const uint8_t *hp = hsh + (rl < n ? rl : 0) * SB_SP + 2 * (256 * (part - kp0) + 8 * grp) + 256 * h;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            acc = mfma_f16(*reinterpret_cast<const half8 *>(hp + 64 * s), sb_bf16_to_half8(w.q[s]), acc);
+        return;
+    }
+    const int u = i / TE, su = u - u0, cnt = R.cnt[u];
+    const uint8_t *hp = hr + (su * SMALL_MAX_TOK + (rl < cnt ? rl : 0)) * SB_HP + 2 * 64 * grp;
+    half8 dsc, msc;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int b = 4 * h + s;  // block of the row
+        if (b >= nbf) break;
+        const uint32_t ddb = sb_u32_of(w.dd0, w.dd1, w.doff + b);
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
-            const half8 a1 = *reinterpret_cast<const half8 *>(hp + 64 * min(cc + 1, 7));
-            acc[cc & 1] = mfma_f16(a, sb_bf16_to_half8(w.q[cc]), acc[cc & 1]);
-            a = a1;
+            const uint4 qv = q2k_b_lookup(QT, w.q[s], cc, rl);
+            const half8 a = *reinterpret_cast<const half8 *>(hp + 512 * b + 16 * cc);
+            acc = mfma_f16(a, q2k_b_finish(qv, w.sc[s], ddb, cc, dsc, msc), acc);
         }
-        const floatx4 y4 = acc[0] + acc[1];
+    }
+}
+
+// Unit i's rows, times the routing weight and the h scales, added into out.
+__device__ __forceinline__ void sb_dn_store(const Layer &L, const SbRoute &R, const float *hsc, int u0,
+                                            const float *shsc, int i, int nr, int TE, int n, const floatx4 &acc,
+                                            float *__restrict__ out) {
+    const int lane = threadIdx.x & 63, rl = lane & 15, grp = lane >> 4;
+    const int E = L.n_embd, k = L.top_k;
+    if (i >= nr) {
+        const int row = 16 * ((i - nr) % TE) + rl;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int t = 4 * grp + v;
-            if (t < n) atomicAdd(out + (int64_t)t * E + row, y4[v] * shsc[t]);
+            if (t < n) atomicAdd(out + (int64_t)t * E + row, acc[v] * shsc[t]);
         }
         return;
     }
-    const int u = i / TE, tile = i - u * TE, row = 16 * tile + rl, su = u - u0;
+    const int u = i / TE, row = 16 * (i - u * TE) + rl, su = u - u0;
     const int beg = R.beg[u], cnt = R.cnt[u];
-    const uint8_t *hp = hr + (su * SMALL_MAX_TOK + (rl < cnt ? rl : 0)) * SB_HP + 2 * 64 * grp;
-    uint4 qv = q2k_b_lookup(QT, w.q[0], 0, rl);
-    half8 a = *reinterpret_cast<const half8 *>(hp);
-    half8 dsc, msc;
-#pragma unroll
-    for (int st = 0; st < 64; ++st) {
-        const int b = st >> 3, cc = st & 7;
-        if (b >= nbf) break;
-        const int bn = min((st + 1) >> 3, 7), cn = (st + 1) & 7;
-        const uint4 qv1 = q2k_b_lookup(QT, w.q[bn], cn, rl);
-        const half8 a1 = *reinterpret_cast<const half8 *>(hp + 512 * bn + 16 * cn);
-        const half8 bw = q2k_b_finish(qv, w.sc[b], sb_u32_of(w.dd0, w.dd1, w.doff + b), cc, dsc, msc);
-        acc[cc & 1] = mfma_f16(a, bw, acc[cc & 1]);
-        qv = qv1, a = a1;
-    }
-    const floatx4 y4 = acc[0] + acc[1];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int ii = 4 * grp + v;
         if (ii < cnt) {
             const int q = R.lst[beg + ii];
-            atomicAdd(out + (int64_t)(q / k) * E + row, R.wq[q] * y4[v] * hsc[su * SMALL_MAX_TOK + ii]);
+            atomicAdd(out + (int64_t)(q / k) * E + row, R.wq[q] * acc[v] * hsc[su * SMALL_MAX_TOK + ii]);
         }
     }
 }
 
-// Stage h = SiLU(g) u of `rows` sum rows (row r at gu + src[r] 2 F, K range
-// [k0, k0 + nk)) into LDS as fp16 under a power-of-two scale per row: dst row
-// r at dst + r * pitch, its scale (2^e, undoing the staging's 2^-e) in sc[r].
-// nk is a multiple of 256 and rows * nk <= SB_THREADS * 32.
-__device__ void sb_stage_h(const float *__restrict__ gu, int F, const int *src, int rows, int k0, int nk,
-                           uint8_t *dst, int pitch, float *sc, uint32_t *hmax) {
-    const int tid = threadIdx.x, n8 = nk >> 3, nv = rows * n8;  // groups of 8 values
-    float h[4][8];
+// Staging of h = SiLU(g) u for `rows` rows of sums (row r of slot u's list,
+// or row SMALL_MAX_TOK k + r, the shared expert of token r, when u < 0), K
+// range [k0, k0 + nk), into LDS as fp16 under a power-of-two scale per row:
+// dst row r at dst + r * pitch, its scale (2^e, undoing the staging's 2^-e)
+// in sc[r].  nk is a multiple of 256 and rows * nk <= SB_THREADS * 8 SB_HV.
+// In two parts: sb_stage_issue loads the thread's sums (so other loads can
+// be issued behind them), sb_stage_finish forms h, takes the per-row maxima
+// (hmax, zero on entry) and stores.
+struct SbStage {
+    float4 g[SB_HV][2], u[SB_HV][2];
+};
+__device__ __forceinline__ void sb_stage_issue(const float *__restrict__ gu, int F, const SbRoute &R, int u, int k,
+                                               int rows, int k0, int nk, SbStage &st) {
+    const int tid = threadIdx.x, n8 = nk >> 3;  // groups of 8 values per row
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < SB_HV; ++j) {
+        if (SB_THREADS * j >= rows * n8) break;  // uniform
+        // past the last group: the last row again (in range, unused)
+        const int iv = tid + SB_THREADS * j, r = min(iv / n8, rows - 1), c = 8 * (iv - (iv / n8) * n8);
+        const int src = u >= 0 ? R.lst[R.beg[u] + r] : SMALL_MAX_TOK * k + r;
+        const float *p = gu + (int64_t)src * 2 * F + k0 + min(c, nk - 8);
+        st.g[j][0] = *reinterpret_cast<const float4 *>(p);
+        st.g[j][1] = *reinterpret_cast<const float4 *>(p + 4);
+        st.u[j][0] = *reinterpret_cast<const float4 *>(p + F);
+        st.u[j][1] = *reinterpret_cast<const float4 *>(p + F + 4);
+    }
+}
+__device__ void sb_stage_finish(int rows, int nk, const SbStage &st, uint8_t *dst, int pitch, float *sc,
+                                uint32_t *hmax) {
+    const int tid = threadIdx.x, n8 = nk >> 3, nv = rows * n8;
+    float h[SB_HV][8];
+#pragma unroll
+    for (int j = 0; j < SB_HV; ++j) {
+        if (SB_THREADS * j >= nv) break;  // uniform, as in sb_stage_issue
         const int iv = tid + SB_THREADS * j;
-        const int r = min(iv / n8, rows - 1), c = 8 * (iv - (iv / n8) * n8);
-        const float *g = gu + (int64_t)src[r] * 2 * F + k0 + min(c, nk - 8);
-        const float4 g0 = *reinterpret_cast<const float4 *>(g), g1 = *reinterpret_cast<const float4 *>(g + 4);
-        const float4 u0 = *reinterpret_cast<const float4 *>(g + F), u1 = *reinterpret_cast<const float4 *>(g + F + 4);
-        h[j][0] = silu(g0.x) * u0.x, h[j][1] = silu(g0.y) * u0.y, h[j][2] = silu(g0.z) * u0.z;
-        h[j][3] = silu(g0.w) * u0.w, h[j][4] = silu(g1.x) * u1.x, h[j][5] = silu(g1.y) * u1.y;
-        h[j][6] = silu(g1.z) * u1.z, h[j][7] = silu(g1.w) * u1.w;
+        const float g[8] = {st.g[j][0].x, st.g[j][0].y, st.g[j][0].z, st.g[j][0].w,
+                            st.g[j][1].x, st.g[j][1].y, st.g[j][1].z, st.g[j][1].w};
+        const float u[8] = {st.u[j][0].x, st.u[j][0].y, st.u[j][0].z, st.u[j][0].w,
+                            st.u[j][1].x, st.u[j][1].y, st.u[j][1].z, st.u[j][1].w};
         float m = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(h[j][q]));
+        for (int q = 0; q < 8; ++q) {
+            h[j][q] = silu(g[q]) * u[q];
+            m = fmaxf(m, fabsf(h[j][q]));
+        }
         // 32 consecutive groups (256 values) always belong to one row
-        m = sb_max32(m);
-        if (SB_THREADS * j < nv && iv < nv && (tid & 31) == 0) atomicMax(&hmax[iv / n8], __float_as_uint(m));
+        m = sb_max32_last(m);
+        if (iv < nv && (tid & 31) == 31) atomicMax(&hmax[iv / n8], __float_as_uint(m));
     }
     __syncthreads();
     if (tid < rows) sc[tid] = sb_pow2(sb_scale_exp(__uint_as_float(hmax[tid])));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < SB_HV; ++j) {
         const int iv = tid + SB_THREADS * j;
-        if (iv < nv) {
+        if (SB_THREADS * j < nv && iv < nv) {
             const int r = iv / n8, c = 8 * (iv - r * n8);
             const float down = sb_pow2(-sb_scale_exp(__uint_as_float(hmax[r])));
             half8 o;
@@ -508,8 +560,7 @@ __global__ __launch_bounds__(SB_THREADS, 1) void k_small_down(Layer L, Work W, c
     __shared__ __align__(16) uint8_t hsh[SMALL_MAX_TOK * SB_SP];
     __shared__ SbRoute R;
     __shared__ int offs[MAX_EXPERT + 1];
-    __shared__ int src[2 * SMALL_MAX_TOK];
-    __shared__ uint32_t hmax[2 * SMALL_MAX_TOK];
+    __shared__ uint32_t hmax[3 * SMALL_MAX_TOK];  // per-row maxima: routed slots u0, u0 + 1, shared
     __shared__ float hsc[2 * SMALL_MAX_TOK], shsc[SMALL_MAX_TOK];
     const int tid = threadIdx.x, wave = tid >> 6;
     const int E = L.n_embd, F = L.n_ff, k = L.top_k;
@@ -520,40 +571,53 @@ __global__ __launch_bounds__(SB_THREADS, 1) void k_small_down(Layer L, Work W, c
         const int z1 = (int)((int64_t)(zn >> 2) * (blockIdx.x + 1) / gridDim.x);
         for (int z = z0 + tid; z < z1; z += SB_THREADS) reinterpret_cast<float4 *>(gz)[z] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    if (tid < 3 * SMALL_MAX_TOK) hmax[tid] = 0u;
     sb_read_route(L, W, n, R, offs);
     const int TE = E >> 4, U = R.U;
     const int nr = U * TE, ns = L.n_shared ? TE * (F >> 8) : 0;
     int g0, g1;
     sb_range(nr, SB_DN_COST_ROUTED, ns, SB_DN_COST_SHARED, g0, g1);
     int i = g0 + wave;
-    SbDW wa, wb;
-    sb_dn_load(L, R, i, nr, TE, i >= g1, wa);
-    q2k_build_table(QT, tid, SB_THREADS);
     // the routed slots (at most two: a range is shorter than a slot's units,
     // which the grid size guarantees) and the shared K parts (at most two) of
-    // this workgroup's units
+    // this workgroup's units, whose h vectors are staged
     const int u0 = g0 < nr ? g0 / TE : 0, u1 = g0 < nr ? (min(g1, nr) - 1) / TE : -1;
     const int kp0 = g1 > nr ? (max(g0, nr) - nr) / TE : 0, kp1 = g1 > nr ? (g1 - 1 - nr) / TE : -1;
-    if (tid < 2 * SMALL_MAX_TOK) hmax[tid] = 0u;
-    for (int u = u0; u <= u1 && g0 < g1; ++u) {
-        const int s = u - u0;
-        if (tid < R.cnt[u]) src[tid] = R.lst[R.beg[u] + tid];
-        __syncthreads();
-        sb_stage_h(gu, F, src, R.cnt[u], 0, F, hr + s * SMALL_MAX_TOK * SB_HP, SB_HP, hsc + s * SMALL_MAX_TOK,
-                   hmax + s * SMALL_MAX_TOK);
-        __syncthreads();
+    const bool rt = g0 < g1 && u1 >= u0, sh = g0 < g1 && kp1 >= kp0;
+    const int shk0 = 256 * kp0, shnk = 256 * (kp1 - kp0 + 1);
+    // the h vectors are staged before the first unit's weights are requested:
+    // behind every CU's weight requests the sums would take several times as
+    // long to arrive
+    SbStage st;
+    q2k_build_table(QT, tid, SB_THREADS);
+    if (rt) {
+        sb_stage_issue(gu, F, R, u0, k, R.cnt[u0], 0, F, st);
+        sb_stage_finish(R.cnt[u0], F, st, hr, SB_HP, hsc, hmax);
+    } else if (sh) {
+        sb_stage_issue(gu, F, R, -1, k, n, shk0, shnk, st);
+        sb_stage_finish(n, shnk, st, hsh, SB_SP, shsc, hmax + 2 * SMALL_MAX_TOK);
     }
-    if (kp1 >= kp0 && g0 < g1) {
-        if (tid < SMALL_MAX_TOK) hmax[tid] = 0u, src[tid] = SMALL_MAX_TOK * k + tid;
-        __syncthreads();
-        sb_stage_h(gu, F, src, n, 256 * kp0, 256 * (kp1 - kp0 + 1), hsh, SB_SP, shsc, hmax);
+    if (rt && u1 > u0) {
+        sb_stage_issue(gu, F, R, u1, k, R.cnt[u1], 0, F, st);
+        sb_stage_finish(R.cnt[u1], F, st, hr + SMALL_MAX_TOK * SB_HP, SB_HP, hsc + SMALL_MAX_TOK,
+                        hmax + SMALL_MAX_TOK);
     }
+    if (rt && sh) {
+        sb_stage_issue(gu, F, R, -1, k, n, shk0, shnk, st);
+        sb_stage_finish(n, shnk, st, hsh, SB_SP, shsc, hmax + 2 * SMALL_MAX_TOK);
+    }
+    SbDW wa, wb;
+    sb_dn_load(L, R, i, 0, nr, TE, i >= g1, wa);
     __syncthreads();
-    // the wave's units, pipelined as in k_small_gateup
+    // the wave's units by halves, as in k_small_gateup
     for (; i < g1; i += SB_WAVES) {
-        sb_dn_load(L, R, i + SB_WAVES, nr, TE, i + SB_WAVES >= g1, wb);
-        sb_dn_compute(L, R, QT, hr, hsc, u0, hsh, shsc, kp0, i, nr, TE, n, wa, out);
-        wa = wb;
+        sb_dn_load(L, R, i, 1, nr, TE, false, wb);
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        sb_dn_compute(L, R, QT, hr, u0, hsh, kp0, i, 0, nr, TE, n, wa, acc);
+        const int nx = i + SB_WAVES;
+        sb_dn_load(L, R, nx, 0, nr, TE, nx >= g1, wa);
+        sb_dn_compute(L, R, QT, hr, u0, hsh, kp0, i, 1, nr, TE, n, wb, acc);
+        sb_dn_store(L, R, hsc, u0, shsc, i, nr, TE, n, acc, out);
     }
 }
 
