@@ -237,9 +237,11 @@ hipError_t launch_dequant_q2k(const Layer &L, int expert, float *dst, hipStream_
 
 hipError_t launch_router_prep(const float *router, int NE, int E, uint16_t *hml, float *norm, hipStream_t s);
 // ep: this handle's count of routing launches so far (the small-batch router's
-// hand-off tag is ep + 1, never 0)
+// hand-off tag is ep + 1, never 0).  lists = false: up to 64 tokens of a
+// learned layer, the per-expert lists are not built (the small-batch kernels
+// build them from W.idx); otherwise W holds the lists too.
 hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s,
-                        unsigned long long ep);
+                        unsigned long long ep, bool lists = true);
 // The shared expert of large bf16 calls on hipBLASLt (shared_blas.hip):
 // gate/up GEMM + SiLU split into W.hsh_hi / hsh_lo, then the down GEMMs
 // into out.  Requires sh_up == sh_gate + n_ff * n_embd.

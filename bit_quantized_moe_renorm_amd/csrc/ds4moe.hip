@@ -720,9 +720,9 @@ static int run_small(ds4moe *h, const Work &W, const void *x, int n, float *out,
     return DS4MOE_OK;
 }
 
-static int run_route(ds4moe *h, const Work &W, const void *x, int n, hipStream_t s) {
+static int run_route(ds4moe *h, const Work &W, const void *x, int n, hipStream_t s, bool lists = true) {
     int tb = h->tbegin(TK_ROUTE, s);
-    int rc = check_launch(h, launch_route(h->L, W, x, n, s, h->route_calls++), "route");
+    int rc = check_launch(h, launch_route(h->L, W, x, n, s, h->route_calls++, lists), "route");
     h->tend(tb, s);
     return rc;
 }
@@ -835,7 +835,8 @@ static int forward_impl(ds4moe_t *h, const void *x, const int32_t *ids, int32_t 
         h->tend(tf, s);
         return rc;
     }
-    if ((rc = run_route(h, W, x, n_tok, s))) return rc;
+    // the small-batch kernels build the per-expert lists themselves
+    if ((rc = run_route(h, W, x, n_tok, s, path != DS4MOE_PATH_SMALL))) return rc;
     return path == DS4MOE_PATH_GEMV    ? run_gemv(h, W, x, n_tok, out, s)
            : path == DS4MOE_PATH_SMALL ? run_small(h, W, x, n_tok, out, s)
                                        : run_gemm(h, W, x, n_tok, out, s);

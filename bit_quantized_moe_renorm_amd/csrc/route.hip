@@ -214,7 +214,9 @@ __device__ void bucket_small(const unsigned long long *__restrict__ itag, uint32
 // token, chunks past the quarter re-read its first; neither is summed), and
 // the quarters are added in order by wave 0.
 // With fuse_tail, the last workgroup of each token tile takes the tile's top-k,
-// and the last of those builds the per-expert lists.
+// and (fuse_tail 1) the last of those builds the per-expert lists; with
+// fuse_tail 2 the lists are left to the kernels that follow (the small-batch
+// kernels build them from the selections).
 constexpr int RT_KCH = 4;  // 256-value chunks per wave at most
 template <bool XBF16, int TT>
 __global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ R, const float *__restrict__ bias,
@@ -282,6 +284,10 @@ __global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ 
     if (!last) return;
     for (int t = t0 + wave; t < t0 + nt; t += RT_WAVES) topk_tagged(W, W.ltag, t, NE, k, tag, W.idx, W.w, W.itag);
     __syncthreads();
+    if (fuse_tail == 2) {
+        if (threadIdx.x == 0) W.counters[1 + blockIdx.y] = 0;
+        return;
+    }
     if (threadIdx.x == 0) {
         W.counters[1 + blockIdx.y] = 0;
         last = atomicAdd(&W.counters[0], 1) == (int)gridDim.y - 1;
@@ -801,7 +807,7 @@ __global__ __launch_bounds__(256) void k_route_hashed(const float *__restrict__ 
 }
 
 hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok, hipStream_t s,
-                        unsigned long long ep) {
+                        unsigned long long ep, bool lists) {
     const uint32_t tag = (uint32_t)(ep % 0xFFFFFFFFull) + 1u;
     const int NE = L.n_expert;
     if (L.hash_table) {
@@ -825,12 +831,14 @@ hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok,
         hipLaunchKernelGGL(k_fill_lists, dim3(NE), dim3(256), 0, s, n_tok, NE, L.top_k, W);
         return hipGetLastError();
     }
-    const int fuse = n_tok <= ROUTE_SMALL_MAX;
-    // token tiles of 1, 2, 4 or 8 for calls of up to 8 tokens (a larger tile
-    // would load and multiply clamped copies of the last token), and 8 up to
-    // 64 tokens too: the 16-token tile takes 252 VGPRs (2 waves per SIMD), and
-    // 8-token tiles measured 44 -> 33 us at 16 tokens, 52 -> 47 at 32
-    const int tt = n_tok == 1 ? 1 : n_tok == 2 ? 2 : n_tok <= 4 ? 4 : fuse ? 8 : RT_TOK;
+    const int fuse = n_tok <= ROUTE_SMALL_MAX ? (lists ? 1 : 2) : 0;
+    // token tiles of 1, 2 or 4 for calls of up to 8 tokens (a larger tile
+    // would load and multiply clamped copies of the last token; 4-token tiles
+    // at 5..8 tokens let two tiles' last workgroups take the top-k side by
+    // side), and 8 up to 64 tokens: the 16-token tile takes 252 VGPRs (2 waves
+    // per SIMD), and 8-token tiles measured 44 -> 33 us at 16 tokens, 52 -> 47
+    // at 32
+    const int tt = n_tok == 1 ? 1 : n_tok == 2 ? 2 : n_tok <= 8 ? 4 : fuse ? 8 : RT_TOK;
     const dim3 grid(NE, (n_tok + tt - 1) / tt);
     const bool bf = L.act_dtype == 1;
 #define DS4_ROUTE_LAUNCH(T)                                                                                   \

@@ -53,32 +53,77 @@ constexpr int SB_HP = 2 * SMALL_MAX_FF + 16;        // routed h row pitch, bytes
 constexpr int SB_SHK = 512;                         // shared down: K values of h staged (two 256-K parts)
 constexpr int SB_SP = 2 * SB_SHK + 16;              // shared h row pitch, bytes
 
-// The call's routing (written by the router kernel earlier on the stream):
-// active expert u = e[u], in weight slot wslot[u], with cnt[u] selections at
-// list positions beg[u].. (entries t k + j, ascending t); wq[q] is the
-// renormalised weight of selection q = t k + j.
+// The call's routing, built from the selections the router kernel wrote
+// earlier on the stream (W.idx, W.w: expert and weight of selection q = t k +
+// j): active expert u = e[u] (ascending), in weight slot wslot[u], with cnt[u]
+// selections at list positions beg[u].. (entries q, ascending t); wq[q] is
+// selection q's renormalised weight.
 struct SbRoute {
     int U;
     int e[SB_SLOTS], wslot[SB_SLOTS], beg[SB_SLOTS], cnt[SB_SLOTS];
-    int lst[SB_SLOTS];
+    int lst[SB_SLOTS], sel[SB_SLOTS];
     float wq[SB_SLOTS];
+    int wtot[4], wact[4];
 };
 
-__device__ void sb_read_route(const Layer &L, const Work &W, int n, SbRoute &R, int *offs) {
-    const int tid = threadIdx.x, NE = L.n_expert, nq = n * L.top_k;
-    if (tid <= NE) offs[tid] = W.offsets[tid];
+// Every workgroup builds the same tables (a count per expert, a scan over the
+// experts, each selection's rank among the earlier ones of its expert);
+// with export_lists, it also writes the per-expert lists to W (offsets,
+// active experts, entries) as the router's own list step would, for the
+// routing export.  cnt: MAX_EXPERT + 1 ints of LDS.
+__device__ void sb_read_route(const Layer &L, const Work &W, int n, SbRoute &R, int *cnt, bool export_lists) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int NE = L.n_expert, nq = n * L.top_k;
+    int e = 0;
     if (tid < nq) {
-        R.lst[tid] = W.list[tid];
+        e = W.idx[tid];
+        R.sel[tid] = e;
         R.wq[tid] = W.w[tid];
     }
-    const int ae = tid < min(NE, SB_SLOTS) ? W.active[1 + tid] : 0;
-    if (tid == 0) R.U = W.active[0];
+    if (tid <= MAX_EXPERT) cnt[tid] = 0;
     __syncthreads();
-    if (tid < R.U) {
-        R.e[tid] = ae;
-        R.wslot[tid] = expert_slot(L, ae);
-        R.beg[tid] = offs[ae];
-        R.cnt[tid] = offs[ae + 1] - offs[ae];
+    if (tid < nq) atomicAdd(&cnt[e], 1);
+    __syncthreads();
+    // thread x < 256 holds expert x: exclusive scans of the counts and of the
+    // active flags, by wave scans and the four wave totals
+    const int c = tid < NE ? cnt[tid] : 0;
+    int v = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    const uint64_t am = __ballot(c > 0);
+    if (tid < 256 && lane == 63) R.wtot[wave] = v;
+    if (tid < 256 && lane == 0) R.wact[wave] = __popcll(am);
+    __syncthreads();
+    if (tid < 256) {
+        int pre = 0, apre = 0;
+        for (int w = 0; w < wave; ++w) pre += R.wtot[w], apre += R.wact[w];
+        const int start = pre + v - c;
+        if (c > 0) {
+            const int u = apre + __popcll(am & ((1ull << lane) - 1ull));
+            R.e[u] = tid;
+            R.wslot[u] = expert_slot(L, tid);
+            R.beg[u] = start;
+            R.cnt[u] = c;
+            if (export_lists) W.active[1 + u] = tid;
+        }
+        if (export_lists && tid <= NE) W.offsets[tid] = start;  // (tid == NE: start = nq)
+        if (tid == 255) {
+            R.U = apre + __popcll(am);
+            if (export_lists) W.active[0] = R.U;
+        }
+        cnt[tid] = start;  // offsets, for the entries below (read after the barrier)
+    }
+    if (export_lists && NE == 256 && tid == 256) W.offsets[256] = nq;
+    __syncthreads();
+    if (tid < nq) {
+        // entry position: the expert's offset plus the earlier selections of it
+        int r = 0;
+        for (int q = 0; q < tid; ++q) r += R.sel[q] == e;
+        R.lst[cnt[e] + r] = tid;
+        if (export_lists) W.list[cnt[e] + r] = tid;
     }
     __syncthreads();
 }
@@ -299,7 +344,7 @@ __global__ __launch_bounds__(SB_THREADS, 1) void k_small_gateup(Layer L, Work W,
     __shared__ uint4 T[256 * IQ2_REPL];
     __shared__ __align__(16) uint8_t xs[SMALL_MAX_TOK * SB_XP];
     __shared__ SbRoute R;
-    __shared__ int offs[MAX_EXPERT + 1];
+    __shared__ int ecnt[MAX_EXPERT + 1];
     __shared__ uint32_t xmax[SMALL_MAX_TOK];
     __shared__ float xsc[SMALL_MAX_TOK];
     const int tid = threadIdx.x, wave = tid >> 6;
@@ -315,7 +360,7 @@ __global__ __launch_bounds__(SB_THREADS, 1) void k_small_gateup(Layer L, Work W,
         xr[j] = *reinterpret_cast<const uint4 *>(x + 8 * (int64_t)i);
     }
     if (tid < SMALL_MAX_TOK) xmax[tid] = 0u;
-    sb_read_route(L, W, n, R, offs);
+    sb_read_route(L, W, n, R, ecnt, blockIdx.x == 0);
     // units: shared (F / 16 tiles x nbe parts), then routed (U slots x tiles x parts)
     const int TG = F >> 4, bpu = min(8, nbe), pr = nbe / bpu;
     const int ns = L.n_shared ? TG * nbe : 0;
@@ -572,7 +617,7 @@ __global__ __launch_bounds__(SB_THREADS, 1) void k_small_down(Layer L, Work W, c
         for (int z = z0 + tid; z < z1; z += SB_THREADS) reinterpret_cast<float4 *>(gz)[z] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (tid < 3 * SMALL_MAX_TOK) hmax[tid] = 0u;
-    sb_read_route(L, W, n, R, offs);
+    sb_read_route(L, W, n, R, offs, false);
     const int TE = E >> 4, U = R.U;
     const int nr = U * TE, ns = L.n_shared ? TE * (F >> 8) : 0;
     int g0, g1;

@@ -177,34 +177,62 @@ def test_hash_q4_layer_in_chunks():
 def test_hash_stack_with_learned_layers():
     """Three hash layers then two learned ones, one library call, against the
     oracle's stack taken one layer at a time from the GPU's own inputs
-    (teacher-forced: a last-bit difference cannot flip a later routing)."""
+    (teacher-forced: a last-bit difference cannot flip a later routing).
+    The one-call stack and the layer-by-layer run add the layer outputs in
+    different orders, so their residuals differ in the last bits, and an
+    element at a bf16 rounding boundary of the next RMSNorm moves by a bf16
+    ulp (2^-8 relative): after a few layers a logit can move by about 1e-3 of
+    itself, and a learned layer can pick a different k-th expert for a token
+    whose k-th and (k+1)-th logits are that close.  Such tokens (checked to be
+    within 1e-2 by the oracle's logits; a wrong layer order or a missing
+    normalisation would move every token far more) are left out of the final
+    comparison."""
     kinds = ["ds4_hash", "ds4_hash", "ds4_hash", "ds4", "ds4"]
-    devs = [device_layer(k, 64) for k in kinds]
-    h0 = synth.residual(7, 4, 4096)
-    ids = synth.token_ids(7, 4, synth.N_VOCAB)
+    # a handle per layer (distinct max_tokens), so each keeps its layer's routing
+    devs = [device_layer(kd, 64 + i) for i, kd in enumerate(kinds)]
+    n = 4
+    h0 = synth.residual(7, n, 4096)
+    ids = synth.token_ids(7, n, synth.N_VOCAB)
     h = torch.from_numpy(h0.copy()).cuda()
     d_ids = m.to_device_ids(ids)
     m.forward_stack(devs, h, ids=d_ids)
     torch.cuda.synchronize()
     got = h.cpu().numpy()
+    stack_idx = [dev.last_routing(n)[0].cpu().numpy().reshape(n, -1) for dev in devs]
     # layer by layer on the GPU, each layer's input checked against the oracle
     hg = torch.from_numpy(h0.copy()).cuda()
-    for i, (k, dev) in enumerate(zip(kinds, devs)):
+    flipped = np.zeros(n, dtype=bool)
+    for i, (kd, dev) in enumerate(zip(kinds, devs)):
         x = m.rmsnorm(hg)
         before = hg.cpu().numpy().astype(np.float64)
         out = torch.zeros_like(hg)
         dev.forward(x, out, ids=d_ids)
         torch.cuda.synchronize()
+        lbl_idx = dev.last_routing(n)[0].cpu().numpy().reshape(n, -1)
         x_np = x.cpu().view(torch.int16).numpy().view(np.uint16)
-        ref, ridx, _ = oracle.forward(host_layer(k), x_np, token_ids=ids if k == "ds4_hash" else None)
+        lay = host_layer(kd)
+        ref, ridx, _ = oracle.forward(lay, x_np, token_ids=ids if kd == "ds4_hash" else None)
         err = rel_err(out.cpu().numpy(), ref)
-        log(f"[gpu] stack layer {i} ({k}): rel err {err:.2e}")
+        log(f"[gpu] stack layer {i} ({kd}): rel err {err:.2e}")
         assert err <= REL_TOL
-        if k == "ds4_hash":
-            assert np.array_equal(ridx, host_layer(k).hash_table[ids])
+        assert np.array_equal(lbl_idx, ridx)
+        if kd == "ds4_hash":
+            assert np.array_equal(ridx, lay.hash_table[ids])
+            assert np.array_equal(stack_idx[i], ridx)
+        else:
+            lg, _, _, _ = oracle.route(x_np, lay.router, lay.router_bias, lay.spec.top_k)
+            for t in np.nonzero(np.any(stack_idx[i] != lbl_idx, axis=1))[0]:
+                srt = np.sort(lg[t].astype(np.float64))[::-1]
+                k = lay.spec.top_k
+                gap = (srt[k - 1] - srt[k]) / max(abs(srt[k - 1]), 1e-30)
+                log(f"[gpu] stack layer {i} token {t}: routing differs at a tie gap of {gap:.1e}")
+                assert gap < 1e-2, "the one-call stack changed a routing that no last-bit difference explains"
+                flipped[t] = True
         hg += out
         assert np.all(np.isfinite(before))
-    assert rel_err(got - h0, hg.cpu().numpy() - h0) <= REL_TOL
+    keep = ~flipped
+    assert keep.sum() >= n - 1
+    assert rel_err((got - h0)[keep], (hg.cpu().numpy() - h0)[keep]) <= REL_TOL
 
 
 def test_hash_errors():
