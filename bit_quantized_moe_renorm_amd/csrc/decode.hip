@@ -136,9 +136,10 @@ struct RouteCache {
 // The weights and the export of a routing whose lane j < k holds slot j's
 // expert and fp32 logit: one exp per lane (relative to the largest of the k
 // logits, slot 0's for a top-k selection), the denominator by a sum over the
-// k lanes.
+// k lanes.  set_experts: also record the experts in rc (a hash layer has them
+// there already, and other waves may be reading them).
 __device__ __forceinline__ void dec_route_finish(const Layer &L, const Work &W, int myE, float myL, RouteCache *rc,
-                                                 bool write_global) {
+                                                 bool write_global, bool set_experts = true) {
     const int lane = threadIdx.x & 63;
     const int NE = L.n_expert, k = L.top_k;
     float M = (lane < k) ? myL : -INFINITY;
@@ -148,9 +149,11 @@ __device__ __forceinline__ void dec_route_finish(const Layer &L, const Work &W, 
     const double z = wave_sum(ex);
     const float wj = (float)(ex / z);
     if (lane < k) {
-        rc->idx[lane] = myE;
+        if (set_experts) {
+            rc->idx[lane] = myE;
+            rc->slot[lane] = expert_slot(L, myE);
+        }
         rc->w[lane] = wj;
-        rc->slot[lane] = expert_slot(L, myE);
     }
     if (!write_global) return;
     if (lane < k) {
@@ -472,10 +475,11 @@ __device__ __forceinline__ void dec_route_poll(const Layer &L, const Work &W, ui
     }
 }
 
-// The routing of a hash layer's token: lane j < k polls the four tagged
+// The weights of a hash layer's token: lane j < k polls the four tagged
 // words of slot j's expert (row `trow` of the table), then the weights are
-// taken over those k logits.  A bad id (decided by every workgroup alike from
-// the same word) skips the wait and fails the call.
+// taken over those k logits.  The experts themselves are already in rc (set
+// from the table row when the call starts).  A bad id (decided by every
+// workgroup alike from the same word) skips the wait and fails the call.
 __device__ __forceinline__ void dec_route_poll_hashed(const Layer &L, const Work &W, uint32_t tag,
                                                       const int32_t *trow, bool bad_id, RouteCache *rc,
                                                       int *lds_flag) {
@@ -509,7 +513,7 @@ __device__ __forceinline__ void dec_route_poll_hashed(const Layer &L, const Work
             if (ok) {
                 const double h0 = __longlong_as_double((long long)((v[0] & 0xFFFFFFFFull) | (v[1] << 32)));
                 const double h1 = __longlong_as_double((long long)((v[2] & 0xFFFFFFFFull) | (v[3] << 32)));
-                dec_route_finish(L, W, e, (float)(h0 + h1 + (double)b), rc, blockIdx.x == 0);
+                dec_route_finish(L, W, e, (float)(h0 + h1 + (double)b), rc, blockIdx.x == 0, false);
             }
         }
         if (lane == 0) *lds_flag = ok;
@@ -986,7 +990,21 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
         }
         if (threadIdx.x == 0) lds_flag = 1;
     } else if (hashed) {
-        dec_route_poll_hashed(L, W, tag, trow, bad_id, &rc, &lds_flag);
+        // a hash layer's experts are its table row's, known at once: routed
+        // gate/up starts without waiting for the logits, which set only the
+        // weights and are polled before routed down (below)
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            if (!bad_id && lane < L.top_k) {
+                const int e = trow[lane];
+                rc.idx[lane] = e;
+                rc.slot[lane] = expert_slot(L, e);
+            }
+            if (lane == 0) {
+                if (bad_id) report_bad_id(W, tag);
+                lds_flag = bad_id ? 0 : 1;
+            }
+        }
     } else {
         dec_route_poll(L, W, tag, &rc, &lds_flag);
     }
@@ -1032,6 +1050,15 @@ __global__ __launch_bounds__(DEC_THREADS, DEC_WG_PER_CU) void k_decode_fused(Lay
             case 4: dec_shdn_item<4>(L, W, out, it - b2, tag, H, hid, ok); break;
             default: dec_shdn_item<8>(L, W, out, it - b2, tag, H, hid, ok); break;
         }
+    }
+    // a hash layer's weights: wave 0 polls the k experts' logits (long since
+    // written by the router items); every workgroup with routed down units
+    // needs them, and workgroup 0 also exports the routing
+    if (hashed && !P.pre_routed) {
+        const bool poll = ok && (it < b4 || blockIdx.x == 0);
+        if (poll) dec_route_poll_hashed(L, W, tag, trow, false, &rc, &lds_flag);
+        __syncthreads();
+        if (poll) ok = lds_flag != 0;
     }
     // routed down: each workgroup takes consecutive units (slot-major), so
     // its units mostly share one h vector, staged in LDS when the slot

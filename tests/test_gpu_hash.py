@@ -186,7 +186,9 @@ def test_hash_stack_with_learned_layers():
     whose k-th and (k+1)-th logits are that close.  Such tokens (checked to be
     within 1e-2 by the oracle's logits; a wrong layer order or a missing
     normalisation would move every token far more) are left out of the final
-    comparison."""
+    comparison.  Two nearly equal logits among the selected ones can likewise
+    swap places in the top-k order; that keeps the token's output, and is
+    accepted when those logits are within 1e-2."""
     kinds = ["ds4_hash", "ds4_hash", "ds4_hash", "ds4", "ds4"]
     # a handle per layer (distinct max_tokens), so each keeps its layer's routing
     devs = [device_layer(kd, 64 + i) for i, kd in enumerate(kinds)]
@@ -221,9 +223,20 @@ def test_hash_stack_with_learned_layers():
             assert np.array_equal(stack_idx[i], ridx)
         else:
             lg, _, _, _ = oracle.route(x_np, lay.router, lay.router_bias, lay.spec.top_k)
+            k = lay.spec.top_k
             for t in np.nonzero(np.any(stack_idx[i] != lbl_idx, axis=1))[0]:
+                if flipped[t]:
+                    continue  # its input here already differs
+                if set(stack_idx[i][t].tolist()) == set(lbl_idx[t].tolist()):
+                    # the same experts in another order: nearly equal logits
+                    # swapped places; each weight moves with its expert, so the
+                    # output is the same
+                    v = lg[t][lbl_idx[t][stack_idx[i][t] != lbl_idx[t]]].astype(np.float64)
+                    spread = (v.max() - v.min()) / max(abs(v.max()), 1e-30)
+                    log(f"[gpu] stack layer {i} token {t}: same experts, order swapped at a spread of {spread:.1e}")
+                    assert spread < 1e-2, "the one-call stack reordered experts whose logits are far apart"
+                    continue
                 srt = np.sort(lg[t].astype(np.float64))[::-1]
-                k = lay.spec.top_k
                 gap = (srt[k - 1] - srt[k]) / max(abs(srt[k - 1]), 1e-30)
                 log(f"[gpu] stack layer {i} token {t}: routing differs at a tie gap of {gap:.1e}")
                 assert gap < 1e-2, "the one-call stack changed a routing that no last-bit difference explains"
