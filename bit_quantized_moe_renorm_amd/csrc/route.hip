@@ -15,7 +15,7 @@ namespace ds4 {
 
 constexpr int RT_WAVES = 4;         // waves per router workgroup (one K quarter each)
 constexpr int RT_TOK = 16;          // tokens per router workgroup beyond 64 tokens (fp32 activations; bf16 ones take the batched router)
-constexpr int ROUTE_SMALL_MAX = 64; // fused top-k/bucketing in the last workgroup up to this n_tok
+constexpr int ROUTE_SMALL_MAX = 64; // fused top-k/bucketing (a tail workgroup per token tile) up to this n_tok
 
 template <bool XBF16>
 __device__ __forceinline__ void load_x4(const void *x, int64_t off, double v[4]) {
@@ -88,12 +88,26 @@ __device__ void topk_tagged(const Work &W, const unsigned long long *__restrict_
                             uint32_t tag, int32_t *__restrict__ idx, float *__restrict__ w,
                             unsigned long long *__restrict__ itag) {
     const int lane = threadIdx.x & 63;
+    const unsigned long long *row = ltag + (int64_t)t * MAX_EXPERT;
     unsigned long long v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = rt_poll(ltag + (int64_t)t * MAX_EXPERT + min(lane + 64 * i, NE - 1));
+    // all four words in flight at once each round (a word that already
+    // carries the tag reads the same again), until all carry it; bounded
+    const uint32_t want = tag ^ W.want_xor;
     bool ok = true;
+    for (int spins = 0;; ++spins) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ok &= rt_wait(W, ltag + (int64_t)t * MAX_EXPERT + min(lane + 64 * i, NE - 1), tag, v[i]);
+        for (int i = 0; i < 4; ++i) v[i] = rt_poll(row + min(lane + 64 * i, NE - 1));
+        bool have = true;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) have &= (uint32_t)(v[i] >> 32) == want;
+        if (__all(have)) break;
+        if (spins > W.spin_limit) {
+            if (lane == 0) report_wait_expired(W, tag);
+            ok = have;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
     // DPP maxima and ballots: no cross-lane round trip through LDS
     uint32_t key[4];
 #pragma unroll
@@ -213,10 +227,12 @@ __device__ void bucket_small(const unsigned long long *__restrict__ itag, uint32
 // flight together (unconditional: tokens past the tile's end re-read its last
 // token, chunks past the quarter re-read its first; neither is summed), and
 // the quarters are added in order by wave 0.
-// With fuse_tail, the last workgroup of each token tile takes the tile's top-k,
-// and (fuse_tail 1) the last of those builds the per-expert lists; with
-// fuse_tail 2 the lists are left to the kernels that follow (the small-batch
-// kernels build them from the selections).
+// With fuse_tail, the grid has one more column: its workgroup in row y takes
+// token tile y's top-k from the tagged logits, and (fuse_tail 1) the last of
+// those tails builds the per-expert lists; with fuse_tail 2 the lists are
+// left to the kernels that follow (the small-batch kernels build them from
+// the selections).  A tail is dispatched after its tile's expert workgroups
+// (row-major order) and waits only on them, so it never holds up their start.
 constexpr int RT_KCH = 4;  // 256-value chunks per wave at most
 template <bool XBF16, int TT>
 __global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ R, const float *__restrict__ bias,
@@ -227,6 +243,24 @@ __global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ 
     const int e = blockIdx.x;
     const int t0 = blockIdx.y * TT;
     const int nt = min(TT, n_tok - t0);
+    if (fuse_tail && e == NE) {
+        // the token tile's tail (the grid's extra column, dispatched after the
+        // tile's expert workgroups): polls the tile's tagged logits from the
+        // start, then takes each token's top-k.  No tickets: 256 workgroups
+        // taking one from the same counter queued for microseconds
+        for (int t = t0 + wave; t < t0 + nt; t += RT_WAVES) topk_tagged(W, W.ltag, t, NE, k, tag, W.idx, W.w, W.itag);
+        if (fuse_tail == 2) return;
+        // the lists: the last of the tails (a ticket among the gridDim.y of
+        // them; the last taker resets it) polls every token's selection
+        __shared__ int last;
+        __syncthreads();
+        if (threadIdx.x == 0) last = atomicAdd(&W.counters[0], 1) == (int)gridDim.y - 1;
+        __syncthreads();
+        if (!last) return;
+        bucket_small(W.itag, tag, n_tok, k, NE, W);
+        if (threadIdx.x == 0) W.counters[0] = 0;
+        return;
+    }
     const int kq = E / RT_WAVES, kb = wave * kq;
     {
         double acc[TT];
@@ -272,30 +306,6 @@ __global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ 
         else
             W.logits[(int64_t)(t0 + lane) * NE + e] = L;
     }
-    if (!fuse_tail) return;
-    // tickets (slot 0 of the counters: word 0 for the lists, word 1 + y for
-    // token tile y; each last taker resets its word).  A ticket needs no
-    // fence: the tail polls the tagged words, whose stores were all issued
-    // before the ticket was taken, so every wait ends.
-    __shared__ int last;
-    __syncthreads();
-    if (threadIdx.x == 0) last = atomicAdd(&W.counters[1 + blockIdx.y], 1) == (int)gridDim.x - 1;
-    __syncthreads();
-    if (!last) return;
-    for (int t = t0 + wave; t < t0 + nt; t += RT_WAVES) topk_tagged(W, W.ltag, t, NE, k, tag, W.idx, W.w, W.itag);
-    __syncthreads();
-    if (fuse_tail == 2) {
-        if (threadIdx.x == 0) W.counters[1 + blockIdx.y] = 0;
-        return;
-    }
-    if (threadIdx.x == 0) {
-        W.counters[1 + blockIdx.y] = 0;
-        last = atomicAdd(&W.counters[0], 1) == (int)gridDim.y - 1;
-    }
-    __syncthreads();
-    if (!last) return;
-    bucket_small(W.itag, tag, n_tok, k, NE, W);
-    if (threadIdx.x == 0) W.counters[0] = 0;
 }
 
 // Top-k for many tokens: one wavefront per token.
@@ -834,12 +844,13 @@ hipError_t launch_route(const Layer &L, const Work &W, const void *x, int n_tok,
     const int fuse = n_tok <= ROUTE_SMALL_MAX ? (lists ? 1 : 2) : 0;
     // token tiles of 1, 2 or 4 for calls of up to 8 tokens (a larger tile
     // would load and multiply clamped copies of the last token; 4-token tiles
-    // at 5..8 tokens let two tiles' last workgroups take the top-k side by
+    // at 5..8 tokens let two tiles' tail workgroups take the top-k side by
     // side), and 8 up to 64 tokens: the 16-token tile takes 252 VGPRs (2 waves
     // per SIMD), and 8-token tiles measured 44 -> 33 us at 16 tokens, 52 -> 47
     // at 32
     const int tt = n_tok == 1 ? 1 : n_tok == 2 ? 2 : n_tok <= 8 ? 4 : fuse ? 8 : RT_TOK;
-    const dim3 grid(NE, (n_tok + tt - 1) / tt);
+    // with the fused tail, one more workgroup per token tile takes its top-k
+    const dim3 grid(NE + (fuse ? 1 : 0), (n_tok + tt - 1) / tt);
     const bool bf = L.act_dtype == 1;
 #define DS4_ROUTE_LAUNCH(T)                                                                                   \
     hipLaunchKernelGGL((bf ? k_route_logits<true, T> : k_route_logits<false, T>), grid, dim3(256), 0, s, L.router, \
