@@ -81,6 +81,20 @@ __device__ __forceinline__ bool rt_wait(const Work &W, const unsigned long long 
     return true;
 }
 
+// Renormalised weight of selection `lane` (< k) among the k selected logits
+// (every lane holds all of them; selection 0 is the largest): one exp per lane
+// relative to the largest, the denominator by a sum over the lanes (all 64
+// lanes call it; lanes >= k add 0 and get a value that is not used).  It was
+// a loop of k exps in every lane, about 2 us of fp64 work in the router's tail.
+__device__ __forceinline__ float topk_weight(const float (&sel_L)[MAX_TOPK], int k, int lane) {
+    float myL = sel_L[0];
+#pragma unroll
+    for (int j = 1; j < MAX_TOPK; ++j)
+        if (j == lane) myL = sel_L[j];
+    const double ex = lane < k ? exp((double)myL - (double)sel_L[0]) : 0.0;
+    return (float)(ex / wave_sum(ex));
+}
+
 // Top-k + renormalised weights for token t, by one wavefront, from the tagged
 // logits of this call; the selection also goes to the tagged itag words.  An
 // expired wait poisons the token's weights with NaN.
@@ -113,23 +127,21 @@ __device__ void topk_tagged(const Work &W, const unsigned long long *__restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i) key[i] = lane + 64 * i < NE ? logit_key32(__uint_as_float((uint32_t)v[i])) : 0u;
     const bool bad = __ballot(!ok) != 0ull;
-    float sel_L[MAX_TOPK];
-    int sel_e[MAX_TOPK];
+    float sel_L[MAX_TOPK] = {};
+    int sel_e[MAX_TOPK] = {};
     for (int j = 0; j < k; ++j) {
         uint32_t m;
         topk_round(key, m, sel_e[j]);
         sel_L[j] = key32_logit(m);
     }
+    const float wj = topk_weight(sel_L, k, lane);
+    int e = sel_e[0];
+#pragma unroll
+    for (int j = 1; j < MAX_TOPK; ++j)
+        if (j == lane) e = sel_e[j];
     if (lane < k) {
-        double m = (double)sel_L[0], z = 0.0, num = 0.0;
-        int e = 0;
-        for (int j = 0; j < k; ++j) {
-            const double ex = exp((double)sel_L[j] - m);
-            z += ex;
-            if (j == lane) num = ex, e = sel_e[j];
-        }
         idx[(int64_t)t * k + lane] = e;
-        w[(int64_t)t * k + lane] = bad ? __builtin_nanf("") : (float)(num / z);
+        w[(int64_t)t * k + lane] = bad ? __builtin_nanf("") : wj;
         rt_put(itag + (int64_t)t * MAX_TOPK + lane, tag, (uint32_t)e);
     }
 }
@@ -144,26 +156,21 @@ __device__ void topk_token(const float *__restrict__ logits, int t, int NE, int 
         const int e = lane + 64 * i;
         key[i] = e < NE ? logit_key32(logits[(int64_t)t * NE + e]) : 0u;
     }
-    float sel_L[MAX_TOPK];
-    int sel_e[MAX_TOPK];
+    float sel_L[MAX_TOPK] = {};
+    int sel_e[MAX_TOPK] = {};
     for (int j = 0; j < k; ++j) {
         uint32_t m;
         topk_round(key, m, sel_e[j]);
         sel_L[j] = key32_logit(m);  // no reload: the key holds the logit
     }
+    const float wj = topk_weight(sel_L, k, lane);
+    int e = sel_e[0];
+#pragma unroll
+    for (int j = 1; j < MAX_TOPK; ++j)
+        if (j == lane) e = sel_e[j];
     if (lane < k) {
-        // every lane < k evaluates the common denominator; lane j also its numerator
-        double m = (double)sel_L[0], z = 0.0, num = 0.0;
-        for (int j = 0; j < k; ++j) {
-            double ex = exp((double)sel_L[j] - m);
-            z += ex;
-            if (j == lane) num = ex;
-        }
-        int e = 0;
-        for (int j = 0; j < k; ++j)
-            if (j == lane) e = sel_e[j];
         idx[(int64_t)t * k + lane] = e;
-        w[(int64_t)t * k + lane] = (float)(num / z);
+        w[(int64_t)t * k + lane] = wj;
     }
 }
 
@@ -690,8 +697,8 @@ __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ 
             }
     }
     // top-k among the candidates, renormalised weights
-    float sel_L[MAX_TOPK];
-    int sel_e[MAX_TOPK];
+    float sel_L[MAX_TOPK] = {};
+    int sel_e[MAX_TOPK] = {};
     for (int j = 0; j < k; ++j) {
         uint64_t best = key[0];
 #pragma unroll
@@ -705,16 +712,14 @@ __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ 
             if (lane + 64 * i == e) Le = Lv[i], key[i] = 0ull;
         sel_L[j] = __shfl(Le, e & 63, 64);
     }
+    const float wj = topk_weight(sel_L, k, lane);
+    int e = sel_e[0];
+#pragma unroll
+    for (int j = 1; j < MAX_TOPK; ++j)
+        if (j == lane) e = sel_e[j];
     if (lane < k) {
-        double m = (double)sel_L[0], z = 0.0, num = 0.0;
-        int e = 0;
-        for (int j = 0; j < k; ++j) {
-            const double ex = exp((double)sel_L[j] - m);
-            z += ex;
-            if (j == lane) num = ex, e = sel_e[j];
-        }
         W.idx[(int64_t)t * k + lane] = e;
-        W.w[(int64_t)t * k + lane] = (float)(num / z);
+        W.w[(int64_t)t * k + lane] = wj;
         atomicAdd(&W.ecount[e], 1);
     }
 }
