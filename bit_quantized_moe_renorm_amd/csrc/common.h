@@ -219,6 +219,43 @@ __device__ __forceinline__ void topk_round(uint32_t (&key)[4], uint32_t &m, int 
         if (lane + 64 * i == e) key[i] = 0u;
 }
 
+// Sum and maximum over the wave's 64 lanes by DPP, in the tree of
+// wave_max_u32 (prefixes within each 16-lane row, then the row broadcasts;
+// lane 63 ends with the result, which every lane reads back), with no round
+// trip through LDS: a shuffle tree costs one LDS permute per step and 32-bit
+// half.  Lanes whose DPP source lies outside their row take the identity.
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ double dpp_f64(double v) {
+    return __hiloint2double(__builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROW_MASK, 0xF, BOUND),
+                            __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, 0xF, BOUND));
+}
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+    v += dpp_f64<0x111, 0xF, true>(v);   // row_shr:1
+    v += dpp_f64<0x112, 0xF, true>(v);   // row_shr:2
+    v += dpp_f64<0x114, 0xF, true>(v);   // row_shr:4
+    v += dpp_f64<0x118, 0xF, true>(v);   // row_shr:8
+    v += dpp_f64<0x142, 0xA, false>(v);  // row_bcast:15
+    v += dpp_f64<0x143, 0xC, false>(v);  // row_bcast:31
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
+                            __builtin_amdgcn_readlane(__double2loint(v), 63));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_f32(float v) {
+    // a lane without a source keeps -inf (the old value; bound_ctrl off)
+    const float o = __int_as_float(__builtin_amdgcn_update_dpp((int)0xFF800000u, __float_as_int(v), CTRL,
+                                                               ROW_MASK, 0xF, false));
+    return fmaxf(v, o);
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = dpp_max_f32<0x111, 0xF>(v);
+    v = dpp_max_f32<0x112, 0xF>(v);
+    v = dpp_max_f32<0x114, 0xF>(v);
+    v = dpp_max_f32<0x118, 0xF>(v);
+    v = dpp_max_f32<0x142, 0xA>(v);
+    v = dpp_max_f32<0x143, 0xC>(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

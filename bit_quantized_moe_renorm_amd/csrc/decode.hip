@@ -143,10 +143,9 @@ __device__ __forceinline__ void dec_route_finish(const Layer &L, const Work &W, 
     const int lane = threadIdx.x & 63;
     const int NE = L.n_expert, k = L.top_k;
     float M = (lane < k) ? myL : -INFINITY;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    M = wave_max_dpp(M);
     const double ex = (lane < k) ? exp((double)myL - (double)M) : 0.0;
-    const double z = wave_sum(ex);
+    const double z = wave_sum_dpp(ex);
     const float wj = (float)(ex / z);
     if (lane < k) {
         if (set_experts) {
@@ -228,7 +227,7 @@ __device__ __forceinline__ void dec_route_item(const Layer &L, const Work &W, co
         acc = fma((double)xv.z, (double)r.z, acc);
         acc = fma((double)xv.w, (double)r.w, acc);
     }
-    acc = wave_sum(acc);
+    acc = wave_sum_dpp(acc);
     if (lane == 0) lds_part[wave] = acc;
     __syncthreads();
     if (threadIdx.x < 2) {

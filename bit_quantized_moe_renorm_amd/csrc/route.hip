@@ -92,7 +92,7 @@ __device__ __forceinline__ float topk_weight(const float (&sel_L)[MAX_TOPK], int
     for (int j = 1; j < MAX_TOPK; ++j)
         if (j == lane) myL = sel_L[j];
     const double ex = lane < k ? exp((double)myL - (double)sel_L[0]) : 0.0;
-    return (float)(ex / wave_sum(ex));
+    return (float)(ex / wave_sum_dpp(ex));
 }
 
 // Top-k + renormalised weights for token t, by one wavefront, from the tagged
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256) void k_route_logits(const float *__restrict__ 
         }
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-            const double s = wave_sum(acc[t]);
+            const double s = wave_sum_dpp(acc[t]);
             if (lane == 0) part[wave][t] = s;
         }
     }
