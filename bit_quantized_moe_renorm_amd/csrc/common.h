@@ -255,6 +255,24 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
     v = dpp_max_f32<0x143, 0xC>(v);
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_max_f64(double v) {
+    // a lane without a source keeps -inf (0xFFF00000 00000000; bound_ctrl off)
+    const double o = __hiloint2double(
+        __builtin_amdgcn_update_dpp((int)0xFFF00000u, __double2hiint(v), CTRL, ROW_MASK, 0xF, false),
+        __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, 0xF, false));
+    return fmax(v, o);
+}
+__device__ __forceinline__ double wave_max_dpp(double v) {
+    v = dpp_max_f64<0x111, 0xF>(v);
+    v = dpp_max_f64<0x112, 0xF>(v);
+    v = dpp_max_f64<0x114, 0xF>(v);
+    v = dpp_max_f64<0x118, 0xF>(v);
+    v = dpp_max_f64<0x142, 0xA>(v);
+    v = dpp_max_f64<0x143, 0xC>(v);
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
+                            __builtin_amdgcn_readlane(__double2loint(v), 63));
+}
 
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {

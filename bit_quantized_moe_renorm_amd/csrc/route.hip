@@ -610,7 +610,7 @@ __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ 
 #pragma unroll
         for (int j = 0; j < 4; ++j) ss = fma((double)xv[4 * m + j], (double)xv[4 * m + j], ss);
     }
-    const double xn = sqrt(wave_sum(ss)) * (1.0 + 1e-12);
+    const double xn = sqrt(wave_sum_dpp(ss)) * (1.0 + 1e-12);
     // bounds of every expert (lane l: experts l + 64 i)
     double lb[4], ub[4], bb[4];
 #pragma unroll
@@ -638,9 +638,7 @@ __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ 
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (!taken[i] && lb[i] > best) best = lb[i], bi = i;
-            double m = best;
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off, 64));
+            const double m = wave_max_dpp(best);
             theta = m;
             // the lowest lane holding the maximum gives it up
             const uint64_t holders = __ballot(bi >= 0 && best == m);
@@ -688,7 +686,7 @@ __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ 
             s1 = fma((double)xv[4 * m + 6], (double)r[m + 1].z, s1);
             s1 = fma((double)xv[4 * m + 7], (double)r[m + 1].w, s1);
         }
-        const double sv = wave_sum(s0 + s1);
+        const double sv = wave_sum_dpp(s0 + s1);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (lane + 64 * i == e) {
