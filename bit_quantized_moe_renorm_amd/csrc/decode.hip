@@ -45,10 +45,6 @@ __device__ __forceinline__ float dec_dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 __device__ __forceinline__ float dec_silu(float z) { return z / (1.0f + expf(-z)); }
-__device__ __forceinline__ float dec_group_sum(float v, int lpr) {
-    for (int off = lpr >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
 // Sum over each group of lpr consecutive lanes (lpr a power of two up to 64),
 // left in the group's last lane, by DPP alone (row shifts, then the two row
 // broadcasts): plain VALU work that never waits on LDS traffic in flight.
@@ -830,11 +826,13 @@ __device__ __forceinline__ bool dec_h16_finish(const Work &W, int F, int slot, u
             mx = fmaxf(mx, fabsf(h[e]));
             hs += h[e];
         }
-        // chunk c = p / 8 is 8 consecutive lanes; sub-block s = (p / 2) % 4 is 2
-        mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
-        hs += __shfl_xor(hs, 1, 64);
+        // chunk c = p / 8 is 8 consecutive lanes; sub-block s = (p / 2) % 4 is 2.
+        // By DPP (no LDS round trip): lane pairs, quad halves, then each lane
+        // with its mirror in the other quad of the 8
+        mx = fmaxf(mx, dec_dpp<0xB1, 0xF, false>(mx));   // quad_perm [1,0,3,2]
+        mx = fmaxf(mx, dec_dpp<0x4E, 0xF, false>(mx));   // quad_perm [2,3,0,1]
+        mx = fmaxf(mx, dec_dpp<0x141, 0xF, false>(mx));  // row_half_mirror
+        hs += dec_dpp<0xB1, 0xF, false>(hs);
         if (mine) {
             const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFFu) - 127;
             const int e = min(max(ex - 14, -100), 100);
@@ -908,8 +906,8 @@ __device__ __forceinline__ void dec_rdn_compute16(const Layer &L, float *__restr
         const int row = r0 + r * rpw;
         const uint32_t dd = w.dd[r];
         float y = half_to_f32((uint16_t)(dd & 0xFFFFu)) * (A[r] * hsc) - half_to_f32((uint16_t)(dd >> 16)) * B[r];
-        y = dec_group_sum(y, lpr);
-        if (c == 0 && row < E) atomicAdd(out + row, wgt * y);
+        y = dec_group_sum_last(y, lpr);
+        if (c == lpr - 1 && row < E) atomicAdd(out + row, wgt * y);
     }
 }
 
