@@ -225,6 +225,22 @@ __device__ __forceinline__ void topk_round(uint32_t (&key)[4], uint32_t &m, int 
 // trip through LDS: a shuffle tree costs one LDS permute per step and 32-bit
 // half.  Lanes whose DPP source lies outside their row take the identity.
 template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, BOUND));
+}
+// Sum over each group of lpr consecutive lanes (lpr a power of two up to 64),
+// left in the group's last lane, by DPP alone (row shifts, then the two row
+// broadcasts): plain VALU work that never waits on LDS traffic in flight.
+__device__ __forceinline__ float group_sum_last(float v, int lpr) {
+    if (lpr > 1) v += dpp_f32<0x111, 0xF, true>(v);    // row_shr:1
+    if (lpr > 2) v += dpp_f32<0x112, 0xF, true>(v);    // row_shr:2
+    if (lpr > 4) v += dpp_f32<0x114, 0xF, true>(v);    // row_shr:4
+    if (lpr > 8) v += dpp_f32<0x118, 0xF, true>(v);    // row_shr:8
+    if (lpr > 16) v += dpp_f32<0x142, 0xA, false>(v);  // row_bcast:15
+    if (lpr > 32) v += dpp_f32<0x143, 0xC, false>(v);  // row_bcast:31
+    return v;
+}
+template <int CTRL, int ROW_MASK, bool BOUND>
 __device__ __forceinline__ double dpp_f64(double v) {
     return __hiloint2double(__builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROW_MASK, 0xF, BOUND),
                             __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, 0xF, BOUND));

@@ -45,22 +45,6 @@ __device__ __forceinline__ float dec_dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 __device__ __forceinline__ float dec_silu(float z) { return z / (1.0f + expf(-z)); }
-// Sum over each group of lpr consecutive lanes (lpr a power of two up to 64),
-// left in the group's last lane, by DPP alone (row shifts, then the two row
-// broadcasts): plain VALU work that never waits on LDS traffic in flight.
-template <int CTRL, int ROW_MASK, bool BOUND_CTRL>
-__device__ __forceinline__ float dec_dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, BOUND_CTRL));
-}
-__device__ __forceinline__ float dec_group_sum_last(float v, int lpr) {
-    if (lpr > 1) v += dec_dpp<0x111, 0xF, true>(v);    // row_shr:1
-    if (lpr > 2) v += dec_dpp<0x112, 0xF, true>(v);    // row_shr:2
-    if (lpr > 4) v += dec_dpp<0x114, 0xF, true>(v);    // row_shr:4
-    if (lpr > 8) v += dec_dpp<0x118, 0xF, true>(v);    // row_shr:8
-    if (lpr > 16) v += dec_dpp<0x142, 0xA, false>(v);  // row_bcast:15
-    if (lpr > 32) v += dec_dpp<0x143, 0xC, false>(v);  // row_bcast:31
-    return v;
-}
 
 
 // Load at a 32-bit byte offset from a workgroup-uniform base.  Every plane
@@ -593,8 +577,8 @@ __device__ __forceinline__ void dec_rgu_compute(const Layer &L, const Work &W, c
             const int r = n >> 2, f = f0 + r * rpw;
             float g = a[0] * (half_to_f32((uint16_t)w.dg[r]) * xc.scale);
             float u = a[1] * (half_to_f32((uint16_t)w.du[r]) * xc.scale);
-            g = dec_group_sum_last(g, lpr) * 0.015625f;
-            u = dec_group_sum_last(u, lpr) * 0.015625f;
+            g = group_sum_last(g, lpr) * 0.015625f;
+            u = group_sum_last(u, lpr) * 0.015625f;
             if (c == lpr - 1 && f < F) st_tagged(W.htag + (int64_t)j * F + f, dec_silu(g) * u, tag);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -829,10 +813,10 @@ __device__ __forceinline__ bool dec_h16_finish(const Work &W, int F, int slot, u
         // chunk c = p / 8 is 8 consecutive lanes; sub-block s = (p / 2) % 4 is 2.
         // By DPP (no LDS round trip): lane pairs, quad halves, then each lane
         // with its mirror in the other quad of the 8
-        mx = fmaxf(mx, dec_dpp<0xB1, 0xF, false>(mx));   // quad_perm [1,0,3,2]
-        mx = fmaxf(mx, dec_dpp<0x4E, 0xF, false>(mx));   // quad_perm [2,3,0,1]
-        mx = fmaxf(mx, dec_dpp<0x141, 0xF, false>(mx));  // row_half_mirror
-        hs += dec_dpp<0xB1, 0xF, false>(hs);
+        mx = fmaxf(mx, dpp_f32<0xB1, 0xF, false>(mx));   // quad_perm [1,0,3,2]
+        mx = fmaxf(mx, dpp_f32<0x4E, 0xF, false>(mx));   // quad_perm [2,3,0,1]
+        mx = fmaxf(mx, dpp_f32<0x141, 0xF, false>(mx));  // row_half_mirror
+        hs += dpp_f32<0xB1, 0xF, false>(hs);
         if (mine) {
             const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFFu) - 127;
             const int e = min(max(ex - 14, -100), 100);
@@ -906,7 +890,7 @@ __device__ __forceinline__ void dec_rdn_compute16(const Layer &L, float *__restr
         const int row = r0 + r * rpw;
         const uint32_t dd = w.dd[r];
         float y = half_to_f32((uint16_t)(dd & 0xFFFFu)) * (A[r] * hsc) - half_to_f32((uint16_t)(dd >> 16)) * B[r];
-        y = dec_group_sum_last(y, lpr);
+        y = group_sum_last(y, lpr);
         if (c == lpr - 1 && row < E) atomicAdd(out + row, wgt * y);
     }
 }

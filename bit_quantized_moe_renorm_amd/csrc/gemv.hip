@@ -28,10 +28,6 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-__device__ __forceinline__ float group_sum(float v, int lpr) {
-    for (int off = lpr >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
 
 // x of one token for a 64-weight chunk: bf16 pairs (32 dwords) or fp32 (64 floats).
 template <bool XBF16>
@@ -158,9 +154,10 @@ __global__ __launch_bounds__(512) void k_gemv_gateup_routed(Layer L, Work W, con
             if (i < m) {
                 float g = iq2_chunk_dot<XBF16>(T, qg[r], xc[i], rep) * dg[r];
                 float uu = iq2_chunk_dot<XBF16>(T, qu[r], xc[i], rep) * du[r];
-                g = group_sum(g, lpr) * 0.015625f;
-                uu = group_sum(uu, lpr) * 0.015625f;
-                if (c == 0 && f < F) W.hbuf[(int64_t)slot[i] * F + f] = silu(g) * uu;
+                // the row's sums in the last lane of its group, by DPP
+                g = group_sum_last(g, lpr) * 0.015625f;
+                uu = group_sum_last(uu, lpr) * 0.015625f;
+                if (c == lpr - 1 && f < F) W.hbuf[(int64_t)slot[i] * F + f] = silu(g) * uu;
             }
         }
     }
@@ -319,8 +316,8 @@ __global__ __launch_bounds__(256) void k_gemv_down_routed(Layer L, Work W, float
         for (int r = 0; r < DN_NR; ++r) {
             const int row = r0 + r * rpw;
             float y = q2k_chunk_dot(qs[r], sc[r], dd[r], hv, hs);
-            y = group_sum(y, lpr);
-            if (c == 0 && row < E) atomicAdd(out + (int64_t)t * E + row, wgt * y);
+            y = group_sum_last(y, lpr);
+            if (c == lpr - 1 && row < E) atomicAdd(out + (int64_t)t * E + row, wgt * y);
         }
     }
 }

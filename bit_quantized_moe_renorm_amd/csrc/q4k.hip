@@ -99,11 +99,6 @@ __device__ __forceinline__ void q4_load_half(const void *src, int64_t off, float
     vs = a;
 }
 
-__device__ __forceinline__ float q4_group_sum(float v, int lpr) {
-    for (int off = lpr >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
 constexpr int Q4_WAVES = 4;
 constexpr int Q4_GU_NR = 2;  // gate/up rows per lane slot (each row: gate and up)
 constexpr int Q4_DN_NR = 4;  // down rows per lane slot
@@ -157,9 +152,10 @@ __global__ __launch_bounds__(64 * Q4_WAVES) void k_q4_gateup_routed(Layer L, Wor
 #pragma unroll
         for (int r = 0; r < Q4_GU_NR; ++r) {
             const int f = f0 + r * rpw;
-            const float g = q4_group_sum(q4k_acc_value(ag[r], mg[r]), lpr);
-            const float uu = q4_group_sum(q4k_acc_value(au[r], mu[r]), lpr);
-            if (c == 0 && f < F) W.hbuf[(int64_t)q * F + f] = q4_silu(g) * uu;
+            // the row's sums in the last lane of its group, by DPP
+            const float g = group_sum_last(q4k_acc_value(ag[r], mg[r]), lpr);
+            const float uu = group_sum_last(q4k_acc_value(au[r], mu[r]), lpr);
+            if (c == lpr - 1 && f < F) W.hbuf[(int64_t)q * F + f] = q4_silu(g) * uu;
         }
     }
 }
@@ -205,8 +201,8 @@ __global__ __launch_bounds__(64 * Q4_WAVES) void k_q4_down_routed(Layer L, Work 
 #pragma unroll
         for (int r = 0; r < Q4_DN_NR; ++r) {
             const int row = r0 + r * rpw;
-            const float y = q4_group_sum(q4k_acc_value(ad[r], md[r]), lpr);
-            if (c == 0 && row < E) atomicAdd(out + (int64_t)(q / k) * E + row, wgt * y);
+            const float y = group_sum_last(q4k_acc_value(ad[r], md[r]), lpr);
+            if (c == lpr - 1 && row < E) atomicAdd(out + (int64_t)(q / k) * E + row, wgt * y);
         }
     }
 }
