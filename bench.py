@@ -435,7 +435,9 @@ def run_prefill(args, layer=None, cpu=True):
                    "layer_hbm_frac": round(bytes_one / step_s / 1e9 / HBM_PEAK_GBS, 4),
                    "per_kernel": per_kernel},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": profile_traffic("prefill_2048_ds4_gemm_kernels.md"),
+                     "traffic_unit": "bytes per launch",
                      "algorithmic_flop_per_launch": fl[dom], "avg_launch_us": per_kernel[dom]["avg_us"]},
         "chunks_512": {"us_per_call": round(1e6 * call_s, 2), "tok_s": round(chunk / call_s, 1),
                        "distinct_experts": round(float(np.mean(us)), 2), "touched_expert_bytes": round(bytes_c),
