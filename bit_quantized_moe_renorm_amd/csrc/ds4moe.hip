@@ -87,6 +87,11 @@ struct ds4moe {
     Layer Lhost{};
     std::vector<void *> host_allocs;      // pinned host memory of the backing store
     SharedBlas *sblas = nullptr;          // the shared expert of large bf16 calls on hipBLASLt, if any
+    // with sblas: a stream for the shared expert, which then runs beside the
+    // routing and the routed gate/up GEMM (forked from and joined back into
+    // the caller's stream within the call)
+    hipStream_t s2 = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     // timing
     bool timing = false;
     std::vector<hipEvent_t> events;  // pairs
@@ -101,6 +106,9 @@ struct ds4moe {
         if (status_host) (void)hipHostFree(status_host);
         for (void *p : host_allocs) (void)hipHostFree(p);
         sblas_destroy(sblas);
+        if (ev_fork) (void)hipEventDestroy(ev_fork);
+        if (ev_join) (void)hipEventDestroy(ev_join);
+        if (s2) (void)hipStreamDestroy(s2);
     }
     void *alloc(size_t bytes, hipError_t &err) {
         void *p = nullptr;
@@ -516,6 +524,16 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     if (d->n_shared && d->act_dtype == DS4MOE_BF16 && d->max_tokens >= SBLAS_MIN_TOK &&
         sblas_create(&h->sblas, (int)F) != 0)
         h->sblas = nullptr;
+    if (h->sblas) {
+        // the shared expert's stream (default priority) and its fork and join
+        if (hipStreamCreateWithFlags(&h->s2, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess) {
+            (void)hipGetLastError();
+            delete h;
+            return fail(DS4MOE_EHIP, "create: the shared expert's stream or its events");
+        }
+    }
     h->decode_grid = decode_grid(d->act_dtype == DS4MOE_BF16);
     // the small-batch kernels stage at most two routed slots' and two shared
     // K parts' h vectors per workgroup: a workgroup's range of down units must
@@ -670,7 +688,30 @@ static int run_gemv(ds4moe *h, const Work &W, const void *x, int n, float *out, 
 
 // The expert kernels after the routing, any n: activation copies and chunk
 // table, then the four grouped GEMMs.
-static int run_gemm(ds4moe *h, const Work &W, const void *x, int n, float *out, hipStream_t s) {
+// The shared expert of a large call on hipBLASLt, on the handle's second
+// stream: forked after everything the caller's stream holds so far (before
+// the routing), joined back by run_gemm before the routed down GEMM (both add
+// into out; the shared one by a non-atomic read-modify-write).
+static bool shared_forks(const ds4moe *h, int n) {
+    return h->s2 && h->sblas && h->L.n_shared && n >= SBLAS_MIN_TOK;
+}
+static int fork_shared(ds4moe *h, const Work &W, const void *x, int n, float *out, hipStream_t s) {
+    hipStream_t s2 = h->s2;
+    int rc;
+    if ((rc = check_launch(h, hipEventRecord(h->ev_fork, s), "shared fork record"))) return rc;
+    if ((rc = check_launch(h, hipStreamWaitEvent(s2, h->ev_fork, 0), "shared fork wait"))) return rc;
+    int tb = h->tbegin(TK_GEMM_GU_SHARED, s2);
+    rc = check_launch(h, sblas_gateup(h->sblas, h->L, W, x, n, s2), "gemm shared gate/up");
+    h->tend(tb, s2);
+    if (rc) return rc;
+    tb = h->tbegin(TK_GEMM_DN_SHARED, s2);
+    rc = check_launch(h, sblas_down(h->sblas, h->L, W, n, out, s2), "gemm shared down");
+    h->tend(tb, s2);
+    if (rc) return rc;
+    return check_launch(h, hipEventRecord(h->ev_join, s2), "shared join record");
+}
+
+static int run_gemm(ds4moe *h, const Work &W, const void *x, int n, float *out, hipStream_t s, bool forked = false) {
     int tb = h->tbegin(TK_GEMM_PREP, s);
     int rc = check_launch(h, launch_gemm_prep(h->L, W, x, n, s), "gemm prep");
     h->tend(tb, s);
@@ -680,18 +721,20 @@ static int run_gemm(ds4moe *h, const Work &W, const void *x, int n, float *out, 
     h->tend(tb, s);
     if (rc) return rc;
     const bool blas = h->sblas && n >= SBLAS_MIN_TOK;
-    if (h->L.n_shared) {
+    if (h->L.n_shared && !forked) {
         tb = h->tbegin(TK_GEMM_GU_SHARED, s);
         rc = check_launch(h, blas ? sblas_gateup(h->sblas, h->L, W, x, n, s) : launch_gemm_gateup_shared(h->L, W, x, n, s),
                           "gemm shared gate/up");
         h->tend(tb, s);
         if (rc) return rc;
     }
+    // the forked shared expert has added into out before the routed atomics start
+    if (forked && (rc = check_launch(h, hipStreamWaitEvent(s, h->ev_join, 0), "shared join wait"))) return rc;
     tb = h->tbegin(TK_GEMM_DN_ROUTED, s);
     rc = check_launch(h, launch_gemm_down_routed(h->L, W, n, out, s), "gemm routed down");
     h->tend(tb, s);
     if (rc) return rc;
-    if (h->L.n_shared) {
+    if (h->L.n_shared && !forked) {
         tb = h->tbegin(TK_GEMM_DN_SHARED, s);
         rc = check_launch(h, blas ? sblas_down(h->sblas, h->L, W, n, out, s) : launch_gemm_down_shared(h->L, W, n, out, s),
                           "gemm shared down");
@@ -836,10 +879,13 @@ static int forward_impl(ds4moe_t *h, const void *x, const int32_t *ids, int32_t 
         return rc;
     }
     // the small-batch kernels build the per-expert lists themselves
+    // a large call's shared expert runs beside the routing and routed gate/up
+    const bool forked = path == DS4MOE_PATH_GEMM && shared_forks(h, n_tok);
+    if (forked && (rc = fork_shared(h, W, x, n_tok, out, s))) return rc;
     if ((rc = run_route(h, W, x, n_tok, s, path != DS4MOE_PATH_SMALL))) return rc;
     return path == DS4MOE_PATH_GEMV    ? run_gemv(h, W, x, n_tok, out, s)
            : path == DS4MOE_PATH_SMALL ? run_small(h, W, x, n_tok, out, s)
-                                       : run_gemm(h, W, x, n_tok, out, s);
+                                       : run_gemm(h, W, x, n_tok, out, s, forked);
 }
 
 int ds4moe_forward(ds4moe_t *h, const void *x, int32_t n_tok, float *out, void *stream) {
