@@ -95,6 +95,7 @@ struct Work {
     uint16_t *xhi, *xlo;  // [max_tokens][E] bf16 high / low parts of fp32 x (fp32 activations only)
     uint16_t *hsh_hi, *hsh_lo;  // [max_tokens][F] shared-expert activations, bf16 high / low parts
     float *part;          // [PART_ROWS][max(2F, E)] batched GEMMs: partial sums over K splits
+    float *part2;         // the same for the shared expert's tiles when they run on a second stream (or null)
     int4 *chunks;         // [gemm_max_chunks] (expert, first list position, count)
     int32_t *nchunks;     // number of valid chunks
     int32_t *ecount;      // [MAX_EXPERT] tokens per expert (batched router)

@@ -87,9 +87,9 @@ struct ds4moe {
     Layer Lhost{};
     std::vector<void *> host_allocs;      // pinned host memory of the backing store
     SharedBlas *sblas = nullptr;          // the shared expert of large bf16 calls on hipBLASLt, if any
-    // with sblas: a stream for the shared expert, which then runs beside the
-    // routing and the routed gate/up GEMM (forked from and joined back into
-    // the caller's stream within the call)
+    // a stream for the shared expert of calls on the grouped path (bf16
+    // tokens), which then runs beside the routing and the routed gate/up GEMM
+    // (forked from and joined back into the caller's stream within the call)
     hipStream_t s2 = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     // timing
@@ -326,6 +326,10 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     size_t o_xhi = carve(xf32 ? T * E * 2 : 0), o_xlo = carve(xf32 ? T * E * 2 : 0);
     size_t o_shh = carve(d->n_shared ? T * F * 2 : 0), o_shl = carve(d->n_shared ? T * F * 2 : 0);
     size_t o_part = carve((size_t)PART_ROWS * std::max<int64_t>(2 * F, E) * 4);
+    // a second one for the shared expert's tiles, which run beside the routed
+    // GEMMs on a second stream in calls of bf16 tokens on the grouped path
+    const bool fork_tiles = !xf32 && d->n_shared && T >= 2;
+    size_t o_part2 = carve(fork_tiles ? (size_t)PART_ROWS * std::max<int64_t>(2 * F, E) * 4 : 0);
     size_t o_chunks = carve((size_t)gemm_max_chunks((int)T, (int)NE, (int)k) * 16), o_nch = carve(4);
     size_t o_ecnt = carve(MAX_EXPERT * 4), o_rest = carve(4 * T * NE * 4), o_rtag = carve(4 * MAX_EXPERT * 8);
     size_t o_htag = carve((size_t)(k + 1) * F * 8);
@@ -373,6 +377,7 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     W.hsh_hi = d->n_shared ? (uint16_t *)(ws + o_shh) : nullptr;
     W.hsh_lo = d->n_shared ? (uint16_t *)(ws + o_shl) : nullptr;
     W.part = (float *)(ws + o_part);
+    W.part2 = fork_tiles ? (float *)(ws + o_part2) : nullptr;
     W.chunks = (int4 *)(ws + o_chunks);
     W.nchunks = (int32_t *)(ws + o_nch);
     W.ecount = (int32_t *)(ws + o_ecnt);
@@ -524,7 +529,7 @@ int ds4moe_create(const ds4moe_desc *d, void *stream, ds4moe_t **out) {
     if (d->n_shared && d->act_dtype == DS4MOE_BF16 && d->max_tokens >= SBLAS_MIN_TOK &&
         sblas_create(&h->sblas, (int)F) != 0)
         h->sblas = nullptr;
-    if (h->sblas) {
+    if (h->sblas || h->W.part2) {
         // the shared expert's stream (default priority) and its fork and join
         if (hipStreamCreateWithFlags(&h->s2, hipStreamNonBlocking) != hipSuccess ||
             hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
@@ -688,24 +693,33 @@ static int run_gemv(ds4moe *h, const Work &W, const void *x, int n, float *out, 
 
 // The expert kernels after the routing, any n: activation copies and chunk
 // table, then the four grouped GEMMs.
-// The shared expert of a large call on hipBLASLt, on the handle's second
-// stream: forked after everything the caller's stream holds so far (before
-// the routing), joined back by run_gemm before the routed down GEMM (both add
-// into out; the shared one by a non-atomic read-modify-write).
+// The shared expert of a call on the grouped path (hipBLASLt from
+// SBLAS_MIN_TOK tokens, else the grouped tiles with their own partial-sum
+// buffer), on the handle's second stream: forked after everything the
+// caller's stream holds so far (before the routing), joined back by run_gemm
+// before the routed down GEMM (both add into out; the shared one by a
+// non-atomic read-modify-write).  bf16 tokens only: the tiles read x as it
+// comes, where fp32 tokens need the split the activation copy makes.
 static bool shared_forks(const ds4moe *h, int n) {
-    return h->s2 && h->sblas && h->L.n_shared && n >= SBLAS_MIN_TOK;
+    if (!h->s2 || !h->L.n_shared || h->L.act_dtype != DS4MOE_BF16) return false;
+    return (h->sblas && n >= SBLAS_MIN_TOK) || h->W.part2;
 }
 static int fork_shared(ds4moe *h, const Work &W, const void *x, int n, float *out, hipStream_t s) {
     hipStream_t s2 = h->s2;
     int rc;
     if ((rc = check_launch(h, hipEventRecord(h->ev_fork, s), "shared fork record"))) return rc;
     if ((rc = check_launch(h, hipStreamWaitEvent(s2, h->ev_fork, 0), "shared fork wait"))) return rc;
+    const bool blas = h->sblas && n >= SBLAS_MIN_TOK;
+    Work Ws = W;
+    Ws.part = W.part2;  // the tiles' partial sums (the routed gate/up GEMM uses W.part meanwhile)
     int tb = h->tbegin(TK_GEMM_GU_SHARED, s2);
-    rc = check_launch(h, sblas_gateup(h->sblas, h->L, W, x, n, s2), "gemm shared gate/up");
+    rc = check_launch(h, blas ? sblas_gateup(h->sblas, h->L, W, x, n, s2) : launch_gemm_gateup_shared(h->L, Ws, x, n, s2),
+                      "gemm shared gate/up");
     h->tend(tb, s2);
     if (rc) return rc;
     tb = h->tbegin(TK_GEMM_DN_SHARED, s2);
-    rc = check_launch(h, sblas_down(h->sblas, h->L, W, n, out, s2), "gemm shared down");
+    rc = check_launch(h, blas ? sblas_down(h->sblas, h->L, W, n, out, s2) : launch_gemm_down_shared(h->L, Ws, n, out, s2),
+                      "gemm shared down");
     h->tend(tb, s2);
     if (rc) return rc;
     return check_launch(h, hipEventRecord(h->ev_join, s2), "shared join record");

@@ -36,11 +36,11 @@
  * a hipStream_t (NULL = the null stream).  Every call that takes a stream only
  * enqueues work on it: no host synchronisation and no allocation happen in
  * ds4moe_route / ds4moe_forward / ds4moe_dequantize / ds4moe_rmsnorm.  A
- * forward call of a bf16 layer made with max_tokens >= 128 runs the shared
- * expert of calls of 128 tokens or more on a second stream of the handle
- * (created with it): forked from `stream` by an event, and joined back into
- * `stream` within the call, so that all of the call's work is ordered before
- * whatever is enqueued on `stream` after it.
+ * forward call on a bf16 layer with a shared expert that takes the grouped
+ * path (more tokens than the small-batch kernels take) runs the shared expert
+ * on a second stream of the handle (created with it): forked from `stream`
+ * by an event, and joined back into `stream` within the call, so that all of
+ * the call's work is ordered before whatever is enqueued on `stream` after it.
  *
  * Errors.  Every entry point returns DS4MOE_OK (0) or a negative status.
  * Arguments are validated before anything is enqueued; on a validation error
