@@ -291,6 +291,18 @@ __device__ __forceinline__ double wave_max_dpp(double v) {
                             __builtin_amdgcn_readlane(__double2loint(v), 63));
 }
 
+// Lanes of the wave whose key equals this lane's (keys below 2^bits), by
+// one ballot per key bit; every lane of the wave takes part.
+__device__ __forceinline__ uint64_t wave_match_any(uint32_t key, int bits) {
+    uint64_t m = ~0ull;
+    for (int b = 0; b < bits; ++b) {
+        const uint32_t kb = (key >> b) & 1u;
+        const uint64_t bb = __ballot(kb);
+        m &= kb ? bb : ~bb;
+    }
+    return m;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

@@ -220,11 +220,41 @@ __device__ void bucket_small(const unsigned long long *__restrict__ itag, uint32
         W.offsets[NE] = pre + v;
         W.active[0] = apre + __popcll(am);
     }
-    // list entries of expert tid, ascending
-    if (tid < NE && c > 0) {
-        int pos = start;
-        for (int q = 0; q < nq; ++q)
-            if (sidx[q] == tid) W.list[pos++] = q;
+    // list entries, ascending within each expert: selection q = tid + 256 j
+    // (group g = 4 j + wave of 64 consecutive selections) goes to its
+    // expert's start plus the earlier selections of that expert: those of its
+    // own group by a wave match, those of earlier groups from each group's
+    // per-expert counts (written by the group's first lane of each expert).
+    // A serial scan of all selections per expert took 5-10 us here.
+    constexpr int BS_GROUPS = BS_MAXQ / 64;
+    static_assert(BS_MAXQ <= 2 * 256 && MAX_EXPERT == 256, "two rounds of 256 selections, experts 8 bits");
+    __shared__ int ghist[BS_GROUPS][MAX_EXPERT];
+    __shared__ int estart[MAX_EXPERT];
+    const int ng = (nq + 63) / 64;
+    for (int i = tid; i < ng * MAX_EXPERT; i += 256) ghist[i / MAX_EXPERT][i % MAX_EXPERT] = 0;
+    estart[tid] = start;
+    __syncthreads();
+    int rank[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (256 * j >= nq) break;  // uniform
+        const int q = tid + 256 * j;
+        const bool in = q < nq;
+        const int e = in ? sidx[q] : 0;
+        const uint64_t m = wave_match_any((uint32_t)e, 8) & __ballot(in);
+        const uint64_t below = m & ((1ull << lane) - 1ull);
+        if (in && below == 0) ghist[4 * j + wave][e] = __popcll(m);
+        rank[j] = __popcll(below);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int q = tid + 256 * j;
+        if (q >= nq) break;
+        const int e = sidx[q], g = 4 * j + wave;
+        int r = rank[j];
+        for (int h = 0; h < g; ++h) r += ghist[h][e];
+        W.list[estart[e] + r] = q;
     }
 }
 

@@ -118,12 +118,17 @@ __device__ void sb_read_route(const Layer &L, const Work &W, int n, SbRoute &R, 
     }
     if (export_lists && NE == 256 && tid == 256) W.offsets[256] = nq;
     __syncthreads();
-    if (tid < nq) {
-        // entry position: the expert's offset plus the earlier selections of it
-        int r = 0;
-        for (int q = 0; q < tid; ++q) r += R.sel[q] == e;
-        R.lst[cnt[e] + r] = tid;
-        if (export_lists) W.list[cnt[e] + r] = tid;
+    if (wave == 0) {
+        // entry position: the expert's offset plus the earlier selections of
+        // it, counted by a wave match (every selection is in wave 0: nq <= 64)
+        static_assert(SB_SLOTS <= 64 && MAX_EXPERT <= 256, "the selections fit one wave, experts 8 bits");
+        const bool v = tid < nq;
+        const uint64_t m = wave_match_any((uint32_t)e, 8) & __ballot(v);
+        if (v) {
+            const int r = __popcll(m & ((1ull << lane) - 1ull));
+            R.lst[cnt[e] + r] = tid;
+            if (export_lists) W.list[cnt[e] + r] = tid;
+        }
     }
     __syncthreads();
 }
