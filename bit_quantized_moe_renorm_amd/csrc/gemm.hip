@@ -155,7 +155,8 @@ __device__ __forceinline__ half8 block_a(const uint8_t *stg, int i, int c, int r
 // Main loop and epilogue of the routed gate/up GEMM for a chunk of NT token
 // tiles (NT is a template parameter so the step bodies have no branches).
 template <int NT>
-__device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &W, const uint4 *T, uint8_t *stg0,
+__device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &W, const uint4 *T, const uint4 *ST,
+                                                    uint8_t *stg0,
                                                     uint8_t *stg1, const BlockLoader &ld, uint4 (&xr)[LD_V],
                                                     const uint8_t *qg, const uint16_t *dg, int fq, int fd, int f0,
                                                     int beg, int cnt, int rl, int grp, int nbe, float *part,
@@ -208,9 +209,15 @@ __device__ __forceinline__ void gateup_routed_tiles(const Layer &L, const Work &
         half2v scl[GU_NF];
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
+            // signs from the mask table for one or two token tiles; with more
+            // tiles the A reads keep the LDS busy and the bit arithmetic is
+            // cheaper (2048-token prefill: 698 -> 782 us with the table)
             half8 b[GU_NF];
 #pragma unroll
-            for (int fi = 0; fi < GU_NF; ++fi) b[fi] = iq2_b_operand(T, wcur[fi], dcur[fi], cc, rl, scl[fi]);
+            for (int fi = 0; fi < GU_NF; ++fi)
+                b[fi] = NT <= 2 ? iq2_b_finish_masked(iq2_b_lookup(T, wcur[fi], cc, rl), iq2_s_lookup(ST, wcur[fi], cc, rl),
+                                                      wcur[fi], dcur[fi], cc, scl[fi])
+                                : iq2_b_operand(T, wcur[fi], dcur[fi], cc, rl, scl[fi]);
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
                 const half8 a = block_a(cur, i, cc, rl, grp);
@@ -305,6 +312,7 @@ __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_gateup_routed(Layer L, W
     const int4 ch = W.chunks[c];
     const int e = ch.x, beg = ch.y, cnt = ch.z;
     __shared__ uint4 T[256 * IQ2_REPL];
+    __shared__ uint4 ST[128 * IQ2S_REPL];
     __shared__ __align__(16) uint8_t stg[2][RB_STAGE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rl = lane & 15, grp = lane >> 4;
@@ -324,13 +332,14 @@ __global__ __launch_bounds__(RB_THREADS, 1) void k_gemm_gateup_routed(Layer L, W
     uint4 xr[LD_V];
     ld.load(0, xr);
     iq2_build_lut<true>(T, L.codebook, tid, RB_THREADS);
+    if (cnt <= 32) iq2_build_sign_table(ST, tid, RB_THREADS);
     ld.store(stg[0], xr);
     __syncthreads();
     switch ((cnt + 15) >> 4) {
-        case 1: gateup_routed_tiles<1>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
-        case 2: gateup_routed_tiles<2>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
-        case 3: gateup_routed_tiles<3>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
-        default: gateup_routed_tiles<4>(L, W, T, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
+        case 1: gateup_routed_tiles<1>(L, W, T, ST, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
+        case 2: gateup_routed_tiles<2>(L, W, T, ST, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
+        case 3: gateup_routed_tiles<3>(L, W, T, ST, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
+        default: gateup_routed_tiles<4>(L, W, T, ST, stg[0], stg[1], ld, xr, qg, dg, fq, fd, f0, beg, cnt, rl, grp, bps, part, nq); break;
     }
 }
 
@@ -879,14 +888,18 @@ hipError_t launch_gemm_down_shared(const Layer &L, const Work &W, int n_tok, flo
 // Debug: one routed expert matrix exactly as the grouped GEMMs feed it to
 // the MFMAs, through iq2_b_operand and q2k_b_operand (which 0 gate, 1 up:
 // [n_ff][n_embd]; 2 down: [n_embd][n_ff]), each fp16 value widened to fp32.
+// IQ2 values are also decoded with the sign-mask table (iq2_b_finish_masked);
+// a value on which the two decodes differ in any bit is written as NaN.
 // One thread per (row, 256-K block, lane quarter g), its 8 steps in order.
 __global__ __launch_bounds__(256) void k_debug_gemm_b(Layer L, int which, int expert, float *__restrict__ dst) {
     __shared__ uint4 T[256 * IQ2_REPL];
+    __shared__ uint4 ST[128 * IQ2S_REPL];
     __shared__ uint2 QT[256 * QT_REPL];
     const int tid = threadIdx.x;
-    if (which < 2)
+    if (which < 2) {
         iq2_build_lut<true>(T, L.codebook, tid, 256);
-    else
+        iq2_build_sign_table(ST, tid, 256);
+    } else
         q2k_build_table(QT, tid, 256);
     __syncthreads();
     const int rows = which < 2 ? L.n_ff : L.n_embd, nb = which < 2 ? L.nbe : L.nbf;
@@ -901,10 +914,14 @@ __global__ __launch_bounds__(256) void k_debug_gemm_b(Layer L, int which, int ex
     if (which < 2) {
         const uint4 w = *reinterpret_cast<const uint4 *>(L.iq2_qs[which] + rb * 64 + 16 * g);
         const uint16_t d = L.iq2_d[which][rb];
-        half2v scl;
+        half2v scl, scl2;
         for (int cc = 0; cc < 8; ++cc) {
             const half8 b = iq2_b_operand(T, w, d, cc, rl, scl);
-            for (int j = 0; j < 8; ++j) o[8 * cc + j] = (float)b[j];
+            const half8 b2 = iq2_b_finish_masked(iq2_b_lookup(T, w, cc, rl), iq2_s_lookup(ST, w, cc, rl), w, d, cc, scl2);
+            const uint4 u = __builtin_bit_cast(uint4, b), u2 = __builtin_bit_cast(uint4, b2);
+            const uint32_t dx[4] = {u.x ^ u2.x, u.y ^ u2.y, u.z ^ u2.z, u.w ^ u2.w};
+            for (int j = 0; j < 8; ++j)
+                o[8 * cc + j] = ((dx[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) ? __builtin_nanf("") : (float)b[j];
         }
     } else {
         const uint4 q = *reinterpret_cast<const uint4 *>(L.q2k_qs + rb * 64 + 16 * g);

@@ -60,6 +60,37 @@ __device__ __forceinline__ half8 iq2_b_operand(const uint4 *T, const uint4 &w, u
     return iq2_b_finish(iq2_b_lookup(T, w, cc, rl), w, d, cc, scl);
 }
 
+// Sign masks from a table instead of bit arithmetic: entry s7 (the 7 stored
+// sign bits of a group) holds the group's four XOR masks (bit 15 and bit 31
+// of dword j for weights 2j and 2j+1, the 8th sign from the parity), that is
+// iq2_apply_signs of zero levels, so the signed levels are identical.  128
+// entries, IQ2S_REPL replicas interleaved at 16-byte granularity (entry s,
+// replica r at uint4 index s IQ2S_REPL + r); lane l reads replica l & 7, so at
+// most two of the 16 lanes served together share a bank quad.  Five VALU
+// operations per group fewer than the bit arithmetic, one more LDS read: it
+// pays where the IQ2 decode is shared by few token tiles (the A operand's LDS
+// reads are then few).
+constexpr int IQ2S_REPL = 8;
+__device__ __forceinline__ void iq2_build_sign_table(uint4 *ST, int tid, int nthreads) {
+    for (int i = tid; i < 128 * IQ2S_REPL; i += nthreads)
+        ST[i] = iq2_apply_signs(make_uint4(0u, 0u, 0u, 0u), (uint32_t)i / IQ2S_REPL);
+}
+__device__ __forceinline__ uint4 iq2_s_lookup(const uint4 *ST, const uint4 &w, int cc, int rl) {
+    const uint32_t sw = (cc < 4) ? w.y : w.w;
+    return ST[((sw >> (7 * (cc & 3))) & 0x7Fu) * IQ2S_REPL + (rl & 7)];
+}
+// iq2_b_finish with the signs as looked-up masks sm.
+__device__ __forceinline__ half8 iq2_b_finish_masked(uint4 lv, const uint4 &sm, const uint4 &w, uint16_t d, int cc,
+                                                     half2v &scl) {
+    const uint32_t sw = (cc < 4) ? w.y : w.w;
+    if ((cc & 3) == 0) {
+        const _Float16 s = (_Float16)(half_to_f32(d) * (0.015625f * (float)(2u * (sw >> 28) + 1u)));
+        scl = half2v{s, s};
+    }
+    lv.x ^= sm.x, lv.y ^= sm.y, lv.z ^= sm.z, lv.w ^= sm.w;
+    return as_half8(lv) * __builtin_shufflevector(scl, scl, 0, 1, 0, 1, 0, 1, 0, 1);
+}
+
 // Q2_K B decode: a table of the four 2-bit values of each qs byte as fp16
 // (8 bytes per entry), 16 replicas interleaved per entry; lane l reads replica l % 16.
 constexpr int QT_REPL = 16;

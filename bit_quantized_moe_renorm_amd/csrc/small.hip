@@ -7,7 +7,8 @@
 // stream from HBM once per call, for all of the tokens that chose it, with
 // every CU streaming.  Here:
 //   k_small_gateup: every workgroup stages all tokens' x in LDS (fp16 under a
-//     per-token power-of-two scale) and the IQ2 level table, then streams a
+//     per-token power-of-two scale), the IQ2 level table and the sign-mask
+//     table (mfma_ops.h), then streams a
 //     contiguous range of units: the shared expert's gate and up (16 rows x
 //     256 K, bf16) and each selected expert's gate and up (16 rows x up to
 //     eight 256-K blocks, IQ2).  A unit is one wave's MFMA tile: 16 weight
@@ -269,7 +270,8 @@ __device__ __forceinline__ void sb_gu_load(const Layer &L, const SbRoute &R, int
 // Half h of unit i into the gate and up accumulators (16 tokens x 16 rows).
 // Lanes past the unit's tokens read its first token's x: their products land
 // in C rows never stored.
-__device__ __forceinline__ void sb_gu_compute(const Layer &L, const SbRoute &R, const uint4 *T, const uint8_t *xs,
+__device__ __forceinline__ void sb_gu_compute(const Layer &L, const SbRoute &R, const uint4 *T, const uint4 *ST,
+                                              const uint8_t *xs,
                                               int i, int h, int ns, int TG, int pr, int bpu, int n, const SbW &w,
                                               floatx4 &ag, floatx4 &au) {
     const int lane = threadIdx.x & 63, rl = lane & 15, grp = lane >> 4;
@@ -299,9 +301,10 @@ __device__ __forceinline__ void sb_gu_compute(const Layer &L, const SbRoute &R, 
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
             const uint4 lg = iq2_b_lookup(T, w.q[s], cc, rl), lu = iq2_b_lookup(T, w.q[4 + s], cc, rl);
+            const uint4 mg = iq2_s_lookup(ST, w.q[s], cc, rl), mu = iq2_s_lookup(ST, w.q[4 + s], cc, rl);
             const half8 a = *reinterpret_cast<const half8 *>(xr + 512 * b + 16 * cc);
-            const half8 bg = iq2_b_finish(lg, w.q[s], (uint16_t)dgb, cc, sg);
-            const half8 bu = iq2_b_finish(lu, w.q[4 + s], (uint16_t)dub, cc, su);
+            const half8 bg = iq2_b_finish_masked(lg, mg, w.q[s], (uint16_t)dgb, cc, sg);
+            const half8 bu = iq2_b_finish_masked(lu, mu, w.q[4 + s], (uint16_t)dub, cc, su);
             ag = mfma_f16(a, bg, ag);
             au = mfma_f16(a, bu, au);
         }
@@ -343,10 +346,11 @@ __device__ __forceinline__ void sb_gu_store(const Layer &L, const SbRoute &R, co
     }
 }
 
-// grid: one workgroup per CU (LDS: the level table and x), SB_THREADS threads.
+// grid: one workgroup per CU (LDS: the level and sign tables and x), SB_THREADS threads.
 __global__ __launch_bounds__(SB_THREADS, 1) void k_small_gateup(Layer L, Work W, const uint16_t *__restrict__ x,
                                                                 int n, float *__restrict__ gu) {
     __shared__ uint4 T[256 * IQ2_REPL];
+    __shared__ uint4 ST[128 * IQ2S_REPL];
     __shared__ __align__(16) uint8_t xs[SMALL_MAX_TOK * SB_XP];
     __shared__ SbRoute R;
     __shared__ int ecnt[MAX_EXPERT + 1];
@@ -389,6 +393,7 @@ __global__ __launch_bounds__(SB_THREADS, 1) void k_small_gateup(Layer L, Work W,
         if (iv < nv && (tid & 31) == 31) atomicMax(&xmax[iv / e8], __float_as_uint(m));
     }
     if (tid < 256) iq2_lut_entry<true>(T, tid, cbw);
+    iq2_build_sign_table(ST, tid, SB_THREADS);
     __syncthreads();
     if (tid < n) xsc[tid] = sb_pow2(sb_scale_exp(__uint_as_float(xmax[tid])));
 #pragma unroll
@@ -414,10 +419,10 @@ __global__ __launch_bounds__(SB_THREADS, 1) void k_small_gateup(Layer L, Work W,
     for (; i < g1; i += SB_WAVES) {
         sb_gu_load(L, R, i, 1, ns, TG, pr, bpu, false, wb);
         floatx4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-        sb_gu_compute(L, R, T, xs, i, 0, ns, TG, pr, bpu, n, wa, ag, au);
+        sb_gu_compute(L, R, T, ST, xs, i, 0, ns, TG, pr, bpu, n, wa, ag, au);
         const int nx = i + SB_WAVES;
         sb_gu_load(L, R, nx, 0, ns, TG, pr, bpu, nx >= g1, wa);
-        sb_gu_compute(L, R, T, xs, i, 1, ns, TG, pr, bpu, n, wb, ag, au);
+        sb_gu_compute(L, R, T, ST, xs, i, 1, ns, TG, pr, bpu, n, wb, ag, au);
         sb_gu_store(L, R, xsc, i, ns, TG, pr, n, ag, au, gu);
     }
 }

@@ -9,7 +9,10 @@ The routed GEMMs take their 2-bit weights as fp16 B operands
         + |dmin m| + |w|) (1 + 2^-10) + 3 * 2^-25 (the last term for results
         or minima in fp16's subnormal range).
 The bounds follow from the roundings alone, so a wrong index, sign, scale or
-K position fails them by orders of magnitude.
+K position fails them by orders of magnitude.  The debug kernel also decodes
+every IQ2 value with the sign-mask table (the path of one- and two-tile
+chunks and of the small-batch kernels) and writes NaN where the two decodes
+differ in any bit, which fails the bound.
 """
 import numpy as np
 import pytest
