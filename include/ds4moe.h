@@ -290,8 +290,11 @@ int ds4moe_dequantize(ds4moe_t *h, int32_t expert, int32_t which, float *dst, vo
  * device code (which and dst as for ds4moe_dequantize).  The 2-bit weights
  * are rounded to fp16 there: an IQ2 weight is its signed level times
  * fp16(d (2 ls + 1) / 64), rounded again in the product; a Q2_K weight is
- * fma(q, fp16(d sc), fp16(-dmin m)) in fp16.  DS4MOE_EUNSUPPORTED for a q4
- * layer (its kernels keep the weights exact in fp32).
+ * fma(q, fp16(d sc), fp16(-dmin m)) in fp16.  IQ2 values are decoded twice,
+ * with the signs from bit arithmetic and from the sign-mask table (the two
+ * decodes the kernels use); a value on which they differ in any bit is
+ * written as NaN.  DS4MOE_EUNSUPPORTED for a q4 layer (its kernels keep the
+ * weights exact in fp32).
  */
 int ds4moe_debug_gemm_b(ds4moe_t *h, int32_t expert, int32_t which, float *dst, void *stream);
 
