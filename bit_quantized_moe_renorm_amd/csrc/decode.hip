@@ -847,7 +847,10 @@ __device__ __forceinline__ bool dec_stage_h16(const Work &W, int F, int slot, ui
 // The 2-bit codes of byte pair k become fp16 pairs by one byte permute (bytes
 // 2k, 2k+1 into the low bytes of the two halves) and, per position u, one mask
 // (bits 2u, 2u+1 of each low byte): the subnormal q * 4^u * 2^-24, whose
-// product with the staged h * 2^-e * 4^-u is exact.
+// product with the staged h * 2^-e * 4^-u would be exact.  The dot product
+// instruction does not keep it so on gfx950: with one subnormal operand a
+// probe found results off by up to 3.1e-4 relative (normal operands: at most
+// one fp32 ulp), an error of the same order as h's fp16 rounding.
 __device__ __forceinline__ void dec_rdn_compute16(const Layer &L, float *__restrict__ out, int item, const DecPlan &P,
                                                   const RouteCache *rc, const RdnW &w, const uint4 *Hq,
                                                   const float *Hsc, const float *Hsum) {

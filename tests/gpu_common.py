@@ -19,7 +19,10 @@ GEMV_TOL = 1e-5
 # projections.  The rounding error of one h is at most 2^-12 of |h|; over the
 # 2048 terms of a down row they add up like a random walk, to about
 # 2^-12 / sqrt(3) ~ 1.4e-4 of the rms term, ~5e-5 of max|out| on the DS4 shapes.
-# The check takes 4x that.
+# The 2-bit codes enter the fp16 dot products as subnormals, whose products the
+# instruction rounds on gfx950 (a probe: up to 3.1e-4 relative, typically far
+# less), a second random error of the same order.  The check takes 4x the
+# h-rounding figure.
 FUSED_TOL = 2e-4
 
 
