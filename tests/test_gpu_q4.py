@@ -99,3 +99,36 @@ def test_q4_forward_static_and_route():
         dev.set_path(m.PATH_GEMM)
     assert ei.value.code == m.EUNSUPPORTED
     assert REL_TOL >= GEMV_TOL
+
+
+def _wide_range(x32):
+    """Seeded activations with a different power-of-two magnitude per 64-value
+    chunk (2^-20 .. 2^20), an all-zero chunk 0 and one large value in chunk 1:
+    the Q4_K kernels stage their inputs per chunk under a power-of-two scale,
+    so this covers empty chunks, both ends of the scale and a chunk whose
+    values span 2^25."""
+    x = np.array(x32, dtype=np.float32, copy=True)
+    nch = x.shape[1] // 64
+    for c in range(nch):
+        x[:, 64 * c:64 * c + 64] *= np.float32(2.0 ** (((7 * c) % 41) - 20))
+    x[:, 0:64] = 0.0
+    x[:, 64:128] *= np.float32(2.0 ** -12)
+    x[:, 69] = np.float32(3.0e4)
+    return x
+
+
+@pytest.mark.parametrize("kind,n", [("tiny", 1), ("tiny", 3), ("ds4", 1), ("ds4", 2)])
+def test_q4_wide_range_inputs(kind, n):
+    lay, dev = _host(kind), _dev(kind)
+    E = lay.spec.n_embd
+    if kind == "tiny":
+        x = _wide_range(synth.activations(0, n, E, bf16=False, start=20))
+    else:
+        x32 = synth.bf16_bits_to_f32(synth.activations(1, n, E, start=120))
+        x = synth.f32_to_bf16_bits(_wide_range(x32))
+    got = _run(dev, x)
+    ref, ridx, _ = oracle.forward(lay, x)
+    err = rel_err(got, ref)
+    log(f"[gpu] q4 {kind} wide-range n={n} rel err {err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= GEMV_TOL
