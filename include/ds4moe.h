@@ -293,8 +293,9 @@ int ds4moe_dequantize(ds4moe_t *h, int32_t expert, int32_t which, float *dst, vo
  * fma(q, fp16(d sc), fp16(-dmin m)) in fp16.  IQ2 values are decoded twice,
  * with the signs from bit arithmetic and from the sign-mask table (the two
  * decodes the kernels use); a value on which they differ in any bit is
- * written as NaN.  DS4MOE_EUNSUPPORTED for a q4 layer (its kernels keep the
- * weights exact in fp32).
+ * written as NaN.  DS4MOE_EUNSUPPORTED for a q4 layer (its kernels form no
+ * rounded weight: the 4-bit codes enter fp16 dot products exactly, as
+ * 1 + q/64, and d sc and dmin m are applied in fp32 per sub-block).
  */
 int ds4moe_debug_gemm_b(ds4moe_t *h, int32_t expert, int32_t which, float *dst, void *stream);
 
