@@ -203,7 +203,7 @@ __device__ __forceinline__ void q4_read_x(const Q4X &X, int hh, int c, uint4 (&x
 
 constexpr int Q4_WAVES = 4;
 constexpr int Q4_GU_NR = 2;  // gate/up rows per lane slot (each row: gate and up)
-constexpr int Q4_DN_NR = 4;  // down rows per lane slot
+constexpr int Q4_DN_NR = 2;  // down rows per lane slot (122 VGPRs: 4 waves per SIMD)
 
 // Routed gate/up: blockIdx.y = active expert slot, blockIdx.x = tile of rows.
 // h = SiLU(gate) up of every token of the expert -> hbuf (fp32, slot rows).
